@@ -1,0 +1,72 @@
+"""Test-side construction of stored blocks from hand-chosen fields.
+
+These builders let a test pick the exact quantized fields (so the dense
+weights are known by construction) and lay them out in the stored byte
+order: Q8_0 = fp16 d + 32 int8; Q4_K = fp16 d, fp16 dmin, 12 packed 6-bit
+(sc, m) bytes, 128 quant bytes (byte 32c+l: element l of sub-block 2c low
+nibble, of 2c+1 high nibble).  They contain no dequantization.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def half_bits_value(bits: int) -> float:
+    return float(np.array([bits], dtype=np.uint16).view(np.float16)[0])
+
+
+def q8_0_row(d_bits: int, q: np.ndarray) -> bytes:
+    q = np.asarray(q, dtype=np.int64)
+    assert q.size % 32 == 0
+    out = bytearray()
+    for b in range(q.size // 32):
+        out += bytes([d_bits & 0xFF, d_bits >> 8])
+        out += bytes(int(v) & 0xFF for v in q[b * 32:(b + 1) * 32])
+    return bytes(out)
+
+
+def q4k_superblock(d_bits: int, dmin_bits: int, sc, m, q) -> bytes:
+    """q: [8][32] ints in 0..15; sc, m: 8 ints in 0..63."""
+    s12 = [0] * 12
+    for j in range(4):
+        s12[j] = (sc[j] & 63) | ((sc[j + 4] >> 4) << 6)
+        s12[j + 4] = (m[j] & 63) | ((m[j + 4] >> 4) << 6)
+        s12[j + 8] = (sc[j + 4] & 15) | ((m[j + 4] & 15) << 4)
+    qs = [0] * 128
+    for j in range(8):
+        for l in range(32):
+            qs[(j // 2) * 32 + l] |= int(q[j][l]) << (4 * (j % 2))
+    return bytes([d_bits & 0xFF, d_bits >> 8, dmin_bits & 0xFF, dmin_bits >> 8] + s12 + qs)
+
+
+def random_q8_0_matrix(rng: np.random.Generator, rows: int, cols: int, d_bits: int = 0x2400):
+    """A Q8_0 matrix with one fixed d; returns (stored bytes, exact dense float64 values)."""
+    q = rng.integers(-127, 128, size=(rows, cols))
+    raw = b"".join(q8_0_row(d_bits, q[r]) for r in range(rows))
+    return np.frombuffer(raw, dtype=np.uint8).copy(), half_bits_value(d_bits) * q.astype(np.float64)
+
+
+def random_q4k_matrix(rng: np.random.Generator, rows: int, cols: int, d_bits: int = 0x2000,
+                      dmin_bits: int = 0x1C00):
+    """A Q4_K matrix with random 6-bit scales/mins and 4-bit quants; returns (bytes, exact dense values)."""
+    d, dmin = half_bits_value(d_bits), half_bits_value(dmin_bits)
+    dense = np.empty((rows, cols), dtype=np.float64)
+    parts = []
+    for r in range(rows):
+        for sb in range(cols // 256):
+            sc = rng.integers(0, 64, size=8)
+            m = rng.integers(0, 64, size=8)
+            q = rng.integers(0, 16, size=(8, 32))
+            parts.append(q4k_superblock(d_bits, dmin_bits, sc, m, q))
+            for j in range(8):
+                dense[r, sb * 256 + j * 32: sb * 256 + (j + 1) * 32] = d * sc[j] * q[j] - dmin * m[j]
+    return np.frombuffer(b"".join(parts), dtype=np.uint8).copy(), dense
+
+
+def random_expert(rng: np.random.Generator, fmt: int, H: int, I: int):
+    """Canonical blob Wg|Wu|Wd with exactly known dense matrices."""
+    make = random_q8_0_matrix if fmt == 0 else random_q4k_matrix
+    bg, g = make(rng, I, H)
+    bu, u = make(rng, I, H)
+    bd, dn = make(rng, H, I)
+    return np.concatenate([bg, bu, bd]), (g, u, dn)

@@ -1,0 +1,271 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each pin is checked twice: the oracle as written passes it, and a planted
+mistake in the oracle (``oracle.set_defect``) makes it fail, so a pin that
+could not notice its defect is itself caught.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from scipy.special import expit, softmax
+
+import fixtures as F
+import oracle as O
+from tests import _blocks as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLD = os.path.join(ROOT, "tests", "golden")
+
+
+@pytest.fixture(autouse=True)
+def _clean_defect():
+    O.set_threads(4)
+    O.set_defect(0)
+    yield
+    O.set_defect(0)
+
+
+# ----------------------------------------------------------------- pins
+
+def pin_golden_blocks() -> bool:
+    doc = json.load(open(os.path.join(GOLD, "quant_blocks.json")))
+    ok = True
+    for case in doc["cases"]:
+        raw = np.frombuffer(bytes.fromhex(case["bytes_hex"]), dtype=np.uint8)
+        fmt = O.Q8_0 if case["format"] == "Q8_0" else O.Q4K
+        got = O.dequant(fmt, raw, len(case["expected"]))
+        want = np.array([float(Fraction(v)) for v in case["expected"]])
+        ok &= bool(np.array_equal(got, want))
+    return ok
+
+
+def pin_encoder_round_trip() -> bool:
+    """The encoder (input generator, separate code) and the oracle's decoder
+    agree: every weight is reproduced within the quantization step bound."""
+    ok = True
+    w = F.matrix_f32(11, 0, 3, 0, 64, 2048).astype(np.float64)
+    for fmt in (O.Q8_0, O.Q4K):
+        raw = F.encode(fmt, w.astype(np.float32))
+        got = O.dequant(fmt, raw, w.size).reshape(w.shape)
+        err = np.abs(got - w)
+        if fmt == O.Q8_0:
+            d = np.array([B.half_bits_value(int(raw[i]) | (int(raw[i + 1]) << 8))
+                          for i in range(0, raw.size, 34)]).reshape(64, -1)
+            bound = np.repeat(d * (0.5 + 127 * 2.0 ** -11) + 1e-12, 32, axis=1)
+        else:
+            d = np.array([B.half_bits_value(int(raw[i]) | (int(raw[i + 1]) << 8)) for i in range(0, raw.size, 144)])
+            dm = np.array([B.half_bits_value(int(raw[i + 2]) | (int(raw[i + 3]) << 8))
+                           for i in range(0, raw.size, 144)])
+            # q rounding (<= d*sc/2 <= 31.5 d), scale rounding over 15 steps (<= 7.5 d),
+            # min rounding (<= dmin/2) and fp16 slack on both.
+            bound = np.repeat((40 * d + 0.5 * dm) * (1 + 2.0 ** -9) + 1e-12, 256).reshape(w.shape)
+        ok &= bool(np.all(err <= bound))
+        ok &= bool(np.sqrt(np.mean(err ** 2)) < 0.2 * w.std())
+        ok &= bool(np.corrcoef(got.ravel(), w.ravel())[0, 1] > 0.98)
+    return ok
+
+
+def pin_routing_golden() -> bool:
+    doc = json.load(open(os.path.join(GOLD, "routing.json")))
+    ok = True
+    for c in doc["cases"]:
+        ids, w = O.route(np.array(c["logits"], dtype=np.float32), c["k"],
+                         O.SOFTMAX if c["score"] == "softmax" else O.SIGMOID, c["renormalize"], c["scale"])
+        ok &= ids.tolist() == c["ids"]
+        ok &= bool(np.allclose(w, np.array(c["w"]), rtol=0, atol=1e-14))
+    return ok
+
+
+def pin_routing_vs_library(score: int) -> bool:
+    rng = np.random.default_rng(5)
+    T, E, k = 64, 48, 6
+    lg = rng.normal(size=(T, E)).astype(np.float32)
+    lg[3, 10] = lg[3, 20] = lg[3, 30] = np.float32(4.5)  # a tie inside the top k
+    scale = 2.5 if score == O.SIGMOID else 1.0
+    ids, w = O.route(lg, k, score, True, scale)
+    want_ids = np.argsort(-lg, axis=1, kind="stable")[:, :k]
+    p = softmax(lg.astype(np.float64), axis=1) if score == O.SOFTMAX else expit(lg.astype(np.float64))
+    sel = np.take_along_axis(p, want_ids, axis=1)
+    want_w = scale * sel / sel.sum(axis=1, keepdims=True)
+    return bool(np.array_equal(ids, want_ids)) and bool(np.allclose(w, want_w, rtol=1e-13, atol=0)) and \
+        bool(np.allclose(w.sum(axis=1), scale, rtol=1e-13))
+
+
+def pin_batches_vs_sort() -> bool:
+    rng = np.random.default_rng(9)
+    T, E, k, S = 37, 40, 5, 24
+    lg = rng.normal(size=(T, E)).astype(np.float32)
+    ids, w = O.route(lg, k)
+    soe = np.full(E, -1, dtype=np.int32)
+    chosen = rng.permutation(E)[:S]
+    soe[chosen] = rng.permutation(S)
+    got = O.batches(ids, w, E, soe, S)
+    pairs = [(int(soe[ids.ravel()[p]]), p) for p in range(T * k)]
+    res = sorted([q for q in pairs if q[0] >= 0], key=lambda q: q[0])  # Python's sort is stable
+    ok = got["perm_pair"].tolist() == [p for _, p in res]
+    counts = np.bincount([s for s, _ in res], minlength=S)
+    ok &= got["slot_offsets"].tolist() == [0] + np.cumsum(counts).tolist()
+    ok &= got["active_slots"].tolist() == [s for s in range(S) if counts[s] > 0]
+    host = [p for s, p in pairs if s < 0]
+    ok &= got["host_token"].tolist() == [p // k for p in host]
+    ok &= got["host_expert"].tolist() == [int(ids.ravel()[p]) for p in host]
+    ok &= bool(np.array_equal(got["host_weight"], w.ravel()[host]))
+    ok &= int(got["slot_offsets"][S]) + int(got["host_count"][0]) == T * k
+    return ok
+
+
+def _dense_ffn(g, u, dn, x):
+    gx, ux = g @ x, u @ x
+    return dn @ (gx * expit(gx) * ux)
+
+
+def pin_ffn_dense(fmt: int) -> bool:
+    rng = np.random.default_rng(17 + fmt)
+    H, I = (512, 256) if fmt == O.Q4K else (96, 64)
+    blob, (g, u, dn) = B.random_expert(rng, fmt, H, I)
+    x = rng.normal(size=H)
+    got = O.expert_ffn(fmt, blob, H, I, x)
+    want = _dense_ffn(g, u, dn, x)
+    return bool(np.allclose(got, want, rtol=1e-11, atol=1e-11 * np.abs(want).max()))
+
+
+def _layer_case(fmt, rng, E=6, H=256, I=256, T=5, k=2):
+    experts = [B.random_expert(rng, fmt, H, I) for _ in range(E)]
+    shared_blob, shared_dense = B.random_expert(rng, O.Q8_0, H, 64)
+    x = rng.normal(size=(T, H))
+    lg = rng.normal(size=(T, E)).astype(np.float32)
+    return experts, shared_blob, shared_dense, x, lg
+
+
+def pin_layer_brute_force(score: int, partial: bool) -> bool:
+    """y = sum over ALL experts of mask * weight * FFN_e(x) + shared, with dense
+    matrices: the all-expert masked sum the method avoids computing."""
+    rng = np.random.default_rng(23 + 2 * score + int(partial))
+    E, H, I, T, k = 6, 256, 256, 5, 2
+    experts, sblob, sd, x, lg = _layer_case(O.Q4K, rng, E, H, I, T, k)
+    scale = 2.5 if score == O.SIGMOID else 1.0
+    soe = np.arange(E, dtype=np.int32)
+    if partial:
+        soe[[1, 4]] = -1
+    out = O.moe_layer(O.Q4K, [b for b, _ in experts], H, I, x, lg, k, score, True, scale, soe, sblob, O.Q8_0, 64)
+    order = np.argsort(-lg, axis=1, kind="stable")
+    p = softmax(lg.astype(np.float64), axis=1) if score == O.SOFTMAX else expit(lg.astype(np.float64))
+    want = np.zeros((T, H))
+    for t in range(T):
+        sel = order[t, :k]
+        z = p[t, sel].sum()
+        for e in range(E):
+            if e in sel and soe[e] >= 0:
+                want[t] += scale * p[t, e] / z * _dense_ffn(*experts[e][1], x[t])
+        want[t] += _dense_ffn(*sd, x[t])
+    return bool(np.allclose(out["y"], want, rtol=1e-11, atol=1e-11 * np.abs(want).max()))
+
+
+def pin_disjoint_halves() -> bool:
+    """Residency splits additively: y(A) + y(B) = y(A u B) for disjoint A, B (no shared expert)."""
+    rng = np.random.default_rng(31)
+    E, H, I, T, k = 8, 256, 256, 6, 3
+    experts, _, _, x, lg = _layer_case(O.Q4K, rng, E, H, I, T, k)
+    blobs = [b for b, _ in experts]
+    a = np.array([0, -1, 1, -1, 2, -1, 3, -1], dtype=np.int32)
+    b = np.array([-1, 0, -1, 1, -1, 2, -1, 3], dtype=np.int32)
+    y_a = O.moe_layer(O.Q4K, blobs, H, I, x, lg, k, slot_of_expert=a)["y"]
+    y_b = O.moe_layer(O.Q4K, blobs, H, I, x, lg, k, slot_of_expert=b)["y"]
+    y_all = O.moe_layer(O.Q4K, blobs, H, I, x, lg, k)["y"]
+    ok = bool(np.allclose(y_a + y_b, y_all, rtol=1e-12, atol=1e-12 * np.abs(y_all).max()))
+    ok &= not np.allclose(y_a, y_all)  # the halves are not trivial
+    return ok
+
+
+def pin_host_leg_completion() -> bool:
+    """The card's partial y plus the host list's pairs, served by the same FFN, is the all-resident y."""
+    rng = np.random.default_rng(37)
+    E, H, I, T, k = 8, 256, 256, 4, 3
+    experts, _, _, x, lg = _layer_case(O.Q4K, rng, E, H, I, T, k)
+    blobs = [b for b, _ in experts]
+    soe = np.array([0, -1, 1, 2, -1, 3, -1, 4], dtype=np.int32)
+    part = O.moe_layer(O.Q4K, blobs, H, I, x, lg, k, slot_of_expert=soe)
+    bat = O.batches(part["ids"], part["w"], E, soe, 5)
+    y = part["y"].copy()
+    for t, e, w in zip(bat["host_token"], bat["host_expert"], bat["host_weight"]):
+        y[t] += w * O.expert_ffn(O.Q4K, blobs[e], H, I, x[t])
+    y_all = O.moe_layer(O.Q4K, blobs, H, I, x, lg, k)["y"]
+    return bool(np.allclose(y, y_all, rtol=1e-12, atol=1e-12 * np.abs(y_all).max()))
+
+
+def pin_shared_is_forced_expert() -> bool:
+    rng = np.random.default_rng(41)
+    E, H, I, T, k = 4, 256, 256, 3, 2
+    experts, sblob, sd, x, lg = _layer_case(O.Q4K, rng, E, H, I, T, k)
+    blobs = [b for b, _ in experts]
+    with_s = O.moe_layer(O.Q4K, blobs, H, I, x, lg, k, shared_blob=sblob, shared_fmt=O.Q8_0, I_shared=64)["y"]
+    without = O.moe_layer(O.Q4K, blobs, H, I, x, lg, k)["y"]
+    want = np.stack([_dense_ffn(*sd, x[t]) for t in range(T)])
+    return bool(np.allclose(with_s - without, want, rtol=1e-10, atol=1e-11 * np.abs(want).max()))
+
+
+def pin_zero_input() -> bool:
+    rng = np.random.default_rng(43)
+    blob, _ = B.random_expert(rng, O.Q4K, 256, 256)
+    return bool(np.all(O.expert_ffn(O.Q4K, blob, 256, 256, np.zeros(256)) == 0.0))
+
+
+PINS = {
+    "golden_blocks": pin_golden_blocks,
+    "encoder_round_trip": pin_encoder_round_trip,
+    "routing_golden": pin_routing_golden,
+    "routing_softmax_vs_library": lambda: pin_routing_vs_library(O.SOFTMAX),
+    "routing_sigmoid_vs_library": lambda: pin_routing_vs_library(O.SIGMOID),
+    "batches_vs_sort": pin_batches_vs_sort,
+    "ffn_dense_q8_0": lambda: pin_ffn_dense(O.Q8_0),
+    "ffn_dense_q4k": lambda: pin_ffn_dense(O.Q4K),
+    "layer_brute_softmax_partial": lambda: pin_layer_brute_force(O.SOFTMAX, True),
+    "layer_brute_sigmoid_full": lambda: pin_layer_brute_force(O.SIGMOID, False),
+    "disjoint_halves": pin_disjoint_halves,
+    "host_leg_completion": pin_host_leg_completion,
+    "shared_is_forced_expert": pin_shared_is_forced_expert,
+    "zero_input": pin_zero_input,
+}
+
+
+@pytest.mark.parametrize("name", sorted(PINS))
+def test_pin_holds(name):
+    assert PINS[name]()
+
+
+# Each planted oracle mistake and a pin that must catch it.
+DEFECTS = [
+    (1, "golden_blocks"),                  # drop -dmin*m
+    (1, "ffn_dense_q4k"),
+    (2, "golden_blocks"),                  # wrong byte for the high scale bits
+    (3, "golden_blocks"),                  # Q8_0 read unsigned
+    (3, "ffn_dense_q8_0"),
+    (4, "ffn_dense_q4k"),                  # silu on the wrong operand
+    (4, "layer_brute_softmax_partial"),
+    (5, "routing_golden"),                 # tie order
+    (5, "routing_softmax_vs_library"),
+    (6, "routing_golden"),                 # scale inside the renormalisation
+    (6, "routing_sigmoid_vs_library"),
+    (7, "batches_vs_sort"),                # unstable grouping
+    (8, "shared_is_forced_expert"),        # shared expert dropped
+    (8, "layer_brute_sigmoid_full"),
+    (9, "ffn_dense_q8_0"),                 # gate and up matrices swapped
+    (10, "routing_golden"),                # no renormalisation
+    (10, "layer_brute_softmax_partial"),
+    (11, "golden_blocks"),                 # nibble halves swapped
+    (11, "encoder_round_trip"),
+    (12, "disjoint_halves"),               # residency ignored in the combine
+    (12, "layer_brute_softmax_partial"),
+]
+
+
+@pytest.mark.parametrize("defect,pin", DEFECTS)
+def test_pin_catches_planted_defect(defect, pin):
+    O.set_defect(defect)
+    try:
+        assert not PINS[pin]()
+    finally:
+        O.set_defect(0)
