@@ -352,6 +352,34 @@ void fx_gen_expert(int fmt, uint32_t seed, uint32_t layer, uint32_t expert, int6
     gen_matrix(fmt, seed, layer, expert, 2, H, I, std, out + 2 * gb);
 }
 
+/* Several experts at once, one parallel loop over every row of every matrix:
+ * out[i] = fx_gen_expert(fmt, seed, layer, experts[i], ...), blob i at
+ * out + i * fx_expert_bytes(fmt, H, I). */
+void fx_gen_experts(int fmt, uint32_t seed, uint32_t layer, const int32_t* experts, int n, int64_t H, int64_t I,
+                    float std, uint8_t* out) {
+    int64_t eb = fx_expert_bytes(fmt, H, I);
+    int64_t gb = fx_matrix_bytes(fmt, I, H);
+    int64_t rbH = row_bytes(fmt, H), rbI = row_bytes(fmt, I);
+    int64_t rows_per_expert = 2 * I + H;
+    int64_t total = (int64_t)n * rows_per_expert;
+#pragma omp parallel
+    {
+        float* buf = (float*)malloc((size_t)(H > I ? H : I) * sizeof(float));
+#pragma omp for schedule(dynamic, 64)
+        for (int64_t g = 0; g < total; ++g) {
+            int64_t i = g / rows_per_expert, r = g % rows_per_expert;
+            uint32_t matrix = r < I ? 0u : (r < 2 * I ? 1u : 2u);
+            int64_t row = matrix == 2 ? r - 2 * I : r - (int64_t)matrix * I;
+            int64_t cols = matrix == 2 ? I : H;
+            uint8_t* dst = out + i * eb + (matrix == 2 ? 2 * gb + row * rbI : matrix * gb + row * rbH);
+            normal_row(seed, 0x57000000u | matrix, (uint32_t)row, (uint32_t)experts[i], layer, 0.0f, std, buf, cols);
+            if (fmt == FX_Q8_0) fx_encode_q8_0(buf, cols, dst);
+            else fx_encode_q4k(buf, cols, dst);
+        }
+        free(buf);
+    }
+}
+
 /* Dense float copy of one generated matrix (before encoding), for tests of the encoders. */
 void fx_gen_matrix_f32(uint32_t seed, uint32_t layer, uint32_t expert, uint32_t matrix, int64_t rows,
                        int64_t cols, float std, float* out) {

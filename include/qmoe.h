@@ -1,0 +1,234 @@
+/*
+ * qmoe: one routed-expert mixture-of-experts layer over block-quantized
+ * expert weights, for AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The layer is the per-token hot path of an offloading MoE inference engine
+ * (bloomery README 0.3.1, opening list: routed experts live on the GPU and in
+ * host RAM, and the engine moves the experts it calls most onto the card;
+ * bloomery README of 2026-09-24: each routed layer keeps some of its experts
+ * on the GPU and the rest run on a host tier inside the same step).  One
+ * layer is five calls on one stream:
+ *
+ *   moe_route_topk            gate logits -> top-k expert ids and weights
+ *   moe_build_expert_batches  ids + slot map -> per-slot token batches and the
+ *                             list of pairs whose expert is not on the card
+ *   moe_expert_ffn_q4k /      dequantize + SwiGLU expert FFN over each slot's
+ *   moe_expert_ffn_q8_0       batch (decode GEMV or prefill MFMA GEMM)
+ *   moe_combine               weighted sum of the pairs (+ shared expert)
+ *
+ * Conventions for every call:
+ *   - Pointers marked "device" are device (HBM) addresses, "host" are host
+ *     addresses.  The caller allocates and owns every buffer, including the
+ *     workspaces sized by the *_workspace_size queries.  The library
+ *     allocates nothing and keeps no state between calls, except the
+ *     calling thread's error text and the optional stage timers.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Device calls
+ *     only enqueue work: they never synchronize and never read device memory
+ *     on the host, so a sequence of them can be captured into a hipGraph.
+ *   - Host-checkable arguments are checked before anything is enqueued; on
+ *     failure the call returns a non-zero status, writes no memory and
+ *     leaves a description in moe_last_error().  A failed launch returns
+ *     MOE_ERR_HIP.  Contents of device buffers (ids in range, a slot map
+ *     that is injective on its non-negative values) are preconditions; the
+ *     kernels clamp what they index with so that a violation gives wrong
+ *     values, never an out-of-bounds access.
+ *   - Enums travel as int.
+ */
+#ifndef QMOE_H
+#define QMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARGUMENT = 1,   /* null pointer, size out of range, bad enum */
+    MOE_ERR_UNSUPPORTED = 2,        /* valid request this build does not implement */
+    MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+    MOE_ERR_HIP = 4                 /* a HIP runtime call failed */
+} moe_status;
+
+typedef enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+typedef enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 } moe_path;
+typedef enum moe_format { MOE_FMT_Q8_0 = 0, MOE_FMT_Q4K = 1 } moe_format;
+
+/* Limits checked by the calls below. */
+#define MOE_MAX_EXPERTS 1024 /* E */
+#define MOE_MAX_TOPK 64      /* k */
+
+/* Name of a status code ("MOE_OK", ...); never NULL. */
+const char* moe_status_name(int status);
+
+/* Text of the last failure on the calling thread ("" if none).  The pointer
+ * stays valid until the thread's next failing call. */
+const char* moe_last_error(void);
+
+/* ------------------------------------------------------------------ route
+ * Top-k routing (bloomery README of 2026-09-24, "Oracle sets against
+ * ik_llama.cpp": router top-k ids must match exactly outside tie bands;
+ * bloomery README of 2026-09-24, reference list: the router core).
+ *
+ * logits   device, fp32 [T, E] row-major, finite.
+ * T        rows (tokens), >= 0.  T = 0 enqueues nothing.
+ * E        experts, 1..MOE_MAX_EXPERTS.
+ * k        experts per row, 1..min(E, MOE_MAX_TOPK).
+ * score    MOE_SCORE_SOFTMAX: p = softmax over the row's E logits.
+ *          MOE_SCORE_SIGMOID: p = 1 / (1 + exp(-logit)).
+ * renormalize  non-zero: w_j = p_j / sum of the k selected p; zero: w_j = p_j.
+ * scale    multiplies every weight after the rule above (e.g. 1.0, 2.5).
+ * topk_ids device, int32 [T, k]: the k experts in rank order, rank = logit
+ *          descending, equal logits by ascending id (both scores are
+ *          increasing in the logit, so this is the score order).
+ * topk_w   device, fp32 [T, k], weights in the same order.
+ */
+moe_status moe_route_topk(const float* logits, int T, int E, int k, int score, int renormalize, float scale,
+                          int32_t* topk_ids, float* topk_w, void* stream);
+
+/* ---------------------------------------------------------------- batches
+ * Group token-expert pairs by the HBM slot that holds the expert ("each
+ * expert over all its tokens at once": bloomery V4.1 README, "Batched
+ * prompts"; experts split between card and host: bloomery README of
+ * 2026-09-24, opening list).
+ *
+ * Pair p = t*k + j is (token t, expert topk_ids[p], weight topk_w[p]).  The
+ * pair is resident iff slot_of_expert[expert] is in [0, S).
+ *
+ * topk_ids, topk_w   device, [T*k] (output of moe_route_topk).
+ * slot_of_expert     device, int32 [E]; -1 = not on the card.  Must be
+ *                    injective on its values in [0, S) (moe_validate_slot_map).
+ * S                  slots, 0..E.
+ * slot_offsets       device, int32 [S+1]: exclusive prefix of per-slot counts;
+ *                    slot s owns perm_pair[slot_offsets[s] .. slot_offsets[s+1]).
+ * active_slots       device, int32 [min(S, T*k)]: the slots with a non-empty
+ *                    batch, ascending; only the first *num_active are written.
+ * num_active         device, int32 [1].
+ * perm_pair          device, int32 [T*k]: resident pairs, by slot ascending,
+ *                    inside a slot by ascending p (stable).  The first
+ *                    slot_offsets[S] entries are written.
+ * host_token, host_expert, host_weight
+ *                    device, [T*k]: the non-resident pairs in ascending p as
+ *                    (t, expert, weight): the host leg's work list.
+ * host_count         device, int32 [1].
+ * ws, ws_bytes       device workspace of at least moe_batches_workspace_size().
+ * Every output is a pure function of the inputs (no atomics-order effects).
+ */
+size_t moe_batches_workspace_size(int T, int k, int E, int S);
+moe_status moe_build_expert_batches(const int32_t* topk_ids, const float* topk_w, int T, int k, int E,
+                                    const int32_t* slot_of_expert, int S, int32_t* slot_offsets,
+                                    int32_t* active_slots, int32_t* num_active, int32_t* perm_pair,
+                                    int32_t* host_token, int32_t* host_expert, float* host_weight,
+                                    int32_t* host_count, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------ expert blobs
+ * Each HBM slot holds one expert as a packed blob: the canonical stored
+ * blocks of W_gate [I, H], W_up [I, H] and W_down [H, I] (rows = output
+ * features, blocks along the input dimension), rearranged for the kernels.
+ * Packing moves whole fields and bytes (Q4_K quants are re-ordered inside
+ * their sub-block, Q8_0 quants are stored offset by 128); a packed blob has
+ * exactly as many bytes as the canonical one.
+ *
+ * Canonical blocks (the stored types: bloomery README 0.3.1, "Status
+ * (0.3.1)" table, "Quant types" row, and README of 2026-09-24: shared
+ * experts in Q8_0):
+ *   Q8_0 (34 B / 32 weights): fp16 d, 32 int8 q;           w = d*q.
+ *   Q4_K (144 B / 256 weights): fp16 d, fp16 dmin, 12 B of 6-bit (sc, m)
+ *        for 8 sub-blocks of 32, 128 B of 4-bit q;        w = d*sc_j*q - dmin*m_j.
+ * Canonical blob = W_gate | W_up | W_down, each row-major.
+ *
+ * Supported shapes: Q4_K needs H % 256 == 0 and I % 256 == 0; Q8_0 needs
+ * H % 128 == 0 and I % 128 == 0.
+ */
+size_t moe_expert_blob_bytes(int format, int H, int I);
+
+/* Host, synchronous: canonical blob -> packed blob (both host memory,
+ * moe_expert_blob_bytes bytes each, not overlapping). */
+moe_status moe_pack_expert(int format, const void* canonical, void* packed, int H, int I);
+
+/* Host, synchronous: packed blob -> canonical blob (the exact inverse). */
+moe_status moe_unpack_expert(int format, const void* packed, void* canonical, int H, int I);
+
+/* Host: checks that every value is -1 or in [0, S) and that no slot is used
+ * twice.  E in 1..MOE_MAX_EXPERTS, S in 0..E. */
+moe_status moe_validate_slot_map(const int32_t* slot_of_expert, int E, int S);
+
+/* ------------------------------------------------------------- expert FFN
+ * For every resident pair, in its slot's batch: g = W_gate x_t,
+ * u = W_up x_t, h = silu(g) * u (silu(z) = z / (1 + exp(-z))),
+ * y_pairs[p] = W_down h.  Card experts run "in their stored quantization"
+ * (bloomery README 0.3.1, Status table, "Quant types" row); prompts run each
+ * expert over all its tokens at once as a GEMM (V4.1 README, "Batched
+ * prompts"; README 0.3.1, "Why it is fast": prompts as tensor-core GEMMs).
+ *
+ * slot_pool     device: S packed blobs at slot_pool + s * slot_stride;
+ *               16-byte aligned.  slot_stride >= moe_expert_blob_bytes and a
+ *               multiple of 16.
+ * S             slots, 1..MOE_MAX_EXPERTS (the S given to the batches call).
+ * H, I          hidden and expert-intermediate sizes.
+ * x             device, [T, H] row-major, x_dtype MOE_F32 or MOE_BF16.
+ * T, k          as in the batches call.
+ * slot_offsets, active_slots, num_active, perm_pair
+ *               device, outputs of moe_build_expert_batches for this T, k, S.
+ * y_pairs       device, [T*k, H] of y_dtype, indexed by pair p.  Rows of
+ *               resident pairs are written; other rows are left untouched.
+ * path          MOE_PATH_DECODE: GEMV, fp16 activations in fp32-accumulated
+ *               dot products, y_pairs MOE_F32.
+ *               MOE_PATH_PREFILL (Q4_K only): bf16 x, weights dequantized to
+ *               bf16 tiles, bf16 MFMA with fp32 accumulate, h rounded to bf16;
+ *               y_pairs MOE_F32 or MOE_BF16.
+ *               MOE_PATH_AUTO: PREFILL for Q4_K when T > 32, else DECODE.
+ * ws, ws_bytes  device workspace, at least moe_ffn_workspace_size(format, T,
+ *               k, H, I, path).
+ *
+ * The shared expert of a layer is served by moe_expert_ffn_q8_0 with a
+ * one-slot identity batch: S = 1, k = 1, slot_offsets = {0, T},
+ * active_slots = {0}, num_active = {1}, perm_pair = {0..T-1}.
+ */
+size_t moe_ffn_workspace_size(int format, int T, int k, int H, int I, int path);
+moe_status moe_expert_ffn_q4k(const void* slot_pool, size_t slot_stride, int S, int H, int I, const void* x,
+                              int x_dtype, int T, int k, const int32_t* slot_offsets, const int32_t* active_slots,
+                              const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype,
+                              int path, void* ws, size_t ws_bytes, void* stream);
+moe_status moe_expert_ffn_q8_0(const void* slot_pool, size_t slot_stride, int S, int H, int I, const void* x,
+                               int x_dtype, int T, int k, const int32_t* slot_offsets, const int32_t* active_slots,
+                               const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype,
+                               int path, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- combine
+ * y[t] = sum over j < k, in j order, of [slot_of_expert[id] >= 0] *
+ * topk_w[t,j] * y_pairs[t*k+j]  (+ y_shared[t] if y_shared is not NULL).
+ * Non-resident pairs contribute exactly 0 on the card; the host leg adds
+ * them (bloomery README of 2026-09-24: experts split between card and host).
+ *
+ * y_pairs   device, [T*k, H], y_pairs_dtype.
+ * topk_ids, topk_w, slot_of_expert (E entries): device, as above.
+ * y_shared  device, fp32 [T, H], or NULL.
+ * y         device, [T, H], y_dtype (MOE_F32 or MOE_BF16, round to nearest even).
+ * H % 8 == 0.  Accumulation in fp32.
+ */
+moe_status moe_combine(const void* y_pairs, int y_pairs_dtype, const int32_t* topk_ids, const float* topk_w,
+                       const int32_t* slot_of_expert, int E, const float* y_shared, int T, int k, int H, void* y,
+                       int y_dtype, void* stream);
+
+/* ------------------------------------------------------------ stage timers
+ * Diagnostics: hipEvent pairs recorded around every launch of one stage, on
+ * the launch's stream.  Not for use while a stream is being captured.
+ *   stage: 0 route, 1 batches, 2 ffn activation prep, 3 ffn gate/up,
+ *          4 ffn down, 5 combine, 6 prefill gate/up GEMM, 7 prefill down GEMM.
+ * moe_timer_begin arms the stage for up to `capacity` launches (events are
+ * created here, on the current device); moe_timer_end waits for the last
+ * recorded event, returns the summed kernel time in milliseconds and the
+ * number of launches timed, and releases the events.
+ */
+#define MOE_STAGE_COUNT 8
+moe_status moe_timer_begin(int stage, int capacity);
+moe_status moe_timer_end(int stage, double* total_ms, int* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMOE_H */

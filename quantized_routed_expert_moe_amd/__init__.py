@@ -1,0 +1,239 @@
+"""Python binding of libqmoe (include/qmoe.h): one routed-expert MoE layer on MI355X.
+
+Argument marshalling only: every function here has the name of a C entry
+point, checks that the tensors it is given are contiguous device tensors of
+the right dtype, and passes their addresses, the sizes and the current HIP
+stream to the library.  All compute runs in the library's HIP kernels.  If
+the library is not built the first call raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqmoe.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "qmoe.h")
+
+MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+MOE_F32, MOE_BF16 = 0, 1
+MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL = 0, 1, 2
+MOE_FMT_Q8_0, MOE_FMT_Q4K = 0, 1
+STAGES = ("route", "batches", "ffn_prep", "ffn_gateup", "ffn_down", "combine", "prefill_gateup", "prefill_down")
+
+
+class QmoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        super().__init__(f"{_status_name(status)}: {message}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, f32, vp, sz = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+        L.moe_status_name.argtypes = [i32]
+        L.moe_status_name.restype = ctypes.c_char_p
+        L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_route_topk.argtypes = [vp, i32, i32, i32, i32, i32, f32, vp, vp, vp]
+        L.moe_batches_workspace_size.argtypes = [i32, i32, i32, i32]
+        L.moe_batches_workspace_size.restype = sz
+        L.moe_build_expert_batches.argtypes = [vp, vp, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                               vp]
+        L.moe_expert_blob_bytes.argtypes = [i32, i32, i32]
+        L.moe_expert_blob_bytes.restype = sz
+        L.moe_pack_expert.argtypes = [i32, vp, vp, i32, i32]
+        L.moe_unpack_expert.argtypes = [i32, vp, vp, i32, i32]
+        L.moe_validate_slot_map.argtypes = [vp, i32, i32]
+        L.moe_ffn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+        L.moe_ffn_workspace_size.restype = sz
+        ffn = [vp, sz, i32, i32, i32, vp, i32, i32, i32, vp, vp, vp, vp, vp, i32, i32, vp, sz, vp]
+        L.moe_expert_ffn_q4k.argtypes = ffn
+        L.moe_expert_ffn_q8_0.argtypes = ffn
+        L.moe_combine.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, i32, i32, vp, i32, vp]
+        L.moe_timer_begin.argtypes = [i32, i32]
+        L.moe_timer_end.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
+        for name in ("moe_route_topk", "moe_build_expert_batches", "moe_pack_expert", "moe_unpack_expert",
+                     "moe_validate_slot_map", "moe_expert_ffn_q4k", "moe_expert_ffn_q8_0", "moe_combine",
+                     "moe_timer_begin", "moe_timer_end"):
+            getattr(L, name).restype = i32
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/qmoe.h declares."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def _status_name(st: int) -> str:
+    return lib().moe_status_name(st).decode()
+
+
+def _check(st: int) -> None:
+    if st != MOE_OK:
+        raise QmoeError(st, lib().moe_last_error().decode())
+
+
+# ------------------------------------------------------------ marshalling
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t, dtypes=None, name="tensor") -> int:
+    if t is None:
+        return 0
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _i32():
+    import torch
+    return (torch.int32,)
+
+
+def _f32():
+    import torch
+    return (torch.float32,)
+
+
+def _fb():
+    import torch
+    return (torch.float32, torch.bfloat16)
+
+
+# ------------------------------------------------------------------ calls
+
+def moe_route_topk(logits, k: int, score: int, renormalize: bool, scale: float, topk_ids, topk_w, stream=None):
+    T, E = logits.shape
+    _check(lib().moe_route_topk(_dev(logits, _f32(), "logits"), T, E, k, score, int(bool(renormalize)), float(scale),
+                                _dev(topk_ids, _i32(), "topk_ids"), _dev(topk_w, _f32(), "topk_w"),
+                                _stream(stream)))
+
+
+def moe_batches_workspace_size(T: int, k: int, E: int, S: int) -> int:
+    return int(lib().moe_batches_workspace_size(T, k, E, S))
+
+
+def moe_build_expert_batches(topk_ids, topk_w, E: int, slot_of_expert, S: int, slot_offsets, active_slots, num_active,
+                             perm_pair, host_token, host_expert, host_weight, host_count, ws=None, stream=None):
+    T, k = topk_ids.shape
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().moe_build_expert_batches(
+        _dev(topk_ids, _i32(), "topk_ids"), _dev(topk_w, _f32(), "topk_w"), T, k, E,
+        _dev(slot_of_expert, _i32(), "slot_of_expert"), S, _dev(slot_offsets, _i32(), "slot_offsets"),
+        _dev(active_slots, _i32(), "active_slots"), _dev(num_active, _i32(), "num_active"),
+        _dev(perm_pair, _i32(), "perm_pair"), _dev(host_token, _i32(), "host_token"),
+        _dev(host_expert, _i32(), "host_expert"), _dev(host_weight, _f32(), "host_weight"),
+        _dev(host_count, _i32(), "host_count"), _dev(ws, None, "ws"), ws_bytes, _stream(stream)))
+
+
+def moe_expert_blob_bytes(fmt: int, H: int, I: int) -> int:
+    return int(lib().moe_expert_blob_bytes(fmt, H, I))
+
+
+def moe_pack_expert(fmt: int, canonical: np.ndarray, H: int, I: int, out: np.ndarray | None = None) -> np.ndarray:
+    n = moe_expert_blob_bytes(fmt, H, I)
+    canonical = np.ascontiguousarray(canonical, dtype=np.uint8)
+    if canonical.nbytes != n:
+        raise ValueError(f"canonical blob has {canonical.nbytes} bytes, expected {n}")
+    if out is None:
+        out = np.empty(n, dtype=np.uint8)
+    _check(lib().moe_pack_expert(fmt, canonical.ctypes.data, out.ctypes.data, H, I))
+    return out
+
+
+def moe_unpack_expert(fmt: int, packed: np.ndarray, H: int, I: int) -> np.ndarray:
+    n = moe_expert_blob_bytes(fmt, H, I)
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    if packed.nbytes != n:
+        raise ValueError(f"packed blob has {packed.nbytes} bytes, expected {n}")
+    out = np.empty(n, dtype=np.uint8)
+    _check(lib().moe_unpack_expert(fmt, packed.ctypes.data, out.ctypes.data, H, I))
+    return out
+
+
+def moe_validate_slot_map(slot_of_expert: np.ndarray, S: int) -> None:
+    soe = np.ascontiguousarray(slot_of_expert, dtype=np.int32)
+    _check(lib().moe_validate_slot_map(soe.ctypes.data, soe.size, S))
+
+
+def moe_ffn_workspace_size(fmt: int, T: int, k: int, H: int, I: int, path: int) -> int:
+    return int(lib().moe_ffn_workspace_size(fmt, T, k, H, I, path))
+
+
+def _ffn(fn, slot_pool, slot_stride: int, S: int, H: int, I: int, x, k: int, slot_offsets, active_slots, num_active,
+         perm_pair, y_pairs, path: int, ws, stream):
+    T = x.shape[0]
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    pool_ptr = slot_pool if isinstance(slot_pool, int) else _dev(slot_pool, None, "slot_pool")
+    _check(fn(pool_ptr, slot_stride, S, H, I, _dev(x, _fb(), "x"), _dtype_code(x), T, k,
+              _dev(slot_offsets, _i32(), "slot_offsets"), _dev(active_slots, _i32(), "active_slots"),
+              _dev(num_active, _i32(), "num_active"), _dev(perm_pair, _i32(), "perm_pair"),
+              _dev(y_pairs, _fb(), "y_pairs"), _dtype_code(y_pairs), path, _dev(ws, None, "ws"), ws_bytes,
+              _stream(stream)))
+
+
+def moe_expert_ffn_q4k(slot_pool, slot_stride, S, H, I, x, k, slot_offsets, active_slots, num_active, perm_pair,
+                       y_pairs, path=MOE_PATH_AUTO, ws=None, stream=None):
+    _ffn(lib().moe_expert_ffn_q4k, slot_pool, slot_stride, S, H, I, x, k, slot_offsets, active_slots, num_active,
+         perm_pair, y_pairs, path, ws, stream)
+
+
+def moe_expert_ffn_q8_0(slot_pool, slot_stride, S, H, I, x, k, slot_offsets, active_slots, num_active, perm_pair,
+                        y_pairs, path=MOE_PATH_AUTO, ws=None, stream=None):
+    _ffn(lib().moe_expert_ffn_q8_0, slot_pool, slot_stride, S, H, I, x, k, slot_offsets, active_slots, num_active,
+         perm_pair, y_pairs, path, ws, stream)
+
+
+def moe_combine(y_pairs, topk_ids, topk_w, slot_of_expert, y_shared, y, stream=None):
+    T, k = topk_ids.shape
+    H = y.shape[1]
+    E = slot_of_expert.numel()
+    _check(lib().moe_combine(_dev(y_pairs, _fb(), "y_pairs"), _dtype_code(y_pairs), _dev(topk_ids, _i32(), "topk_ids"),
+                             _dev(topk_w, _f32(), "topk_w"), _dev(slot_of_expert, _i32(), "slot_of_expert"), E,
+                             _dev(y_shared, _f32(), "y_shared"), T, k, H, _dev(y, _fb(), "y"), _dtype_code(y),
+                             _stream(stream)))
+
+
+def moe_timer_begin(stage: int, capacity: int) -> None:
+    _check(lib().moe_timer_begin(stage, capacity))
+
+
+def moe_timer_end(stage: int) -> tuple[float, int]:
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int(0)
+    _check(lib().moe_timer_end(stage, ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

@@ -1,0 +1,494 @@
+// C ABI of the qmoe library: argument checks, named statuses, packing of
+// expert blobs, stage timers and dispatch to the HIP launchers.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "qmoe.h"
+#include "qmoe_internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return st;
+}
+
+moe_status hip_fail(hipError_t e, const char* what) {
+    return fail(MOE_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr long long kMaxPairs = 1ll << 24;
+
+moe_status check_route_shape(int T, int E, int k) {
+    if (T < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "T = %d must be >= 0", T);
+    if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_ERR_INVALID_ARGUMENT, "E = %d outside 1..%d", E, MOE_MAX_EXPERTS);
+    if (k < 1 || k > E || k > MOE_MAX_TOPK)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "k = %d outside 1..min(E=%d, %d)", k, E, MOE_MAX_TOPK);
+    if ((long long)T * k > kMaxPairs) return fail(MOE_ERR_INVALID_ARGUMENT, "T*k = %lld exceeds 2^24", (long long)T * k);
+    return MOE_OK;
+}
+
+moe_status check_shape(int format, int H, int I) {
+    if (format != MOE_FMT_Q8_0 && format != MOE_FMT_Q4K)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "format = %d is not MOE_FMT_Q8_0 or MOE_FMT_Q4K", format);
+    const int m = format == MOE_FMT_Q4K ? 256 : 128;
+    if (H <= 0 || I <= 0) return fail(MOE_ERR_INVALID_ARGUMENT, "H = %d, I = %d must be positive", H, I);
+    if (H % m || I % m)
+        return fail(MOE_ERR_UNSUPPORTED, "%s needs H and I multiples of %d (H = %d, I = %d)",
+                    format == MOE_FMT_Q4K ? "Q4_K" : "Q8_0", m, H, I);
+    if ((long long)H * I > (1ll << 31))
+        return fail(MOE_ERR_UNSUPPORTED, "H*I = %lld too large", (long long)H * I);
+    return MOE_OK;
+}
+
+size_t blob_bytes(int format, int H, int I) {
+    const size_t w = (size_t)H * I;  // weights per matrix
+    return format == MOE_FMT_Q4K ? 3 * w / 256 * 144 : 3 * w / 32 * 34;
+}
+
+int resolve_path(int format, int T, int path) {
+    if (path != MOE_PATH_AUTO) return path;
+    return (format == MOE_FMT_Q4K && T > 32) ? MOE_PATH_PREFILL : MOE_PATH_DECODE;
+}
+
+// ------------------------------------------------------------------ timers
+struct StageTimer {
+    std::atomic<int> armed{0};
+    int capacity = 0;
+    int used = 0;
+    std::vector<hipEvent_t> start, stop;
+};
+StageTimer g_timer[qmoe::kStageCount];
+std::mutex g_timer_mu;
+
+// ------------------------------------------------------------------ packing
+// Q4_K: the 32 quants of sub-block j of a canonical super-block.
+void q4k_subblock(const uint8_t* blk, int j, uint8_t* q) {
+    const uint8_t* qs = blk + 16 + (j / 2) * 32;
+    for (int l = 0; l < 32; ++l) q[l] = (j % 2 == 0) ? (qs[l] & 15) : (qs[l] >> 4);
+}
+void q4k_set_subblock(uint8_t* blk, int j, const uint8_t* q) {
+    uint8_t* qs = blk + 16 + (j / 2) * 32;
+    for (int l = 0; l < 32; ++l) {
+        if (j % 2 == 0) qs[l] = (uint8_t)((qs[l] & 0xF0) | q[l]);
+        else qs[l] = (uint8_t)((qs[l] & 0x0F) | (q[l] << 4));
+    }
+}
+// 32 quants -> 16 packed bytes: element 8d+n in nibble n of little-endian dword d.
+void nibbles_pack(const uint8_t* q, uint8_t* dst) {
+    for (int d = 0; d < 4; ++d) {
+        uint32_t w = 0;
+        for (int n = 0; n < 8; ++n) w |= (uint32_t)(q[8 * d + n] & 15) << (4 * n);
+        memcpy(dst + 4 * d, &w, 4);
+    }
+}
+void nibbles_unpack(const uint8_t* src, uint8_t* q) {
+    for (int d = 0; d < 4; ++d) {
+        uint32_t w;
+        memcpy(&w, src + 4 * d, 4);
+        for (int n = 0; n < 8; ++n) q[8 * d + n] = (uint8_t)((w >> (4 * n)) & 15);
+    }
+}
+
+// Move every field of a blob between the canonical and the packed layout
+// (PACK: canonical -> packed; otherwise packed -> canonical).
+template <bool PACK>
+void q4k_walk(const uint8_t* in, uint8_t* out, int H, int I) {
+    const size_t rbH = (size_t)H / 256 * 144, rbI = (size_t)I / 256 * 144;
+    const size_t gbytes = (size_t)I * rbH;
+    const int SBH = H / 256, SBI = I / 256;
+    uint8_t q[32];
+    // gate/up section
+    for (int rg = 0; rg < I / 64; ++rg)
+        for (int sb = 0; sb < SBH; ++sb) {
+            const size_t tile = ((size_t)rg * SBH + sb) * qmoe::kQ4kGateUpTile;
+            for (int r = 0; r < 64; ++r) {
+                const size_t row = (size_t)rg * 64 + r;
+                for (int mat = 0; mat < 2; ++mat) {
+                    const size_t canon = mat * gbytes + row * rbH + (size_t)sb * 144;
+                    const size_t hdr = tile + mat * 1024 + r * 16;
+                    if (PACK) {
+                        memcpy(out + hdr, in + canon, 16);
+                        for (int j = 0; j < 8; ++j) {
+                            q4k_subblock(in + canon, j, q);
+                            nibbles_pack(q, out + tile + 2048 + j * 2048 + mat * 1024 + r * 16);
+                        }
+                    } else {
+                        memcpy(out + canon, in + hdr, 16);
+                        for (int j = 0; j < 8; ++j) {
+                            nibbles_unpack(in + tile + 2048 + j * 2048 + mat * 1024 + r * 16, q);
+                            q4k_set_subblock(out + canon, j, q);
+                        }
+                    }
+                }
+            }
+        }
+    // down section
+    const size_t base = qmoe::q4k_gateup_bytes(H, I);
+    for (int rg = 0; rg < H / 64; ++rg)
+        for (int sb = 0; sb < SBI; ++sb) {
+            const size_t tile = base + ((size_t)rg * SBI + sb) * qmoe::kQ4kDownTile;
+            for (int r = 0; r < 64; ++r) {
+                const size_t row = (size_t)rg * 64 + r;
+                const size_t canon = 2 * gbytes + row * rbI + (size_t)sb * 144;
+                if (PACK) {
+                    memcpy(out + tile + r * 16, in + canon, 16);
+                    for (int j = 0; j < 8; ++j) {
+                        q4k_subblock(in + canon, j, q);
+                        nibbles_pack(q, out + tile + 1024 + j * 1024 + r * 16);
+                    }
+                } else {
+                    memcpy(out + canon, in + tile + r * 16, 16);
+                    for (int j = 0; j < 8; ++j) {
+                        nibbles_unpack(in + tile + 1024 + j * 1024 + r * 16, q);
+                        q4k_set_subblock(out + canon, j, q);
+                    }
+                }
+            }
+        }
+}
+
+template <bool PACK>
+void q8_walk(const uint8_t* in, uint8_t* out, int H, int I) {
+    const size_t rbH = (size_t)H / 32 * 34, rbI = (size_t)I / 32 * 34;
+    const size_t gbytes = (size_t)I * rbH;
+    const int BH = H / 128, BI = I / 128;
+    // one 34-byte block <-> (2-byte scale, two 16-byte halves), quants offset by 128
+    auto move = [](const uint8_t* src_blk, uint8_t* scale, uint8_t* lo, uint8_t* hi, uint8_t* dst_blk, bool pack) {
+        if (pack) {
+            memcpy(scale, src_blk, 2);
+            for (int e = 0; e < 16; ++e) lo[e] = src_blk[2 + e] ^ 0x80;
+            for (int e = 0; e < 16; ++e) hi[e] = src_blk[18 + e] ^ 0x80;
+        } else {
+            memcpy(dst_blk, scale, 2);
+            for (int e = 0; e < 16; ++e) dst_blk[2 + e] = lo[e] ^ 0x80;
+            for (int e = 0; e < 16; ++e) dst_blk[18 + e] = hi[e] ^ 0x80;
+        }
+    };
+    for (int rg = 0; rg < I / 64; ++rg)
+        for (int bg = 0; bg < BH; ++bg) {
+            const size_t tile = ((size_t)rg * BH + bg) * qmoe::kQ8GateUpTile;
+            for (int r = 0; r < 64; ++r) {
+                const size_t row = (size_t)rg * 64 + r;
+                for (int mat = 0; mat < 2; ++mat)
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const size_t canon = mat * gbytes + row * rbH + (size_t)(bg * 4 + jj) * 34;
+                        uint8_t* sc = (PACK ? out : const_cast<uint8_t*>(in)) + tile + mat * 512 + r * 8 + jj * 2;
+                        uint8_t* lo =
+                            (PACK ? out : const_cast<uint8_t*>(in)) + tile + 1024 + mat * 2048 + jj * 4096 + r * 16;
+                        uint8_t* hi = lo + 1024;
+                        if (PACK) move(in + canon, sc, lo, hi, nullptr, true);
+                        else move(nullptr, sc, lo, hi, out + canon, false);
+                    }
+            }
+        }
+    const size_t base = qmoe::q8_gateup_bytes(H, I);
+    for (int rg = 0; rg < H / 64; ++rg)
+        for (int bg = 0; bg < BI; ++bg) {
+            const size_t tile = base + ((size_t)rg * BI + bg) * qmoe::kQ8DownTile;
+            for (int r = 0; r < 64; ++r) {
+                const size_t row = (size_t)rg * 64 + r;
+                for (int jj = 0; jj < 4; ++jj) {
+                    const size_t canon = 2 * gbytes + row * rbI + (size_t)(bg * 4 + jj) * 34;
+                    uint8_t* sc = (PACK ? out : const_cast<uint8_t*>(in)) + tile + r * 8 + jj * 2;
+                    uint8_t* lo = (PACK ? out : const_cast<uint8_t*>(in)) + tile + 512 + jj * 2048 + r * 16;
+                    uint8_t* hi = lo + 1024;
+                    if (PACK) move(in + canon, sc, lo, hi, nullptr, true);
+                    else move(nullptr, sc, lo, hi, out + canon, false);
+                }
+            }
+        }
+}
+
+moe_status ffn_common(int format, const void* slot_pool, size_t slot_stride, int S, int H, int I, const void* x,
+                      int x_dtype, int T, int k, const int32_t* slot_offsets, const int32_t* active_slots,
+                      const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype, int path,
+                      void* ws, size_t ws_bytes, void* stream) {
+    moe_status st = check_shape(format, H, I);
+    if (st != MOE_OK) return st;
+    if (S < 1 || S > MOE_MAX_EXPERTS) return fail(MOE_ERR_INVALID_ARGUMENT, "S = %d outside 1..%d", S, MOE_MAX_EXPERTS);
+    if (T < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "T = %d must be >= 0", T);
+    if (k < 1 || k > MOE_MAX_TOPK) return fail(MOE_ERR_INVALID_ARGUMENT, "k = %d outside 1..%d", k, MOE_MAX_TOPK);
+    if ((long long)T * k > kMaxPairs) return fail(MOE_ERR_INVALID_ARGUMENT, "T*k exceeds 2^24");
+    if (!slot_pool || !x || !slot_offsets || !active_slots || !num_active || !perm_pair || !y_pairs)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+    if (!aligned16(slot_pool) || (slot_stride & 15u))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "slot_pool and slot_stride must be 16-byte aligned");
+    if (slot_stride < blob_bytes(format, H, I))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "slot_stride %zu is smaller than the blob (%zu bytes)", slot_stride,
+                    blob_bytes(format, H, I));
+    if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARGUMENT, "bad x_dtype %d", x_dtype);
+    if (y_dtype != MOE_F32 && y_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARGUMENT, "bad y_dtype %d", y_dtype);
+    if (path < MOE_PATH_AUTO || path > MOE_PATH_PREFILL) return fail(MOE_ERR_INVALID_ARGUMENT, "bad path %d", path);
+    if (!aligned16(x) || !aligned16(y_pairs)) return fail(MOE_ERR_INVALID_ARGUMENT, "x and y_pairs must be 16-byte aligned");
+    const int p = resolve_path(format, T, path);
+    size_t need;
+    if (p == MOE_PATH_DECODE) {
+        if (y_dtype != MOE_F32) return fail(MOE_ERR_UNSUPPORTED, "the decode path writes MOE_F32 y_pairs");
+        need = qmoe::decode_workspace_bytes(T, k, H, I);
+    } else {
+        if (format != MOE_FMT_Q4K) return fail(MOE_ERR_UNSUPPORTED, "the prefill path is implemented for Q4_K only");
+        return fail(MOE_ERR_UNSUPPORTED, "the prefill path is not built in this library");
+        if (x_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the prefill path takes MOE_BF16 x");
+        need = qmoe::prefill_workspace_bytes(T, k, H, I);
+    }
+    if (ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, %zu needed", ws_bytes, need);
+    if (need > 0 && !ws) return fail(MOE_ERR_INVALID_ARGUMENT, "workspace pointer is NULL");
+    if (need > 0 && !aligned16(ws)) return fail(MOE_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+    if (T == 0) return MOE_OK;
+
+    qmoe::FfnArgs a{format, static_cast<const uint8_t*>(slot_pool), slot_stride, S, H, I, x, x_dtype, T, k,
+                    slot_offsets, active_slots, num_active, perm_pair, y_pairs, y_dtype, ws};
+    hipError_t e = p == MOE_PATH_DECODE ? qmoe::launch_ffn_decode(a, (hipStream_t)stream)
+                                        : qmoe::launch_ffn_prefill_q4k(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "expert FFN launch");
+    return MOE_OK;
+}
+
+}  // namespace
+
+namespace qmoe {
+
+void timer_before(int stage, hipStream_t s) {
+    StageTimer& t = g_timer[stage];
+    if (!t.armed.load(std::memory_order_relaxed)) return;
+    std::lock_guard<std::mutex> lk(g_timer_mu);
+    if (t.used < t.capacity) hipEventRecord(t.start[t.used], s);
+}
+
+void timer_after(int stage, hipStream_t s) {
+    StageTimer& t = g_timer[stage];
+    if (!t.armed.load(std::memory_order_relaxed)) return;
+    std::lock_guard<std::mutex> lk(g_timer_mu);
+    if (t.used < t.capacity) {
+        hipEventRecord(t.stop[t.used], s);
+        ++t.used;
+    }
+}
+
+}  // namespace qmoe
+
+extern "C" {
+
+const char* moe_status_name(int status) {
+    switch (status) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+        case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP";
+        default: return "MOE_STATUS_UNKNOWN";
+    }
+}
+
+const char* moe_last_error(void) { return g_error.c_str(); }
+
+moe_status moe_route_topk(const float* logits, int T, int E, int k, int score, int renormalize, float scale,
+                          int32_t* topk_ids, float* topk_w, void* stream) {
+    moe_status st = check_route_shape(T, E, k);
+    if (st != MOE_OK) return st;
+    if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "score = %d is not softmax or sigmoid", score);
+    if (T > 0 && (!logits || !topk_ids || !topk_w)) return fail(MOE_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+    if (!(scale == scale)) return fail(MOE_ERR_INVALID_ARGUMENT, "scale is NaN");
+    hipError_t e = qmoe::launch_route_topk(logits, T, E, k, score, renormalize, scale, topk_ids, topk_w,
+                                           (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "route launch");
+    return MOE_OK;
+}
+
+size_t moe_batches_workspace_size(int T, int k, int E, int S) {
+    (void)T; (void)k; (void)E; (void)S;
+    return 0;
+}
+
+moe_status moe_build_expert_batches(const int32_t* topk_ids, const float* topk_w, int T, int k, int E,
+                                    const int32_t* slot_of_expert, int S, int32_t* slot_offsets,
+                                    int32_t* active_slots, int32_t* num_active, int32_t* perm_pair,
+                                    int32_t* host_token, int32_t* host_expert, float* host_weight,
+                                    int32_t* host_count, void* ws, size_t ws_bytes, void* stream) {
+    (void)ws;
+    moe_status st = check_route_shape(T, E, k);
+    if (st != MOE_OK) return st;
+    if (S < 0 || S > E) return fail(MOE_ERR_INVALID_ARGUMENT, "S = %d outside 0..E (%d)", S, E);
+    if (!slot_of_expert || !slot_offsets || !num_active || !host_count)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+    if (T > 0 && (!topk_ids || !topk_w || !perm_pair || !host_token || !host_expert || !host_weight ||
+                  (S > 0 && !active_slots)))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+    if (ws_bytes < moe_batches_workspace_size(T, k, E, S))
+        return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "batches workspace too small");
+    hipError_t e = qmoe::launch_batches(topk_ids, topk_w, T, k, E, slot_of_expert, S, slot_offsets, active_slots,
+                                        num_active, perm_pair, host_token, host_expert, host_weight, host_count,
+                                        (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "batches launch");
+    return MOE_OK;
+}
+
+size_t moe_expert_blob_bytes(int format, int H, int I) {
+    if (check_shape(format, H, I) != MOE_OK) return 0;
+    return blob_bytes(format, H, I);
+}
+
+moe_status moe_pack_expert(int format, const void* canonical, void* packed, int H, int I) {
+    moe_status st = check_shape(format, H, I);
+    if (st != MOE_OK) return st;
+    if (!canonical || !packed) return fail(MOE_ERR_INVALID_ARGUMENT, "NULL blob pointer");
+    const uint8_t* in = static_cast<const uint8_t*>(canonical);
+    uint8_t* out = static_cast<uint8_t*>(packed);
+    const size_t n = blob_bytes(format, H, I);
+    if (in < out + n && out < in + n) return fail(MOE_ERR_INVALID_ARGUMENT, "blobs overlap");
+    memset(out, 0, n);
+    if (format == MOE_FMT_Q4K) q4k_walk<true>(in, out, H, I);
+    else q8_walk<true>(in, out, H, I);
+    return MOE_OK;
+}
+
+moe_status moe_unpack_expert(int format, const void* packed, void* canonical, int H, int I) {
+    moe_status st = check_shape(format, H, I);
+    if (st != MOE_OK) return st;
+    if (!canonical || !packed) return fail(MOE_ERR_INVALID_ARGUMENT, "NULL blob pointer");
+    const uint8_t* in = static_cast<const uint8_t*>(packed);
+    uint8_t* out = static_cast<uint8_t*>(canonical);
+    const size_t n = blob_bytes(format, H, I);
+    if (in < out + n && out < in + n) return fail(MOE_ERR_INVALID_ARGUMENT, "blobs overlap");
+    memset(out, 0, n);
+    if (format == MOE_FMT_Q4K) q4k_walk<false>(in, out, H, I);
+    else q8_walk<false>(in, out, H, I);
+    return MOE_OK;
+}
+
+moe_status moe_validate_slot_map(const int32_t* slot_of_expert, int E, int S) {
+    if (!slot_of_expert) return fail(MOE_ERR_INVALID_ARGUMENT, "slot_of_expert is NULL");
+    if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_ERR_INVALID_ARGUMENT, "E = %d outside 1..%d", E, MOE_MAX_EXPERTS);
+    if (S < 0 || S > E) return fail(MOE_ERR_INVALID_ARGUMENT, "S = %d outside 0..E", S);
+    std::vector<int> owner(S, -1);
+    for (int e = 0; e < E; ++e) {
+        const int s = slot_of_expert[e];
+        if (s == -1) continue;
+        if (s < 0 || s >= S) return fail(MOE_ERR_INVALID_ARGUMENT, "expert %d maps to slot %d outside [0, %d)", e, s, S);
+        if (owner[s] >= 0) return fail(MOE_ERR_INVALID_ARGUMENT, "slot %d holds experts %d and %d", s, owner[s], e);
+        owner[s] = e;
+    }
+    return MOE_OK;
+}
+
+size_t moe_ffn_workspace_size(int format, int T, int k, int H, int I, int path) {
+    if (check_shape(format, H, I) != MOE_OK || T < 0 || k < 1 || k > MOE_MAX_TOPK) return 0;
+    const size_t dec = qmoe::decode_workspace_bytes(T, k, H, I);
+    if (format != MOE_FMT_Q4K || path == MOE_PATH_DECODE) return dec;
+    const size_t pre = qmoe::prefill_workspace_bytes(T, k, H, I);
+    if (path == MOE_PATH_PREFILL) return pre;
+    return std::max(dec, pre);
+}
+
+moe_status moe_expert_ffn_q4k(const void* slot_pool, size_t slot_stride, int S, int H, int I, const void* x,
+                              int x_dtype, int T, int k, const int32_t* slot_offsets, const int32_t* active_slots,
+                              const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype,
+                              int path, void* ws, size_t ws_bytes, void* stream) {
+    return ffn_common(MOE_FMT_Q4K, slot_pool, slot_stride, S, H, I, x, x_dtype, T, k, slot_offsets, active_slots,
+                      num_active, perm_pair, y_pairs, y_dtype, path, ws, ws_bytes, stream);
+}
+
+moe_status moe_expert_ffn_q8_0(const void* slot_pool, size_t slot_stride, int S, int H, int I, const void* x,
+                               int x_dtype, int T, int k, const int32_t* slot_offsets, const int32_t* active_slots,
+                               const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype,
+                               int path, void* ws, size_t ws_bytes, void* stream) {
+    return ffn_common(MOE_FMT_Q8_0, slot_pool, slot_stride, S, H, I, x, x_dtype, T, k, slot_offsets, active_slots,
+                      num_active, perm_pair, y_pairs, y_dtype, path, ws, ws_bytes, stream);
+}
+
+moe_status moe_combine(const void* y_pairs, int y_pairs_dtype, const int32_t* topk_ids, const float* topk_w,
+                       const int32_t* slot_of_expert, int E, const float* y_shared, int T, int k, int H, void* y,
+                       int y_dtype, void* stream) {
+    if (T < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "T = %d must be >= 0", T);
+    if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_ERR_INVALID_ARGUMENT, "E = %d outside 1..%d", E, MOE_MAX_EXPERTS);
+    if (k < 1 || k > MOE_MAX_TOPK) return fail(MOE_ERR_INVALID_ARGUMENT, "k = %d outside 1..%d", k, MOE_MAX_TOPK);
+    if (H <= 0 || H % 8) return fail(MOE_ERR_UNSUPPORTED, "H = %d must be a positive multiple of 8", H);
+    if ((long long)T * k > kMaxPairs) return fail(MOE_ERR_INVALID_ARGUMENT, "T*k exceeds 2^24");
+    if (y_pairs_dtype != MOE_F32 && y_pairs_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARGUMENT, "bad y_pairs dtype");
+    if (y_dtype != MOE_F32 && y_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARGUMENT, "bad y dtype");
+    if (T > 0 && (!y_pairs || !topk_ids || !topk_w || !slot_of_expert || !y))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+    if (T > 0 && (!aligned16(y_pairs) || !aligned16(y) || (y_shared && !aligned16(y_shared))))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "y_pairs, y and y_shared must be 16-byte aligned");
+    hipError_t e = qmoe::launch_combine(y_pairs, y_pairs_dtype, topk_ids, topk_w, slot_of_expert, E, y_shared, T, k,
+                                        H, y, y_dtype, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+    return MOE_OK;
+}
+
+moe_status moe_timer_begin(int stage, int capacity) {
+    if (stage < 0 || stage >= qmoe::kStageCount) return fail(MOE_ERR_INVALID_ARGUMENT, "bad stage %d", stage);
+    if (capacity < 1 || capacity > (1 << 20)) return fail(MOE_ERR_INVALID_ARGUMENT, "bad capacity %d", capacity);
+    std::lock_guard<std::mutex> lk(g_timer_mu);
+    StageTimer& t = g_timer[stage];
+    if (t.armed.load()) return fail(MOE_ERR_INVALID_ARGUMENT, "stage %d timer already armed", stage);
+    t.start.assign(capacity, nullptr);
+    t.stop.assign(capacity, nullptr);
+    for (int i = 0; i < capacity; ++i) {
+        hipError_t e1 = hipEventCreate(&t.start[i]);
+        hipError_t e2 = hipEventCreate(&t.stop[i]);
+        if (e1 != hipSuccess || e2 != hipSuccess) {
+            for (int j = 0; j <= i; ++j) {
+                if (t.start[j]) hipEventDestroy(t.start[j]);
+                if (t.stop[j]) hipEventDestroy(t.stop[j]);
+            }
+            t.start.clear();
+            t.stop.clear();
+            return hip_fail(e1 != hipSuccess ? e1 : e2, "hipEventCreate");
+        }
+    }
+    t.capacity = capacity;
+    t.used = 0;
+    t.armed.store(1);
+    return MOE_OK;
+}
+
+moe_status moe_timer_end(int stage, double* total_ms, int* launches) {
+    if (stage < 0 || stage >= qmoe::kStageCount) return fail(MOE_ERR_INVALID_ARGUMENT, "bad stage %d", stage);
+    if (!total_ms || !launches) return fail(MOE_ERR_INVALID_ARGUMENT, "NULL output pointer");
+    std::lock_guard<std::mutex> lk(g_timer_mu);
+    StageTimer& t = g_timer[stage];
+    if (!t.armed.load()) return fail(MOE_ERR_INVALID_ARGUMENT, "stage %d timer not armed", stage);
+    t.armed.store(0);
+    double sum = 0.0;
+    hipError_t err = hipSuccess;
+    if (t.used > 0) err = hipEventSynchronize(t.stop[t.used - 1]);
+    for (int i = 0; i < t.used && err == hipSuccess; ++i) {
+        float ms = 0.f;
+        err = hipEventElapsedTime(&ms, t.start[i], t.stop[i]);
+        sum += ms;
+    }
+    for (int i = 0; i < t.capacity; ++i) {
+        hipEventDestroy(t.start[i]);
+        hipEventDestroy(t.stop[i]);
+    }
+    *total_ms = sum;
+    *launches = t.used;
+    t.start.clear();
+    t.stop.clear();
+    t.capacity = t.used = 0;
+    if (err != hipSuccess) return hip_fail(err, "stage timer");
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,155 @@
+// Token -> slot grouping: histogram, exclusive scan and a stable scatter
+// ("each expert over all its tokens at once": bloomery V4.1 README, "Batched
+// prompts"; pairs whose expert is not on the card go to the host tier:
+// bloomery README of 2026-09-24, opening list).
+//
+// One workgroup of 8 waves.  Bucket b of pair p is its slot, or S for "not
+// resident".  Wave w owns a contiguous run of pairs, walked in 64-pair steps.
+// Inside a step, lanes with equal buckets are found with one ballot per
+// bucket bit (a deterministic match), which gives each lane its rank among
+// the earlier lanes of its bucket without atomics.  Pass A counts per wave
+// and bucket; the counts are turned into per-wave starting positions
+// (exclusive over waves, then over buckets); pass B places every pair at
+// start + running count + rank.  Every output is therefore a pure function of
+// the inputs: stable in p and identical from run to run.
+#include "device_common.h"
+#include "qmoe_internal.h"
+
+namespace qmoe {
+
+constexpr int kBatchWaves = 8;
+
+__device__ __forceinline__ int bucket_of(const int32_t* __restrict__ ids, const int32_t* __restrict__ soe, int p,
+                                         int E, int S) {
+    const int id = ids[p];
+    const int s = (id >= 0 && id < E) ? soe[id] : -1;
+    return (s >= 0 && s < S) ? s : S;
+}
+
+// Lanes (among `valid`) whose bucket equals this lane's.
+__device__ __forceinline__ unsigned long long match_bucket(int b, bool valid, int nbits) {
+    unsigned long long m = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+        const bool set = (b >> bit) & 1;
+        const unsigned long long bb = __ballot(set);
+        m &= set ? bb : ~bb;
+    }
+    return m;
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(v, off, 64);
+        if (lane >= off) v += t;
+    }
+    return v;
+}
+
+__global__ __launch_bounds__(512) void batches_kernel(const int32_t* __restrict__ ids, const float* __restrict__ w,
+                                                      int T, int k, int E, const int32_t* __restrict__ soe, int S,
+                                                      int nbits, int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ active, int32_t* __restrict__ num_active,
+                                                      int32_t* __restrict__ perm, int32_t* __restrict__ host_token,
+                                                      int32_t* __restrict__ host_expert,
+                                                      float* __restrict__ host_weight,
+                                                      int32_t* __restrict__ host_count) {
+    extern __shared__ int lds[];
+    const int NB = S + 1;
+    int* cnt = lds;                     // [kBatchWaves][NB]
+    int* start = lds + kBatchWaves * NB;  // [NB]
+    const int P = T * k;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const unsigned long long lt = (1ull << lane) - 1ull;
+
+    for (int i = tid; i < kBatchWaves * NB; i += blockDim.x) cnt[i] = 0;
+    __syncthreads();
+
+    const int chunk = (((P + kBatchWaves - 1) / kBatchWaves) + 63) / 64 * 64;
+    const int begin = min(P, wave * chunk), end = min(P, begin + chunk);
+
+    // Pass A: per-wave bucket counts.
+    for (int base = begin; base < end; base += 64) {
+        const int p = base + lane;
+        const bool valid = p < end;
+        const int b = valid ? bucket_of(ids, soe, p, E, S) : 0;
+        const unsigned long long m = match_bucket(b, valid, nbits);
+        if (valid && (m & lt) == 0ull) cnt[wave * NB + b] += __popcll(m);
+    }
+    __syncthreads();
+
+    // Per bucket: exclusive prefix over waves; totals into start[].
+    for (int b = tid; b < NB; b += blockDim.x) {
+        int run = 0;
+        for (int wv = 0; wv < kBatchWaves; ++wv) {
+            const int c = cnt[wv * NB + b];
+            cnt[wv * NB + b] = run;
+            run += c;
+        }
+        start[b] = run;
+    }
+    __syncthreads();
+
+    // Exclusive prefix over slots (wave 0): slot offsets and the active list.
+    if (wave == 0) {
+        int carry = 0, acarry = 0;
+        for (int c0 = 0; c0 < S; c0 += 64) {
+            const int b = c0 + lane;
+            const int c = b < S ? start[b] : 0;
+            const int inc = wave_inclusive_scan(c, lane);
+            const int f = c > 0 ? 1 : 0;
+            const int finc = wave_inclusive_scan(f, lane);
+            if (b < S) {
+                offsets[b] = carry + inc - c;
+                start[b] = carry + inc - c;
+                if (f) active[acarry + finc - f] = b;
+            }
+            carry += __shfl(inc, 63, 64);
+            acarry += __shfl(finc, 63, 64);
+        }
+        if (lane == 0) {
+            offsets[S] = carry;
+            *num_active = acarry;
+            *host_count = start[S];
+            start[S] = 0;
+        }
+    }
+    __syncthreads();
+
+    // Pass B: stable scatter.
+    for (int base = begin; base < end; base += 64) {
+        const int p = base + lane;
+        const bool valid = p < end;
+        const int b = valid ? bucket_of(ids, soe, p, E, S) : 0;
+        const unsigned long long m = match_bucket(b, valid, nbits);
+        if (valid) {
+            const int pos = start[b] + cnt[wave * NB + b] + __popcll(m & lt);
+            if (b < S) {
+                perm[pos] = p;
+            } else {
+                host_token[pos] = p / k;
+                host_expert[pos] = ids[p];
+                host_weight[pos] = w[p];
+            }
+        }
+        // Every lane has read its running count above before a leader updates it
+        // (LDS operations of one wave complete in order).
+        if (valid && (m & lt) == 0ull) cnt[wave * NB + b] += __popcll(m);
+    }
+}
+
+hipError_t launch_batches(const int32_t* ids, const float* w, int T, int k, int E, const int32_t* soe, int S,
+                          int32_t* offsets, int32_t* active, int32_t* num_active, int32_t* perm,
+                          int32_t* host_token, int32_t* host_expert, float* host_weight, int32_t* host_count,
+                          hipStream_t s) {
+    int nbits = 1;
+    while ((1 << nbits) <= S) ++nbits;  // buckets 0..S
+    const size_t lds = (size_t)(kBatchWaves + 1) * (S + 1) * sizeof(int);
+    timer_before(kStageBatches, s);
+    hipLaunchKernelGGL(batches_kernel, dim3(1), dim3(64 * kBatchWaves), lds, s, ids, w, T, k, E, soe, S, nbits,
+                       offsets, active, num_active, perm, host_token, host_expert, host_weight, host_count);
+    timer_after(kStageBatches, s);
+    return hipGetLastError();
+}
+
+}  // namespace qmoe

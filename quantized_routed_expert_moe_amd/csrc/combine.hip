@@ -1,0 +1,75 @@
+// Weighted combine of the resident pairs plus the shared expert.  Non-resident
+// pairs add nothing on the card (their work is the host leg's: bloomery
+// README of 2026-09-24, opening list).  Summation in j order, fp32.
+#include "device_common.h"
+#include "qmoe_internal.h"
+
+namespace qmoe {
+
+__device__ __forceinline__ void load8(const void* base, int dtype, size_t idx, float* v) {
+    if (dtype == 0) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+        const float4 a = p[0], b = p[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = bf16_to_float(w[i] & 0xFFFFu);
+            v[2 * i + 1] = bf16_to_float(w[i] >> 16);
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ yp, int yp_dtype,
+                                                      const int32_t* __restrict__ ids, const float* __restrict__ w,
+                                                      const int32_t* __restrict__ soe, int E,
+                                                      const float* __restrict__ ysh, int T, int k, int H,
+                                                      void* __restrict__ y, int y_dtype) {
+    const int t = blockIdx.y;
+    const int h0 = (blockIdx.x * 256 + threadIdx.x) * 8;
+    if (h0 >= H) return;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+        const size_t p = (size_t)t * k + j;
+        const int id = ids[p];
+        if (id < 0 || id >= E || soe[id] < 0) continue;
+        const float wj = w[p];
+        float v[8];
+        load8(yp, yp_dtype, p * H + h0, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
+    }
+    if (ysh) {
+        float v[8];
+        load8(ysh, 0, (size_t)t * H + h0, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    if (y_dtype == 0) {
+        float4* o = reinterpret_cast<float4*>(static_cast<float*>(y) + (size_t)t * H + h0);
+        o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    } else {
+        uint32_t q[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = float_to_bf16_bits(acc[2 * i]) | (float_to_bf16_bits(acc[2 * i + 1]) << 16);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + (size_t)t * H + h0) = make_uint4(q[0], q[1], q[2], q[3]);
+    }
+}
+
+hipError_t launch_combine(const void* y_pairs, int yp_dtype, const int32_t* ids, const float* w,
+                          const int32_t* soe, int E, const float* y_shared, int T, int k, int H, void* y, int y_dtype,
+                          hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    dim3 grid((H / 8 + 255) / 256, T);
+    timer_before(kStageCombine, s);
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, y_pairs, yp_dtype, ids, w, soe, E, y_shared, T, k, H, y,
+                       y_dtype);
+    timer_after(kStageCombine, s);
+    return hipGetLastError();
+}
+
+}  // namespace qmoe

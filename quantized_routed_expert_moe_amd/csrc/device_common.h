@@ -1,0 +1,48 @@
+// Device helpers shared by the qmoe kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmoe {
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// fp32 += a.lo*b.lo + a.hi*b.hi on packed fp16 pairs (v_dot2_f32_f16).
+__device__ __forceinline__ float fdot2u(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, a), __builtin_bit_cast(half2v, b), c, false);
+}
+
+__device__ __forceinline__ float half_to_float(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits16 & 0xFFFFu));
+}
+
+// fp32 -> fp16 bits, round to nearest even (v_cvt_f16_f32).
+__device__ __forceinline__ uint32_t float_to_half_bits(float f) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+__device__ __forceinline__ float bf16_to_float(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
+    uint32_t x = __float_as_uint(f);
+    x += 0x7FFFu + ((x >> 16) & 1u);
+    return x >> 16;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Sum over each aligned group of 32 lanes (lanes 0-31 and 32-63 separately).
+__device__ __forceinline__ float half_wave_sum(float v) {
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+}  // namespace qmoe

@@ -1,0 +1,111 @@
+// Internal declarations of the qmoe HIP library: packed-blob layout,
+// kernel launchers and the stage timers.  Not part of the C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qmoe {
+
+// ----------------------------------------------------------------- layout
+//
+// Packed Q4_K blob (H, I multiples of 256).  Two sections of tiles, each
+// tile covering 64 consecutive output rows and one 256-wide super-block of
+// the input dimension:
+//
+//   gate/up section, tile (rg, sb), rg < I/64, sb < H/256, 18432 bytes at
+//   ((rg * H/256) + sb) * 18432:
+//     [0, 1024)         gate headers: row 64rg+r at 16r: d, dmin, 12 scale bytes
+//     [1024, 2048)      up headers, same order
+//     [2048 + 2048j, +1024)   gate quants of sub-block j: row r at 16r
+//     [3072 + 2048j, +1024)   up quants of sub-block j
+//   down section (after the gate/up section), tile (rg, sb), rg < H/64,
+//   sb < I/256, 9216 bytes at ((rg * I/256) + sb) * 9216:
+//     [0, 1024)         headers
+//     [1024 + 1024j, +1024)   quants of sub-block j
+//
+// The 16 quant bytes of one row and sub-block hold element e = 8d + n in
+// nibble n (bits 4n..4n+3) of little-endian dword d (d < 4, n < 8).
+//
+// Packed Q8_0 blob (H, I multiples of 128), tiles of 64 rows x 4 blocks:
+//   gate/up tile (rg, bg), bg < H/128, 17408 bytes:
+//     [0, 512)          gate scales: row r at 8r: fp16 d of blocks 4bg..4bg+3
+//     [512, 1024)       up scales
+//     [1024 + 4096jj, +2048)  gate quants of block jj: elements 0-15 of row r
+//                       at 16r, elements 16-31 of row r at 1024 + 16r
+//     [3072 + 4096jj, +2048)  up quants of block jj, same order
+//   down tile (rg, bg), bg < I/128, 8704 bytes:
+//     [0, 512) scales; [512 + 2048jj, +2048) quants of block jj
+// Q8_0 quant bytes are stored as q + 128 (q xor 0x80), element e at byte e.
+
+constexpr int kQ4kGateUpTile = 18432;
+constexpr int kQ4kDownTile = 9216;
+constexpr int kQ8GateUpTile = 17408;
+constexpr int kQ8DownTile = 8704;
+
+__host__ __device__ inline size_t q4k_gateup_bytes(int H, int I) { return (size_t)(I / 64) * (H / 256) * kQ4kGateUpTile; }
+__host__ __device__ inline size_t q8_gateup_bytes(int H, int I) { return (size_t)(I / 64) * (H / 128) * kQ8GateUpTile; }
+
+// Per-token activation records of the decode path, one per 32-element
+// block of the input dimension: 16 dwords of fp16 pairs laid out to match
+// the packed quants, then (C, S): C is the constant the magic-number nibble
+// or byte conversion adds to the dot product, S the fp32 block sum.
+struct ActRec;  // (documentation only; the buffers are plain uint32/float2 arrays)
+
+// ---------------------------------------------------------------- stages
+enum Stage {
+    kStageRoute = 0,
+    kStageBatches = 1,
+    kStagePrep = 2,
+    kStageGateUp = 3,
+    kStageDown = 4,
+    kStageCombine = 5,
+    kStagePrefillGateUp = 6,
+    kStagePrefillDown = 7,
+    kStageCount = 8
+};
+
+// Record the start / stop event of a launch of `stage` if its timer is armed.
+void timer_before(int stage, hipStream_t s);
+void timer_after(int stage, hipStream_t s);
+
+// --------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.  Arguments are checked by the
+// ABI layer before these run.
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int score, int renormalize, float scale,
+                             int32_t* ids, float* w, hipStream_t s);
+
+hipError_t launch_batches(const int32_t* ids, const float* w, int T, int k, int E, const int32_t* slot_of_expert,
+                          int S, int32_t* slot_offsets, int32_t* active_slots, int32_t* num_active,
+                          int32_t* perm_pair, int32_t* host_token, int32_t* host_expert, float* host_weight,
+                          int32_t* host_count, hipStream_t s);
+
+struct FfnArgs {
+    int format;  // 0 Q8_0, 1 Q4_K
+    const uint8_t* pool;
+    size_t stride;
+    int S, H, I;
+    const void* x;
+    int x_dtype;
+    int T, k;
+    const int32_t* slot_offsets;
+    const int32_t* active_slots;
+    const int32_t* num_active;
+    const int32_t* perm_pair;
+    void* y_pairs;
+    int y_dtype;
+    void* ws;
+};
+
+size_t decode_workspace_bytes(int T, int k, int H, int I);
+hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s);
+
+size_t prefill_workspace_bytes(int T, int k, int H, int I);
+hipError_t launch_ffn_prefill_q4k(const FfnArgs& a, hipStream_t s);
+
+hipError_t launch_combine(const void* y_pairs, int yp_dtype, const int32_t* ids, const float* w,
+                          const int32_t* slot_of_expert, int E, const float* y_shared, int T, int k, int H, void* y,
+                          int y_dtype, hipStream_t s);
+
+}  // namespace qmoe

@@ -1,0 +1,119 @@
+// Top-k routing from gate logits (bloomery README of 2026-09-24, "Oracle
+// sets against ik_llama.cpp": router top-k ids exact outside tie bands; its
+// reference list names the router core).
+//
+// One wave64 per token row.  Each lane keeps E/64 logits in registers; k
+// rounds of a wave-wide arg-max (butterfly shuffles on the key (logit desc,
+// id asc)) pick the experts in rank order, lane j keeping pick j.  Weights
+// are then formed from the k picks in fp32 (softmax renormalised over the
+// picks equals the full softmax renormalised; the full denominator is only
+// needed when renormalisation is off).
+#include <climits>
+
+#include "device_common.h"
+#include "qmoe_internal.h"
+
+namespace qmoe {
+
+// Is (va, ia) ranked before (vb, ib)?  ib == INT_MAX marks "no candidate".
+__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
+    if (ia == INT_MAX) return false;
+    if (ib == INT_MAX) return true;
+    return va > vb || (va == vb && ia < ib);
+}
+
+template <int PER_LANE>
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                         int score, int renormalize, float scale,
+                                                         int32_t* __restrict__ ids, float* __restrict__ w) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= T) return;  // whole wave
+    const float* l = logits + (size_t)row * E;
+
+    float v[PER_LANE];
+    bool avail[PER_LANE];
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) {
+        const int e = lane + 64 * i;
+        avail[i] = e < E;
+        v[i] = avail[i] ? l[e] : 0.0f;
+    }
+
+    float pick_v = 0.0f;
+    int pick_id = 0;
+    for (int r = 0; r < k; ++r) {
+        float bv = 0.0f;
+        int bi = INT_MAX;
+#pragma unroll
+        for (int i = 0; i < PER_LANE; ++i) {
+            const int e = lane + 64 * i;
+            if (avail[i] && better(v[i], e, bv, bi)) {
+                bv = v[i];
+                bi = e;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const float ov = __shfl_xor(bv, off, 64);
+            const int oi = __shfl_xor(bi, off, 64);
+            if (better(ov, oi, bv, bi)) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        if (lane == r) {
+            pick_v = bv;
+            pick_id = bi;
+        }
+#pragma unroll
+        for (int i = 0; i < PER_LANE; ++i)
+            if (lane + 64 * i == bi) avail[i] = false;
+    }
+
+    float p;
+    if (score == 0) {
+        const float mx = __shfl(pick_v, 0, 64);
+        const float e_r = lane < k ? expf(pick_v - mx) : 0.0f;
+        float z;
+        if (renormalize) {
+            z = wave_sum(e_r);
+        } else {
+            float zl = 0.0f;
+#pragma unroll
+            for (int i = 0; i < PER_LANE; ++i)
+                if (lane + 64 * i < E) zl += expf(v[i] - mx);
+            z = wave_sum(zl);
+        }
+        p = e_r / z;
+    } else {
+        const float s_r = lane < k ? 1.0f / (1.0f + expf(-pick_v)) : 0.0f;
+        p = renormalize ? s_r / wave_sum(s_r) : s_r;
+    }
+    if (lane < k) {
+        ids[(size_t)row * k + lane] = pick_id;
+        w[(size_t)row * k + lane] = scale * p;
+    }
+}
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int score, int renormalize, float scale,
+                             int32_t* ids, float* w, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    dim3 grid((T + 3) / 4), block(256);
+    timer_before(kStageRoute, s);
+    if (E <= 64)
+        hipLaunchKernelGGL(route_topk_kernel<1>, grid, block, 0, s, logits, T, E, k, score, renormalize, scale, ids, w);
+    else if (E <= 128)
+        hipLaunchKernelGGL(route_topk_kernel<2>, grid, block, 0, s, logits, T, E, k, score, renormalize, scale, ids, w);
+    else if (E <= 256)
+        hipLaunchKernelGGL(route_topk_kernel<4>, grid, block, 0, s, logits, T, E, k, score, renormalize, scale, ids, w);
+    else if (E <= 512)
+        hipLaunchKernelGGL(route_topk_kernel<8>, grid, block, 0, s, logits, T, E, k, score, renormalize, scale, ids, w);
+    else
+        hipLaunchKernelGGL(route_topk_kernel<16>, grid, block, 0, s, logits, T, E, k, score, renormalize, scale, ids,
+                           w);
+    timer_after(kStageRoute, s);
+    return hipGetLastError();
+}
+
+}  // namespace qmoe

@@ -1,0 +1,100 @@
+"""One MoE layer as the sequence of the five library calls, with its buffers.
+
+Orchestration only: device buffers come from torch, every step is a call
+into libqmoe.  The optional shared expert runs through moe_expert_ffn_q8_0
+with a one-slot identity batch.  All work is enqueued on one stream, without
+host synchronisation, so `forward` can be captured into a HIP graph.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import (MOE_FMT_Q4K, MOE_FMT_Q8_0, MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL, moe_batches_workspace_size,
+               moe_build_expert_batches, moe_combine, moe_expert_blob_bytes, moe_expert_ffn_q4k,
+               moe_expert_ffn_q8_0, moe_ffn_workspace_size, moe_pack_expert, moe_route_topk)
+
+
+def upload_packed_experts(fmt: int, canonical_blobs: np.ndarray, H: int, I: int, stride: int | None = None,
+                          device="cuda") -> tuple[torch.Tensor, int]:
+    """Pack canonical blobs [n, bytes] on the host and upload them as a slot pool [n, stride] (uint8)."""
+    n_bytes = moe_expert_blob_bytes(fmt, H, I)
+    stride = stride or (n_bytes + 255) // 256 * 256
+    n = canonical_blobs.shape[0]
+    host = np.zeros((n, stride), dtype=np.uint8)
+    for s in range(n):
+        moe_pack_expert(fmt, canonical_blobs[s], H, I, out=host[s, :n_bytes])
+    return torch.from_numpy(host).to(device), stride
+
+
+@dataclass
+class LayerSpec:
+    fmt: int
+    H: int
+    I: int
+    E: int
+    k: int
+    score: int = 0
+    renormalize: bool = True
+    scale: float = 1.0
+    I_shared: int = 0  # 0 = no shared expert
+
+
+class MoELayer:
+    def __init__(self, spec: LayerSpec, T_max: int, S: int, slot_pool: torch.Tensor, stride: int,
+                 slot_of_expert: torch.Tensor, shared_pool: torch.Tensor | None = None,
+                 path: int = MOE_PATH_AUTO, y_dtype=torch.float32, pair_dtype=torch.float32, device="cuda"):
+        self.spec, self.T_max, self.S, self.path = spec, T_max, S, path
+        self.slot_pool, self.stride, self.slot_of_expert = slot_pool, stride, slot_of_expert
+        self.shared_pool = shared_pool
+        k, H, E = spec.k, spec.H, spec.E
+        P = T_max * k
+        i32 = dict(dtype=torch.int32, device=device)
+        self.ids = torch.zeros((T_max, k), **i32)
+        self.w = torch.zeros((T_max, k), dtype=torch.float32, device=device)
+        self.slot_offsets = torch.zeros(S + 1, **i32)
+        self.active_slots = torch.zeros(max(1, min(S, P)), **i32)
+        self.num_active = torch.zeros(1, **i32)
+        self.perm_pair = torch.zeros(max(1, P), **i32)
+        self.host_token = torch.zeros(max(1, P), **i32)
+        self.host_expert = torch.zeros(max(1, P), **i32)
+        self.host_weight = torch.zeros(max(1, P), dtype=torch.float32, device=device)
+        self.host_count = torch.zeros(1, **i32)
+        bws = moe_batches_workspace_size(T_max, k, E, S)
+        self.batch_ws = torch.zeros(max(1, bws), dtype=torch.uint8, device=device) if bws else None
+        self.ws = torch.zeros(max(1, moe_ffn_workspace_size(spec.fmt, T_max, k, H, spec.I, path)), dtype=torch.uint8,
+                              device=device)
+        self.y_pairs = torch.zeros((max(1, P), H), dtype=pair_dtype, device=device)
+        self.y = torch.zeros((T_max, H), dtype=y_dtype, device=device)
+        if spec.I_shared:
+            assert shared_pool is not None
+            self.sh_offsets = torch.tensor([0, T_max], **i32)
+            self.sh_active = torch.zeros(1, **i32)
+            self.sh_num = torch.ones(1, **i32)
+            self.sh_perm = torch.arange(T_max, **i32)
+            self.sh_ws = torch.zeros(max(1, moe_ffn_workspace_size(MOE_FMT_Q8_0, T_max, 1, H, spec.I_shared,
+                                                                   MOE_PATH_DECODE)), dtype=torch.uint8, device=device)
+            self.y_shared = torch.zeros((T_max, H), dtype=torch.float32, device=device)
+            self.sh_stride = shared_pool.shape[-1]
+
+    def forward(self, x: torch.Tensor, logits: torch.Tensor, stream=None, slot_pool: torch.Tensor | None = None):
+        spec, T = self.spec, x.shape[0]
+        assert T == self.T_max, "buffers are sized for T_max rows"
+        pool = self.slot_pool if slot_pool is None else slot_pool
+        moe_route_topk(logits, spec.k, spec.score, spec.renormalize, spec.scale, self.ids, self.w, stream)
+        moe_build_expert_batches(self.ids, self.w, spec.E, self.slot_of_expert, self.S, self.slot_offsets,
+                                 self.active_slots, self.num_active, self.perm_pair, self.host_token, self.host_expert,
+                                 self.host_weight, self.host_count, self.batch_ws, stream)
+        ffn = moe_expert_ffn_q4k if spec.fmt == MOE_FMT_Q4K else moe_expert_ffn_q8_0
+        ffn(pool, self.stride, self.S, spec.H, spec.I, x, spec.k, self.slot_offsets, self.active_slots,
+            self.num_active, self.perm_pair, self.y_pairs, self.path, self.ws, stream)
+        y_shared = None
+        if spec.I_shared:
+            moe_expert_ffn_q8_0(self.shared_pool, self.sh_stride, 1, spec.H, spec.I_shared, x, 1, self.sh_offsets,
+                                self.sh_active, self.sh_num, self.sh_perm, self.y_shared, MOE_PATH_DECODE, self.sh_ws,
+                                stream)
+            y_shared = self.y_shared
+        moe_combine(self.y_pairs, self.ids, self.w, self.slot_of_expert, y_shared, self.y, stream)
+        return self.y

@@ -1,0 +1,158 @@
+"""The C-ABI library without a GPU: it loads, exports what the header
+declares, packs blobs reversibly and refuses bad arguments by name before
+touching the device."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import fixtures as F
+import quantized_routed_expert_moe_amd as Q
+
+
+def test_library_exports_every_header_function():
+    names = Q.header_functions()
+    assert "moe_route_topk" in names and "moe_combine" in names and len(names) >= 15
+    L = Q.lib()
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_status_names():
+    assert Q._status_name(0) == "MOE_OK"
+    assert Q._status_name(3) == "MOE_ERR_WORKSPACE_TOO_SMALL"
+    assert Q._status_name(99) == "MOE_STATUS_UNKNOWN"
+
+
+def _call(name, *args):
+    st = getattr(Q.lib(), name)(*args)
+    return st, Q.lib().moe_last_error().decode()
+
+
+FAKE = 1 << 20  # aligned non-null address; never dereferenced on these paths
+
+
+@pytest.mark.parametrize("T,E,k,score,want", [
+    (-1, 8, 2, 0, Q.MOE_ERR_INVALID_ARGUMENT),
+    (4, 0, 1, 0, Q.MOE_ERR_INVALID_ARGUMENT),
+    (4, 2000, 2, 0, Q.MOE_ERR_INVALID_ARGUMENT),
+    (4, 8, 9, 0, Q.MOE_ERR_INVALID_ARGUMENT),
+    (4, 256, 65, 0, Q.MOE_ERR_INVALID_ARGUMENT),
+    (4, 8, 0, 0, Q.MOE_ERR_INVALID_ARGUMENT),
+    (4, 8, 2, 7, Q.MOE_ERR_INVALID_ARGUMENT),
+    (1 << 22, 64, 8, 0, Q.MOE_ERR_INVALID_ARGUMENT),
+])
+def test_route_rejects(T, E, k, score, want):
+    st, msg = _call("moe_route_topk", FAKE, T, E, k, score, 1, ctypes.c_float(1.0), FAKE, FAKE, None)
+    assert st == want and msg
+
+
+def test_route_rejects_null():
+    st, msg = _call("moe_route_topk", None, 4, 8, 2, 0, 1, ctypes.c_float(1.0), FAKE, FAKE, None)
+    assert st == Q.MOE_ERR_INVALID_ARGUMENT and "NULL" in msg
+
+
+def test_batches_rejects_bad_slot_count():
+    st, msg = _call("moe_build_expert_batches", FAKE, FAKE, 4, 2, 8, FAKE, 9, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                    FAKE, None, 0, None)
+    assert st == Q.MOE_ERR_INVALID_ARGUMENT and "S = 9" in msg
+
+
+def _ffn(name, **kw):
+    a = dict(pool=FAKE, stride=Q.moe_expert_blob_bytes(Q.MOE_FMT_Q4K, 2048, 768) // 16 * 16 + 256, S=128, H=2048,
+             I=768, x=FAKE, x_dtype=Q.MOE_F32, T=2, k=8, offs=FAKE, act=FAKE, na=FAKE, perm=FAKE, yp=FAKE,
+             y_dtype=Q.MOE_F32, path=Q.MOE_PATH_DECODE, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return _call(name, a["pool"], a["stride"], a["S"], a["H"], a["I"], a["x"], a["x_dtype"], a["T"], a["k"],
+                 a["offs"], a["act"], a["na"], a["perm"], a["yp"], a["y_dtype"], a["path"], a["ws"], a["ws_bytes"],
+                 None)
+
+
+@pytest.mark.parametrize("kw,want,needle", [
+    (dict(H=2000), Q.MOE_ERR_UNSUPPORTED, "multiples of 256"),
+    (dict(I=640), Q.MOE_ERR_UNSUPPORTED, "multiples of 256"),
+    (dict(pool=None), Q.MOE_ERR_INVALID_ARGUMENT, "NULL"),
+    (dict(pool=FAKE + 8), Q.MOE_ERR_INVALID_ARGUMENT, "aligned"),
+    (dict(stride=1024), Q.MOE_ERR_INVALID_ARGUMENT, "smaller than the blob"),
+    (dict(S=0), Q.MOE_ERR_INVALID_ARGUMENT, "S = 0"),
+    (dict(k=65), Q.MOE_ERR_INVALID_ARGUMENT, "k = 65"),
+    (dict(ws_bytes=100), Q.MOE_ERR_WORKSPACE_TOO_SMALL, "workspace"),
+    (dict(y_dtype=Q.MOE_BF16), Q.MOE_ERR_UNSUPPORTED, "decode path"),
+    (dict(path=7), Q.MOE_ERR_INVALID_ARGUMENT, "bad path"),
+    (dict(x_dtype=5), Q.MOE_ERR_INVALID_ARGUMENT, "bad x_dtype"),
+])
+def test_ffn_q4k_rejects(kw, want, needle):
+    st, msg = _ffn("moe_expert_ffn_q4k", **kw)
+    assert st == want and needle in msg, msg
+
+
+def test_ffn_q8_0_rejects_prefill():
+    st, msg = _ffn("moe_expert_ffn_q8_0", H=256, I=128, stride=Q.moe_expert_blob_bytes(Q.MOE_FMT_Q8_0, 256, 128) + 64,
+                   path=Q.MOE_PATH_PREFILL, x_dtype=Q.MOE_BF16)
+    assert st == Q.MOE_ERR_UNSUPPORTED and "Q4_K only" in msg
+
+
+def test_ffn_q8_0_rejects_shape():
+    st, msg = _ffn("moe_expert_ffn_q8_0", H=256, I=96)
+    assert st == Q.MOE_ERR_UNSUPPORTED and "multiples of 128" in msg
+
+
+def test_combine_rejects():
+    st, msg = _call("moe_combine", FAKE, 0, FAKE, FAKE, FAKE, 8, None, 4, 2, 252, FAKE, 0, None)
+    assert st == Q.MOE_ERR_UNSUPPORTED and "multiple of 8" in msg
+    st, msg = _call("moe_combine", FAKE, 3, FAKE, FAKE, FAKE, 8, None, 4, 2, 256, FAKE, 0, None)
+    assert st == Q.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_sizes_are_monotone():
+    a = Q.moe_ffn_workspace_size(Q.MOE_FMT_Q4K, 2, 8, 7168, 2048, Q.MOE_PATH_DECODE)
+    b = Q.moe_ffn_workspace_size(Q.MOE_FMT_Q4K, 4, 8, 7168, 2048, Q.MOE_PATH_DECODE)
+    assert 0 < a < b
+    assert Q.moe_ffn_workspace_size(Q.MOE_FMT_Q4K, 2, 8, 7000, 2048, Q.MOE_PATH_DECODE) == 0
+
+
+@pytest.mark.parametrize("fmt,H,I", [(Q.MOE_FMT_Q4K, 512, 256), (Q.MOE_FMT_Q4K, 768, 512), (Q.MOE_FMT_Q8_0, 256, 128),
+                                     (Q.MOE_FMT_Q8_0, 384, 256)])
+def test_pack_round_trip(fmt, H, I):
+    blob = F.expert_blob(fmt, 5, 0, 1, H, I)
+    packed = Q.moe_pack_expert(fmt, blob, H, I)
+    assert packed.nbytes == blob.nbytes == Q.moe_expert_blob_bytes(fmt, H, I)
+    assert not np.array_equal(packed, blob)
+    assert np.array_equal(Q.moe_unpack_expert(fmt, packed, H, I), blob)
+
+
+def test_pack_places_q4k_fields():
+    """Row r, super-block sb of W_up: its 16 header bytes sit at tile (r//64, sb), offset 1024 + 16*(r%64);
+    quant element 8d+n of sub-block j sits in nibble n of dword d of its 16-byte slot."""
+    H, I = 512, 256
+    blob = F.expert_blob(Q.MOE_FMT_Q4K, 2, 0, 0, H, I)
+    packed = Q.moe_pack_expert(Q.MOE_FMT_Q4K, blob, H, I)
+    rb = H // 256 * 144
+    for r, sb in [(0, 0), (70, 1), (255, 1)]:
+        canon = blob[I * rb + r * rb + sb * 144: I * rb + r * rb + (sb + 1) * 144]
+        tile = ((r // 64) * (H // 256) + sb) * 18432
+        assert np.array_equal(packed[tile + 1024 + 16 * (r % 64): tile + 1040 + 16 * (r % 64)], canon[:16])
+        for j in (0, 3, 7):
+            slot = packed[tile + 3072 + j * 2048 + 16 * (r % 64): tile + 3088 + j * 2048 + 16 * (r % 64)]
+            words = slot.view(np.uint32)
+            for e in (0, 9, 31):
+                byte = canon[16 + (j // 2) * 32 + e]
+                q = (byte >> 4) if j % 2 else (byte & 15)
+                assert (int(words[e // 8]) >> (4 * (e % 8))) & 15 == q
+
+
+def test_validate_slot_map():
+    Q.moe_validate_slot_map(np.array([0, -1, 2, 1], dtype=np.int32), 3)
+    with pytest.raises(Q.QmoeError, match="slot 1 holds"):
+        Q.moe_validate_slot_map(np.array([1, 1, -1], dtype=np.int32), 2)
+    with pytest.raises(Q.QmoeError, match="outside"):
+        Q.moe_validate_slot_map(np.array([0, 3], dtype=np.int32), 2)
+    with pytest.raises(Q.QmoeError, match="outside"):
+        Q.moe_validate_slot_map(np.array([0, -2], dtype=np.int32), 2)
+
+
+def test_timer_misuse():
+    st, msg = _call("moe_timer_end", 0, ctypes.byref(ctypes.c_double()), ctypes.byref(ctypes.c_int()))
+    assert st == Q.MOE_ERR_INVALID_ARGUMENT and "not armed" in msg
+    st, msg = _call("moe_timer_begin", 99, 4)
+    assert st == Q.MOE_ERR_INVALID_ARGUMENT

@@ -1,0 +1,282 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Integer outputs (expert ids, slot offsets, active slots, the permutation,
+the host list) must match bit for bit.  Routing weights: |w - w*| <= 1e-6 *
+max(1, scale).  Decode outputs: max |y - y*| <= 2e-3 * max |y*| over the
+whole [T, H] output (fp16 activations, fp32 accumulation).
+"""
+import numpy as np
+import pytest
+import torch
+
+import fixtures as F
+import oracle as O
+import quantized_routed_expert_moe_amd as Q
+from fixtures import workloads as W
+from tests.gpu_util import THREADS, device_layer, rel_max_err, run_device, run_oracle, say
+
+pytestmark = pytest.mark.gpu
+
+DECODE_TOL = 2e-3
+
+
+def _w_tol(w):
+    return 1e-6 * max(1.0, w.scale)
+
+
+# ------------------------------------------------------------------ route
+
+def _route_device(logits, k, score, renorm, scale):
+    T, E = logits.shape
+    ld = torch.from_numpy(np.ascontiguousarray(logits)).cuda()
+    ids = torch.full((max(T, 1), k), -7, dtype=torch.int32, device="cuda")[:T]
+    w = torch.zeros((max(T, 1), k), dtype=torch.float32, device="cuda")[:T]
+    Q.moe_route_topk(ld, k, score, renorm, scale, ids, w)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), w.cpu().numpy()
+
+
+@pytest.mark.parametrize("wl", [W.TINY, W.QWEN3_DECODE_T2, W.QWEN3_PREFILL, W.DSV3_DECODE_T4, W.DSV3_STACK],
+                         ids=lambda w: w.name.split(",")[0][:24])
+def test_route_matches_oracle(wl):
+    say(f"route {wl.name}")
+    lg = W.logits_of(wl)
+    ids, w = _route_device(lg, wl.k, wl.score, wl.renormalize, wl.scale)
+    oids, ow = O.route(lg, wl.k, wl.score, wl.renormalize, wl.scale)
+    assert np.array_equal(ids, oids)
+    assert np.abs(w - ow).max() <= _w_tol(wl)
+
+
+@pytest.mark.parametrize("T,E,k,score,renorm,scale", [
+    (33, 1000, 64, 0, True, 1.0),
+    (5, 1024, 8, 1, True, 2.5),
+    (7, 64, 64, 0, True, 1.0),
+    (9, 130, 3, 0, False, 1.0),
+    (9, 130, 3, 1, False, 0.5),
+    (1, 1, 1, 0, True, 1.0),
+])
+def test_route_shapes(T, E, k, score, renorm, scale):
+    say(f"route T={T} E={E} k={k} score={score} renorm={renorm}")
+    lg = F.logits_normal(3, 0, T, E)
+    ids, w = _route_device(lg, k, score, renorm, scale)
+    oids, ow = O.route(lg, k, score, renorm, scale)
+    assert np.array_equal(ids, oids)
+    assert np.abs(w - ow).max() <= 1e-6 * max(1.0, scale)
+
+
+def test_route_ties_take_lower_id():
+    say("route ties")
+    lg = np.zeros((4, 200), dtype=np.float32)
+    lg[0] = 1.0                      # all equal
+    lg[1, ::7] = 2.0                 # equal maxima spread over lanes
+    lg[2, [3, 67, 131, 195]] = 5.0   # equal maxima in the same lane slot of different registers
+    lg[3] = np.arange(200) % 5       # many tie groups
+    for score in (0, 1):
+        ids, w = _route_device(lg, 16, score, True, 1.0)
+        oids, ow = O.route(lg, 16, score, True, 1.0)
+        assert np.array_equal(ids, oids)
+        assert np.abs(w - ow).max() <= 1e-6
+
+
+def test_route_empty():
+    say("route T=0")
+    ids, w = _route_device(np.zeros((0, 64), dtype=np.float32), 4, 0, True, 1.0)
+    assert ids.shape == (0, 4)
+
+
+# ---------------------------------------------------------------- batches
+
+def _batches_device(ids, w, E, soe, S):
+    T, k = ids.shape
+    P = T * k
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    i32 = dict(dtype=torch.int32, device="cuda")
+    out = dict(slot_offsets=torch.full((S + 1,), -5, **i32), active_slots=torch.full((max(1, min(S, P)),), -5, **i32),
+               num_active=torch.full((1,), -5, **i32), perm_pair=torch.full((max(1, P),), -5, **i32),
+               host_token=torch.full((max(1, P),), -5, **i32), host_expert=torch.full((max(1, P),), -5, **i32),
+               host_weight=torch.full((max(1, P),), -5.0, dtype=torch.float32, device="cuda"),
+               host_count=torch.full((1,), -5, **i32))
+    Q.moe_build_expert_batches(dev(ids.astype(np.int32)), dev(w.astype(np.float32)), E, dev(soe), S,
+                               out["slot_offsets"], out["active_slots"], out["num_active"], out["perm_pair"],
+                               out["host_token"], out["host_expert"], out["host_weight"], out["host_count"])
+    torch.cuda.synchronize()
+    o = {key: v.cpu().numpy() for key, v in out.items()}
+    na, nres, hc = int(o["num_active"][0]), int(o["slot_offsets"][S]), int(o["host_count"][0])
+    o["active_slots"] = o["active_slots"][:na]
+    o["perm_pair"] = o["perm_pair"][:nres]
+    for key in ("host_token", "host_expert", "host_weight"):
+        o[key] = o[key][:hc]
+    return o
+
+
+def _slot_maps(E, rng):
+    perm = rng.permutation(E).astype(np.int32)
+    half = np.full(E, -1, dtype=np.int32)
+    chosen = rng.permutation(E)[:E // 2]
+    half[chosen] = rng.permutation(E // 2)
+    return {"identity": (np.arange(E, dtype=np.int32), E), "shuffled": (perm, E), "half": (half, E // 2 + 3),
+            "none": (np.full(E, -1, dtype=np.int32), 0)}
+
+
+@pytest.mark.parametrize("wl", [W.TINY, W.QWEN3_DECODE_T1, W.QWEN3_PREFILL, W.DSV3_DECODE_T4],
+                         ids=lambda w: w.name.split(",")[0][:24])
+@pytest.mark.parametrize("smap", ["identity", "shuffled", "half", "none"])
+def test_batches_match_oracle(wl, smap):
+    say(f"batches {wl.name} map={smap}")
+    lg = W.logits_of(wl)
+    ids, w = O.route(lg, wl.k, wl.score, wl.renormalize, wl.scale)
+    soe, S = _slot_maps(wl.E, np.random.default_rng(wl.E + len(smap)))[smap]
+    got = _batches_device(ids, w, wl.E, soe, S)
+    want = O.batches(ids, w, wl.E, soe, S)
+    for key in ("slot_offsets", "active_slots", "perm_pair", "host_token", "host_expert"):
+        assert np.array_equal(got[key], want[key]), key
+    assert int(got["num_active"][0]) == int(want["num_active"][0])
+    assert int(got["host_count"][0]) == int(want["host_count"][0])
+    assert np.array_equal(got["host_weight"], w.astype(np.float32).ravel()[
+        [t * wl.k + j for t in range(wl.T) for j in range(wl.k)
+         if not (0 <= soe[ids[t, j]] < S)]])
+
+
+def test_batches_stack_residency():
+    wl = W.DSV3_STACK
+    for layer in (0, 29, 57):
+        say(f"batches stack layer {layer}")
+        soe, S = W.slot_map(wl, layer)
+        lg = W.logits_of(wl, layer)
+        ids, w = O.route(lg, wl.k, wl.score, wl.renormalize, wl.scale)
+        got = _batches_device(ids, w, wl.E, soe, S)
+        want = O.batches(ids, w, wl.E, soe, S)
+        for key in ("slot_offsets", "active_slots", "perm_pair", "host_token", "host_expert"):
+            assert np.array_equal(got[key], want[key]), key
+
+
+def test_batches_empty():
+    say("batches T=0")
+    got = _batches_device(np.zeros((0, 4), np.int32), np.zeros((0, 4), np.float32), 16, np.arange(16, dtype=np.int32),
+                          16)
+    assert got["slot_offsets"].tolist() == [0] * 17 and int(got["num_active"][0]) == 0
+    assert int(got["host_count"][0]) == 0
+
+
+# ------------------------------------------------------------ decode layer
+
+def _layer_case(wl, blobs=None, soe=None, S=None, T=None, path=Q.MOE_PATH_AUTO, x=None, logits=None):
+    soe_, S_ = W.slot_map(wl)
+    soe = soe_ if soe is None else soe
+    S = S_ if S is None else S
+    x = W.x_of(wl) if x is None else x
+    logits = W.logits_of(wl) if logits is None else logits
+    T = x.shape[0]
+    if blobs is None:
+        blobs = W.expert_blobs(wl)
+    shared = W.shared_blob(wl)
+    layer = device_layer(wl, blobs, soe, S, shared, T, path)
+    got = run_device(layer, x, logits)
+    want = run_oracle(wl, blobs, x, logits, soe, shared, want_pairs=True)
+    return got, want, soe, S
+
+
+def _check_layer(wl, got, want, soe, S, tol=DECODE_TOL):
+    assert np.array_equal(got["ids"], want["ids"])
+    assert np.abs(got["w"] - want["w"]).max() <= _w_tol(wl)
+    ob = O.batches(want["ids"], want["w"], wl.E, soe, S)
+    for key in ("slot_offsets", "active_slots", "perm_pair", "host_token", "host_expert"):
+        assert np.array_equal(got[key], ob[key]), key
+    err = rel_max_err(got["y"], want["y"])
+    say(f"  max|y-y*|/max|y*| = {err:.3e}")
+    assert err <= tol
+
+
+@pytest.mark.parametrize("wl", [W.TINY, W.QWEN3_DECODE_T1, W.QWEN3_DECODE_T2],
+                         ids=lambda w: w.name.split(",")[0][:24] + f"-T{w.T}")
+def test_decode_layer_matches_oracle(wl):
+    say(f"decode layer {wl.name}")
+    got, want, soe, S = _layer_case(wl)
+    _check_layer(wl, got, want, soe, S)
+    # every resident pair's own output, too
+    res = [p for p in range(wl.T * wl.k) if soe[want["ids"].ravel()[p]] >= 0]
+    assert rel_max_err(got["y_pairs"][res], want["y_pairs"][res]) <= DECODE_TOL
+
+
+@pytest.fixture(scope="module")
+def dsv3_blobs():
+    say("generating 256 DeepSeek-V3-shaped Q4_K experts")
+    F.set_num_threads(THREADS)
+    return W.expert_blobs(W.DSV3_DECODE_T2)
+
+
+@pytest.mark.parametrize("wl", [W.DSV3_DECODE_T2, W.DSV3_DECODE_T4], ids=["T2", "T4"])
+def test_dsv3_decode_layer_matches_oracle(wl, dsv3_blobs):
+    say(f"decode layer {wl.name}")
+    got, want, soe, S = _layer_case(wl, blobs=dsv3_blobs)
+    _check_layer(wl, got, want, soe, S)
+
+
+def test_dsv3_partial_residency(dsv3_blobs):
+    """Stack layer 0's 96-of-256 residency on the DeepSeek-V3-shaped layer:
+    non-resident pairs add nothing on the card and form the host list."""
+    wl = W.DSV3_STACK
+    soe, S = W.slot_map(wl, 0)
+    base = W.DSV3_DECODE_T2
+    say("decode layer with 96 resident experts")
+    got, want, soe, S = _layer_case(base, blobs=dsv3_blobs, soe=soe, S=S, logits=W.logits_of(wl, 0))
+    _check_layer(base, got, want, soe, S)
+    assert got["host_count"] > 0 and got["num_active"] > 0
+
+
+def test_decode_many_tokens_per_slot():
+    """48 tokens over 8 experts on the decode path: slots hold up to dozens of
+    tokens (chunks of four plus a remainder)."""
+    wl = W.Workload("small Q4_K layer, 48 tokens", F.Q4K, 512, 256, 8, 3, 48)
+    say(wl.name)
+    got, want, soe, S = _layer_case(wl, path=Q.MOE_PATH_DECODE)
+    _check_layer(wl, got, want, soe, S)
+
+
+def test_decode_q8_0_many_tokens():
+    wl = W.Workload("small Q8_0 layer, 37 tokens, partial residency", F.Q8_0, 384, 256, 12, 4, 37)
+    say(wl.name)
+    soe = np.array([3, -1, 0, 5, -1, 1, 2, -1, 4, 6, -1, 7], dtype=np.int32)
+    got, want, soe, S = _layer_case(wl, soe=soe, S=9)
+    _check_layer(wl, got, want, soe, S)
+
+
+def test_decode_zero_input_gives_zero():
+    wl = W.QWEN3_DECODE_T2
+    say("decode x = 0")
+    x = np.zeros((wl.T, wl.H), dtype=np.float32)
+    got, want, soe, S = _layer_case(wl, x=x)
+    assert np.all(got["y"] == 0.0)
+
+
+# ---------------------------------------------------- determinism and graphs
+
+def test_eager_runs_bitwise_equal_and_graph_replay_equals_eager():
+    wl = W.QWEN3_DECODE_T2
+    say("determinism and graph replay")
+    blobs = W.expert_blobs(wl)
+    soe, S = W.slot_map(wl)
+    layer = device_layer(wl, blobs, soe, S, None, wl.T)
+    xs = [torch.from_numpy(W.x_of(wl, seed=s)).cuda() for s in range(3)]
+    ls = [torch.from_numpy(W.logits_of(wl, seed=s)).cuda() for s in range(3)]
+    eager = []
+    for i in range(3):
+        eager.append(layer.forward(xs[i], ls[i]).clone())
+    again = layer.forward(xs[0], ls[0]).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(eager[0], again)
+    # capture one forward on static inputs, replay with new contents
+    x_static, l_static = xs[0].clone(), ls[0].clone()
+    layer.forward(x_static, l_static)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        y_graph = layer.forward(x_static, l_static)
+    for rep in range(3):
+        for i in (2, 0, 1):
+            x_static.copy_(xs[i])
+            l_static.copy_(ls[i])
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y_graph, eager[i]), (rep, i)
+            torch.cuda.synchronize()
