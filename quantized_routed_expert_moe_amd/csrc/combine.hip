@@ -32,15 +32,27 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
     const int h0 = (blockIdx.x * 256 + threadIdx.x) * 8;
     if (h0 >= H) return;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-        const size_t p = (size_t)t * k + j;
-        const int id = ids[p];
-        if (id < 0 || id >= E || soe[id] < 0) continue;
-        const float wj = w[p];
-        float v[8];
-        load8(yp, yp_dtype, p * H + h0, v);
+    // Rows of non-resident pairs are read too (they are in bounds, possibly
+    // never written) and dropped by a select, so the loads of all k pairs
+    // can be in flight together instead of waiting on the residency test.
+    constexpr int kBatch = 8;
+    for (int j0 = 0; j0 < k; j0 += kBatch) {
+        float v[kBatch][8];
+        bool res[kBatch];
+        float wj[kBatch];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
+        for (int jj = 0; jj < kBatch; ++jj) {
+            const int j = min(j0 + jj, k - 1);
+            const size_t p = (size_t)t * k + j;
+            const int id = ids[p];
+            res[jj] = (j0 + jj < k) && id >= 0 && id < E && soe[id] >= 0;
+            wj[jj] = w[p];
+            load8(yp, yp_dtype, p * H + h0, v[jj]);
+        }
+#pragma unroll
+        for (int jj = 0; jj < kBatch; ++jj)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = res[jj] ? fmaf(wj[jj], v[jj][i], acc[i]) : acc[i];
     }
     if (ysh) {
         float v[8];

@@ -18,25 +18,24 @@
 //     1152 * sum x for Q8_0) is precomputed per 32-element block of the
 //     activation and subtracted once per block, together with the Q4_K min
 //     term dmin * m_j * sum x.
-//   * Activations (token rows, and the intermediate h) are read through
-//     wave-uniform addresses, i.e. scalar loads into SGPR operands of the dot
-//     instructions; each is a 64-byte record per 32 elements laid out in the
-//     order the nibble/byte extraction produces.
+//   * Activations (token rows, and the intermediate h) are 64-byte records per
+//     32 elements, laid out in the order the nibble/byte extraction produces.
+//     Each wave copies the records of its K range for the tokens of the
+//     current chunk into its own LDS region with coalesced loads once; the
+//     inner loop then reads them as wave-wide broadcasts (every lane reads the
+//     same address), so no load latency sits inside the dot-product loop.
 #include "device_common.h"
 #include "qmoe_internal.h"
 
 namespace qmoe {
 
-constexpr int kMaxTok = 4;     // tokens of one slot handled per pass over its weights
+constexpr int kMaxTok = 2;     // tokens of one slot handled per pass over its weights
 constexpr int kMaxWaves = 8;   // waves per workgroup (split of the K dimension)
 constexpr uint32_t kMagic = 0x64006400u;  // fp16 1024.0 in both halves
 
-// Activation and h records are written by an earlier launch and only read
-// by the GEMV kernels, so they are read through the constant address space:
-// wave-uniform reads then become scalar loads whose results feed the dot
-// instructions as SGPR operands (no vector-memory traffic, no VGPRs).
-typedef const uint32_t __attribute__((address_space(4))) cu32;
-typedef const float __attribute__((address_space(4))) cf32;  // (C, S) pairs, two floats each
+// Records staged in LDS: X words [16 per record] and (C, S) pairs.
+typedef const uint32_t cu32;
+typedef const float cf32;  // (C, S) pairs, two floats each
 
 // ----------------------------------------------------------- activations
 
@@ -174,67 +173,146 @@ __device__ __forceinline__ void q4k_header(const uint4 h, float* ds, float* dm) 
 __device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint2 ld8(const uint8_t* p) { return *reinterpret_cast<const uint2*>(p); }
 
-// ------------------------------------------------------------ gate / up
+// ------------------------------------------------------------ GEMV core
+//
+// One kernel template serves gate/up (NMAT = 2: the gate and up rows of the
+// same intermediate feature, interleaved per tile) and down (NMAT = 1).
+// Per workgroup: one active slot (blockIdx.y) and one 64-row tile
+// (blockIdx.x); its waves split the K units (Q4_K super-blocks or Q8_0
+// groups of four blocks).  Per unit a wave: issues the weight loads of the
+// unit, loads the activation records of the unit for the chunk's tokens,
+// writes them to its LDS region, and runs the dot products with the records
+// read back as broadcasts.  The first unit's weights are requested right
+// after the slot lookup, before the batch bookkeeping, so their HBM latency
+// overlaps the dependent loads of offsets, permutation and records.
 
-// Partial gate and up dot products of this lane's row over K units
-// [u0, u1) for NT tokens whose activation records start at rec[t].
-template <int FMT, int NT>
-__device__ __forceinline__ void gateup_partial(const uint8_t* __restrict__ tiles, int u0, int u1, int lane,
-                                               cu32* const* rec, cf32* const* rcs, float* g,
-                                               float* u) {
-    for (int un = u0; un < u1; ++un) {
-        if (FMT == 1) {
-            const uint8_t* tile = tiles + (size_t)un * kQ4kGateUpTile;
-            const uint4 hg = ld16(tile + lane * 16);
-            const uint4 hu = ld16(tile + 1024 + lane * 16);
-            uint4 qg[8], qu[8];
+template <int FMT> struct Unit {
+    static constexpr int kRecords = FMT == 1 ? 8 : 4;  // 32-element blocks per unit
+};
+
+template <int FMT, int NMAT> struct UnitRegs;
+template <int NMAT> struct UnitRegs<1, NMAT> {
+    uint4 hdr[NMAT];
+    uint4 q[8][NMAT];
+};
+template <int NMAT> struct UnitRegs<0, NMAT> {
+    uint2 sc[NMAT];
+    uint4 q[4][NMAT][2];
+};
+
+template <int FMT, int NMAT>
+__device__ __forceinline__ constexpr int tile_bytes() {
+    return FMT == 1 ? NMAT * 9216 : NMAT * 8704;
+}
+
+// This lane's bytes of one packed tile (layouts in qmoe_internal.h; the
+// down tile is the NMAT = 1 case of the same formulas).
+template <int NMAT>
+__device__ __forceinline__ void load_unit(const uint8_t* __restrict__ tile, int lane, UnitRegs<1, NMAT>& r) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                qg[j] = ld16(tile + 2048 + j * 2048 + lane * 16);
-                qu[j] = ld16(tile + 3072 + j * 2048 + lane * 16);
-            }
-            float dsg[8], dmg[8], dsu[8], dmu[8];
-            q4k_header(hg, dsg, dmg);
-            q4k_header(hu, dsu, dmu);
+    for (int m = 0; m < NMAT; ++m) r.hdr[m] = ld16(tile + m * 1024 + lane * 16);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    cu32* X = rec[t] + (size_t)(un * 8 + j) * 16;
-                    const float c = rcs[t][2 * (un * 8 + j)], sx = rcs[t][2 * (un * 8 + j) + 1];
-                    const float ag = q4k_dot(qg[j], X);
-                    const float au = q4k_dot(qu[j], X);
-                    g[t] += dsg[j] * (ag - c) - dmg[j] * sx;
-                    u[t] += dsu[j] * (au - c) - dmu[j] * sx;
-                }
-            }
-        } else {
-            const uint8_t* tile = tiles + (size_t)un * kQ8GateUpTile;
-            const uint2 sg = ld8(tile + lane * 8);
-            const uint2 su = ld8(tile + 512 + lane * 8);
-            uint4 qg[8], qu[8];
+        for (int m = 0; m < NMAT; ++m) r.q[j][m] = ld16(tile + NMAT * 1024 + j * NMAT * 1024 + m * 1024 + lane * 16);
+}
+template <int NMAT>
+__device__ __forceinline__ void load_unit(const uint8_t* __restrict__ tile, int lane, UnitRegs<0, NMAT>& r) {
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                qg[2 * jj] = ld16(tile + 1024 + jj * 4096 + lane * 16);
-                qg[2 * jj + 1] = ld16(tile + 2048 + jj * 4096 + lane * 16);
-                qu[2 * jj] = ld16(tile + 3072 + jj * 4096 + lane * 16);
-                qu[2 * jj + 1] = ld16(tile + 4096 + jj * 4096 + lane * 16);
-            }
-            const float dg[4] = {half_to_float(sg.x), half_to_float(sg.x >> 16), half_to_float(sg.y),
-                                 half_to_float(sg.y >> 16)};
-            const float du[4] = {half_to_float(su.x), half_to_float(su.x >> 16), half_to_float(su.y),
-                                 half_to_float(su.y >> 16)};
+    for (int m = 0; m < NMAT; ++m) r.sc[m] = ld8(tile + m * 512 + lane * 8);
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
+    for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    cu32* X = rec[t] + (size_t)(un * 4 + jj) * 16;
-                    const float c = rcs[t][2 * (un * 4 + jj)];
-                    g[t] += dg[jj] * (q8_dot(qg[2 * jj], qg[2 * jj + 1], X) - c);
-                    u[t] += du[jj] * (q8_dot(qu[2 * jj], qu[2 * jj + 1], X) - c);
-                }
-            }
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+                r.q[jj][m][hf] = ld16(tile + NMAT * 512 + jj * NMAT * 2048 + m * 2048 + hf * 1024 + lane * 16);
+}
+
+// LDS region of one wave: words [kMaxTok][8][16] dwords, then (C, S) [kMaxTok][8][2].
+constexpr int kStageWords = kMaxTok * 8 * 16;
+constexpr int kStageFloats = kMaxTok * 8 * 2;
+
+// Copy the RB records starting at record r0 of each of the NT token rows
+// into the wave's LDS region (lane i < 4*RB moves 16 bytes of words; lanes
+// 32..32+RB-1 move one (C, S) pair).
+template <int RB, int NT>
+__device__ __forceinline__ void stage_unit(const uint32_t* const* rec_g, const float2* const* rcs_g, int r0, int lane,
+                                           uint32_t* lw, float* lc) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        if (lane < 4 * RB) {
+            const uint4 v = reinterpret_cast<const uint4*>(rec_g[t] + (size_t)r0 * 16)[lane];
+            reinterpret_cast<uint4*>(lw + t * RB * 16)[lane] = v;
+        } else if (lane >= 32 && lane < 32 + RB) {
+            const float2 v = rcs_g[t][r0 + lane - 32];
+            reinterpret_cast<float2*>(lc + t * RB * 2)[lane - 32] = v;
         }
+    }
+    // LDS operations of one wave complete in order; the fence keeps the
+    // compiler from moving the broadcast reads above these writes.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// acc[t][m] += dot of the unit's weights (matrix m) with token t's records.
+template <int NT, int NMAT>
+__device__ __forceinline__ void unit_dots(const UnitRegs<1, NMAT>& r, const uint32_t* lw, const float* lc,
+                                          float (*acc)[NMAT]) {
+    float ds[NMAT][8], dm[NMAT][8];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) q4k_header(r.hdr[m], ds[m], dm[m]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const uint32_t* X = lw + (t * 8 + j) * 16;
+            const float c = lc[(t * 8 + j) * 2], sx = lc[(t * 8 + j) * 2 + 1];
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) acc[t][m] += ds[m][j] * (q4k_dot(r.q[j][m], X) - c) - dm[m][j] * sx;
+        }
+        // keep the scheduler from hoisting every sub-block's nibble
+        // extraction at once (that alone would need 256 VGPRs)
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+template <int NT, int NMAT>
+__device__ __forceinline__ void unit_dots(const UnitRegs<0, NMAT>& r, const uint32_t* lw, const float* lc,
+                                          float (*acc)[NMAT]) {
+    float d[NMAT][4];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+        d[m][0] = half_to_float(r.sc[m].x);
+        d[m][1] = half_to_float(r.sc[m].x >> 16);
+        d[m][2] = half_to_float(r.sc[m].y);
+        d[m][3] = half_to_float(r.sc[m].y >> 16);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const uint32_t* X = lw + (t * 4 + jj) * 16;
+            const float c = lc[(t * 4 + jj) * 2];
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) acc[t][m] += d[m][jj] * (q8_dot(r.q[jj][m][0], r.q[jj][m][1], X) - c);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// K units [u0, u0 + nu) of this lane's row(s) for NT tokens.  `w` holds the
+// weights of unit u0 on entry when `have_first` is set.
+template <int FMT, int NMAT, int NT>
+__device__ __forceinline__ void gemv_units(const uint8_t* __restrict__ tiles, int u0, int nu, int lane,
+                                           UnitRegs<FMT, NMAT>& w, bool have_first, const uint32_t* const* rec_g,
+                                           const float2* const* rcs_g, uint32_t* lw, float* lc,
+                                           float (*acc)[NMAT]) {
+    constexpr int RB = Unit<FMT>::kRecords;
+    for (int ul = 0; ul < nu; ++ul) {
+        if (ul > 0 || !have_first) load_unit(tiles + (size_t)(u0 + ul) * tile_bytes<FMT, NMAT>(), lane, w);
+        stage_unit<RB, NT>(rec_g, rcs_g, (u0 + ul) * RB, lane, lw, lc);
+        unit_dots<NT, NMAT>(w, lw, lc, acc);
     }
 }
 
@@ -260,178 +338,101 @@ __device__ __forceinline__ void store_h_record(float h, int rg, int lane, uint32
     const uint32_t bits = float_to_half_bits(v);
     reinterpret_cast<uint16_t*>(hw_q + (size_t)blk * 16)[word * 2 + half] = (uint16_t)bits;
     const float c = half_wave_sum(half_to_float(bits)) * (FMT == 1 ? 1024.0f : 1152.0f);
-    const float s = half_wave_sum(h);
-    if (e == 0) hcs_q[blk] = make_float2(c, s);
+    const float sx = half_wave_sum(h);
+    if (e == 0) hcs_q[blk] = make_float2(c, sx);
 }
 
-template <int FMT>
-__global__ __launch_bounds__(512) void gateup_kernel(const uint8_t* __restrict__ pool, size_t stride, int S, int H,
-                                                     int I, const uint32_t* __restrict__ xw,
-                                                     const float2* __restrict__ xcs, int T, int k,
-                                                     const int32_t* __restrict__ offsets,
-                                                     const int32_t* __restrict__ active,
-                                                     const int32_t* __restrict__ num_active,
-                                                     const int32_t* __restrict__ perm, uint32_t* __restrict__ hw,
-                                                     float2* __restrict__ hcs, int units_per_wave) {
-    __shared__ float red[kMaxWaves][kMaxTok][2][64];
-    if ((int)blockIdx.y >= *num_active) return;
-    const int slot = active[blockIdx.y];
-    if (slot < 0 || slot >= S) return;
-    const int P = T * k;
-    const int q0 = offsets[slot], q1 = offsets[slot + 1];
-    if (q0 < 0 || q1 > P || q1 < q0) return;
-
-    const int rg = blockIdx.x;
-    // wave index made visibly uniform, so K-loop bounds and record addresses stay scalar
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
-    const int units = FMT == 1 ? H / 256 : H / 128;
-    const int u0 = min(units, wave * units_per_wave), u1 = min(units, u0 + units_per_wave);
-    const int nblkH = H / 32, nblkI = I / 32;
-    const uint8_t* tiles = pool + (size_t)slot * stride +
-                           (size_t)rg * units * (FMT == 1 ? kQ4kGateUpTile : kQ8GateUpTile);
-
-    for (int c = q0; c < q1; c += kMaxTok) {
-        const int nt = min(kMaxTok, q1 - c);
-        cu32* rec[kMaxTok];
-        cf32* rcs[kMaxTok];
-#pragma unroll
-        for (int i = 0; i < kMaxTok; ++i) {
-            int p = perm[c + min(i, nt - 1)];
-            int t = (p >= 0 && p < P) ? p / k : 0;
-            rec[i] = (cu32*)(xw + (size_t)t * nblkH * 16);
-            rcs[i] = (cf32*)(xcs + (size_t)t * nblkH);
-        }
-        float g[kMaxTok] = {0.f, 0.f, 0.f, 0.f}, u[kMaxTok] = {0.f, 0.f, 0.f, 0.f};
-        switch (nt) {
-            case 1: gateup_partial<FMT, 1>(tiles, u0, u1, lane, rec, rcs, g, u); break;
-            case 2: gateup_partial<FMT, 2>(tiles, u0, u1, lane, rec, rcs, g, u); break;
-            case 3: gateup_partial<FMT, 3>(tiles, u0, u1, lane, rec, rcs, g, u); break;
-            default: gateup_partial<FMT, 4>(tiles, u0, u1, lane, rec, rcs, g, u); break;
-        }
-#pragma unroll
-        for (int i = 0; i < kMaxTok; ++i) {
-            red[wave][i][0][lane] = g[i];
-            red[wave][i][1][lane] = u[i];
-        }
-        __syncthreads();
-        if (wave == 0) {
-            for (int i = 0; i < nt; ++i) {
-                float G = 0.f, U = 0.f;
-                for (int w = 0; w < nw; ++w) {
-                    G += red[w][i][0][lane];
-                    U += red[w][i][1][lane];
-                }
-                const float h = silu(G) * U;
-                const size_t q = (size_t)(c + i);
-                store_h_record<FMT>(h, rg, lane, hw + q * nblkI * 16, hcs + q * nblkI);
-            }
-        }
-        __syncthreads();
-    }
-}
-
-// ------------------------------------------------------------------ down
-
-template <int FMT, int NT>
-__device__ __forceinline__ void down_partial(const uint8_t* __restrict__ tiles, int u0, int u1, int lane,
-                                             cu32* const* rec, cf32* const* rcs, float* y) {
-    for (int un = u0; un < u1; ++un) {
-        if (FMT == 1) {
-            const uint8_t* tile = tiles + (size_t)un * kQ4kDownTile;
-            const uint4 hd = ld16(tile + lane * 16);
-            uint4 qd[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) qd[j] = ld16(tile + 1024 + j * 1024 + lane * 16);
-            float ds[8], dm[8];
-            q4k_header(hd, ds, dm);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    cu32* X = rec[t] + (size_t)(un * 8 + j) * 16;
-                    const float c = rcs[t][2 * (un * 8 + j)], sx = rcs[t][2 * (un * 8 + j) + 1];
-                    y[t] += ds[j] * (q4k_dot(qd[j], X) - c) - dm[j] * sx;
-                }
-            }
-        } else {
-            const uint8_t* tile = tiles + (size_t)un * kQ8DownTile;
-            const uint2 sd = ld8(tile + lane * 8);
-            uint4 qd[8];
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                qd[2 * jj] = ld16(tile + 512 + jj * 2048 + lane * 16);
-                qd[2 * jj + 1] = ld16(tile + 1536 + jj * 2048 + lane * 16);
-            }
-            const float dd[4] = {half_to_float(sd.x), half_to_float(sd.x >> 16), half_to_float(sd.y),
-                                 half_to_float(sd.y >> 16)};
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    cu32* X = rec[t] + (size_t)(un * 4 + jj) * 16;
-                    const float c = rcs[t][2 * (un * 4 + jj)];
-                    y[t] += dd[jj] * (q8_dot(qd[2 * jj], qd[2 * jj + 1], X) - c);
-                }
-            }
-        }
-    }
-}
-
-template <int FMT>
-__global__ __launch_bounds__(512) void down_kernel(const uint8_t* __restrict__ pool, size_t stride, int S, int H,
-                                                   int I, const uint32_t* __restrict__ hw,
-                                                   const float2* __restrict__ hcs, int T, int k,
+// NMAT = 2: gate/up GEMV + SwiGLU over a slot's tokens (records of token
+// rows, indexed by perm_pair / k), writing h records at each pair's
+// position q.  NMAT = 1: down GEMV (records of h at position q) writing
+// y_pairs at pair perm_pair[q].
+template <int FMT, int NMAT>
+__global__ __launch_bounds__(512) void gemv_kernel(const uint8_t* __restrict__ pool, size_t stride, int S, int K,
+                                                   int rows, size_t section, const uint32_t* __restrict__ rw,
+                                                   const float2* __restrict__ rcs, int T, int k,
                                                    const int32_t* __restrict__ offsets,
                                                    const int32_t* __restrict__ active,
                                                    const int32_t* __restrict__ num_active,
-                                                   const int32_t* __restrict__ perm, float* __restrict__ y_pairs,
+                                                   const int32_t* __restrict__ perm, uint32_t* __restrict__ hw,
+                                                   float2* __restrict__ hcs, float* __restrict__ y_pairs,
                                                    int units_per_wave) {
-    __shared__ float red[kMaxWaves][kMaxTok][64];
-    if ((int)blockIdx.y >= *num_active) return;
+    __shared__ __align__(16) uint32_t stage_w[kMaxWaves][kStageWords];
+    __shared__ __align__(16) float stage_c[kMaxWaves][kStageFloats];
+    __shared__ float red[kMaxWaves][kMaxTok][NMAT][64];
+    constexpr int RB = Unit<FMT>::kRecords;
+
+    // slot lookup: both loads in flight together
+    const int na = *num_active;
     const int slot = active[blockIdx.y];
-    if (slot < 0 || slot >= S) return;
+    if ((int)blockIdx.y >= na || slot < 0 || slot >= S) return;
+
+    const int rg = blockIdx.x;
+    // wave index made visibly uniform, so K-loop bounds stay scalar
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+    const int units = FMT == 1 ? K / 256 : K / 128;
+    const int u0 = min(units, wave * units_per_wave), nu = min(units, u0 + units_per_wave) - u0;
+    const uint8_t* tiles = pool + (size_t)slot * stride + section + (size_t)rg * units * tile_bytes<FMT, NMAT>();
+
+    UnitRegs<FMT, NMAT> w;
+    if (nu > 0) load_unit(tiles + (size_t)u0 * tile_bytes<FMT, NMAT>(), lane, w);
+
     const int P = T * k;
     const int q0 = offsets[slot], q1 = offsets[slot + 1];
     if (q0 < 0 || q1 > P || q1 < q0) return;
-
-    const int rg = blockIdx.x;
-    // wave index made visibly uniform, so K-loop bounds and record addresses stay scalar
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
-    const int units = FMT == 1 ? I / 256 : I / 128;
-    const int u0 = min(units, wave * units_per_wave), u1 = min(units, u0 + units_per_wave);
-    const int nblkI = I / 32;
-    const size_t gateup = FMT == 1 ? q4k_gateup_bytes(H, I) : q8_gateup_bytes(H, I);
-    const uint8_t* tiles = pool + (size_t)slot * stride + gateup +
-                           (size_t)rg * units * (FMT == 1 ? kQ4kDownTile : kQ8DownTile);
+    const int nblk = K / 32;
+    uint32_t* lw = stage_w[wave];
+    float* lc = stage_c[wave];
 
     for (int c = q0; c < q1; c += kMaxTok) {
         const int nt = min(kMaxTok, q1 - c);
-        cu32* rec[kMaxTok];
-        cf32* rcs[kMaxTok];
+        const uint32_t* rec_g[kMaxTok];
+        const float2* rcs_g[kMaxTok];
 #pragma unroll
         for (int i = 0; i < kMaxTok; ++i) {
-            const size_t q = (size_t)(c + min(i, nt - 1));
-            rec[i] = (cu32*)(hw + q * nblkI * 16);
-            rcs[i] = (cf32*)(hcs + q * nblkI);
+            const int q = c + min(i, nt - 1);
+            size_t row;
+            if (NMAT == 2) {
+                const int p = perm[q];
+                row = (p >= 0 && p < P) ? (size_t)(p / k) : 0;
+            } else {
+                row = (size_t)q;
+            }
+            rec_g[i] = rw + row * nblk * 16;
+            rcs_g[i] = rcs + row * nblk;
         }
-        float y[kMaxTok] = {0.f, 0.f, 0.f, 0.f};
+        const bool first = c == q0;
+        float acc[kMaxTok][NMAT];
+#pragma unroll
+        for (int i = 0; i < kMaxTok; ++i)
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) acc[i][m] = 0.f;
         switch (nt) {
-            case 1: down_partial<FMT, 1>(tiles, u0, u1, lane, rec, rcs, y); break;
-            case 2: down_partial<FMT, 2>(tiles, u0, u1, lane, rec, rcs, y); break;
-            case 3: down_partial<FMT, 3>(tiles, u0, u1, lane, rec, rcs, y); break;
-            default: down_partial<FMT, 4>(tiles, u0, u1, lane, rec, rcs, y); break;
+            case 1: gemv_units<FMT, NMAT, 1>(tiles, u0, nu, lane, w, first, rec_g, rcs_g, lw, lc, acc); break;
+            default: gemv_units<FMT, NMAT, 2>(tiles, u0, nu, lane, w, first, rec_g, rcs_g, lw, lc, acc); break;
         }
 #pragma unroll
-        for (int i = 0; i < kMaxTok; ++i) red[wave][i][lane] = y[i];
+        for (int i = 0; i < kMaxTok; ++i)
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) red[wave][i][m][lane] = acc[i][m];
         __syncthreads();
         if (wave == 0) {
             for (int i = 0; i < nt; ++i) {
-                float acc = 0.f;
-                for (int w = 0; w < nw; ++w) acc += red[w][i][lane];
-                const int p = perm[c + i];
-                if (p >= 0 && p < P) y_pairs[(size_t)p * H + rg * 64 + lane] = acc;
+                float v[NMAT];
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m) v[m] = 0.f;
+                for (int wv = 0; wv < nw; ++wv)
+#pragma unroll
+                    for (int m = 0; m < NMAT; ++m) v[m] += red[wv][i][m][lane];
+                const int q = c + i;
+                if (NMAT == 2) {
+                    const float h = silu(v[0]) * v[NMAT - 1];
+                    const int nblk_out = rows / 32;
+                    store_h_record<FMT>(h, rg, lane, hw + (size_t)q * nblk_out * 16, hcs + (size_t)q * nblk_out);
+                } else {
+                    const int p = perm[q];
+                    if (p >= 0 && p < P) y_pairs[(size_t)p * rows + rg * 64 + lane] = v[0];
+                }
             }
         }
         __syncthreads();
@@ -494,11 +495,13 @@ hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s) {
         dim3 grid(a.I / 64, max_active);
         timer_before(kStageGateUp, s);
         if (a.format == 1)
-            hipLaunchKernelGGL(gateup_kernel<1>, grid, dim3(64 * nw), 0, s, a.pool, a.stride, a.S, a.H, a.I, xw, xcs,
-                               a.T, a.k, a.slot_offsets, a.active_slots, a.num_active, a.perm_pair, hw, hcs, upw);
+            hipLaunchKernelGGL((gemv_kernel<1, 2>), grid, dim3(64 * nw), 0, s, a.pool, a.stride, a.S, a.H, a.I,
+                               (size_t)0, xw, xcs, a.T, a.k, a.slot_offsets, a.active_slots, a.num_active, a.perm_pair,
+                               hw, hcs, (float*)nullptr, upw);
         else
-            hipLaunchKernelGGL(gateup_kernel<0>, grid, dim3(64 * nw), 0, s, a.pool, a.stride, a.S, a.H, a.I, xw, xcs,
-                               a.T, a.k, a.slot_offsets, a.active_slots, a.num_active, a.perm_pair, hw, hcs, upw);
+            hipLaunchKernelGGL((gemv_kernel<0, 2>), grid, dim3(64 * nw), 0, s, a.pool, a.stride, a.S, a.H, a.I,
+                               (size_t)0, xw, xcs, a.T, a.k, a.slot_offsets, a.active_slots, a.num_active, a.perm_pair,
+                               hw, hcs, (float*)nullptr, upw);
         timer_after(kStageGateUp, s);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -510,13 +513,18 @@ hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s) {
         split_k(units, (long)(a.H / 64) * max_active, &nw, &upw);
         dim3 grid(a.H / 64, max_active);
         float* yp = static_cast<float*>(a.y_pairs);
+        const size_t section = a.format == 1 ? q4k_gateup_bytes(a.H, a.I) : q8_gateup_bytes(a.H, a.I);
         timer_before(kStageDown, s);
         if (a.format == 1)
-            hipLaunchKernelGGL(down_kernel<1>, grid, dim3(64 * nw), 0, s, a.pool, a.stride, a.S, a.H, a.I, hw, hcs,
-                               a.T, a.k, a.slot_offsets, a.active_slots, a.num_active, a.perm_pair, yp, upw);
+            hipLaunchKernelGGL((gemv_kernel<1, 1>), grid, dim3(64 * nw), 0, s, a.pool, a.stride, a.S, a.I, a.H,
+                               section, (const uint32_t*)hw, (const float2*)hcs, a.T, a.k, a.slot_offsets,
+                               a.active_slots, a.num_active, a.perm_pair, (uint32_t*)nullptr, (float2*)nullptr, yp,
+                               upw);
         else
-            hipLaunchKernelGGL(down_kernel<0>, grid, dim3(64 * nw), 0, s, a.pool, a.stride, a.S, a.H, a.I, hw, hcs,
-                               a.T, a.k, a.slot_offsets, a.active_slots, a.num_active, a.perm_pair, yp, upw);
+            hipLaunchKernelGGL((gemv_kernel<0, 1>), grid, dim3(64 * nw), 0, s, a.pool, a.stride, a.S, a.I, a.H,
+                               section, (const uint32_t*)hw, (const float2*)hcs, a.T, a.k, a.slot_offsets,
+                               a.active_slots, a.num_active, a.perm_pair, (uint32_t*)nullptr, (float2*)nullptr, yp,
+                               upw);
         timer_after(kStageDown, s);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

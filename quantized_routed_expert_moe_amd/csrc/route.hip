@@ -3,8 +3,10 @@
 // reference list names the router core).
 //
 // One wave64 per token row.  Each lane keeps E/64 logits in registers; k
-// rounds of a wave-wide arg-max (butterfly shuffles on the key (logit desc,
-// id asc)) pick the experts in rank order, lane j keeping pick j.  Weights
+// rounds of a wave-wide arg-max on the key (logit desc, id asc) pick the
+// experts in rank order, lane j keeping pick j.  The arg-max is a DPP
+// reduction (quad permutes, row mirrors, row broadcasts) into lane 63 and a
+// read of that lane: register-to-register moves, no LDS round trips.  Weights
 // are then formed from the k picks in fp32 (softmax renormalised over the
 // picks equals the full softmax renormalised; the full denominator is only
 // needed when renormalisation is off).
@@ -20,6 +22,31 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
     if (ia == INT_MAX) return false;
     if (ib == INT_MAX) return true;
     return va > vb || (va == vb && ia < ib);
+}
+
+// Combine (v, i) with the candidate DPP_CTRL moves into this lane (rows
+// outside ROW_MASK keep their own value, i.e. compare with themselves).
+template <int DPP_CTRL, int ROW_MASK>
+__device__ __forceinline__ void argmax_step(float& v, int& i) {
+    const float ov = __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), DPP_CTRL, ROW_MASK, 0xF, false));
+    const int oi = __builtin_amdgcn_update_dpp(i, i, DPP_CTRL, ROW_MASK, 0xF, false);
+    if (better(ov, oi, v, i)) {
+        v = ov;
+        i = oi;
+    }
+}
+
+// Wave-wide best (v, i); every lane receives the result.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+    argmax_step<0xB1, 0xF>(v, i);   // quad_perm [1,0,3,2]
+    argmax_step<0x4E, 0xF>(v, i);   // quad_perm [2,3,0,1]
+    argmax_step<0x141, 0xF>(v, i);  // row_half_mirror
+    argmax_step<0x140, 0xF>(v, i);  // row_mirror
+    argmax_step<0x142, 0xA>(v, i);  // row_bcast:15 into rows 1 and 3
+    argmax_step<0x143, 0xC>(v, i);  // row_bcast:31 into rows 2 and 3
+    v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+    i = __builtin_amdgcn_readlane(i, 63);
 }
 
 template <int PER_LANE>
@@ -53,15 +80,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
                 bi = e;
             }
         }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, 64);
-            const int oi = __shfl_xor(bi, off, 64);
-            if (better(ov, oi, bv, bi)) {
-                bv = ov;
-                bi = oi;
-            }
-        }
+        wave_argmax(bv, bi);
         if (lane == r) {
             pick_v = bv;
             pick_id = bi;
