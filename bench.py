@@ -184,7 +184,7 @@ def main():
         import oracle as O
         O.set_threads(threads)
         n_done, c0 = 0, time.time()
-        while time.time() - c0 < args.cpu_seconds and n_done < 4 * nbatch:
+        while time.time() - c0 < args.cpu_seconds:
             i = n_done % nbatch
             lg = ls[i].cpu().numpy()
             x = xs[i].cpu().numpy().astype(np.float64)

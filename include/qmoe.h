@@ -180,7 +180,8 @@ moe_status moe_validate_slot_map(const int32_t* slot_of_expert, int E, int S);
  *               MOE_PATH_PREFILL (Q4_K only): bf16 x, weights dequantized to
  *               bf16 tiles, bf16 MFMA with fp32 accumulate, h rounded to bf16;
  *               y_pairs MOE_F32 or MOE_BF16.
- *               MOE_PATH_AUTO: PREFILL for Q4_K when T > 32, else DECODE.
+ *               MOE_PATH_AUTO: PREFILL for Q4_K with bf16 x when T > 32, else
+               DECODE.
  * ws, ws_bytes  device workspace, at least moe_ffn_workspace_size(format, T,
  *               k, H, I, path).
  *

@@ -63,9 +63,9 @@ size_t blob_bytes(int format, int H, int I) {
     return format == MOE_FMT_Q4K ? 3 * w / 256 * 144 : 3 * w / 32 * 34;
 }
 
-int resolve_path(int format, int T, int path) {
+int resolve_path(int format, int T, int x_dtype, int path) {
     if (path != MOE_PATH_AUTO) return path;
-    return (format == MOE_FMT_Q4K && T > 32) ? MOE_PATH_PREFILL : MOE_PATH_DECODE;
+    return (format == MOE_FMT_Q4K && x_dtype == MOE_BF16 && T > 32) ? MOE_PATH_PREFILL : MOE_PATH_DECODE;
 }
 
 // ------------------------------------------------------------------ timers
@@ -238,14 +238,13 @@ moe_status ffn_common(int format, const void* slot_pool, size_t slot_stride, int
     if (y_dtype != MOE_F32 && y_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARGUMENT, "bad y_dtype %d", y_dtype);
     if (path < MOE_PATH_AUTO || path > MOE_PATH_PREFILL) return fail(MOE_ERR_INVALID_ARGUMENT, "bad path %d", path);
     if (!aligned16(x) || !aligned16(y_pairs)) return fail(MOE_ERR_INVALID_ARGUMENT, "x and y_pairs must be 16-byte aligned");
-    const int p = resolve_path(format, T, path);
+    const int p = resolve_path(format, T, x_dtype, path);
     size_t need;
     if (p == MOE_PATH_DECODE) {
         if (y_dtype != MOE_F32) return fail(MOE_ERR_UNSUPPORTED, "the decode path writes MOE_F32 y_pairs");
         need = qmoe::decode_workspace_bytes(T, k, H, I);
     } else {
         if (format != MOE_FMT_Q4K) return fail(MOE_ERR_UNSUPPORTED, "the prefill path is implemented for Q4_K only");
-        return fail(MOE_ERR_UNSUPPORTED, "the prefill path is not built in this library");
         if (x_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the prefill path takes MOE_BF16 x");
         need = qmoe::prefill_workspace_bytes(T, k, H, I);
     }
@@ -394,6 +393,7 @@ moe_status moe_validate_slot_map(const int32_t* slot_of_expert, int E, int S) {
 size_t moe_ffn_workspace_size(int format, int T, int k, int H, int I, int path) {
     if (check_shape(format, H, I) != MOE_OK || T < 0 || k < 1 || k > MOE_MAX_TOPK) return 0;
     const size_t dec = qmoe::decode_workspace_bytes(T, k, H, I);
+    static_assert(MOE_MAX_EXPERTS == qmoe::kMaxExpertsInternal, "expert limits differ");
     if (format != MOE_FMT_Q4K || path == MOE_PATH_DECODE) return dec;
     const size_t pre = qmoe::prefill_workspace_bytes(T, k, H, I);
     if (path == MOE_PATH_PREFILL) return pre;

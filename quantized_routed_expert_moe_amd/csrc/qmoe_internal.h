@@ -38,6 +38,8 @@ namespace qmoe {
 //     [0, 512) scales; [512 + 2048jj, +2048) quants of block jj
 // Q8_0 quant bytes are stored as q + 128 (q xor 0x80), element e at byte e.
 
+constexpr int kMaxExpertsInternal = 1024;  // equals MOE_MAX_EXPERTS of the C ABI
+
 constexpr int kQ4kGateUpTile = 18432;
 constexpr int kQ4kDownTile = 9216;
 constexpr int kQ8GateUpTile = 17408;

@@ -1,0 +1,152 @@
+"""Parity of the prefill path (bf16 MFMA grouped GEMM over Q4_K tiles) with
+the CPU oracle.
+
+Ids, slot offsets, active slots, permutation and host list: bit-exact on
+every row.  Outputs: per token row t, max_i |y_ti - y*_ti| <= 1e-2 *
+max_i |y*_ti| (bf16 activations, weights rounded to bf16 tiles, h rounded
+to bf16, fp32 accumulation).  At the full 4096-token size the oracle runs on
+a seeded sample of rows (routing is per row, so a row's output depends only
+on that row's x and logits).
+"""
+import numpy as np
+import pytest
+import torch
+
+import fixtures as F
+import oracle as O
+import quantized_routed_expert_moe_amd as Q
+from fixtures import workloads as W
+from tests.gpu_util import THREADS, device_layer, run_device, run_oracle, say
+
+pytestmark = pytest.mark.gpu
+
+PREFILL_TOL = 1e-2
+
+
+def _row_err(got, want):
+    return float(np.max(np.abs(got - want).max(axis=1) / np.maximum(np.abs(want).max(axis=1), 1e-30)))
+
+
+def _check_ints(wl, got, ids, w, soe, S):
+    ob = O.batches(ids, w, wl.E, soe, S)
+    for key in ("slot_offsets", "active_slots", "perm_pair", "host_token", "host_expert"):
+        assert np.array_equal(got[key], ob[key]), key
+
+
+def _prefill_case(wl, soe=None, S=None, pair_dtype=torch.bfloat16, y_dtype=torch.bfloat16, sample=None, blobs=None):
+    soe_, S_ = W.slot_map(wl)
+    soe = soe_ if soe is None else soe
+    S = S_ if S is None else S
+    x, logits = W.x_of(wl), W.logits_of(wl)
+    blobs = W.expert_blobs(wl) if blobs is None else blobs
+    layer = device_layer(wl, blobs, soe, S, None, wl.T, Q.MOE_PATH_PREFILL, pair_dtype=pair_dtype, y_dtype=y_dtype)
+    got = run_device(layer, x, logits)
+    ids, w = O.route(logits, wl.k, wl.score, wl.renormalize, wl.scale)
+    assert np.array_equal(got["ids"], ids)
+    assert np.abs(got["w"] - w).max() <= 1e-6
+    _check_ints(wl, got, ids, w, soe, S)
+    rows = np.arange(wl.T) if sample is None else sample
+    want = run_oracle(wl, blobs, x[rows], logits[rows], soe, None)
+    err = _row_err(got["y"][rows], want["y"])
+    say(f"  rows checked {len(rows)}, max per-row error {err:.3e}")
+    return err
+
+
+def test_prefill_qwen3_full_size():
+    """4096 tokens, Zipf(1.0)-skewed loads over 128 experts, all resident."""
+    wl = W.QWEN3_PREFILL
+    say(wl.name)
+    F.set_num_threads(THREADS)
+    rng = np.random.default_rng(0)
+    sample = np.sort(rng.choice(wl.T, size=96, replace=False))
+    assert _prefill_case(wl, sample=sample) <= PREFILL_TOL
+
+
+@pytest.mark.parametrize("T,E,k,pd,yd", [
+    (300, 16, 4, torch.bfloat16, torch.bfloat16),
+    (129, 8, 2, torch.float32, torch.float32),
+    (64, 32, 8, torch.float32, torch.bfloat16),
+])
+def test_prefill_small_layers(T, E, k, pd, yd):
+    """Several M tiles per slot, ragged last tiles, slots with a single row."""
+    wl = W.Workload(f"prefill T{T} E{E} k{k}", F.Q4K, 512, 256, E, k, T, x_bf16=True, zipf_s=1.0, seed=3)
+    say(wl.name)
+    assert _prefill_case(wl, pair_dtype=pd, y_dtype=yd) <= PREFILL_TOL
+
+
+def test_prefill_partial_residency():
+    wl = W.Workload("prefill T200 E24 k3, 15 resident of 24", F.Q4K, 768, 512, 24, 3, 200, x_bf16=True,
+                    zipf_s=1.2, seed=5)
+    say(wl.name)
+    rng = np.random.default_rng(1)
+    soe = np.full(24, -1, dtype=np.int32)
+    soe[rng.permutation(24)[:15]] = rng.permutation(17)[:15]
+    assert _prefill_case(wl, soe=soe, S=17) <= PREFILL_TOL
+
+
+def test_prefill_tile_boundaries():
+    """One expert receives exactly 128, another 129, another 1 pair."""
+    wl = W.Workload("prefill tile boundaries", F.Q4K, 256, 256, 4, 1, 258, x_bf16=True, seed=7)
+    say(wl.name)
+    x = W.x_of(wl)
+    logits = np.zeros((258, 4), dtype=np.float32)
+    logits[:, 3] = -1.0
+    logits[:128, 0] = 5.0
+    logits[128:257, 1] = 5.0
+    logits[257, 2] = 5.0
+    blobs = W.expert_blobs(wl)
+    soe, S = W.slot_map(wl)
+    layer = device_layer(wl, blobs, soe, S, None, wl.T, Q.MOE_PATH_PREFILL, pair_dtype=torch.float32)
+    got = run_device(layer, x, logits)
+    assert got["slot_offsets"].tolist() == [0, 128, 257, 258, 258]
+    want = run_oracle(wl, blobs, x, logits, soe, None)
+    assert _row_err(got["y"], want["y"]) <= PREFILL_TOL
+
+
+def test_prefill_matches_decode_path_closely():
+    """The same layer through both paths: decode (fp16 activations) and
+    prefill (bf16 tiles) agree within the prefill tolerance."""
+    wl = W.Workload("prefill vs decode", F.Q4K, 512, 512, 8, 2, 40, x_bf16=True, seed=9)
+    say(wl.name)
+    x, logits = W.x_of(wl), W.logits_of(wl)
+    blobs = W.expert_blobs(wl)
+    soe, S = W.slot_map(wl)
+    pre = run_device(device_layer(wl, blobs, soe, S, None, wl.T, Q.MOE_PATH_PREFILL, pair_dtype=torch.float32),
+                     x, logits)
+    dec = run_device(device_layer(wl, blobs, soe, S, None, wl.T, Q.MOE_PATH_DECODE), x, logits)
+    assert _row_err(pre["y"], dec["y"]) <= PREFILL_TOL
+
+
+def _bf16_round(a: np.ndarray) -> np.ndarray:
+    return F.bf16_bits_to_f32(F.to_bf16_bits(a.astype(np.float32))).astype(np.float64)
+
+
+def test_prefill_equals_its_bf16_rounding_model():
+    """The prefill arithmetic is the exact layer with three roundings: each
+    dequantized weight to fp32 then bf16, and h to bf16.  Emulating those
+    roundings on the oracle's fp64 dequantized weights must reproduce the
+    GPU's y_pairs up to fp32 accumulation noise."""
+    wl = W.Workload("prefill rounding model", F.Q4K, 512, 256, 4, 2, 64, x_bf16=True, seed=11)
+    say(wl.name)
+    x, logits = W.x_of(wl), W.logits_of(wl)
+    blobs = W.expert_blobs(wl)
+    soe, S = W.slot_map(wl)
+    got = run_device(device_layer(wl, blobs, soe, S, None, wl.T, Q.MOE_PATH_PREFILL, pair_dtype=torch.float32),
+                     x, logits)
+    H, I = wl.H, wl.I
+    gb = F.matrix_bytes(F.Q4K, I, H)
+    xf = W.x_f64(wl, x)
+    worst = 0.0
+    for t in range(wl.T):
+        for j in range(wl.k):
+            e = int(got["ids"][t, j])
+            b = blobs[e]
+            Wg = _bf16_round(O.dequant(O.Q4K, b[:gb], I * H)).reshape(I, H)
+            Wu = _bf16_round(O.dequant(O.Q4K, b[gb:2 * gb], I * H)).reshape(I, H)
+            Wd = _bf16_round(O.dequant(O.Q4K, b[2 * gb:], H * I)).reshape(H, I)
+            g, u = Wg @ xf[t], Wu @ xf[t]
+            h = _bf16_round(g / (1 + np.exp(-g)) * u)
+            y = Wd @ h
+            worst = max(worst, float(np.abs(got["y_pairs"][t * wl.k + j] - y).max() / np.abs(y).max()))
+    say(f"  max |y_pair - model| / max |model| = {worst:.3e}")
+    assert worst <= 2e-5
