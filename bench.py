@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA util (prefill), 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ffn_gateup_q4k_qwen3_decode.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "quantized_routed_expert_moe_amd", "csrc", "ffn_decode.hip")
@@ -46,6 +47,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=16, help="slot-pool replicas rotated over the steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bounded CPU-oracle sample (wall seconds)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--prefill-steps", type=int, default=30,
+                    help="timed steps of the T=4096 prefill layer reported beside the decode line (0 = skip)")
     ap.add_argument("--profile-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
     return ap.parse_args()
@@ -201,6 +204,10 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
 
+    prefill = None
+    if args.prefill_steps > 0:
+        prefill = bench_prefill(args, blobs, pool0, stride)
+
     traffic = read_traffic()
     out = {
         "metric": METRIC,
@@ -225,6 +232,7 @@ def main():
                      "algorithmic_bytes_per_launch": round(gu_bytes / args.steps),
                      "avg_launch_us": round(kern["ffn_gateup"]["avg_us"], 3)},
         "cpu_baseline": cpu,
+        "prefill": prefill,
         "kernels_us": {k2: round(v["avg_us"], 3) for k2, v in kern.items()},
         "down_gemv_GBs": round(dn_gbs, 1),
         "layer_effective_GBs": round(layer_gbs, 1),
@@ -234,6 +242,70 @@ def main():
         "setup_s": round(setup_s, 1),
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_prefill(args, blobs, pool, stride) -> dict:
+    """The same Qwen3-30B-A3B-shaped layer at prefill: 4096 bf16 tokens with
+    Zipf(1.0)-skewed routing, through the grouped bf16 MFMA GEMM path."""
+    import numpy as np
+    import torch
+
+    import quantized_routed_expert_moe_amd as Q
+    from fixtures import workloads as W
+    from quantized_routed_expert_moe_amd.layer import LayerSpec, MoELayer
+
+    wl = W.QWEN3_PREFILL
+    x = torch.from_numpy(W.x_of(wl).view(np.int16)).cuda().view(torch.bfloat16)
+    lg = torch.from_numpy(W.logits_of(wl)).cuda()
+    soe = torch.arange(wl.E, dtype=torch.int32, device="cuda")
+    spec = LayerSpec(wl.fmt, wl.H, wl.I, wl.E, wl.k, wl.score, wl.renormalize, wl.scale)
+    layer = MoELayer(spec, wl.T, wl.E, pool, stride, soe, path=Q.MOE_PATH_PREFILL, y_dtype=torch.bfloat16,
+                     pair_dtype=torch.bfloat16)
+    for _ in range(3):
+        layer.forward(x, lg)
+    torch.cuda.synchronize()
+    M = int(layer.slot_offsets[-1].item())  # resident pairs = GEMM rows over all experts
+    counts = np.diff(layer.slot_offsets.cpu().numpy())
+    stages = {"route": 0, "batches": 1, "tiles": 2, "gemm_gateup": 6, "gemm_down": 7, "combine": 5}
+    for st in stages.values():
+        Q.moe_timer_begin(st, args.prefill_steps)
+    for _ in range(args.prefill_steps):
+        layer.forward(x, lg)
+    torch.cuda.synchronize()
+    kern = {}
+    for name, st in stages.items():
+        ms, n = Q.moe_timer_end(st)
+        kern[name] = 1e3 * ms / max(n, 1)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(x, lg)
+    g.replay()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.prefill_steps):
+        g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.prefill_steps
+    gu_flop = 2.0 * M * (2 * wl.I) * wl.H
+    dn_flop = 2.0 * M * wl.H * wl.I
+    gu_tf = gu_flop / (kern["gemm_gateup"] * 1e-6) / 1e12
+    dn_tf = dn_flop / (kern["gemm_down"] * 1e-6) / 1e12
+    return {
+        "workload": wl.name, "T": wl.T, "steps": args.prefill_steps, "ms_per_step": round(ms_step, 4),
+        "tokens_per_s": round(wl.T / (ms_step * 1e-3), 1),
+        "expert_rows": {"total": M, "max": int(counts.max()), "median": float(np.median(counts)),
+                        "min": int(counts.min())},
+        "roofline": {"bound": "mfma", "kernel": "prefill gate/up grouped GEMM (Q4_K->bf16 tiles, bf16 MFMA)",
+                     "achieved": round(gu_tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gu_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "algorithmic_flop_per_launch": gu_flop, "avg_launch_us": round(kern["gemm_gateup"], 2)},
+        "down_gemm_TFLOPs": round(dn_tf, 1),
+        "expert_gemms_TFLOPs": round((gu_flop + dn_flop) / ((kern["gemm_gateup"] + kern["gemm_down"]) * 1e-6) / 1e12,
+                                     1),
+        "kernels_us": {k2: round(v, 2) for k2, v in kern.items()},
+    }
 
 
 if __name__ == "__main__":

@@ -64,7 +64,7 @@ def lib() -> ctypes.CDLL:
         L.fx_normal_rows.argtypes = [u32, u32, u32, i64, i64, f32, f32, vp]
         L.fx_logits_normal.argtypes = [u32, u32, i64, i32, vp]
         L.fx_permutation.argtypes = [u32, u32, i32, vp]
-        L.fx_logits_zipf.argtypes = [u32, u32, i64, i32, f64, vp]
+        L.fx_logits_zipf.argtypes = [u32, u32, u32, i64, i32, f64, vp]
         L.fx_num_threads.restype = i32
         L.fx_set_num_threads.argtypes = [i32]
         _lib = L
@@ -174,10 +174,11 @@ def permutation(seed: int, layer: int, E: int) -> np.ndarray:
     return out
 
 
-def logits_zipf(seed: int, layer: int, T: int, E: int, s: float) -> np.ndarray:
-    """Gumbel-perturbed Zipf(s) log-probabilities, float32 [T, E], no ties in a row."""
+def logits_zipf(seed: int, layer: int, T: int, E: int, s: float, perm_seed: int | None = None) -> np.ndarray:
+    """Gumbel-perturbed Zipf(s) log-probabilities, float32 [T, E], no ties in a row.
+    The expert ranking comes from perm_seed (default: seed), the noise from seed."""
     out = np.empty((T, E), dtype=np.float32)
-    lib().fx_logits_zipf(seed, layer, T, E, float(s), _p(out))
+    lib().fx_logits_zipf(seed, seed if perm_seed is None else perm_seed, layer, T, E, float(s), _p(out))
     return out
 
 

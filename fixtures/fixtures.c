@@ -453,13 +453,14 @@ void fx_permutation(uint32_t seed, uint32_t layer, int E, int32_t* perm) {
 }
 
 /* Zipf-skewed gate logits: l[t][e] = log p(rank_of[e]) + Gumbel(0,1), with
- * p(r) = r^-s / sum_r' r'^-s over ranks r = 1..E and rank_of[e] = perm[e] + 1.
- * Taking the top k of such a row samples k experts without replacement with
- * probabilities p, so expert loads follow the Zipf law.  Ties redrawn. */
-void fx_logits_zipf(uint32_t seed, uint32_t layer, int64_t T, int E, double s, float* out) {
+ * p(r) = r^-s / sum_r' r'^-s over ranks r = 1..E and rank_of[e] = perm[e] + 1
+ * (perm drawn from perm_seed, the Gumbel noise from seed).  Taking the top k
+ * of such a row samples k experts without replacement with probabilities p,
+ * so expert loads follow the Zipf law.  Ties redrawn. */
+void fx_logits_zipf(uint32_t seed, uint32_t perm_seed, uint32_t layer, int64_t T, int E, double s, float* out) {
     int32_t* perm = (int32_t*)malloc((size_t)E * sizeof(int32_t));
     double* logp = (double*)malloc((size_t)E * sizeof(double));
-    fx_permutation(seed, layer, E, perm);
+    fx_permutation(perm_seed, layer, E, perm);
     double z = 0.0;
     for (int r = 1; r <= E; ++r) z += pow((double)r, -s);
     for (int e = 0; e < E; ++e) logp[e] = -s * log((double)(perm[e] + 1)) - log(z);

@@ -74,7 +74,7 @@ def logits_of(w: Workload, layer: int = 0, seed: int | None = None, T: int | Non
     s = w.seed if seed is None else seed
     T = w.T if T is None else T
     if w.zipf_s:
-        return logits_zipf(s, layer, T, w.E, w.zipf_s)
+        return logits_zipf(s, layer, T, w.E, w.zipf_s, perm_seed=w.seed)
     return logits_normal(s, layer, T, w.E)
 
 
@@ -94,7 +94,7 @@ def frequency_resident_set(w: Workload, layer: int) -> np.ndarray:
     """Experts ranked by how often the layer's Zipf routing picks them over
     count_tokens draws (ties: lower id); the first `resident` are resident,
     slot r holding rank r."""
-    lg = logits_zipf(w.seed + 1, layer, w.count_tokens, w.E, w.zipf_s)
+    lg = logits_zipf(w.seed + 1, layer, w.count_tokens, w.E, w.zipf_s, perm_seed=w.seed)
     top = np.argsort(-lg, axis=1, kind="stable")[:, :w.k]
     counts = np.bincount(top.ravel(), minlength=w.E)
     ranked = np.lexsort((np.arange(w.E), -counts))

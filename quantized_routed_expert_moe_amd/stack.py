@@ -1,0 +1,218 @@
+"""A stack of MoE layers under partial residency, replayed as one HIP graph,
+with expert swaps between replays.
+
+Each layer keeps some of its routed experts in HBM slots and routes the rest
+to a host list (bloomery README of 2026-09-24, opening list: each routed
+layer keeps some of its experts on the GPU, the rest run on the host tier
+inside the same captured step; bloomery V4.1 README, "Adaptive residency":
+experts are swapped between the card and the host between steps).
+
+Orchestration only; every computation is a libqmoe call:
+  * per layer: an HBM slot pool of S = resident + staging slots, a slot map
+    (expert -> slot, -1 = host), a shared expert, the layer's buffers;
+  * capture(): all layers back to back on one stream into one graph, each
+    layer followed by the D2H copy of its host list into pinned memory;
+  * swap(): for every layer, copy the packed blobs of `n` incoming experts
+    from pinned host memory into free slots with hipMemcpyAsync on a side
+    stream (overlapping the running replay: free slots are not in the
+    current map), then, once the replay has finished, upload the new slot
+    maps; the next replay waits for that.
+
+Swap rule (the pages only say experts are swapped between steps): the
+incoming experts are the next `n` non-resident ones in the layer's frequency
+ranking after a cursor that starts at the first non-resident rank and wraps;
+the outgoing ones are the `n` lowest-ranked resident experts.  Incoming
+experts take the free slots (at first the staging slots, then the slots the
+previous round freed).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import MOE_FMT_Q4K, MOE_PATH_DECODE, moe_validate_slot_map
+from .layer import LayerSpec, MoELayer
+
+
+class ResidentStack:
+    def __init__(self, spec: LayerSpec, n_layers: int, T: int, n_resident: int, n_staging: int,
+                 ranked: list, blob_of, host_blobs: torch.Tensor, dev_blobs: torch.Tensor | None,
+                 shared_of, shared_host: torch.Tensor):
+        """ranked[l]: experts of layer l by descending routing frequency (rank r
+        resident in slot r at start).  blob_of(l, e): row of host_blobs (packed,
+        pinned, [n_blobs, stride]) holding expert e of layer l.  dev_blobs: the
+        same rows on the device (used to fill the pools quickly; may be None).
+        shared_of(l): row of shared_host (packed Q8_0 blobs) for layer l."""
+        assert spec.fmt == MOE_FMT_Q4K
+        self.spec, self.L, self.T = spec, n_layers, T
+        self.nres, self.nstage = n_resident, n_staging
+        self.S = n_resident + n_staging
+        self.ranked = [np.asarray(r, dtype=np.int64) for r in ranked]
+        self.blob_of, self.host_blobs = blob_of, host_blobs
+        self.stride = host_blobs.shape[1]
+        E = spec.E
+        dev = "cuda"
+        self.maps = []            # host slot maps (np.int32 [E]) of the next replay
+        self.free = []            # free slots per layer
+        self.cursor = []          # swap cursor into ranked[l]
+        self.pools, self.dev_maps, self.layers = [], [], []
+        self.x, self.logits = [], []
+        self.pin_host = []        # per layer pinned (token, expert, weight, count)
+        src = dev_blobs if dev_blobs is not None else host_blobs
+        for l in range(n_layers):
+            soe = np.full(E, -1, dtype=np.int32)
+            soe[self.ranked[l][:n_resident]] = np.arange(n_resident, dtype=np.int32)
+            self.maps.append(soe)
+            self.free.append(list(range(n_resident, self.S)))
+            self.cursor.append(n_resident)
+            pool = torch.empty((self.S, self.stride), dtype=torch.uint8, device=dev)
+            self.pools.append(pool)
+            self.dev_maps.append(torch.from_numpy(soe.copy()).to(dev))
+        # fill resident slots, grouped by source blob so each source stays hot in cache
+        jobs = []
+        for l in range(n_layers):
+            for s in range(n_resident):
+                jobs.append((self.blob_of(l, int(self.ranked[l][s])), l, s))
+        jobs.sort()
+        for b, l, s in jobs:
+            self.pools[l][s].copy_(src[b], non_blocking=True)
+        self.shared_pools = []
+        for l in range(n_layers):
+            sp = torch.empty((1, shared_host.shape[1]), dtype=torch.uint8, device=dev)
+            sp[0].copy_(shared_host[shared_of(l)], non_blocking=True)
+            self.shared_pools.append(sp)
+        torch.cuda.synchronize()
+        for l in range(n_layers):
+            self.layers.append(MoELayer(spec, T, self.S, self.pools[l], self.stride, self.dev_maps[l],
+                                        self.shared_pools[l], MOE_PATH_DECODE))
+            self.x.append(torch.zeros((T, spec.H), dtype=torch.float32, device=dev))
+            self.logits.append(torch.zeros((T, E), dtype=torch.float32, device=dev))
+            P = T * spec.k
+            self.pin_host.append(dict(
+                token=torch.zeros(P, dtype=torch.int32).pin_memory(),
+                expert=torch.zeros(P, dtype=torch.int32).pin_memory(),
+                weight=torch.zeros(P, dtype=torch.float32).pin_memory(),
+                count=torch.zeros(1, dtype=torch.int32).pin_memory()))
+        self.pin_maps = [torch.zeros(E, dtype=torch.int32).pin_memory() for _ in range(n_layers)]
+        self.graph = None
+        self.side = torch.cuda.Stream()
+        self.replay_done = torch.cuda.Event(enable_timing=True)
+        self.replay_start = torch.cuda.Event(enable_timing=True)
+        self.swap_start = torch.cuda.Event(enable_timing=True)
+        self.swap_copies_done = torch.cuda.Event(enable_timing=True)
+        self.maps_done = torch.cuda.Event(enable_timing=True)
+        self.pending_maps = False
+
+    # ------------------------------------------------------------ step
+    def set_inputs(self, xs, logits) -> None:
+        for l in range(self.L):
+            self.x[l].copy_(xs[l])
+            self.logits[l].copy_(logits[l])
+
+    def _step_body(self) -> None:
+        for l in range(self.L):
+            lay = self.layers[l]
+            lay.forward(self.x[l], self.logits[l])
+            h = self.pin_host[l]
+            h["token"].copy_(lay.host_token, non_blocking=True)
+            h["expert"].copy_(lay.host_expert, non_blocking=True)
+            h["weight"].copy_(lay.host_weight, non_blocking=True)
+            h["count"].copy_(lay.host_count, non_blocking=True)
+
+    def run_eager(self) -> None:
+        self._wait_maps()
+        self._step_body()
+        self.replay_done.record()
+
+    def capture(self) -> torch.cuda.CUDAGraph:
+        self._step_body()  # warm-up outside capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph(keep_graph=True)
+        with torch.cuda.graph(g):
+            self._step_body()
+        g.instantiate()
+        self.graph = g
+        return g
+
+    def graph_node_count(self) -> int:
+        import ctypes
+        hip = ctypes.CDLL("libamdhip64.so")
+        n = ctypes.c_size_t(0)
+        rc = hip.hipGraphGetNodes(ctypes.c_void_p(self.graph.raw_cuda_graph()), None, ctypes.byref(n))
+        if rc != 0:
+            raise RuntimeError(f"hipGraphGetNodes failed ({rc})")
+        return int(n.value)
+
+    def _wait_maps(self) -> None:
+        if self.pending_maps:
+            torch.cuda.current_stream().wait_event(self.maps_done)
+            self.pending_maps = False
+
+    def replay(self) -> None:
+        self._wait_maps()
+        self.replay_start.record()
+        self.graph.replay()
+        self.replay_done.record()
+
+    def outputs(self) -> list:
+        return [lay.y for lay in self.layers]
+
+    def host_lists(self, l: int) -> dict:
+        h = self.pin_host[l]
+        c = int(h["count"][0])
+        return dict(token=h["token"][:c].numpy().copy(), expert=h["expert"][:c].numpy().copy(),
+                    weight=h["weight"][:c].numpy().copy())
+
+    # ------------------------------------------------------------ swaps
+    def plan_swap(self, l: int, n: int) -> tuple[list, list]:
+        """(incoming experts, outgoing experts) of layer l for the next round."""
+        soe, ranked, E = self.maps[l], self.ranked[l], self.spec.E
+        incoming, c = [], self.cursor[l]
+        for _ in range(E):
+            e = int(ranked[c % E])
+            c += 1
+            if soe[e] < 0:
+                incoming.append(e)
+                if len(incoming) == n:
+                    break
+        self.cursor[l] = c % E
+        rank_of = np.empty(E, dtype=np.int64)
+        rank_of[ranked] = np.arange(E)
+        resident = [int(e) for e in np.nonzero(soe >= 0)[0]]
+        resident.sort(key=lambda e: -rank_of[e])
+        outgoing = resident[:n]
+        return incoming, outgoing
+
+    def swap(self, n: int = 8) -> dict:
+        """One swap round on every layer: copies on the side stream overlap the
+        replay in flight; the new slot maps are uploaded after it finishes."""
+        plans = []
+        side = self.side
+        side.synchronize()  # the previous round's copies and map uploads are complete
+        self.swap_start.record(side)
+        with torch.cuda.stream(side):
+            for l in range(self.L):
+                inc, out = self.plan_swap(l, n)
+                assert len(self.free[l]) >= len(inc)
+                slots = [self.free[l].pop(0) for _ in inc]
+                for e, s in zip(inc, slots):
+                    self.pools[l][s].copy_(self.host_blobs[self.blob_of(l, e)], non_blocking=True)
+                plans.append((inc, out, slots))
+            self.swap_copies_done.record(side)
+            side.wait_event(self.replay_done)  # the running replay still reads the old maps
+            for l, (inc, out, slots) in enumerate(plans):
+                soe = self.maps[l]
+                for e, s in zip(inc, slots):
+                    soe[e] = s
+                for e in out:
+                    self.free[l].append(int(soe[e]))
+                    soe[e] = -1
+                moe_validate_slot_map(soe, self.S)
+                self.pin_maps[l].copy_(torch.from_numpy(soe))
+                self.dev_maps[l].copy_(self.pin_maps[l], non_blocking=True)
+            self.maps_done.record(side)
+        self.pending_maps = True
+        return dict(incoming=[p[0] for p in plans], outgoing=[p[1] for p in plans])
+
+    def current_maps(self) -> list:
+        return [m.copy() for m in self.maps]
