@@ -315,8 +315,8 @@ moe_status moe_route_topk(const float* logits, int T, int E, int k, int score, i
 }
 
 size_t moe_batches_workspace_size(int T, int k, int E, int S) {
-    (void)T; (void)k; (void)E; (void)S;
-    return 0;
+    if (T < 0 || k < 1 || E < 1 || S < 0 || S > E || E > MOE_MAX_EXPERTS) return 0;
+    return qmoe::batches_workspace_bytes(T, k, S);
 }
 
 moe_status moe_build_expert_batches(const int32_t* topk_ids, const float* topk_w, int T, int k, int E,
@@ -324,7 +324,6 @@ moe_status moe_build_expert_batches(const int32_t* topk_ids, const float* topk_w
                                     int32_t* active_slots, int32_t* num_active, int32_t* perm_pair,
                                     int32_t* host_token, int32_t* host_expert, float* host_weight,
                                     int32_t* host_count, void* ws, size_t ws_bytes, void* stream) {
-    (void)ws;
     moe_status st = check_route_shape(T, E, k);
     if (st != MOE_OK) return st;
     if (S < 0 || S > E) return fail(MOE_ERR_INVALID_ARGUMENT, "S = %d outside 0..E (%d)", S, E);
@@ -333,10 +332,12 @@ moe_status moe_build_expert_batches(const int32_t* topk_ids, const float* topk_w
     if (T > 0 && (!topk_ids || !topk_w || !perm_pair || !host_token || !host_expert || !host_weight ||
                   (S > 0 && !active_slots)))
         return fail(MOE_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
-    if (ws_bytes < moe_batches_workspace_size(T, k, E, S))
-        return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "batches workspace too small");
+    const size_t need = moe_batches_workspace_size(T, k, E, S);
+    if (ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "batches workspace %zu bytes, %zu needed", ws_bytes, need);
+    if (need > 0 && !ws) return fail(MOE_ERR_INVALID_ARGUMENT, "batches workspace pointer is NULL");
     hipError_t e = qmoe::launch_batches(topk_ids, topk_w, T, k, E, slot_of_expert, S, slot_offsets, active_slots,
-                                        num_active, perm_pair, host_token, host_expert, host_weight, host_count,
+                                        num_active, perm_pair, host_token, host_expert, host_weight, host_count, ws,
                                         (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "batches launch");
     return MOE_OK;

@@ -3,7 +3,12 @@
 // prompts"; pairs whose expert is not on the card go to the host tier:
 // bloomery README of 2026-09-24, opening list).
 //
-// One workgroup of 8 waves.  Bucket b of pair p is its slot, or S for "not
+// Up to kSingleMaxPairs pairs: one workgroup of 8 waves (below).  Above:
+// three launches over 1024-pair blocks -- per-block bucket counts, one
+// workgroup scanning (bucket, block) counts into starting positions, and a
+// per-block stable scatter -- with the same in-wave ranking.
+//
+// Single workgroup: 8 waves.  Bucket b of pair p is its slot, or S for "not
 // resident".  Wave w owns a contiguous run of pairs, walked in 64-pair steps.
 // Inside a step, lanes with equal buckets are found with one ballot per
 // bucket bit (a deterministic match), which gives each lane its rank among
@@ -138,16 +143,167 @@ __global__ __launch_bounds__(512) void batches_kernel(const int32_t* __restrict_
     }
 }
 
+// ------------------------------------------------------------- multi-block
+
+constexpr int kSingleMaxPairs = 8192;
+constexpr int kBlockPairs = 1024;  // pairs per block: 4 waves x 256
+constexpr int kMbWaves = 4;
+
+size_t batches_workspace_bytes(int T, int k, int S) {
+    const long P = (long)T * k;
+    if (P <= kSingleMaxPairs) return 0;
+    const long nblk = (P + kBlockPairs - 1) / kBlockPairs;
+    return (size_t)((nblk * (S + 1) * 4 + 255) & ~255L);
+}
+
+// Per-wave bucket counts of this block's pairs into wcnt[wave][bucket].
+__device__ __forceinline__ void block_wave_counts(const int32_t* __restrict__ ids, const int32_t* __restrict__ soe,
+                                                  int P, int E, int S, int nbits, int* wcnt) {
+    const int NB = S + 1;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    for (int i = tid; i < kMbWaves * NB; i += blockDim.x) wcnt[i] = 0;
+    __syncthreads();
+    const int begin = blockIdx.x * kBlockPairs + wave * (kBlockPairs / kMbWaves);
+    const int end = min(P, begin + kBlockPairs / kMbWaves);
+    for (int base = begin; base < end; base += 64) {
+        const int p = base + lane;
+        const bool valid = p < end;
+        const int b = valid ? bucket_of(ids, soe, p, E, S) : 0;
+        const unsigned long long m = match_bucket(b, valid, nbits);
+        if (valid && (m & lt) == 0ull) wcnt[wave * NB + b] += __popcll(m);
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void batches_count_kernel(const int32_t* __restrict__ ids,
+                                                            const int32_t* __restrict__ soe, int P, int E, int S,
+                                                            int nbits, int32_t* __restrict__ gcnt) {
+    extern __shared__ int wcnt[];
+    block_wave_counts(ids, soe, P, E, S, nbits, wcnt);
+    const int NB = S + 1;
+    for (int b = threadIdx.x; b < NB; b += blockDim.x) {
+        int c = 0;
+        for (int w = 0; w < kMbWaves; ++w) c += wcnt[w * NB + b];
+        gcnt[(size_t)blockIdx.x * NB + b] = c;
+    }
+}
+
+// gcnt[blk][b] -> first output position of block blk's pairs in bucket b
+// (slot buckets: into perm_pair; bucket S: into the host list).
+__global__ __launch_bounds__(1024) void batches_scan_kernel(int nblk, int S, int32_t* __restrict__ gcnt,
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ active,
+                                                            int32_t* __restrict__ num_active,
+                                                            int32_t* __restrict__ host_count) {
+    __shared__ int start[kMaxExpertsInternal + 1];
+    const int NB = S + 1;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    for (int b = tid; b < NB; b += blockDim.x) {
+        int run = 0;
+        for (int blk = 0; blk < nblk; ++blk) {
+            const int c = gcnt[(size_t)blk * NB + b];
+            gcnt[(size_t)blk * NB + b] = run;
+            run += c;
+        }
+        start[b] = run;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        int carry = 0, acarry = 0;
+        for (int c0 = 0; c0 < S; c0 += 64) {
+            const int b = c0 + lane;
+            const int c = b < S ? start[b] : 0;
+            const int inc = wave_inclusive_scan(c, lane);
+            const int f = c > 0 ? 1 : 0;
+            const int finc = wave_inclusive_scan(f, lane);
+            if (b < S) {
+                offsets[b] = carry + inc - c;
+                start[b] = carry + inc - c;
+                if (f) active[acarry + finc - f] = b;
+            }
+            carry += __shfl(inc, 63, 64);
+            acarry += __shfl(finc, 63, 64);
+        }
+        if (lane == 0) {
+            offsets[S] = carry;
+            *num_active = acarry;
+            *host_count = start[S];
+            start[S] = 0;
+        }
+    }
+    __syncthreads();
+    for (int b = tid; b < NB; b += blockDim.x)
+        for (int blk = 0; blk < nblk; ++blk) gcnt[(size_t)blk * NB + b] += start[b];
+}
+
+__global__ __launch_bounds__(256) void batches_scatter_kernel(const int32_t* __restrict__ ids,
+                                                              const float* __restrict__ w, int T, int k, int E,
+                                                              const int32_t* __restrict__ soe, int S, int nbits,
+                                                              const int32_t* __restrict__ gcnt,
+                                                              int32_t* __restrict__ perm,
+                                                              int32_t* __restrict__ host_token,
+                                                              int32_t* __restrict__ host_expert,
+                                                              float* __restrict__ host_weight) {
+    extern __shared__ int wcnt[];
+    const int P = T * k;
+    block_wave_counts(ids, soe, P, E, S, nbits, wcnt);
+    const int NB = S + 1;
+    // this block's start per bucket + exclusive prefix over its waves
+    for (int b = threadIdx.x; b < NB; b += blockDim.x) {
+        int run = gcnt[(size_t)blockIdx.x * NB + b];
+        for (int wv = 0; wv < kMbWaves; ++wv) {
+            const int c = wcnt[wv * NB + b];
+            wcnt[wv * NB + b] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    const int begin = blockIdx.x * kBlockPairs + wave * (kBlockPairs / kMbWaves);
+    const int end = min(P, begin + kBlockPairs / kMbWaves);
+    for (int base = begin; base < end; base += 64) {
+        const int p = base + lane;
+        const bool valid = p < end;
+        const int b = valid ? bucket_of(ids, soe, p, E, S) : 0;
+        const unsigned long long m = match_bucket(b, valid, nbits);
+        if (valid) {
+            const int pos = wcnt[wave * NB + b] + __popcll(m & lt);
+            if (b < S) {
+                perm[pos] = p;
+            } else {
+                host_token[pos] = p / k;
+                host_expert[pos] = ids[p];
+                host_weight[pos] = w[p];
+            }
+        }
+        if (valid && (m & lt) == 0ull) wcnt[wave * NB + b] += __popcll(m);
+    }
+}
+
 hipError_t launch_batches(const int32_t* ids, const float* w, int T, int k, int E, const int32_t* soe, int S,
                           int32_t* offsets, int32_t* active, int32_t* num_active, int32_t* perm,
                           int32_t* host_token, int32_t* host_expert, float* host_weight, int32_t* host_count,
-                          hipStream_t s) {
+                          void* ws, hipStream_t s) {
     int nbits = 1;
     while ((1 << nbits) <= S) ++nbits;  // buckets 0..S
-    const size_t lds = (size_t)(kBatchWaves + 1) * (S + 1) * sizeof(int);
+    const long P = (long)T * k;
     timer_before(kStageBatches, s);
-    hipLaunchKernelGGL(batches_kernel, dim3(1), dim3(64 * kBatchWaves), lds, s, ids, w, T, k, E, soe, S, nbits,
-                       offsets, active, num_active, perm, host_token, host_expert, host_weight, host_count);
+    if (P <= kSingleMaxPairs) {
+        const size_t lds = (size_t)(kBatchWaves + 1) * (S + 1) * sizeof(int);
+        hipLaunchKernelGGL(batches_kernel, dim3(1), dim3(64 * kBatchWaves), lds, s, ids, w, T, k, E, soe, S, nbits,
+                           offsets, active, num_active, perm, host_token, host_expert, host_weight, host_count);
+    } else {
+        const int nblk = (int)((P + kBlockPairs - 1) / kBlockPairs);
+        int32_t* gcnt = static_cast<int32_t*>(ws);
+        const size_t lds = (size_t)kMbWaves * (S + 1) * sizeof(int);
+        hipLaunchKernelGGL(batches_count_kernel, dim3(nblk), dim3(256), lds, s, ids, soe, (int)P, E, S, nbits, gcnt);
+        hipLaunchKernelGGL(batches_scan_kernel, dim3(1), dim3(1024), 0, s, nblk, S, gcnt, offsets, active, num_active,
+                           host_count);
+        hipLaunchKernelGGL(batches_scatter_kernel, dim3(nblk), dim3(256), lds, s, ids, w, T, k, E, soe, S, nbits,
+                           (const int32_t*)gcnt, perm, host_token, host_expert, host_weight);
+    }
     timer_after(kStageBatches, s);
     return hipGetLastError();
 }

@@ -96,9 +96,11 @@ def _batches_device(ids, w, E, soe, S):
                host_token=torch.full((max(1, P),), -5, **i32), host_expert=torch.full((max(1, P),), -5, **i32),
                host_weight=torch.full((max(1, P),), -5.0, dtype=torch.float32, device="cuda"),
                host_count=torch.full((1,), -5, **i32))
+    wsb = Q.moe_batches_workspace_size(T, k, E, S)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda") if wsb else None
     Q.moe_build_expert_batches(dev(ids.astype(np.int32)), dev(w.astype(np.float32)), E, dev(soe), S,
                                out["slot_offsets"], out["active_slots"], out["num_active"], out["perm_pair"],
-                               out["host_token"], out["host_expert"], out["host_weight"], out["host_count"])
+                               out["host_token"], out["host_expert"], out["host_weight"], out["host_count"], ws)
     torch.cuda.synchronize()
     o = {key: v.cpu().numpy() for key, v in out.items()}
     na, nres, hc = int(o["num_active"][0]), int(o["slot_offsets"][S]), int(o["host_count"][0])
@@ -148,6 +150,11 @@ def test_batches_stack_residency():
         want = O.batches(ids, w, wl.E, soe, S)
         for key in ("slot_offsets", "active_slots", "perm_pair", "host_token", "host_expert"):
             assert np.array_equal(got[key], want[key]), key
+
+
+def test_batches_workspace_required_for_large_batches():
+    assert Q.moe_batches_workspace_size(64, 8, 128, 128) == 0
+    assert Q.moe_batches_workspace_size(4096, 8, 128, 128) > 0
 
 
 def test_batches_empty():
