@@ -91,18 +91,21 @@ void q4k_set_subblock(uint8_t* blk, int j, const uint8_t* q) {
         else qs[l] = (uint8_t)((qs[l] & 0x0F) | (q[l] << 4));
     }
 }
-// 32 quants -> 16 packed bytes: element 8d+n in nibble n of little-endian dword d.
+// 32 quants -> 16 packed bytes: element 8d+n in nibble n of the little-endian
+// dword of group d, groups stored in the order 0, 2, 1, 3 (so the two groups
+// one MFMA operand lane needs for a 32-wide sub-block are adjacent).
+constexpr int kDwordSlot[4] = {0, 2, 1, 3};
 void nibbles_pack(const uint8_t* q, uint8_t* dst) {
     for (int d = 0; d < 4; ++d) {
         uint32_t w = 0;
         for (int n = 0; n < 8; ++n) w |= (uint32_t)(q[8 * d + n] & 15) << (4 * n);
-        memcpy(dst + 4 * d, &w, 4);
+        memcpy(dst + 4 * kDwordSlot[d], &w, 4);
     }
 }
 void nibbles_unpack(const uint8_t* src, uint8_t* q) {
     for (int d = 0; d < 4; ++d) {
         uint32_t w;
-        memcpy(&w, src + 4 * d, 4);
+        memcpy(&w, src + 4 * kDwordSlot[d], 4);
         for (int n = 0; n < 8; ++n) q[8 * d + n] = (uint8_t)((w >> (4 * n)) & 15);
     }
 }

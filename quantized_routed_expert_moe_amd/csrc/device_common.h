@@ -45,4 +45,23 @@ __device__ __forceinline__ float half_wave_sum(float v) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// d*sc_j and dmin*m_j of the eight sub-blocks of a Q4_K super-block header
+// (16 bytes: d, dmin, then the 12 packed scale bytes).
+__device__ __forceinline__ void q4k_header(const uint4 h, float* ds, float* dm) {
+    const float d = half_to_float(h.x);
+    const float dmin = half_to_float(h.x >> 16);
+    const uint32_t a = h.y, b = h.z, c = h.w;
+    const uint32_t sc_lo = a & 0x3F3F3F3Fu;
+    const uint32_t m_lo = b & 0x3F3F3F3Fu;
+    const uint32_t sc_hi = (c & 0x0F0F0F0Fu) | ((a >> 2) & 0x30303030u);
+    const uint32_t m_hi = ((c >> 4) & 0x0F0F0F0Fu) | ((b >> 2) & 0x30303030u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        ds[j] = d * (float)((sc_lo >> (8 * j)) & 0xFFu);
+        dm[j] = dmin * (float)((m_lo >> (8 * j)) & 0xFFu);
+        ds[j + 4] = d * (float)((sc_hi >> (8 * j)) & 0xFFu);
+        dm[j + 4] = dmin * (float)((m_hi >> (8 * j)) & 0xFFu);
+    }
+}
+
 }  // namespace qmoe

@@ -122,10 +122,10 @@ __global__ __launch_bounds__(256) void prep_kernel(const void* __restrict__ x, i
 // ------------------------------------------------------- block dot products
 
 // Q4_K: 16 quant bytes of one row and sub-block (element 8d+n in nibble n of
-// dword d) against one activation record.  Returns sum_e (1024 + q_e) x'_e
-// where x' is the record's stored value (x or x/16).
+// group d; groups stored 0, 2, 1, 3) against one activation record.  Returns
+// sum_e (1024 + q_e) x'_e where x' is the record's stored value (x or x/16).
 __device__ __forceinline__ float q4k_dot(const uint4 q, cu32* X) {
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    const uint32_t w[4] = {q.x, q.z, q.y, q.w};
     float acc = 0.0f;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
@@ -149,25 +149,6 @@ __device__ __forceinline__ float q8_dot(const uint4 a, const uint4 b, cu32* X) {
         acc = fdot2u(((w[d] >> 8) & 0x00FF00FFu) | kMagic, X[2 * d + 1], acc);
     }
     return acc;
-}
-
-// d*sc_j and dmin*m_j of the eight sub-blocks of a Q4_K super-block header
-// (16 bytes: d, dmin, then the 12 packed scale bytes).
-__device__ __forceinline__ void q4k_header(const uint4 h, float* ds, float* dm) {
-    const float d = half_to_float(h.x);
-    const float dmin = half_to_float(h.x >> 16);
-    const uint32_t a = h.y, b = h.z, c = h.w;
-    const uint32_t sc_lo = a & 0x3F3F3F3Fu;
-    const uint32_t m_lo = b & 0x3F3F3F3Fu;
-    const uint32_t sc_hi = (c & 0x0F0F0F0Fu) | ((a >> 2) & 0x30303030u);
-    const uint32_t m_hi = ((c >> 4) & 0x0F0F0F0Fu) | ((b >> 2) & 0x30303030u);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        ds[j] = d * (float)((sc_lo >> (8 * j)) & 0xFFu);
-        dm[j] = dmin * (float)((m_lo >> (8 * j)) & 0xFFu);
-        ds[j + 4] = d * (float)((sc_hi >> (8 * j)) & 0xFFu);
-        dm[j + 4] = dmin * (float)((m_hi >> (8 * j)) & 0xFFu);
-    }
 }
 
 __device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }

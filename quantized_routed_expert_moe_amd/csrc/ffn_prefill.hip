@@ -2,34 +2,56 @@
 // batches.  Prompts run "each expert over all its tokens at once" (bloomery
 // V4.1 README, "Batched prompts") as matrix-core GEMMs (bloomery README
 // 0.3.1, "Why it is fast": Qwen prompts as tensor-core GEMMs).  On gfx950 the
-// contraction is bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32 accumulate); the
-// Q4_K weights are dequantized tile by tile into LDS as bf16.
+// contraction is bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32 accumulate) over
+// Q4_K weights dequantized to bf16 on the fly.
 //
-//   tiles kernel  one workgroup lists the (slot, first position, rows) of
-//                 every 128-row M tile of every active slot.
-//   gate/up GEMM  workgroup = one 128-row M tile x 128 intermediate features:
-//                 the gate and up rows of two packed tiles (N = 256), K = H.
-//                 Epilogue h = silu(g) * u, rounded to bf16, stored at the
-//                 pair's position q.
+//   tiles kernel  lists the (slot, first position, rows, 32-row blocks) of
+//                 every M tile (up to 256 rows of one slot), tiles with more
+//                 row blocks first.
+//   gate/up GEMM  workgroup = one M tile x 128 intermediate features; each
+//                 wave owns 32 features and computes both their gate and up
+//                 rows (2 x 32 columns), K = H.  Epilogue h = silu(g) * u,
+//                 rounded to bf16, stored at the pair's position q.
 //   down GEMM     workgroup = one M tile x 256 output features (four packed
-//                 64-row tiles), K = I, A = h rows (contiguous in q).  The
-//                 result row of position q goes to pair perm_pair[q].
+//                 64-row tiles, one per wave), K = I, A = h rows (contiguous
+//                 in q).  The result row of position q goes to pair
+//                 perm_pair[q].
 //
-// Eight waves; each owns 64 rows x 64 columns of the tile as 2 x 2 blocks of
-// v_mfma_f32_32x32x16_bf16 (operand lanes: row/column = lane % 32,
-// k = 8*(lane/32)..+8; result lane l, register r: row 8*(r/4) + 4*(l/32) +
-// r%4, column l % 32).  K advances 64 at a time (two 32-weight sub-blocks of
-// one super-block).  Global loads run two stages ahead (register double
-// buffer); LDS is double buffered.  Dequantizing the B tile costs about as
-// many VALU cycles as the tile's MFMAs take on the matrix pipe, so the two
-// are interleaved inside every wave: each group of four MFMAs of the current
-// stage is followed by the dequantization (w = d*sc*q - dmin*m in fp32,
-// rounded to bf16) of one eighth of this thread's weights of the next stage,
-// which issue while the MFMAs execute.  The stage body is branch-free so the
-// scheduler keeps that order.
-// Workgroups are numbered so that the N tiles of one M tile, and
-// consecutive M tiles of one slot, run on the same XCD (its L2 keeps the
-// shared A rows and weight tiles).
+// Four waves, one per SIMD, each owning all 256 rows of the tile times its
+// 64 columns: 8 x 2 blocks of v_mfma_f32_32x32x16_bf16 with the 256
+// accumulator registers in AGPRs.  Dequantizing a weight costs VALU issue
+// slots on the SIMD that also issues the MFMAs, so the tile height is what
+// amortizes it: each dequantized weight feeds 8 MFMA row blocks.
+//
+// Operand placement.  A 32x32x16 B-operand lane holds one column (a weight
+// row) and 8 consecutive K values, exactly one 32-bit group of 8 packed
+// nibbles; the packed layout stores the two groups a lane needs for a
+// sub-block's two k16 steps next to each other.  So each wave loads its own
+// weight rows' quants straight into registers (8 bytes per lane per
+// sub-block) and dequantizes them into B fragments: the weights never pass
+// through LDS and each is dequantized exactly once per M tile.  A nibble q
+// held in a byte of its own is the fp8 (e4m3) code of q / 512, so one
+// v_cvt_pk_f32_fp8 turns two nibbles into floats; w = (512 d sc) (q / 512) -
+// dmin m is then one fma with a single rounding, and one v_cvt_pk_bf16_f32
+// rounds a pair to bf16.
+// The A tile is shared by the four waves through LDS, written by
+// global_load_lds_dwordx4 (no register staging).  One DMA instruction moves
+// 8 rows x 128 bytes (whole cache lines): lane l takes row l / 8 of the
+// group and 16-byte chunk (l % 8) xor (l / 8) of the half stage, and lands at
+// 16 l of the group's 1 KB block.  The xor swizzle makes the MFMA fragment
+// reads (32 rows, one chunk each) hit 8 distinct bank groups per 8 lanes:
+// conflict-free ds_read_b128.
+//
+// Pipeline: K advances 128 per stage (four 32-weight sub-blocks, half a
+// super-block), one barrier per stage.  During stage t the DMA of stage
+// t + 1's A rows and the loads of its quants are in flight; they are waited
+// for at the end of the stage.  Inside a stage the A fragments and B
+// dequantization of k16 step s + 1 are issued between the MFMAs of step s.
+// Row blocks past the tile's rows are neither loaded nor multiplied (the
+// kernel body is instantiated per row-block count).
+// Workgroup numbering: the N tiles of one M tile run on one XCD (hardware:
+// XCD = workgroup id mod 8), consecutive M tiles on consecutive XCDs, so the
+// L2 of an XCD serves the A rows shared by its N tiles.
 #include "device_common.h"
 #include "qmoe_internal.h"
 
@@ -38,15 +60,21 @@ namespace qmoe {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBM = 128;        // rows (pair positions) per M tile
-constexpr int kBN = 256;        // columns per workgroup
-constexpr int kThreads = 512;   // eight waves
-constexpr int kBK = 64;         // K per pipeline stage
-constexpr int kLda = kBK + 8;   // LDS row stride in bf16 (16-byte pad against bank conflicts)
+constexpr int kBM = 256;                   // rows (pair positions) per M tile
+constexpr int kRowBlocks = kBM / 32;       // 32-row MFMA blocks per tile
+constexpr int kWaves = 4;                  // waves per workgroup, one per SIMD
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBK = 128;                   // K per pipeline stage
+constexpr int kK16 = kBK / 16;             // k16 steps per stage
+constexpr int kGateUpFeatures = 32 * kWaves;  // intermediate features per gate/up workgroup
+constexpr int kDownColumns = 64 * kWaves;     // output features per down workgroup
+constexpr int kStageLdsFrags = kK16 * kRowBlocks;  // 1 KB A fragments per stage buffer
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Upper bound of the tile count: sum over slots of ceil(n_s / 256).
 static int max_tiles(int P, int S) { return (P + kBM - 1) / kBM + std::min(S, P); }
 
 size_t prefill_workspace_bytes(int T, int k, int H, int I) {
@@ -57,142 +85,386 @@ size_t prefill_workspace_bytes(int T, int k, int H, int I) {
 
 // ---------------------------------------------------------------- tiles
 
-__global__ __launch_bounds__(256) void prefill_tiles_kernel(const int32_t* __restrict__ offsets,
-                                                            const int32_t* __restrict__ active,
-                                                            const int32_t* __restrict__ num_active, int S, int P,
-                                                            int4* __restrict__ tiles, int32_t* __restrict__ ntiles) {
-    __shared__ int base[kMaxExpertsInternal + 1];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int na = min(*num_active, min(S, P));
-    if (tid < 64) {
-        int carry = 0;
-        for (int a0 = 0; a0 < na; a0 += 64) {
-            const int a = a0 + lane;
-            int c = 0;
-            if (a < na) {
-                const int s = active[a];
-                const int n = (s >= 0 && s < S) ? offsets[s + 1] - offsets[s] : 0;
-                c = n > 0 ? (n + kBM - 1) / kBM : 0;
-            }
-            int v = c;
+// Exclusive prefix sum over the 1024 threads' values; returns the total.
+__device__ __forceinline__ int block_exclusive_scan_1024(int v, int* part, int* out_total) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int incl = v;
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int t = __shfl_up(v, off, 64);
-                if (lane >= off) v += t;
-            }
-            if (a < na) base[a] = carry + v - c;
-            carry += __shfl(v, 63, 64);
+    for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += t;
+    }
+    if (lane == 63) part[wave] = incl;
+    __syncthreads();
+    if (tid < 16) {
+        int w = part[tid], wi = w;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            const int t = __shfl_up(wi, off, 16);
+            if ((tid & 15) >= off) wi += t;
         }
-        if (lane == 0) base[na] = carry;
+        part[16 + tid] = wi - w;
+        if (tid == 15) *out_total = wi;
     }
     __syncthreads();
-    for (int a = tid; a < na; a += blockDim.x) {
-        const int s = active[a];
-        if (s < 0 || s >= S) continue;
-        const int q0 = offsets[s], n = offsets[s + 1] - q0;
-        for (int t = 0; t * kBM < n; ++t) tiles[base[a] + t] = make_int4(s, q0 + t * kBM, min(kBM, n - t * kBM), 0);
+    const int r = part[16 + wave] + incl - v;
+    __syncthreads();
+    return r;
+}
+
+// One workgroup of 1024 threads, one active slot per thread.  Tiles are
+// grouped by row-block count, largest first (bucket 8 holds the full tiles),
+// and within a bucket ordered by slot.
+__global__ __launch_bounds__(1024) void prefill_tiles_kernel(const int32_t* __restrict__ offsets,
+                                                             const int32_t* __restrict__ active,
+                                                             const int32_t* __restrict__ num_active, int S, int P,
+                                                             int4* __restrict__ tiles, int32_t* __restrict__ ntiles) {
+    __shared__ int part[32];
+    __shared__ int total;
+    const int tid = threadIdx.x;
+    const int na = min(*num_active, min(S, P));
+    int slot = -1, q0 = 0, n = 0;
+    if (tid < na) {
+        const int s = active[tid];
+        if (s >= 0 && s < S) {
+            slot = s;
+            q0 = offsets[s];
+            n = offsets[s + 1] - q0;
+        }
     }
-    if (tid == 0) *ntiles = base[na];
+    const int full = n / kBM, rem = n - full * kBM;
+    const int pblocks = (rem + 31) / 32;  // row blocks of the partial tile (0: none)
+    int base = 0;
+    for (int b = kRowBlocks; b >= 1; --b) {
+        const int c = (b == kRowBlocks ? full : 0) + (pblocks == b ? 1 : 0);
+        const int pos = base + block_exclusive_scan_1024(c, part, &total);
+        if (c > 0) {
+            int t = 0;
+            if (b == kRowBlocks)
+                for (; t < full; ++t) tiles[pos + t] = make_int4(slot, q0 + t * kBM, kBM, kRowBlocks);
+            if (pblocks == b) tiles[pos + t] = make_int4(slot, q0 + full * kBM, rem, b);
+        }
+        __syncthreads();
+        base += total;
+        __syncthreads();
+    }
+    if (tid == 0) *ntiles = base;
 }
 
 // ------------------------------------------------------------- helpers
 
-__device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+template <typename T> __device__ __forceinline__ T ldg(const void* p) { return *reinterpret_cast<const T*>(p); }
 
-// 6-bit scale and min of sub-block j from the 12 packed bytes (header bytes
-// 4..15), without branches: j < 4 takes the low 6 bits of bytes j / j+4;
-// j >= 4 the nibbles of byte j+4 and the top two bits of bytes j-4 / j.
-__device__ __forceinline__ void q4k_scale_min(const uint4 h, int j, float* dsc, float* dmm) {
-    const float d = half_to_float(h.x), dmin = half_to_float(h.x >> 16);
-    const uint32_t a = h.y, b = h.z, c = h.w;
-    const int s = 8 * (j & 3);
-    const uint32_t sc_lo = (a >> s) & 63u, m_lo = (b >> s) & 63u;
-    const uint32_t sc_hi = ((c >> s) & 15u) | ((((a >> s) >> 6) & 3u) << 4);
-    const uint32_t m_hi = (((c >> s) >> 4) & 15u) | ((((b >> s) >> 6) & 3u) << 4);
-    const bool lo = j < 4;
-    *dsc = d * (float)(lo ? sc_lo : sc_hi);
-    *dmm = dmin * (float)(lo ? m_lo : m_hi);
+// Scale and min words of one Q4_K super-block header (16 bytes: d, dmin,
+// then the 12 packed scale bytes): byte j % 4 of sc[j / 4] is the 6-bit
+// scale of sub-block j, likewise mn for the mins; d512 = 512 d.
+struct HeaderWords {
+    float d512, dmin;
+    uint32_t sc[2], mn[2];
+};
+
+__device__ __forceinline__ HeaderWords header_words(const uint4 h) {
+    HeaderWords w;
+    w.d512 = half_to_float(h.x) * 512.0f;
+    w.dmin = half_to_float(h.x >> 16);
+    w.sc[0] = h.y & 0x3F3F3F3Fu;
+    w.mn[0] = h.z & 0x3F3F3F3Fu;
+    w.sc[1] = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
+    w.mn[1] = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
+    return w;
 }
 
-// Quants 8d..8d+7 of a 32-weight sub-block (dword d of its 16 packed bytes)
-// -> eight bf16 d*sc*q - dmin*m as one 16-byte LDS store.
-__device__ __forceinline__ void dequant8_to_lds(uint32_t w, float dsc, float dmm, uint16_t* dst) {
+// Eight nibbles of one packed group (element n in nibble n) -> B fragment of
+// bf16 d*sc*q - dmin*m.  lo holds the even nibbles in its bytes, hi the odd
+// ones; each byte 0..15 is the e4m3 code of q / 512, converted two at a time.
+// ds512 = 512 d sc, so ds512 * (q / 512) is the exact d sc q and the fma
+// rounds once.
+__device__ __forceinline__ bf16x8 dequant_frag(uint32_t w, float ds512, float ndm) {
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    const f32x2 e02 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);  // nibbles 0, 2
+    const f32x2 e46 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);   // nibbles 4, 6
+    const f32x2 e13 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);  // nibbles 1, 3
+    const f32x2 e57 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);   // nibbles 5, 7
+    const float q[8] = {e02[0], e13[0], e02[1], e13[1], e46[0], e57[0], e46[1], e57[1]};
     uint32_t out[4];
 #pragma unroll
-    for (int n = 0; n < 8; n += 2) {
+    for (int b = 0; b < 4; ++b) {
         bf16x2 v;
-        v[0] = (__bf16)fmaf(dsc, (float)((w >> (4 * n)) & 15u), -dmm);
-        v[1] = (__bf16)fmaf(dsc, (float)((w >> (4 * n + 4)) & 15u), -dmm);
-        out[n / 2] = __builtin_bit_cast(uint32_t, v);
+        v[0] = (__bf16)fmaf(ds512, q[2 * b], ndm);
+        v[1] = (__bf16)fmaf(ds512, q[2 * b + 1], ndm);
+        out[b] = __builtin_bit_cast(uint32_t, v);
     }
-    *reinterpret_cast<uint4*>(dst) = make_uint4(out[0], out[1], out[2], out[3]);
+    return __builtin_bit_cast(bf16x8, make_uint4(out[0], out[1], out[2], out[3]));
 }
 
-// 32 quants (element 8d+n in nibble n of dword d) -> bf16 d*sc*q - dmin*m,
-// written as 64 contiguous bytes of an LDS row.
-__device__ __forceinline__ void dequant32_to_lds(const uint4 q, float dsc, float dmm, uint16_t* dst) {
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+// dequant_frag in three pieces, so the work can be spread between MFMAs:
+// (a) nibbles -> floats q / 512, (b) and (c) the fma and bf16 rounding of
+// elements 0-3 and 4-7.
+struct DqPart {
+    float q[8];
+    uint32_t out[4];
+};
+
+__device__ __forceinline__ void dq_a(DqPart& d, uint32_t w) {
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    const f32x2 e02 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
+    const f32x2 e46 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+    const f32x2 e13 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+    const f32x2 e57 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+    d.q[0] = e02[0]; d.q[1] = e13[0]; d.q[2] = e02[1]; d.q[3] = e13[1];
+    d.q[4] = e46[0]; d.q[5] = e57[0]; d.q[6] = e46[1]; d.q[7] = e57[1];
+}
+
+__device__ __forceinline__ void dq_bc(DqPart& d, int half, float ds512, float ndm) {
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        uint32_t out[4];
-#pragma unroll
-        for (int n = 0; n < 8; n += 2) {
-            bf16x2 v;
-            v[0] = (__bf16)fmaf(dsc, (float)((w[d] >> (4 * n)) & 15u), -dmm);
-            v[1] = (__bf16)fmaf(dsc, (float)((w[d] >> (4 * n + 4)) & 15u), -dmm);
-            out[n / 2] = __builtin_bit_cast(uint32_t, v);
-        }
-        reinterpret_cast<uint4*>(dst)[d] = make_uint4(out[0], out[1], out[2], out[3]);
+    for (int b = 2 * half; b < 2 * half + 2; ++b) {
+        bf16x2 v;
+        v[0] = (__bf16)fmaf(ds512, d.q[2 * b], ndm);
+        v[1] = (__bf16)fmaf(ds512, d.q[2 * b + 1], ndm);
+        d.out[b] = __builtin_bit_cast(uint32_t, v);
     }
 }
 
-__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+// silu(z) = z / (1 + e^-z) with the hardware exp2 and reciprocal.
+__device__ __forceinline__ float fast_silu(float z) {
+    return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
 }
+
+// s_waitcnt vmcnt(0), other counters unconstrained (gfx9 encoding).
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // ------------------------------------------------------------- GEMM body
 
-// Logical tile of this workgroup: the G valid workgroups (lowest linear ids)
-// are spread over the 8 XCDs (hardware: XCD = id mod 8) so that XCD x runs
-// the contiguous logical range [start_x, start_x + c_x).  Returns -1 past G.
-__device__ __forceinline__ int xcd_logical_tile(int id, int G) {
-    if (id >= G) return -1;
-    const int x = id & 7, i = id >> 3;
-    const int base = G >> 3, extra = G & 7;
-    const int start = x * base + min(x, extra);
-    return start + i;
-}
-
-// One stage of one thread: 16 bf16 of one A row; the quants of one
-// (B row, sub-block) and the row's super-block header.
-struct PrefetchSlot {
-    uint4 a0, a1;
-    uint4 q, h;
+struct TileCtx {
+    const uint8_t* b_rowgroup;  // first super-block tile of this wave's packed row group
+    int hdr_off[2], q_off[2];   // per block: header / quant byte offsets inside a tile (lane's row)
+    int q_step, tile_bytes;
+    const uint8_t* a_base;      // A matrix
+    uint32_t a_off[kRowBlocks]; // byte offset of this lane's DMA row in row group wave + 4 t, plus its chunk
+    int K;
 };
 
+template <bool GATEUP, int NB>
+__device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* sA1, int wave, int lane,
+                                          f32x16 (&acc)[kRowBlocks][2]) {
+    // Two distinct LDS arrays (not one [2][..] array): the compiler can then
+    // tell the DMA into one buffer from the fragment reads of the other and
+    // does not make those reads wait for the DMA.
+    auto buffer = [&](int b) { return b ? sA1 : sA0; };
+    const int nsb = c.K / 256, nstages = 2 * nsb;
+    struct BQuant { uint2 v[2][4]; };  // [block][sub-block of the stage]
+
+    // DMA unit (row group g = wave + 4 t, half h): 8 rows x 64 K values into
+    // the 1 KB block 2 g + h.  Row groups past the tile's row blocks are
+    // skipped (t < NB).
+    auto dma_unit = [&](int st, int buf, int t) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            __builtin_amdgcn_global_load_lds(c.a_base + c.a_off[t] + st * (kBK * 2) + h * 128,
+                                             buffer(buf) + (2 * (wave + 4 * t) + h) * 64, 16, 0, 0);
+    };
+    auto dma_a = [&](int st, int buf) {
+#pragma unroll
+        for (int t = 0; t < NB; ++t) dma_unit(st, buf, t);
+    };
+    auto load_b_one = [&](int st, BQuant& r, int m, int jj) {
+        const uint8_t* tile = c.b_rowgroup + (size_t)(st >> 1) * c.tile_bytes;
+        r.v[m][jj] = ldg<uint2>(tile + c.q_off[m] + (4 * (st & 1) + jj) * c.q_step);
+    };
+    auto load_b = [&](int st, BQuant& r) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) load_b_one(st, r, m, jj);
+    };
+    auto load_hdr = [&](int sb, uint4* h) {
+        const uint8_t* tile = c.b_rowgroup + (size_t)sb * c.tile_bytes;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) h[m] = ldg<uint4>(tile + c.hdr_off[m]);
+    };
+
+    BQuant rb[2];
+    uint4 hdr[2];
+    load_hdr(0, hdr);
+    dma_a(0, 0);
+    load_b(0, rb[0]);
+    wait_vmem_all();
+    // B fragments of the next stage's first k16 step, dequantized ahead
+    // (during the previous stage's last MFMAs, here for stage 0).
+    bf16x8 fb_next0[2];
+    {
+        HeaderWords hw0[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            hw0[m] = header_words(hdr[m]);
+            fb_next0[m] = dequant_frag(rb[0].v[m][0].x, hw0[m].d512 * (float)(hw0[m].sc[0] & 0xFFu),
+                                       -(hw0[m].dmin * (float)(hw0[m].mn[0] & 0xFFu)));
+        }
+    }
+    __syncthreads();
+
+    int sb = 0;
+    do {
+        HeaderWords hw[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) hw[m] = header_words(hdr[m]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int st = 2 * sb + u;
+            const int cur = u;
+            // Prefetch of the next stage in the first half of the stage (the
+            // memory-instruction queue never fills, and the last load still
+            // has half a stage to land before the barrier): A rows by DMA into
+            // the other buffer (last read before the previous barrier), quants
+            // into registers, and in the second stage of a super-block the
+            // next one's headers.  Past the last stage the loads repeat it (in
+            // bounds, cache hits, never used).
+            const int nst = min(st + 1, nstages - 1);
+            float ds512[2][4], ndm[2][4];
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int j = 4 * u + jj;
+                    ds512[m][jj] = hw[m].d512 * (float)((hw[m].sc[j >> 2] >> (8 * (j & 3))) & 0xFFu);
+                    ndm[m][jj] = -(hw[m].dmin * (float)((hw[m].mn[j >> 2] >> (8 * (j & 3))) & 0xFFu));
+                }
+            bf16x8 fa[2][NB], fb[2][2];
+            // Fragment of row block i, k16 step s: row 32 i + lane % 32 sits in
+            // row group 4 i + (lane % 32) / 8 at row lane % 8; its chunk
+            // 2 s + lane / 32 in half s / 4, slot (chunk % 8) xor (lane % 8).
+            const int frag_row = ((lane & 31) >> 3) * 128 + (lane & 7) * 8;
+            auto a_frags = [&](int s, int slot) {
+                const int chunk = 2 * s + (lane >> 5);
+                const int off = frag_row + (chunk >> 3) * 64 + ((chunk & 7) ^ (lane & 7));
+#pragma unroll
+                for (int i = 0; i < NB; ++i) fa[slot][i] = __builtin_bit_cast(bf16x8, buffer(cur)[i * 512 + off]);
+            };
+            auto b_frags = [&](int s, int slot) {
+                const int jj = s >> 1;
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const uint32_t w = (s & 1) ? rb[cur].v[m][jj].y : rb[cur].v[m][jj].x;
+                    fb[slot][m] = dequant_frag(w, ds512[m][jj], ndm[m][jj]);
+                }
+            };
+            a_frags(0, 0);
+#pragma unroll
+            for (int m = 0; m < 2; ++m) fb[0][m] = fb_next0[m];
+            // Each k16 step: 2 NB MFMAs, and between them, in a fixed order,
+            // the work that prepares the next step (its NB A fragment reads
+            // and two B dequantizations in three pieces each) plus, in the
+            // first four steps, the prefetch loads of the next stage.  Item j
+            // of the 16 follows MFMA (j * 2 NB) / 16; sched_barrier keeps the
+            // order.
+#pragma unroll
+            for (int s = 0; s < kK16; ++s) {
+                const bool last = s + 1 == kK16;
+                DqPart dp[2];
+                uint32_t wsrc[2];
+                float dsv[2], ndv[2];
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    if (!last) {
+                        const int jj = (s + 1) >> 1;
+                        wsrc[m] = ((s + 1) & 1) ? rb[cur].v[m][jj].y : rb[cur].v[m][jj].x;
+                        dsv[m] = ds512[m][jj];
+                        ndv[m] = ndm[m][jj];
+                    } else {
+                        // first k16 step of the next stage: sub-block 4 of this
+                        // super-block, or sub-block 0 of the next one
+                        wsrc[m] = rb[cur ^ 1].v[m][0].x;
+                        if (u == 0) {
+                            dsv[m] = hw[m].d512 * (float)(hw[m].sc[1] & 0xFFu);
+                            ndv[m] = -(hw[m].dmin * (float)(hw[m].mn[1] & 0xFFu));
+                        } else {
+                            const HeaderWords hn = header_words(hdr[m]);
+                            dsv[m] = hn.d512 * (float)(hn.sc[0] & 0xFFu);
+                            ndv[m] = -(hn.dmin * (float)(hn.mn[0] & 0xFFu));
+                        }
+                    }
+                }
+                auto item = [&](int j) {
+                    switch (j) {
+                        case 0:
+                            if (s < 4) {
+                                if (2 * s < NB) dma_unit(nst, cur ^ 1, 2 * s);
+                                load_b_one(nst, rb[cur ^ 1], 0, s);
+                                if (u == 1 && s == 0) load_hdr(min(sb + 1, nsb - 1), hdr);
+                            }
+                            break;
+                        case 3:
+                            if (s < 4) {
+                                if (2 * s + 1 < NB) dma_unit(nst, cur ^ 1, 2 * s + 1);
+                                load_b_one(nst, rb[cur ^ 1], 1, s);
+                            }
+                            break;
+                        case 2: dq_a(dp[0], wsrc[0]); break;
+                        case 5: dq_bc(dp[0], 0, dsv[0], ndv[0]); break;
+                        case 7: dq_bc(dp[0], 1, dsv[0], ndv[0]); break;
+                        case 9: dq_a(dp[1], wsrc[1]); break;
+                        case 11: dq_bc(dp[1], 0, dsv[1], ndv[1]); break;
+                        case 13: dq_bc(dp[1], 1, dsv[1], ndv[1]); break;
+                        default: {
+                            // A fragment reads: items 1, 4, 6, 8, 10, 12, 14, 15
+                            const int ri = j == 1 ? 0 : j == 4 ? 1 : j == 6 ? 2 : j == 8 ? 3 : j == 10 ? 4
+                                         : j == 12 ? 5 : j == 14 ? 6 : 7;
+                            if (!last && ri < NB) {
+                                const int chunk = 2 * (s + 1) + (lane >> 5);
+                                const int off = frag_row + (chunk >> 3) * 64 + ((chunk & 7) ^ (lane & 7));
+                                fa[(s + 1) & 1][ri] = __builtin_bit_cast(bf16x8, buffer(cur)[ri * 512 + off]);
+                            }
+                            break;
+                        }
+                    }
+                };
+#pragma unroll
+                for (int n = 0; n < 2 * NB; ++n) {
+                    const int i = n >> 1, m = n & 1;
+                    acc[i][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][i], fb[s & 1][m], acc[i][m], 0, 0, 0);
+                    // items j with (j * 2 NB) / 16 == n
+#pragma unroll
+                    for (int j = (16 * n + 2 * NB - 1) / (2 * NB); j < (16 * (n + 1) + 2 * NB - 1) / (2 * NB); ++j) item(j);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const bf16x8 f = __builtin_bit_cast(bf16x8, make_uint4(dp[m].out[0], dp[m].out[1], dp[m].out[2],
+                                                                         dp[m].out[3]));
+                    if (!last) fb[(s + 1) & 1][m] = f;
+                    else fb_next0[m] = f;
+                }
+            }
+            // The next stage's A (DMA) and quants must have landed, and every
+            // wave must be done reading buffer `cur`, before either is reused.
+            wait_vmem_all();
+            __syncthreads();
+        }
+    } while (++sb < nsb);
+}
+
 template <bool GATEUP>
-__global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_gemm_kernel(
     const uint8_t* __restrict__ pool, size_t stride, int S, int H, int I, const uint16_t* __restrict__ ain, int T,
     int k, const int32_t* __restrict__ perm, const int4* __restrict__ tiles, const int32_t* __restrict__ ntiles,
     void* __restrict__ out, int y_dtype) {
-    __shared__ __align__(16) uint16_t sA[2][kBM][kLda];
-    __shared__ __align__(16) uint16_t sB[2][kBN][kLda];
+    __shared__ __align__(16) uint4 sA0[kStageLdsFrags * 64];
+    __shared__ __align__(16) uint4 sA1[kStageLdsFrags * 64];
     __shared__ int sidx[kBM];  // gate/up: token row of each tile row; down: its output pair (-1: none)
 
-    const int K = GATEUP ? H : I;               // contraction length
-    const int NT = GATEUP ? I / 128 : H / 256;  // N tiles
-    const int lt = xcd_logical_tile(blockIdx.x, *ntiles * NT);
-    if (lt < 0) return;
-    const int mt = lt / NT, nt = lt - mt * NT;
+    const int NT = GATEUP ? I / kGateUpFeatures : H / kDownColumns;
+    const int x = blockIdx.x & 7, gi = blockIdx.x >> 3;
+    const int mt = 8 * (gi / NT) + x, nt = gi - (gi / NT) * NT;
+    if (mt >= *ntiles) return;
     const int4 tl = tiles[mt];
-    const int slot = tl.x, qb = tl.y, rows = tl.z;
-    if (slot < 0 || slot >= S) return;
+    const int slot = tl.x, qb = tl.y, rows = tl.z, nblk = tl.w;
+    if (slot < 0 || slot >= S || rows < 1 || nblk < 1 || nblk > kRowBlocks) return;
     const int P = T * k;
     const uint8_t* wbase = pool + (size_t)slot * stride;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    if (tid < kBM) {
+    {
         int v = -1;
         if (tid < rows) {
             const int p = perm[qb + tid];
@@ -202,158 +474,145 @@ __global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(
     }
     __syncthreads();
 
-    // A: thread -> row tid/4, 16 columns at (tid%4)*16.  Rows past the batch
-    // read the tile's first row instead; their results are never stored.
-    const int ar = tid >> 2, ac = (tid & 3) * 16;
-    const uint16_t* a_src;
-    if (GATEUP) {
-        int tok = sidx[ar];
-        if (tok < 0) tok = max(sidx[0], 0);
-        a_src = ain + (size_t)tok * H + ac;
-    } else {
-        a_src = ain + (size_t)(qb + min(ar, rows - 1)) * I + ac;
+    TileCtx c;
+    c.K = GATEUP ? H : I;
+    const int r32 = lane & 31, hsel = lane >> 5;
+    c.a_base = reinterpret_cast<const uint8_t*>(ain);
+    {
+        // This lane's DMA row in row group wave + 4 t: row 32 t + 8 wave +
+        // lane / 8; chunk (lane % 8) xor (lane / 8).  Rows past the batch read
+        // a valid row of the tile; their results are never stored.
+        const int chunk = (lane & 7) ^ (lane >> 3);
+#pragma unroll
+        for (int t = 0; t < kRowBlocks; ++t) {
+            const int row = min(32 * t + 8 * wave + (lane >> 3), rows - 1);
+            uint32_t arow;
+            if (GATEUP) {
+                int tok = sidx[row];
+                if (tok < 0) tok = max(sidx[0], 0);
+                arow = (uint32_t)tok;
+            } else {
+                arow = (uint32_t)(qb + row);
+            }
+            c.a_off[t] = arow * (uint32_t)c.K * 2u + 16u * chunk;
+        }
     }
-    // B: thread -> LDS row bn (0..255), sub-block bj (0, 1) of the stage.
-    const int bn = tid & 255, bj = tid >> 8;
-    const uint8_t* b_tile;
-    int b_hdr, b_q, b_qstep, b_tile_bytes;
+    // B: this wave's two 32-row blocks of weight rows.  Gate/up: feature
+    // block fb (32 features) = rows (fb & 1) * 32.. of packed tile fb / 2,
+    // block 0 its gate rows, block 1 its up rows.  Down: packed tile cb,
+    // block m = rows 32m..32m+31.  Lane: row lane % 32, quant bytes
+    // 8 * (lane / 32).. of each (row, sub-block) slot.
     if (GATEUP) {
-        // LDS rows [rl][mat][64]: rl = packed tile 2*nt + rl, mat 0 gate / 1 up
-        const int rl = bn >> 7, mat = (bn >> 6) & 1, r = bn & 63;
-        b_tile = wbase + (size_t)(2 * nt + rl) * (H / 256) * kQ4kGateUpTile;
-        b_hdr = mat * 1024 + r * 16;
-        b_q = 2048 + mat * 1024 + r * 16;
-        b_qstep = 2048;
-        b_tile_bytes = kQ4kGateUpTile;
+        const int fb = nt * kWaves + wave;
+        c.b_rowgroup = wbase + (size_t)(fb >> 1) * (H / 256) * kQ4kGateUpTile;
+        const int r = (fb & 1) * 32 + r32;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            c.hdr_off[m] = m * 1024 + r * 16;
+            c.q_off[m] = 2048 + m * 1024 + r * 16 + 8 * hsel;
+        }
+        c.q_step = 2048;
+        c.tile_bytes = kQ4kGateUpTile;
     } else {
-        const int rg = 4 * nt + (bn >> 6), r = bn & 63;
-        b_tile = wbase + q4k_gateup_bytes(H, I) + (size_t)rg * (I / 256) * kQ4kDownTile;
-        b_hdr = r * 16;
-        b_q = 1024 + r * 16;
-        b_qstep = 1024;
-        b_tile_bytes = kQ4kDownTile;
+        const int cb = nt * kWaves + wave;
+        c.b_rowgroup = wbase + q4k_gateup_bytes(H, I) + (size_t)cb * (I / 256) * kQ4kDownTile;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            c.hdr_off[m] = (32 * m + r32) * 16;
+            c.q_off[m] = 1024 + (32 * m + r32) * 16 + 8 * hsel;
+        }
+        c.q_step = 1024;
+        c.tile_bytes = kQ4kDownTile;
     }
 
-    const int wm = wave & 1, wn = wave >> 1;
-    int brow[2];
-    if (GATEUP) {
-        const int rl = wn >> 1, half = (wn & 1) * 32;
-        brow[0] = rl * 128 + half;       // gate rows of 32 features
-        brow[1] = rl * 128 + 64 + half;  // up rows of the same features
-    } else {
-        brow[0] = 64 * wn;
-        brow[1] = 64 * wn + 32;
-    }
-    f32x16 acc[2][2];
+    f32x16 acc[kRowBlocks][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kRowBlocks; ++i)
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][m][r] = 0.f;
 
-    auto gload = [&](int step, PrefetchSlot& st) {
-        const int kk = step * kBK;
-        st.a0 = ldg16(a_src + kk);
-        st.a1 = ldg16(a_src + kk + 8);
-        const int j = ((kk & 255) >> 5) + bj;
-        const uint8_t* tile = b_tile + (size_t)(kk >> 8) * b_tile_bytes;
-        st.h = ldg16(tile + b_hdr);
-        st.q = ldg16(tile + b_q + j * b_qstep);
-    };
-    // MFMAs of LDS buffer `cur`, interleaved with storing `st` (stage `nstep`)
-    // into buffer `nxt`: k16 step i is followed by the dequantization of
-    // quant dword i.
-    auto stage = [&](int cur, bool store, int nstep, const PrefetchSlot& st, int nxt) {
-        float dsc = 0.f, dmm = 0.f;
-        if (store) {
-            uint4* da = reinterpret_cast<uint4*>(&sA[nxt][ar][ac]);
-            da[0] = st.a0;
-            da[1] = st.a1;
-            const int j = (((nstep * kBK) & 255) >> 5) + bj;
-            q4k_scale_min(st.h, j, &dsc, &dmm);
-        }
-        const uint32_t qw[4] = {st.q.x, st.q.y, st.q.z, st.q.w};
-#pragma unroll
-        for (int k16 = 0; k16 < kBK / 16; ++k16) {
-            const int kc = k16 * 16 + 8 * (lane >> 5);
-            bf16x8 fa[2], fb[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) fa[i] = lds_frag(&sA[cur][64 * wm + 32 * i + (lane & 31)][kc]);
-#pragma unroll
-            for (int m = 0; m < 2; ++m) fb[m] = lds_frag(&sB[cur][brow[m] + (lane & 31)][kc]);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int m = 0; m < 2; ++m)
-                    acc[i][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[m], acc[i][m], 0, 0, 0);
-            if (store) dequant8_to_lds(qw[k16], dsc, dmm, &sB[nxt][bn][bj * 32 + 8 * k16]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-
-    // Pipeline over nsteps (even, >= 4) stages: slots r0/r1 hold the loads
-    // of the next two stages, LDS buffers 0/1 alternate.
-    const int nsteps = K / kBK;
-    PrefetchSlot r0, r1;
-    gload(0, r0);
-    gload(1, r1);
-    {  // stage 0 into buffer 0 (no MFMA yet)
-        uint4* da = reinterpret_cast<uint4*>(&sA[0][ar][ac]);
-        da[0] = r0.a0;
-        da[1] = r0.a1;
-        float dsc, dmm;
-        q4k_scale_min(r0.h, bj, &dsc, &dmm);
-        const uint32_t qw[4] = {r0.q.x, r0.q.y, r0.q.z, r0.q.w};
-#pragma unroll
-        for (int d = 0; d < 4; ++d) dequant8_to_lds(qw[d], dsc, dmm, &sB[0][bn][bj * 32 + 8 * d]);
+    switch (nblk) {
+        case 1: tile_gemm<GATEUP, 1>(c, sA0, sA1, wave, lane, acc); break;
+        case 2: tile_gemm<GATEUP, 2>(c, sA0, sA1, wave, lane, acc); break;
+        case 3: tile_gemm<GATEUP, 3>(c, sA0, sA1, wave, lane, acc); break;
+        case 4: tile_gemm<GATEUP, 4>(c, sA0, sA1, wave, lane, acc); break;
+        case 5: tile_gemm<GATEUP, 5>(c, sA0, sA1, wave, lane, acc); break;
+        case 6: tile_gemm<GATEUP, 6>(c, sA0, sA1, wave, lane, acc); break;
+        case 7: tile_gemm<GATEUP, 7>(c, sA0, sA1, wave, lane, acc); break;
+        default: tile_gemm<GATEUP, 8>(c, sA0, sA1, wave, lane, acc); break;
     }
-    __syncthreads();
-    int step = 0;
-    for (; step + 3 < nsteps; step += 2) {
-        gload(step + 2, r0);
-        stage(0, true, step + 1, r1, 1);
-        __syncthreads();
-        gload(step + 3, r1);
-        stage(1, true, step + 2, r0, 0);
-        __syncthreads();
-    }
-    // last two stages: step = nsteps - 2 in buffer 0, stage nsteps - 1 in r1
-    stage(0, true, step + 1, r1, 1);
-    __syncthreads();
-    stage(1, false, 0, r1, 0);
 
+    // Epilogue through LDS (both A buffers are free after the loop's last
+    // barrier): in passes over row blocks, the waves write their accumulator
+    // rows row-major into one buffer, then every thread stores 16-byte chunks
+    // of whole rows.  Passes alternate between the two buffers, so one
+    // barrier per pass suffices.
     if (GATEUP) {
-        // h = silu(g) * u -> bf16 at position qb + row, feature 128 nt + 64 rl + half + lane % 32
-        uint16_t* hout = static_cast<uint16_t*>(out);
-        const int f = 128 * nt + 64 * (wn >> 1) + (wn & 1) * 32 + (lane & 31);
+        // h = silu(g) * u, rounded to bf16: 128 rows x 128 features per pass
+        // (row stride 272 bytes), stored at position qb + row.
+        constexpr int kStride = kGateUpFeatures * 2 + 16;
+        constexpr int kChunks = kGateUpFeatures * 2 / 16;  // per row
+        const int f = 32 * wave + r32;
+        uint16_t* hout = static_cast<uint16_t*>(out) + (size_t)nt * kGateUpFeatures;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int pass = 0; pass < 2; ++pass) {
+            if (4 * pass >= nblk) break;
+            uint8_t* stage = reinterpret_cast<uint8_t*>(pass ? sA1 : sA0);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (row < rows) {
-                    const float hv = silu(acc[i][0][r]) * acc[i][1][r];
-                    hout[(size_t)(qb + row) * I + f] = __builtin_bit_cast(uint16_t, (__bf16)hv);
-                }
-            }
-    } else {
+            for (int ii = 0; ii < 4; ++ii) {
+                const int i = 4 * pass + ii;
+                if (i < nblk) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const int col = 256 * nt + brow[m] + (lane & 31);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    const int p = row < rows ? sidx[row] : -1;
-                    if (p >= 0) {
-                        const size_t o = (size_t)p * H + col;
-                        if (y_dtype == 0) static_cast<float*>(out)[o] = acc[i][m][r];
-                        else static_cast<uint16_t*>(out)[o] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][m][r]);
+                    for (int r = 0; r < 16; ++r) {
+                        const int rl = 32 * ii + 8 * (r >> 2) + 4 * hsel + (r & 3);
+                        const float hv = fast_silu(acc[i][0][r]) * acc[i][1][r];
+                        *reinterpret_cast<uint16_t*>(stage + rl * kStride + 2 * f) =
+                            __builtin_bit_cast(uint16_t, (__bf16)hv);
                     }
                 }
             }
+            __syncthreads();
+            const int prow = min(128, rows - 128 * pass);
+            for (int ch = tid; ch < prow * kChunks; ch += kThreads) {
+                const int rl = ch / kChunks, cc = ch - rl * kChunks;
+                const uint4 v = *reinterpret_cast<const uint4*>(stage + rl * kStride + 16 * cc);
+                *reinterpret_cast<uint4*>(hout + (size_t)(qb + 128 * pass + rl) * I + 8 * cc) = v;
+            }
+        }
+    } else {
+        // y: 32 rows x 256 columns (fp32 or bf16) per pass, each row stored
+        // to its pair's row of y_pairs.
+        const int esize = y_dtype == 0 ? 4 : 2;
+        const int stride = kDownColumns * esize + 16;
+        const int cpr = kDownColumns * esize / 16;  // 16-byte chunks per row
+        const int col0 = 64 * wave + r32;
+        uint8_t* y = static_cast<uint8_t*>(out);
+#pragma unroll
+        for (int i = 0; i < kRowBlocks; ++i) {
+            if (i >= nblk) break;
+            uint8_t* stage = reinterpret_cast<uint8_t*>((i & 1) ? sA1 : sA0);
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int rl = 8 * (r >> 2) + 4 * hsel + (r & 3);
+                    uint8_t* d = stage + rl * stride + (col0 + 32 * m) * esize;
+                    if (esize == 4) *reinterpret_cast<float*>(d) = acc[i][m][r];
+                    else *reinterpret_cast<uint16_t*>(d) = __builtin_bit_cast(uint16_t, (__bf16)acc[i][m][r]);
+                }
+            __syncthreads();
+            const int prow = min(32, rows - 32 * i);
+            for (int ch = tid; ch < prow * cpr; ch += kThreads) {
+                const int rl = ch / cpr, cc = ch - rl * cpr;
+                const int p = sidx[32 * i + rl];
+                if (p >= 0) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(stage + rl * stride + 16 * cc);
+                    *reinterpret_cast<uint4*>(y + ((size_t)p * H + (size_t)nt * kDownColumns) * esize + 16 * cc) = v;
+                }
+            }
+        }
     }
 }
 
@@ -362,6 +621,7 @@ __global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(
 hipError_t launch_ffn_prefill_q4k(const FfnArgs& a, hipStream_t s) {
     const int P = a.T * a.k;
     const int mt = max_tiles(P, a.S);
+    if (a.S > 1024) return hipErrorInvalidValue;  // one tiles-kernel thread per active slot
     uint8_t* ws = static_cast<uint8_t*>(a.ws);
     uint16_t* h = reinterpret_cast<uint16_t*>(ws);
     size_t off = align256((size_t)P * a.I * 2);
@@ -370,22 +630,25 @@ hipError_t launch_ffn_prefill_q4k(const FfnArgs& a, hipStream_t s) {
     int32_t* ntiles = reinterpret_cast<int32_t*>(ws + off);
 
     timer_before(kStagePrep, s);
-    hipLaunchKernelGGL(prefill_tiles_kernel, dim3(1), dim3(256), 0, s, a.slot_offsets, a.active_slots, a.num_active,
+    hipLaunchKernelGGL(prefill_tiles_kernel, dim3(1), dim3(1024), 0, s, a.slot_offsets, a.active_slots, a.num_active,
                        a.S, P, tiles, ntiles);
     timer_after(kStagePrep, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
+    // Grid: 8 XCD lanes x (N tiles x ceil(M tiles / 8)).
+    const int mgroups = (mt + 7) / 8;
+    const int nt_gu = a.I / kGateUpFeatures, nt_dn = a.H / kDownColumns;
     timer_before(kStagePrefillGateUp, s);
-    hipLaunchKernelGGL(prefill_gemm_kernel<true>, dim3(mt * (a.I / 128)), dim3(kThreads), 0, s, a.pool, a.stride, a.S,
-                       a.H, a.I, static_cast<const uint16_t*>(a.x), a.T, a.k, a.perm_pair, tiles, ntiles,
+    hipLaunchKernelGGL(prefill_gemm_kernel<true>, dim3(8 * nt_gu * mgroups), dim3(kThreads), 0, s, a.pool, a.stride,
+                       a.S, a.H, a.I, static_cast<const uint16_t*>(a.x), a.T, a.k, a.perm_pair, tiles, ntiles,
                        static_cast<void*>(h), 0);
     timer_after(kStagePrefillGateUp, s);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 
     timer_before(kStagePrefillDown, s);
-    hipLaunchKernelGGL(prefill_gemm_kernel<false>, dim3(mt * (a.H / 256)), dim3(kThreads), 0, s, a.pool, a.stride,
+    hipLaunchKernelGGL(prefill_gemm_kernel<false>, dim3(8 * nt_dn * mgroups), dim3(kThreads), 0, s, a.pool, a.stride,
                        a.S, a.H, a.I, (const uint16_t*)h, a.T, a.k, a.perm_pair, tiles, ntiles, a.y_pairs, a.y_dtype);
     timer_after(kStagePrefillDown, s);
     return hipGetLastError();

@@ -25,7 +25,11 @@ namespace qmoe {
 //     [1024 + 1024j, +1024)   quants of sub-block j
 //
 // The 16 quant bytes of one row and sub-block hold element e = 8d + n in
-// nibble n (bits 4n..4n+3) of little-endian dword d (d < 4, n < 8).
+// nibble n (bits 4n..4n+3) of the little-endian dword of group d (d < 4,
+// n < 8); the groups are stored in the order 0, 2, 1, 3, so bytes 0-7 hold
+// elements 0-7 and 16-23 and bytes 8-15 elements 8-15 and 24-31 (the K
+// values one 32x32x16 MFMA operand lane needs for the sub-block's two
+// k-steps).
 //
 // Packed Q8_0 blob (H, I multiples of 128), tiles of 64 rows x 4 blocks:
 //   gate/up tile (rg, bg), bg < H/128, 17408 bytes:

@@ -123,7 +123,7 @@ def test_pack_round_trip(fmt, H, I):
 
 def test_pack_places_q4k_fields():
     """Row r, super-block sb of W_up: its 16 header bytes sit at tile (r//64, sb), offset 1024 + 16*(r%64);
-    quant element 8d+n of sub-block j sits in nibble n of dword d of its 16-byte slot."""
+    quant element 8d+n of sub-block j sits in nibble n of the dword of group d, groups stored 0, 2, 1, 3."""
     H, I = 512, 256
     blob = F.expert_blob(Q.MOE_FMT_Q4K, 2, 0, 0, H, I)
     packed = Q.moe_pack_expert(Q.MOE_FMT_Q4K, blob, H, I)
@@ -138,7 +138,7 @@ def test_pack_places_q4k_fields():
             for e in (0, 9, 31):
                 byte = canon[16 + (j // 2) * 32 + e]
                 q = (byte >> 4) if j % 2 else (byte & 15)
-                assert (int(words[e // 8]) >> (4 * (e % 8))) & 15 == q
+                assert (int(words[[0, 2, 1, 3][e // 8]]) >> (4 * (e % 8))) & 15 == q
 
 
 def test_validate_slot_map():
