@@ -136,7 +136,7 @@ def main():
     torch.cuda.synchronize()
 
     # ---- eager pass with HIP-event stage timers (kernel durations on the launch stream)
-    stages = {"route": 0, "batches": 1, "ffn_prep": 2, "ffn_gateup": 3, "ffn_down": 4, "combine": 5}
+    stages = {"route": 0, "batches": 1, "ffn_gateup": 3, "ffn_down": 4, "combine": 5}
     for s in stages.values():
         Q.moe_timer_begin(s, args.steps)
     torch.cuda.synchronize()

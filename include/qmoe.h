@@ -218,8 +218,8 @@ moe_status moe_combine(const void* y_pairs, int y_pairs_dtype, const int32_t* to
 /* ------------------------------------------------------------ stage timers
  * Diagnostics: hipEvent pairs recorded around every launch of one stage, on
  * the launch's stream.  Not for use while a stream is being captured.
- *   stage: 0 route, 1 batches, 2 ffn activation prep, 3 ffn gate/up,
- *          4 ffn down, 5 combine, 6 prefill gate/up GEMM, 7 prefill down GEMM.
+ *   stage: 0 route, 1 batches, 2 prefill tile list, 3 ffn gate/up (decode),
+ *          4 ffn down (decode), 5 combine, 6 prefill gate/up GEMM, 7 prefill down GEMM.
  * moe_timer_begin arms the stage for up to `capacity` launches (events are
  * created here, on the current device); moe_timer_end waits for the last
  * recorded event, returns the summed kernel time in milliseconds and the

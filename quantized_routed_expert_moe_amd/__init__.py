@@ -23,7 +23,7 @@ MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_F32, MOE_BF16 = 0, 1
 MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL = 0, 1, 2
 MOE_FMT_Q8_0, MOE_FMT_Q4K = 0, 1
-STAGES = ("route", "batches", "ffn_prep", "ffn_gateup", "ffn_down", "combine", "prefill_gateup", "prefill_down")
+STAGES = ("route", "batches", "prefill_tiles", "ffn_gateup", "ffn_down", "combine", "prefill_gateup", "prefill_down")
 
 
 class QmoeError(RuntimeError):

@@ -249,6 +249,12 @@ moe_status ffn_common(int format, const void* slot_pool, size_t slot_stride, int
     } else {
         if (format != MOE_FMT_Q4K) return fail(MOE_ERR_UNSUPPORTED, "the prefill path is implemented for Q4_K only");
         if (x_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the prefill path takes MOE_BF16 x");
+        // The GEMMs address x and h rows with 32-bit byte offsets, and the
+        // tile list counts tiles in 16 bits.
+        const long long P = (long long)T * k;
+        if ((long long)T * H * 2 > 0xFFFFFFFFLL || P * I * 2 > 0xFFFFFFFFLL || (P + 255) / 256 + 1024 > 0xFFFF)
+            return fail(MOE_ERR_UNSUPPORTED, "prefill path limits: T*H*2 and T*k*I*2 below 4 GiB, T*k below %d",
+                        (0xFFFF - 1024) * 256);
         need = qmoe::prefill_workspace_bytes(T, k, H, I);
     }
     if (ws_bytes < need)

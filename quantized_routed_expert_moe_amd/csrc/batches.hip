@@ -3,7 +3,8 @@
 // prompts"; pairs whose expert is not on the card go to the host tier:
 // bloomery README of 2026-09-24, opening list).
 //
-// Up to kSingleMaxPairs pairs: one workgroup of 8 waves (below).  Above:
+// Up to 64 pairs (decode): a single wave, no workgroup barriers.  Up to
+// kSingleMaxPairs pairs: one workgroup of 8 waves (below).  Above:
 // three launches over 1024-pair blocks -- per-block bucket counts, one
 // workgroup scanning (bucket, block) counts into starting positions, and a
 // per-block stable scatter -- with the same in-wave ranking.
@@ -49,6 +50,86 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
         if (lane >= off) v += t;
     }
     return v;
+}
+
+// Inclusive prefix sum over the wave with DPP moves (row shifts, then row
+// broadcasts across the four 16-lane rows).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_add_i(int v) {
+    return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+__device__ __forceinline__ int wave_scan_dpp(int v) {
+    v = dpp_add_i<0x111>(v);  // row_shr:1
+    v = dpp_add_i<0x112>(v);  // row_shr:2
+    v = dpp_add_i<0x114>(v);  // row_shr:4
+    v = dpp_add_i<0x118>(v);  // row_shr:8
+    v = dpp_add_i<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v = dpp_add_i<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// P <= 64: lane p owns pair p.  Same outputs as the workgroup kernel (bucket
+// match by ballots, stable positions start[b] + rank), with the bucket scan
+// done by one wave in 64-bucket steps.
+__global__ __launch_bounds__(64) void batches_wave_kernel(const int32_t* __restrict__ ids, const float* __restrict__ w,
+                                                          int T, int k, int E, const int32_t* __restrict__ soe, int S,
+                                                          int nbits, int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ active,
+                                                          int32_t* __restrict__ num_active,
+                                                          int32_t* __restrict__ perm, int32_t* __restrict__ host_token,
+                                                          int32_t* __restrict__ host_expert,
+                                                          float* __restrict__ host_weight,
+                                                          int32_t* __restrict__ host_count) {
+    extern __shared__ int cnt[];  // [S + 1]: counts, then starting positions
+    const int P = T * k;
+    const int lane = threadIdx.x;
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    const bool valid = lane < P;
+    const int id = valid ? ids[lane] : 0;
+    const float wt = valid ? w[lane] : 0.0f;
+    for (int i = lane; i <= S; i += 64) cnt[i] = 0;
+    const int sl = (valid && id >= 0 && id < E) ? soe[id] : -1;
+    const int b = valid ? ((sl >= 0 && sl < S) ? sl : S) : 0;
+    const unsigned long long m = match_bucket(b, valid, nbits);
+    const int rank = __popcll(m & lt);
+    wave_lds_sync();
+    if (valid && rank == 0) cnt[b] = __popcll(m);
+    wave_lds_sync();
+    int carry = 0, acarry = 0;
+    for (int c0 = 0; c0 < S; c0 += 64) {
+        const int bb = c0 + lane;
+        const int c = bb < S ? cnt[bb] : 0;
+        const int f = c > 0 ? 1 : 0;
+        const int inc = wave_scan_dpp(c), finc = wave_scan_dpp(f);
+        if (bb < S) {
+            offsets[bb] = carry + inc - c;
+            cnt[bb] = carry + inc - c;
+            if (f) active[acarry + finc - f] = bb;
+        }
+        carry += __builtin_amdgcn_readlane(inc, 63);
+        acarry += __builtin_amdgcn_readlane(finc, 63);
+    }
+    if (lane == 0) {
+        offsets[S] = carry;
+        *num_active = acarry;
+        *host_count = cnt[S];
+    }
+    wave_lds_sync();
+    if (valid) {
+        if (b < S) {
+            perm[cnt[b] + rank] = lane;
+        } else {
+            host_token[rank] = lane / k;
+            host_expert[rank] = id;
+            host_weight[rank] = wt;
+        }
+    }
 }
 
 __global__ __launch_bounds__(512) void batches_kernel(const int32_t* __restrict__ ids, const float* __restrict__ w,
@@ -290,7 +371,11 @@ hipError_t launch_batches(const int32_t* ids, const float* w, int T, int k, int 
     while ((1 << nbits) <= S) ++nbits;  // buckets 0..S
     const long P = (long)T * k;
     timer_before(kStageBatches, s);
-    if (P <= kSingleMaxPairs) {
+    if (P <= 64) {
+        hipLaunchKernelGGL(batches_wave_kernel, dim3(1), dim3(64), (size_t)(S + 1) * sizeof(int), s, ids, w, T, k, E,
+                           soe, S, nbits, offsets, active, num_active, perm, host_token, host_expert, host_weight,
+                           host_count);
+    } else if (P <= kSingleMaxPairs) {
         const size_t lds = (size_t)(kBatchWaves + 1) * (S + 1) * sizeof(int);
         hipLaunchKernelGGL(batches_kernel, dim3(1), dim3(64 * kBatchWaves), lds, s, ids, w, T, k, E, soe, S, nbits,
                            offsets, active, num_active, perm, host_token, host_expert, host_weight, host_count);

@@ -28,38 +28,54 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
                                                       const int32_t* __restrict__ soe, int E,
                                                       const float* __restrict__ ysh, int T, int k, int H,
                                                       void* __restrict__ y, int y_dtype) {
-    const int t = blockIdx.y;
-    const int h0 = (blockIdx.x * 256 + threadIdx.x) * 8;
-    if (h0 >= H) return;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    // Rows of non-resident pairs are read too (they are in bounds, possibly
-    // never written) and dropped by a select, so the loads of all k pairs
-    // can be in flight together instead of waiting on the residency test.
+    // The slot map goes to LDS, loaded together with the first batch of pair
+    // ids, weights and rows, so the residency test is an LDS read rather than
+    // a second dependent global load.  Rows of non-resident pairs are read too
+    // (in bounds, possibly never written) and dropped by a select, so the
+    // loads of a batch are in flight together.
+    __shared__ int sm[kMaxExpertsInternal];
     constexpr int kBatch = 8;
-    for (int j0 = 0; j0 < k; j0 += kBatch) {
-        float v[kBatch][8];
-        bool res[kBatch];
-        float wj[kBatch];
+    const int t = blockIdx.y;
+    const int h0 = min((blockIdx.x * 256 + threadIdx.x) * 8, H - 8);  // threads past H redo the last columns
+    const bool owner = (blockIdx.x * 256 + threadIdx.x) * 8 < H;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float v[kBatch][8];
+    int idb[kBatch];
+    float wj[kBatch];
+    auto load_batch = [&](int j0) {
 #pragma unroll
         for (int jj = 0; jj < kBatch; ++jj) {
             const int j = min(j0 + jj, k - 1);
             const size_t p = (size_t)t * k + j;
-            const int id = ids[p];
-            res[jj] = (j0 + jj < k) && id >= 0 && id < E && soe[id] >= 0;
+            idb[jj] = ids[p];
             wj[jj] = w[p];
             load8(yp, yp_dtype, p * H + h0, v[jj]);
         }
+    };
+    auto add_batch = [&](int j0) {
 #pragma unroll
-        for (int jj = 0; jj < kBatch; ++jj)
+        for (int jj = 0; jj < kBatch; ++jj) {
+            const int id = idb[jj];
+            const bool res = (j0 + jj < k) && id >= 0 && id < E && sm[id] >= 0;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = res[jj] ? fmaf(wj[jj], v[jj][i], acc[i]) : acc[i];
+            for (int i = 0; i < 8; ++i) acc[i] = res ? fmaf(wj[jj], v[jj][i], acc[i]) : acc[i];
+        }
+    };
+    load_batch(0);
+    for (int e = threadIdx.x; e < E; e += blockDim.x) sm[e] = soe[e];
+    __syncthreads();
+    add_batch(0);
+    for (int j0 = kBatch; j0 < k; j0 += kBatch) {
+        load_batch(j0);
+        add_batch(j0);
     }
     if (ysh) {
-        float v[8];
-        load8(ysh, 0, (size_t)t * H + h0, v);
+        float u[8];
+        load8(ysh, 0, (size_t)t * H + h0, u);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += v[i];
+        for (int i = 0; i < 8; ++i) acc[i] += u[i];
     }
+    if (!owner) return;
     if (y_dtype == 0) {
         float4* o = reinterpret_cast<float4*>(static_cast<float*>(y) + (size_t)t * H + h0);
         o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);

@@ -30,17 +30,33 @@ __device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
     return x >> 16;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+// v + the value DPP_CTRL moves into this lane (lanes outside ROW_MASK add 0).
+template <int DPP_CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), DPP_CTRL, ROW_MASK, 0xF, false));
+}
+
+// Sum over each 16-lane row, in every lane of the row (DPP register moves).
+__device__ __forceinline__ float row16_sum(float v) {
+    v = dpp_add<0xB1>(v);   // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]
+    v = dpp_add<0x141>(v);  // row_half_mirror
+    v = dpp_add<0x140>(v);  // row_mirror
     return v;
+}
+
+// Sum over the wave, in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row16_sum(v);
+    v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // Sum over each aligned group of 32 lanes (lanes 0-31 and 32-63 separately).
 __device__ __forceinline__ float half_wave_sum(float v) {
-#pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    v = row16_sum(v);
+    return v + __shfl_xor(v, 16, 64);
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }

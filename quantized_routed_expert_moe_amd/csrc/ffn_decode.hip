@@ -20,10 +20,12 @@
 //     term dmin * m_j * sum x.
 //   * Activations (token rows, and the intermediate h) are 64-byte records per
 //     32 elements, laid out in the order the nibble/byte extraction produces.
-//     Each wave copies the records of its K range for the tokens of the
-//     current chunk into its own LDS region with coalesced loads once; the
-//     inner loop then reads them as wave-wide broadcasts (every lane reads the
-//     same address), so no load latency sits inside the dot-product loop.
+//     Each wave puts the records of its K range for the tokens of the current
+//     chunk into its own LDS region once: gate/up builds them from the x rows
+//     (no separate conversion kernel), down copies the h records the gate/up
+//     epilogue wrote.  The inner loop then reads them as wave-wide broadcasts
+//     (every lane reads the same address), so no load latency sits inside the
+//     dot-product loop.
 #include "device_common.h"
 #include "qmoe_internal.h"
 
@@ -36,88 +38,6 @@ constexpr uint32_t kMagic = 0x64006400u;  // fp16 1024.0 in both halves
 // Records staged in LDS: X words [16 per record] and (C, S) pairs.
 typedef const uint32_t cu32;
 typedef const float cf32;  // (C, S) pairs, two floats each
-
-// ----------------------------------------------------------- activations
-
-// Pack 32 activation values of one block into the record layout of `FMT`.
-//   Q4_K: word 4d+0 = (v[8d], v[8d+4]), 4d+1 = (v[8d+1], v[8d+5]) / 16,
-//         4d+2 = (v[8d+2], v[8d+6]),    4d+3 = (v[8d+3], v[8d+7]) / 16.
-//   Q8_0: word 2d = (v[4d], v[4d+2]), 2d+1 = (v[4d+1], v[4d+3]).
-// cs.x = (1024 | 1152) * sum of the stored fp16 values, cs.y = fp32 sum of v.
-template <int FMT>
-__device__ __forceinline__ void pack_record(const float* v, uint32_t* words, float2* cs) {
-    float sum16 = 0.0f, sum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) sum += v[i];
-    if (FMT == 1) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                float sc = (p & 1) ? 0.0625f : 1.0f;
-                uint32_t lo = float_to_half_bits(v[8 * d + p] * sc);
-                uint32_t hi = float_to_half_bits(v[8 * d + p + 4] * sc);
-                sum16 += half_to_float(lo) + half_to_float(hi);
-                words[4 * d + p] = lo | (hi << 16);
-            }
-        }
-        *cs = make_float2(1024.0f * sum16, sum);
-    } else {
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-#pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                uint32_t lo = float_to_half_bits(v[4 * d + p]);
-                uint32_t hi = float_to_half_bits(v[4 * d + p + 2]);
-                sum16 += half_to_float(lo) + half_to_float(hi);
-                words[2 * d + p] = lo | (hi << 16);
-            }
-        }
-        *cs = make_float2(1152.0f * sum16, sum);
-    }
-}
-
-// x [T, H] (fp32 or bf16) -> records [T][H/32][16 words] and [T][H/32] (C, S).
-template <int FMT>
-__global__ __launch_bounds__(256) void prep_kernel(const void* __restrict__ x, int x_dtype, int H,
-                                                   uint32_t* __restrict__ xw, float2* __restrict__ xcs) {
-    const int t = blockIdx.y;
-    const int nblk = H / 32;
-    const int b = blockIdx.x * 256 + threadIdx.x;
-    if (b >= nblk) return;
-    float v[32];
-    if (x_dtype == 0) {
-        const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(x) + (size_t)t * H + b * 32);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float4 f = src[i];
-            v[4 * i] = f.x;
-            v[4 * i + 1] = f.y;
-            v[4 * i + 2] = f.z;
-            v[4 * i + 3] = f.w;
-        }
-    } else {
-        const uint4* src =
-            reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + (size_t)t * H + b * 32);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint4 u = src[i];
-            uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                v[8 * i + 2 * j] = bf16_to_float(w4[j] & 0xFFFFu);
-                v[8 * i + 2 * j + 1] = bf16_to_float(w4[j] >> 16);
-            }
-        }
-    }
-    uint32_t words[16];
-    float2 cs;
-    pack_record<FMT>(v, words, &cs);
-    uint4* dst = reinterpret_cast<uint4*>(xw + ((size_t)t * nblk + b) * 16);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = make_uint4(words[4 * i], words[4 * i + 1], words[4 * i + 2], words[4 * i + 3]);
-    xcs[(size_t)t * nblk + b] = cs;
-}
 
 // ------------------------------------------------------- block dot products
 
@@ -237,6 +157,85 @@ __device__ __forceinline__ void stage_unit(const uint32_t* const* rec_g, const f
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Build the RB records starting at block r0 of each of the NT token rows
+// straight from x (fp32 or bf16) into the wave's LDS region.  A record holds
+// 32 activation values of one block as 16 words of fp16 pairs, in the order
+// the nibble / byte extraction of the weights produces:
+//   Q4_K: word 4d+0 = (v[8d], v[8d+4]), 4d+1 = (v[8d+1], v[8d+5]) / 16,
+//         4d+2 = (v[8d+2], v[8d+6]),    4d+3 = (v[8d+3], v[8d+7]) / 16;
+//   Q8_0: word 2d = (v[4d], v[4d+2]), 2d+1 = (v[4d+1], v[4d+3]);
+// with (C, S) = ((1024 | 1152) * sum of the stored fp16 values, fp32 sum of
+// v).
+//   Q4_K (RB = 8): lane l packs values 4 (l % 8)..+4 of block l / 8.  The two
+//     lanes of a pair (values 8d..8d+3 and 8d+4..8d+7) swap two values by DPP
+//     so that the even lane forms words 4d, 4d+1 and the odd lane 4d+2,
+//     4d+3 (word 4d+p = (v[8d+p], v[8d+p+4]), odd p scaled by 1/16).
+//   Q8_0 (RB = 4): lane l packs values 4 (l % 8)..+4 of block (l / 8) % 4 of
+//     token l / 32 into words 2 (l % 8), +1 ((v0, v2), (v1, v3)).
+// Block sums (fp32 sum of x, and the sum of the stored fp16 values) are
+// 8-lane DPP reductions.
+template <int FMT>
+__device__ __forceinline__ void load4(const void* xrow, int x_dtype, int e, float* v) {
+    if (x_dtype == 0) {
+        const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(xrow) + e);
+        v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+    } else {
+        const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(xrow) + e);
+        v[0] = bf16_to_float(u.x & 0xFFFFu); v[1] = bf16_to_float(u.x >> 16);
+        v[2] = bf16_to_float(u.y & 0xFFFFu); v[3] = bf16_to_float(u.y >> 16);
+    }
+}
+
+__device__ __forceinline__ float sum8_lanes(float v) {
+    v = dpp_add<0xB1>(v);   // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]
+    return dpp_add<0x141>(v);  // row_half_mirror: the other quad of the 8
+}
+
+template <int FMT, int RB, int NT>
+__device__ __forceinline__ void stage_from_x(const void* const* xrow, int x_dtype, int r0, int lane, uint32_t* lw,
+                                             float* lc) {
+    const int sl = lane & 7;
+    if (FMT == 1) {
+        const int jb = lane >> 3;
+        const bool even = (sl & 1) == 0;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            float v[4];
+            load4<FMT>(xrow[t], x_dtype, (r0 + jb) * 32 + 4 * sl, v);
+            const float send0 = even ? v[2] : v[0], send1 = even ? v[3] : v[1];
+            const float recv0 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send0), 0xB1, 0xF, 0xF, false));
+            const float recv1 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send1), 0xB1, 0xF, 0xF, false));
+            // even lane: words p = 0, 1; odd lane: p = 2, 3
+            const float lo0 = even ? v[0] : recv0, hi0 = even ? recv0 : v[2];
+            const float lo1 = (even ? v[1] : recv1) * 0.0625f, hi1 = (even ? recv1 : v[3]) * 0.0625f;
+            const uint32_t b0 = float_to_half_bits(lo0), b1 = float_to_half_bits(hi0);
+            const uint32_t b2 = float_to_half_bits(lo1), b3 = float_to_half_bits(hi1);
+            *reinterpret_cast<uint2*>(lw + (t * RB + jb) * 16 + 2 * sl) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+            const float s16 = sum8_lanes(half_to_float(b0) + half_to_float(b1) + half_to_float(b2) + half_to_float(b3));
+            const float sx = sum8_lanes(v[0] + v[1] + v[2] + v[3]);
+            if (sl == 0) *reinterpret_cast<float2*>(lc + (t * RB + jb) * 2) = make_float2(1024.0f * s16, sx);
+        }
+    } else {
+        const int jb = (lane >> 3) & 3, t = lane >> 5;
+        if (t < NT) {
+            float v[4];
+            load4<FMT>(xrow[t], x_dtype, (r0 + jb) * 32 + 4 * sl, v);
+            const uint32_t b0 = float_to_half_bits(v[0]), b1 = float_to_half_bits(v[2]);
+            const uint32_t b2 = float_to_half_bits(v[1]), b3 = float_to_half_bits(v[3]);
+            *reinterpret_cast<uint2*>(lw + (t * RB + jb) * 16 + 2 * sl) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+            const float s16 = half_to_float(b0) + half_to_float(b1) + half_to_float(b2) + half_to_float(b3);
+            const float sx = v[0] + v[1] + v[2] + v[3];
+            // lanes of token 1 sit in rows 2-3: the 8-lane sums stay within a token
+            const float c16 = sum8_lanes(s16), csx = sum8_lanes(sx);
+            if (sl == 0) *reinterpret_cast<float2*>(lc + (t * RB + jb) * 2) = make_float2(1152.0f * c16, csx);
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // acc[t][m] += dot of the unit's weights (matrix m) with token t's records.
 template <int NT, int NMAT>
 __device__ __forceinline__ void unit_dots(const UnitRegs<1, NMAT>& r, const uint32_t* lw, const float* lc,
@@ -287,12 +286,13 @@ __device__ __forceinline__ void unit_dots(const UnitRegs<0, NMAT>& r, const uint
 template <int FMT, int NMAT, int NT>
 __device__ __forceinline__ void gemv_units(const uint8_t* __restrict__ tiles, int u0, int nu, int lane,
                                            UnitRegs<FMT, NMAT>& w, bool have_first, const uint32_t* const* rec_g,
-                                           const float2* const* rcs_g, uint32_t* lw, float* lc,
-                                           float (*acc)[NMAT]) {
+                                           const float2* const* rcs_g, const void* const* xrow, int x_dtype,
+                                           uint32_t* lw, float* lc, float (*acc)[NMAT]) {
     constexpr int RB = Unit<FMT>::kRecords;
     for (int ul = 0; ul < nu; ++ul) {
         if (ul > 0 || !have_first) load_unit(tiles + (size_t)(u0 + ul) * tile_bytes<FMT, NMAT>(), lane, w);
-        stage_unit<RB, NT>(rec_g, rcs_g, (u0 + ul) * RB, lane, lw, lc);
+        if (NMAT == 2) stage_from_x<FMT, RB, NT>(xrow, x_dtype, (u0 + ul) * RB, lane, lw, lc);
+        else stage_unit<RB, NT>(rec_g, rcs_g, (u0 + ul) * RB, lane, lw, lc);
         unit_dots<NT, NMAT>(w, lw, lc, acc);
     }
 }
@@ -323,13 +323,14 @@ __device__ __forceinline__ void store_h_record(float h, int rg, int lane, uint32
     if (e == 0) hcs_q[blk] = make_float2(c, sx);
 }
 
-// NMAT = 2: gate/up GEMV + SwiGLU over a slot's tokens (records of token
-// rows, indexed by perm_pair / k), writing h records at each pair's
-// position q.  NMAT = 1: down GEMV (records of h at position q) writing
+// NMAT = 2: gate/up GEMV + SwiGLU over a slot's tokens (records built from
+// the token rows of x, indexed by perm_pair / k), writing h records at each
+// pair's position q.  NMAT = 1: down GEMV (records of h at position q) writing
 // y_pairs at pair perm_pair[q].
 template <int FMT, int NMAT>
 __global__ __launch_bounds__(512) void gemv_kernel(const uint8_t* __restrict__ pool, size_t stride, int S, int K,
-                                                   int rows, size_t section, const uint32_t* __restrict__ rw,
+                                                   int rows, size_t section, const void* __restrict__ xin,
+                                                   int x_dtype, const uint32_t* __restrict__ rw,
                                                    const float2* __restrict__ rcs, int T, int k,
                                                    const int32_t* __restrict__ offsets,
                                                    const int32_t* __restrict__ active,
@@ -369,6 +370,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(const uint8_t* __restrict__ p
         const int nt = min(kMaxTok, q1 - c);
         const uint32_t* rec_g[kMaxTok];
         const float2* rcs_g[kMaxTok];
+        const void* xrow[kMaxTok];
 #pragma unroll
         for (int i = 0; i < kMaxTok; ++i) {
             const int q = c + min(i, nt - 1);
@@ -376,11 +378,16 @@ __global__ __launch_bounds__(512) void gemv_kernel(const uint8_t* __restrict__ p
             if (NMAT == 2) {
                 const int p = perm[q];
                 row = (p >= 0 && p < P) ? (size_t)(p / k) : 0;
+                xrow[i] = x_dtype == 0 ? (const void*)(static_cast<const float*>(xin) + row * K)
+                                       : (const void*)(static_cast<const uint16_t*>(xin) + row * K);
+                rec_g[i] = nullptr;
+                rcs_g[i] = nullptr;
             } else {
                 row = (size_t)q;
+                rec_g[i] = rw + row * nblk * 16;
+                rcs_g[i] = rcs + row * nblk;
+                xrow[i] = nullptr;
             }
-            rec_g[i] = rw + row * nblk * 16;
-            rcs_g[i] = rcs + row * nblk;
         }
         const bool first = c == q0;
         float acc[kMaxTok][NMAT];
@@ -389,8 +396,8 @@ __global__ __launch_bounds__(512) void gemv_kernel(const uint8_t* __restrict__ p
 #pragma unroll
             for (int m = 0; m < NMAT; ++m) acc[i][m] = 0.f;
         switch (nt) {
-            case 1: gemv_units<FMT, NMAT, 1>(tiles, u0, nu, lane, w, first, rec_g, rcs_g, lw, lc, acc); break;
-            default: gemv_units<FMT, NMAT, 2>(tiles, u0, nu, lane, w, first, rec_g, rcs_g, lw, lc, acc); break;
+            case 1: gemv_units<FMT, NMAT, 1>(tiles, u0, nu, lane, w, first, rec_g, rcs_g, xrow, x_dtype, lw, lc, acc); break;
+            default: gemv_units<FMT, NMAT, 2>(tiles, u0, nu, lane, w, first, rec_g, rcs_g, xrow, x_dtype, lw, lc, acc); break;
         }
 #pragma unroll
         for (int i = 0; i < kMaxTok; ++i)
@@ -424,11 +431,11 @@ __global__ __launch_bounds__(512) void gemv_kernel(const uint8_t* __restrict__ p
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Workspace: token records [T][H/32] (64 B + 8 B) then h records [T*k][I/32].
+// Workspace: h records [T*k][I/32] (64 B + 8 B).
 size_t decode_workspace_bytes(int T, int k, int H, int I) {
+    (void)H;
     const size_t P = (size_t)T * k;
-    return align256((size_t)T * (H / 32) * 64) + align256((size_t)T * (H / 32) * 8) +
-           align256(P * (I / 32) * 64) + align256(P * (I / 32) * 8);
+    return align256(P * (I / 32) * 64) + align256(P * (I / 32) * 8);
 }
 
 // Waves per workgroup and K units per wave: aim for ~4096 waves in flight
@@ -445,29 +452,12 @@ static void split_k(int units, long tiles_total, int* nw, int* upw) {
 hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s) {
     const size_t P = (size_t)a.T * a.k;
     uint8_t* ws = static_cast<uint8_t*>(a.ws);
-    uint32_t* xw = reinterpret_cast<uint32_t*>(ws);
-    size_t off = align256((size_t)a.T * (a.H / 32) * 64);
-    float2* xcs = reinterpret_cast<float2*>(ws + off);
-    off += align256((size_t)a.T * (a.H / 32) * 8);
-    uint32_t* hw = reinterpret_cast<uint32_t*>(ws + off);
-    off += align256(P * (a.I / 32) * 64);
-    float2* hcs = reinterpret_cast<float2*>(ws + off);
+    uint32_t* hw = reinterpret_cast<uint32_t*>(ws);
+    float2* hcs = reinterpret_cast<float2*>(ws + align256(P * (a.I / 32) * 64));
 
     const int max_active = (int)std::min<size_t>((size_t)a.S, P);
     if (max_active == 0 || a.T == 0) return hipSuccess;
 
-    // activation records
-    {
-        dim3 grid((a.H / 32 + 255) / 256, a.T);
-        timer_before(kStagePrep, s);
-        if (a.format == 1)
-            hipLaunchKernelGGL(prep_kernel<1>, grid, dim3(256), 0, s, a.x, a.x_dtype, a.H, xw, xcs);
-        else
-            hipLaunchKernelGGL(prep_kernel<0>, grid, dim3(256), 0, s, a.x, a.x_dtype, a.H, xw, xcs);
-        timer_after(kStagePrep, s);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
     // gate/up + SwiGLU
     {
         const int units = a.format == 1 ? a.H / 256 : a.H / 128;
@@ -477,11 +467,11 @@ hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s) {
         timer_before(kStageGateUp, s);
         if (a.format == 1)
             hipLaunchKernelGGL((gemv_kernel<1, 2>), grid, dim3(64 * nw), 0, s, a.pool, a.stride, a.S, a.H, a.I,
-                               (size_t)0, xw, xcs, a.T, a.k, a.slot_offsets, a.active_slots, a.num_active, a.perm_pair,
+                               (size_t)0, a.x, a.x_dtype, (const uint32_t*)nullptr, (const float2*)nullptr, a.T, a.k, a.slot_offsets, a.active_slots, a.num_active, a.perm_pair,
                                hw, hcs, (float*)nullptr, upw);
         else
             hipLaunchKernelGGL((gemv_kernel<0, 2>), grid, dim3(64 * nw), 0, s, a.pool, a.stride, a.S, a.H, a.I,
-                               (size_t)0, xw, xcs, a.T, a.k, a.slot_offsets, a.active_slots, a.num_active, a.perm_pair,
+                               (size_t)0, a.x, a.x_dtype, (const uint32_t*)nullptr, (const float2*)nullptr, a.T, a.k, a.slot_offsets, a.active_slots, a.num_active, a.perm_pair,
                                hw, hcs, (float*)nullptr, upw);
         timer_after(kStageGateUp, s);
         hipError_t e = hipGetLastError();
@@ -498,12 +488,14 @@ hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s) {
         timer_before(kStageDown, s);
         if (a.format == 1)
             hipLaunchKernelGGL((gemv_kernel<1, 1>), grid, dim3(64 * nw), 0, s, a.pool, a.stride, a.S, a.I, a.H,
-                               section, (const uint32_t*)hw, (const float2*)hcs, a.T, a.k, a.slot_offsets,
+                               section, (const void*)nullptr, 0, (const uint32_t*)hw, (const float2*)hcs, a.T, a.k,
+                               a.slot_offsets,
                                a.active_slots, a.num_active, a.perm_pair, (uint32_t*)nullptr, (float2*)nullptr, yp,
                                upw);
         else
             hipLaunchKernelGGL((gemv_kernel<0, 1>), grid, dim3(64 * nw), 0, s, a.pool, a.stride, a.S, a.I, a.H,
-                               section, (const uint32_t*)hw, (const float2*)hcs, a.T, a.k, a.slot_offsets,
+                               section, (const void*)nullptr, 0, (const uint32_t*)hw, (const float2*)hcs, a.T, a.k,
+                               a.slot_offsets,
                                a.active_slots, a.num_active, a.perm_pair, (uint32_t*)nullptr, (float2*)nullptr, yp,
                                upw);
         timer_after(kStageDown, s);

@@ -85,43 +85,23 @@ size_t prefill_workspace_bytes(int T, int k, int H, int I) {
 
 // ---------------------------------------------------------------- tiles
 
-// Exclusive prefix sum over the 1024 threads' values; returns the total.
-__device__ __forceinline__ int block_exclusive_scan_1024(int v, int* part, int* out_total) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += t;
-    }
-    if (lane == 63) part[wave] = incl;
-    __syncthreads();
-    if (tid < 16) {
-        int w = part[tid], wi = w;
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-            const int t = __shfl_up(wi, off, 16);
-            if ((tid & 15) >= off) wi += t;
-        }
-        part[16 + tid] = wi - w;
-        if (tid == 15) *out_total = wi;
-    }
-    __syncthreads();
-    const int r = part[16 + wave] + incl - v;
-    __syncthreads();
-    return r;
-}
-
 // One workgroup of 1024 threads, one active slot per thread.  Tiles are
 // grouped by row-block count, largest first (bucket 8 holds the full tiles),
-// and within a bucket ordered by slot.
+// and within a bucket ordered by slot.  The eight per-slot bucket counts are
+// packed as 16-bit fields into two 64-bit words (buckets 8..5 and 4..1) and
+// prefix-summed in one block scan; a count never exceeds the tile bound
+// (P / 256 + slots), checked on the host to fit 16 bits.
+__device__ __forceinline__ uint64_t shfl_up_u64(uint64_t v, int off) {
+    const uint32_t lo = __shfl_up((uint32_t)v, off, 64), hi = __shfl_up((uint32_t)(v >> 32), off, 64);
+    return ((uint64_t)hi << 32) | lo;
+}
+
 __global__ __launch_bounds__(1024) void prefill_tiles_kernel(const int32_t* __restrict__ offsets,
                                                              const int32_t* __restrict__ active,
                                                              const int32_t* __restrict__ num_active, int S, int P,
                                                              int4* __restrict__ tiles, int32_t* __restrict__ ntiles) {
-    __shared__ int part[32];
-    __shared__ int total;
-    const int tid = threadIdx.x;
+    __shared__ uint64_t wsum[2][16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int na = min(*num_active, min(S, P));
     int slot = -1, q0 = 0, n = 0;
     if (tid < na) {
@@ -134,21 +114,63 @@ __global__ __launch_bounds__(1024) void prefill_tiles_kernel(const int32_t* __re
     }
     const int full = n / kBM, rem = n - full * kBM;
     const int pblocks = (rem + 31) / 32;  // row blocks of the partial tile (0: none)
-    int base = 0;
-    for (int b = kRowBlocks; b >= 1; --b) {
-        const int c = (b == kRowBlocks ? full : 0) + (pblocks == b ? 1 : 0);
-        const int pos = base + block_exclusive_scan_1024(c, part, &total);
-        if (c > 0) {
-            int t = 0;
-            if (b == kRowBlocks)
-                for (; t < full; ++t) tiles[pos + t] = make_int4(slot, q0 + t * kBM, kBM, kRowBlocks);
-            if (pblocks == b) tiles[pos + t] = make_int4(slot, q0 + full * kBM, rem, b);
-        }
-        __syncthreads();
-        base += total;
-        __syncthreads();
+    // field f of word 0: bucket 8 - f; of word 1: bucket 4 - f
+    uint64_t c[2] = {0, 0};
+    c[0] = (uint64_t)(full + (pblocks == kRowBlocks ? 1 : 0));
+    if (pblocks >= 1 && pblocks < kRowBlocks) {
+        const int b = pblocks;
+        if (b >= 5) c[0] += (uint64_t)1 << (16 * (8 - b));
+        else c[1] += (uint64_t)1 << (16 * (4 - b));
     }
-    if (tid == 0) *ntiles = base;
+    uint64_t incl[2] = {c[0], c[1]};
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            const uint64_t t = shfl_up_u64(incl[w], off);
+            if (lane >= off) incl[w] += t;
+        }
+    }
+    if (lane == 63) {
+        wsum[0][wave] = incl[0];
+        wsum[1][wave] = incl[1];
+    }
+    __syncthreads();
+    uint64_t before[2] = {0, 0}, total[2] = {0, 0};
+    for (int w = 0; w < 16; ++w) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            if (w < wave) before[k] += wsum[k][w];
+            total[k] += wsum[k][w];
+        }
+    }
+    uint64_t excl[2] = {before[0] + incl[0] - c[0], before[1] + incl[1] - c[1]};
+    // bucket bases: bucket 8 first, then 7, ..., 1
+    int base[9];
+    int acc_base = 0;
+#pragma unroll
+    for (int b = kRowBlocks; b >= 1; --b) {
+        base[b] = acc_base;
+        const int w = b >= 5 ? 0 : 1, f = b >= 5 ? 8 - b : 4 - b;
+        acc_base += (int)((total[w] >> (16 * f)) & 0xFFFFu);
+    }
+    auto excl_of = [&](int b) {
+        const int w = b >= 5 ? 0 : 1, f = b >= 5 ? 8 - b : 4 - b;
+        return (int)((excl[w] >> (16 * f)) & 0xFFFFu);
+    };
+    if (slot >= 0) {
+        const int p8 = base[kRowBlocks] + excl_of(kRowBlocks);
+        for (int t = 0; t < full; ++t) tiles[p8 + t] = make_int4(slot, q0 + t * kBM, kBM, kRowBlocks);
+        if (pblocks == kRowBlocks) tiles[p8 + full] = make_int4(slot, q0 + full * kBM, rem, kRowBlocks);
+        else if (pblocks >= 1) {
+            int pb = 0;
+#pragma unroll
+            for (int b = 1; b < kRowBlocks; ++b)
+                if (b == pblocks) pb = base[b] + excl_of(b);
+            tiles[pb] = make_int4(slot, q0 + full * kBM, rem, pblocks);
+        }
+    }
+    if (tid == 0) *ntiles = acc_base;
 }
 
 // ------------------------------------------------------------- helpers
@@ -546,71 +568,103 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
     // Epilogue through LDS (both A buffers are free after the loop's last
     // barrier): in passes over row blocks, the waves write their accumulator
-    // rows row-major into one buffer, then every thread stores 16-byte chunks
-    // of whole rows.  Passes alternate between the two buffers, so one
-    // barrier per pass suffices.
+    // rows row-major into one 64 KB buffer, then every thread stores 16-byte
+    // chunks of whole rows.  Passes alternate between the two buffers, so one
+    // barrier per pass suffices.  Rows are unpadded; the 16-byte chunk index
+    // is xor-ed with 4 on rows whose bit 2 is set, so the two half-waves'
+    // writes (rows r and r + 4) fall in different banks.
+    auto swz = [](int row, int chunk) { return chunk ^ (((row >> 2) & 1) << 2); };
     if (GATEUP) {
-        // h = silu(g) * u, rounded to bf16: 128 rows x 128 features per pass
-        // (row stride 272 bytes), stored at position qb + row.
-        constexpr int kStride = kGateUpFeatures * 2 + 16;
-        constexpr int kChunks = kGateUpFeatures * 2 / 16;  // per row
+        // h = silu(g) * u, rounded to bf16: all rows x 128 features (256
+        // bytes per row) in one pass, stored at position qb + row.
+        constexpr int kRowBytes = kGateUpFeatures * 2;
+        constexpr int kChunks = kRowBytes / 16;
         const int f = 32 * wave + r32;
+        uint8_t* stage = reinterpret_cast<uint8_t*>(sA0);
         uint16_t* hout = static_cast<uint16_t*>(out) + (size_t)nt * kGateUpFeatures;
-#pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-            if (4 * pass >= nblk) break;
-            uint8_t* stage = reinterpret_cast<uint8_t*>(pass ? sA1 : sA0);
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int i = 4 * pass + ii;
-                if (i < nblk) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int rl = 32 * ii + 8 * (r >> 2) + 4 * hsel + (r & 3);
-                        const float hv = fast_silu(acc[i][0][r]) * acc[i][1][r];
-                        *reinterpret_cast<uint16_t*>(stage + rl * kStride + 2 * f) =
-                            __builtin_bit_cast(uint16_t, (__bf16)hv);
-                    }
-                }
-            }
-            __syncthreads();
-            const int prow = min(128, rows - 128 * pass);
-            for (int ch = tid; ch < prow * kChunks; ch += kThreads) {
-                const int rl = ch / kChunks, cc = ch - rl * kChunks;
-                const uint4 v = *reinterpret_cast<const uint4*>(stage + rl * kStride + 16 * cc);
-                *reinterpret_cast<uint4*>(hout + (size_t)(qb + 128 * pass + rl) * I + 8 * cc) = v;
-            }
-        }
-    } else {
-        // y: 32 rows x 256 columns (fp32 or bf16) per pass, each row stored
-        // to its pair's row of y_pairs.
-        const int esize = y_dtype == 0 ? 4 : 2;
-        const int stride = kDownColumns * esize + 16;
-        const int cpr = kDownColumns * esize / 16;  // 16-byte chunks per row
-        const int col0 = 64 * wave + r32;
-        uint8_t* y = static_cast<uint8_t*>(out);
 #pragma unroll
         for (int i = 0; i < kRowBlocks; ++i) {
             if (i >= nblk) break;
-            uint8_t* stage = reinterpret_cast<uint8_t*>((i & 1) ? sA1 : sA0);
 #pragma unroll
-            for (int m = 0; m < 2; ++m)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int rl = 8 * (r >> 2) + 4 * hsel + (r & 3);
-                    uint8_t* d = stage + rl * stride + (col0 + 32 * m) * esize;
-                    if (esize == 4) *reinterpret_cast<float*>(d) = acc[i][m][r];
-                    else *reinterpret_cast<uint16_t*>(d) = __builtin_bit_cast(uint16_t, (__bf16)acc[i][m][r]);
-                }
-            __syncthreads();
-            const int prow = min(32, rows - 32 * i);
-            for (int ch = tid; ch < prow * cpr; ch += kThreads) {
+            for (int r = 0; r < 16; ++r) {
+                const int row = 32 * i + 8 * (r >> 2) + 4 * hsel + (r & 3);
+                const float hv = fast_silu(acc[i][0][r]) * acc[i][1][r];
+                *reinterpret_cast<uint16_t*>(stage + row * kRowBytes + 16 * swz(row, f >> 3) + 2 * (f & 7)) =
+                    __builtin_bit_cast(uint16_t, (__bf16)hv);
+            }
+        }
+        __syncthreads();
+        for (int ch = tid; ch < rows * kChunks; ch += kThreads) {
+            const int row = ch / kChunks, cc = ch - row * kChunks;
+            const uint4 v = *reinterpret_cast<const uint4*>(stage + row * kRowBytes + 16 * swz(row, cc));
+            *reinterpret_cast<uint4*>(hout + (size_t)(qb + row) * I + 8 * cc) = v;
+        }
+    } else {
+        // y: 256 columns per row, 128 rows per pass in bf16, 64 in fp32; each
+        // row stored to its pair's row of y_pairs.
+        uint8_t* y = static_cast<uint8_t*>(out);
+        auto store_rows = [&](const uint8_t* stage, int row0, int nrows, int row_bytes) {
+            const int cpr = row_bytes / 16;
+            for (int ch = tid; ch < nrows * cpr; ch += kThreads) {
                 const int rl = ch / cpr, cc = ch - rl * cpr;
-                const int p = sidx[32 * i + rl];
+                const int p = sidx[row0 + rl];
                 if (p >= 0) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(stage + rl * stride + 16 * cc);
-                    *reinterpret_cast<uint4*>(y + ((size_t)p * H + (size_t)nt * kDownColumns) * esize + 16 * cc) = v;
+                    const uint4 v = *reinterpret_cast<const uint4*>(stage + rl * row_bytes + 16 * swz(rl, cc));
+                    *reinterpret_cast<uint4*>(y + ((size_t)p * H + (size_t)nt * kDownColumns) * (row_bytes / kDownColumns) +
+                                              16 * cc) = v;
                 }
+            }
+        };
+        if (y_dtype != 0) {
+            constexpr int kRowBytes = kDownColumns * 2;
+#pragma unroll
+            for (int pass = 0; pass < 2; ++pass) {
+                if (4 * pass >= nblk) break;
+                uint8_t* stage = reinterpret_cast<uint8_t*>(pass ? sA1 : sA0);
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int i = 4 * pass + ii;
+                    if (i < nblk) {
+#pragma unroll
+                        for (int m = 0; m < 2; ++m) {
+                            const int col = 64 * wave + 32 * m + r32;
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int rl = 32 * ii + 8 * (r >> 2) + 4 * hsel + (r & 3);
+                                *reinterpret_cast<uint16_t*>(stage + rl * kRowBytes + 16 * swz(rl, col >> 3) +
+                                                             2 * (col & 7)) =
+                                    __builtin_bit_cast(uint16_t, (__bf16)acc[i][m][r]);
+                            }
+                        }
+                    }
+                }
+                __syncthreads();
+                store_rows(stage, 128 * pass, min(128, rows - 128 * pass), kRowBytes);
+            }
+        } else {
+            constexpr int kRowBytes = kDownColumns * 4;
+#pragma unroll
+            for (int pass = 0; pass < 4; ++pass) {
+                if (2 * pass >= nblk) break;
+                uint8_t* stage = reinterpret_cast<uint8_t*>((pass & 1) ? sA1 : sA0);
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii) {
+                    const int i = 2 * pass + ii;
+                    if (i < nblk) {
+#pragma unroll
+                        for (int m = 0; m < 2; ++m) {
+                            const int col = 64 * wave + 32 * m + r32;
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int rl = 32 * ii + 8 * (r >> 2) + 4 * hsel + (r & 3);
+                                *reinterpret_cast<float*>(stage + rl * kRowBytes + 16 * swz(rl, col >> 2) +
+                                                          4 * (col & 3)) = acc[i][m][r];
+                            }
+                        }
+                    }
+                }
+                __syncthreads();
+                store_rows(stage, 64 * pass, min(64, rows - 64 * pass), kRowBytes);
             }
         }
     }
@@ -622,6 +676,7 @@ hipError_t launch_ffn_prefill_q4k(const FfnArgs& a, hipStream_t s) {
     const int P = a.T * a.k;
     const int mt = max_tiles(P, a.S);
     if (a.S > 1024) return hipErrorInvalidValue;  // one tiles-kernel thread per active slot
+    if (mt > 0xFFFF) return hipErrorInvalidValue;  // 16-bit bucket counts in the tiles kernel
     uint8_t* ws = static_cast<uint8_t*>(a.ws);
     uint16_t* h = reinterpret_cast<uint16_t*>(ws);
     size_t off = align256((size_t)P * a.I * 2);
@@ -629,10 +684,10 @@ hipError_t launch_ffn_prefill_q4k(const FfnArgs& a, hipStream_t s) {
     off += align256((size_t)max_tiles(P, kMaxExpertsInternal) * 16);
     int32_t* ntiles = reinterpret_cast<int32_t*>(ws + off);
 
-    timer_before(kStagePrep, s);
+    timer_before(kStagePrefillTiles, s);
     hipLaunchKernelGGL(prefill_tiles_kernel, dim3(1), dim3(1024), 0, s, a.slot_offsets, a.active_slots, a.num_active,
                        a.S, P, tiles, ntiles);
-    timer_after(kStagePrep, s);
+    timer_after(kStagePrefillTiles, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 

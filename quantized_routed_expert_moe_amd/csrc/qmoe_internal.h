@@ -62,7 +62,7 @@ struct ActRec;  // (documentation only; the buffers are plain uint32/float2 arra
 enum Stage {
     kStageRoute = 0,
     kStageBatches = 1,
-    kStagePrep = 2,
+    kStagePrefillTiles = 2,
     kStageGateUp = 3,
     kStageDown = 4,
     kStageCombine = 5,

@@ -92,6 +92,14 @@ def test_ffn_q8_0_rejects_prefill():
     assert st == Q.MOE_ERR_UNSUPPORTED and "Q4_K only" in msg
 
 
+def test_ffn_q4k_prefill_size_limits():
+    """The prefill GEMMs address activation rows with 32-bit byte offsets:
+    a token count whose h buffer (T*k*I*2 bytes) reaches 4 GiB is refused."""
+    st, msg = _ffn("moe_expert_ffn_q4k", T=400000, k=8, H=2048, I=768, path=Q.MOE_PATH_PREFILL, x_dtype=Q.MOE_BF16,
+                   y_dtype=Q.MOE_BF16, ws_bytes=1 << 40)
+    assert st == Q.MOE_ERR_UNSUPPORTED and "prefill path limits" in msg, msg
+
+
 def test_ffn_q8_0_rejects_shape():
     st, msg = _ffn("moe_expert_ffn_q8_0", H=256, I=96)
     assert st == Q.MOE_ERR_UNSUPPORTED and "multiples of 128" in msg
