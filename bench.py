@@ -35,7 +35,10 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA util (prefill), 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ffn_gateup_q4k_qwen3_decode.txt")
-KERNEL_SOURCE = os.path.join(ROOT, "quantized_routed_expert_moe_amd", "csrc", "ffn_decode.hip")
+# sources the decode gate/up kernel is compiled from (the traffic figures are
+# valid only for exactly these)
+KERNEL_SOURCES = [os.path.join(ROOT, "quantized_routed_expert_moe_amd", "csrc", f)
+                  for f in ("ffn_decode.hip", "device_common.h", "qmoe_internal.h")]
 
 
 def parse():
@@ -54,8 +57,11 @@ def parse():
     return ap.parse_args()
 
 
-def source_hash(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_hash(paths: list) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic() -> dict | None:
@@ -68,7 +74,7 @@ def read_traffic() -> dict | None:
         if "=" in line and not line.startswith("#"):
             key, val = line.split("=", 1)
             kv[key.strip()] = val.strip()
-    if kv.get("kernel_source_sha256_16") != source_hash(KERNEL_SOURCE):
+    if kv.get("kernel_source_sha256_16") != source_hash(KERNEL_SOURCES):
         return None
     try:
         return dict(bytes_per_launch=float(kv["hbm_bytes_per_launch"]), note=kv.get("note", ""))

@@ -59,7 +59,10 @@ __device__ __forceinline__ float half_wave_sum(float v) {
     return v + __shfl_xor(v, 16, 64);
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// silu(z) = z / (1 + e^-z) with the hardware exp2 and reciprocal (a few ulp).
+__device__ __forceinline__ float fast_silu(float z) {
+    return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
+}
 
 // d*sc_j and dmin*m_j of the eight sub-blocks of a Q4_K super-block header
 // (16 bytes: d, dmin, then the 12 packed scale bytes).

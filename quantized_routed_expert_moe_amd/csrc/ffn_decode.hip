@@ -414,7 +414,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(const uint8_t* __restrict__ p
                     for (int m = 0; m < NMAT; ++m) v[m] += red[wv][i][m][lane];
                 const int q = c + i;
                 if (NMAT == 2) {
-                    const float h = silu(v[0]) * v[NMAT - 1];
+                    const float h = fast_silu(v[0]) * v[NMAT - 1];
                     const int nblk_out = rows / 32;
                     store_h_record<FMT>(h, rg, lane, hw + (size_t)q * nblk_out * 16, hcs + (size_t)q * nblk_out);
                 } else {
@@ -423,7 +423,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(const uint8_t* __restrict__ p
                 }
             }
         }
-        __syncthreads();
+        if (c + kMaxTok < q1) __syncthreads();  // red[] is reused by the next chunk
     }
 }
 

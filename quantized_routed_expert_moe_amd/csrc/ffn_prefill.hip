@@ -247,11 +247,6 @@ __device__ __forceinline__ void dq_bc(DqPart& d, int half, float ds512, float nd
     }
 }
 
-// silu(z) = z / (1 + e^-z) with the hardware exp2 and reciprocal.
-__device__ __forceinline__ float fast_silu(float z) {
-    return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
-}
-
 // s_waitcnt vmcnt(0), other counters unconstrained (gfx9 encoding).
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
