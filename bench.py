@@ -52,6 +52,10 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=30,
                     help="timed steps of the T=4096 prefill layer reported beside the decode line (0 = skip)")
+    ap.add_argument("--dsv3-steps", type=int, default=400,
+                    help="timed steps of the DeepSeek-V3-shaped decode layer at T=2 and T=4 (0 = skip)")
+    ap.add_argument("--stack-replays", type=int, default=10,
+                    help="timed replays of the 58-layer partial-residency stack (0 = skip)")
     ap.add_argument("--profile-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
     return ap.parse_args()
@@ -213,6 +217,10 @@ def main():
     prefill = None
     if args.prefill_steps > 0:
         prefill = bench_prefill(args, blobs, pool0, stride)
+    del pools, pool0
+    torch.cuda.empty_cache()
+    dsv3 = bench_dsv3(args, threads) if args.dsv3_steps > 0 else None
+    stack = bench_stack(args, threads) if args.stack_replays > 0 else None
 
     traffic = read_traffic()
     out = {
@@ -239,6 +247,8 @@ def main():
                      "avg_launch_us": round(kern["ffn_gateup"]["avg_us"], 3)},
         "cpu_baseline": cpu,
         "prefill": prefill,
+        "dsv3_decode": dsv3,
+        "stack": stack,
         "kernels_us": {k2: round(v["avg_us"], 3) for k2, v in kern.items()},
         "down_gemv_GBs": round(dn_gbs, 1),
         "layer_effective_GBs": round(layer_gbs, 1),
@@ -310,8 +320,213 @@ def bench_prefill(args, blobs, pool, stride) -> dict:
         "down_gemm_TFLOPs": round(dn_tf, 1),
         "expert_gemms_TFLOPs": round((gu_flop + dn_flop) / ((kern["gemm_gateup"] + kern["gemm_down"]) * 1e-6) / 1e12,
                                      1),
+        "expert_gemms_frac": round((gu_flop + dn_flop) / ((kern["gemm_gateup"] + kern["gemm_down"]) * 1e-6) / 1e12 /
+                                   MFMA_BF16_PEAK_TFLOPS, 4),
         "kernels_us": {k2: round(v, 2) for k2, v in kern.items()},
     }
+
+
+def bench_dsv3(args, threads: int) -> dict:
+    """The DeepSeek-V3-shaped decode layer (256 Q4_K routed experts, top-8
+    sigmoid x2.5, one Q8_0 shared expert) at T = 2 and T = 4, graph-replayed
+    like the headline layer; all 256 experts resident (6.3 GB pool, so a step's
+    ~16 experts x 24.8 MB never sit in the 256 MB Infinity Cache)."""
+    import numpy as np
+    import torch
+
+    import fixtures as F
+    import quantized_routed_expert_moe_amd as Q
+    from concurrent.futures import ThreadPoolExecutor
+    from fixtures import workloads as W
+    from quantized_routed_expert_moe_amd.layer import LayerSpec, MoELayer
+
+    res = {}
+    wl0 = W.DSV3_DECODE_T2
+    blobs = W.expert_blobs(wl0)
+    nb = Q.moe_expert_blob_bytes(wl0.fmt, wl0.H, wl0.I)
+    stride = (nb + 255) // 256 * 256
+    host = np.zeros((wl0.E, stride), dtype=np.uint8)
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(lambda e: Q.moe_pack_expert(wl0.fmt, blobs[e], wl0.H, wl0.I, out=host[e, :nb]), range(wl0.E)))
+    pool = torch.from_numpy(host).cuda()
+    del host, blobs
+    sh = W.shared_blob(wl0)
+    nbs = Q.moe_expert_blob_bytes(F.Q8_0, wl0.H, wl0.I_shared)
+    sh_host = np.zeros((1, (nbs + 255) // 256 * 256), dtype=np.uint8)
+    Q.moe_pack_expert(F.Q8_0, sh, wl0.H, wl0.I_shared, out=sh_host[0, :nbs])
+    shared = torch.from_numpy(sh_host).cuda()
+    soe = torch.arange(wl0.E, dtype=torch.int32, device="cuda")
+    expert_bytes = 3 * wl0.H * wl0.I // 256 * 144
+    gateup_bytes = 2 * wl0.H * wl0.I // 256 * 144
+    shared_bytes = 3 * wl0.H * wl0.I_shared // 32 * 34
+    for wl in (W.DSV3_DECODE_T2, W.DSV3_DECODE_T4):
+        spec = LayerSpec(wl.fmt, wl.H, wl.I, wl.E, wl.k, wl.score, wl.renormalize, wl.scale, wl.I_shared)
+        layer = MoELayer(spec, wl.T, wl.E, pool, stride, soe, shared, Q.MOE_PATH_DECODE)
+        nbatch = 8
+        xs = [torch.from_numpy(W.x_of(wl, seed=200 + i)).cuda() for i in range(nbatch)]
+        ls = [torch.from_numpy(W.logits_of(wl, seed=200 + i)).cuda() for i in range(nbatch)]
+        uniq = []
+        for i in range(nbatch):
+            layer.forward(xs[i], ls[i])
+            uniq.append(int(torch.unique(layer.ids).numel()))
+        torch.cuda.synchronize()
+        steps = args.dsv3_steps
+        Q.moe_timer_begin(3, steps)
+        for i in range(steps):
+            layer.forward(xs[i % nbatch], ls[i % nbatch])
+        torch.cuda.synchronize()
+        gu_ms, gu_n = Q.moe_timer_end(3)
+        # gate/up launches alternate routed and shared; the routed ones are every other one
+        graphs = []
+        for i in range(nbatch):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                layer.forward(xs[i], ls[i])
+            graphs.append(g)
+        for i in range(16):
+            graphs[i % nbatch].replay()
+        torch.cuda.synchronize()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(steps):
+            graphs[i % nbatch].replay()
+        stop.record()
+        torch.cuda.synchronize()
+        ms_step = start.elapsed_time(stop) / steps
+        mean_uniq = float(np.mean([uniq[i % nbatch] for i in range(steps)]))
+        layer_bytes = mean_uniq * expert_bytes + shared_bytes
+        layer_gbs = layer_bytes / (ms_step * 1e-3) / 1e9
+        res[f"T{wl.T}"] = {
+            "workload": wl.name, "tokens_per_s": round(wl.T / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 4),
+            "unique_experts_per_step": round(mean_uniq, 2),
+            "layer_bytes_per_step": round(layer_bytes), "layer_GBs": round(layer_gbs, 1),
+            "layer_frac_of_hbm": round(layer_gbs / HBM_PEAK_GBS, 4),
+            "gateup_launch_us_routed_and_shared_avg": round(1e3 * gu_ms / max(gu_n, 1), 2),
+        }
+        del graphs, layer
+        torch.cuda.empty_cache()
+    res["bytes"] = {"routed_q4k_expert": expert_bytes, "routed_gateup": gateup_bytes, "shared_q8_0": shared_bytes}
+    res["note"] = ("layer_GBs = (unique routed experts x 24.77 MB + 46.79 MB shared) per step / graph-replayed step "
+                   "time, i.e. the whole layer (five routed and two shared-expert kernels) against the HBM peak")
+    del pool, shared
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_stack(args, threads: int) -> dict:
+    """The 58-layer DeepSeek-V3-shaped stack under partial residency (96 of 256
+    experts per layer + 8 staging slots, one hipGraph), decode T = 2: replay
+    time and bytes, swap-round copy rate alone and while replays run, graph
+    node count."""
+    import numpy as np
+    import torch
+
+    import fixtures as F
+    import quantized_routed_expert_moe_amd as Q
+    from concurrent.futures import ThreadPoolExecutor
+    from fixtures import workloads as W
+    from quantized_routed_expert_moe_amd.layer import LayerSpec
+    from quantized_routed_expert_moe_amd.stack import ResidentStack
+
+    wl = W.DSV3_STACK
+    n_blobs, n_shared = 256, 8
+    t0 = time.time()
+    blobs = W.expert_blobs(wl)  # blob b = expert b of layer 0; expert e of layer l uses blob (e + 37 l) mod 256
+    nb = Q.moe_expert_blob_bytes(wl.fmt, wl.H, wl.I)
+    stride = (nb + 255) // 256 * 256
+    host_blobs = torch.zeros((n_blobs, stride), dtype=torch.uint8).pin_memory()
+    hb = host_blobs.numpy()
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(lambda b: Q.moe_pack_expert(wl.fmt, blobs[b], wl.H, wl.I, out=hb[b, :nb]), range(n_blobs)))
+    del blobs
+    dev_blobs = host_blobs.cuda()
+    nbs = Q.moe_expert_blob_bytes(F.Q8_0, wl.H, wl.I_shared)
+    sh_host = torch.zeros((n_shared, (nbs + 255) // 256 * 256), dtype=torch.uint8).pin_memory()
+    for i in range(n_shared):
+        sh = F.expert_blob(F.Q8_0, wl.seed, 100 + i, F.TAG_SHARED_EXPERT, wl.H, wl.I_shared)
+        Q.moe_pack_expert(F.Q8_0, sh, wl.H, wl.I_shared, out=sh_host.numpy()[i, :nbs])
+    ranked = [W.frequency_resident_set(wl, l) for l in range(wl.layers)]
+    spec = LayerSpec(wl.fmt, wl.H, wl.I, wl.E, wl.k, wl.score, wl.renormalize, wl.scale, wl.I_shared)
+    st = ResidentStack(spec, wl.layers, wl.T, wl.resident, wl.staging, ranked,
+                       lambda l, e: (e + 37 * l) % n_blobs, host_blobs, dev_blobs, lambda l: l % n_shared, sh_host)
+    del dev_blobs
+    torch.cuda.empty_cache()
+    st.set_inputs([torch.from_numpy(W.x_of(wl, l)) for l in range(wl.layers)],
+                  [torch.from_numpy(W.logits_of(wl, l)) for l in range(wl.layers)])
+    setup_s = time.time() - t0
+    st.capture()
+    nodes = st.graph_node_count()
+    for _ in range(3):
+        st.replay()
+    torch.cuda.synchronize()
+
+    def replay_bytes() -> tuple[float, float]:
+        expert_bytes = 3 * wl.H * wl.I // 256 * 144
+        shared_bytes = 3 * wl.H * wl.I_shared // 32 * 34
+        total, served = 0.0, 0.0
+        for l, lay in enumerate(st.layers):
+            ids = lay.ids.cpu().numpy().ravel()
+            soe = st.maps[l]
+            resident = {int(e) for e in ids if soe[e] >= 0}
+            total += len(resident) * expert_bytes + shared_bytes
+            served += float(np.mean(soe[ids] >= 0))
+        return total, served / wl.layers
+
+    # replays alone
+    R = args.stack_replays
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(R):
+        st.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    replay_ms = start.elapsed_time(stop) / R
+    nbytes, share = replay_bytes()
+    swap_bytes = 8 * wl.layers * (3 * wl.H * wl.I // 256 * 144)
+
+    # one swap round with nothing else on the GPU
+    st.swap_begin(8)
+    st.swap_copies_done.synchronize()
+    swap_alone_ms = st.swap_start.elapsed_time(st.swap_copies_done)
+    st.swap_commit(block=True)
+    st.replay()
+    torch.cuda.synchronize()
+
+    # one swap round while replays run back to back on the compute stream
+    st.swap_begin(8)
+    w0 = time.time()
+    n_during = 0
+    while not st.swap_copies_done.query() and n_during < 1000:
+        st.replay()
+        st.replay_done.synchronize()
+        n_during += 1
+    during_s = time.time() - w0
+    st.swap_copies_done.synchronize()
+    swap_during_ms = st.swap_start.elapsed_time(st.swap_copies_done)
+    st.swap_commit(block=True)
+    st.replay()
+    torch.cuda.synchronize()
+    replay_ms_during = 1e3 * during_s / max(n_during, 1)
+    out = {
+        "workload": wl.name, "layers": wl.layers, "resident": wl.resident, "staging": wl.staging,
+        "graph_nodes": nodes, "replays": R, "replay_ms": round(replay_ms, 3),
+        "layer_us": round(1e3 * replay_ms / wl.layers, 2),
+        "tokens_per_s_per_layer": round(wl.T / (replay_ms * 1e-3 / wl.layers), 1),
+        "stack_tokens_per_s": round(wl.T / (replay_ms * 1e-3), 1),
+        "bytes_per_replay": round(nbytes), "replay_GBs": round(nbytes / (replay_ms * 1e-3) / 1e9, 1),
+        "replay_frac_of_hbm": round(nbytes / (replay_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "card_served_share": round(share, 4),
+        "swap_round_bytes": swap_bytes,
+        "swap_alone_ms": round(swap_alone_ms, 1), "swap_alone_GBs": round(swap_bytes / (swap_alone_ms * 1e-3) / 1e9, 1),
+        "swap_during_replays_ms": round(swap_during_ms, 1),
+        "swap_during_replays_GBs": round(swap_bytes / (swap_during_ms * 1e-3) / 1e9, 1),
+        "replays_during_swap": n_during, "replay_ms_during_swap": round(replay_ms_during, 3),
+        "pcie_gen5_x16_GBs": 64.0,
+        "setup_s": round(setup_s, 1),
+    }
+    del st
+    torch.cuda.empty_cache()
+    return out
 
 
 if __name__ == "__main__":

@@ -401,31 +401,36 @@ __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* s
                         }
                     }
                 }
+                // Item order: the A fragment reads come first (items 0-10), so
+                // they have returned long before the next step's first MFMA.
+                // That matters because while a global->LDS DMA is in flight
+                // the compiler can only wait for LDS reads with lgkmcnt(0),
+                // i.e. for all of them.
                 auto item = [&](int j) {
                     switch (j) {
-                        case 0:
+                        case 2:
                             if (s < 4) {
                                 if (2 * s < NB) dma_unit(nst, cur ^ 1, 2 * s);
                                 load_b_one(nst, rb[cur ^ 1], 0, s);
                                 if (u == 1 && s == 0) load_hdr(min(sb + 1, nsb - 1), hdr);
                             }
                             break;
-                        case 3:
+                        case 8:
                             if (s < 4) {
                                 if (2 * s + 1 < NB) dma_unit(nst, cur ^ 1, 2 * s + 1);
                                 load_b_one(nst, rb[cur ^ 1], 1, s);
                             }
                             break;
-                        case 2: dq_a(dp[0], wsrc[0]); break;
-                        case 5: dq_bc(dp[0], 0, dsv[0], ndv[0]); break;
-                        case 7: dq_bc(dp[0], 1, dsv[0], ndv[0]); break;
-                        case 9: dq_a(dp[1], wsrc[1]); break;
-                        case 11: dq_bc(dp[1], 0, dsv[1], ndv[1]); break;
-                        case 13: dq_bc(dp[1], 1, dsv[1], ndv[1]); break;
+                        case 5: dq_a(dp[0], wsrc[0]); break;
+                        case 11: dq_bc(dp[0], 0, dsv[0], ndv[0]); break;
+                        case 12: dq_bc(dp[0], 1, dsv[0], ndv[0]); break;
+                        case 13: dq_a(dp[1], wsrc[1]); break;
+                        case 14: dq_bc(dp[1], 0, dsv[1], ndv[1]); break;
+                        case 15: dq_bc(dp[1], 1, dsv[1], ndv[1]); break;
                         default: {
-                            // A fragment reads: items 1, 4, 6, 8, 10, 12, 14, 15
-                            const int ri = j == 1 ? 0 : j == 4 ? 1 : j == 6 ? 2 : j == 8 ? 3 : j == 10 ? 4
-                                         : j == 12 ? 5 : j == 14 ? 6 : 7;
+                            // A fragment reads: items 0, 1, 3, 4, 6, 7, 9, 10
+                            const int ri = j == 0 ? 0 : j == 1 ? 1 : j == 3 ? 2 : j == 4 ? 3 : j == 6 ? 4 : j == 7 ? 5
+                                         : j == 9 ? 6 : 7;
                             if (!last && ri < NB) {
                                 const int chunk = 2 * (s + 1) + (lane >> 5);
                                 const int off = frag_row + (chunk >> 3) * 64 + ((chunk & 7) ^ (lane & 7));
@@ -435,6 +440,12 @@ __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* s
                         }
                     }
                 };
+                // The previous step's fragment reads were all issued at least
+                // five MFMAs ago: wait for them here, where it costs nothing,
+                // instead of wherever the first use of a fragment lands (an
+                // LDS DMA in flight makes every LDS wait a wait for all reads).
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt unconstrained
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int n = 0; n < 2 * NB; ++n) {
                     const int i = n >> 1, m = n & 1;

@@ -2,8 +2,9 @@
 
 Orchestration only: device buffers come from torch, every step is a call
 into libqmoe.  The optional shared expert runs through moe_expert_ffn_q8_0
-with a one-slot identity batch.  All work is enqueued on one stream, without
-host synchronisation, so `forward` can be captured into a HIP graph.
+with a one-slot identity batch, on a side stream forked from the layer's
+stream by an event and joined before the combine.  Nothing synchronises with
+the host, so `forward` can be captured into a HIP graph.
 """
 from __future__ import annotations
 
@@ -78,11 +79,27 @@ class MoELayer:
                                                                    MOE_PATH_DECODE)), dtype=torch.uint8, device=device)
             self.y_shared = torch.zeros((T_max, H), dtype=torch.float32, device=device)
             self.sh_stride = shared_pool.shape[-1]
+            # The shared expert needs no routing: it runs on a side stream
+            # (default priority) forked from the layer's stream, so its weight
+            # stream overlaps routing, batching and the routed FFN; combine
+            # joins it.  Fork and join are events, so the pattern is captured
+            # into graphs as two dependency edges.
+            self.sh_stream = torch.cuda.Stream(device=device)
+            self.sh_fork = torch.cuda.Event()
+            self.sh_join = torch.cuda.Event()
 
     def forward(self, x: torch.Tensor, logits: torch.Tensor, stream=None, slot_pool: torch.Tensor | None = None):
         spec, T = self.spec, x.shape[0]
         assert T == self.T_max, "buffers are sized for T_max rows"
         pool = self.slot_pool if slot_pool is None else slot_pool
+        main = torch.cuda.current_stream() if stream is None else stream
+        if spec.I_shared:
+            self.sh_fork.record(main)
+            self.sh_stream.wait_event(self.sh_fork)
+            moe_expert_ffn_q8_0(self.shared_pool, self.sh_stride, 1, spec.H, spec.I_shared, x, 1, self.sh_offsets,
+                                self.sh_active, self.sh_num, self.sh_perm, self.y_shared, MOE_PATH_DECODE, self.sh_ws,
+                                self.sh_stream)
+            self.sh_join.record(self.sh_stream)
         moe_route_topk(logits, spec.k, spec.score, spec.renormalize, spec.scale, self.ids, self.w, stream)
         moe_build_expert_batches(self.ids, self.w, spec.E, self.slot_of_expert, self.S, self.slot_offsets,
                                  self.active_slots, self.num_active, self.perm_pair, self.host_token, self.host_expert,
@@ -92,9 +109,7 @@ class MoELayer:
             self.num_active, self.perm_pair, self.y_pairs, self.path, self.ws, stream)
         y_shared = None
         if spec.I_shared:
-            moe_expert_ffn_q8_0(self.shared_pool, self.sh_stride, 1, spec.H, spec.I_shared, x, 1, self.sh_offsets,
-                                self.sh_active, self.sh_num, self.sh_perm, self.y_shared, MOE_PATH_DECODE, self.sh_ws,
-                                stream)
+            main.wait_event(self.sh_join)
             y_shared = self.y_shared
         moe_combine(self.y_pairs, self.ids, self.w, self.slot_of_expert, y_shared, self.y, stream)
         return self.y

@@ -12,11 +12,12 @@ Orchestration only; every computation is a libqmoe call:
     (expert -> slot, -1 = host), a shared expert, the layer's buffers;
   * capture(): all layers back to back on one stream into one graph, each
     layer followed by the D2H copy of its host list into pinned memory;
-  * swap(): for every layer, copy the packed blobs of `n` incoming experts
-    from pinned host memory into free slots with hipMemcpyAsync on a side
-    stream (overlapping the running replay: free slots are not in the
-    current map), then, once the replay has finished, upload the new slot
-    maps; the next replay waits for that.
+  * swap_begin() / swap_commit(): for every layer, copy the packed blobs of
+    `n` incoming experts from pinned host memory into free slots with
+    hipMemcpyAsync on a side stream, overlapping any number of replays (free
+    slots are not in the current maps); once the copies have landed, upload
+    the new slot maps after the replay in flight; the next replay waits for
+    that.  swap() does both for one round.
 
 Swap rule (the pages only say experts are swapped between steps): the
 incoming experts are the next `n` non-resident ones in the layer's frequency
@@ -102,6 +103,8 @@ class ResidentStack:
         self.swap_copies_done = torch.cuda.Event(enable_timing=True)
         self.maps_done = torch.cuda.Event(enable_timing=True)
         self.pending_maps = False
+        self.swap_in_flight = False
+        self.swap_plans = None
 
     # ------------------------------------------------------------ step
     def set_inputs(self, xs, logits) -> None:
@@ -183,14 +186,17 @@ class ResidentStack:
         outgoing = resident[:n]
         return incoming, outgoing
 
-    def swap(self, n: int = 8) -> dict:
-        """One swap round on every layer: copies on the side stream overlap the
-        replay in flight; the new slot maps are uploaded after it finishes."""
+    def swap_begin(self, n: int = 8) -> dict:
+        """Start one swap round on every layer: plan it and enqueue the copies
+        of the incoming experts into free slots on the side stream.  Returns at
+        once; replays may go on with the current maps meanwhile (free slots are
+        not referenced by them).  The side stream runs the rounds in order, so
+        these copies also follow the previous round's map upload, i.e. the
+        last replay that could still use a slot freed by that round."""
+        assert not self.swap_in_flight, "commit the previous swap round first"
         plans = []
-        side = self.side
-        side.synchronize()  # the previous round's copies and map uploads are complete
-        self.swap_start.record(side)
-        with torch.cuda.stream(side):
+        self.swap_start.record(self.side)
+        with torch.cuda.stream(self.side):
             for l in range(self.L):
                 inc, out = self.plan_swap(l, n)
                 assert len(self.free[l]) >= len(inc)
@@ -198,9 +204,27 @@ class ResidentStack:
                 for e, s in zip(inc, slots):
                     self.pools[l][s].copy_(self.host_blobs[self.blob_of(l, e)], non_blocking=True)
                 plans.append((inc, out, slots))
-            self.swap_copies_done.record(side)
-            side.wait_event(self.replay_done)  # the running replay still reads the old maps
-            for l, (inc, out, slots) in enumerate(plans):
+            self.swap_copies_done.record(self.side)
+        self.swap_plans = plans
+        self.swap_in_flight = True
+        return dict(incoming=[p[0] for p in plans], outgoing=[p[1] for p in plans])
+
+    def swap_commit(self, block: bool = False) -> bool:
+        """If the copies of the round in flight have landed (or, with block,
+        once they have), switch to the new slot maps: the side stream waits for
+        the replay in flight, uploads the maps, and the next replay waits for
+        the upload.  Returns whether the round was committed."""
+        if not self.swap_in_flight:
+            return False
+        # Once this round's copies are done, so is everything earlier on the
+        # side stream, including the previous upload from the pinned maps.
+        if block:
+            self.swap_copies_done.synchronize()
+        elif not self.swap_copies_done.query():
+            return False
+        with torch.cuda.stream(self.side):
+            self.side.wait_event(self.replay_done)  # the running replay still reads the old maps
+            for l, (inc, out, slots) in enumerate(self.swap_plans):
                 soe = self.maps[l]
                 for e, s in zip(inc, slots):
                     soe[e] = s
@@ -210,9 +234,18 @@ class ResidentStack:
                 moe_validate_slot_map(soe, self.S)
                 self.pin_maps[l].copy_(torch.from_numpy(soe))
                 self.dev_maps[l].copy_(self.pin_maps[l], non_blocking=True)
-            self.maps_done.record(side)
+            self.maps_done.record(self.side)
         self.pending_maps = True
-        return dict(incoming=[p[0] for p in plans], outgoing=[p[1] for p in plans])
+        self.swap_in_flight = False
+        self.swap_plans = None
+        return True
+
+    def swap(self, n: int = 8) -> dict:
+        """One swap round on every layer: copies on the side stream overlap the
+        replay in flight; the new slot maps are uploaded after it finishes."""
+        plan = self.swap_begin(n)
+        self.swap_commit(block=True)
+        return plan
 
     def current_maps(self) -> list:
         return [m.copy() for m in self.maps]
