@@ -59,6 +59,9 @@ __device__ __forceinline__ float half_wave_sum(float v) {
     return v + __shfl_xor(v, 16, 64);
 }
 
+// s_waitcnt vmcnt(0), other counters unconstrained (gfx9 encoding).
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // silu(z) = z / (1 + e^-z) with the hardware exp2 and reciprocal (a few ulp).
 __device__ __forceinline__ float fast_silu(float z) {
     return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));

@@ -34,6 +34,10 @@ namespace qmoe {
 constexpr int kMaxTok = 2;     // tokens of one slot handled per pass over its weights
 constexpr int kMaxWaves = 8;   // waves per workgroup (split of the K dimension)
 constexpr uint32_t kMagic = 0x64006400u;  // fp16 1024.0 in both halves
+// Buffer resource word 3 for raw dword loads on gfx9-family parts (32-bit
+// data format, zero stride), and a unit offset beyond any tile range.
+constexpr int kBufferDword3 = 0x00020000;
+constexpr int kPastEnd = 0x40000000;
 
 // Records staged in LDS: X words [16 per record] and (C, S) pairs.
 typedef const uint32_t cu32;
@@ -91,13 +95,13 @@ template <int FMT> struct Unit {
     static constexpr int kRecords = FMT == 1 ? 8 : 4;  // 32-element blocks per unit
 };
 
+// Weight registers of one unit for this lane's row(s); the Q4_K header or
+// Q8_0 block scales are held apart (two slots, current and next unit).
 template <int FMT, int NMAT> struct UnitRegs;
 template <int NMAT> struct UnitRegs<1, NMAT> {
-    uint4 hdr[NMAT];
     uint4 q[8][NMAT];
 };
 template <int NMAT> struct UnitRegs<0, NMAT> {
-    uint2 sc[NMAT];
     uint4 q[4][NMAT][2];
 };
 
@@ -106,83 +110,80 @@ __device__ __forceinline__ constexpr int tile_bytes() {
     return FMT == 1 ? NMAT * 9216 : NMAT * 8704;
 }
 
-// This lane's bytes of one packed tile (layouts in qmoe_internal.h; the
-// down tile is the NMAT = 1 case of the same formulas).
-template <int NMAT>
-__device__ __forceinline__ void load_unit(const uint8_t* __restrict__ tile, int lane, UnitRegs<1, NMAT>& r) {
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m) r.hdr[m] = ld16(tile + m * 1024 + lane * 16);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m) r.q[j][m] = ld16(tile + NMAT * 1024 + j * NMAT * 1024 + m * 1024 + lane * 16);
-}
-template <int NMAT>
-__device__ __forceinline__ void load_unit(const uint8_t* __restrict__ tile, int lane, UnitRegs<0, NMAT>& r) {
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m) r.sc[m] = ld8(tile + m * 512 + lane * 8);
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-                r.q[jj][m][hf] = ld16(tile + NMAT * 512 + jj * NMAT * 2048 + m * 2048 + hf * 1024 + lane * 16);
-}
-
 // LDS region of one wave: words [kMaxTok][8][16] dwords, then (C, S) [kMaxTok][8][2].
 constexpr int kStageWords = kMaxTok * 8 * 16;
 constexpr int kStageFloats = kMaxTok * 8 * 2;
 
-// Copy the RB records starting at record r0 of each of the NT token rows
-// into the wave's LDS region (lane i < 4*RB moves 16 bytes of words; lanes
-// 32..32+RB-1 move one (C, S) pair).
-template <int RB, int NT>
-__device__ __forceinline__ void stage_unit(const uint32_t* const* rec_g, const float2* const* rcs_g, int r0, int lane,
-                                           uint32_t* lw, float* lc) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        if (lane < 4 * RB) {
-            const uint4 v = reinterpret_cast<const uint4*>(rec_g[t] + (size_t)r0 * 16)[lane];
-            reinterpret_cast<uint4*>(lw + t * RB * 16)[lane] = v;
-        } else if (lane >= 32 && lane < 32 + RB) {
-            const float2 v = rcs_g[t][r0 + lane - 32];
-            reinterpret_cast<float2*>(lc + t * RB * 2)[lane - 32] = v;
-        }
-    }
-    // LDS operations of one wave complete in order; the fence keeps the
-    // compiler from moving the broadcast reads above these writes.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+// Activation data of one unit, held in registers from its global load to
+// its packing into the wave's LDS region, so the load of unit u + 1 can be in
+// flight while unit u is computed.
+//   gate/up (NMAT = 2): 4 x values per lane and token (raw bits), packed
+//     into records by act_store (layout below);
+//   down (NMAT = 1): the h records as the gate/up epilogue wrote them: 8
+//     bytes of words per lane, one (C, S) pair per lane.
+// Every lane loads and stores something, lanes beyond the data repeating
+// another lane's (same value to the same LDS address), so that no branch on
+// the lane index splits the loop body: a divergent branch there makes the
+// compiler wait for all outstanding loads, the weight prefetch included.
+struct ActRegs {
+    uint4 xr[kMaxTok];
+    uint2 rw[kMaxTok];
+    float2 rc[kMaxTok];
+};
+
+// Four consecutive x values from element e of a row, kept as raw bits (fp32:
+// four words; bf16: two words) so that no conversion waits on the load;
+// x4_values converts them when the records are built.
+__device__ __forceinline__ uint4 x4_load(const void* xrow, int x_dtype, int e) {
+    if (x_dtype == 0) return *reinterpret_cast<const uint4*>(static_cast<const float*>(xrow) + e);
+    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(xrow) + e);
+    return make_uint4(u.x, u.y, 0u, 0u);
+}
+__device__ __forceinline__ void x4_values(uint4 r, int x_dtype, float* v) {
+    const bool f = x_dtype == 0;
+    v[0] = f ? __uint_as_float(r.x) : bf16_to_float(r.x & 0xFFFFu);
+    v[1] = f ? __uint_as_float(r.y) : bf16_to_float(r.x >> 16);
+    v[2] = f ? __uint_as_float(r.z) : bf16_to_float(r.y & 0xFFFFu);
+    v[3] = f ? __uint_as_float(r.w) : bf16_to_float(r.y >> 16);
 }
 
-// Build the RB records starting at block r0 of each of the NT token rows
-// straight from x (fp32 or bf16) into the wave's LDS region.  A record holds
-// 32 activation values of one block as 16 words of fp16 pairs, in the order
-// the nibble / byte extraction of the weights produces:
-//   Q4_K: word 4d+0 = (v[8d], v[8d+4]), 4d+1 = (v[8d+1], v[8d+5]) / 16,
-//         4d+2 = (v[8d+2], v[8d+6]),    4d+3 = (v[8d+3], v[8d+7]) / 16;
-//   Q8_0: word 2d = (v[4d], v[4d+2]), 2d+1 = (v[4d+1], v[4d+3]);
-// with (C, S) = ((1024 | 1152) * sum of the stored fp16 values, fp32 sum of
-// v).
-//   Q4_K (RB = 8): lane l packs values 4 (l % 8)..+4 of block l / 8.  The two
-//     lanes of a pair (values 8d..8d+3 and 8d+4..8d+7) swap two values by DPP
-//     so that the even lane forms words 4d, 4d+1 and the odd lane 4d+2,
-//     4d+3 (word 4d+p = (v[8d+p], v[8d+p+4]), odd p scaled by 1/16).
-//   Q8_0 (RB = 4): lane l packs values 4 (l % 8)..+4 of block (l / 8) % 4 of
-//     token l / 32 into words 2 (l % 8), +1 ((v0, v2), (v1, v3)).
-// Block sums (fp32 sum of x, and the sum of the stored fp16 values) are
-// 8-lane DPP reductions.
-template <int FMT>
-__device__ __forceinline__ void load4(const void* xrow, int x_dtype, int e, float* v) {
-    if (x_dtype == 0) {
-        const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(xrow) + e);
-        v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+template <int FMT, int NMAT, int RB, int NT>
+__device__ __forceinline__ void act_load(const void* const* xrow, int x_dtype, const uint32_t* const* rec_g,
+                                         const float2* const* rcs_g, int r0, int lane, ActRegs& a) {
+    if (NMAT == 2) {
+        const int sl = lane & 7;
+        if (FMT == 1) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) a.xr[t] = x4_load(xrow[t], x_dtype, (r0 + (lane >> 3)) * 32 + 4 * sl);
+        } else {
+            // lanes 32-63 take token 1; with one token they repeat token 0
+            // (a select of the two pointer values: indexing xrow by lane
+            // would put the array in memory)
+            const void* const x0 = xrow[0];
+            const void* const x1 = xrow[NT - 1];
+            a.xr[0] = x4_load(lane < 32 ? x0 : x1, x_dtype, (r0 + ((lane >> 3) & 3)) * 32 + 4 * sl);
+        }
     } else {
-        const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(xrow) + e);
-        v[0] = bf16_to_float(u.x & 0xFFFFu); v[1] = bf16_to_float(u.x >> 16);
-        v[2] = bf16_to_float(u.y & 0xFFFFu); v[3] = bf16_to_float(u.y >> 16);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            a.rw[t] = reinterpret_cast<const uint2*>(rec_g[t] + (size_t)r0 * 16)[lane & (8 * RB - 1)];
+            a.rc[t] = rcs_g[t][r0 + (lane & (RB - 1))];
+        }
+    }
+}
+
+// An empty asm that reads (and may rewrite) the activation registers in use:
+// the compiler must wait for their loads right here.  (An s_waitcnt alone
+// does not stop it from moving the loads below the wait.)
+template <int FMT, int NMAT, int NT>
+__device__ __forceinline__ void act_arrived(ActRegs& a) {
+    if (NMAT == 2) {
+#pragma unroll
+        for (int t = 0; t < (FMT == 1 ? NT : 1); ++t)
+            asm volatile("" : "+v"(a.xr[t].x), "+v"(a.xr[t].y), "+v"(a.xr[t].z), "+v"(a.xr[t].w));
+    } else {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) asm volatile("" : "+v"(a.rw[t].x), "+v"(a.rw[t].y), "+v"(a.rc[t].x), "+v"(a.rc[t].y));
     }
 }
 
@@ -192,59 +193,138 @@ __device__ __forceinline__ float sum8_lanes(float v) {
     return dpp_add<0x141>(v);  // row_half_mirror: the other quad of the 8
 }
 
-template <int FMT, int RB, int NT>
-__device__ __forceinline__ void stage_from_x(const void* const* xrow, int x_dtype, int r0, int lane, uint32_t* lw,
-                                             float* lc) {
-    const int sl = lane & 7;
-    if (FMT == 1) {
-        const int jb = lane >> 3;
-        const bool even = (sl & 1) == 0;
+// Put the RB records of the unit into the wave's LDS region.  A record holds
+// 32 activation values of one block as 16 words of fp16 pairs, in the order
+// the nibble / byte extraction of the weights produces:
+//   Q4_K: word 4d+0 = (v[8d], v[8d+4]), 4d+1 = (v[8d+1], v[8d+5]) / 16,
+//         4d+2 = (v[8d+2], v[8d+6]),    4d+3 = (v[8d+3], v[8d+7]) / 16;
+//   Q8_0: word 2d = (v[4d], v[4d+2]), 2d+1 = (v[4d+1], v[4d+3]);
+// with (C, S) = ((1024 | 1152) * sum of the stored fp16 values, fp32 sum of
+// v).  Built from x (gate/up):
+//   Q4_K (RB = 8): lane l packs values 4 (l % 8)..+4 of block l / 8.  The two
+//     lanes of a pair (values 8d..8d+3 and 8d+4..8d+7) swap two values by DPP
+//     so that the even lane forms words 4d, 4d+1 and the odd lane 4d+2,
+//     4d+3 (word 4d+p = (v[8d+p], v[8d+p+4]), odd p scaled by 1/16).
+//   Q8_0 (RB = 4): lane l packs values 4 (l % 8)..+4 of block (l / 8) % 4 of
+//     token l / 32 into words 2 (l % 8), +1 ((v0, v2), (v1, v3)).
+//   Block sums (fp32 sum of x, and the sum of the stored fp16 values) are
+//   8-lane DPP reductions.
+// Copied (down): the records of h as loaded.
+template <int FMT, int NMAT, int RB, int NT>
+__device__ __forceinline__ void act_store(const ActRegs& a, int x_dtype, int lane, uint32_t* lw, float* lc) {
+    if (NMAT == 2) {
+        const int sl = lane & 7;
+        if (FMT == 1) {
+            const int jb = lane >> 3;
+            const bool even = (sl & 1) == 0;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
+            for (int t = 0; t < NT; ++t) {
+                float v[4];
+                x4_values(a.xr[t], x_dtype, v);
+                const float send0 = even ? v[2] : v[0], send1 = even ? v[3] : v[1];
+                const float recv0 =
+                    __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send0), 0xB1, 0xF, 0xF, false));
+                const float recv1 =
+                    __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send1), 0xB1, 0xF, 0xF, false));
+                // even lane: words p = 0, 1; odd lane: p = 2, 3
+                const float lo0 = even ? v[0] : recv0, hi0 = even ? recv0 : v[2];
+                const float lo1 = (even ? v[1] : recv1) * 0.0625f, hi1 = (even ? recv1 : v[3]) * 0.0625f;
+                const uint32_t b0 = float_to_half_bits(lo0), b1 = float_to_half_bits(hi0);
+                const uint32_t b2 = float_to_half_bits(lo1), b3 = float_to_half_bits(hi1);
+                *reinterpret_cast<uint2*>(lw + (t * RB + jb) * 16 + 2 * sl) =
+                    make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+                const float s16 =
+                    sum8_lanes(half_to_float(b0) + half_to_float(b1) + half_to_float(b2) + half_to_float(b3));
+                const float sx = sum8_lanes(v[0] + v[1] + v[2] + v[3]);
+                // all 8 lanes of the block hold the sums
+                *reinterpret_cast<float2*>(lc + (t * RB + jb) * 2) = make_float2(1024.0f * s16, sx);
+            }
+        } else {
+            // token lane / 32 (< kMaxTok: with one token, lanes 32-63 fill
+            // the unused second region with token 0's records)
+            const int jb = (lane >> 3) & 3, t = lane >> 5;
             float v[4];
-            load4<FMT>(xrow[t], x_dtype, (r0 + jb) * 32 + 4 * sl, v);
-            const float send0 = even ? v[2] : v[0], send1 = even ? v[3] : v[1];
-            const float recv0 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send0), 0xB1, 0xF, 0xF, false));
-            const float recv1 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send1), 0xB1, 0xF, 0xF, false));
-            // even lane: words p = 0, 1; odd lane: p = 2, 3
-            const float lo0 = even ? v[0] : recv0, hi0 = even ? recv0 : v[2];
-            const float lo1 = (even ? v[1] : recv1) * 0.0625f, hi1 = (even ? recv1 : v[3]) * 0.0625f;
-            const uint32_t b0 = float_to_half_bits(lo0), b1 = float_to_half_bits(hi0);
-            const uint32_t b2 = float_to_half_bits(lo1), b3 = float_to_half_bits(hi1);
-            *reinterpret_cast<uint2*>(lw + (t * RB + jb) * 16 + 2 * sl) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-            const float s16 = sum8_lanes(half_to_float(b0) + half_to_float(b1) + half_to_float(b2) + half_to_float(b3));
-            const float sx = sum8_lanes(v[0] + v[1] + v[2] + v[3]);
-            if (sl == 0) *reinterpret_cast<float2*>(lc + (t * RB + jb) * 2) = make_float2(1024.0f * s16, sx);
-        }
-    } else {
-        const int jb = (lane >> 3) & 3, t = lane >> 5;
-        if (t < NT) {
-            float v[4];
-            load4<FMT>(xrow[t], x_dtype, (r0 + jb) * 32 + 4 * sl, v);
+            x4_values(a.xr[0], x_dtype, v);
             const uint32_t b0 = float_to_half_bits(v[0]), b1 = float_to_half_bits(v[2]);
             const uint32_t b2 = float_to_half_bits(v[1]), b3 = float_to_half_bits(v[3]);
             *reinterpret_cast<uint2*>(lw + (t * RB + jb) * 16 + 2 * sl) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
             const float s16 = half_to_float(b0) + half_to_float(b1) + half_to_float(b2) + half_to_float(b3);
             const float sx = v[0] + v[1] + v[2] + v[3];
-            // lanes of token 1 sit in rows 2-3: the 8-lane sums stay within a token
+            // the 8 lanes of a block share a row of 16 lanes: the sums stay within a block
             const float c16 = sum8_lanes(s16), csx = sum8_lanes(sx);
-            if (sl == 0) *reinterpret_cast<float2*>(lc + (t * RB + jb) * 2) = make_float2(1152.0f * c16, csx);
+            *reinterpret_cast<float2*>(lc + (t * RB + jb) * 2) = make_float2(1152.0f * c16, csx);
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            reinterpret_cast<uint2*>(lw + t * RB * 16)[lane & (8 * RB - 1)] = a.rw[t];
+            reinterpret_cast<float2*>(lc + t * RB * 2)[lane & (RB - 1)] = a.rc[t];
         }
     }
+    // LDS operations of one wave complete in order; the fence keeps the
+    // compiler from moving the broadcast reads above these writes.
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// acc[t][m] += dot of the unit's weights (matrix m) with token t's records.
+// The weight tiles of one (slot, row tile) are read through a buffer
+// resource spanning exactly their bytes: a load whose unit offset is set past
+// the end returns zeros without a memory access.  The pipeline below uses
+// that to skip the refill after a wave's last unit without a branch (a
+// branch around the refill makes the compiler keep both register sets).
+__device__ __forceinline__ uint4 ldb16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint2 ldb8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    return make_uint2(v[0], v[1]);
+}
+
+// Weights of half a unit (Q4_K: sub-blocks 4h..4h+3; Q8_0: blocks 2h, 2h+1)
+// of the unit at byte offset `uoff` into their slots of `r` (the lane's
+// offset in a VGPR, the rest in the scalar offset); with h = 0 also
+// the unit's header / scales, into `hdr` (the caller keeps the current
+// unit's while the next one loads).
+template <int NMAT>
+__device__ __forceinline__ void load_half(__amdgpu_buffer_rsrc_t src, int uoff, int lane, int h,
+                                          UnitRegs<1, NMAT>& r, uint4* hdr) {
+    if (h == 0) {
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) hdr[m] = ldb16(src, lane * 16, uoff + m * 1024);
+    }
+#pragma unroll
+    for (int j = 4 * h; j < 4 * h + 4; ++j)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) r.q[j][m] = ldb16(src, lane * 16, uoff + NMAT * 1024 + j * NMAT * 1024 + m * 1024);
+}
+template <int NMAT>
+__device__ __forceinline__ void load_half(__amdgpu_buffer_rsrc_t src, int uoff, int lane, int h,
+                                          UnitRegs<0, NMAT>& r, uint2* sc) {
+    if (h == 0) {
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) sc[m] = ldb8(src, lane * 8, uoff + m * 512);
+    }
+#pragma unroll
+    for (int jj = 2 * h; jj < 2 * h + 2; ++jj)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+                r.q[jj][m][hf] = ldb16(src, lane * 16, uoff + NMAT * 512 + jj * NMAT * 2048 + m * 2048 + hf * 1024);
+}
+
+// acc[t][m] += dot of half h of the unit's weights (matrix m) with token t's
+// records; `hdr` is the unit's header (Q4_K) or block scales (Q8_0).
 template <int NT, int NMAT>
-__device__ __forceinline__ void unit_dots(const UnitRegs<1, NMAT>& r, const uint32_t* lw, const float* lc,
-                                          float (*acc)[NMAT]) {
+__device__ __forceinline__ void half_dots(const UnitRegs<1, NMAT>& r, const uint4* hdr, int h, const uint32_t* lw,
+                                          const float* lc, float (*acc)[NMAT]) {
     float ds[NMAT][8], dm[NMAT][8];
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) q4k_header(r.hdr[m], ds[m], dm[m]);
+    for (int m = 0; m < NMAT; ++m) q4k_header(hdr[m], ds[m], dm[m]);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 4 * h; j < 4 * h + 4; ++j) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const uint32_t* X = lw + (t * 8 + j) * 16;
@@ -253,47 +333,92 @@ __device__ __forceinline__ void unit_dots(const UnitRegs<1, NMAT>& r, const uint
             for (int m = 0; m < NMAT; ++m) acc[t][m] += ds[m][j] * (q4k_dot(r.q[j][m], X) - c) - dm[m][j] * sx;
         }
         // keep the scheduler from hoisting every sub-block's nibble
-        // extraction at once (that alone would need 256 VGPRs)
+        // extraction at once
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 template <int NT, int NMAT>
-__device__ __forceinline__ void unit_dots(const UnitRegs<0, NMAT>& r, const uint32_t* lw, const float* lc,
-                                          float (*acc)[NMAT]) {
-    float d[NMAT][4];
+__device__ __forceinline__ void half_dots(const UnitRegs<0, NMAT>& r, const uint2* sc, int h, const uint32_t* lw,
+                                          const float* lc, float (*acc)[NMAT]) {
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) {
-        d[m][0] = half_to_float(r.sc[m].x);
-        d[m][1] = half_to_float(r.sc[m].x >> 16);
-        d[m][2] = half_to_float(r.sc[m].y);
-        d[m][3] = half_to_float(r.sc[m].y >> 16);
-    }
+    for (int jj = 2 * h; jj < 2 * h + 2; ++jj) {
+        float d[NMAT];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
+        for (int m = 0; m < NMAT; ++m) d[m] = half_to_float((jj < 2 ? sc[m].x : sc[m].y) >> (16 * (jj & 1)));
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const uint32_t* X = lw + (t * 4 + jj) * 16;
             const float c = lc[(t * 4 + jj) * 2];
 #pragma unroll
-            for (int m = 0; m < NMAT; ++m) acc[t][m] += d[m][jj] * (q8_dot(r.q[jj][m][0], r.q[jj][m][1], X) - c);
+            for (int m = 0; m < NMAT; ++m) acc[t][m] += d[m] * (q8_dot(r.q[jj][m][0], r.q[jj][m][1], X) - c);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-// K units [u0, u0 + nu) of this lane's row(s) for NT tokens.  `w` holds the
-// weights of unit u0 on entry when `have_first` is set.
-template <int FMT, int NMAT, int NT>
-__device__ __forceinline__ void gemv_units(const uint8_t* __restrict__ tiles, int u0, int nu, int lane,
-                                           UnitRegs<FMT, NMAT>& w, bool have_first, const uint32_t* const* rec_g,
+template <int FMT> struct HdrType { typedef uint4 T; };
+template <> struct HdrType<0> { typedef uint2 T; };
+
+// K units [u0, u0 + nu) of this lane's row(s) for NT tokens.  On entry `w`
+// and `hdr0` hold (or are loading) unit u0.  Per unit u: its records go to
+// LDS from registers (their global load was issued during unit u - 1), the
+// activations of unit u + 1 are requested, half 0 is computed and its weight
+// registers are refilled with half 0 of unit u + 1, then the same for half 1.
+// A wave thus always has about half a unit of weights in flight, in the
+// registers one unit occupies.  The two header slots alternate by unit.  With
+// `again` (the slot has another chunk of tokens) the last unit refills with
+// unit u0.  The activation index past the range is clamped to the last unit
+// (a repeated small load that nothing uses).  PIPE = false is the launch
+// with one unit per wave: nothing to prefetch, so no refill is issued except
+// the reload of the unit for another chunk.
+template <int FMT, int NMAT, int NT, bool PIPE>
+__device__ __forceinline__ void gemv_units(__amdgpu_buffer_rsrc_t src, int u0, int nu, int lane, bool again,
+                                           UnitRegs<FMT, NMAT>& w, typename HdrType<FMT>::T* hdr0,
+                                           typename HdrType<FMT>::T* hdr1, const uint32_t* const* rec_g,
                                            const float2* const* rcs_g, const void* const* xrow, int x_dtype,
                                            uint32_t* lw, float* lc, float (*acc)[NMAT]) {
     constexpr int RB = Unit<FMT>::kRecords;
-    for (int ul = 0; ul < nu; ++ul) {
-        if (ul > 0 || !have_first) load_unit(tiles + (size_t)(u0 + ul) * tile_bytes<FMT, NMAT>(), lane, w);
-        if (NMAT == 2) stage_from_x<FMT, RB, NT>(xrow, x_dtype, (u0 + ul) * RB, lane, lw, lc);
-        else stage_unit<RB, NT>(rec_g, rcs_g, (u0 + ul) * RB, lane, lw, lc);
-        unit_dots<NT, NMAT>(w, lw, lc, acc);
+    constexpr int TB = tile_bytes<FMT, NMAT>();
+    typedef typename HdrType<FMT>::T HT;
+    ActRegs a;
+    if (!PIPE) {
+        if (nu != 1) return;
+        act_load<FMT, NMAT, RB, NT>(xrow, x_dtype, rec_g, rcs_g, u0 * RB, lane, a);
+        act_store<FMT, NMAT, RB, NT>(a, x_dtype, lane, lw, lc);
+        half_dots<NT, NMAT>(w, hdr0, 0, lw, lc, acc);
+        half_dots<NT, NMAT>(w, hdr0, 1, lw, lc, acc);
+        if (again) {
+            load_half(src, u0 * TB, lane, 0, w, hdr0);
+            load_half(src, u0 * TB, lane, 1, w, hdr0);
+        }
+        return;
+    }
+    const int ulast = u0 + nu - 1;
+    act_load<FMT, NMAT, RB, NT>(xrow, x_dtype, rec_g, rcs_g, u0 * RB, lane, a);
+    // The first unit needs these activations, the newest loads; waiting for
+    // them here (rather than at the loop head, where the compiler would place
+    // the same full wait on every iteration) keeps the loop's waits partial:
+    // at its head the outstanding loads are always, oldest first, activations
+    // of unit u, then its two halves of weights.
+    act_arrived<FMT, NMAT, NT>(a);
+    auto unit = [&](int ul, HT* hc, HT* hn) {
+        // byte offset of the unit to refill with; past the end when none
+        const int unext = ul + 1 < nu ? (u0 + ul + 1) * TB : again ? u0 * TB : kPastEnd;
+        // the barriers pin the issue order of the three load groups
+        __builtin_amdgcn_sched_barrier(0);
+        act_store<FMT, NMAT, RB, NT>(a, x_dtype, lane, lw, lc);
+        act_load<FMT, NMAT, RB, NT>(xrow, x_dtype, rec_g, rcs_g, min(u0 + ul + 1, ulast) * RB, lane, a);
+        __builtin_amdgcn_sched_barrier(0);
+        half_dots<NT, NMAT>(w, hc, 0, lw, lc, acc);
+        load_half(src, unext, lane, 0, w, hn);
+        __builtin_amdgcn_sched_barrier(0);
+        half_dots<NT, NMAT>(w, hc, 1, lw, lc, acc);
+        load_half(src, unext, lane, 1, w, hn);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int ul = 0; ul < nu; ul += 2) {
+        unit(ul, hdr0, hdr1);
+        if (ul + 1 < nu) unit(ul + 1, hdr1, hdr0);
     }
 }
 
@@ -327,7 +452,7 @@ __device__ __forceinline__ void store_h_record(float h, int rg, int lane, uint32
 // the token rows of x, indexed by perm_pair / k), writing h records at each
 // pair's position q.  NMAT = 1: down GEMV (records of h at position q) writing
 // y_pairs at pair perm_pair[q].
-template <int FMT, int NMAT>
+template <int FMT, int NMAT, bool PIPE>
 __global__ __launch_bounds__(512) void gemv_kernel(const uint8_t* __restrict__ pool, size_t stride, int S, int K,
                                                    int rows, size_t section, const void* __restrict__ xin,
                                                    int x_dtype, const uint32_t* __restrict__ rw,
@@ -355,9 +480,15 @@ __global__ __launch_bounds__(512) void gemv_kernel(const uint8_t* __restrict__ p
     const int units = FMT == 1 ? K / 256 : K / 128;
     const int u0 = min(units, wave * units_per_wave), nu = min(units, u0 + units_per_wave) - u0;
     const uint8_t* tiles = pool + (size_t)slot * stride + section + (size_t)rg * units * tile_bytes<FMT, NMAT>();
+    const __amdgpu_buffer_rsrc_t src =
+        __builtin_amdgcn_make_buffer_rsrc((void*)tiles, 0, units * tile_bytes<FMT, NMAT>(), kBufferDword3);
 
     UnitRegs<FMT, NMAT> w;
-    if (nu > 0) load_unit(tiles + (size_t)u0 * tile_bytes<FMT, NMAT>(), lane, w);
+    typename HdrType<FMT>::T hdr0[NMAT], hdr1[NMAT];
+    if (nu > 0) {
+        load_half(src, u0 * tile_bytes<FMT, NMAT>(), lane, 0, w, hdr0);
+        load_half(src, u0 * tile_bytes<FMT, NMAT>(), lane, 1, w, hdr0);
+    }
 
     const int P = T * k;
     const int q0 = offsets[slot], q1 = offsets[slot + 1];
@@ -389,15 +520,27 @@ __global__ __launch_bounds__(512) void gemv_kernel(const uint8_t* __restrict__ p
                 xrow[i] = nullptr;
             }
         }
-        const bool first = c == q0;
+        const bool again = c + kMaxTok < q1;
         float acc[kMaxTok][NMAT];
 #pragma unroll
         for (int i = 0; i < kMaxTok; ++i)
 #pragma unroll
             for (int m = 0; m < NMAT; ++m) acc[i][m] = 0.f;
         switch (nt) {
-            case 1: gemv_units<FMT, NMAT, 1>(tiles, u0, nu, lane, w, first, rec_g, rcs_g, xrow, x_dtype, lw, lc, acc); break;
-            default: gemv_units<FMT, NMAT, 2>(tiles, u0, nu, lane, w, first, rec_g, rcs_g, xrow, x_dtype, lw, lc, acc); break;
+            case 1:
+                gemv_units<FMT, NMAT, 1, PIPE>(src, u0, nu, lane, again, w, hdr0, hdr1, rec_g, rcs_g, xrow, x_dtype, lw,
+                                         lc, acc);
+                break;
+            default:
+                gemv_units<FMT, NMAT, 2, PIPE>(src, u0, nu, lane, again, w, hdr0, hdr1, rec_g, rcs_g, xrow, x_dtype, lw,
+                                         lc, acc);
+                break;
+        }
+        // the last unit re-requested unit u0 for the next chunk; with an odd
+        // unit count its header went to the second slot
+        if (PIPE && again && (nu & 1)) {
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) hdr0[m] = hdr1[m];
         }
 #pragma unroll
         for (int i = 0; i < kMaxTok; ++i)
@@ -449,6 +592,37 @@ static void split_k(int units, long tiles_total, int* nw, int* upw) {
     *nw = (units + per - 1) / per;
 }
 
+// Kernel arguments of one GEMV launch (gate/up or down).
+struct GemvLaunch {
+    const uint8_t* pool;
+    size_t stride;
+    int S, K, rows;
+    size_t section;
+    const void* x;
+    int x_dtype;
+    const uint32_t* rw;
+    const float2* rcs;
+    int T, k;
+    const int32_t *offsets, *active, *num_active, *perm;
+    uint32_t* hw;
+    float2* hcs;
+    float* y_pairs;
+    int units_per_wave;
+};
+
+// The pipelined kernel when a wave has more than one K unit.
+template <int FMT, int NMAT>
+static void launch_gemv(const GemvLaunch& g, dim3 grid, dim3 block, hipStream_t s) {
+    if (g.units_per_wave > 1)
+        hipLaunchKernelGGL((gemv_kernel<FMT, NMAT, true>), grid, block, 0, s, g.pool, g.stride, g.S, g.K, g.rows,
+                           g.section, g.x, g.x_dtype, g.rw, g.rcs, g.T, g.k, g.offsets, g.active, g.num_active, g.perm,
+                           g.hw, g.hcs, g.y_pairs, g.units_per_wave);
+    else
+        hipLaunchKernelGGL((gemv_kernel<FMT, NMAT, false>), grid, block, 0, s, g.pool, g.stride, g.S, g.K, g.rows,
+                           g.section, g.x, g.x_dtype, g.rw, g.rcs, g.T, g.k, g.offsets, g.active, g.num_active, g.perm,
+                           g.hw, g.hcs, g.y_pairs, g.units_per_wave);
+}
+
 hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s) {
     const size_t P = (size_t)a.T * a.k;
     uint8_t* ws = static_cast<uint8_t*>(a.ws);
@@ -463,16 +637,14 @@ hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s) {
         const int units = a.format == 1 ? a.H / 256 : a.H / 128;
         int nw, upw;
         split_k(units, (long)(a.I / 64) * max_active, &nw, &upw);
-        dim3 grid(a.I / 64, max_active);
+        const dim3 grid(a.I / 64, max_active), block(64 * nw);
         timer_before(kStageGateUp, s);
+        const GemvLaunch g{a.pool, a.stride, a.S, a.H, a.I, 0, a.x, a.x_dtype, nullptr, nullptr, a.T, a.k,
+                           a.slot_offsets, a.active_slots, a.num_active, a.perm_pair, hw, hcs, nullptr, upw};
         if (a.format == 1)
-            hipLaunchKernelGGL((gemv_kernel<1, 2>), grid, dim3(64 * nw), 0, s, a.pool, a.stride, a.S, a.H, a.I,
-                               (size_t)0, a.x, a.x_dtype, (const uint32_t*)nullptr, (const float2*)nullptr, a.T, a.k, a.slot_offsets, a.active_slots, a.num_active, a.perm_pair,
-                               hw, hcs, (float*)nullptr, upw);
+            launch_gemv<1, 2>(g, grid, block, s);
         else
-            hipLaunchKernelGGL((gemv_kernel<0, 2>), grid, dim3(64 * nw), 0, s, a.pool, a.stride, a.S, a.H, a.I,
-                               (size_t)0, a.x, a.x_dtype, (const uint32_t*)nullptr, (const float2*)nullptr, a.T, a.k, a.slot_offsets, a.active_slots, a.num_active, a.perm_pair,
-                               hw, hcs, (float*)nullptr, upw);
+            launch_gemv<0, 2>(g, grid, block, s);
         timer_after(kStageGateUp, s);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -482,22 +654,16 @@ hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s) {
         const int units = a.format == 1 ? a.I / 256 : a.I / 128;
         int nw, upw;
         split_k(units, (long)(a.H / 64) * max_active, &nw, &upw);
-        dim3 grid(a.H / 64, max_active);
-        float* yp = static_cast<float*>(a.y_pairs);
+        const dim3 grid(a.H / 64, max_active), block(64 * nw);
         const size_t section = a.format == 1 ? q4k_gateup_bytes(a.H, a.I) : q8_gateup_bytes(a.H, a.I);
         timer_before(kStageDown, s);
+        const GemvLaunch g{a.pool, a.stride, a.S, a.I, a.H, section, nullptr, 0, hw, hcs, a.T, a.k,
+                           a.slot_offsets, a.active_slots, a.num_active, a.perm_pair, nullptr, nullptr,
+                           static_cast<float*>(a.y_pairs), upw};
         if (a.format == 1)
-            hipLaunchKernelGGL((gemv_kernel<1, 1>), grid, dim3(64 * nw), 0, s, a.pool, a.stride, a.S, a.I, a.H,
-                               section, (const void*)nullptr, 0, (const uint32_t*)hw, (const float2*)hcs, a.T, a.k,
-                               a.slot_offsets,
-                               a.active_slots, a.num_active, a.perm_pair, (uint32_t*)nullptr, (float2*)nullptr, yp,
-                               upw);
+            launch_gemv<1, 1>(g, grid, block, s);
         else
-            hipLaunchKernelGGL((gemv_kernel<0, 1>), grid, dim3(64 * nw), 0, s, a.pool, a.stride, a.S, a.I, a.H,
-                               section, (const void*)nullptr, 0, (const uint32_t*)hw, (const float2*)hcs, a.T, a.k,
-                               a.slot_offsets,
-                               a.active_slots, a.num_active, a.perm_pair, (uint32_t*)nullptr, (float2*)nullptr, yp,
-                               upw);
+            launch_gemv<0, 1>(g, grid, block, s);
         timer_after(kStageDown, s);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

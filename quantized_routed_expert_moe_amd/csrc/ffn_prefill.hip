@@ -247,9 +247,6 @@ __device__ __forceinline__ void dq_bc(DqPart& d, int half, float ds512, float nd
     }
 }
 
-// s_waitcnt vmcnt(0), other counters unconstrained (gfx9 encoding).
-__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
 // ------------------------------------------------------------- GEMM body
 
 struct TileCtx {

@@ -231,9 +231,21 @@ def test_dsv3_partial_residency(dsv3_blobs):
     assert got["host_count"] > 0 and got["num_active"] > 0
 
 
+def test_dsv3_experts_many_tokens_per_slot(dsv3_blobs):
+    """DeepSeek-V3-sized experts (H 7168, I 2048) with 24 tokens over 16
+    experts on the decode path: the K split gives each wave several units
+    (the prefetching loop, with odd and even unit counts) and slots hold
+    several chunks of tokens (the loop's refill with the first unit)."""
+    wl = W.Workload("DeepSeek-V3-sized Q4_K experts, 16 resident, 24 tokens", F.Q4K, 7168, 2048, 16, 2, 24)
+    say(wl.name)
+    got, want, soe, S = _layer_case(wl, blobs=dsv3_blobs[:16], path=Q.MOE_PATH_DECODE)
+    _check_layer(wl, got, want, soe, S)
+    assert int(np.diff(got["slot_offsets"]).max()) > 2
+
+
 def test_decode_many_tokens_per_slot():
     """48 tokens over 8 experts on the decode path: slots hold up to dozens of
-    tokens (chunks of four plus a remainder)."""
+    tokens (chunks of two plus a remainder)."""
     wl = W.Workload("small Q4_K layer, 48 tokens", F.Q4K, 512, 256, 8, 3, 48)
     say(wl.name)
     got, want, soe, S = _layer_case(wl, path=Q.MOE_PATH_DECODE)
