@@ -111,9 +111,16 @@ moe_status moe_route_topk(const float* logits, int T, int E, int k, int score, i
  *                    inside a slot by ascending p (stable).  The first
  *                    slot_offsets[S] entries are written.
  * host_token, host_expert, host_weight
- *                    device, [T*k]: the non-resident pairs in ascending p as
- *                    (t, expert, weight): the host leg's work list.
- * host_count         device, int32 [1].
+ *                    device-addressable, [T*k]: the non-resident pairs in
+ *                    ascending p as (t, expert, weight): the host leg's work
+ *                    list.
+ * host_count         device-addressable, int32 [1].
+ *                    These four may be device memory or the device address
+ *                    of pinned host memory (hipHostMalloc, address from
+ *                    hipHostGetDevicePointer): the kernels only store to them
+ *                    (plain stores, no atomics), so the list then reaches the
+ *                    host with no copy; it is complete once the stream has
+ *                    passed this call.
  * ws, ws_bytes       device workspace of at least moe_batches_workspace_size().
  * Every output is a pure function of the inputs (no atomics-order effects).
  */

@@ -112,6 +112,31 @@ def _dev(t, dtypes=None, name="tensor") -> int:
     return t.data_ptr()
 
 
+_MAPPED = {}  # pinned host allocation base -> its device address
+
+
+def _dev_or_mapped(t, dtypes=None, name="tensor") -> int:
+    """Device address of a device tensor, or of a pinned host tensor (the
+    device-side address of its pinned allocation from hipHostGetDevicePointer;
+    an allocation the device cannot address raises here, before any launch)."""
+    import torch
+    if isinstance(t, torch.Tensor) and not t.is_cuda and t.is_pinned():
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if dtypes is not None and t.dtype not in dtypes:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+        base = t.untyped_storage().data_ptr()
+        if base not in _MAPPED:
+            hip = ctypes.CDLL("libamdhip64.so")
+            dptr = ctypes.c_void_p()
+            rc = hip.hipHostGetDevicePointer(ctypes.byref(dptr), ctypes.c_void_p(base), 0)
+            if rc != 0 or not dptr.value:
+                raise QmoeError(f"{name}: pinned host memory has no device address (hip error {rc})")
+            _MAPPED[base] = dptr.value
+        return _MAPPED[base] + (t.data_ptr() - base)
+    return _dev(t, dtypes, name)
+
+
 def _stream(stream) -> int:
     import torch
     if stream is None:
@@ -155,9 +180,9 @@ def moe_build_expert_batches(topk_ids, topk_w, E: int, slot_of_expert, S: int, s
         _dev(topk_ids, _i32(), "topk_ids"), _dev(topk_w, _f32(), "topk_w"), T, k, E,
         _dev(slot_of_expert, _i32(), "slot_of_expert"), S, _dev(slot_offsets, _i32(), "slot_offsets"),
         _dev(active_slots, _i32(), "active_slots"), _dev(num_active, _i32(), "num_active"),
-        _dev(perm_pair, _i32(), "perm_pair"), _dev(host_token, _i32(), "host_token"),
-        _dev(host_expert, _i32(), "host_expert"), _dev(host_weight, _f32(), "host_weight"),
-        _dev(host_count, _i32(), "host_count"), _dev(ws, None, "ws"), ws_bytes, _stream(stream)))
+        _dev(perm_pair, _i32(), "perm_pair"), _dev_or_mapped(host_token, _i32(), "host_token"),
+        _dev_or_mapped(host_expert, _i32(), "host_expert"), _dev_or_mapped(host_weight, _f32(), "host_weight"),
+        _dev_or_mapped(host_count, _i32(), "host_count"), _dev(ws, None, "ws"), ws_bytes, _stream(stream)))
 
 
 def moe_expert_blob_bytes(fmt: int, H: int, I: int) -> int:

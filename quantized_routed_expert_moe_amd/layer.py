@@ -46,7 +46,8 @@ class LayerSpec:
 class MoELayer:
     def __init__(self, spec: LayerSpec, T_max: int, S: int, slot_pool: torch.Tensor, stride: int,
                  slot_of_expert: torch.Tensor, shared_pool: torch.Tensor | None = None,
-                 path: int = MOE_PATH_AUTO, y_dtype=torch.float32, pair_dtype=torch.float32, device="cuda"):
+                 path: int = MOE_PATH_AUTO, y_dtype=torch.float32, pair_dtype=torch.float32, device="cuda",
+                 host_list_pinned: bool = False):
         self.spec, self.T_max, self.S, self.path = spec, T_max, S, path
         self.slot_pool, self.stride, self.slot_of_expert = slot_pool, stride, slot_of_expert
         self.shared_pool = shared_pool
@@ -59,10 +60,20 @@ class MoELayer:
         self.active_slots = torch.zeros(max(1, min(S, P)), **i32)
         self.num_active = torch.zeros(1, **i32)
         self.perm_pair = torch.zeros(max(1, P), **i32)
-        self.host_token = torch.zeros(max(1, P), **i32)
-        self.host_expert = torch.zeros(max(1, P), **i32)
-        self.host_weight = torch.zeros(max(1, P), dtype=torch.float32, device=device)
-        self.host_count = torch.zeros(1, **i32)
+        # The host list (token, expert, weight per non-resident pair, then the
+        # count) lives in one int32 buffer; the four arrays are views into it.
+        # With host_list_pinned the buffer is pinned host memory that the
+        # batching kernel writes directly (no copy): read it only once the
+        # stream has passed forward().
+        Pl = max(1, P)
+        if host_list_pinned:
+            self.host_list = torch.zeros(3 * Pl + 1, dtype=torch.int32, pin_memory=True)
+        else:
+            self.host_list = torch.zeros(3 * Pl + 1, **i32)
+        self.host_token = self.host_list[0:Pl]
+        self.host_expert = self.host_list[Pl:2 * Pl]
+        self.host_weight = self.host_list[2 * Pl:3 * Pl].view(torch.float32)
+        self.host_count = self.host_list[3 * Pl:]
         bws = moe_batches_workspace_size(T_max, k, E, S)
         self.batch_ws = torch.zeros(max(1, bws), dtype=torch.uint8, device=device) if bws else None
         self.ws = torch.zeros(max(1, moe_ffn_workspace_size(spec.fmt, T_max, k, H, spec.I, path)), dtype=torch.uint8,

@@ -10,8 +10,9 @@ experts are swapped between the card and the host between steps).
 Orchestration only; every computation is a libqmoe call:
   * per layer: an HBM slot pool of S = resident + staging slots, a slot map
     (expert -> slot, -1 = host), a shared expert, the layer's buffers;
-  * capture(): all layers back to back on one stream into one graph, each
-    layer followed by the D2H copy of its host list into pinned memory;
+  * capture(): all layers back to back on one stream into one graph; each
+    layer's batching kernel writes its host list straight into pinned host
+    memory, so the graph holds no copies;
   * swap_begin() / swap_commit(): for every layer, copy the packed blobs of
     `n` incoming experts from pinned host memory into free slots with
     hipMemcpyAsync on a side stream, overlapping any number of replays (free
@@ -58,7 +59,6 @@ class ResidentStack:
         self.cursor = []          # swap cursor into ranked[l]
         self.pools, self.dev_maps, self.layers = [], [], []
         self.x, self.logits = [], []
-        self.pin_host = []        # per layer pinned (token, expert, weight, count)
         src = dev_blobs if dev_blobs is not None else host_blobs
         for l in range(n_layers):
             soe = np.full(E, -1, dtype=np.int32)
@@ -85,15 +85,9 @@ class ResidentStack:
         torch.cuda.synchronize()
         for l in range(n_layers):
             self.layers.append(MoELayer(spec, T, self.S, self.pools[l], self.stride, self.dev_maps[l],
-                                        self.shared_pools[l], MOE_PATH_DECODE))
+                                        self.shared_pools[l], MOE_PATH_DECODE, host_list_pinned=True))
             self.x.append(torch.zeros((T, spec.H), dtype=torch.float32, device=dev))
             self.logits.append(torch.zeros((T, E), dtype=torch.float32, device=dev))
-            P = T * spec.k
-            self.pin_host.append(dict(
-                token=torch.zeros(P, dtype=torch.int32).pin_memory(),
-                expert=torch.zeros(P, dtype=torch.int32).pin_memory(),
-                weight=torch.zeros(P, dtype=torch.float32).pin_memory(),
-                count=torch.zeros(1, dtype=torch.int32).pin_memory()))
         self.pin_maps = [torch.zeros(E, dtype=torch.int32).pin_memory() for _ in range(n_layers)]
         self.graph = None
         self.side = torch.cuda.Stream()
@@ -114,13 +108,7 @@ class ResidentStack:
 
     def _step_body(self) -> None:
         for l in range(self.L):
-            lay = self.layers[l]
-            lay.forward(self.x[l], self.logits[l])
-            h = self.pin_host[l]
-            h["token"].copy_(lay.host_token, non_blocking=True)
-            h["expert"].copy_(lay.host_expert, non_blocking=True)
-            h["weight"].copy_(lay.host_weight, non_blocking=True)
-            h["count"].copy_(lay.host_count, non_blocking=True)
+            self.layers[l].forward(self.x[l], self.logits[l])
 
     def run_eager(self) -> None:
         self._wait_maps()
@@ -161,10 +149,12 @@ class ResidentStack:
         return [lay.y for lay in self.layers]
 
     def host_lists(self, l: int) -> dict:
-        h = self.pin_host[l]
-        c = int(h["count"][0])
-        return dict(token=h["token"][:c].numpy().copy(), expert=h["expert"][:c].numpy().copy(),
-                    weight=h["weight"][:c].numpy().copy())
+        """Layer l's host list from the last completed replay (the caller
+        synchronises first)."""
+        h = self.layers[l].host_list.numpy()
+        P = (h.size - 1) // 3
+        c = int(h[3 * P])
+        return dict(token=h[:c].copy(), expert=h[P:P + c].copy(), weight=h[2 * P:2 * P + c].view(np.float32).copy())
 
     # ------------------------------------------------------------ swaps
     def plan_swap(self, l: int, n: int) -> tuple[list, list]:

@@ -47,7 +47,7 @@ def spec_of(w: W.Workload) -> LayerSpec:
 
 def device_layer(w: W.Workload, blobs: np.ndarray, soe: np.ndarray, S: int, shared: np.ndarray | None,
                  T: int, path: int = Q.MOE_PATH_AUTO, pair_dtype=torch.float32, y_dtype=torch.float32,
-                 pool=None) -> MoELayer:
+                 pool=None, host_list_pinned: bool = False) -> MoELayer:
     """blobs: canonical blobs indexed by expert id (all E)."""
     if pool is None:
         slots = [None] * S
@@ -61,7 +61,7 @@ def device_layer(w: W.Workload, blobs: np.ndarray, soe: np.ndarray, S: int, shar
     if shared is not None:
         shared_pool, _ = pack_pool(F.Q8_0, shared[None, :], w.H, w.I_shared, [0], 1)
     return MoELayer(spec_of(w), T, S, pool, stride, torch.from_numpy(soe).cuda(), shared_pool, path,
-                    y_dtype=y_dtype, pair_dtype=pair_dtype)
+                    y_dtype=y_dtype, pair_dtype=pair_dtype, host_list_pinned=host_list_pinned)
 
 
 def to_dev_x(x: np.ndarray) -> torch.Tensor:

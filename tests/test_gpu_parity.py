@@ -167,7 +167,8 @@ def test_batches_empty():
 
 # ------------------------------------------------------------ decode layer
 
-def _layer_case(wl, blobs=None, soe=None, S=None, T=None, path=Q.MOE_PATH_AUTO, x=None, logits=None):
+def _layer_case(wl, blobs=None, soe=None, S=None, T=None, path=Q.MOE_PATH_AUTO, x=None, logits=None,
+                host_list_pinned=False):
     soe_, S_ = W.slot_map(wl)
     soe = soe_ if soe is None else soe
     S = S_ if S is None else S
@@ -177,7 +178,7 @@ def _layer_case(wl, blobs=None, soe=None, S=None, T=None, path=Q.MOE_PATH_AUTO, 
     if blobs is None:
         blobs = W.expert_blobs(wl)
     shared = W.shared_blob(wl)
-    layer = device_layer(wl, blobs, soe, S, shared, T, path)
+    layer = device_layer(wl, blobs, soe, S, shared, T, path, host_list_pinned=host_list_pinned)
     got = run_device(layer, x, logits)
     want = run_oracle(wl, blobs, x, logits, soe, shared, want_pairs=True)
     return got, want, soe, S
@@ -189,6 +190,7 @@ def _check_layer(wl, got, want, soe, S, tol=DECODE_TOL):
     ob = O.batches(want["ids"], want["w"], wl.E, soe, S)
     for key in ("slot_offsets", "active_slots", "perm_pair", "host_token", "host_expert"):
         assert np.array_equal(got[key], ob[key]), key
+    assert np.abs(got["host_weight"] - ob["host_weight"]).max(initial=0.0) <= _w_tol(wl)
     err = rel_max_err(got["y"], want["y"])
     say(f"  max|y-y*|/max|y*| = {err:.3e}")
     assert err <= tol
@@ -258,6 +260,17 @@ def test_decode_q8_0_many_tokens():
     soe = np.array([3, -1, 0, 5, -1, 1, 2, -1, 4, 6, -1, 7], dtype=np.int32)
     got, want, soe, S = _layer_case(wl, soe=soe, S=9)
     _check_layer(wl, got, want, soe, S)
+
+
+def test_host_list_written_into_pinned_memory():
+    """The batching kernel stores the host list straight into pinned host
+    memory (its device address); nothing is copied."""
+    wl = W.Workload("small Q8_0 layer, 37 tokens, partial residency", F.Q8_0, 384, 256, 12, 4, 37)
+    say(wl.name + ", host list in pinned memory")
+    soe = np.array([3, -1, 0, 5, -1, 1, 2, -1, 4, 6, -1, 7], dtype=np.int32)
+    got, want, soe, S = _layer_case(wl, soe=soe, S=9, host_list_pinned=True)
+    _check_layer(wl, got, want, soe, S)
+    assert got["host_count"] > 0
 
 
 def test_decode_zero_input_gives_zero():

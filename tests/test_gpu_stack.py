@@ -23,7 +23,7 @@ pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 WL = W.DSV3_STACK
 N_BLOBS, N_SHARED = 256, 8
 SAMPLE_LAYERS = (0, 29, 57)
-NODES_PER_LAYER = 11  # route, batches, 2 expert-FFN kernels, 2 shared-FFN kernels, combine, 4 host-list copies
+NODES_PER_LAYER = 7  # route, batches, 2 expert-FFN kernels, 2 shared-FFN kernels, combine (host list: no copy)
 
 
 def blob_of(l, e):
@@ -81,6 +81,7 @@ def _check_replay(ctx, check_layers):
         ob = O.batches(ids, w, WL.E, maps[l], st.S)
         hl = st.host_lists(l)
         assert np.array_equal(hl["token"], ob["host_token"]) and np.array_equal(hl["expert"], ob["host_expert"]), l
+        assert np.abs(hl["weight"] - ob["host_weight"]).max(initial=0.0) <= 1e-6 * WL.scale, l
     for l in check_layers:
         needed = set(ctx["lgs"][l].argsort(axis=1)[:, ::-1][:, :WL.k].ravel().tolist())
         experts = [ctx["blobs"][blob_of(l, e)] if e in needed else None for e in range(WL.E)]
