@@ -146,7 +146,7 @@ def main():
     torch.cuda.synchronize()
 
     # ---- eager pass with HIP-event stage timers (kernel durations on the launch stream)
-    stages = {"route": 0, "batches": 1, "ffn_gateup": 3, "ffn_down": 4, "combine": 5}
+    stages = {"route_batches": 8, "ffn_gateup": 3, "ffn_down": 4, "combine": 5}
     for s in stages.values():
         Q.moe_timer_begin(s, args.steps)
     torch.cuda.synchronize()
@@ -323,7 +323,37 @@ def bench_prefill(args, blobs, pool, stride) -> dict:
         "expert_gemms_frac": round((gu_flop + dn_flop) / ((kern["gemm_gateup"] + kern["gemm_down"]) * 1e-6) / 1e12 /
                                    MFMA_BF16_PEAK_TFLOPS, 4),
         "kernels_us": {k2: round(v, 2) for k2, v in kern.items()},
+        "library_gemm_ceiling": library_gemm_ceiling(M, wl.H, wl.I),
     }
+
+
+def library_gemm_ceiling(M: int, H: int, I: int, reps: int = 20) -> dict:
+    """What the platform's tuned dense bf16 GEMM (torch.matmul, i.e.
+    hipBLASLt) reaches on plain dense operands of the prefill's total shapes
+    (all M rows in one GEMM, weights already bf16, no grouping or
+    dequantization), and on a large square GEMM: the practical MFMA ceiling
+    the grouped kernels are read against.  Run only; nothing of it is used."""
+    import torch
+
+    out = {}
+    for name, (m, k, n) in {"gateup_shape": (M, H, 2 * I), "down_shape": (M, I, H),
+                            "square_8192": (8192, 8192, 8192)}.items():
+        a = torch.randn(m, k, device="cuda", dtype=torch.bfloat16)
+        b = torch.randn(k, n, device="cuda", dtype=torch.bfloat16).contiguous()
+        for _ in range(3):
+            torch.matmul(a, b)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / reps
+        out[name] = {"m_k_n": [m, k, n], "us": round(us, 2), "TFLOPs": round(2.0 * m * k * n / (us * 1e-6) / 1e12, 1)}
+        del a, b
+    torch.cuda.empty_cache()
+    return out
 
 
 def bench_dsv3(args, threads: int) -> dict:

@@ -12,6 +12,8 @@
  *   moe_route_topk            gate logits -> top-k expert ids and weights
  *   moe_build_expert_batches  ids + slot map -> per-slot token batches and the
  *                             list of pairs whose expert is not on the card
+ *   (moe_route_and_batch      the two above in one call: one launch at decode
+ *                             sizes)
  *   moe_expert_ffn_q4k /      dequantize + SwiGLU expert FFN over each slot's
  *   moe_expert_ffn_q8_0       batch (decode GEMV or prefill MFMA GEMM)
  *   moe_combine               weighted sum of the pairs (+ shared expert)
@@ -131,6 +133,24 @@ moe_status moe_build_expert_batches(const int32_t* topk_ids, const float* topk_w
                                     int32_t* host_token, int32_t* host_expert, float* host_weight,
                                     int32_t* host_count, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------- route and batch
+ * moe_route_topk followed by moe_build_expert_batches on the same stream,
+ * with the arguments of both (logits .. topk_w as for moe_route_topk, the
+ * rest as for moe_build_expert_batches; topk_ids and topk_w are outputs
+ * here).  Same outputs, bit for bit, and the same error behaviour (every
+ * check of both calls, before anything is enqueued).  With T <= 4,
+ * T*k <= 64 and E <= 256 (decode steps) it is a single workgroup launch that
+ * keeps the picks in LDS, saving a launch and the round trip of the ids and
+ * weights through memory; otherwise it launches the two calls' kernels.
+ * The workspace is that of moe_build_expert_batches
+ * (moe_batches_workspace_size).
+ */
+moe_status moe_route_and_batch(const float* logits, int T, int E, int k, int score, int renormalize, float scale,
+                               int32_t* topk_ids, float* topk_w, const int32_t* slot_of_expert, int S,
+                               int32_t* slot_offsets, int32_t* active_slots, int32_t* num_active, int32_t* perm_pair,
+                               int32_t* host_token, int32_t* host_expert, float* host_weight, int32_t* host_count,
+                               void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------ expert blobs
  * Each HBM slot holds one expert as a packed blob: the canonical stored
  * blocks of W_gate [I, H], W_up [I, H] and W_down [H, I] (rows = output
@@ -226,7 +246,8 @@ moe_status moe_combine(const void* y_pairs, int y_pairs_dtype, const int32_t* to
  * Diagnostics: hipEvent pairs recorded around every launch of one stage, on
  * the launch's stream.  Not for use while a stream is being captured.
  *   stage: 0 route, 1 batches, 2 prefill tile list, 3 ffn gate/up (decode),
- *          4 ffn down (decode), 5 combine, 6 prefill gate/up GEMM, 7 prefill down GEMM.
+ *          4 ffn down (decode), 5 combine, 6 prefill gate/up GEMM, 7 prefill down GEMM,
+ *          8 fused route + batches.
  * moe_timer_begin arms the stage for up to `capacity` launches (events are
  * created here, on the current device); moe_timer_end waits for the last
  * recorded event, returns the summed kernel time in milliseconds and the

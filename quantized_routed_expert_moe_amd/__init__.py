@@ -23,7 +23,8 @@ MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_F32, MOE_BF16 = 0, 1
 MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL = 0, 1, 2
 MOE_FMT_Q8_0, MOE_FMT_Q4K = 0, 1
-STAGES = ("route", "batches", "prefill_tiles", "ffn_gateup", "ffn_down", "combine", "prefill_gateup", "prefill_down")
+STAGES = ("route", "batches", "prefill_tiles", "ffn_gateup", "ffn_down", "combine", "prefill_gateup", "prefill_down",
+          "route_batches")
 
 
 class QmoeError(RuntimeError):
@@ -51,6 +52,8 @@ def lib() -> ctypes.CDLL:
         L.moe_batches_workspace_size.restype = sz
         L.moe_build_expert_batches.argtypes = [vp, vp, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                                vp]
+        L.moe_route_and_batch.argtypes = [vp, i32, i32, i32, i32, i32, f32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
+                                          vp, vp, vp, sz, vp]
         L.moe_expert_blob_bytes.argtypes = [i32, i32, i32]
         L.moe_expert_blob_bytes.restype = sz
         L.moe_pack_expert.argtypes = [i32, vp, vp, i32, i32]
@@ -178,6 +181,23 @@ def moe_build_expert_batches(topk_ids, topk_w, E: int, slot_of_expert, S: int, s
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().moe_build_expert_batches(
         _dev(topk_ids, _i32(), "topk_ids"), _dev(topk_w, _f32(), "topk_w"), T, k, E,
+        _dev(slot_of_expert, _i32(), "slot_of_expert"), S, _dev(slot_offsets, _i32(), "slot_offsets"),
+        _dev(active_slots, _i32(), "active_slots"), _dev(num_active, _i32(), "num_active"),
+        _dev(perm_pair, _i32(), "perm_pair"), _dev_or_mapped(host_token, _i32(), "host_token"),
+        _dev_or_mapped(host_expert, _i32(), "host_expert"), _dev_or_mapped(host_weight, _f32(), "host_weight"),
+        _dev_or_mapped(host_count, _i32(), "host_count"), _dev(ws, None, "ws"), ws_bytes, _stream(stream)))
+
+
+def moe_route_and_batch(logits, k: int, score: int, renormalize: bool, scale: float, topk_ids, topk_w, E: int,
+                        slot_of_expert, S: int, slot_offsets, active_slots, num_active, perm_pair, host_token,
+                        host_expert, host_weight, host_count, ws=None, stream=None):
+    T, E_ = logits.shape
+    if E_ != E:
+        raise ValueError(f"logits have {E_} experts, E = {E}")
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().moe_route_and_batch(
+        _dev(logits, _f32(), "logits"), T, E, k, score, int(bool(renormalize)), float(scale),
+        _dev(topk_ids, _i32(), "topk_ids"), _dev(topk_w, _f32(), "topk_w"),
         _dev(slot_of_expert, _i32(), "slot_of_expert"), S, _dev(slot_offsets, _i32(), "slot_offsets"),
         _dev(active_slots, _i32(), "active_slots"), _dev(num_active, _i32(), "num_active"),
         _dev(perm_pair, _i32(), "perm_pair"), _dev_or_mapped(host_token, _i32(), "host_token"),

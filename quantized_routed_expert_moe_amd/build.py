@@ -17,7 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 SO = os.path.join(HERE, "libqmoe.so")
 
-SOURCES = ["abi.cpp", "route.hip", "batches.hip", "ffn_decode.hip", "ffn_prefill.hip", "combine.hip"]
+SOURCES = ["abi.cpp", "route.hip", "batches.hip", "route_batches.hip", "ffn_decode.hip", "ffn_prefill.hip",
+           "combine.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -352,6 +352,34 @@ moe_status moe_build_expert_batches(const int32_t* topk_ids, const float* topk_w
     return MOE_OK;
 }
 
+moe_status moe_route_and_batch(const float* logits, int T, int E, int k, int score, int renormalize, float scale,
+                               int32_t* topk_ids, float* topk_w, const int32_t* slot_of_expert, int S,
+                               int32_t* slot_offsets, int32_t* active_slots, int32_t* num_active, int32_t* perm_pair,
+                               int32_t* host_token, int32_t* host_expert, float* host_weight, int32_t* host_count,
+                               void* ws, size_t ws_bytes, void* stream) {
+    moe_status st = check_route_shape(T, E, k);
+    if (st != MOE_OK) return st;
+    if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "score = %d is not softmax or sigmoid", score);
+    if (!(scale == scale)) return fail(MOE_ERR_INVALID_ARGUMENT, "scale is NaN");
+    if (S < 0 || S > E) return fail(MOE_ERR_INVALID_ARGUMENT, "S = %d outside 0..E (%d)", S, E);
+    if (!slot_of_expert || !slot_offsets || !num_active || !host_count)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+    if (T > 0 && (!logits || !topk_ids || !topk_w || !perm_pair || !host_token || !host_expert || !host_weight ||
+                  (S > 0 && !active_slots)))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+    const size_t need = moe_batches_workspace_size(T, k, E, S);
+    if (ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "batches workspace %zu bytes, %zu needed", ws_bytes, need);
+    if (need > 0 && !ws) return fail(MOE_ERR_INVALID_ARGUMENT, "batches workspace pointer is NULL");
+    hipError_t e = qmoe::launch_route_batches(logits, T, E, k, score, renormalize, scale, topk_ids, topk_w,
+                                              slot_of_expert, S, slot_offsets, active_slots, num_active, perm_pair,
+                                              host_token, host_expert, host_weight, host_count, ws,
+                                              (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "route and batch launch");
+    return MOE_OK;
+}
+
 size_t moe_expert_blob_bytes(int format, int H, int I) {
     if (check_shape(format, H, I) != MOE_OK) return 0;
     return blob_bytes(format, H, I);

@@ -18,6 +18,7 @@
 // (exclusive over waves, then over buckets); pass B places every pair at
 // start + running count + rank.  Every output is therefore a pure function of
 // the inputs: stable in p and identical from run to run.
+#include "batches_common.h"
 #include "device_common.h"
 #include "qmoe_internal.h"
 
@@ -32,17 +33,6 @@ __device__ __forceinline__ int bucket_of(const int32_t* __restrict__ ids, const 
     return (s >= 0 && s < S) ? s : S;
 }
 
-// Lanes (among `valid`) whose bucket equals this lane's.
-__device__ __forceinline__ unsigned long long match_bucket(int b, bool valid, int nbits) {
-    unsigned long long m = __ballot(valid);
-    for (int bit = 0; bit < nbits; ++bit) {
-        const bool set = (b >> bit) & 1;
-        const unsigned long long bb = __ballot(set);
-        m &= set ? bb : ~bb;
-    }
-    return m;
-}
-
 __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -52,31 +42,7 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
     return v;
 }
 
-// Inclusive prefix sum over the wave with DPP moves (row shifts, then row
-// broadcasts across the four 16-lane rows).
-template <int CTRL, int ROW_MASK = 0xF>
-__device__ __forceinline__ int dpp_add_i(int v) {
-    return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
-}
-__device__ __forceinline__ int wave_scan_dpp(int v) {
-    v = dpp_add_i<0x111>(v);  // row_shr:1
-    v = dpp_add_i<0x112>(v);  // row_shr:2
-    v = dpp_add_i<0x114>(v);  // row_shr:4
-    v = dpp_add_i<0x118>(v);  // row_shr:8
-    v = dpp_add_i<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
-    v = dpp_add_i<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
-    return v;
-}
-
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// P <= 64: lane p owns pair p.  Same outputs as the workgroup kernel (bucket
-// match by ballots, stable positions start[b] + rank), with the bucket scan
-// done by one wave in 64-bucket steps.
+// P <= 64: lane p owns pair p (batch_wave).
 __global__ __launch_bounds__(64) void batches_wave_kernel(const int32_t* __restrict__ ids, const float* __restrict__ w,
                                                           int T, int k, int E, const int32_t* __restrict__ soe, int S,
                                                           int nbits, int32_t* __restrict__ offsets,
@@ -89,47 +55,12 @@ __global__ __launch_bounds__(64) void batches_wave_kernel(const int32_t* __restr
     extern __shared__ int cnt[];  // [S + 1]: counts, then starting positions
     const int P = T * k;
     const int lane = threadIdx.x;
-    const unsigned long long lt = (1ull << lane) - 1ull;
     const bool valid = lane < P;
     const int id = valid ? ids[lane] : 0;
     const float wt = valid ? w[lane] : 0.0f;
-    for (int i = lane; i <= S; i += 64) cnt[i] = 0;
     const int sl = (valid && id >= 0 && id < E) ? soe[id] : -1;
-    const int b = valid ? ((sl >= 0 && sl < S) ? sl : S) : 0;
-    const unsigned long long m = match_bucket(b, valid, nbits);
-    const int rank = __popcll(m & lt);
-    wave_lds_sync();
-    if (valid && rank == 0) cnt[b] = __popcll(m);
-    wave_lds_sync();
-    int carry = 0, acarry = 0;
-    for (int c0 = 0; c0 < S; c0 += 64) {
-        const int bb = c0 + lane;
-        const int c = bb < S ? cnt[bb] : 0;
-        const int f = c > 0 ? 1 : 0;
-        const int inc = wave_scan_dpp(c), finc = wave_scan_dpp(f);
-        if (bb < S) {
-            offsets[bb] = carry + inc - c;
-            cnt[bb] = carry + inc - c;
-            if (f) active[acarry + finc - f] = bb;
-        }
-        carry += __builtin_amdgcn_readlane(inc, 63);
-        acarry += __builtin_amdgcn_readlane(finc, 63);
-    }
-    if (lane == 0) {
-        offsets[S] = carry;
-        *num_active = acarry;
-        *host_count = cnt[S];
-    }
-    wave_lds_sync();
-    if (valid) {
-        if (b < S) {
-            perm[cnt[b] + rank] = lane;
-        } else {
-            host_token[rank] = lane / k;
-            host_expert[rank] = id;
-            host_weight[rank] = wt;
-        }
-    }
+    batch_wave(lane, P, k, S, nbits, id, wt, sl, cnt, offsets, active, num_active, perm, host_token, host_expert,
+               host_weight, host_count);
 }
 
 __global__ __launch_bounds__(512) void batches_kernel(const int32_t* __restrict__ ids, const float* __restrict__ w,

@@ -68,7 +68,8 @@ enum Stage {
     kStageCombine = 5,
     kStagePrefillGateUp = 6,
     kStagePrefillDown = 7,
-    kStageCount = 8
+    kStageRouteBatches = 8,
+    kStageCount = 9
 };
 
 // Record the start / stop event of a launch of `stage` if its timer is armed.
@@ -87,6 +88,14 @@ hipError_t launch_batches(const int32_t* ids, const float* w, int T, int k, int 
                           int S, int32_t* slot_offsets, int32_t* active_slots, int32_t* num_active,
                           int32_t* perm_pair, int32_t* host_token, int32_t* host_expert, float* host_weight,
                           int32_t* host_count, void* ws, hipStream_t s);
+
+// moe_route_topk then moe_build_expert_batches; one fused launch for up to
+// four rows, 64 pairs and 256 experts.
+hipError_t launch_route_batches(const float* logits, int T, int E, int k, int score, int renormalize, float scale,
+                                int32_t* ids, float* w, const int32_t* slot_of_expert, int S, int32_t* slot_offsets,
+                                int32_t* active_slots, int32_t* num_active, int32_t* perm_pair, int32_t* host_token,
+                                int32_t* host_expert, float* host_weight, int32_t* host_count, void* ws,
+                                hipStream_t s);
 
 struct FfnArgs {
     int format;  // 0 Q8_0, 1 Q4_K

@@ -1,7 +1,8 @@
-"""One MoE layer as the sequence of the five library calls, with its buffers.
+"""One MoE layer as a sequence of library calls, with its buffers.
 
 Orchestration only: device buffers come from torch, every step is a call
-into libqmoe.  The optional shared expert runs through moe_expert_ffn_q8_0
+into libqmoe: routing and batching (moe_route_and_batch, one launch at decode
+sizes), the expert FFN, the combine.  The optional shared expert runs through moe_expert_ffn_q8_0
 with a one-slot identity batch, on a side stream forked from the layer's
 stream by an event and joined before the combine.  Nothing synchronises with
 the host, so `forward` can be captured into a HIP graph.
@@ -14,8 +15,8 @@ import numpy as np
 import torch
 
 from . import (MOE_FMT_Q4K, MOE_FMT_Q8_0, MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL, moe_batches_workspace_size,
-               moe_build_expert_batches, moe_combine, moe_expert_blob_bytes, moe_expert_ffn_q4k,
-               moe_expert_ffn_q8_0, moe_ffn_workspace_size, moe_pack_expert, moe_route_topk)
+               moe_combine, moe_expert_blob_bytes, moe_expert_ffn_q4k, moe_expert_ffn_q8_0, moe_ffn_workspace_size,
+               moe_pack_expert, moe_route_and_batch)
 
 
 def upload_packed_experts(fmt: int, canonical_blobs: np.ndarray, H: int, I: int, stride: int | None = None,
@@ -111,10 +112,10 @@ class MoELayer:
                                 self.sh_active, self.sh_num, self.sh_perm, self.y_shared, MOE_PATH_DECODE, self.sh_ws,
                                 self.sh_stream)
             self.sh_join.record(self.sh_stream)
-        moe_route_topk(logits, spec.k, spec.score, spec.renormalize, spec.scale, self.ids, self.w, stream)
-        moe_build_expert_batches(self.ids, self.w, spec.E, self.slot_of_expert, self.S, self.slot_offsets,
-                                 self.active_slots, self.num_active, self.perm_pair, self.host_token, self.host_expert,
-                                 self.host_weight, self.host_count, self.batch_ws, stream)
+        moe_route_and_batch(logits, spec.k, spec.score, spec.renormalize, spec.scale, self.ids, self.w, spec.E,
+                            self.slot_of_expert, self.S, self.slot_offsets, self.active_slots, self.num_active,
+                            self.perm_pair, self.host_token, self.host_expert, self.host_weight, self.host_count,
+                            self.batch_ws, stream)
         ffn = moe_expert_ffn_q4k if spec.fmt == MOE_FMT_Q4K else moe_expert_ffn_q8_0
         ffn(pool, self.stride, self.S, spec.H, spec.I, x, spec.k, self.slot_offsets, self.active_slots,
             self.num_active, self.perm_pair, self.y_pairs, self.path, self.ws, stream)

@@ -52,6 +52,24 @@ def test_route_rejects_null():
     assert st == Q.MOE_ERR_INVALID_ARGUMENT and "NULL" in msg
 
 
+def _route_batch(T=4, E=8, k=2, score=0, scale=1.0, S=8, ws_bytes=0, logits=FAKE):
+    return _call("moe_route_and_batch", logits, T, E, k, score, 1, ctypes.c_float(scale), FAKE, FAKE, FAKE, S, FAKE,
+                 FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,want,needle", [
+    (dict(k=9), Q.MOE_ERR_INVALID_ARGUMENT, ""),
+    (dict(score=7), Q.MOE_ERR_INVALID_ARGUMENT, "score"),
+    (dict(scale=float("nan")), Q.MOE_ERR_INVALID_ARGUMENT, "NaN"),
+    (dict(S=9), Q.MOE_ERR_INVALID_ARGUMENT, "S = 9"),
+    (dict(logits=None), Q.MOE_ERR_INVALID_ARGUMENT, "NULL"),
+    (dict(T=4096, E=128, k=8, S=128), Q.MOE_ERR_WORKSPACE_TOO_SMALL, "workspace"),
+])
+def test_route_and_batch_rejects(kw, want, needle):
+    st, msg = _route_batch(**kw)
+    assert st == want and needle in msg, msg
+
+
 def test_batches_rejects_bad_slot_count():
     st, msg = _call("moe_build_expert_batches", FAKE, FAKE, 4, 2, 8, FAKE, 9, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                     FAKE, None, 0, None)

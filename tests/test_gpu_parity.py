@@ -139,6 +139,87 @@ def test_batches_match_oracle(wl, smap):
          if not (0 <= soe[ids[t, j]] < S)]])
 
 
+# ------------------------------------------------------- route and batch
+
+def _route_batch_device(logits, k, score, renorm, scale, soe, S):
+    T, E = logits.shape
+    P = T * k
+    i32 = dict(dtype=torch.int32, device="cuda")
+    ids = torch.full((max(T, 1), k), -7, **i32)[:T]
+    w = torch.zeros((max(T, 1), k), dtype=torch.float32, device="cuda")[:T]
+    out = dict(slot_offsets=torch.full((S + 1,), -5, **i32), active_slots=torch.full((max(1, min(S, P)),), -5, **i32),
+               num_active=torch.full((1,), -5, **i32), perm_pair=torch.full((max(1, P),), -5, **i32),
+               host_token=torch.full((max(1, P),), -5, **i32), host_expert=torch.full((max(1, P),), -5, **i32),
+               host_weight=torch.full((max(1, P),), -5.0, dtype=torch.float32, device="cuda"),
+               host_count=torch.full((1,), -5, **i32))
+    wsb = Q.moe_batches_workspace_size(T, k, E, S)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda") if wsb else None
+    Q.moe_route_and_batch(torch.from_numpy(np.ascontiguousarray(logits)).cuda(), k, score, renorm, scale, ids, w, E,
+                          torch.from_numpy(soe).cuda(), S, out["slot_offsets"], out["active_slots"],
+                          out["num_active"], out["perm_pair"], out["host_token"], out["host_expert"],
+                          out["host_weight"], out["host_count"], ws)
+    torch.cuda.synchronize()
+    o = {key: v.cpu().numpy() for key, v in out.items()}
+    na, nres, hc = int(o["num_active"][0]), int(o["slot_offsets"][S]), int(o["host_count"][0])
+    o["active_slots"] = o["active_slots"][:na]
+    o["perm_pair"] = o["perm_pair"][:nres]
+    for key in ("host_token", "host_expert", "host_weight"):
+        o[key] = o[key][:hc]
+    o["ids"], o["w"] = ids.cpu().numpy(), w.cpu().numpy()
+    return o
+
+
+@pytest.mark.parametrize("T,E,k,score,renorm,scale", [
+    (1, 128, 8, 0, True, 1.0),     # fused: Qwen3 decode shape
+    (2, 128, 8, 0, True, 1.0),
+    (4, 256, 8, 1, True, 2.5),     # fused: DeepSeek-V3 decode shape
+    (4, 8, 2, 0, True, 1.0),       # fused: tiny
+    (4, 256, 16, 0, False, 1.0),   # fused: 64 pairs, full softmax denominator
+    (3, 100, 5, 1, False, 0.5),    # fused: E not a power of two
+    (5, 128, 8, 0, True, 1.0),     # two launches: T > 4
+    (2, 64, 40, 0, True, 1.0),     # two launches: 80 pairs
+    (3, 300, 8, 1, True, 2.5),     # two launches: E > 256
+])
+@pytest.mark.parametrize("smap", ["identity", "half", "none"])
+def test_route_and_batch_matches_oracle_and_two_calls(T, E, k, score, renorm, scale, smap):
+    say(f"route and batch T={T} E={E} k={k} score={score} renorm={renorm} map={smap}")
+    lg = F.logits_normal(11, T, T, E)
+    soe, S = _slot_maps(E, np.random.default_rng(E + T + len(smap)))[smap]
+    got = _route_batch_device(lg, k, score, renorm, scale, soe, S)
+    oids, ow = O.route(lg, k, score, renorm, scale)
+    assert np.array_equal(got["ids"], oids)
+    assert np.abs(got["w"] - ow).max() <= 1e-6 * max(1.0, scale)
+    want = O.batches(oids, ow, E, soe, S)
+    for key in ("slot_offsets", "active_slots", "perm_pair", "host_token", "host_expert"):
+        assert np.array_equal(got[key], want[key]), key
+    assert int(got["num_active"][0]) == int(want["num_active"][0])
+    assert int(got["host_count"][0]) == int(want["host_count"][0])
+    # the same bits as the two separate calls
+    ids2, w2 = _route_device(lg, k, score, renorm, scale)
+    assert np.array_equal(got["ids"], ids2) and np.array_equal(got["w"].view(np.uint32), w2.view(np.uint32))
+    two = _batches_device(ids2, w2, E, soe, S)
+    for key in ("slot_offsets", "active_slots", "perm_pair", "host_token", "host_expert", "host_weight"):
+        assert np.array_equal(got[key], two[key]), key
+
+
+def test_route_and_batch_ties():
+    """The rank order (logit desc, id asc) with many equal logits, through the
+    single-launch path (4 rows, 64 pairs)."""
+    say("route and batch ties")
+    lg = np.zeros((4, 200), dtype=np.float32)
+    lg[0] = 1.0
+    lg[1, ::7] = 2.0
+    lg[2, [3, 67, 131, 195]] = 5.0
+    lg[3] = np.arange(200) % 5
+    soe, S = _slot_maps(200, np.random.default_rng(5))["half"]
+    got = _route_batch_device(lg, 16, 0, True, 1.0, soe, S)
+    oids, ow = O.route(lg, 16, 0, True, 1.0)
+    assert np.array_equal(got["ids"], oids)
+    want = O.batches(oids, ow, 200, soe, S)
+    for key in ("slot_offsets", "active_slots", "perm_pair", "host_token", "host_expert"):
+        assert np.array_equal(got[key], want[key]), key
+
+
 def test_batches_stack_residency():
     wl = W.DSV3_STACK
     for layer in (0, 29, 57):
