@@ -130,8 +130,8 @@ __global__ __launch_bounds__(256) void route_rank_kernel(const float* __restrict
     const int row = blockIdx.x, tid = threadIdx.x;
     const float* l = logits + (size_t)row * E;
     const float v = (tid < EMAX && tid < E) ? l[tid] : 0.0f;
-    route_row<EMAX>(sh, v, l, E, k, score, renormalize, scale, ids + (size_t)row * k, w + (size_t)row * k, nullptr,
-                    nullptr);
+    route_row<EMAX>(sh, tid, v, l, E, k, score, renormalize, scale, ids + (size_t)row * k, w + (size_t)row * k,
+                    nullptr, nullptr);
 }
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int score, int renormalize, float scale,

@@ -1,11 +1,12 @@
 // Routing and batching of a decode-sized step in one workgroup.  The two
 // steps are a dependent chain of tiny launches (a few rows of logits, at most
 // 64 pairs); run back to back they cost two launch latencies and a round trip
-// of the ids and weights through memory.  Here one 256-thread workgroup
-// requests every logit of the step and the slot map at once, selects each
-// row's top k with the rank count of the routing kernel (route_row), keeps
-// the picks in LDS, and its first wave groups the pairs with the same
-// ballot-match batching as the single-wave batching kernel (batch_wave).
+// of the ids and weights through memory.  Here one workgroup of 256 threads
+// per row requests every logit of the step and the slot map at once, each
+// 256-thread group selects its row's top k with the rank count of the
+// routing kernel (route_row, all rows at once), the picks stay in LDS, and
+// the first wave groups the pairs with the same ballot-match batching as the
+// single-wave batching kernel (batch_wave).
 // Outputs are those of moe_route_topk followed by moe_build_expert_batches,
 // bit for bit.  Larger steps launch those two kernels.
 #include "batches_common.h"
@@ -18,35 +19,31 @@ namespace qmoe {
 constexpr int kFusedMaxRows = 4;
 
 template <int EMAX>
-__global__ __launch_bounds__(256) void route_batches_kernel(
+__global__ __launch_bounds__(256 * kFusedMaxRows) void route_batches_kernel(
     const float* __restrict__ logits, int T, int E, int k, int score, int renormalize, float scale,
     int32_t* __restrict__ ids, float* __restrict__ w, const int32_t* __restrict__ soe, int S, int nbits,
     int32_t* __restrict__ offsets, int32_t* __restrict__ active, int32_t* __restrict__ num_active,
     int32_t* __restrict__ perm, int32_t* __restrict__ host_token, int32_t* __restrict__ host_expert,
     float* __restrict__ host_weight, int32_t* __restrict__ host_count) {
-    __shared__ __align__(16) RouteShared<EMAX> sh;
+    __shared__ __align__(16) RouteShared<EMAX> sh[kFusedMaxRows];
     __shared__ int32_t s_ids[64];
     __shared__ float s_w[64];
     __shared__ int s_soe[EMAX];
     __shared__ int cnt[EMAX + 1];
-    const int tid = threadIdx.x;
-    float v[kFusedMaxRows];
-#pragma unroll
-    for (int t = 0; t < kFusedMaxRows; ++t) v[t] = (t < T && tid < E) ? logits[(size_t)t * E + tid] : 0.0f;
-    if (tid < E) s_soe[tid] = soe[tid];
-#pragma unroll
-    for (int t = 0; t < kFusedMaxRows; ++t)
-        if (t < T)
-            route_row<EMAX>(sh, v[t], logits + (size_t)t * E, E, k, score, renormalize, scale, ids + t * k,
-                            w + t * k, s_ids + t * k, s_w + t * k);
+    const int t = threadIdx.x >> 8, tid = threadIdx.x & 255;  // row, thread within its row's group (blockDim = 256 T)
+    const float* l = logits + (size_t)t * E;
+    const float v = tid < E ? l[tid] : 0.0f;
+    if (threadIdx.x < E) s_soe[threadIdx.x] = soe[threadIdx.x];
+    route_row<EMAX>(sh[t], tid, v, l, E, k, score, renormalize, scale, ids + t * k, w + t * k, s_ids + t * k,
+                    s_w + t * k);
     __syncthreads();
-    if (tid < 64) {
-        const int P = T * k;
-        const bool valid = tid < P;
-        const int id = valid ? s_ids[tid] : 0;
-        const float wt = valid ? s_w[tid] : 0.0f;
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x, P = T * k;
+        const bool valid = lane < P;
+        const int id = valid ? s_ids[lane] : 0;
+        const float wt = valid ? s_w[lane] : 0.0f;
         const int sl = (valid && id >= 0 && id < E) ? s_soe[id] : -1;
-        batch_wave(tid, P, k, S, nbits, id, wt, sl, cnt, offsets, active, num_active, perm, host_token, host_expert,
+        batch_wave(lane, P, k, S, nbits, id, wt, sl, cnt, offsets, active, num_active, perm, host_token, host_expert,
                    host_weight, host_count);
     }
 }
@@ -67,11 +64,11 @@ hipError_t launch_route_batches(const float* logits, int T, int E, int k, int sc
     while ((1 << nbits) <= S) ++nbits;  // buckets 0..S
     timer_before(kStageRouteBatches, s);
     if (E <= 128)
-        hipLaunchKernelGGL(route_batches_kernel<128>, dim3(1), dim3(256), 0, s, logits, T, E, k, score, renormalize,
+        hipLaunchKernelGGL(route_batches_kernel<128>, dim3(1), dim3(256 * T), 0, s, logits, T, E, k, score, renormalize,
                            scale, ids, w, soe, S, nbits, offsets, active, num_active, perm, host_token, host_expert,
                            host_weight, host_count);
     else
-        hipLaunchKernelGGL(route_batches_kernel<256>, dim3(1), dim3(256), 0, s, logits, T, E, k, score, renormalize,
+        hipLaunchKernelGGL(route_batches_kernel<256>, dim3(1), dim3(256 * T), 0, s, logits, T, E, k, score, renormalize,
                            scale, ids, w, soe, S, nbits, offsets, active, num_active, perm, host_token, host_expert,
                            host_weight, host_count);
     timer_after(kStageRouteBatches, s);

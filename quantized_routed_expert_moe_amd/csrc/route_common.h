@@ -51,21 +51,22 @@ struct RouteShared {
     int pi[64];
 };
 
-// All 256 threads of the workgroup select the top k of one row (E <= EMAX
-// logits at `l`; thread t < EMAX passes logit t in v).  Thread t ranks key
+// A group of 256 threads (thread index `tid` within the group) selects the
+// top k of one row (E <= EMAX logits at `l`; thread t < EMAX passes logit t
+// in v).  Every thread of the workgroup calls it together (it holds
+// workgroup barriers), each group with its own row and `sh`.  Thread t ranks key
 // t % EMAX against the keys [h * EMAX / NH, (h + 1) * EMAX / NH), h = t /
 // EMAX (NH = 2 halves when EMAX <= 128, else 1); the partial ranks meet in
-// LDS, and ranks < k place the picks in order.  Wave 0 then forms the weights
-// and writes ids / scale * weights to ids[0..k) and w[0..k), and to lds_ids /
-// lds_w when those are given.  Safe to call for consecutive rows with the
+// LDS, and ranks < k place the picks in order.  The group's first wave then
+// forms the weights and writes ids / scale * weights to ids[0..k) and
+// w[0..k), and to lds_ids / lds_w when those are given.  Safe to call for consecutive rows with the
 // same `sh` (each of the shared arrays is rewritten only after a barrier
 // that every reader of its previous contents has passed).
 template <int EMAX>
-__device__ __forceinline__ void route_row(RouteShared<EMAX>& sh, float v, const float* l, int E, int k, int score,
-                                          int renormalize, float scale, int32_t* ids, float* w, int32_t* lds_ids,
-                                          float* lds_w) {
+__device__ __forceinline__ void route_row(RouteShared<EMAX>& sh, int tid, float v, const float* l, int E, int k,
+                                          int score, int renormalize, float scale, int32_t* ids, float* w,
+                                          int32_t* lds_ids, float* lds_w) {
     constexpr int NH = RouteShared<EMAX>::kHalves;
-    const int tid = threadIdx.x;
     const int e = tid % EMAX, h = tid / EMAX;
     if (tid < EMAX) sh.key[e] = e < E ? rank_key(v, e) : 0;  // padding keys rank after every real key
     if (tid < 64) {  // every pick slot holds a valid entry even if ranks collide (non-finite logits)
