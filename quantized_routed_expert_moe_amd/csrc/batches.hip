@@ -4,10 +4,11 @@
 // bloomery README of 2026-09-24, opening list).
 //
 // Up to 64 pairs (decode): a single wave, no workgroup barriers.  Up to
-// kSingleMaxPairs pairs: one workgroup of 8 waves (below).  Above:
-// three launches over 1024-pair blocks -- per-block bucket counts, one
-// workgroup scanning (bucket, block) counts into starting positions, and a
-// per-block stable scatter -- with the same in-wave ranking.
+// kSingleMaxPairs pairs: one workgroup of 8 waves (below).  Above: launches
+// over 1024-pair blocks -- per-block bucket counts, then a per-block stable
+// scatter with the same in-wave ranking.  Up to 64 blocks every scatter block
+// scans the count table itself; beyond that one workgroup scans (bucket,
+// block) counts into starting positions between the two.
 //
 // Single workgroup: 8 waves.  Bucket b of pair p is its slot, or S for "not
 // resident".  Wave w owns a contiguous run of pairs, walked in 64-pair steps.
@@ -294,6 +295,98 @@ __global__ __launch_bounds__(256) void batches_scatter_kernel(const int32_t* __r
     }
 }
 
+// Up to kScanInScatterBlocks blocks: the scan folded into the scatter.  Every
+// block reads the count table (nblk x (S+1) ints, in L2) and forms its own
+// starting positions -- the bucket totals' exclusive scan plus the counts of
+// the blocks before it -- so no separate scan launch is needed; block 0 also
+// writes slot_offsets, the active slots and the counts.
+constexpr int kScanInScatterBlocks = 64;
+
+__global__ __launch_bounds__(256) void batches_scan_scatter_kernel(
+    const int32_t* __restrict__ ids, const float* __restrict__ w, int T, int k, int E, const int32_t* __restrict__ soe,
+    int S, int nbits, int nblk, const int32_t* __restrict__ gcnt, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ active, int32_t* __restrict__ num_active, int32_t* __restrict__ perm,
+    int32_t* __restrict__ host_token, int32_t* __restrict__ host_expert, float* __restrict__ host_weight,
+    int32_t* __restrict__ host_count) {
+    extern __shared__ int lds[];
+    const int NB = S + 1;
+    int* wcnt = lds;                    // [kMbWaves][NB]
+    int* start = lds + kMbWaves * NB;   // [NB]: bucket totals, then this block's starting positions
+    int* before = start + NB;           // [NB]: counts of the blocks before this one
+    const int P = T * k;
+    block_wave_counts(ids, soe, P, E, S, nbits, wcnt);
+    for (int b = threadIdx.x; b < NB; b += blockDim.x) {
+        int tot = 0, pre = 0;
+#pragma unroll 8
+        for (int blk = 0; blk < nblk; ++blk) {
+            const int c = gcnt[(size_t)blk * NB + b];
+            tot += c;
+            pre += blk < (int)blockIdx.x ? c : 0;
+        }
+        start[b] = tot;
+        before[b] = pre;
+    }
+    __syncthreads();
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    if (wave == 0) {  // exclusive scan of the slot buckets; the host bucket starts at 0
+        int carry = 0, acarry = 0;
+        for (int c0 = 0; c0 < S; c0 += 64) {
+            const int b = c0 + lane;
+            const int c = b < S ? start[b] : 0;
+            const int f = c > 0 ? 1 : 0;
+            const int inc = wave_scan_dpp(c), finc = wave_scan_dpp(f);
+            if (b < S) {
+                start[b] = carry + inc - c;
+                if (blockIdx.x == 0) {
+                    offsets[b] = carry + inc - c;
+                    if (f) active[acarry + finc - f] = b;
+                }
+            }
+            carry += __builtin_amdgcn_readlane(inc, 63);
+            acarry += __builtin_amdgcn_readlane(finc, 63);
+        }
+        if (lane == 0) {
+            if (blockIdx.x == 0) {
+                offsets[S] = carry;
+                *num_active = acarry;
+                *host_count = start[S];
+            }
+            start[S] = 0;
+        }
+    }
+    __syncthreads();
+    // this block's start per bucket + exclusive prefix over its waves
+    for (int b = threadIdx.x; b < NB; b += blockDim.x) {
+        int run = start[b] + before[b];
+        for (int wv = 0; wv < kMbWaves; ++wv) {
+            const int c = wcnt[wv * NB + b];
+            wcnt[wv * NB + b] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    const int begin = blockIdx.x * kBlockPairs + wave * (kBlockPairs / kMbWaves);
+    const int end = min(P, begin + kBlockPairs / kMbWaves);
+    for (int base = begin; base < end; base += 64) {
+        const int p = base + lane;
+        const bool valid = p < end;
+        const int b = valid ? bucket_of(ids, soe, p, E, S) : 0;
+        const unsigned long long m = match_bucket(b, valid, nbits);
+        if (valid) {
+            const int pos = wcnt[wave * NB + b] + __popcll(m & lt);
+            if (b < S) {
+                perm[pos] = p;
+            } else {
+                host_token[pos] = p / k;
+                host_expert[pos] = ids[p];
+                host_weight[pos] = w[p];
+            }
+        }
+        if (valid && (m & lt) == 0ull) wcnt[wave * NB + b] += __popcll(m);
+    }
+}
+
 hipError_t launch_batches(const int32_t* ids, const float* w, int T, int k, int E, const int32_t* soe, int S,
                           int32_t* offsets, int32_t* active, int32_t* num_active, int32_t* perm,
                           int32_t* host_token, int32_t* host_expert, float* host_weight, int32_t* host_count,
@@ -315,10 +408,17 @@ hipError_t launch_batches(const int32_t* ids, const float* w, int T, int k, int 
         int32_t* gcnt = static_cast<int32_t*>(ws);
         const size_t lds = (size_t)kMbWaves * (S + 1) * sizeof(int);
         hipLaunchKernelGGL(batches_count_kernel, dim3(nblk), dim3(256), lds, s, ids, soe, (int)P, E, S, nbits, gcnt);
-        hipLaunchKernelGGL(batches_scan_kernel, dim3(1), dim3(1024), 0, s, nblk, S, gcnt, offsets, active, num_active,
-                           host_count);
-        hipLaunchKernelGGL(batches_scatter_kernel, dim3(nblk), dim3(256), lds, s, ids, w, T, k, E, soe, S, nbits,
-                           (const int32_t*)gcnt, perm, host_token, host_expert, host_weight);
+        if (nblk <= kScanInScatterBlocks) {
+            const size_t lds2 = (size_t)(kMbWaves + 2) * (S + 1) * sizeof(int);
+            hipLaunchKernelGGL(batches_scan_scatter_kernel, dim3(nblk), dim3(256), lds2, s, ids, w, T, k, E, soe, S,
+                               nbits, nblk, (const int32_t*)gcnt, offsets, active, num_active, perm, host_token,
+                               host_expert, host_weight, host_count);
+        } else {
+            hipLaunchKernelGGL(batches_scan_kernel, dim3(1), dim3(1024), 0, s, nblk, S, gcnt, offsets, active,
+                               num_active, host_count);
+            hipLaunchKernelGGL(batches_scatter_kernel, dim3(nblk), dim3(256), lds, s, ids, w, T, k, E, soe, S, nbits,
+                               (const int32_t*)gcnt, perm, host_token, host_expert, host_weight);
+        }
     }
     timer_after(kStageBatches, s);
     return hipGetLastError();

@@ -220,6 +220,22 @@ def test_route_and_batch_ties():
         assert np.array_equal(got[key], want[key]), key
 
 
+@pytest.mark.parametrize("T", [8192, 9000])
+def test_batches_block_counts_around_the_fused_scan_limit(T):
+    """64 blocks of 1024 pairs (the scan folded into the scatter) and 71
+    blocks (the separate scan launch)."""
+    E, k = 128, 8
+    say(f"batches T={T} k={k} ({T * k} pairs)")
+    lg = F.logits_normal(21, 0, T, E)
+    ids, w = O.route(lg, k, 0, True, 1.0)
+    soe, S = _slot_maps(E, np.random.default_rng(T))["half"]
+    got = _batches_device(ids, w, E, soe, S)
+    want = O.batches(ids, w, E, soe, S)
+    for key in ("slot_offsets", "active_slots", "perm_pair", "host_token", "host_expert"):
+        assert np.array_equal(got[key], want[key]), key
+    assert int(got["host_count"][0]) == int(want["host_count"][0])
+
+
 def test_batches_stack_residency():
     wl = W.DSV3_STACK
     for layer in (0, 29, 57):
