@@ -54,6 +54,8 @@ def test_route_matches_oracle(wl):
     (9, 130, 3, 0, False, 1.0),
     (9, 130, 3, 1, False, 0.5),
     (1, 1, 1, 0, True, 1.0),
+    (3, 256, 64, 0, True, 1.0),    # two-level rank: every key a candidate
+    (4, 200, 33, 1, True, 2.5),    # two-level rank, ragged last group
 ])
 def test_route_shapes(T, E, k, score, renorm, scale):
     say(f"route T={T} E={E} k={k} score={score} renorm={renorm}")
