@@ -462,7 +462,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(const uint8_t* __restrict__ p
                                                    const int32_t* __restrict__ num_active,
                                                    const int32_t* __restrict__ perm, uint32_t* __restrict__ hw,
                                                    float2* __restrict__ hcs, float* __restrict__ y_pairs,
-                                                   int units_per_wave) {
+                                                   int units_per_wave, float* __restrict__ part) {
     __shared__ __align__(16) uint32_t stage_w[kMaxWaves][kStageWords];
     __shared__ __align__(16) float stage_c[kMaxWaves][kStageFloats];
     __shared__ float red[kMaxWaves][kMaxTok][NMAT][64];
@@ -478,7 +478,10 @@ __global__ __launch_bounds__(512) void gemv_kernel(const uint8_t* __restrict__ p
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
     const int units = FMT == 1 ? K / 256 : K / 128;
-    const int u0 = min(units, wave * units_per_wave), nu = min(units, u0 + units_per_wave) - u0;
+    // K range of this workgroup (blockIdx.z: its part of a K split across
+    // workgroups), then of this wave
+    const int kbase = blockIdx.z * nw * units_per_wave, kend = min(units, kbase + nw * units_per_wave);
+    const int u0 = min(kend, kbase + wave * units_per_wave), nu = min(kend, u0 + units_per_wave) - u0;
     const uint8_t* tiles = pool + (size_t)slot * stride + section + (size_t)rg * units * tile_bytes<FMT, NMAT>();
     const __amdgpu_buffer_rsrc_t src =
         __builtin_amdgcn_make_buffer_rsrc((void*)tiles, 0, units * tile_bytes<FMT, NMAT>(), kBufferDword3);
@@ -556,7 +559,11 @@ __global__ __launch_bounds__(512) void gemv_kernel(const uint8_t* __restrict__ p
 #pragma unroll
                     for (int m = 0; m < NMAT; ++m) v[m] += red[wv][i][m][lane];
                 const int q = c + i;
-                if (NMAT == 2) {
+                if (part) {  // K split across workgroups: this part's sums; the reduce kernel finishes
+#pragma unroll
+                    for (int m = 0; m < NMAT; ++m)
+                        part[(((size_t)blockIdx.z * P + q) * NMAT + m) * rows + rg * 64 + lane] = v[m];
+                } else if (NMAT == 2) {
                     const float h = fast_silu(v[0]) * v[NMAT - 1];
                     const int nblk_out = rows / 32;
                     store_h_record<FMT>(h, rg, lane, hw + (size_t)q * nblk_out * 16, hcs + (size_t)q * nblk_out);
@@ -570,15 +577,62 @@ __global__ __launch_bounds__(512) void gemv_kernel(const uint8_t* __restrict__ p
     }
 }
 
+// Finish a K split across workgroups: sum the parts in order for one pair
+// position q and 64 rows (lane = row), then the GEMV's own epilogue (SwiGLU
+// and the h record, or the y_pairs row).  Positions past the resident pairs
+// have no parts and return.
+template <int FMT, int NMAT>
+__global__ __launch_bounds__(64) void gemv_reduce_kernel(const float* __restrict__ part, int kparts, int P, int rows,
+                                                         const int32_t* __restrict__ n_resident,
+                                                         const int32_t* __restrict__ perm, uint32_t* __restrict__ hw,
+                                                         float2* __restrict__ hcs, float* __restrict__ y_pairs) {
+    const int rg = blockIdx.x, q = blockIdx.y, lane = threadIdx.x;
+    if (q >= *n_resident) return;
+    float v[NMAT];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+        v[m] = 0.0f;
+        for (int kp = 0; kp < kparts; ++kp) v[m] += part[(((size_t)kp * P + q) * NMAT + m) * rows + rg * 64 + lane];
+    }
+    if (NMAT == 2) {
+        const float h = fast_silu(v[0]) * v[NMAT - 1];
+        const int nblk_out = rows / 32;
+        store_h_record<FMT>(h, rg, lane, hw + (size_t)q * nblk_out * 16, hcs + (size_t)q * nblk_out);
+    } else {
+        const int p = perm[q];
+        if (p >= 0 && p < P) y_pairs[(size_t)p * rows + rg * 64 + lane] = v[0];
+    }
+}
+
 // --------------------------------------------------------------- launch
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Workspace: h records [T*k][I/32] (64 B + 8 B).
+// A K split across workgroups keeps kparts x P x NMAT x rows fp32 partial
+// sums; kparts x P is held to this many, which bounds the buffer.
+constexpr int kMaxPartRows = 64;
+
+// Workspace: h records [T*k][I/32] (64 B + 8 B), then the partial sums of a
+// K split across workgroups (gate/up and down use it in turn).
 size_t decode_workspace_bytes(int T, int k, int H, int I) {
-    (void)H;
     const size_t P = (size_t)T * k;
-    return align256(P * (I / 32) * 64) + align256(P * (I / 32) * 8);
+    const size_t part = (size_t)kMaxPartRows * std::max(2 * (size_t)I, (size_t)H) * sizeof(float);
+    return align256(P * (I / 32) * 64) + align256(P * (I / 32) * 8) + align256(part);
+}
+
+// With few row tiles (e.g. one slot: the shared expert) the waves of one
+// workgroup per tile leave most of the chip idle while each streams several
+// units.  Then split K across workgroups as well: one unit per wave, as many
+// waves as the unit count allows, kparts workgroups per tile, finished by
+// the reduce kernel (if the partial sums fit).
+static int split_k_parts(int units, long tiles_total, int P, int* nw, int* upw) {
+    if (*upw <= 1 || tiles_total * *nw >= 2048) return 1;
+    const int nw1 = std::min(kMaxWaves, units);
+    const int kp = (units + nw1 - 1) / nw1;
+    if ((long)kp * P > kMaxPartRows) return 1;
+    *nw = nw1;
+    *upw = 1;
+    return kp;
 }
 
 // Waves per workgroup and K units per wave, given the row tiles times the
@@ -614,19 +668,29 @@ struct GemvLaunch {
     float2* hcs;
     float* y_pairs;
     int units_per_wave;
+    int kparts;
+    float* part;  // partial sums when kparts > 1
 };
 
-// The pipelined kernel when a wave has more than one K unit.
+// The pipelined kernel when a wave has more than one K unit; with a K split
+// across workgroups (grid.z parts) the reduce kernel follows.
 template <int FMT, int NMAT>
 static void launch_gemv(const GemvLaunch& g, dim3 grid, dim3 block, hipStream_t s) {
+    float* part = g.kparts > 1 ? g.part : nullptr;
+    grid.z = g.kparts;
     if (g.units_per_wave > 1)
         hipLaunchKernelGGL((gemv_kernel<FMT, NMAT, true>), grid, block, 0, s, g.pool, g.stride, g.S, g.K, g.rows,
                            g.section, g.x, g.x_dtype, g.rw, g.rcs, g.T, g.k, g.offsets, g.active, g.num_active, g.perm,
-                           g.hw, g.hcs, g.y_pairs, g.units_per_wave);
+                           g.hw, g.hcs, g.y_pairs, g.units_per_wave, part);
     else
         hipLaunchKernelGGL((gemv_kernel<FMT, NMAT, false>), grid, block, 0, s, g.pool, g.stride, g.S, g.K, g.rows,
                            g.section, g.x, g.x_dtype, g.rw, g.rcs, g.T, g.k, g.offsets, g.active, g.num_active, g.perm,
-                           g.hw, g.hcs, g.y_pairs, g.units_per_wave);
+                           g.hw, g.hcs, g.y_pairs, g.units_per_wave, part);
+    if (part) {
+        const int P = g.T * g.k;
+        hipLaunchKernelGGL((gemv_reduce_kernel<FMT, NMAT>), dim3(g.rows / 64, P), dim3(64), 0, s, part, g.kparts, P,
+                           g.rows, g.offsets + g.S, g.perm, g.hw, g.hcs, g.y_pairs);
+    }
 }
 
 hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s) {
@@ -634,6 +698,7 @@ hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s) {
     uint8_t* ws = static_cast<uint8_t*>(a.ws);
     uint32_t* hw = reinterpret_cast<uint32_t*>(ws);
     float2* hcs = reinterpret_cast<float2*>(ws + align256(P * (a.I / 32) * 64));
+    float* part = reinterpret_cast<float*>(ws + align256(P * (a.I / 32) * 64) + align256(P * (a.I / 32) * 8));
 
     const int max_active = (int)std::min<size_t>((size_t)a.S, P);
     if (max_active == 0 || a.T == 0) return hipSuccess;
@@ -643,10 +708,12 @@ hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s) {
         const int units = a.format == 1 ? a.H / 256 : a.H / 128;
         int nw, upw;
         split_k(units, (long)(a.I / 64) * max_active, &nw, &upw);
+        const int kparts = split_k_parts(units, (long)(a.I / 64) * max_active, (int)P, &nw, &upw);
         const dim3 grid(a.I / 64, max_active), block(64 * nw);
         timer_before(kStageGateUp, s);
         const GemvLaunch g{a.pool, a.stride, a.S, a.H, a.I, 0, a.x, a.x_dtype, nullptr, nullptr, a.T, a.k,
-                           a.slot_offsets, a.active_slots, a.num_active, a.perm_pair, hw, hcs, nullptr, upw};
+                           a.slot_offsets, a.active_slots, a.num_active, a.perm_pair, hw, hcs, nullptr, upw,
+                           kparts, part};
         if (a.format == 1)
             launch_gemv<1, 2>(g, grid, block, s);
         else
@@ -660,12 +727,13 @@ hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s) {
         const int units = a.format == 1 ? a.I / 256 : a.I / 128;
         int nw, upw;
         split_k(units, (long)(a.H / 64) * max_active, &nw, &upw);
+        const int kparts = split_k_parts(units, (long)(a.H / 64) * max_active, (int)P, &nw, &upw);
         const dim3 grid(a.H / 64, max_active), block(64 * nw);
         const size_t section = a.format == 1 ? q4k_gateup_bytes(a.H, a.I) : q8_gateup_bytes(a.H, a.I);
         timer_before(kStageDown, s);
         const GemvLaunch g{a.pool, a.stride, a.S, a.I, a.H, section, nullptr, 0, hw, hcs, a.T, a.k,
                            a.slot_offsets, a.active_slots, a.num_active, a.perm_pair, nullptr, nullptr,
-                           static_cast<float*>(a.y_pairs), upw};
+                           static_cast<float*>(a.y_pairs), upw, kparts, part};
         if (a.format == 1)
             launch_gemv<1, 1>(g, grid, block, s);
         else

@@ -344,6 +344,19 @@ def test_dsv3_experts_many_tokens_per_slot(dsv3_blobs):
     assert int(np.diff(got["slot_offsets"]).max()) > 2
 
 
+@pytest.mark.parametrize("fmt", [F.Q4K, F.Q8_0])
+def test_decode_k_split_across_workgroups(fmt):
+    """Two experts with a long K (H 7168): too few row tiles to fill the chip,
+    so K is split across workgroups too (partial sums finished by the reduce
+    kernel), with an uneven last part and a slot holding several chunks of
+    tokens."""
+    wl = W.Workload(f"{'Q4_K' if fmt == F.Q4K else 'Q8_0'} layer H 7168, 2 experts, k 1, T 5", fmt, 7168, 256, 2, 1,
+                    5)
+    say(wl.name)
+    got, want, soe, S = _layer_case(wl, path=Q.MOE_PATH_DECODE)
+    _check_layer(wl, got, want, soe, S)
+
+
 def test_decode_many_tokens_per_slot():
     """48 tokens over 8 experts on the decode path: slots hold up to dozens of
     tokens (chunks of two plus a remainder)."""

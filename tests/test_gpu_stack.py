@@ -23,7 +23,7 @@ pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 WL = W.DSV3_STACK
 N_BLOBS, N_SHARED = 256, 8
 SAMPLE_LAYERS = (0, 29, 57)
-NODES_PER_LAYER = 6  # fused route + batches, 2 expert-FFN kernels, 2 shared-FFN kernels, combine (no copies)
+NODES_PER_LAYER = 8  # route + batches, 2 expert-FFN kernels, 2 shared-FFN kernels + their K-split reductions, combine
 
 
 def blob_of(l, e):
