@@ -468,7 +468,7 @@ def bench_stack(args, threads: int) -> dict:
     hb = host_blobs.numpy()
     with ThreadPoolExecutor(threads) as ex:
         list(ex.map(lambda b: Q.moe_pack_expert(wl.fmt, blobs[b], wl.H, wl.I, out=hb[b, :nb]), range(n_blobs)))
-    del blobs
+    # `blobs` (canonical) stays: the host leg reads the experts the card does not hold from them
     dev_blobs = host_blobs.cuda()
     nbs = Q.moe_expert_blob_bytes(F.Q8_0, wl.H, wl.I_shared)
     sh_host = torch.zeros((n_shared, (nbs + 255) // 256 * 256), dtype=torch.uint8).pin_memory()
@@ -481,8 +481,8 @@ def bench_stack(args, threads: int) -> dict:
                        lambda l, e: (e + 37 * l) % n_blobs, host_blobs, dev_blobs, lambda l: l % n_shared, sh_host)
     del dev_blobs
     torch.cuda.empty_cache()
-    st.set_inputs([torch.from_numpy(W.x_of(wl, l)) for l in range(wl.layers)],
-                  [torch.from_numpy(W.logits_of(wl, l)) for l in range(wl.layers)])
+    xs = [W.x_of(wl, l) for l in range(wl.layers)]
+    st.set_inputs([torch.from_numpy(a) for a in xs], [torch.from_numpy(W.logits_of(wl, l)) for l in range(wl.layers)])
     setup_s = time.time() - t0
     st.capture()
     nodes = st.graph_node_count()
@@ -537,6 +537,31 @@ def bench_stack(args, threads: int) -> dict:
     st.replay()
     torch.cuda.synchronize()
     replay_ms_during = 1e3 * during_s / max(n_during, 1)
+
+    # the host leg: one replay's pairs that the card does not hold, on the
+    # host cores, from the canonical blobs in host memory
+    st.replay()
+    torch.cuda.synchronize()
+    lists = [st.host_lists(l) for l in range(wl.layers)]
+    expert_bytes = 3 * wl.H * wl.I // 256 * 144
+    h0 = time.time()
+    host_pairs = host_experts = 0
+    for l, hl in enumerate(lists):
+        if len(hl["token"]) == 0:
+            continue
+        experts = [None] * wl.E
+        for e in set(hl["expert"].tolist()):
+            experts[e] = blobs[(e + 37 * l) % n_blobs]
+        host_experts += sum(b is not None for b in experts)
+        host_pairs += len(hl["token"])
+        Q.moe_host_leg(wl.fmt, experts, wl.H, wl.I, xs[l], hl["token"], hl["expert"], hl["weight"], threads=threads)
+    host_ms = 1e3 * (time.time() - h0)
+    host_leg = {"pairs_per_replay": host_pairs, "host_experts_per_replay": host_experts,
+                "ms_per_replay": round(host_ms, 2), "threads": threads,
+                "weight_GBs": round(host_experts * expert_bytes / (host_ms * 1e-3) / 1e9, 1),
+                "stack_tokens_per_s_card_then_host": round(wl.T / ((replay_ms + host_ms) * 1e-3), 1),
+                "note": "the host leg reads each listed expert's canonical Q4_K blocks once per replay (grouped by "
+                        "expert); weight_GBs = those bytes over its wall time"}
     out = {
         "workload": wl.name, "layers": wl.layers, "resident": wl.resident, "staging": wl.staging,
         "graph_nodes": nodes, "replays": R, "replay_ms": round(replay_ms, 3),
@@ -552,6 +577,7 @@ def bench_stack(args, threads: int) -> dict:
         "swap_during_replays_GBs": round(swap_bytes / (swap_during_ms * 1e-3) / 1e9, 1),
         "replays_during_swap": n_during, "replay_ms_during_swap": round(replay_ms_during, 3),
         "pcie_gen5_x16_GBs": 64.0,
+        "host_leg": host_leg,
         "setup_s": round(setup_s, 1),
     }
     del st

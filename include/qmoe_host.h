@@ -1,0 +1,73 @@
+/*
+ * qmoe host leg: the expert FFN of the token-expert pairs whose expert is not
+ * on the card, computed on the host CPU from the host list that
+ * moe_build_expert_batches emits.
+ *
+ * An offloading engine keeps some routed experts in HBM and runs the others
+ * on the host tier in the same step, from the experts' stored blocks in host
+ * RAM (bloomery README of 2026-09-24, opening list: each routed layer keeps
+ * some experts on the GPU, the rest run on an AVX2 host; bloomery README
+ * 0.3.1, opening list: experts live on the GPU and in host RAM).  The card's
+ * layer output leaves those pairs out (they contribute 0 there); this leg
+ * computes exactly their share, so
+ *
+ *     y = y_card + y_host
+ *
+ * is the layer output with every expert served.  The host leg is not a
+ * substitute for the card path: it only ever computes pairs the card does
+ * not hold.
+ *
+ * Host-only C ABI (libqmoe_host.so, x86-64 with AVX2, FMA and F16C; no GPU
+ * calls).  Statuses are those of qmoe.h (0 = MOE_OK).
+ */
+#ifndef QMOE_HOST_H
+#define QMOE_HOST_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * y_host[t] = sum over the listed pairs of token t of
+ *             host_weight[p] * FFN_{host_expert[p]}(x[t]),
+ * FFN_e(x) = W_down,e (silu(W_gate,e x) * W_up,e x), silu(z) = z / (1 + e^-z).
+ *
+ * format        0 = Q8_0, 1 = Q4_K (the blocks' stored type, as in qmoe.h).
+ * expert_blob   host, [E] pointers: expert e's canonical blob (W_gate [I,H],
+ *               then W_up [I,H], then W_down [H,I], rows of blocks along the
+ *               input dimension, as moe_pack_expert takes them), or NULL for
+ *               an expert that no listed pair uses.  Read only.
+ * E, H, I       experts, hidden, intermediate.  Q4_K: H, I multiples of
+ *               256; Q8_0: multiples of 32.
+ * x             host, fp32 [T, H].
+ * host_token, host_expert, host_weight
+ *               host, [count]: the pairs (token, expert, weight), as in the
+ *               host list of moe_build_expert_batches.
+ * y_host        host, fp32 [T, H]; overwritten (rows with no pair are 0).
+ * threads       worker threads (<= 0: the OpenMP default).
+ *
+ * Order: pairs are grouped by expert (ascending id; each expert's weights
+ * are read once for all of its tokens), and a token's pairs are summed in
+ * that order, so the result is the same for any thread count.  fp32
+ * arithmetic: each weight row is dequantized to fp32 (Q4_K: d sc_j q -
+ * dmin m_j by one fused multiply-add; Q8_0: d q) and dotted with x, or h,
+ * in fp32 fused multiply-adds; h = silu(g) u in fp32.
+ * Returns MOE_OK, MOE_ERR_INVALID_ARGUMENT (bad sizes, a pair outside [0, T)
+ * x [0, E), a listed expert without a blob, NULL buffers) or
+ * MOE_ERR_UNSUPPORTED (format, shape, or a CPU without AVX2/FMA/F16C);
+ * the error text is in moe_host_last_error().  Nothing is written on error.
+ */
+int moe_host_leg(int format, const uint8_t* const* expert_blob, int E, int H, int I, const float* x, int T,
+                 const int32_t* host_token, const int32_t* host_expert, const float* host_weight, int count,
+                 float* y_host, int threads);
+
+const char* moe_host_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMOE_HOST_H */

@@ -273,6 +273,59 @@ def moe_combine(y_pairs, topk_ids, topk_w, slot_of_expert, y_shared, y, stream=N
                              _stream(stream)))
 
 
+# ------------------------------------------------------------ host leg
+
+HOST_LIB_PATH = os.path.join(_HERE, "libqmoe_host.so")
+_host_lib = None
+
+
+def host_lib() -> ctypes.CDLL:
+    """libqmoe_host.so: the CPU expert FFN for the pairs the card does not
+    hold (include/qmoe_host.h)."""
+    global _host_lib
+    if _host_lib is None:
+        if not os.path.exists(HOST_LIB_PATH):
+            raise ImportError(f"{HOST_LIB_PATH} is not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(HOST_LIB_PATH)
+        vp = ctypes.c_void_p
+        i32 = ctypes.c_int
+        L.moe_host_leg.argtypes = [i32, vp, i32, i32, i32, vp, i32, vp, vp, vp, i32, vp, i32]
+        L.moe_host_leg.restype = i32
+        L.moe_host_last_error.restype = ctypes.c_char_p
+        _host_lib = L
+    return _host_lib
+
+
+def moe_host_leg(fmt: int, expert_blobs, H: int, I: int, x: np.ndarray, host_token, host_expert, host_weight,
+                 threads: int = 0, out: np.ndarray | None = None) -> np.ndarray:
+    """y_host [T, H] fp32 of the listed (token, expert, weight) pairs.
+    expert_blobs: E entries, each a canonical blob (uint8 array) or None."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    T = x.shape[0]
+    tok = np.ascontiguousarray(host_token, dtype=np.int32)
+    exp = np.ascontiguousarray(host_expert, dtype=np.int32)
+    wt = np.ascontiguousarray(host_weight, dtype=np.float32)
+    if not (tok.shape == exp.shape == wt.shape) or tok.ndim != 1:
+        raise ValueError("host_token, host_expert and host_weight must be 1-D of equal length")
+    E = len(expert_blobs)
+    keep = []
+    ptrs = (ctypes.c_void_p * max(E, 1))()
+    for e, b in enumerate(expert_blobs):
+        if b is not None:
+            b = np.ascontiguousarray(b, dtype=np.uint8)
+            keep.append(b)
+            ptrs[e] = b.ctypes.data
+    y = np.empty((T, H), dtype=np.float32) if out is None else out
+    if y.shape != (T, H) or y.dtype != np.float32 or not y.flags.c_contiguous:
+        raise ValueError("out must be a contiguous float32 [T, H] array")
+    st = host_lib().moe_host_leg(fmt, ctypes.cast(ptrs, ctypes.c_void_p), E, H, I, x.ctypes.data, T,
+                                 tok.ctypes.data, exp.ctypes.data, wt.ctypes.data, int(tok.size), y.ctypes.data,
+                                 int(threads))
+    if st != 0:
+        raise QmoeError(st, host_lib().moe_host_last_error().decode())
+    return y
+
+
 def moe_timer_begin(stage: int, capacity: int) -> None:
     _check(lib().moe_timer_begin(stage, capacity))
 

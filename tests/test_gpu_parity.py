@@ -327,9 +327,18 @@ def test_dsv3_partial_residency(dsv3_blobs):
     soe, S = W.slot_map(wl, 0)
     base = W.DSV3_DECODE_T2
     say("decode layer with 96 resident experts")
-    got, want, soe, S = _layer_case(base, blobs=dsv3_blobs, soe=soe, S=S, logits=W.logits_of(wl, 0))
+    logits = W.logits_of(wl, 0)
+    got, want, soe, S = _layer_case(base, blobs=dsv3_blobs, soe=soe, S=S, logits=logits)
     _check_layer(base, got, want, soe, S)
     assert got["host_count"] > 0 and got["num_active"] > 0
+    # the host leg on the card's host list completes the layer: card + host = every expert served
+    x = W.x_of(base)
+    y_host = Q.moe_host_leg(base.fmt, list(dsv3_blobs), base.H, base.I, x, got["host_token"], got["host_expert"],
+                            got["host_weight"], threads=THREADS)
+    full = run_oracle(base, dsv3_blobs, x, logits, np.arange(base.E, dtype=np.int32), W.shared_blob(base))
+    err = rel_max_err(got["y"] + y_host, full["y"])
+    say(f"  card + host leg vs all experts served: {err:.2e}")
+    assert err <= DECODE_TOL
 
 
 def test_dsv3_experts_many_tokens_per_slot(dsv3_blobs):
