@@ -1,7 +1,8 @@
 /*
- * qmoe host leg: the expert FFN of the token-expert pairs whose expert is not
- * on the card, computed on the host CPU from the host list that
- * moe_build_expert_batches emits.
+ * qmoe host library: the host leg, i.e. the expert FFN of the token-expert
+ * pairs whose expert is not on the card, computed on the host CPU from the
+ * host list that moe_build_expert_batches emits; and the adaptive residency
+ * policy that decides which experts the card holds.
  *
  * An offloading engine keeps some routed experts in HBM and runs the others
  * on the host tier in the same step, from the experts' stored blocks in host
@@ -65,6 +66,55 @@ int moe_host_leg(int format, const uint8_t* const* expert_blob, int E, int H, in
                  float* y_host, int threads);
 
 const char* moe_host_last_error(void);
+
+/* ----------------------------------------------------- adaptive residency
+ * The policy that moves the experts a layer calls most onto the card (bloomery
+ * V4.1 README, "Adaptive residency": the engine counts its own routing and
+ * swaps experts between card and host between steps; a prompt call streams
+ * its hottest host experts into the card's pool).  The pages give no
+ * formula; the rule below is the plain reading this library takes.
+ *
+ * Counting is on the device: moe_route_and_batch (route_counts) and
+ * moe_count_routes (qmoe.h) add one per routed pair to the pair's expert,
+ * resident or not.  The caller reads the counters between steps and passes
+ * the increase since its last read as the window.
+ *
+ * Score: an unsigned 64-bit fixed-point moving average with
+ * MOE_RESIDENCY_FRAC_BITS fraction bits, per expert, updated once per step:
+ *     s <- s - (s >> decay_shift) + (window << MOE_RESIDENCY_FRAC_BITS)
+ * (weight 2^-decay_shift on the newest window; decay_shift = 0 keeps only
+ * the window).
+ *
+ * Ranking: expert a ranks before b iff s_a > s_b, or s_a == s_b and a < b.
+ */
+#define MOE_RESIDENCY_FRAC_BITS 16
+
+/* score   host, uint64 [E], updated in place.
+ * window  host, uint32 [E]: pairs routed to each expert since the last update.
+ * Returns MOE_OK or MOE_ERR_INVALID_ARGUMENT (E outside 1..MOE_MAX_EXPERTS,
+ * decay_shift outside 0..63, NULL pointers; nothing written). */
+int moe_residency_update_scores(uint64_t* score, const uint32_t* window, int E, int decay_shift);
+
+/* Swap plan of one layer.  The host experts (slot_of_expert[e] < 0) in
+ * ranking order are paired with the resident experts in reverse ranking
+ * order; pair i is swapped (incoming[i] comes onto the card in the place of
+ * outgoing[i]) while i < max_swaps and s(incoming) > s(outgoing) + margin.
+ * The plan therefore raises the card's total score by as much as any set of
+ * at most max_swaps swaps can, and never swaps on a tie.
+ *
+ * score           host, uint64 [E].
+ * slot_of_expert  host, int32 [E] (only its sign is read).
+ * incoming, outgoing
+ *                 host, int32 [max_swaps] each (may be NULL if max_swaps = 0).
+ * n_swaps         host, out: the number of pairs written.
+ * A prompt call's plan takes the prompt's counts << MOE_RESIDENCY_FRAC_BITS
+ * as the score, max_swaps = the resident count and margin 0: the card then
+ * holds the prompt's most-used experts.  Slots are the caller's: an
+ * incoming expert may take its outgoing partner's slot once no running work
+ * reads it, or a free slot.
+ * Returns MOE_OK or MOE_ERR_INVALID_ARGUMENT (nothing written). */
+int moe_residency_plan(const uint64_t* score, int E, const int32_t* slot_of_expert, int max_swaps, uint64_t margin,
+                       int32_t* incoming, int32_t* outgoing, int* n_swaps);
 
 #ifdef __cplusplus
 }

@@ -281,7 +281,7 @@ _host_lib = None
 
 def host_lib() -> ctypes.CDLL:
     """libqmoe_host.so: the CPU expert FFN for the pairs the card does not
-    hold (include/qmoe_host.h)."""
+    hold, and the adaptive residency policy (include/qmoe_host.h)."""
     global _host_lib
     if _host_lib is None:
         if not os.path.exists(HOST_LIB_PATH):
@@ -292,6 +292,10 @@ def host_lib() -> ctypes.CDLL:
         L.moe_host_leg.argtypes = [i32, vp, i32, i32, i32, vp, i32, vp, vp, vp, i32, vp, i32]
         L.moe_host_leg.restype = i32
         L.moe_host_last_error.restype = ctypes.c_char_p
+        L.moe_residency_update_scores.argtypes = [vp, vp, i32, i32]
+        L.moe_residency_update_scores.restype = i32
+        L.moe_residency_plan.argtypes = [vp, i32, vp, i32, ctypes.c_uint64, vp, vp, vp]
+        L.moe_residency_plan.restype = i32
         _host_lib = L
     return _host_lib
 
@@ -324,6 +328,40 @@ def moe_host_leg(fmt: int, expert_blobs, H: int, I: int, x: np.ndarray, host_tok
     if st != 0:
         raise QmoeError(st, host_lib().moe_host_last_error().decode())
     return y
+
+
+RESIDENCY_FRAC_BITS = 16  # MOE_RESIDENCY_FRAC_BITS
+
+
+def moe_residency_update_scores(score: np.ndarray, window, decay_shift: int) -> np.ndarray:
+    """score (uint64 [E], updated in place) <- score - (score >> decay_shift)
+    + (window << 16); window: uint32 [E] pairs routed since the last update."""
+    if score.dtype != np.uint64 or score.ndim != 1 or not score.flags.c_contiguous:
+        raise ValueError("score must be a contiguous uint64 [E] array")
+    win = np.ascontiguousarray(window, dtype=np.uint32)
+    if win.shape != score.shape:
+        raise ValueError("window must have the shape of score")
+    st = host_lib().moe_residency_update_scores(score.ctypes.data, win.ctypes.data, int(score.size), int(decay_shift))
+    if st != 0:
+        raise QmoeError(st, host_lib().moe_host_last_error().decode())
+    return score
+
+
+def moe_residency_plan(score, slot_of_expert, max_swaps: int, margin: int = 0) -> tuple[list, list]:
+    """(incoming, outgoing) experts of one layer's swap plan."""
+    sc = np.ascontiguousarray(score, dtype=np.uint64)
+    soe = np.ascontiguousarray(slot_of_expert, dtype=np.int32)
+    if sc.ndim != 1 or soe.shape != sc.shape:
+        raise ValueError("score and slot_of_expert must be 1-D of equal length")
+    m = max(int(max_swaps), 0)
+    inc = np.zeros(max(m, 1), dtype=np.int32)
+    out = np.zeros(max(m, 1), dtype=np.int32)
+    n = ctypes.c_int(0)
+    st = host_lib().moe_residency_plan(sc.ctypes.data, int(sc.size), soe.ctypes.data, int(max_swaps), int(margin),
+                                       inc.ctypes.data, out.ctypes.data, ctypes.byref(n))
+    if st != 0:
+        raise QmoeError(st, host_lib().moe_host_last_error().decode())
+    return inc[:n.value].tolist(), out[:n.value].tolist()
 
 
 def moe_timer_begin(stage: int, capacity: int) -> None:

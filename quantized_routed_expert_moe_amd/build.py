@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 SO = os.path.join(HERE, "libqmoe.so")
-HOST_SO = os.path.join(HERE, "libqmoe_host.so")  # the host leg (CPU only, g++)
+HOST_SO = os.path.join(HERE, "libqmoe_host.so")  # host leg + residency policy (CPU only, g++)
 
 SOURCES = ["abi.cpp", "route.hip", "batches.hip", "route_batches.hip", "ffn_decode.hip", "ffn_prefill.hip",
            "combine.hip"]
@@ -53,11 +53,13 @@ def build(jobs: int = 8) -> str:
 
 
 def build_host() -> str:
-    """The host leg: plain g++ (the AVX2 kernels carry their own target
-    attributes and run only after a CPU feature check), OpenMP."""
+    """The host library (the host leg and the residency policy): plain g++
+    (the AVX2 kernels carry their own target attributes and run only after a
+    CPU feature check), OpenMP."""
     tmp = HOST_SO + ".tmp"
     cmd = [os.environ.get("CXX", "g++"), "-O3", "-std=c++17", "-fPIC", "-shared", "-fopenmp", "-Wall",
-           "-I" + os.path.join(ROOT, "include"), os.path.join(HERE, "host", "host_leg.cpp"), "-o", tmp]
+           "-I" + os.path.join(ROOT, "include"), os.path.join(HERE, "host", "host_leg.cpp"),
+           os.path.join(HERE, "host", "residency.cpp"), "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"host leg build failed:\n{r.stderr}")

@@ -215,6 +215,14 @@ void run(int format, const uint8_t* const* expert_blob, int H, int I, const floa
 
 }  // namespace
 
+namespace qmoe_host {
+// The library's one error text, also set by the residency policy.
+__attribute__((visibility("hidden"))) int set_error(int status, const char* msg) {
+    g_error = msg;
+    return status;
+}
+}  // namespace qmoe_host
+
 extern "C" {
 
 const char* moe_host_last_error(void) { return g_error.c_str(); }
