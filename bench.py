@@ -54,6 +54,8 @@ def parse():
                     help="timed steps of the T=4096 prefill layer reported beside the decode line (0 = skip)")
     ap.add_argument("--dsv3-steps", type=int, default=400,
                     help="timed steps of the DeepSeek-V3-shaped decode layer at T=2 and T=4 (0 = skip)")
+    ap.add_argument("--residency-steps", type=int, default=96,
+                    help="decode steps per arm of the adaptive residency run on the stack (0: skip it)")
     ap.add_argument("--stack-replays", type=int, default=10,
                     help="timed replays of the 58-layer partial-residency stack (0 = skip)")
     ap.add_argument("--profile-copy", action="store_true",
@@ -479,8 +481,9 @@ def bench_stack(args, threads: int) -> dict:
     spec = LayerSpec(wl.fmt, wl.H, wl.I, wl.E, wl.k, wl.score, wl.renormalize, wl.scale, wl.I_shared)
     st = ResidentStack(spec, wl.layers, wl.T, wl.resident, wl.staging, ranked,
                        lambda l, e: (e + 37 * l) % n_blobs, host_blobs, dev_blobs, lambda l: l % n_shared, sh_host)
-    del dev_blobs
-    torch.cuda.empty_cache()
+    if args.residency_steps <= 0:
+        del dev_blobs
+        torch.cuda.empty_cache()
     xs = [W.x_of(wl, l) for l in range(wl.layers)]
     st.set_inputs([torch.from_numpy(a) for a in xs], [torch.from_numpy(W.logits_of(wl, l)) for l in range(wl.layers)])
     setup_s = time.time() - t0
@@ -562,6 +565,12 @@ def bench_stack(args, threads: int) -> dict:
                 "stack_tokens_per_s_card_then_host": round(wl.T / ((replay_ms + host_ms) * 1e-3), 1),
                 "note": "the host leg reads each listed expert's canonical Q4_K blocks once per replay (grouped by "
                         "expert); weight_GBs = those bytes over its wall time"}
+    residency = None
+    if args.residency_steps > 0:
+        residency = bench_residency(st, wl, blobs, xs, dev_blobs, args.residency_steps, threads,
+                                    lambda l, e: (e + 37 * l) % n_blobs)
+        del dev_blobs
+        torch.cuda.empty_cache()
     out = {
         "workload": wl.name, "layers": wl.layers, "resident": wl.resident, "staging": wl.staging,
         "graph_nodes": nodes, "replays": R, "replay_ms": round(replay_ms, 3),
@@ -578,10 +587,105 @@ def bench_stack(args, threads: int) -> dict:
         "replays_during_swap": n_during, "replay_ms_during_swap": round(replay_ms_during, 3),
         "pcie_gen5_x16_GBs": 64.0,
         "host_leg": host_leg,
+        "adaptive_residency": residency,
         "setup_s": round(setup_s, 1),
     }
     del st
     torch.cuda.empty_cache()
+    return out
+
+
+def bench_residency(st, wl, blobs, xs, dev_blobs, steps: int, threads: int, blob_of) -> dict:
+    """The adaptive residency policy on the stack, measured the way the pages
+    measure it: decode steps from a start where each layer holds its lowest
+    expert ids, with the policy off, with the swap rule, and with the swap
+    rule after a prompt call has streamed its most-used experts onto the card.
+    Each step: one graph replay (card), then the host leg for every pair the
+    card does not hold (host cores), then the policy (counters -> scores ->
+    an 8-swap plan per layer), whose copies run on a side stream beside the
+    next steps and are committed between steps once they have landed."""
+    import numpy as np
+    import torch
+
+    import fixtures as F
+    import quantized_routed_expert_moe_amd as Q
+    from quantized_routed_expert_moe_amd.stack import AdaptiveResidency
+
+    L, E, T, k = wl.layers, wl.E, wl.T, wl.k
+    lowest = [np.arange(E) for _ in range(L)]
+    prompt_rows = 512
+    margin, decay = 1 << Q.RESIDENCY_FRAC_BITS, 4
+    step_logits = [np.stack([F.logits_zipf(wl.seed + 1000 + i, l, T, E, wl.zipf_s, perm_seed=wl.seed)
+                             for l in range(L)]) for i in range(steps)]
+
+    def host_leg() -> tuple[int, float]:
+        pairs = 0
+        h0 = time.time()
+        for l in range(L):
+            hl = st.host_lists(l)
+            if len(hl["token"]) == 0:
+                continue
+            experts = [None] * E
+            for e in set(hl["expert"].tolist()):
+                experts[e] = blobs[blob_of(l, e)]
+            pairs += len(hl["token"])
+            Q.moe_host_leg(wl.fmt, experts, wl.H, wl.I, xs[l], hl["token"], hl["expert"], hl["weight"],
+                           threads=threads)
+        return pairs, time.time() - h0
+
+    def arm(policy: bool, prompt: bool) -> dict:
+        st.reset(lowest, dev_blobs)
+        pol = AdaptiveResidency(st, decay_shift=decay, margin=margin) if policy else None
+        res = {}
+        if prompt:
+            plg = [F.logits_zipf(wl.seed + 500, l, prompt_rows, E, wl.zipf_s, perm_seed=wl.seed) for l in range(L)]
+            plans = pol.prompt_plans(st.prompt_counts(plg))
+            n = sum(len(p[0]) for p in plans)
+            secs = st.stream_in(plans)
+            nb = n * Q.moe_expert_blob_bytes(wl.fmt, wl.H, wl.I)
+            res.update(prompt_rows=prompt_rows, streamed_experts=n, stream_s=round(secs, 3),
+                       stream_GBs=round(nb / max(secs, 1e-9) / 1e9, 1))
+        share, card_s, host_s = [], 0.0, 0.0
+        swaps = rounds = 0
+        for i in range(steps):
+            if st.swap_in_flight:
+                st.swap_commit(block=False)
+            st.set_logits(step_logits[i])
+            c0 = time.time()
+            st.replay()
+            st.replay_done.synchronize()
+            card_s += time.time() - c0
+            pairs, hs = host_leg()
+            host_s += hs
+            share.append(1.0 - pairs / (L * T * k))
+            if pol is not None:
+                pol.observe()
+                if not st.swap_in_flight:
+                    plans = pol.plans(wl.staging)
+                    n = sum(len(p[0]) for p in plans)
+                    if n:
+                        st.swap_begin(plans=plans)
+                        swaps += n
+                        rounds += 1
+        if st.swap_in_flight:
+            st.swap_commit(block=True)
+        torch.cuda.synchronize()
+        q = max(1, min(16, steps // 4))
+        res.update(card_served_first=round(float(np.mean(share[:q])), 4),
+                   card_served_last=round(float(np.mean(share[-q:])), 4),
+                   card_served_all=round(float(np.mean(share)), 4),
+                   replay_ms=round(1e3 * card_s / steps, 3), host_leg_ms=round(1e3 * host_s / steps, 2),
+                   tokens_per_s=round(T * steps / (card_s + host_s), 2), swap_rounds=rounds, experts_swapped=swaps)
+        return res
+
+    out = {"steps": steps, "window": f"first/last {max(1, min(16, steps // 4))} steps",
+           "start": "each layer's lowest 96 expert ids on the card",
+           "policy": {"decay_shift": decay, "margin": margin, "swaps_per_layer_per_round": wl.staging,
+                      "prompt_plan": "prompt counts, as many swaps as raise the card's count, margin 0"},
+           "routing": "the stack workload's Zipf(1.1) ranking per layer; fresh Gumbel noise every step",
+           "off": arm(False, False), "swap_rule": arm(True, False), "swap_rule_and_prompt_streaming": arm(True, True)}
+    out["note"] = ("tokens_per_s = T x steps / (card replay + host leg), run one after the other; swap copies "
+                   "overlap both")
     return out
 
 

@@ -144,12 +144,31 @@ moe_status moe_build_expert_batches(const int32_t* topk_ids, const float* topk_w
  * weights through memory; otherwise it launches the two calls' kernels.
  * The workspace is that of moe_build_expert_batches
  * (moe_batches_workspace_size).
+ * route_counts  device, uint32 [E], or NULL: if given, each of the T*k
+ *               pairs also adds one to route_counts[its expert], as
+ *               moe_count_routes does (same totals; the adds are atomic, so
+ *               only the totals are defined, which is all the counters hold).
  */
 moe_status moe_route_and_batch(const float* logits, int T, int E, int k, int score, int renormalize, float scale,
                                int32_t* topk_ids, float* topk_w, const int32_t* slot_of_expert, int S,
                                int32_t* slot_offsets, int32_t* active_slots, int32_t* num_active, int32_t* perm_pair,
                                int32_t* host_token, int32_t* host_expert, float* host_weight, int32_t* host_count,
-                               void* ws, size_t ws_bytes, void* stream);
+                               uint32_t* route_counts, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------- routing counts
+ * counts[e] += the number of pairs (t, j) with topk_ids[t*k + j] == e, for
+ * every e in [0, E) (ids outside that range are skipped).  The counters of
+ * the adaptive residency policy: the engine counts its own routing, resident
+ * experts and host experts alike, and moves the experts it calls most onto
+ * the card (bloomery V4.1 README, "Adaptive residency"; the policy itself is
+ * in qmoe_host.h).  uint32 counters wrap modulo 2^32; the caller reads
+ * differences between steps.
+ * topk_ids  device, int32 [T, k].   counts  device, uint32 [E], accumulated.
+ * T in 0..(2^24 / k), E in 1..MOE_MAX_EXPERTS, k in 1..min(E, MOE_MAX_TOPK).
+ * Enqueued on `stream`; capturable.  Returns MOE_OK, MOE_ERR_INVALID_ARGUMENT
+ * (nothing enqueued) or MOE_ERR_HIP.
+ */
+moe_status moe_count_routes(const int32_t* topk_ids, int T, int k, int E, uint32_t* counts, void* stream);
 
 /* ------------------------------------------------------------ expert blobs
  * Each HBM slot holds one expert as a packed blob: the canonical stored

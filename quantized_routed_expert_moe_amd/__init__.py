@@ -53,7 +53,8 @@ def lib() -> ctypes.CDLL:
         L.moe_build_expert_batches.argtypes = [vp, vp, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                                vp]
         L.moe_route_and_batch.argtypes = [vp, i32, i32, i32, i32, i32, f32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
-                                          vp, vp, vp, sz, vp]
+                                          vp, vp, vp, vp, sz, vp]
+        L.moe_count_routes.argtypes = [vp, i32, i32, i32, vp, vp]
         L.moe_expert_blob_bytes.argtypes = [i32, i32, i32]
         L.moe_expert_blob_bytes.restype = sz
         L.moe_pack_expert.argtypes = [i32, vp, vp, i32, i32]
@@ -67,7 +68,8 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, i32, i32, vp, i32, vp]
         L.moe_timer_begin.argtypes = [i32, i32]
         L.moe_timer_end.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
-        for name in ("moe_route_topk", "moe_build_expert_batches", "moe_pack_expert", "moe_unpack_expert",
+        for name in ("moe_route_topk", "moe_build_expert_batches", "moe_route_and_batch", "moe_count_routes",
+                     "moe_pack_expert", "moe_unpack_expert",
                      "moe_validate_slot_map", "moe_expert_ffn_q4k", "moe_expert_ffn_q8_0", "moe_combine",
                      "moe_timer_begin", "moe_timer_end"):
             getattr(L, name).restype = i32
@@ -134,7 +136,7 @@ def _dev_or_mapped(t, dtypes=None, name="tensor") -> int:
             dptr = ctypes.c_void_p()
             rc = hip.hipHostGetDevicePointer(ctypes.byref(dptr), ctypes.c_void_p(base), 0)
             if rc != 0 or not dptr.value:
-                raise QmoeError(f"{name}: pinned host memory has no device address (hip error {rc})")
+                raise QmoeError(MOE_ERR_HIP, f"{name}: pinned host memory has no device address (hip error {rc})")
             _MAPPED[base] = dptr.value
         return _MAPPED[base] + (t.data_ptr() - base)
     return _dev(t, dtypes, name)
@@ -160,6 +162,12 @@ def _f32():
 def _fb():
     import torch
     return (torch.float32, torch.bfloat16)
+
+
+def _u32():
+    """Counters: uint32 in the ABI; an int32 tensor holds the same bits."""
+    import torch
+    return tuple(t for t in (torch.int32, getattr(torch, "uint32", None)) if t is not None)
 
 
 # ------------------------------------------------------------------ calls
@@ -190,7 +198,9 @@ def moe_build_expert_batches(topk_ids, topk_w, E: int, slot_of_expert, S: int, s
 
 def moe_route_and_batch(logits, k: int, score: int, renormalize: bool, scale: float, topk_ids, topk_w, E: int,
                         slot_of_expert, S: int, slot_offsets, active_slots, num_active, perm_pair, host_token,
-                        host_expert, host_weight, host_count, ws=None, stream=None):
+                        host_expert, host_weight, host_count, ws=None, stream=None, route_counts=None):
+    """route_counts: optional device int32/uint32 [E] routing counters (each
+    pair adds one to its expert)."""
     T, E_ = logits.shape
     if E_ != E:
         raise ValueError(f"logits have {E_} experts, E = {E}")
@@ -202,7 +212,17 @@ def moe_route_and_batch(logits, k: int, score: int, renormalize: bool, scale: fl
         _dev(active_slots, _i32(), "active_slots"), _dev(num_active, _i32(), "num_active"),
         _dev(perm_pair, _i32(), "perm_pair"), _dev_or_mapped(host_token, _i32(), "host_token"),
         _dev_or_mapped(host_expert, _i32(), "host_expert"), _dev_or_mapped(host_weight, _f32(), "host_weight"),
-        _dev_or_mapped(host_count, _i32(), "host_count"), _dev(ws, None, "ws"), ws_bytes, _stream(stream)))
+        _dev_or_mapped(host_count, _i32(), "host_count"), _dev(route_counts, _u32(), "route_counts"),
+        _dev(ws, None, "ws"), ws_bytes, _stream(stream)))
+
+
+def moe_count_routes(topk_ids, E: int, counts, stream=None):
+    """counts[e] += pairs of topk_ids [T, k] routed to e (device, int32/uint32 [E])."""
+    T, k = topk_ids.shape
+    if counts is None:
+        raise ValueError("counts must be a device tensor")
+    _check(lib().moe_count_routes(_dev(topk_ids, _i32(), "topk_ids"), T, k, E, _dev(counts, _u32(), "counts"),
+                                  _stream(stream)))
 
 
 def moe_expert_blob_bytes(fmt: int, H: int, I: int) -> int:

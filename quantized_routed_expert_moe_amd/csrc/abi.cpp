@@ -356,7 +356,7 @@ moe_status moe_route_and_batch(const float* logits, int T, int E, int k, int sco
                                int32_t* topk_ids, float* topk_w, const int32_t* slot_of_expert, int S,
                                int32_t* slot_offsets, int32_t* active_slots, int32_t* num_active, int32_t* perm_pair,
                                int32_t* host_token, int32_t* host_expert, float* host_weight, int32_t* host_count,
-                               void* ws, size_t ws_bytes, void* stream) {
+                               uint32_t* route_counts, void* ws, size_t ws_bytes, void* stream) {
     moe_status st = check_route_shape(T, E, k);
     if (st != MOE_OK) return st;
     if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID)
@@ -374,9 +374,18 @@ moe_status moe_route_and_batch(const float* logits, int T, int E, int k, int sco
     if (need > 0 && !ws) return fail(MOE_ERR_INVALID_ARGUMENT, "batches workspace pointer is NULL");
     hipError_t e = qmoe::launch_route_batches(logits, T, E, k, score, renormalize, scale, topk_ids, topk_w,
                                               slot_of_expert, S, slot_offsets, active_slots, num_active, perm_pair,
-                                              host_token, host_expert, host_weight, host_count, ws,
+                                              host_token, host_expert, host_weight, host_count, route_counts, ws,
                                               (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "route and batch launch");
+    return MOE_OK;
+}
+
+moe_status moe_count_routes(const int32_t* topk_ids, int T, int k, int E, uint32_t* counts, void* stream) {
+    moe_status st = check_route_shape(T, E, k);
+    if (st != MOE_OK) return st;
+    if (!counts || (T > 0 && !topk_ids)) return fail(MOE_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+    hipError_t e = qmoe::launch_count_routes(topk_ids, T * k, E, counts, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "count launch");
     return MOE_OK;
 }
 

@@ -94,8 +94,9 @@ hipError_t launch_batches(const int32_t* ids, const float* w, int T, int k, int 
 hipError_t launch_route_batches(const float* logits, int T, int E, int k, int score, int renormalize, float scale,
                                 int32_t* ids, float* w, const int32_t* slot_of_expert, int S, int32_t* slot_offsets,
                                 int32_t* active_slots, int32_t* num_active, int32_t* perm_pair, int32_t* host_token,
-                                int32_t* host_expert, float* host_weight, int32_t* host_count, void* ws,
-                                hipStream_t s);
+                                int32_t* host_expert, float* host_weight, int32_t* host_count,
+                                uint32_t* route_counts, void* ws, hipStream_t s);
+hipError_t launch_count_routes(const int32_t* ids, int P, int E, uint32_t* counts, hipStream_t s);
 
 struct FfnArgs {
     int format;  // 0 Q8_0, 1 Q4_K

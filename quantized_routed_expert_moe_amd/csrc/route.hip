@@ -15,9 +15,11 @@
 // Weights are formed from the k picks in fp32 (softmax renormalised over the
 // picks equals the full softmax renormalised; the full denominator is only
 // needed when renormalisation is off).
+#include <algorithm>
 #include <climits>
 
 #include "device_common.h"
+#include "qmoe.h"
 #include "qmoe_internal.h"
 #include "route_common.h"
 
@@ -145,18 +147,42 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int score
     else if (E <= 256)
         hipLaunchKernelGGL(route_rank_kernel<256>, dim3(T), dim3(256), 0, s, logits, T, E, k, score, renormalize, scale,
                            ids, w);
-    else if (E <= 64)
-        hipLaunchKernelGGL(route_topk_kernel<1>, grid, block, 0, s, logits, T, E, k, score, renormalize, scale, ids, w);
-    else if (E <= 128)
-        hipLaunchKernelGGL(route_topk_kernel<2>, grid, block, 0, s, logits, T, E, k, score, renormalize, scale, ids, w);
-    else if (E <= 256)
-        hipLaunchKernelGGL(route_topk_kernel<4>, grid, block, 0, s, logits, T, E, k, score, renormalize, scale, ids, w);
     else if (E <= 512)
         hipLaunchKernelGGL(route_topk_kernel<8>, grid, block, 0, s, logits, T, E, k, score, renormalize, scale, ids, w);
     else
         hipLaunchKernelGGL(route_topk_kernel<16>, grid, block, 0, s, logits, T, E, k, score, renormalize, scale, ids,
                            w);
     timer_after(kStageRoute, s);
+    return hipGetLastError();
+}
+
+// Routing counts for the adaptive residency policy: counts[e] += the number
+// of pairs routed to e.  Each workgroup builds a histogram of its pairs in
+// LDS and adds its non-zero bins to the counters (device-scope atomics, so
+// any number of workgroups and calls accumulate).  Ids outside [0, E) are
+// skipped.
+constexpr int kCountPairsPerBlock = 2048;
+
+__global__ __launch_bounds__(256) void count_routes_kernel(const int32_t* __restrict__ ids, int P, int E,
+                                                           uint32_t* __restrict__ counts) {
+    __shared__ uint32_t hist[MOE_MAX_EXPERTS];
+    for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+    __syncthreads();
+    for (int p = blockIdx.x * 256 + threadIdx.x; p < P; p += gridDim.x * 256) {
+        const int id = ids[p];
+        if ((unsigned)id < (unsigned)E) atomicAdd(&hist[id], 1u);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) {
+        const uint32_t c = hist[e];
+        if (c) __hip_atomic_fetch_add(counts + e, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+hipError_t launch_count_routes(const int32_t* ids, int P, int E, uint32_t* counts, hipStream_t s) {
+    if (P == 0) return hipSuccess;
+    const int blocks = std::min((P + kCountPairsPerBlock - 1) / kCountPairsPerBlock, 1024);
+    hipLaunchKernelGGL(count_routes_kernel, dim3(blocks), dim3(256), 0, s, ids, P, E, counts);
     return hipGetLastError();
 }
 

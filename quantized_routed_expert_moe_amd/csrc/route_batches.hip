@@ -8,7 +8,9 @@
 // the first wave groups the pairs with the same ballot-match batching as the
 // single-wave batching kernel (batch_wave).
 // Outputs are those of moe_route_topk followed by moe_build_expert_batches,
-// bit for bit.  Larger steps launch those two kernels.
+// bit for bit.  Larger steps launch those two kernels.  With route_counts
+// the first wave also adds each pair to its expert's routing counter (one
+// device-scope atomic per pair), for the adaptive residency policy.
 #include "batches_common.h"
 #include "device_common.h"
 #include "qmoe_internal.h"
@@ -24,7 +26,7 @@ __global__ __launch_bounds__(256 * kFusedMaxRows) void route_batches_kernel(
     int32_t* __restrict__ ids, float* __restrict__ w, const int32_t* __restrict__ soe, int S, int nbits,
     int32_t* __restrict__ offsets, int32_t* __restrict__ active, int32_t* __restrict__ num_active,
     int32_t* __restrict__ perm, int32_t* __restrict__ host_token, int32_t* __restrict__ host_expert,
-    float* __restrict__ host_weight, int32_t* __restrict__ host_count) {
+    float* __restrict__ host_weight, int32_t* __restrict__ host_count, uint32_t* __restrict__ route_counts) {
     __shared__ __align__(16) RouteShared<EMAX> sh[kFusedMaxRows];
     __shared__ int32_t s_ids[64];
     __shared__ float s_w[64];
@@ -43,6 +45,8 @@ __global__ __launch_bounds__(256 * kFusedMaxRows) void route_batches_kernel(
         const int id = valid ? s_ids[lane] : 0;
         const float wt = valid ? s_w[lane] : 0.0f;
         const int sl = (valid && id >= 0 && id < E) ? s_soe[id] : -1;
+        if (route_counts && valid && id >= 0 && id < E)
+            __hip_atomic_fetch_add(route_counts + id, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         batch_wave(lane, P, k, S, nbits, id, wt, sl, cnt, offsets, active, num_active, perm, host_token, host_expert,
                    host_weight, host_count);
     }
@@ -51,12 +55,16 @@ __global__ __launch_bounds__(256 * kFusedMaxRows) void route_batches_kernel(
 hipError_t launch_route_batches(const float* logits, int T, int E, int k, int score, int renormalize, float scale,
                                 int32_t* ids, float* w, const int32_t* soe, int S, int32_t* offsets,
                                 int32_t* active, int32_t* num_active, int32_t* perm, int32_t* host_token,
-                                int32_t* host_expert, float* host_weight, int32_t* host_count, void* ws,
-                                hipStream_t s) {
+                                int32_t* host_expert, float* host_weight, int32_t* host_count,
+                                uint32_t* route_counts, void* ws, hipStream_t s) {
     const long P = (long)T * k;
     if (T < 1 || T > kFusedMaxRows || P > 64 || E > 256) {
         hipError_t e = launch_route_topk(logits, T, E, k, score, renormalize, scale, ids, w, s);
         if (e != hipSuccess) return e;
+        if (route_counts) {
+            e = launch_count_routes(ids, (int)P, E, route_counts, s);
+            if (e != hipSuccess) return e;
+        }
         return launch_batches(ids, w, T, k, E, soe, S, offsets, active, num_active, perm, host_token, host_expert,
                               host_weight, host_count, ws, s);
     }
@@ -66,11 +74,11 @@ hipError_t launch_route_batches(const float* logits, int T, int E, int k, int sc
     if (E <= 128)
         hipLaunchKernelGGL(route_batches_kernel<128>, dim3(1), dim3(256 * T), 0, s, logits, T, E, k, score, renormalize,
                            scale, ids, w, soe, S, nbits, offsets, active, num_active, perm, host_token, host_expert,
-                           host_weight, host_count);
+                           host_weight, host_count, route_counts);
     else
         hipLaunchKernelGGL(route_batches_kernel<256>, dim3(1), dim3(256 * T), 0, s, logits, T, E, k, score, renormalize,
                            scale, ids, w, soe, S, nbits, offsets, active, num_active, perm, host_token, host_expert,
-                           host_weight, host_count);
+                           host_weight, host_count, route_counts);
     timer_after(kStageRouteBatches, s);
     return hipGetLastError();
 }

@@ -48,9 +48,13 @@ class MoELayer:
     def __init__(self, spec: LayerSpec, T_max: int, S: int, slot_pool: torch.Tensor, stride: int,
                  slot_of_expert: torch.Tensor, shared_pool: torch.Tensor | None = None,
                  path: int = MOE_PATH_AUTO, y_dtype=torch.float32, pair_dtype=torch.float32, device="cuda",
-                 host_list_pinned: bool = False):
+                 host_list_pinned: bool = False, route_counts: torch.Tensor | None = None):
+        """route_counts: optional device int32 [E] routing counters; every
+        forward adds each routed pair to its expert's counter (the adaptive
+        residency policy reads them)."""
         self.spec, self.T_max, self.S, self.path = spec, T_max, S, path
         self.slot_pool, self.stride, self.slot_of_expert = slot_pool, stride, slot_of_expert
+        self.route_counts = route_counts
         self.shared_pool = shared_pool
         k, H, E = spec.k, spec.H, spec.E
         P = T_max * k
@@ -115,7 +119,7 @@ class MoELayer:
         moe_route_and_batch(logits, spec.k, spec.score, spec.renormalize, spec.scale, self.ids, self.w, spec.E,
                             self.slot_of_expert, self.S, self.slot_offsets, self.active_slots, self.num_active,
                             self.perm_pair, self.host_token, self.host_expert, self.host_weight, self.host_count,
-                            self.batch_ws, stream)
+                            self.batch_ws, stream, route_counts=self.route_counts)
         ffn = moe_expert_ffn_q4k if spec.fmt == MOE_FMT_Q4K else moe_expert_ffn_q8_0
         ffn(pool, self.stride, self.S, spec.H, spec.I, x, spec.k, self.slot_offsets, self.active_slots,
             self.num_active, self.perm_pair, self.y_pairs, self.path, self.ws, stream)

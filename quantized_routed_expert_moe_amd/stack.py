@@ -20,19 +20,29 @@ Orchestration only; every computation is a libqmoe call:
     the new slot maps after the replay in flight; the next replay waits for
     that.  swap() does both for one round.
 
-Swap rule (the pages only say experts are swapped between steps): the
-incoming experts are the next `n` non-resident ones in the layer's frequency
-ranking after a cursor that starts at the first non-resident rank and wraps;
-the outgoing ones are the `n` lowest-ranked resident experts.  Incoming
-experts take the free slots (at first the staging slots, then the slots the
-previous round freed).
+Which experts a round swaps is either given (`plans`, one (incoming,
+outgoing) pair of lists per layer) or, without plans, the rotation rule that
+measures swap throughput: the incoming experts are the next `n` non-resident
+ones in the layer's frequency ranking after a cursor that starts at the first
+non-resident rank and wraps, the outgoing ones the `n` lowest-ranked resident
+experts.  Incoming experts take the free slots (at first the staging slots,
+then the slots the previous round freed).
+
+Adaptive residency (bloomery V4.1 README, "Adaptive residency": the engine
+counts its own routing and swaps experts between card and host between
+steps; a prompt call streams its hottest host experts onto the card): every
+layer's routing launch also adds its pairs to that layer's row of
+`counts` (device, [layers, E]); AdaptiveResidency reads them between steps
+and plans the rounds with the host library's policy, and stream_in() seats a
+prompt's most-used experts before decode starts.
 """
 from __future__ import annotations
 
 import numpy as np
 import torch
 
-from . import MOE_FMT_Q4K, MOE_PATH_DECODE, moe_validate_slot_map
+from . import (MOE_FMT_Q4K, MOE_PATH_DECODE, RESIDENCY_FRAC_BITS, moe_count_routes, moe_residency_plan,
+               moe_residency_update_scores, moe_route_topk, moe_validate_slot_map)
 from .layer import LayerSpec, MoELayer
 
 
@@ -58,7 +68,11 @@ class ResidentStack:
         self.free = []            # free slots per layer
         self.cursor = []          # swap cursor into ranked[l]
         self.pools, self.dev_maps, self.layers = [], [], []
-        self.x, self.logits = [], []
+        self.x = []
+        # routing counters (uint32 bits in int32) and the step's gate logits, one row per layer
+        self.counts = torch.zeros((n_layers, E), dtype=torch.int32, device=dev)
+        self.logits_all = torch.zeros((n_layers, T, E), dtype=torch.float32, device=dev)
+        self.logits = [self.logits_all[l] for l in range(n_layers)]
         src = dev_blobs if dev_blobs is not None else host_blobs
         for l in range(n_layers):
             soe = np.full(E, -1, dtype=np.int32)
@@ -85,9 +99,9 @@ class ResidentStack:
         torch.cuda.synchronize()
         for l in range(n_layers):
             self.layers.append(MoELayer(spec, T, self.S, self.pools[l], self.stride, self.dev_maps[l],
-                                        self.shared_pools[l], MOE_PATH_DECODE, host_list_pinned=True))
+                                        self.shared_pools[l], MOE_PATH_DECODE, host_list_pinned=True,
+                                        route_counts=self.counts[l]))
             self.x.append(torch.zeros((T, spec.H), dtype=torch.float32, device=dev))
-            self.logits.append(torch.zeros((T, E), dtype=torch.float32, device=dev))
         self.pin_maps = [torch.zeros(E, dtype=torch.int32).pin_memory() for _ in range(n_layers)]
         self.graph = None
         self.side = torch.cuda.Stream()
@@ -105,6 +119,31 @@ class ResidentStack:
         for l in range(self.L):
             self.x[l].copy_(xs[l])
             self.logits[l].copy_(logits[l])
+
+    def set_logits(self, logits: np.ndarray) -> None:
+        """The next step's gate logits, float32 [layers, T, E], in one copy
+        (ordered before the next replay on the current stream)."""
+        self.logits_all.copy_(torch.from_numpy(np.ascontiguousarray(logits, dtype=np.float32)))
+
+    def read_counts(self) -> np.ndarray:
+        """The routing counters, uint32 [layers, E], once the current stream
+        has passed every replay so far."""
+        return self.counts.cpu().numpy().view(np.uint32)
+
+    def prompt_counts(self, logits) -> np.ndarray:
+        """A prompt's routing counts per layer, uint32 [layers, E]: each
+        layer's prompt logits (float32 [P, E]) routed on the device and
+        counted there (moe_route_topk, moe_count_routes)."""
+        spec = self.spec
+        counts = torch.zeros((self.L, spec.E), dtype=torch.int32, device="cuda")
+        for l in range(self.L):
+            lg = torch.from_numpy(np.ascontiguousarray(logits[l], dtype=np.float32)).cuda()
+            P = lg.shape[0]
+            ids = torch.empty((P, spec.k), dtype=torch.int32, device="cuda")
+            w = torch.empty((P, spec.k), dtype=torch.float32, device="cuda")
+            moe_route_topk(lg, spec.k, spec.score, spec.renormalize, spec.scale, ids, w)
+            moe_count_routes(ids, spec.E, counts[l])
+        return counts.cpu().numpy().view(np.uint32)
 
     def _step_body(self) -> None:
         for l in range(self.L):
@@ -176,20 +215,27 @@ class ResidentStack:
         outgoing = resident[:n]
         return incoming, outgoing
 
-    def swap_begin(self, n: int = 8) -> dict:
-        """Start one swap round on every layer: plan it and enqueue the copies
-        of the incoming experts into free slots on the side stream.  Returns at
+    def swap_begin(self, n: int = 8, plans: list | None = None) -> dict:
+        """Start one swap round on every layer: take its plan (plans[l] =
+        (incoming, outgoing), at most as many as the layer's free slots) or
+        make one with the rotation rule, and enqueue the copies of the
+        incoming experts into free slots on the side stream.  Returns at
         once; replays may go on with the current maps meanwhile (free slots are
         not referenced by them).  The side stream runs the rounds in order, so
         these copies also follow the previous round's map upload, i.e. the
         last replay that could still use a slot freed by that round."""
         assert not self.swap_in_flight, "commit the previous swap round first"
+        given = plans
         plans = []
         self.swap_start.record(self.side)
         with torch.cuda.stream(self.side):
             for l in range(self.L):
-                inc, out = self.plan_swap(l, n)
-                assert len(self.free[l]) >= len(inc)
+                inc, out = self.plan_swap(l, n) if given is None else (list(given[l][0]), list(given[l][1]))
+                if len(inc) != len(out) or len(self.free[l]) < len(inc):
+                    raise ValueError(f"layer {l}: {len(inc)} incoming, {len(out)} outgoing, "
+                                     f"{len(self.free[l])} free slots")
+                if any(self.maps[l][e] >= 0 for e in inc) or any(self.maps[l][e] < 0 for e in out):
+                    raise ValueError(f"layer {l}: plan swaps in a resident expert or out a host one")
                 slots = [self.free[l].pop(0) for _ in inc]
                 for e, s in zip(inc, slots):
                     self.pools[l][s].copy_(self.host_blobs[self.blob_of(l, e)], non_blocking=True)
@@ -237,5 +283,83 @@ class ResidentStack:
         self.swap_commit(block=True)
         return plan
 
+    def stream_in(self, plans: list) -> float:
+        """Apply plans[l] = (incoming, outgoing) in place, now: each incoming
+        expert's blob is copied from pinned host memory into its outgoing
+        partner's slot.  For the prompt call's streaming, before decode
+        starts: waits for all work on the device first (no replay may still
+        read the slots).  Returns the seconds the copies took."""
+        import time
+        assert not self.swap_in_flight, "commit the swap round in flight first"
+        torch.cuda.synchronize()
+        t0 = time.time()
+        for l in range(self.L):
+            inc, out = plans[l]
+            soe = self.maps[l]
+            if len(inc) != len(out) or any(soe[e] >= 0 for e in inc) or any(soe[e] < 0 for e in out):
+                raise ValueError(f"layer {l}: bad plan")
+            for e_in, e_out in zip(inc, out):
+                slot = int(soe[e_out])
+                self.pools[l][slot].copy_(self.host_blobs[self.blob_of(l, int(e_in))], non_blocking=True)
+                soe[e_in], soe[e_out] = slot, -1
+            moe_validate_slot_map(soe, self.S)
+            self.dev_maps[l].copy_(torch.from_numpy(soe.copy()))
+        torch.cuda.synchronize()
+        return time.time() - t0
+
+    def reset(self, ranked: list, src: torch.Tensor | None = None) -> None:
+        """Start over with ranked[l][:n_resident] in slots 0.. of layer l (the
+        rest on the host, the staging slots free), blobs copied from src
+        (device rows as host_blobs; default host_blobs).  No swap round may be
+        in flight."""
+        assert not self.swap_in_flight, "commit the swap round in flight first"
+        torch.cuda.synchronize()
+        src = self.host_blobs if src is None else src
+        E = self.spec.E
+        self.ranked = [np.asarray(r, dtype=np.int64) for r in ranked]
+        for l in range(self.L):
+            soe = np.full(E, -1, dtype=np.int32)
+            soe[self.ranked[l][:self.nres]] = np.arange(self.nres, dtype=np.int32)
+            self.maps[l][:] = soe
+            self.free[l] = list(range(self.nres, self.S))
+            self.cursor[l] = self.nres
+            for s in range(self.nres):
+                self.pools[l][s].copy_(src[self.blob_of(l, int(self.ranked[l][s]))], non_blocking=True)
+            self.dev_maps[l].copy_(torch.from_numpy(soe))
+        self.pending_maps = False
+        torch.cuda.synchronize()
+
     def current_maps(self) -> list:
         return [m.copy() for m in self.maps]
+
+
+class AdaptiveResidency:
+    """The adaptive residency policy driving a ResidentStack.  Between decode
+    steps, observe() reads the stack's routing counters and updates each
+    layer's running score with the pairs routed since the last read
+    (moe_residency_update_scores); plans() gives each layer's swap plan
+    (moe_residency_plan) for the next swap round.  prompt_plans() turns a
+    prompt's routing counts into the scores and the plans of the prompt
+    call's streaming (as many swaps as raise the card's count, margin 0)."""
+
+    def __init__(self, stack: ResidentStack, decay_shift: int = 4, margin: int = 1 << RESIDENCY_FRAC_BITS):
+        self.st, self.decay_shift, self.margin = stack, decay_shift, margin
+        self.score = np.zeros((stack.L, stack.spec.E), dtype=np.uint64)
+        self.prev = stack.read_counts().copy()
+
+    def observe(self) -> np.ndarray:
+        """Windows (uint32 [layers, E]): pairs routed since the last read; the
+        scores are updated with them."""
+        now = self.st.read_counts().copy()
+        win = now - self.prev  # uint32: modulo 2^32, as the counters wrap
+        self.prev = now
+        for l in range(self.st.L):
+            moe_residency_update_scores(self.score[l], win[l], self.decay_shift)
+        return win
+
+    def plans(self, max_swaps: int) -> list:
+        return [moe_residency_plan(self.score[l], self.st.maps[l], max_swaps, self.margin) for l in range(self.st.L)]
+
+    def prompt_plans(self, prompt_counts: np.ndarray) -> list:
+        self.score = np.ascontiguousarray(prompt_counts, dtype=np.uint64) << np.uint64(RESIDENCY_FRAC_BITS)
+        return [moe_residency_plan(self.score[l], self.st.maps[l], self.st.nres, 0) for l in range(self.st.L)]

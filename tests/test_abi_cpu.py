@@ -54,7 +54,7 @@ def test_route_rejects_null():
 
 def _route_batch(T=4, E=8, k=2, score=0, scale=1.0, S=8, ws_bytes=0, logits=FAKE):
     return _call("moe_route_and_batch", logits, T, E, k, score, 1, ctypes.c_float(scale), FAKE, FAKE, FAKE, S, FAKE,
-                 FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws_bytes, None)
+                 FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,want,needle", [
@@ -68,6 +68,17 @@ def _route_batch(T=4, E=8, k=2, score=0, scale=1.0, S=8, ws_bytes=0, logits=FAKE
 def test_route_and_batch_rejects(kw, want, needle):
     st, msg = _route_batch(**kw)
     assert st == want and needle in msg, msg
+
+
+@pytest.mark.parametrize("T,k,E,ids,counts,needle", [
+    (4, 2, 0, FAKE, FAKE, "E = 0"),
+    (4, 9, 8, FAKE, FAKE, "k = 9"),
+    (4, 2, 8, FAKE, None, "NULL"),
+    (4, 2, 8, None, FAKE, "NULL"),
+])
+def test_count_routes_rejects(T, k, E, ids, counts, needle):
+    st, msg = _call("moe_count_routes", ids, T, k, E, counts, None)
+    assert st == Q.MOE_ERR_INVALID_ARGUMENT and needle in msg, msg
 
 
 def test_batches_rejects_bad_slot_count():

@@ -11,6 +11,7 @@ import torch
 
 import fixtures as F
 import oracle as O
+from oracle import residency as OR
 import quantized_routed_expert_moe_amd as Q
 from fixtures import workloads as W
 from tests.gpu_util import THREADS, device_layer, rel_max_err, run_device, run_oracle, say
@@ -143,7 +144,7 @@ def test_batches_match_oracle(wl, smap):
 
 # ------------------------------------------------------- route and batch
 
-def _route_batch_device(logits, k, score, renorm, scale, soe, S):
+def _route_batch_device(logits, k, score, renorm, scale, soe, S, route_counts=None):
     T, E = logits.shape
     P = T * k
     i32 = dict(dtype=torch.int32, device="cuda")
@@ -159,7 +160,7 @@ def _route_batch_device(logits, k, score, renorm, scale, soe, S):
     Q.moe_route_and_batch(torch.from_numpy(np.ascontiguousarray(logits)).cuda(), k, score, renorm, scale, ids, w, E,
                           torch.from_numpy(soe).cuda(), S, out["slot_offsets"], out["active_slots"],
                           out["num_active"], out["perm_pair"], out["host_token"], out["host_expert"],
-                          out["host_weight"], out["host_count"], ws)
+                          out["host_weight"], out["host_count"], ws, route_counts=route_counts)
     torch.cuda.synchronize()
     o = {key: v.cpu().numpy() for key, v in out.items()}
     na, nres, hc = int(o["num_active"][0]), int(o["slot_offsets"][S]), int(o["host_count"][0])
@@ -202,6 +203,42 @@ def test_route_and_batch_matches_oracle_and_two_calls(T, E, k, score, renorm, sc
     two = _batches_device(ids2, w2, E, soe, S)
     for key in ("slot_offsets", "active_slots", "perm_pair", "host_token", "host_expert", "host_weight"):
         assert np.array_equal(got[key], two[key]), key
+
+
+@pytest.mark.parametrize("T,E,k,score", [
+    (2, 128, 8, 0),    # fused launch
+    (4, 256, 8, 1),    # fused launch, two-level rank
+    (5, 128, 8, 0),    # two launches: T > 4
+    (3, 300, 8, 1),    # two launches: E > 256
+])
+def test_route_and_batch_counts_routing(T, E, k, score):
+    """The routing counters: two calls add twice the oracle's per-expert pair
+    counts to whatever the counters held (uint32, wrapping)."""
+    say(f"route and batch counters T={T} E={E} k={k}")
+    lg = F.logits_normal(31, T, T, E)
+    soe, S = _slot_maps(E, np.random.default_rng(E))["half"]
+    start = np.random.default_rng(T).integers(0, 1 << 32, size=E, dtype=np.uint64).astype(np.uint32)
+    start[:3] = 0xFFFFFFFF  # wraps if routed to
+    counts = torch.from_numpy(start.view(np.int32).copy()).cuda()
+    for _ in range(2):
+        _route_batch_device(lg, k, score, True, 2.5 if score else 1.0, soe, S, route_counts=counts)
+    oids, _ = O.route(lg, k, score, True, 2.5 if score else 1.0)
+    want = (start.astype(np.uint64) + 2 * np.array(OR.route_counts(oids, E), dtype=np.uint64)) % (1 << 32)
+    assert np.array_equal(counts.cpu().numpy().view(np.uint32), want.astype(np.uint32))
+
+
+@pytest.mark.parametrize("T,E,k", [(4096, 128, 8), (700, 1000, 6), (1, 8, 2)])
+def test_count_routes_matches_oracle(T, E, k):
+    say(f"count routes T={T} E={E} k={k}")
+    lg = F.logits_normal(41, T, T, E)
+    oids, _ = O.route(lg, k, 0, True, 1.0)
+    ids = oids.copy()
+    ids[0, 0] = -1      # ids outside [0, E) are skipped
+    ids[-1, -1] = E
+    counts = torch.zeros(E, dtype=torch.int32, device="cuda")
+    Q.moe_count_routes(torch.from_numpy(ids).cuda(), E, counts)
+    torch.cuda.synchronize()
+    assert counts.cpu().numpy().tolist() == OR.route_counts(ids, E)
 
 
 def test_route_and_batch_ties():

@@ -5,7 +5,9 @@ with 8-expert swaps per layer between replays.
 Every layer's expert ids and host list match the oracle bit for bit; the
 outputs of sampled layers are within the decode tolerance of the oracle run
 with that replay's slot map; a graph replay equals eager execution bit for
-bit; the graph's node count is pinned.
+bit; the graph's node count is pinned.  Under the adaptive residency policy
+the routing counters, scores, prompt streaming and swap plans equal the
+oracle's exactly.
 """
 import numpy as np
 import pytest
@@ -15,7 +17,8 @@ import fixtures as F
 import oracle as O
 import quantized_routed_expert_moe_amd as Q
 from fixtures import workloads as W
-from quantized_routed_expert_moe_amd.stack import ResidentStack
+from oracle import residency as OR
+from quantized_routed_expert_moe_amd.stack import AdaptiveResidency, ResidentStack
 from tests.gpu_util import THREADS, pack_pool, rel_max_err, say, spec_of
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
@@ -71,11 +74,12 @@ def stack():
     return dict(st=st, blobs=blobs, shared=shared, xs=xs, lgs=lgs)
 
 
-def _check_replay(ctx, check_layers):
+def _check_replay(ctx, check_layers, lgs=None):
     st = ctx["st"]
+    lgs = ctx["lgs"] if lgs is None else lgs
     maps = st.current_maps()
     for l in range(WL.layers):
-        ids, w = O.route(ctx["lgs"][l], WL.k, WL.score, WL.renormalize, WL.scale)
+        ids, w = O.route(lgs[l], WL.k, WL.score, WL.renormalize, WL.scale)
         got_ids = st.layers[l].ids.cpu().numpy()
         assert np.array_equal(got_ids, ids), l
         ob = O.batches(ids, w, WL.E, maps[l], st.S)
@@ -83,10 +87,10 @@ def _check_replay(ctx, check_layers):
         assert np.array_equal(hl["token"], ob["host_token"]) and np.array_equal(hl["expert"], ob["host_expert"]), l
         assert np.abs(hl["weight"] - ob["host_weight"]).max(initial=0.0) <= 1e-6 * WL.scale, l
     for l in check_layers:
-        needed = set(ctx["lgs"][l].argsort(axis=1)[:, ::-1][:, :WL.k].ravel().tolist())
+        needed = set(lgs[l].argsort(axis=1)[:, ::-1][:, :WL.k].ravel().tolist())
         experts = [ctx["blobs"][blob_of(l, e)] if e in needed else None for e in range(WL.E)]
         O.set_threads(THREADS)
-        want = O.moe_layer(WL.fmt, experts, WL.H, WL.I, ctx["xs"][l].astype(np.float64), ctx["lgs"][l], WL.k,
+        want = O.moe_layer(WL.fmt, experts, WL.H, WL.I, ctx["xs"][l].astype(np.float64), lgs[l], WL.k,
                            WL.score, WL.renormalize, WL.scale, maps[l], ctx["shared"][shared_of(l)], F.Q8_0,
                            WL.I_shared)
         err = rel_max_err(st.layers[l].y.cpu().numpy(), want["y"])
@@ -137,3 +141,67 @@ def test_stack_swap_rounds(stack):
     changed = sum(int((b >= 0).sum() != 0 and not np.array_equal(b >= 0, a >= 0))
                   for a, b in zip(before, st.current_maps()))
     assert changed == WL.layers
+
+
+def test_stack_adaptive_residency(stack):
+    """Routing drifts to another expert ranking: a prompt's counts stream its
+    most-used experts onto the card, then three decode steps run under the
+    policy (counters -> scores -> an 8-swap plan per layer per step)."""
+    st = stack["st"]
+    if st.graph is None:
+        st.capture()
+    margin, decay = 1 << OR.FRAC_BITS, 4
+    pol = AdaptiveResidency(st, decay_shift=decay, margin=margin)
+    drift = WL.seed + 5  # another expert ranking than the one the card was filled by
+    say("prompt: 64 rows per layer, routed and counted on the device")
+    plg = np.stack([F.logits_zipf(drift, l, 64, WL.E, WL.zipf_s, perm_seed=drift) for l in range(WL.layers)])
+    pc = st.prompt_counts(plg)
+    for l in range(WL.layers):
+        oids, _ = O.route(plg[l], WL.k, WL.score, WL.renormalize, WL.scale)
+        assert pc[l].tolist() == OR.route_counts(oids, WL.E), l
+    before = st.current_maps()
+    plans = pol.prompt_plans(pc)
+    for l in range(WL.layers):
+        (inc, out), _ = OR.prompt_plan(pc[l].tolist(), before[l].tolist())
+        assert (list(plans[l][0]), list(plans[l][1])) == (inc, out), l
+    n = sum(len(p[0]) for p in plans)
+    secs = st.stream_in(plans)
+    say(f"  streamed {n} experts in {secs:.2f} s")
+    maps = st.current_maps()
+    for l in range(WL.layers):
+        Q.moe_validate_slot_map(maps[l], st.S)
+        for e_in, e_out in zip(*plans[l]):
+            assert maps[l][e_in] == before[l][e_out] and maps[l][e_out] == -1
+        card = maps[l] >= 0
+        assert int(card.sum()) == WL.resident
+        assert pc[l][card].min() >= pc[l][~card].max(), l  # the prompt's most-used experts are on the card
+    score = [[int(c) << OR.FRAC_BITS for c in pc[l]] for l in range(WL.layers)]
+    for step in range(3):
+        say(f"decode step {step}")
+        lg = np.stack([F.logits_zipf(drift + 100 + step, l, WL.T, WL.E, WL.zipf_s, perm_seed=drift)
+                       for l in range(WL.layers)])
+        st.set_logits(lg)
+        st.replay()
+        torch.cuda.synchronize()
+        _check_replay(stack, (11,) if step == 2 else (), lgs=lg)
+        win = pol.observe()
+        maps = st.current_maps()
+        for l in range(WL.layers):
+            oids, _ = O.route(lg[l], WL.k, WL.score, WL.renormalize, WL.scale)
+            assert win[l].tolist() == OR.route_counts(oids, WL.E), l
+            score[l] = OR.update_scores(score[l], win[l].tolist(), decay)
+            assert pol.score[l].tolist() == score[l], l
+        plans = pol.plans(WL.staging)
+        for l in range(WL.layers):
+            want = OR.plan(score[l], maps[l].tolist(), WL.staging, margin)
+            assert (list(plans[l][0]), list(plans[l][1])) == want, l
+        say(f"  swaps planned: {sum(len(p[0]) for p in plans)}")
+        st.swap_begin(plans=plans)
+        st.swap_commit(block=True)
+        after = st.current_maps()
+        for l in range(WL.layers):
+            assert all(after[l][e] >= 0 for e in plans[l][0]) and all(after[l][e] < 0 for e in plans[l][1])
+            assert int((after[l] >= 0).sum()) == WL.resident
+    st.replay()
+    torch.cuda.synchronize()
+    _check_replay(stack, (40,), lgs=lg)
