@@ -77,9 +77,9 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-def header_functions() -> list[str]:
-    """Names of the functions include/qmoe.h declares."""
-    text = open(HEADER_PATH).read()
+def header_functions(header: str | None = None) -> list[str]:
+    """Names of the functions a header declares (default include/qmoe.h)."""
+    text = open(header or HEADER_PATH).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 

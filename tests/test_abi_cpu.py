@@ -18,6 +18,15 @@ def test_library_exports_every_header_function():
     assert not missing, missing
 
 
+def test_host_library_exports_every_host_header_function():
+    import os
+    names = Q.header_functions(os.path.join(os.path.dirname(Q.HEADER_PATH), "qmoe_host.h"))
+    assert {"moe_host_leg", "moe_residency_plan", "moe_residency_update_scores"} <= set(names)
+    L = Q.host_lib()
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+
+
 def test_status_names():
     assert Q._status_name(0) == "MOE_OK"
     assert Q._status_name(3) == "MOE_ERR_WORKSPACE_TOO_SMALL"
