@@ -312,11 +312,60 @@ void fx_encode_q4k(const float* x, int64_t n, uint8_t* out) {
     }
 }
 
+/* n floats (n % 32 == 0) -> n/32 MXFP4 blocks of 17 bytes: an E8M0 scale
+ * byte X, then element i < 16 in the low nibble of byte 1 + i and element
+ * 16 + i in its high nibble, as FP4 (E2M1) codes.  The scale is the
+ * smallest power of two s = 2^(X - 127) with 6 s >= max |x| (no element
+ * saturates); each x / s goes to the nearest E2M1 magnitude (0, 0.5, 1,
+ * 1.5, 2, 3, 4, 6), ties to the even code, with x's sign.  A zero block
+ * stores X = 0 and zero codes. */
+void fx_encode_mxfp4(const float* x, int64_t n, uint8_t* out) {
+    static const float mag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+    for (int64_t b = 0; b < n / 32; ++b) {
+        const float* v = x + b * 32;
+        uint8_t* o = out + b * 17;
+        float amax = 0.0f;
+        for (int i = 0; i < 32; ++i) {
+            float a = fabsf(v[i]);
+            if (a > amax) amax = a;
+        }
+        memset(o, 0, 17);
+        if (amax == 0.0f) continue;
+        int k;
+        frexpf(amax / 6.0f, &k);  /* amax / 6 in [2^(k-1), 2^k) */
+        while (k > -127 && 6.0f * ldexpf(1.0f, k - 1) >= amax) --k;
+        while (6.0f * ldexpf(1.0f, k) < amax) ++k;
+        if (k < -127) k = -127;
+        if (k > 127) k = 127;
+        o[0] = (uint8_t)(k + 127);
+        const float s = ldexpf(1.0f, k);
+        for (int i = 0; i < 32; ++i) {
+            float a = fabsf(v[i]) / s;
+            int best = 0;
+            for (int c = 1; c < 8; ++c) {
+                float dc = fabsf(a - mag[c]), db = fabsf(a - mag[best]);
+                if (dc < db || (dc == db && (c & 1) == 0)) best = c;
+            }
+            int code = best | ((v[i] < 0.0f && best) ? 8 : 0);
+            if (i < 16) o[1 + i] |= (uint8_t)code;
+            else o[1 + i - 16] |= (uint8_t)(code << 4);
+        }
+    }
+}
+
 /* ------------------------------------------------------------- experts */
 
-enum { FX_Q8_0 = 0, FX_Q4K = 1 };
+enum { FX_Q8_0 = 0, FX_Q4K = 1, FX_MXFP4 = 2 };
 
-static int64_t row_bytes(int fmt, int64_t cols) { return fmt == FX_Q8_0 ? cols / 32 * 34 : cols / 256 * 144; }
+static int64_t row_bytes(int fmt, int64_t cols) {
+    return fmt == FX_Q8_0 ? cols / 32 * 34 : fmt == FX_MXFP4 ? cols / 32 * 17 : cols / 256 * 144;
+}
+
+static void encode_row(int fmt, const float* x, int64_t n, uint8_t* out) {
+    if (fmt == FX_Q8_0) fx_encode_q8_0(x, n, out);
+    else if (fmt == FX_MXFP4) fx_encode_mxfp4(x, n, out);
+    else fx_encode_q4k(x, n, out);
+}
 
 int64_t fx_matrix_bytes(int fmt, int64_t rows, int64_t cols) { return rows * row_bytes(fmt, cols); }
 
@@ -337,8 +386,7 @@ static void gen_matrix(int fmt, uint32_t seed, uint32_t layer, uint32_t expert, 
 #pragma omp for schedule(static)
         for (int64_t r = 0; r < rows; ++r) {
             normal_row(seed, 0x57000000u | matrix, (uint32_t)r, expert, layer, 0.0f, std, buf, cols);
-            if (fmt == FX_Q8_0) fx_encode_q8_0(buf, cols, out + r * rb);
-            else fx_encode_q4k(buf, cols, out + r * rb);
+            encode_row(fmt, buf, cols, out + r * rb);
         }
         free(buf);
     }
@@ -373,8 +421,7 @@ void fx_gen_experts(int fmt, uint32_t seed, uint32_t layer, const int32_t* exper
             int64_t cols = matrix == 2 ? I : H;
             uint8_t* dst = out + i * eb + (matrix == 2 ? 2 * gb + row * rbI : matrix * gb + row * rbH);
             normal_row(seed, 0x57000000u | matrix, (uint32_t)row, (uint32_t)experts[i], layer, 0.0f, std, buf, cols);
-            if (fmt == FX_Q8_0) fx_encode_q8_0(buf, cols, dst);
-            else fx_encode_q4k(buf, cols, dst);
+            encode_row(fmt, buf, cols, dst);
         }
         free(buf);
     }

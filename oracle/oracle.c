@@ -29,7 +29,9 @@ enum {
     D_GATE_UP_SWAPPED = 9,     /* reads W_up as the gate matrix and W_gate as up */
     D_NO_RENORM = 10,          /* softmax weights not renormalised over the k */
     D_Q4K_NIBBLE_SWAP = 11,    /* even sub-blocks read the high nibbles */
-    D_IGNORE_RESIDENCY = 12    /* combine adds non-resident pairs too */
+    D_IGNORE_RESIDENCY = 12,   /* combine adds non-resident pairs too */
+    D_MXFP4_INTERLEAVED = 13,  /* MXFP4 elements read as consecutive nibble pairs */
+    D_MXFP4_BIAS_128 = 14      /* MXFP4 scale exponent bias 128 instead of 127 */
 };
 
 void oracle_set_threads(int n) {
@@ -120,12 +122,43 @@ void oracle_dequant_q4k(const uint8_t* blocks, int64_t n, double* out) {
     }
 }
 
+/* One FP4 (E2M1) code, OCP Microscaling Formats (MX) v1.0, element type
+ * FP4: bit 3 sign, bits 2-1 exponent (bias 1), bit 0 mantissa; exponent 0
+ * is subnormal (0 or 0.5), otherwise (1 + m/2) 2^(e - 1). */
+static double e2m1_value(int code) {
+    int sign = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    double v = e == 0 ? 0.5 * (double)m : ldexp(1.0 + 0.5 * (double)m, e - 1);
+    return sign ? -v : v;
+}
+
+/* MXFP4 block (17 bytes): one E8M0 scale byte X (2^(X - 127); X = 255 is
+ * NaN), then 16 bytes of FP4 codes: element i < 16 in the low nibble of byte
+ * 1 + i, element 16 + i in its high nibble.  w_i = 2^(X - 127) * fp4(q_i).
+ * Parity pinned by hand-built golden blocks (every code, extreme scales)
+ * and the encoder round trip. */
+void oracle_dequant_mxfp4(const uint8_t* blocks, int64_t n, double* out) {
+    for (int64_t b = 0; b < n / 32; ++b) {
+        const uint8_t* blk = blocks + b * 17;
+        int x = blk[0];
+        double scale = x == 255 ? NAN : ldexp(1.0, x - (g_defect == D_MXFP4_BIAS_128 ? 128 : 127));
+        for (int i = 0; i < 32; ++i) {
+            int code;
+            if (g_defect == D_MXFP4_INTERLEAVED) code = (blk[1 + i / 2] >> (4 * (i % 2))) & 15;
+            else code = i < 16 ? (blk[1 + i] & 15) : (blk[1 + i - 16] >> 4);
+            out[b * 32 + i] = scale * e2m1_value(code);
+        }
+    }
+}
+
 static void dequant_row(int fmt, const uint8_t* row, int64_t n, double* out) {
     if (fmt == ORACLE_Q8_0) oracle_dequant_q8_0(row, n, out);
+    else if (fmt == ORACLE_MXFP4) oracle_dequant_mxfp4(row, n, out);
     else oracle_dequant_q4k(row, n, out);
 }
 
-static int64_t row_bytes(int fmt, int64_t cols) { return fmt == ORACLE_Q8_0 ? cols / 32 * 34 : cols / 256 * 144; }
+static int64_t row_bytes(int fmt, int64_t cols) {
+    return fmt == ORACLE_Q8_0 ? cols / 32 * 34 : fmt == ORACLE_MXFP4 ? cols / 32 * 17 : cols / 256 * 144;
+}
 
 /* ------------------------------------------------------------- routing */
 

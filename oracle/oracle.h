@@ -10,6 +10,10 @@
  *   dequantize  Q8_0:  w = d*q                      (32 weights per block)
  *               Q4_K:  w = d*sc_j*q - dmin*m_j      (256 per super-block, 8
  *                                                    sub-blocks j of 32)
+ *               MXFP4: w = 2^(X-127) * fp4(q)        (32 per block; OCP MX v1.0
+ *                                                    E8M0 scale, E2M1 elements;
+ *                                                    card expert type: README
+ *                                                    0.3.1 "Quant types" row)
  *   route       order experts by (logit desc, id asc); the first k are the
  *               ids.  softmax: p = softmax over all E, w_j = p_j / sum p_sel
  *               (renormalised) or p_j; sigmoid: s = 1/(1+e^-l),
@@ -39,12 +43,13 @@
 extern "C" {
 #endif
 
-enum { ORACLE_Q8_0 = 0, ORACLE_Q4K = 1 };
+enum { ORACLE_Q8_0 = 0, ORACLE_Q4K = 1, ORACLE_MXFP4 = 2 };
 enum { ORACLE_SOFTMAX = 0, ORACLE_SIGMOID = 1 };
 
 /* Dequantize n weights (n a multiple of the block size) from stored blocks. */
 void oracle_dequant_q8_0(const uint8_t* blocks, int64_t n, double* out);
 void oracle_dequant_q4k(const uint8_t* blocks, int64_t n, double* out);
+void oracle_dequant_mxfp4(const uint8_t* blocks, int64_t n, double* out);
 
 /* Top-k routing of T rows of E logits.  Returns 0, or -1 on bad sizes. */
 int oracle_route(const float* logits, int T, int E, int k, int score, int renormalize, double scale,

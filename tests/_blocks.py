@@ -4,7 +4,8 @@ These builders let a test pick the exact quantized fields (so the dense
 weights are known by construction) and lay them out in the stored byte
 order: Q8_0 = fp16 d + 32 int8; Q4_K = fp16 d, fp16 dmin, 12 packed 6-bit
 (sc, m) bytes, 128 quant bytes (byte 32c+l: element l of sub-block 2c low
-nibble, of 2c+1 high nibble).  They contain no dequantization.
+nibble, of 2c+1 high nibble); MXFP4 = E8M0 scale byte + 16 bytes of FP4
+codes.  The dense values are written from the chosen fields.
 """
 from __future__ import annotations
 
@@ -63,9 +64,33 @@ def random_q4k_matrix(rng: np.random.Generator, rows: int, cols: int, d_bits: in
     return np.frombuffer(b"".join(parts), dtype=np.uint8).copy(), dense
 
 
+# FP4 (E2M1) magnitudes by code & 7 (OCP Microscaling Formats v1.0); bit 3 = sign.
+E2M1_MAGNITUDES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def mxfp4_block(x_bits: int, codes) -> bytes:
+    """E8M0 scale byte, then element i < 16 in the low nibble of byte 1+i, 16+i in the high."""
+    codes = [int(c) for c in codes]
+    return bytes([x_bits] + [codes[i] | (codes[16 + i] << 4) for i in range(16)])
+
+
+def random_mxfp4_matrix(rng: np.random.Generator, rows: int, cols: int):
+    """An MXFP4 matrix with random codes and per-block scales 2^-9..2^-4; returns (bytes, exact dense values)."""
+    dense = np.empty((rows, cols), dtype=np.float64)
+    parts = []
+    for r in range(rows):
+        for b in range(cols // 32):
+            x_bits = int(rng.integers(118, 124))
+            codes = rng.integers(0, 16, size=32)
+            parts.append(mxfp4_block(x_bits, codes))
+            mag = np.array([E2M1_MAGNITUDES[c & 7] for c in codes])
+            dense[r, b * 32:(b + 1) * 32] = np.where(codes & 8, -mag, mag) * 2.0 ** (x_bits - 127)
+    return np.frombuffer(b"".join(parts), dtype=np.uint8).copy(), dense
+
+
 def random_expert(rng: np.random.Generator, fmt: int, H: int, I: int):
     """Canonical blob Wg|Wu|Wd with exactly known dense matrices."""
-    make = random_q8_0_matrix if fmt == 0 else random_q4k_matrix
+    make = {0: random_q8_0_matrix, 1: random_q4k_matrix, 2: random_mxfp4_matrix}[fmt]
     bg, g = make(rng, I, H)
     bu, u = make(rng, I, H)
     bd, dn = make(rng, H, I)

@@ -7,6 +7,7 @@ computed here with exact rational arithmetic from the block formula:
     Q8_0:  w = d * q                       (fp16 d, 32 signed bytes)
     Q4_K:  w = d * sc_j * q - dmin * m_j   (fp16 d and dmin, eight 6-bit
                                             (sc, m) pairs, 4-bit q)
+    MXFP4: w = 2^(X - 127) * fp4(q)        (E8M0 scale X, 32 E2M1 codes)
 
 Stored types: bloomery README of 2026-09-24 (shared experts kept in Q8_0)
 and bloomery README 0.3.1 ("Status (0.3.1)" table, "Quant types" row: card
@@ -76,6 +77,22 @@ def q4k_case(name: str, d_bits: int, dmin_bits: int, sc: list[int], m: list[int]
                 bytes_hex=bytes(raw).hex(), expected=[frac_str(v) for v in expected])
 
 
+# FP4 (E2M1) magnitudes by code & 7, as the OCP Microscaling Formats (MX)
+# v1.0 specification lists them; bit 3 of the code is the sign.
+E2M1 = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3), Fraction(4), Fraction(6)]
+
+
+def mxfp4_case(name: str, x_bits: int, codes: list[int], note: str) -> dict:
+    """One MXFP4 block: E8M0 scale byte X (2^(X-127)), then element i < 16 in
+    the low nibble of byte 1+i and element 16+i in its high nibble."""
+    assert len(codes) == 32 and all(0 <= c < 16 for c in codes) and 0 <= x_bits < 255
+    raw = [x_bits] + [codes[i] | (codes[16 + i] << 4) for i in range(16)]
+    scale = Fraction(2) ** (x_bits - 127)
+    expected = [scale * (-1 if c & 8 else 1) * E2M1[c & 7] for c in codes]
+    return dict(name=name, format="MXFP4", note=note, x_bits=x_bits, codes=codes, bytes_hex=bytes(raw).hex(),
+                expected=[frac_str(v) for v in expected])
+
+
 def main() -> None:
     cases = []
     cases.append(q8_0_case(
@@ -100,10 +117,22 @@ def main() -> None:
         "q4k_distinct_subblocks", 0x2E00, 0x2A00, [63, 62, 61, 60, 59, 58, 57, 56], [7, 14, 21, 28, 35, 42, 49, 56],
         [[(l * (j + 1) + 5 * j) % 16 for l in range(32)] for j in range(8)],
         "d = 0x2E00, dmin = 0x2A00; every sub-block has its own quant pattern"))
+    cases.append(mxfp4_case(
+        "mxfp4_all_codes", 127, list(range(16)) + list(range(15, -1, -1)),
+        "scale 1; every code once in each half, so any nibble or element-order slip changes a value"))
+    cases.append(mxfp4_case(
+        "mxfp4_scale_8", 130, [(7 * i + 3) % 16 for i in range(32)], "scale 2^3"))
+    cases.append(mxfp4_case(
+        "mxfp4_min_scale", 0, [(5 * i + 1) % 16 for i in range(32)], "scale 2^-127, the smallest E8M0 value"))
+    cases.append(mxfp4_case(
+        "mxfp4_max_scale", 254, [(3 * i) % 16 for i in range(32)], "scale 2^127, the largest finite E8M0 value"))
     doc = dict(
         citation=("Stored block types: bloomery README of 2026-09-24 (shared experts in Q8_0) and bloomery README "
-                  "0.3.1, 'Status (0.3.1)' table, 'Quant types' row; block formulas of the problem statement; "
-                  "Q4_K byte order as read for this build (GGUF order)."),
+                  "0.3.1, 'Status (0.3.1)' table, 'Quant types' row (card experts in Q4_K to Q6_K and MXFP4); "
+                  "block formulas of the problem statement; Q4_K byte order as read for this build (GGUF order); "
+                  "MXFP4 element and scale encodings of the OCP Microscaling Formats (MX) v1.0 specification, "
+                  "byte order as read for this build (scale byte, then elements 0-15 in low nibbles, 16-31 in "
+                  "high nibbles)."),
         derivation="expected[i] written by tests/golden/make_golden.py with exact rationals from the listed fields",
         cases=cases)
     with open(os.path.join(HERE, "quant_blocks.json"), "w") as f:

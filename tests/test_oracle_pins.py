@@ -35,7 +35,7 @@ def pin_golden_blocks() -> bool:
     ok = True
     for case in doc["cases"]:
         raw = np.frombuffer(bytes.fromhex(case["bytes_hex"]), dtype=np.uint8)
-        fmt = O.Q8_0 if case["format"] == "Q8_0" else O.Q4K
+        fmt = {"Q8_0": O.Q8_0, "Q4_K": O.Q4K, "MXFP4": O.MXFP4}[case["format"]]
         got = O.dequant(fmt, raw, len(case["expected"]))
         want = np.array([float(Fraction(v)) for v in case["expected"]])
         ok &= bool(np.array_equal(got, want))
@@ -65,6 +65,15 @@ def pin_encoder_round_trip() -> bool:
         ok &= bool(np.all(err <= bound))
         ok &= bool(np.sqrt(np.mean(err ** 2)) < 0.2 * w.std())
         ok &= bool(np.corrcoef(got.ravel(), w.ravel())[0, 1] > 0.98)
+    # MXFP4: the block scale s = 2^(X-127) has 6 s >= max |x|, so no element
+    # saturates and each lies within half a step of its code: at most s
+    # (the step between 4 s and 6 s is 2 s).
+    raw = F.encode(O.MXFP4, w.astype(np.float32))
+    got = O.dequant(O.MXFP4, raw, w.size).reshape(w.shape)
+    s = np.ldexp(1.0, raw[::17].astype(np.int64) - 127).reshape(64, -1)
+    ok &= bool(np.all(np.abs(got - w) <= np.repeat(s, 32, axis=1)))
+    ok &= bool(np.all(np.abs(w).reshape(64, -1, 32).max(axis=2) <= 6 * s))
+    ok &= bool(np.corrcoef(got.ravel(), w.ravel())[0, 1] > 0.95)
     return ok
 
 
@@ -124,7 +133,7 @@ def _dense_ffn(g, u, dn, x):
 
 def pin_ffn_dense(fmt: int) -> bool:
     rng = np.random.default_rng(17 + fmt)
-    H, I = (512, 256) if fmt == O.Q4K else (96, 64)
+    H, I = {O.Q4K: (512, 256), O.Q8_0: (96, 64), O.MXFP4: (128, 96)}[fmt]
     blob, (g, u, dn) = B.random_expert(rng, fmt, H, I)
     x = rng.normal(size=H)
     got = O.expert_ffn(fmt, blob, H, I, x)
@@ -222,6 +231,7 @@ PINS = {
     "batches_vs_sort": pin_batches_vs_sort,
     "ffn_dense_q8_0": lambda: pin_ffn_dense(O.Q8_0),
     "ffn_dense_q4k": lambda: pin_ffn_dense(O.Q4K),
+    "ffn_dense_mxfp4": lambda: pin_ffn_dense(O.MXFP4),
     "layer_brute_softmax_partial": lambda: pin_layer_brute_force(O.SOFTMAX, True),
     "layer_brute_sigmoid_full": lambda: pin_layer_brute_force(O.SIGMOID, False),
     "disjoint_halves": pin_disjoint_halves,
@@ -259,6 +269,11 @@ DEFECTS = [
     (11, "encoder_round_trip"),
     (12, "disjoint_halves"),               # residency ignored in the combine
     (12, "layer_brute_softmax_partial"),
+    (13, "golden_blocks"),                 # MXFP4 elements as consecutive nibble pairs
+    (13, "ffn_dense_mxfp4"),
+    (13, "encoder_round_trip"),
+    (14, "golden_blocks"),                 # MXFP4 scale bias 128
+    (14, "ffn_dense_mxfp4"),
 ]
 
 
