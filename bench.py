@@ -222,6 +222,7 @@ def main():
     del pools, pool0
     torch.cuda.empty_cache()
     dsv3 = bench_dsv3(args, threads) if args.dsv3_steps > 0 else None
+    mxfp4 = bench_mxfp4(args, threads) if args.dsv3_steps > 0 else None
     stack = bench_stack(args, threads) if args.stack_replays > 0 else None
 
     traffic = read_traffic()
@@ -250,6 +251,7 @@ def main():
         "cpu_baseline": cpu,
         "prefill": prefill,
         "dsv3_decode": dsv3,
+        "mxfp4_decode": mxfp4,
         "stack": stack,
         "kernels_us": {k2: round(v["avg_us"], 3) for k2, v in kern.items()},
         "down_gemv_GBs": round(dn_gbs, 1),
@@ -442,6 +444,94 @@ def bench_dsv3(args, threads: int) -> dict:
                    "time, i.e. the whole layer (five routed and two shared-expert kernels) against the HBM peak")
     del pool, shared
     torch.cuda.empty_cache()
+    return res
+
+
+def bench_mxfp4(args, threads: int) -> dict:
+    """The decode layers with MXFP4 routed experts (17 bytes per 32 weights):
+    Qwen3-shaped at T = 2 (8 pool copies rotated, 2.6 GB, so a step's experts
+    come from HBM), its gate/up GEMV against the HBM peak; DeepSeek-V3-shaped
+    at T = 2 with its Q8_0 shared expert (one 6 GB pool).  Graph-replayed like
+    the other decode layers."""
+    import numpy as np
+    import torch
+
+    import fixtures as F
+    import quantized_routed_expert_moe_amd as Q
+    from concurrent.futures import ThreadPoolExecutor
+    from fixtures import workloads as W
+    from quantized_routed_expert_moe_amd.layer import LayerSpec, MoELayer
+
+    res = {}
+    for key, wl, copies in (("qwen3_T2", W.QWEN3_MXFP4_DECODE_T2, 8), ("dsv3_T2", W.DSV3_MXFP4_DECODE_T2, 1)):
+        blobs = W.expert_blobs(wl)
+        nb = Q.moe_expert_blob_bytes(wl.fmt, wl.H, wl.I)
+        stride = (nb + 255) // 256 * 256
+        host = np.zeros((wl.E, stride), dtype=np.uint8)
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(lambda e: Q.moe_pack_expert(wl.fmt, blobs[e], wl.H, wl.I, out=host[e, :nb]), range(wl.E)))
+        del blobs
+        pools = [torch.from_numpy(host).cuda() for _ in range(copies)]
+        del host
+        shared, shared_bytes = None, 0
+        if wl.I_shared:
+            nbs = Q.moe_expert_blob_bytes(F.Q8_0, wl.H, wl.I_shared)
+            sh_host = np.zeros((1, (nbs + 255) // 256 * 256), dtype=np.uint8)
+            Q.moe_pack_expert(F.Q8_0, W.shared_blob(wl), wl.H, wl.I_shared, out=sh_host[0, :nbs])
+            shared = torch.from_numpy(sh_host).cuda()
+            shared_bytes = nbs
+        soe = torch.arange(wl.E, dtype=torch.int32, device="cuda")
+        spec = LayerSpec(wl.fmt, wl.H, wl.I, wl.E, wl.k, wl.score, wl.renormalize, wl.scale, wl.I_shared)
+        layer = MoELayer(spec, wl.T, wl.E, pools[0], stride, soe, shared, Q.MOE_PATH_DECODE)
+        nbatch = 16
+        xs = [torch.from_numpy(W.x_of(wl, seed=300 + i)).cuda() for i in range(nbatch)]
+        ls = [torch.from_numpy(W.logits_of(wl, seed=300 + i)).cuda() for i in range(nbatch)]
+        uniq = []
+        for i in range(nbatch):
+            layer.forward(xs[i], ls[i], slot_pool=pools[i % copies])
+            uniq.append(int(torch.unique(layer.ids).numel()))
+        torch.cuda.synchronize()
+        steps = args.dsv3_steps
+        Q.moe_timer_begin(3, steps * (2 if wl.I_shared else 1))
+        for i in range(steps):
+            layer.forward(xs[i % nbatch], ls[i % nbatch], slot_pool=pools[i % nbatch % copies])
+        torch.cuda.synchronize()
+        gu_ms, gu_n = Q.moe_timer_end(3)
+        graphs = []
+        for i in range(nbatch):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                layer.forward(xs[i], ls[i], slot_pool=pools[i % copies])
+            graphs.append(g)
+        for i in range(2 * nbatch):
+            graphs[i % nbatch].replay()
+        torch.cuda.synchronize()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(steps):
+            graphs[i % nbatch].replay()
+        stop.record()
+        torch.cuda.synchronize()
+        ms_step = start.elapsed_time(stop) / steps
+        mean_uniq = float(np.mean([uniq[i % nbatch] for i in range(steps)]))
+        layer_bytes = mean_uniq * nb + shared_bytes
+        r = {"workload": wl.name, "tokens_per_s": round(wl.T / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 4),
+             "unique_experts_per_step": round(mean_uniq, 2), "expert_bytes": nb,
+             "layer_bytes_per_step": round(layer_bytes),
+             "layer_GBs": round(layer_bytes / (ms_step * 1e-3) / 1e9, 1),
+             "layer_frac_of_hbm": round(layer_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+             "pool_copies": copies}
+        if not wl.I_shared:  # stage 3 then times only the routed gate/up GEMV
+            gu_us = 1e3 * gu_ms / max(gu_n, 1)
+            gbytes = mean_uniq * 2 * wl.H * wl.I // 32 * 17
+            r["gateup"] = {"avg_launch_us": round(gu_us, 3), "algorithmic_bytes_per_launch": round(gbytes),
+                           "GBs": round(gbytes / (gu_us * 1e-6) / 1e9, 1),
+                           "frac_of_hbm": round(gbytes / (gu_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        res[key] = r
+        del graphs, layer, pools, shared
+        torch.cuda.empty_cache()
+    res["note"] = ("MXFP4 codes converted to fp16 by the hardware FP4 conversion, fp16 x fp16 dot products, fp32 "
+                   "accumulate, each 32-weight block scaled by its E8M0 power of two; same kernels as Q4_K otherwise")
     return res
 
 

@@ -11,7 +11,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from . import Q4K, Q8_0, TAG_SHARED_EXPERT, activations, expert_blob, logits_normal, logits_zipf, to_bf16_bits
+from . import MXFP4, Q4K, Q8_0, TAG_SHARED_EXPERT, activations, expert_blob, logits_normal, logits_zipf, to_bf16_bits
 from . import expert_blobs as _expert_blobs
 
 SOFTMAX, SIGMOID = 0, 1
@@ -54,7 +54,15 @@ DSV3_STACK = Workload("58-layer DeepSeek-V3-shaped stack, 96 of 256 experts resi
                       256, 8, 2, score=SIGMOID, scale=2.5, I_shared=2048, zipf_s=1.1, layers=58, resident=96,
                       staging=8, count_tokens=10000)
 
-ALL = [TINY, QWEN3_DECODE_T1, QWEN3_DECODE_T2, QWEN3_PREFILL, DSV3_DECODE_T2, DSV3_DECODE_T4, DSV3_STACK]
+# The same layers with MXFP4 routed experts (a card expert type of the engine;
+# OCP MX encodings).  Weights: the same seeded normals, MXFP4-encoded.
+QWEN3_MXFP4_DECODE_T2 = Workload("Qwen3-30B-A3B-shaped MoE layer, MXFP4 experts, decode T=2", MXFP4, 2048, 768, 128, 8,
+                                 2)
+DSV3_MXFP4_DECODE_T2 = Workload("DeepSeek-V3-shaped MoE layer, MXFP4 experts, decode T=2 (+shared Q8_0 expert)", MXFP4,
+                                7168, 2048, 256, 8, 2, score=SIGMOID, scale=2.5, I_shared=2048)
+
+ALL = [TINY, QWEN3_DECODE_T1, QWEN3_DECODE_T2, QWEN3_PREFILL, DSV3_DECODE_T2, DSV3_DECODE_T4, DSV3_STACK,
+       QWEN3_MXFP4_DECODE_T2, DSV3_MXFP4_DECODE_T2]
 
 
 def x_of(w: Workload, layer: int = 0, seed: int | None = None) -> np.ndarray:

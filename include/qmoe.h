@@ -15,7 +15,8 @@
  *   (moe_route_and_batch      the two above in one call: one launch at decode
  *                             sizes)
  *   moe_expert_ffn_q4k /      dequantize + SwiGLU expert FFN over each slot's
- *   moe_expert_ffn_q8_0       batch (decode GEMV or prefill MFMA GEMM)
+ *   moe_expert_ffn_q8_0 /     batch (decode GEMV or prefill MFMA GEMM)
+ *   moe_expert_ffn_mxfp4
  *   moe_combine               weighted sum of the pairs (+ shared expert)
  *
  * Conventions for every call:
@@ -57,7 +58,7 @@ typedef enum moe_status {
 typedef enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
 typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 typedef enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 } moe_path;
-typedef enum moe_format { MOE_FMT_Q8_0 = 0, MOE_FMT_Q4K = 1 } moe_format;
+typedef enum moe_format { MOE_FMT_Q8_0 = 0, MOE_FMT_Q4K = 1, MOE_FMT_MXFP4 = 2 } moe_format;
 
 /* Limits checked by the calls below. */
 #define MOE_MAX_EXPERTS 1024 /* E */
@@ -184,10 +185,17 @@ moe_status moe_count_routes(const int32_t* topk_ids, int T, int k, int E, uint32
  *   Q8_0 (34 B / 32 weights): fp16 d, 32 int8 q;           w = d*q.
  *   Q4_K (144 B / 256 weights): fp16 d, fp16 dmin, 12 B of 6-bit (sc, m)
  *        for 8 sub-blocks of 32, 128 B of 4-bit q;        w = d*sc_j*q - dmin*m_j.
+ *   MXFP4 (17 B / 32 weights; a card expert type in README 0.3.1, "Status
+ *        (0.3.1)" table, "Quant types" row; encodings of the OCP Microscaling
+ *        Formats v1.0): one E8M0 scale byte X, then 16 bytes of FP4 (E2M1)
+ *        codes, element i < 16 in the low nibble of byte 1 + i and element
+ *        16 + i in its high nibble;                  w = 2^(X - 127) * fp4(q)
+ *        (fp4: sign bit 3, exponent bits 2-1 with bias 1, mantissa bit 0:
+ *        +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}; X = 255 is NaN).
  * Canonical blob = W_gate | W_up | W_down, each row-major.
  *
- * Supported shapes: Q4_K needs H % 256 == 0 and I % 256 == 0; Q8_0 needs
- * H % 128 == 0 and I % 128 == 0.
+ * Supported shapes: Q4_K and MXFP4 need H % 256 == 0 and I % 256 == 0; Q8_0
+ * needs H % 128 == 0 and I % 128 == 0.
  */
 size_t moe_expert_blob_bytes(int format, int H, int I);
 
@@ -222,12 +230,14 @@ moe_status moe_validate_slot_map(const int32_t* slot_of_expert, int E, int S);
  * y_pairs       device, [T*k, H] of y_dtype, indexed by pair p.  Rows of
  *               resident pairs are written; other rows are left untouched.
  * path          MOE_PATH_DECODE: GEMV, fp16 activations in fp32-accumulated
- *               dot products, y_pairs MOE_F32.
+ *               dot products, y_pairs MOE_F32 (MXFP4: each code converted
+ *               exactly to fp16 by the hardware FP4 conversion, the block's
+ *               dot product then scaled by 2^(X - 127) in fp32).
  *               MOE_PATH_PREFILL (Q4_K only): bf16 x, weights dequantized to
  *               bf16 tiles, bf16 MFMA with fp32 accumulate, h rounded to bf16;
  *               y_pairs MOE_F32 or MOE_BF16.
  *               MOE_PATH_AUTO: PREFILL for Q4_K with bf16 x when T > 32, else
-               DECODE.
+ *               DECODE (always DECODE for Q8_0 and MXFP4).
  * ws, ws_bytes  device workspace, at least moe_ffn_workspace_size(format, T,
  *               k, H, I, path).
  *
@@ -244,6 +254,10 @@ moe_status moe_expert_ffn_q8_0(const void* slot_pool, size_t slot_stride, int S,
                                int x_dtype, int T, int k, const int32_t* slot_offsets, const int32_t* active_slots,
                                const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype,
                                int path, void* ws, size_t ws_bytes, void* stream);
+moe_status moe_expert_ffn_mxfp4(const void* slot_pool, size_t slot_stride, int S, int H, int I, const void* x,
+                                int x_dtype, int T, int k, const int32_t* slot_offsets, const int32_t* active_slots,
+                                const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype,
+                                int path, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- combine
  * y[t] = sum over j < k, in j order, of [slot_of_expert[id] >= 0] *

@@ -46,13 +46,14 @@ moe_status check_route_shape(int T, int E, int k) {
 }
 
 moe_status check_shape(int format, int H, int I) {
-    if (format != MOE_FMT_Q8_0 && format != MOE_FMT_Q4K)
-        return fail(MOE_ERR_INVALID_ARGUMENT, "format = %d is not MOE_FMT_Q8_0 or MOE_FMT_Q4K", format);
-    const int m = format == MOE_FMT_Q4K ? 256 : 128;
+    if (format != MOE_FMT_Q8_0 && format != MOE_FMT_Q4K && format != MOE_FMT_MXFP4)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "format = %d is not MOE_FMT_Q8_0, MOE_FMT_Q4K or MOE_FMT_MXFP4", format);
+    const int m = format == MOE_FMT_Q8_0 ? 128 : 256;
+    static const char* const kNames[] = {"Q8_0", "Q4_K", "MXFP4"};
     if (H <= 0 || I <= 0) return fail(MOE_ERR_INVALID_ARGUMENT, "H = %d, I = %d must be positive", H, I);
     if (H % m || I % m)
         return fail(MOE_ERR_UNSUPPORTED, "%s needs H and I multiples of %d (H = %d, I = %d)",
-                    format == MOE_FMT_Q4K ? "Q4_K" : "Q8_0", m, H, I);
+                    kNames[format], m, H, I);
     if ((long long)H * I > (1ll << 31))
         return fail(MOE_ERR_UNSUPPORTED, "H*I = %lld too large", (long long)H * I);
     return MOE_OK;
@@ -60,7 +61,7 @@ moe_status check_shape(int format, int H, int I) {
 
 size_t blob_bytes(int format, int H, int I) {
     const size_t w = (size_t)H * I;  // weights per matrix
-    return format == MOE_FMT_Q4K ? 3 * w / 256 * 144 : 3 * w / 32 * 34;
+    return format == MOE_FMT_Q4K ? 3 * w / 256 * 144 : format == MOE_FMT_MXFP4 ? 3 * w / 32 * 17 : 3 * w / 32 * 34;
 }
 
 int resolve_path(int format, int T, int x_dtype, int path) {
@@ -220,6 +221,66 @@ void q8_walk(const uint8_t* in, uint8_t* out, int H, int I) {
         }
 }
 
+// MXFP4: one 17-byte block (E8M0 scale, element i < 16 in the low nibble of
+// byte 1 + i, 16 + i in its high nibble) <-> (scale byte, 16 packed code
+// bytes: group d of elements 8d..8d+7 in dword slot 0, 2, 1, 3, byte p =
+// element 8d+p low, 8d+p+4 high).
+void mx4_block(const uint8_t* canon, uint8_t* scale, uint8_t* codes, bool pack) {
+    uint8_t e[32];
+    if (pack) {
+        *scale = canon[0];
+        for (int i = 0; i < 16; ++i) {
+            e[i] = canon[1 + i] & 15;
+            e[16 + i] = canon[1 + i] >> 4;
+        }
+        for (int d = 0; d < 4; ++d)
+            for (int p = 0; p < 4; ++p)
+                codes[4 * kDwordSlot[d] + p] = (uint8_t)(e[8 * d + p] | (e[8 * d + p + 4] << 4));
+    } else {
+        uint8_t* dst = const_cast<uint8_t*>(canon);
+        dst[0] = *scale;
+        for (int d = 0; d < 4; ++d)
+            for (int p = 0; p < 4; ++p) {
+                const uint8_t b = codes[4 * kDwordSlot[d] + p];
+                e[8 * d + p] = b & 15;
+                e[8 * d + p + 4] = b >> 4;
+            }
+        for (int i = 0; i < 16; ++i) dst[1 + i] = (uint8_t)(e[i] | (e[16 + i] << 4));
+    }
+}
+
+template <bool PACK>
+void mx4_walk(const uint8_t* in, uint8_t* out, int H, int I) {
+    const size_t rbH = (size_t)H / 32 * 17, rbI = (size_t)I / 32 * 17;
+    const size_t gbytes = (size_t)I * rbH;
+    const int UH = H / 256, UI = I / 256;
+    uint8_t* dev = PACK ? out : const_cast<uint8_t*>(in);
+    const uint8_t* canon_base = PACK ? in : out;
+    for (int rg = 0; rg < I / 64; ++rg)
+        for (int u = 0; u < UH; ++u) {
+            const size_t tile = ((size_t)rg * UH + u) * qmoe::kMx4GateUpTile;
+            for (int r = 0; r < 64; ++r) {
+                const size_t row = (size_t)rg * 64 + r;
+                for (int mat = 0; mat < 2; ++mat)
+                    for (int j = 0; j < 8; ++j)
+                        mx4_block(canon_base + mat * gbytes + row * rbH + (size_t)(u * 8 + j) * 17,
+                                  dev + tile + mat * 512 + r * 8 + j, dev + tile + 1024 + j * 2048 + mat * 1024 + r * 16,
+                                  PACK);
+            }
+        }
+    const size_t base = qmoe::mx4_gateup_bytes(H, I);
+    for (int rg = 0; rg < H / 64; ++rg)
+        for (int u = 0; u < UI; ++u) {
+            const size_t tile = base + ((size_t)rg * UI + u) * qmoe::kMx4DownTile;
+            for (int r = 0; r < 64; ++r) {
+                const size_t row = (size_t)rg * 64 + r;
+                for (int j = 0; j < 8; ++j)
+                    mx4_block(canon_base + 2 * gbytes + row * rbI + (size_t)(u * 8 + j) * 17, dev + tile + r * 8 + j,
+                              dev + tile + 512 + j * 1024 + r * 16, PACK);
+            }
+        }
+}
+
 moe_status ffn_common(int format, const void* slot_pool, size_t slot_stride, int S, int H, int I, const void* x,
                       int x_dtype, int T, int k, const int32_t* slot_offsets, const int32_t* active_slots,
                       const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype, int path,
@@ -247,7 +308,9 @@ moe_status ffn_common(int format, const void* slot_pool, size_t slot_stride, int
         if (y_dtype != MOE_F32) return fail(MOE_ERR_UNSUPPORTED, "the decode path writes MOE_F32 y_pairs");
         need = qmoe::decode_workspace_bytes(T, k, H, I);
     } else {
-        if (format != MOE_FMT_Q4K) return fail(MOE_ERR_UNSUPPORTED, "the prefill path is implemented for Q4_K only");
+        if (format != MOE_FMT_Q4K)
+            return fail(MOE_ERR_UNSUPPORTED, "the prefill path is implemented for Q4_K only (MOE_PATH_DECODE serves "
+                                             "Q8_0 and MXFP4 at any T)");
         if (x_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the prefill path takes MOE_BF16 x");
         // The GEMMs address x and h rows with 32-bit byte offsets, and the
         // tile list counts tiles in 16 bits.
@@ -404,6 +467,7 @@ moe_status moe_pack_expert(int format, const void* canonical, void* packed, int 
     if (in < out + n && out < in + n) return fail(MOE_ERR_INVALID_ARGUMENT, "blobs overlap");
     memset(out, 0, n);
     if (format == MOE_FMT_Q4K) q4k_walk<true>(in, out, H, I);
+    else if (format == MOE_FMT_MXFP4) mx4_walk<true>(in, out, H, I);
     else q8_walk<true>(in, out, H, I);
     return MOE_OK;
 }
@@ -418,6 +482,7 @@ moe_status moe_unpack_expert(int format, const void* packed, void* canonical, in
     if (in < out + n && out < in + n) return fail(MOE_ERR_INVALID_ARGUMENT, "blobs overlap");
     memset(out, 0, n);
     if (format == MOE_FMT_Q4K) q4k_walk<false>(in, out, H, I);
+    else if (format == MOE_FMT_MXFP4) mx4_walk<false>(in, out, H, I);
     else q8_walk<false>(in, out, H, I);
     return MOE_OK;
 }
@@ -460,6 +525,14 @@ moe_status moe_expert_ffn_q8_0(const void* slot_pool, size_t slot_stride, int S,
                                const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype,
                                int path, void* ws, size_t ws_bytes, void* stream) {
     return ffn_common(MOE_FMT_Q8_0, slot_pool, slot_stride, S, H, I, x, x_dtype, T, k, slot_offsets, active_slots,
+                      num_active, perm_pair, y_pairs, y_dtype, path, ws, ws_bytes, stream);
+}
+
+moe_status moe_expert_ffn_mxfp4(const void* slot_pool, size_t slot_stride, int S, int H, int I, const void* x,
+                                int x_dtype, int T, int k, const int32_t* slot_offsets, const int32_t* active_slots,
+                                const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype,
+                                int path, void* ws, size_t ws_bytes, void* stream) {
+    return ffn_common(MOE_FMT_MXFP4, slot_pool, slot_stride, S, H, I, x, x_dtype, T, k, slot_offsets, active_slots,
                       num_active, perm_pair, y_pairs, y_dtype, path, ws, ws_bytes, stream);
 }
 

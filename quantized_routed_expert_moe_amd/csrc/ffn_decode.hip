@@ -18,6 +18,10 @@
 //     1152 * sum x for Q8_0) is precomputed per 32-element block of the
 //     activation and subtracted once per block, together with the Q4_K min
 //     term dmin * m_j * sum x.
+//   * MXFP4 codes go to fp16 through the gfx950 FP4 conversion (two codes
+//     per instruction, exact), laid out in the Q4_K element order so the two
+//     formats share activation records; each 32-element block's dot product
+//     is scaled by its E8M0 power of two in fp32.
 //   * Activations (token rows, and the intermediate h) are 64-byte records per
 //     32 elements, laid out in the order the nibble/byte extraction produces.
 //     Each wave puts the records of its K range for the tokens of the current
@@ -75,6 +79,36 @@ __device__ __forceinline__ float q8_dot(const uint4 a, const uint4 b, cu32* X) {
     return acc;
 }
 
+// MXFP4: 16 code bytes of one row and block (dword of group d, byte p =
+// element 8d+p low nibble, 8d+p+4 high nibble; groups stored 0, 2, 1, 3)
+// against one record in the Q4_K order: byte p converts to the fp16 pair
+// (fp4 of 8d+p, fp4 of 8d+p+4) of record word 4d+p; the odd words hold x/16,
+// so their codes convert with scale 16 (exact: powers of two).  Returns
+// sum_e fp4(q_e) x_e.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bits(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ float mx4_dot(const uint4 q, cu32* X) {
+    const uint32_t w[4] = {q.x, q.z, q.y, q.w};
+    float acc = 0.0f;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        acc = fdot2u(bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[d], 1.0f, 0)), X[4 * d + 0], acc);
+        acc = fdot2u(bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[d], 16.0f, 1)), X[4 * d + 1], acc);
+        acc = fdot2u(bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[d], 1.0f, 2)), X[4 * d + 2], acc);
+        acc = fdot2u(bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[d], 16.0f, 3)), X[4 * d + 3], acc);
+    }
+    return acc;
+}
+
+// E8M0 scale byte x -> 2^(x - 127) as fp32 bits: x << 23 for x = 1..254;
+// x = 0 (the subnormal 2^-127) and x = 255 (NaN) also need bit 22, which
+// bit 8 of x + 1 or of x - 1 supplies only for those two.  Integer
+// operations only: compares here would each hold a lane mask in scalar
+// registers, and the compiler, hoisting them, ran out of those.
+__device__ __forceinline__ float e8m0_value(uint32_t x) {
+    return __uint_as_float((x << 23) | ((((x + 1) | (x - 1)) & 0x100u) << 14));
+}
+
 __device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint2 ld8(const uint8_t* p) { return *reinterpret_cast<const uint2*>(p); }
 
@@ -83,8 +117,8 @@ __device__ __forceinline__ uint2 ld8(const uint8_t* p) { return *reinterpret_cas
 // One kernel template serves gate/up (NMAT = 2: the gate and up rows of the
 // same intermediate feature, interleaved per tile) and down (NMAT = 1).
 // Per workgroup: one active slot (blockIdx.y) and one 64-row tile
-// (blockIdx.x); its waves split the K units (Q4_K super-blocks or Q8_0
-// groups of four blocks).  Per unit a wave: issues the weight loads of the
+// (blockIdx.x); its waves split the K units (Q4_K super-blocks, Q8_0 groups
+// of four blocks, MXFP4 groups of eight).  Per unit a wave: issues the weight loads of the
 // unit, loads the activation records of the unit for the chunk's tokens,
 // writes them to its LDS region, and runs the dot products with the records
 // read back as broadcasts.  The first unit's weights are requested right
@@ -92,7 +126,7 @@ __device__ __forceinline__ uint2 ld8(const uint8_t* p) { return *reinterpret_cas
 // overlaps the dependent loads of offsets, permutation and records.
 
 template <int FMT> struct Unit {
-    static constexpr int kRecords = FMT == 1 ? 8 : 4;  // 32-element blocks per unit
+    static constexpr int kRecords = FMT == 0 ? 4 : 8;  // 32-element blocks per unit
 };
 
 // Weight registers of one unit for this lane's row(s); the Q4_K header or
@@ -103,6 +137,9 @@ template <int NMAT> struct UnitRegs<1, NMAT> {
 };
 template <int NMAT> struct UnitRegs<0, NMAT> {
     uint4 q[4][NMAT][2];
+};
+template <int NMAT> struct UnitRegs<2, NMAT> {
+    uint4 q[8][NMAT];
 };
 
 template <int FMT, int NMAT>
@@ -152,7 +189,7 @@ __device__ __forceinline__ void act_load(const void* const* xrow, int x_dtype, c
                                          const float2* const* rcs_g, int r0, int lane, ActRegs& a) {
     if (NMAT == 2) {
         const int sl = lane & 7;
-        if (FMT == 1) {
+        if (FMT != 0) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) a.xr[t] = x4_load(xrow[t], x_dtype, (r0 + (lane >> 3)) * 32 + 4 * sl);
         } else {
@@ -179,7 +216,7 @@ template <int FMT, int NMAT, int NT>
 __device__ __forceinline__ void act_arrived(ActRegs& a) {
     if (NMAT == 2) {
 #pragma unroll
-        for (int t = 0; t < (FMT == 1 ? NT : 1); ++t)
+        for (int t = 0; t < (FMT != 0 ? NT : 1); ++t)
             asm volatile("" : "+v"(a.xr[t].x), "+v"(a.xr[t].y), "+v"(a.xr[t].z), "+v"(a.xr[t].w));
     } else {
 #pragma unroll
@@ -214,7 +251,7 @@ template <int FMT, int NMAT, int RB, int NT>
 __device__ __forceinline__ void act_store(const ActRegs& a, int x_dtype, int lane, uint32_t* lw, float* lc) {
     if (NMAT == 2) {
         const int sl = lane & 7;
-        if (FMT == 1) {
+        if (FMT != 0) {
             const int jb = lane >> 3;
             const bool even = (sl & 1) == 0;
 #pragma unroll
@@ -233,8 +270,10 @@ __device__ __forceinline__ void act_store(const ActRegs& a, int x_dtype, int lan
                 const uint32_t b2 = float_to_half_bits(lo1), b3 = float_to_half_bits(hi1);
                 *reinterpret_cast<uint2*>(lw + (t * RB + jb) * 16 + 2 * sl) =
                     make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-                const float s16 =
-                    sum8_lanes(half_to_float(b0) + half_to_float(b1) + half_to_float(b2) + half_to_float(b3));
+                // (MXFP4 has no magic-number constant to remove: C stays 0)
+                const float s16 = FMT == 1 ? sum8_lanes(half_to_float(b0) + half_to_float(b1) + half_to_float(b2) +
+                                                        half_to_float(b3))
+                                           : 0.0f;
                 const float sx = sum8_lanes(v[0] + v[1] + v[2] + v[3]);
                 // all 8 lanes of the block hold the sums
                 *reinterpret_cast<float2*>(lc + (t * RB + jb) * 2) = make_float2(1024.0f * s16, sx);
@@ -356,8 +395,40 @@ __device__ __forceinline__ void half_dots(const UnitRegs<0, NMAT>& r, const uint
     }
 }
 
+template <int NMAT>
+__device__ __forceinline__ void load_half(__amdgpu_buffer_rsrc_t src, int uoff, int lane, int h,
+                                          UnitRegs<2, NMAT>& r, uint2* sc) {
+    if (h == 0) {
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) sc[m] = ldb8(src, lane * 8, uoff + m * 512);
+    }
+#pragma unroll
+    for (int j = 4 * h; j < 4 * h + 4; ++j)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) r.q[j][m] = ldb16(src, lane * 16, uoff + NMAT * 512 + j * NMAT * 1024 + m * 1024);
+}
+template <int NT, int NMAT>
+__device__ __forceinline__ void half_dots(const UnitRegs<2, NMAT>& r, const uint2* sc, int h, const uint32_t* lw,
+                                          const float* lc, float (*acc)[NMAT]) {
+    (void)lc;
+#pragma unroll
+    for (int j = 4 * h; j < 4 * h + 4; ++j) {
+        float s[NMAT];
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) s[m] = e8m0_value(((j < 4 ? sc[m].x : sc[m].y) >> (8 * (j & 3))) & 255u);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const uint32_t* X = lw + (t * 8 + j) * 16;
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) acc[t][m] += s[m] * mx4_dot(r.q[j][m], X);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 template <int FMT> struct HdrType { typedef uint4 T; };
 template <> struct HdrType<0> { typedef uint2 T; };
+template <> struct HdrType<2> { typedef uint2 T; };
 
 // K units [u0, u0 + nu) of this lane's row(s) for NT tokens.  On entry `w`
 // and `hdr0` hold (or are loading) unit u0.  Per unit u: its records go to
@@ -431,7 +502,7 @@ __device__ __forceinline__ void store_h_record(float h, int rg, int lane, uint32
     const int e = lane & 31;
     int word, half;
     float v = h;
-    if (FMT == 1) {
+    if (FMT != 0) {  // Q4_K and MXFP4 share the record order
         const int d = e >> 3, n = e & 7;
         word = 4 * d + (n & 3);
         half = n >> 2;
@@ -443,7 +514,7 @@ __device__ __forceinline__ void store_h_record(float h, int rg, int lane, uint32
     }
     const uint32_t bits = float_to_half_bits(v);
     reinterpret_cast<uint16_t*>(hw_q + (size_t)blk * 16)[word * 2 + half] = (uint16_t)bits;
-    const float c = half_wave_sum(half_to_float(bits)) * (FMT == 1 ? 1024.0f : 1152.0f);
+    const float c = half_wave_sum(half_to_float(bits)) * (FMT == 0 ? 1152.0f : 1024.0f);
     const float sx = half_wave_sum(h);
     if (e == 0) hcs_q[blk] = make_float2(c, sx);
 }
@@ -477,7 +548,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(const uint8_t* __restrict__ p
     // wave index made visibly uniform, so K-loop bounds stay scalar
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
-    const int units = FMT == 1 ? K / 256 : K / 128;
+    const int units = FMT == 0 ? K / 128 : K / 256;
     // K range of this workgroup (blockIdx.z: its part of a K split across
     // workgroups), then of this wave
     const int kbase = blockIdx.z * nw * units_per_wave, kend = min(units, kbase + nw * units_per_wave);
@@ -705,7 +776,7 @@ hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s) {
 
     // gate/up + SwiGLU
     {
-        const int units = a.format == 1 ? a.H / 256 : a.H / 128;
+        const int units = a.format == 0 ? a.H / 128 : a.H / 256;
         int nw, upw;
         split_k(units, (long)(a.I / 64) * max_active, &nw, &upw);
         const int kparts = split_k_parts(units, (long)(a.I / 64) * max_active, (int)P, &nw, &upw);
@@ -716,6 +787,8 @@ hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s) {
                            kparts, part};
         if (a.format == 1)
             launch_gemv<1, 2>(g, grid, block, s);
+        else if (a.format == 2)
+            launch_gemv<2, 2>(g, grid, block, s);
         else
             launch_gemv<0, 2>(g, grid, block, s);
         timer_after(kStageGateUp, s);
@@ -724,18 +797,22 @@ hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s) {
     }
     // down
     {
-        const int units = a.format == 1 ? a.I / 256 : a.I / 128;
+        const int units = a.format == 0 ? a.I / 128 : a.I / 256;
         int nw, upw;
         split_k(units, (long)(a.H / 64) * max_active, &nw, &upw);
         const int kparts = split_k_parts(units, (long)(a.H / 64) * max_active, (int)P, &nw, &upw);
         const dim3 grid(a.H / 64, max_active), block(64 * nw);
-        const size_t section = a.format == 1 ? q4k_gateup_bytes(a.H, a.I) : q8_gateup_bytes(a.H, a.I);
+        const size_t section = a.format == 1   ? q4k_gateup_bytes(a.H, a.I)
+                               : a.format == 2 ? mx4_gateup_bytes(a.H, a.I)
+                                               : q8_gateup_bytes(a.H, a.I);
         timer_before(kStageDown, s);
         const GemvLaunch g{a.pool, a.stride, a.S, a.I, a.H, section, nullptr, 0, hw, hcs, a.T, a.k,
                            a.slot_offsets, a.active_slots, a.num_active, a.perm_pair, nullptr, nullptr,
                            static_cast<float*>(a.y_pairs), upw, kparts, part};
         if (a.format == 1)
             launch_gemv<1, 1>(g, grid, block, s);
+        else if (a.format == 2)
+            launch_gemv<2, 1>(g, grid, block, s);
         else
             launch_gemv<0, 1>(g, grid, block, s);
         timer_after(kStageDown, s);

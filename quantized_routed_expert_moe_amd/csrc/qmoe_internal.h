@@ -42,6 +42,22 @@ namespace qmoe {
 //     [0, 512) scales; [512 + 2048jj, +2048) quants of block jj
 // Q8_0 quant bytes are stored as q + 128 (q xor 0x80), element e at byte e.
 
+//
+// Packed MXFP4 blob (H, I multiples of 256), tiles of 64 rows x 256 inputs
+// (eight 32-element blocks):
+//   gate/up tile (rg, u), u < H/256, 17408 bytes:
+//     [0, 512)          gate scales: row r at 8r: the E8M0 bytes of blocks 8u..8u+7
+//     [512, 1024)       up scales
+//     [1024 + 2048j, +1024)   gate codes of block j: row r at 16r
+//     [2048 + 2048j, +1024)   up codes of block j
+//   down tile (rg, u), u < I/256, 8704 bytes:
+//     [0, 512) scales; [512 + 1024j, +1024) codes of block j
+// The 16 code bytes of one row and block: group d (d < 4) of elements
+// 8d..8d+7 is one little-endian dword whose byte p (p < 4) holds element
+// 8d+p in its low nibble and 8d+p+4 in its high nibble, groups stored in
+// the order 0, 2, 1, 3 (the Q4_K element order, so both formats share the
+// decode path's activation records).
+
 constexpr int kMaxExpertsInternal = 1024;  // equals MOE_MAX_EXPERTS of the C ABI
 
 constexpr int kQ4kGateUpTile = 18432;
@@ -51,6 +67,9 @@ constexpr int kQ8DownTile = 8704;
 
 __host__ __device__ inline size_t q4k_gateup_bytes(int H, int I) { return (size_t)(I / 64) * (H / 256) * kQ4kGateUpTile; }
 __host__ __device__ inline size_t q8_gateup_bytes(int H, int I) { return (size_t)(I / 64) * (H / 128) * kQ8GateUpTile; }
+constexpr int kMx4GateUpTile = 17408;
+constexpr int kMx4DownTile = 8704;
+__host__ __device__ inline size_t mx4_gateup_bytes(int H, int I) { return (size_t)(I / 64) * (H / 256) * kMx4GateUpTile; }
 
 // Per-token activation records of the decode path, one per 32-element
 // block of the input dimension: 16 dwords of fp16 pairs laid out to match

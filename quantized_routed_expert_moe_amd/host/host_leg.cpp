@@ -69,9 +69,12 @@ uint16_t load_u16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
 
 constexpr int kQ4kBlock = 256, kQ4kBytes = 144;
 constexpr int kQ8Block = 32, kQ8Bytes = 34;
+constexpr int kMx4Block = 32, kMx4Bytes = 17;
 
 size_t row_bytes(int format, int n) {
-    return format == MOE_FMT_Q4K ? (size_t)(n / kQ4kBlock) * kQ4kBytes : (size_t)(n / kQ8Block) * kQ8Bytes;
+    if (format == MOE_FMT_Q4K) return (size_t)(n / kQ4kBlock) * kQ4kBytes;
+    if (format == MOE_FMT_MXFP4) return (size_t)(n / kMx4Block) * kMx4Bytes;
+    return (size_t)(n / kQ8Block) * kQ8Bytes;
 }
 
 __attribute__((target("avx2,fma")))
@@ -139,6 +142,36 @@ void dequant_row_q8_0(const uint8_t* row, int n, float* out) {
     }
 }
 
+// One MXFP4 row of n weights (n / 32 blocks of 17 bytes: an E8M0 scale byte
+// X, then element i < 16 in the low nibble of byte 1 + i and 16 + i in its
+// high nibble, FP4 E2M1 codes) -> n floats 2^(X - 127) fp4(q).  The code's
+// magnitude (bits 0-2) selects one of the eight E2M1 values by a register
+// permute, bit 3 becomes the float's sign; X builds the scale's bits
+// directly (X = 0: the subnormal 2^-127, X = 255: NaN).
+__attribute__((target("avx2,fma")))
+void dequant_row_mxfp4(const uint8_t* row, int n, float* out) {
+    const __m256 mag = _mm256_setr_ps(0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f);
+    const __m256i seven = _mm256_set1_epi32(7), eight = _mm256_set1_epi32(8);
+    const __m128i low4 = _mm_set1_epi8(0x0F);
+    for (int b = 0; b < n / kMx4Block; ++b, row += kMx4Bytes, out += kMx4Block) {
+        const uint32_t x = row[0];
+        const uint32_t sbits = x == 0 ? 0x00400000u : (x == 255 ? 0x7FC00000u : x << 23);
+        float sf;
+        std::memcpy(&sf, &sbits, sizeof(sf));
+        const __m256 scale = _mm256_set1_ps(sf);
+        const __m128i v = _mm_loadu_si128(reinterpret_cast<const __m128i*>(row + 1));
+        const __m128i lo = _mm_and_si128(v, low4);                        // elements 0-15
+        const __m128i hi = _mm_and_si128(_mm_srli_epi16(v, 4), low4);     // elements 16-31
+        const __m128i parts[4] = {lo, _mm_srli_si128(lo, 8), hi, _mm_srli_si128(hi, 8)};
+        for (int k = 0; k < 4; ++k) {
+            const __m256i c = _mm256_cvtepu8_epi32(parts[k]);
+            const __m256 m = _mm256_permutevar8x32_ps(mag, _mm256_and_si256(c, seven));
+            const __m256 sign = _mm256_castsi256_ps(_mm256_slli_epi32(_mm256_and_si256(c, eight), 28));
+            _mm256_storeu_ps(out + 8 * k, _mm256_mul_ps(_mm256_xor_ps(m, sign), scale));
+        }
+    }
+}
+
 // sum_i a[i] b[i], n a multiple of 32: four 8-wide FMA accumulators, then a
 // fixed reduction tree.
 __attribute__((target("avx2,fma")))
@@ -173,7 +206,7 @@ void run(int format, const uint8_t* const* expert_blob, int H, int I, const floa
                      [&](int a, int b) { return host_expert[a] < host_expert[b]; });
     const int nthreads = threads > 0 ? threads : omp_get_max_threads();
     const size_t rbH = row_bytes(format, H), rbI = row_bytes(format, I);
-    auto dequant = format == MOE_FMT_Q4K ? dequant_row_q4k : dequant_row_q8_0;
+    auto dequant = format == MOE_FMT_Q4K ? dequant_row_q4k : format == MOE_FMT_MXFP4 ? dequant_row_mxfp4 : dequant_row_q8_0;
     std::vector<float> g, u;
     for (int g0 = 0; g0 < count;) {
         const int e = host_expert[order[g0]];
@@ -230,8 +263,9 @@ const char* moe_host_last_error(void) { return g_error.c_str(); }
 int moe_host_leg(int format, const uint8_t* const* expert_blob, int E, int H, int I, const float* x, int T,
                  const int32_t* host_token, const int32_t* host_expert, const float* host_weight, int count,
                  float* y_host, int threads) {
-    if (format != MOE_FMT_Q4K && format != MOE_FMT_Q8_0) return fail(MOE_ERR_UNSUPPORTED, "bad format %d", format);
-    const int blk = format == MOE_FMT_Q4K ? kQ4kBlock : kQ8Block;
+    if (format != MOE_FMT_Q4K && format != MOE_FMT_Q8_0 && format != MOE_FMT_MXFP4)
+        return fail(MOE_ERR_UNSUPPORTED, "bad format %d", format);
+    const int blk = format == MOE_FMT_Q4K ? kQ4kBlock : format == MOE_FMT_MXFP4 ? kMx4Block : kQ8Block;
     if (H <= 0 || I <= 0 || H % blk || I % blk)
         return fail(MOE_ERR_UNSUPPORTED, "H = %d and I = %d must be positive multiples of %d", H, I, blk);
     if (E < 1 || T < 0 || count < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "E = %d, T = %d, count = %d", E, T, count);

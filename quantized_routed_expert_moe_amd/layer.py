@@ -14,9 +14,9 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-from . import (MOE_FMT_Q4K, MOE_FMT_Q8_0, MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL, moe_batches_workspace_size,
-               moe_combine, moe_expert_blob_bytes, moe_expert_ffn_q4k, moe_expert_ffn_q8_0, moe_ffn_workspace_size,
-               moe_pack_expert, moe_route_and_batch)
+from . import (MOE_FMT_Q8_0, MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL, moe_batches_workspace_size, moe_combine,
+               moe_expert_blob_bytes, moe_expert_ffn, moe_expert_ffn_q8_0, moe_ffn_workspace_size, moe_pack_expert,
+               moe_route_and_batch)
 
 
 def upload_packed_experts(fmt: int, canonical_blobs: np.ndarray, H: int, I: int, stride: int | None = None,
@@ -120,8 +120,7 @@ class MoELayer:
                             self.slot_of_expert, self.S, self.slot_offsets, self.active_slots, self.num_active,
                             self.perm_pair, self.host_token, self.host_expert, self.host_weight, self.host_count,
                             self.batch_ws, stream, route_counts=self.route_counts)
-        ffn = moe_expert_ffn_q4k if spec.fmt == MOE_FMT_Q4K else moe_expert_ffn_q8_0
-        ffn(pool, self.stride, self.S, spec.H, spec.I, x, spec.k, self.slot_offsets, self.active_slots,
+        moe_expert_ffn(spec.fmt)(pool, self.stride, self.S, spec.H, spec.I, x, spec.k, self.slot_offsets, self.active_slots,
             self.num_active, self.perm_pair, self.y_pairs, self.path, self.ws, stream)
         y_shared = None
         if spec.I_shared:

@@ -158,7 +158,8 @@ def test_workspace_sizes_are_monotone():
 
 
 @pytest.mark.parametrize("fmt,H,I", [(Q.MOE_FMT_Q4K, 512, 256), (Q.MOE_FMT_Q4K, 768, 512), (Q.MOE_FMT_Q8_0, 256, 128),
-                                     (Q.MOE_FMT_Q8_0, 384, 256)])
+                                     (Q.MOE_FMT_Q8_0, 384, 256), (Q.MOE_FMT_MXFP4, 512, 256),
+                                     (Q.MOE_FMT_MXFP4, 768, 512)])
 def test_pack_round_trip(fmt, H, I):
     blob = F.expert_blob(fmt, 5, 0, 1, H, I)
     packed = Q.moe_pack_expert(fmt, blob, H, I)
@@ -185,6 +186,29 @@ def test_pack_places_q4k_fields():
                 byte = canon[16 + (j // 2) * 32 + e]
                 q = (byte >> 4) if j % 2 else (byte & 15)
                 assert (int(words[[0, 2, 1, 3][e // 8]]) >> (4 * (e % 8))) & 15 == q
+
+
+def test_pack_places_mxfp4_fields():
+    """Row r of W_down, block b: its E8M0 byte sits at down tile (r//64, b//8), offset 8*(r%64) + b%8; code
+    element 8d+p of the block in the low nibble of byte p of the dword of group d and 8d+p+4 in its high nibble,
+    groups stored 0, 2, 1, 3, at offset 512 + 1024*(b%8) + 16*(r%64)."""
+    H, I = 512, 512
+    blob = F.expert_blob(Q.MOE_FMT_MXFP4, 3, 0, 0, H, I)
+    packed = Q.moe_pack_expert(Q.MOE_FMT_MXFP4, blob, H, I)
+    rbH, rbI = H // 32 * 17, I // 32 * 17
+    down = 2 * I * rbH
+    base = (I // 64) * (H // 256) * 17408
+    for r, b in [(0, 0), (70, 9), (511, 15)]:
+        canon = blob[down + r * rbI + b * 17: down + r * rbI + (b + 1) * 17]
+        codes = [canon[1 + i] & 15 for i in range(16)] + [canon[1 + i] >> 4 for i in range(16)]
+        tile = base + ((r // 64) * (I // 256) + b // 8) * 8704
+        assert packed[tile + 8 * (r % 64) + b % 8] == canon[0]
+        slot = packed[tile + 512 + 1024 * (b % 8) + 16 * (r % 64): tile + 528 + 1024 * (b % 8) + 16 * (r % 64)]
+        words = slot.view(np.uint32)
+        for e in range(32):
+            d, n = e // 8, e % 8
+            p, half = n % 4, n // 4
+            assert (int(words[[0, 2, 1, 3][d]]) >> (8 * p + 4 * half)) & 15 == codes[e]
 
 
 def test_validate_slot_map():

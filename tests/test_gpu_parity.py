@@ -332,8 +332,11 @@ def _check_layer(wl, got, want, soe, S, tol=DECODE_TOL):
     assert err <= tol
 
 
-@pytest.mark.parametrize("wl", [W.TINY, W.QWEN3_DECODE_T1, W.QWEN3_DECODE_T2],
-                         ids=lambda w: w.name.split(",")[0][:24] + f"-T{w.T}")
+MXFP4_SMALL = W.Workload("small MXFP4 layer (H256 E8 k2 I256 T4)", F.MXFP4, 256, 256, 8, 2, 4)
+
+
+@pytest.mark.parametrize("wl", [W.TINY, W.QWEN3_DECODE_T1, W.QWEN3_DECODE_T2, MXFP4_SMALL, W.QWEN3_MXFP4_DECODE_T2],
+                         ids=lambda w: w.name.split(",")[0][:24] + f"-fmt{w.fmt}-T{w.T}")
 def test_decode_layer_matches_oracle(wl):
     say(f"decode layer {wl.name}")
     got, want, soe, S = _layer_case(wl)
@@ -390,14 +393,14 @@ def test_dsv3_experts_many_tokens_per_slot(dsv3_blobs):
     assert int(np.diff(got["slot_offsets"]).max()) > 2
 
 
-@pytest.mark.parametrize("fmt", [F.Q4K, F.Q8_0])
+@pytest.mark.parametrize("fmt", [F.Q4K, F.Q8_0, F.MXFP4])
 def test_decode_k_split_across_workgroups(fmt):
     """Two experts with a long K (H 7168): too few row tiles to fill the chip,
     so K is split across workgroups too (partial sums finished by the reduce
     kernel), with an uneven last part and a slot holding several chunks of
     tokens."""
-    wl = W.Workload(f"{'Q4_K' if fmt == F.Q4K else 'Q8_0'} layer H 7168, 2 experts, k 1, T 5", fmt, 7168, 256, 2, 1,
-                    5)
+    name = {F.Q4K: "Q4_K", F.Q8_0: "Q8_0", F.MXFP4: "MXFP4"}[fmt]
+    wl = W.Workload(f"{name} layer H 7168, 2 experts, k 1, T 5", fmt, 7168, 256, 2, 1, 5)
     say(wl.name)
     got, want, soe, S = _layer_case(wl, path=Q.MOE_PATH_DECODE)
     _check_layer(wl, got, want, soe, S)
@@ -418,6 +421,29 @@ def test_decode_q8_0_many_tokens():
     soe = np.array([3, -1, 0, 5, -1, 1, 2, -1, 4, 6, -1, 7], dtype=np.int32)
     got, want, soe, S = _layer_case(wl, soe=soe, S=9)
     _check_layer(wl, got, want, soe, S)
+
+
+def test_decode_mxfp4_many_tokens_partial_residency():
+    """MXFP4 experts, 37 tokens over 12 experts, 8 of them resident: chunks of
+    two tokens per slot plus remainders, and a host list."""
+    wl = W.Workload("small MXFP4 layer, 37 tokens, partial residency", F.MXFP4, 512, 256, 12, 4, 37)
+    say(wl.name)
+    soe = np.array([3, -1, 0, 5, -1, 1, 2, -1, 4, 6, -1, 7], dtype=np.int32)
+    got, want, soe, S = _layer_case(wl, soe=soe, S=9, path=Q.MOE_PATH_DECODE)
+    _check_layer(wl, got, want, soe, S)
+    assert got["host_count"] > 0
+
+
+def test_dsv3_sized_mxfp4_experts_many_tokens():
+    """DeepSeek-V3-sized MXFP4 experts (H 7168, I 2048), 16 of them, 24
+    tokens: several K units per wave (the prefetching loop) and several
+    chunks of tokens per slot."""
+    wl = W.Workload("DeepSeek-V3-sized MXFP4 experts, 16 resident, 24 tokens", F.MXFP4, 7168, 2048, 16, 2, 24)
+    say(wl.name)
+    F.set_num_threads(THREADS)
+    got, want, soe, S = _layer_case(wl, path=Q.MOE_PATH_DECODE)
+    _check_layer(wl, got, want, soe, S)
+    assert int(np.diff(got["slot_offsets"]).max()) > 2
 
 
 def test_host_list_written_into_pinned_memory():
