@@ -21,6 +21,8 @@ _SO = os.path.join(_HERE, "libqmoe_fixtures.so")
 Q8_0 = 0
 Q4K = 1
 MXFP4 = 2
+Q3K_Q4K = 3  # mixed expert: Q3_K gate and up, Q4_K down
+Q3K = 4
 
 # Counter-stream tags (the second Philox key word) of the non-weight inputs.
 TAG_X = 0x58000000
@@ -56,6 +58,7 @@ def lib() -> ctypes.CDLL:
         L.fx_encode_q8_0.argtypes = [vp, i64, vp]
         L.fx_encode_q4k.argtypes = [vp, i64, vp]
         L.fx_encode_mxfp4.argtypes = [vp, i64, vp]
+        L.fx_encode_q3k.argtypes = [vp, i64, vp]
         L.fx_matrix_bytes.argtypes = [i32, i64, i64]
         L.fx_matrix_bytes.restype = i64
         L.fx_expert_bytes.argtypes = [i32, i64, i64]
@@ -107,10 +110,11 @@ def encode(fmt: int, x: np.ndarray) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float32)
     cols = x.shape[-1]
     rows = x.size // cols
-    if cols % (256 if fmt == Q4K else 32) != 0:
+    if cols % (256 if fmt in (Q4K, Q3K) else 32) != 0:
         raise ValueError(f"row length {cols} is not a whole number of blocks")
     out = np.empty(lib().fx_matrix_bytes(fmt, rows, cols), dtype=np.uint8)
-    enc = {Q8_0: lib().fx_encode_q8_0, Q4K: lib().fx_encode_q4k, MXFP4: lib().fx_encode_mxfp4}[fmt]
+    enc = {Q8_0: lib().fx_encode_q8_0, Q4K: lib().fx_encode_q4k, MXFP4: lib().fx_encode_mxfp4,
+           Q3K: lib().fx_encode_q3k}[fmt]
     enc(_p(x), x.size, _p(out))
     return out
 

@@ -353,17 +353,77 @@ void fx_encode_mxfp4(const float* x, int64_t n, uint8_t* out) {
     }
 }
 
+/* n floats (n % 256 == 0) -> n/256 Q3_K super-blocks of 110 bytes: 32
+ * bytes of high bits, 64 bytes of 2-bit quants, 12 scale bytes, fp16 d.
+ * Per 16-weight sub-block j: the element of largest magnitude m_j sets the
+ * signed scale s_j = -m_j / 4 (it then encodes as -4); d = fp16(max |s_j| /
+ * 31); sc_j = round(s_j / d) clamped to [-32, 31], stored + 32 in 6 bits;
+ * q = round(x / (d sc_j)) clamped to [-4, 3], stored as q + 4 = low two bits
+ * + 4 * high bit.  Element i: half h = i / 128, group g = (i % 128) / 32,
+ * l = i % 32: low bits at bits 2g of qs[32h + l], high bit at bit 4h + g of
+ * hmask[l].  Scale j: low nibble in byte j (j < 8) or the high nibble of
+ * byte j - 8, top two bits at bit 2 (j / 4) of byte 8 + j % 4. */
+void fx_encode_q3k(const float* x, int64_t n, uint8_t* out) {
+    for (int64_t b = 0; b < n / 256; ++b) {
+        const float* v = x + b * 256;
+        uint8_t* o = out + b * 110;
+        memset(o, 0, 110);
+        float s[16], smax = 0.0f;
+        for (int j = 0; j < 16; ++j) {
+            float m = 0.0f;
+            for (int i = 0; i < 16; ++i)
+                if (fabsf(v[16 * j + i]) > fabsf(m)) m = v[16 * j + i];
+            s[j] = -m / 4.0f;
+            if (fabsf(s[j]) > smax) smax = fabsf(s[j]);
+        }
+        uint16_t dh = fx_f32_to_f16(smax / 31.0f);
+        float df = fx_f16_to_f32(dh);
+        uint8_t* hm = o;
+        uint8_t* qs = o + 32;
+        uint8_t* s12 = o + 96;
+        for (int j = 0; j < 16; ++j) {
+            float r = df > 0.0f ? round_half_away(s[j] / df) : 0.0f;
+            int sc = r < -32.0f ? -32 : (r > 31.0f ? 31 : (int)r);
+            int u = sc + 32;
+            if (j < 8) s12[j] |= (uint8_t)(u & 15);
+            else s12[j - 8] |= (uint8_t)((u & 15) << 4);
+            s12[8 + j % 4] |= (uint8_t)((u >> 4) << (2 * (j / 4)));
+            float step = df * (float)sc;
+            for (int i = 0; i < 16; ++i) {
+                int e = 16 * j + i;
+                float q = step != 0.0f ? round_half_away(v[e] / step) : 0.0f;
+                int qi = q < -4.0f ? -4 : (q > 3.0f ? 3 : (int)q);
+                int w = qi + 4;
+                int h = e / 128, g = (e % 128) / 32, l = e % 32;
+                qs[32 * h + l] |= (uint8_t)((w & 3) << (2 * g));
+                hm[l] |= (uint8_t)((w >> 2) << (4 * h + g));
+            }
+        }
+        put_u16(o + 108, dh);
+    }
+}
+
 /* ------------------------------------------------------------- experts */
 
-enum { FX_Q8_0 = 0, FX_Q4K = 1, FX_MXFP4 = 2 };
+/* Block types; FX_Q3K_Q4K is the mixed expert (Q3_K gate and up, Q4_K down). */
+enum { FX_Q8_0 = 0, FX_Q4K = 1, FX_MXFP4 = 2, FX_Q3K_Q4K = 3, FX_Q3K = 4 };
+
+static int gate_up_fmt(int fmt) { return fmt == FX_Q3K_Q4K ? FX_Q3K : fmt; }
+static int down_fmt(int fmt) { return fmt == FX_Q3K_Q4K ? FX_Q4K : fmt; }
 
 static int64_t row_bytes(int fmt, int64_t cols) {
-    return fmt == FX_Q8_0 ? cols / 32 * 34 : fmt == FX_MXFP4 ? cols / 32 * 17 : cols / 256 * 144;
+    switch (fmt) {
+        case FX_Q8_0: return cols / 32 * 34;
+        case FX_MXFP4: return cols / 32 * 17;
+        case FX_Q3K: return cols / 256 * 110;
+        default: return cols / 256 * 144;
+    }
 }
 
 static void encode_row(int fmt, const float* x, int64_t n, uint8_t* out) {
     if (fmt == FX_Q8_0) fx_encode_q8_0(x, n, out);
     else if (fmt == FX_MXFP4) fx_encode_mxfp4(x, n, out);
+    else if (fmt == FX_Q3K) fx_encode_q3k(x, n, out);
     else fx_encode_q4k(x, n, out);
 }
 
@@ -372,7 +432,7 @@ int64_t fx_matrix_bytes(int fmt, int64_t rows, int64_t cols) { return rows * row
 /* Canonical expert blob = W_gate [I x H] | W_up [I x H] | W_down [H x I],
  * every matrix row-major with blocks along its input dimension. */
 int64_t fx_expert_bytes(int fmt, int64_t H, int64_t I) {
-    return 2 * fx_matrix_bytes(fmt, I, H) + fx_matrix_bytes(fmt, H, I);
+    return 2 * fx_matrix_bytes(gate_up_fmt(fmt), I, H) + fx_matrix_bytes(down_fmt(fmt), H, I);
 }
 
 /* One seeded matrix: element (r, c) ~ N(0, std) from counter (chunk, r, expert, layer),
@@ -394,10 +454,10 @@ static void gen_matrix(int fmt, uint32_t seed, uint32_t layer, uint32_t expert, 
 
 void fx_gen_expert(int fmt, uint32_t seed, uint32_t layer, uint32_t expert, int64_t H, int64_t I, float std,
                    uint8_t* out) {
-    int64_t gb = fx_matrix_bytes(fmt, I, H);
-    gen_matrix(fmt, seed, layer, expert, 0, I, H, std, out);
-    gen_matrix(fmt, seed, layer, expert, 1, I, H, std, out + gb);
-    gen_matrix(fmt, seed, layer, expert, 2, H, I, std, out + 2 * gb);
+    int64_t gb = fx_matrix_bytes(gate_up_fmt(fmt), I, H);
+    gen_matrix(gate_up_fmt(fmt), seed, layer, expert, 0, I, H, std, out);
+    gen_matrix(gate_up_fmt(fmt), seed, layer, expert, 1, I, H, std, out + gb);
+    gen_matrix(down_fmt(fmt), seed, layer, expert, 2, H, I, std, out + 2 * gb);
 }
 
 /* Several experts at once, one parallel loop over every row of every matrix:
@@ -406,8 +466,8 @@ void fx_gen_expert(int fmt, uint32_t seed, uint32_t layer, uint32_t expert, int6
 void fx_gen_experts(int fmt, uint32_t seed, uint32_t layer, const int32_t* experts, int n, int64_t H, int64_t I,
                     float std, uint8_t* out) {
     int64_t eb = fx_expert_bytes(fmt, H, I);
-    int64_t gb = fx_matrix_bytes(fmt, I, H);
-    int64_t rbH = row_bytes(fmt, H), rbI = row_bytes(fmt, I);
+    int64_t gb = fx_matrix_bytes(gate_up_fmt(fmt), I, H);
+    int64_t rbH = row_bytes(gate_up_fmt(fmt), H), rbI = row_bytes(down_fmt(fmt), I);
     int64_t rows_per_expert = 2 * I + H;
     int64_t total = (int64_t)n * rows_per_expert;
 #pragma omp parallel
@@ -421,7 +481,7 @@ void fx_gen_experts(int fmt, uint32_t seed, uint32_t layer, const int32_t* exper
             int64_t cols = matrix == 2 ? I : H;
             uint8_t* dst = out + i * eb + (matrix == 2 ? 2 * gb + row * rbI : matrix * gb + row * rbH);
             normal_row(seed, 0x57000000u | matrix, (uint32_t)row, (uint32_t)experts[i], layer, 0.0f, std, buf, cols);
-            encode_row(fmt, buf, cols, dst);
+            encode_row(matrix == 2 ? down_fmt(fmt) : gate_up_fmt(fmt), buf, cols, dst);
         }
         free(buf);
     }

@@ -31,7 +31,9 @@ enum {
     D_Q4K_NIBBLE_SWAP = 11,    /* even sub-blocks read the high nibbles */
     D_IGNORE_RESIDENCY = 12,   /* combine adds non-resident pairs too */
     D_MXFP4_INTERLEAVED = 13,  /* MXFP4 elements read as consecutive nibble pairs */
-    D_MXFP4_BIAS_128 = 14      /* MXFP4 scale exponent bias 128 instead of 127 */
+    D_MXFP4_BIAS_128 = 14,     /* MXFP4 scale exponent bias 128 instead of 127 */
+    D_Q3K_SCALE_UNBIASED = 15, /* Q3_K 6-bit scales used without the -32 */
+    D_Q3K_HMASK_INVERTED = 16  /* Q3_K high bit read with the opposite sense */
 };
 
 void oracle_set_threads(int n) {
@@ -150,15 +152,61 @@ void oracle_dequant_mxfp4(const uint8_t* blocks, int64_t n, double* out) {
     }
 }
 
+/* 6-bit scale of sub-block j (0..15) from the 12 packed bytes: low four
+ * bits from byte j (j < 8) or the high nibble of byte j - 8 (j >= 8); top two
+ * bits from byte 8 + j % 4, at bit 2 * (j / 4). */
+static int q3k_scale(const uint8_t* s12, int j) {
+    int lo = j < 8 ? (s12[j] & 15) : (s12[j - 8] >> 4);
+    int hi = (s12[8 + j % 4] >> (2 * (j / 4))) & 3;
+    return lo | (hi << 4);
+}
+
+/* Q3_K super-block (110 bytes): 32 bytes of high bits (hmask), 64 bytes of
+ * 2-bit quants (qs), 12 scale bytes, fp16 d.  Element i: half h = i / 128,
+ * group g = (i % 128) / 32, l = i % 32; its low two bits are bits 2g..2g+1 of
+ * qs[32h + l], its high bit is bit 4h + g of hmask[l]; q = low + 4 * high - 4
+ * (in -4..3).  Sub-block j = i / 16 has the 6-bit scale sc_j.
+ * w = d * (sc_j - 32) * q.
+ * Parity pinned by hand-built golden blocks and the encoder round trip. */
+void oracle_dequant_q3k(const uint8_t* blocks, int64_t n, double* out) {
+    for (int64_t b = 0; b < n / 256; ++b) {
+        const uint8_t* blk = blocks + b * 110;
+        const uint8_t* hm = blk;
+        const uint8_t* qs = blk + 32;
+        const uint8_t* s12 = blk + 96;
+        double d = half_le(blk + 108);
+        for (int i = 0; i < 256; ++i) {
+            int h = i / 128, g = (i % 128) / 32, l = i % 32;
+            int low = (qs[32 * h + l] >> (2 * g)) & 3;
+            int high = (hm[l] >> (4 * h + g)) & 1;
+            if (g_defect == D_Q3K_HMASK_INVERTED) high = 1 - high;
+            int q = low + 4 * high - 4;
+            int sc = q3k_scale(s12, i / 16) - (g_defect == D_Q3K_SCALE_UNBIASED ? 0 : 32);
+            out[b * 256 + i] = d * (double)sc * (double)q;
+        }
+    }
+}
+
 static void dequant_row(int fmt, const uint8_t* row, int64_t n, double* out) {
     if (fmt == ORACLE_Q8_0) oracle_dequant_q8_0(row, n, out);
     else if (fmt == ORACLE_MXFP4) oracle_dequant_mxfp4(row, n, out);
+    else if (fmt == ORACLE_Q3K) oracle_dequant_q3k(row, n, out);
     else oracle_dequant_q4k(row, n, out);
 }
 
 static int64_t row_bytes(int fmt, int64_t cols) {
-    return fmt == ORACLE_Q8_0 ? cols / 32 * 34 : fmt == ORACLE_MXFP4 ? cols / 32 * 17 : cols / 256 * 144;
+    switch (fmt) {
+        case ORACLE_Q8_0: return cols / 32 * 34;
+        case ORACLE_MXFP4: return cols / 32 * 17;
+        case ORACLE_Q3K: return cols / 256 * 110;
+        default: return cols / 256 * 144;
+    }
 }
+
+/* Block types of an expert's gate/up and down matrices: one type for both,
+ * except the mixed expert (Q3_K gate and up, Q4_K down). */
+static int gate_up_fmt(int fmt) { return fmt == ORACLE_Q3K_Q4K ? ORACLE_Q3K : fmt; }
+static int down_fmt(int fmt) { return fmt == ORACLE_Q3K_Q4K ? ORACLE_Q4K : fmt; }
 
 /* ------------------------------------------------------------- routing */
 
@@ -258,7 +306,8 @@ static double silu(double z) { return z / (1.0 + exp(-z)); }
 /* g = Wg x, u = Wu x (Wg, Wu: I rows of H), h = silu(g) * u, y = Wd h (Wd: H rows of I).
  * Parity pinned against dense matrix products on exactly representable weights. */
 void oracle_expert_ffn(int fmt, const uint8_t* blob, int H, int I, const double* x, double* y) {
-    int64_t rb_h = row_bytes(fmt, H), rb_i = row_bytes(fmt, I);
+    const int fgu = gate_up_fmt(fmt), fdn = down_fmt(fmt);
+    int64_t rb_h = row_bytes(fgu, H), rb_i = row_bytes(fdn, I);
     const uint8_t* wg = blob;
     const uint8_t* wu = blob + (int64_t)I * rb_h;
     const uint8_t* wd = blob + 2 * (int64_t)I * rb_h;
@@ -274,16 +323,16 @@ void oracle_expert_ffn(int fmt, const uint8_t* blob, int H, int I, const double*
 #pragma omp for schedule(static)
         for (int i = 0; i < I; ++i) {
             double g = 0.0, u = 0.0;
-            dequant_row(fmt, wg + (int64_t)i * rb_h, H, row);
+            dequant_row(fgu, wg + (int64_t)i * rb_h, H, row);
             for (int c = 0; c < H; ++c) g += row[c] * x[c];
-            dequant_row(fmt, wu + (int64_t)i * rb_h, H, row);
+            dequant_row(fgu, wu + (int64_t)i * rb_h, H, row);
             for (int c = 0; c < H; ++c) u += row[c] * x[c];
             h[i] = (g_defect == D_SWIGLU_SWAP) ? silu(u) * g : silu(g) * u;
         }
 #pragma omp for schedule(static)
         for (int r = 0; r < H; ++r) {
             double acc = 0.0;
-            dequant_row(fmt, wd + (int64_t)r * rb_i, I, row);
+            dequant_row(fdn, wd + (int64_t)r * rb_i, I, row);
             for (int c = 0; c < I; ++c) acc += row[c] * h[c];
             y[r] = acc;
         }

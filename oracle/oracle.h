@@ -10,6 +10,10 @@
  *   dequantize  Q8_0:  w = d*q                      (32 weights per block)
  *               Q4_K:  w = d*sc_j*q - dmin*m_j      (256 per super-block, 8
  *                                                    sub-blocks j of 32)
+ *               Q3_K:  w = d*(sc_j - 32)*q           (256 per super-block, 16
+ *                                                    sub-blocks of 16, q in -4..3;
+ *                                                    the mixed expert's gate/up:
+ *                                                    README 0.3.11, limits list)
  *               MXFP4: w = 2^(X-127) * fp4(q)        (32 per block; OCP MX v1.0
  *                                                    E8M0 scale, E2M1 elements;
  *                                                    card expert type: README
@@ -43,13 +47,15 @@
 extern "C" {
 #endif
 
-enum { ORACLE_Q8_0 = 0, ORACLE_Q4K = 1, ORACLE_MXFP4 = 2 };
+/* Block types; ORACLE_Q3K_Q4K is the mixed expert: Q3_K gate and up, Q4_K down. */
+enum { ORACLE_Q8_0 = 0, ORACLE_Q4K = 1, ORACLE_MXFP4 = 2, ORACLE_Q3K_Q4K = 3, ORACLE_Q3K = 4 };
 enum { ORACLE_SOFTMAX = 0, ORACLE_SIGMOID = 1 };
 
 /* Dequantize n weights (n a multiple of the block size) from stored blocks. */
 void oracle_dequant_q8_0(const uint8_t* blocks, int64_t n, double* out);
 void oracle_dequant_q4k(const uint8_t* blocks, int64_t n, double* out);
 void oracle_dequant_mxfp4(const uint8_t* blocks, int64_t n, double* out);
+void oracle_dequant_q3k(const uint8_t* blocks, int64_t n, double* out);
 
 /* Top-k routing of T rows of E logits.  Returns 0, or -1 on bad sizes. */
 int oracle_route(const float* logits, int T, int E, int k, int score, int renormalize, double scale,

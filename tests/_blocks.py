@@ -88,10 +88,49 @@ def random_mxfp4_matrix(rng: np.random.Generator, rows: int, cols: int):
     return np.frombuffer(b"".join(parts), dtype=np.uint8).copy(), dense
 
 
+def q3k_superblock(d_bits: int, sc, q) -> bytes:
+    """sc: 16 ints in -32..31; q: 256 ints in -4..3 (stored + 32 / + 4; high bits, low bits, scales, d)."""
+    hm, qs, s12 = [0] * 32, [0] * 64, [0] * 12
+    for i in range(256):
+        u = int(q[i]) + 4
+        h, g, l = i // 128, (i % 128) // 32, i % 32
+        qs[32 * h + l] |= (u & 3) << (2 * g)
+        hm[l] |= (u >> 2) << (4 * h + g)
+    for j in range(16):
+        u = int(sc[j]) + 32
+        if j < 8:
+            s12[j] |= u & 15
+        else:
+            s12[j - 8] |= (u & 15) << 4
+        s12[8 + j % 4] |= (u >> 4) << (2 * (j // 4))
+    return bytes(hm + qs + s12 + [d_bits & 0xFF, d_bits >> 8])
+
+
+def q3k_scale(s12, j: int) -> int:
+    """Stored (unsigned) 6-bit scale j of a Q3_K block's 12 scale bytes."""
+    lo = (int(s12[j]) & 15) if j < 8 else (int(s12[j - 8]) >> 4)
+    return lo | (((int(s12[8 + j % 4]) >> (2 * (j // 4))) & 3) << 4)
+
+
+def random_q3k_matrix(rng: np.random.Generator, rows: int, cols: int, d_bits: int = 0x2000):
+    """A Q3_K matrix with random signed scales and quants; returns (bytes, exact dense values)."""
+    d = half_bits_value(d_bits)
+    dense = np.empty((rows, cols), dtype=np.float64)
+    parts = []
+    for r in range(rows):
+        for sb in range(cols // 256):
+            sc = rng.integers(-32, 32, size=16)
+            q = rng.integers(-4, 4, size=256)
+            parts.append(q3k_superblock(d_bits, sc, q))
+            dense[r, sb * 256:(sb + 1) * 256] = d * np.repeat(sc, 16) * q
+    return np.frombuffer(b"".join(parts), dtype=np.uint8).copy(), dense
+
+
 def random_expert(rng: np.random.Generator, fmt: int, H: int, I: int):
-    """Canonical blob Wg|Wu|Wd with exactly known dense matrices."""
-    make = {0: random_q8_0_matrix, 1: random_q4k_matrix, 2: random_mxfp4_matrix}[fmt]
-    bg, g = make(rng, I, H)
-    bu, u = make(rng, I, H)
-    bd, dn = make(rng, H, I)
+    """Canonical blob Wg|Wu|Wd with exactly known dense matrices (fmt 3: Q3_K gate/up, Q4_K down)."""
+    make_gu = {0: random_q8_0_matrix, 1: random_q4k_matrix, 2: random_mxfp4_matrix, 3: random_q3k_matrix}[fmt]
+    make_dn = random_q4k_matrix if fmt == 3 else make_gu
+    bg, g = make_gu(rng, I, H)
+    bu, u = make_gu(rng, I, H)
+    bd, dn = make_dn(rng, H, I)
     return np.concatenate([bg, bu, bd]), (g, u, dn)

@@ -8,6 +8,8 @@ computed here with exact rational arithmetic from the block formula:
     Q4_K:  w = d * sc_j * q - dmin * m_j   (fp16 d and dmin, eight 6-bit
                                             (sc, m) pairs, 4-bit q)
     MXFP4: w = 2^(X - 127) * fp4(q)        (E8M0 scale X, 32 E2M1 codes)
+    Q3_K:  w = d * sc_j * q                (fp16 d, sixteen signed 6-bit sc_j,
+                                            q in -4..3)
 
 Stored types: bloomery README of 2026-09-24 (shared experts kept in Q8_0)
 and bloomery README 0.3.1 ("Status (0.3.1)" table, "Quant types" row: card
@@ -93,6 +95,37 @@ def mxfp4_case(name: str, x_bits: int, codes: list[int], note: str) -> dict:
                 expected=[frac_str(v) for v in expected])
 
 
+def q3k_case(name: str, d_bits: int, sc: list[int], q: list[int], note: str) -> dict:
+    """One Q3_K super-block from its fields: 16 signed scales sc_j in -32..31
+    (stored + 32 in six bits) and 256 quants q in -4..3 (stored q + 4: two low
+    bits and one high bit).  Byte order as read for this build: 32 bytes of
+    high bits (element i = 128h + 32g + l: bit 4h + g of byte l), 64 bytes of
+    low bits (bits 2g of byte 32h + l), 12 scale bytes (scale j: low nibble of
+    byte j for j < 8, high nibble of byte j - 8 otherwise; top two bits at bit
+    2 (j / 4) of byte 8 + j % 4), fp16 d last."""
+    assert len(sc) == 16 and len(q) == 256
+    assert all(-32 <= v <= 31 for v in sc) and all(-4 <= v <= 3 for v in q)
+    hm, qs, s12 = [0] * 32, [0] * 64, [0] * 12
+    for i, v in enumerate(q):
+        u = v + 4
+        h, g, l = i // 128, (i % 128) // 32, i % 32
+        qs[32 * h + l] |= (u & 3) << (2 * g)
+        hm[l] |= (u >> 2) << (4 * h + g)
+    for j, v in enumerate(sc):
+        u = v + 32
+        if j < 8:
+            s12[j] |= u & 15
+        else:
+            s12[j - 8] |= (u & 15) << 4
+        s12[8 + j % 4] |= (u >> 4) << (2 * (j // 4))
+    raw = hm + qs + s12 + [d_bits & 0xFF, d_bits >> 8]
+    assert len(raw) == 110
+    d = half_value(d_bits)
+    expected = [d * sc[i // 16] * q[i] for i in range(256)]
+    return dict(name=name, format="Q3_K", note=note, d_bits=d_bits, sc=sc, q=q, bytes_hex=bytes(raw).hex(),
+                expected=[frac_str(v) for v in expected])
+
+
 def main() -> None:
     cases = []
     cases.append(q8_0_case(
@@ -126,13 +159,21 @@ def main() -> None:
         "mxfp4_min_scale", 0, [(5 * i + 1) % 16 for i in range(32)], "scale 2^-127, the smallest E8M0 value"))
     cases.append(mxfp4_case(
         "mxfp4_max_scale", 254, [(3 * i) % 16 for i in range(32)], "scale 2^127, the largest finite E8M0 value"))
+    cases.append(q3k_case(
+        "q3k_every_field", 0x3C00, [-32, 31, -1, 0, 1, 17, -17, 5, -5, 30, -30, 8, -8, 12, -12, 3],
+        [((7 * i + i // 16) % 8) - 4 for i in range(256)],
+        "d = 1; scales span -32..31 at all 16 positions; every q value in every sub-block"))
+    cases.append(q3k_case(
+        "q3k_high_bits", 0x2C00, [(5 * j) % 64 - 32 for j in range(16)], [3 if i % 3 else -4 for i in range(256)],
+        "d = 1/16; q alternates between the extremes 3 and -4 (high bit set / clear)"))
     doc = dict(
         citation=("Stored block types: bloomery README of 2026-09-24 (shared experts in Q8_0) and bloomery README "
                   "0.3.1, 'Status (0.3.1)' table, 'Quant types' row (card experts in Q4_K to Q6_K and MXFP4); "
                   "block formulas of the problem statement; Q4_K byte order as read for this build (GGUF order); "
                   "MXFP4 element and scale encodings of the OCP Microscaling Formats (MX) v1.0 specification, "
                   "byte order as read for this build (scale byte, then elements 0-15 in low nibbles, 16-31 in "
-                  "high nibbles)."),
+                  "high nibbles); Q3_K (bloomery README 0.3.11, limits list: the V4.1 card experts' gate and up "
+                  "matrices) in the GGUF order as read for this build."),
         derivation="expected[i] written by tests/golden/make_golden.py with exact rationals from the listed fields",
         cases=cases)
     with open(os.path.join(HERE, "quant_blocks.json"), "w") as f:

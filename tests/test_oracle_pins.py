@@ -35,7 +35,7 @@ def pin_golden_blocks() -> bool:
     ok = True
     for case in doc["cases"]:
         raw = np.frombuffer(bytes.fromhex(case["bytes_hex"]), dtype=np.uint8)
-        fmt = {"Q8_0": O.Q8_0, "Q4_K": O.Q4K, "MXFP4": O.MXFP4}[case["format"]]
+        fmt = {"Q8_0": O.Q8_0, "Q4_K": O.Q4K, "MXFP4": O.MXFP4, "Q3_K": O.Q3K}[case["format"]]
         got = O.dequant(fmt, raw, len(case["expected"]))
         want = np.array([float(Fraction(v)) for v in case["expected"]])
         ok &= bool(np.array_equal(got, want))
@@ -73,6 +73,17 @@ def pin_encoder_round_trip() -> bool:
     s = np.ldexp(1.0, raw[::17].astype(np.int64) - 127).reshape(64, -1)
     ok &= bool(np.all(np.abs(got - w) <= np.repeat(s, 32, axis=1)))
     ok &= bool(np.all(np.abs(w).reshape(64, -1, 32).max(axis=2) <= 6 * s))
+    ok &= bool(np.corrcoef(got.ravel(), w.ravel())[0, 1] > 0.95)
+    # Q3_K: the step d*sc_j of sub-block j maps its largest element to -4 up
+    # to scale rounding (half a d) and clamping at 3; every weight lies within
+    # |d sc_j| + 2.5 d of its value (d: the super-block's fp16 scale).
+    raw = F.encode(O.Q3K, w.astype(np.float32))
+    got = O.dequant(O.Q3K, raw, w.size).reshape(w.shape)
+    blk = raw.reshape(-1, 110)
+    d = np.array([B.half_bits_value(int(b[108]) | (int(b[109]) << 8)) for b in blk])
+    sc = np.array([[B.q3k_scale(b[96:108], j) - 32 for j in range(16)] for b in blk])
+    bound = np.repeat((np.abs(sc) * d[:, None] * 1.001 + 2.5 * d[:, None]).reshape(-1), 16).reshape(w.shape)
+    ok &= bool(np.all(np.abs(got - w) <= bound + 1e-12))
     ok &= bool(np.corrcoef(got.ravel(), w.ravel())[0, 1] > 0.95)
     return ok
 
@@ -133,7 +144,7 @@ def _dense_ffn(g, u, dn, x):
 
 def pin_ffn_dense(fmt: int) -> bool:
     rng = np.random.default_rng(17 + fmt)
-    H, I = {O.Q4K: (512, 256), O.Q8_0: (96, 64), O.MXFP4: (128, 96)}[fmt]
+    H, I = {O.Q4K: (512, 256), O.Q8_0: (96, 64), O.MXFP4: (128, 96), O.Q3K_Q4K: (512, 256)}[fmt]
     blob, (g, u, dn) = B.random_expert(rng, fmt, H, I)
     x = rng.normal(size=H)
     got = O.expert_ffn(fmt, blob, H, I, x)
@@ -232,6 +243,7 @@ PINS = {
     "ffn_dense_q8_0": lambda: pin_ffn_dense(O.Q8_0),
     "ffn_dense_q4k": lambda: pin_ffn_dense(O.Q4K),
     "ffn_dense_mxfp4": lambda: pin_ffn_dense(O.MXFP4),
+    "ffn_dense_q3k_q4k": lambda: pin_ffn_dense(O.Q3K_Q4K),
     "layer_brute_softmax_partial": lambda: pin_layer_brute_force(O.SOFTMAX, True),
     "layer_brute_sigmoid_full": lambda: pin_layer_brute_force(O.SIGMOID, False),
     "disjoint_halves": pin_disjoint_halves,
@@ -274,6 +286,11 @@ DEFECTS = [
     (13, "encoder_round_trip"),
     (14, "golden_blocks"),                 # MXFP4 scale bias 128
     (14, "ffn_dense_mxfp4"),
+    (15, "golden_blocks"),                 # Q3_K scales without the -32
+    (15, "ffn_dense_q3k_q4k"),
+    (16, "golden_blocks"),                 # Q3_K high bit inverted
+    (16, "ffn_dense_q3k_q4k"),
+    (16, "encoder_round_trip"),
 ]
 
 
