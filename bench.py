@@ -222,7 +222,7 @@ def main():
     del pools, pool0
     torch.cuda.empty_cache()
     dsv3 = bench_dsv3(args, threads) if args.dsv3_steps > 0 else None
-    mxfp4 = bench_mxfp4(args, threads) if args.dsv3_steps > 0 else None
+    formats = bench_formats(args, threads) if args.dsv3_steps > 0 else None
     stack = bench_stack(args, threads) if args.stack_replays > 0 else None
 
     traffic = read_traffic()
@@ -251,7 +251,7 @@ def main():
         "cpu_baseline": cpu,
         "prefill": prefill,
         "dsv3_decode": dsv3,
-        "mxfp4_decode": mxfp4,
+        "formats_decode": formats,
         "stack": stack,
         "kernels_us": {k2: round(v["avg_us"], 3) for k2, v in kern.items()},
         "down_gemv_GBs": round(dn_gbs, 1),
@@ -447,12 +447,14 @@ def bench_dsv3(args, threads: int) -> dict:
     return res
 
 
-def bench_mxfp4(args, threads: int) -> dict:
-    """The decode layers with MXFP4 routed experts (17 bytes per 32 weights):
-    Qwen3-shaped at T = 2 (8 pool copies rotated, 2.6 GB, so a step's experts
-    come from HBM), its gate/up GEMV against the HBM peak; DeepSeek-V3-shaped
-    at T = 2 with its Q8_0 shared expert (one 6 GB pool).  Graph-replayed like
-    the other decode layers."""
+def bench_formats(args, threads: int) -> dict:
+    """The decode layers with the other card expert types: MXFP4 (17 bytes per
+    32 weights) Qwen3-shaped at T = 2 (8 pool copies rotated, 2.6 GB, so a
+    step's experts come from HBM), its gate/up GEMV against the HBM peak, and
+    DeepSeek-V3-shaped at T = 2 with the Q8_0 shared expert (one 6 GB pool);
+    the DeepSeek-V3-shaped layer with the mixed experts of the engine's V4.1
+    files (Q3_K gate/up, Q4_K down).  Graph-replayed like the other decode
+    layers."""
     import numpy as np
     import torch
 
@@ -463,13 +465,19 @@ def bench_mxfp4(args, threads: int) -> dict:
     from quantized_routed_expert_moe_amd.layer import LayerSpec, MoELayer
 
     res = {}
-    for key, wl, copies in (("qwen3_T2", W.QWEN3_MXFP4_DECODE_T2, 8), ("dsv3_T2", W.DSV3_MXFP4_DECODE_T2, 1)):
+    def gateup_bytes(wl) -> int:  # stored bytes of one expert's gate and up matrices
+        w = 2 * wl.H * wl.I
+        return {F.MXFP4: w // 32 * 17, F.Q3K_Q4K: w // 256 * 110, F.Q4K: w // 256 * 144}[wl.fmt]
+
+    for key, wl, copies in (("mxfp4_qwen3_T2", W.QWEN3_MXFP4_DECODE_T2, 8), ("mxfp4_dsv3_T2", W.DSV3_MXFP4_DECODE_T2, 1),
+                            ("q3k_q4k_dsv3_T2", W.DSV3_Q3K_DECODE_T2, 1)):
         blobs = W.expert_blobs(wl)
         nb = Q.moe_expert_blob_bytes(wl.fmt, wl.H, wl.I)
-        stride = (nb + 255) // 256 * 256
+        npk = Q.moe_packed_blob_bytes(wl.fmt, wl.H, wl.I)
+        stride = (npk + 255) // 256 * 256
         host = np.zeros((wl.E, stride), dtype=np.uint8)
         with ThreadPoolExecutor(threads) as ex:
-            list(ex.map(lambda e: Q.moe_pack_expert(wl.fmt, blobs[e], wl.H, wl.I, out=host[e, :nb]), range(wl.E)))
+            list(ex.map(lambda e: Q.moe_pack_expert(wl.fmt, blobs[e], wl.H, wl.I, out=host[e, :npk]), range(wl.E)))
         del blobs
         pools = [torch.from_numpy(host).cuda() for _ in range(copies)]
         del host
@@ -516,22 +524,23 @@ def bench_mxfp4(args, threads: int) -> dict:
         mean_uniq = float(np.mean([uniq[i % nbatch] for i in range(steps)]))
         layer_bytes = mean_uniq * nb + shared_bytes
         r = {"workload": wl.name, "tokens_per_s": round(wl.T / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 4),
-             "unique_experts_per_step": round(mean_uniq, 2), "expert_bytes": nb,
+             "unique_experts_per_step": round(mean_uniq, 2), "expert_bytes": nb, "packed_bytes": npk,
              "layer_bytes_per_step": round(layer_bytes),
              "layer_GBs": round(layer_bytes / (ms_step * 1e-3) / 1e9, 1),
              "layer_frac_of_hbm": round(layer_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
              "pool_copies": copies}
         if not wl.I_shared:  # stage 3 then times only the routed gate/up GEMV
             gu_us = 1e3 * gu_ms / max(gu_n, 1)
-            gbytes = mean_uniq * 2 * wl.H * wl.I // 32 * 17
+            gbytes = mean_uniq * gateup_bytes(wl)
             r["gateup"] = {"avg_launch_us": round(gu_us, 3), "algorithmic_bytes_per_launch": round(gbytes),
                            "GBs": round(gbytes / (gu_us * 1e-6) / 1e9, 1),
                            "frac_of_hbm": round(gbytes / (gu_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         res[key] = r
         del graphs, layer, pools, shared
         torch.cuda.empty_cache()
-    res["note"] = ("MXFP4 codes converted to fp16 by the hardware FP4 conversion, fp16 x fp16 dot products, fp32 "
-                   "accumulate, each 32-weight block scaled by its E8M0 power of two; same kernels as Q4_K otherwise")
+    res["note"] = ("MXFP4 codes converted to fp16 by the hardware FP4 conversion, Q3_K quants by two and-or "
+                   "operations per fp16 pair; fp16 x fp16 dot products, fp32 accumulate; expert_bytes and layer bytes "
+                   "count the stored (canonical) bytes")
     return res
 
 

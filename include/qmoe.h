@@ -16,7 +16,8 @@
  *                             sizes)
  *   moe_expert_ffn_q4k /      dequantize + SwiGLU expert FFN over each slot's
  *   moe_expert_ffn_q8_0 /     batch (decode GEMV or prefill MFMA GEMM)
- *   moe_expert_ffn_mxfp4
+ *   moe_expert_ffn_mxfp4 /
+ *   moe_expert_ffn_q3k_q4k
  *   moe_combine               weighted sum of the pairs (+ shared expert)
  *
  * Conventions for every call:
@@ -58,7 +59,12 @@ typedef enum moe_status {
 typedef enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
 typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 typedef enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 } moe_path;
-typedef enum moe_format { MOE_FMT_Q8_0 = 0, MOE_FMT_Q4K = 1, MOE_FMT_MXFP4 = 2 } moe_format;
+typedef enum moe_format {
+    MOE_FMT_Q8_0 = 0,
+    MOE_FMT_Q4K = 1,
+    MOE_FMT_MXFP4 = 2,
+    MOE_FMT_Q3K_Q4K = 3 /* mixed expert: Q3_K gate and up, Q4_K down */
+} moe_format;
 
 /* Limits checked by the calls below. */
 #define MOE_MAX_EXPERTS 1024 /* E */
@@ -192,15 +198,32 @@ moe_status moe_count_routes(const int32_t* topk_ids, int T, int k, int E, uint32
  *        16 + i in its high nibble;                  w = 2^(X - 127) * fp4(q)
  *        (fp4: sign bit 3, exponent bits 2-1 with bias 1, mantissa bit 0:
  *        +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}; X = 255 is NaN).
+ *   Q3_K (110 B / 256 weights): 32 B of high bits, 64 B of 2-bit quants,
+ *        12 B of 6-bit scales for 16 sub-blocks of 16, fp16 d; element i
+ *        (half h = i/128, group g = (i%128)/32, l = i%32): low bits at bits
+ *        2g of quant byte 32h + l, high bit at bit 4h + g of high-bit byte l;
+ *        q = low + 4*high - 4; scale j: low four bits from byte j (j < 8) or
+ *        the high nibble of byte j - 8, top two bits at bit 2*(j/4) of byte
+ *        8 + j%4;                                     w = d*(sc_j - 32)*q.
+ *   MOE_FMT_Q3K_Q4K is the mixed expert DeepSeek-V4.1-class files put on the
+ *        card (bloomery README 0.3.11, limits list: V4.1's card experts are
+ *        Q3_K gate and up with a Q4_K down): W_gate and W_up in Q3_K, W_down
+ *        in Q4_K.
  * Canonical blob = W_gate | W_up | W_down, each row-major.
  *
- * Supported shapes: Q4_K and MXFP4 need H % 256 == 0 and I % 256 == 0; Q8_0
- * needs H % 128 == 0 and I % 128 == 0.
+ * Supported shapes: Q4_K, MXFP4 and Q3_K/Q4_K need H % 256 == 0 and
+ * I % 256 == 0; Q8_0 needs H % 128 == 0 and I % 128 == 0.
  */
 size_t moe_expert_blob_bytes(int format, int H, int I);
 
-/* Host, synchronous: canonical blob -> packed blob (both host memory,
- * moe_expert_blob_bytes bytes each, not overlapping). */
+/* Bytes of a packed blob (what a slot must hold): moe_expert_blob_bytes for
+ * every format but MOE_FMT_Q3K_Q4K, whose Q3_K rows take 112 bytes per 256
+ * inputs packed (a 16-byte header for the 14 bytes of scales and d).  0 for
+ * an unsupported format or shape. */
+size_t moe_packed_blob_bytes(int format, int H, int I);
+
+/* Host, synchronous: canonical blob (moe_expert_blob_bytes) -> packed blob
+ * (moe_packed_blob_bytes), both host memory, not overlapping. */
 moe_status moe_pack_expert(int format, const void* canonical, void* packed, int H, int I);
 
 /* Host, synchronous: packed blob -> canonical blob (the exact inverse). */
@@ -219,7 +242,7 @@ moe_status moe_validate_slot_map(const int32_t* slot_of_expert, int E, int S);
  * prompts"; README 0.3.1, "Why it is fast": prompts as tensor-core GEMMs).
  *
  * slot_pool     device: S packed blobs at slot_pool + s * slot_stride;
- *               16-byte aligned.  slot_stride >= moe_expert_blob_bytes and a
+ *               16-byte aligned.  slot_stride >= moe_packed_blob_bytes and a
  *               multiple of 16.
  * S             slots, 1..MOE_MAX_EXPERTS (the S given to the batches call).
  * H, I          hidden and expert-intermediate sizes.
@@ -232,12 +255,13 @@ moe_status moe_validate_slot_map(const int32_t* slot_of_expert, int E, int S);
  * path          MOE_PATH_DECODE: GEMV, fp16 activations in fp32-accumulated
  *               dot products, y_pairs MOE_F32 (MXFP4: each code converted
  *               exactly to fp16 by the hardware FP4 conversion, the block's
- *               dot product then scaled by 2^(X - 127) in fp32).
+ *               dot product then scaled by 2^(X - 127) in fp32; Q3_K: each
+ *               16-element sub-block's dot product scaled by d (sc_j - 32)).
  *               MOE_PATH_PREFILL (Q4_K only): bf16 x, weights dequantized to
  *               bf16 tiles, bf16 MFMA with fp32 accumulate, h rounded to bf16;
  *               y_pairs MOE_F32 or MOE_BF16.
  *               MOE_PATH_AUTO: PREFILL for Q4_K with bf16 x when T > 32, else
- *               DECODE (always DECODE for Q8_0 and MXFP4).
+ *               DECODE (always DECODE for the other formats).
  * ws, ws_bytes  device workspace, at least moe_ffn_workspace_size(format, T,
  *               k, H, I, path).
  *
@@ -258,6 +282,10 @@ moe_status moe_expert_ffn_mxfp4(const void* slot_pool, size_t slot_stride, int S
                                 int x_dtype, int T, int k, const int32_t* slot_offsets, const int32_t* active_slots,
                                 const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype,
                                 int path, void* ws, size_t ws_bytes, void* stream);
+moe_status moe_expert_ffn_q3k_q4k(const void* slot_pool, size_t slot_stride, int S, int H, int I, const void* x,
+                                  int x_dtype, int T, int k, const int32_t* slot_offsets, const int32_t* active_slots,
+                                  const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype,
+                                  int path, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- combine
  * y[t] = sum over j < k, in j order, of [slot_of_expert[id] >= 0] *

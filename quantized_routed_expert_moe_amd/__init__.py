@@ -22,7 +22,7 @@ MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMA
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_F32, MOE_BF16 = 0, 1
 MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL = 0, 1, 2
-MOE_FMT_Q8_0, MOE_FMT_Q4K, MOE_FMT_MXFP4 = 0, 1, 2
+MOE_FMT_Q8_0, MOE_FMT_Q4K, MOE_FMT_MXFP4, MOE_FMT_Q3K_Q4K = 0, 1, 2, 3  # Q3K_Q4K: Q3_K gate/up, Q4_K down
 STAGES = ("route", "batches", "prefill_tiles", "ffn_gateup", "ffn_down", "combine", "prefill_gateup", "prefill_down",
           "route_batches")
 
@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.moe_count_routes.argtypes = [vp, i32, i32, i32, vp, vp]
         L.moe_expert_blob_bytes.argtypes = [i32, i32, i32]
         L.moe_expert_blob_bytes.restype = sz
+        L.moe_packed_blob_bytes.argtypes = [i32, i32, i32]
+        L.moe_packed_blob_bytes.restype = sz
         L.moe_pack_expert.argtypes = [i32, vp, vp, i32, i32]
         L.moe_unpack_expert.argtypes = [i32, vp, vp, i32, i32]
         L.moe_validate_slot_map.argtypes = [vp, i32, i32]
@@ -66,12 +68,14 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_ffn_q4k.argtypes = ffn
         L.moe_expert_ffn_q8_0.argtypes = ffn
         L.moe_expert_ffn_mxfp4.argtypes = ffn
+        L.moe_expert_ffn_q3k_q4k.argtypes = ffn
         L.moe_combine.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, i32, i32, vp, i32, vp]
         L.moe_timer_begin.argtypes = [i32, i32]
         L.moe_timer_end.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
         for name in ("moe_route_topk", "moe_build_expert_batches", "moe_route_and_batch", "moe_count_routes",
                      "moe_pack_expert", "moe_unpack_expert",
                      "moe_validate_slot_map", "moe_expert_ffn_q4k", "moe_expert_ffn_q8_0", "moe_expert_ffn_mxfp4",
+                     "moe_expert_ffn_q3k_q4k",
                      "moe_combine",
                      "moe_timer_begin", "moe_timer_end"):
             getattr(L, name).restype = i32
@@ -231,22 +235,30 @@ def moe_expert_blob_bytes(fmt: int, H: int, I: int) -> int:
     return int(lib().moe_expert_blob_bytes(fmt, H, I))
 
 
+def moe_packed_blob_bytes(fmt: int, H: int, I: int) -> int:
+    """Bytes of a packed blob (a slot's minimum size)."""
+    return int(lib().moe_packed_blob_bytes(fmt, H, I))
+
+
 def moe_pack_expert(fmt: int, canonical: np.ndarray, H: int, I: int, out: np.ndarray | None = None) -> np.ndarray:
     n = moe_expert_blob_bytes(fmt, H, I)
     canonical = np.ascontiguousarray(canonical, dtype=np.uint8)
     if canonical.nbytes != n:
         raise ValueError(f"canonical blob has {canonical.nbytes} bytes, expected {n}")
+    npk = moe_packed_blob_bytes(fmt, H, I)
     if out is None:
-        out = np.empty(n, dtype=np.uint8)
+        out = np.empty(npk, dtype=np.uint8)
+    if out.nbytes != npk or not out.flags.c_contiguous:
+        raise ValueError(f"out must be a contiguous {npk}-byte array")
     _check(lib().moe_pack_expert(fmt, canonical.ctypes.data, out.ctypes.data, H, I))
     return out
 
 
 def moe_unpack_expert(fmt: int, packed: np.ndarray, H: int, I: int) -> np.ndarray:
-    n = moe_expert_blob_bytes(fmt, H, I)
+    n, npk = moe_expert_blob_bytes(fmt, H, I), moe_packed_blob_bytes(fmt, H, I)
     packed = np.ascontiguousarray(packed, dtype=np.uint8)
-    if packed.nbytes != n:
-        raise ValueError(f"packed blob has {packed.nbytes} bytes, expected {n}")
+    if packed.nbytes != npk:
+        raise ValueError(f"packed blob has {packed.nbytes} bytes, expected {npk}")
     out = np.empty(n, dtype=np.uint8)
     _check(lib().moe_unpack_expert(fmt, packed.ctypes.data, out.ctypes.data, H, I))
     return out
@@ -291,9 +303,16 @@ def moe_expert_ffn_mxfp4(slot_pool, slot_stride, S, H, I, x, k, slot_offsets, ac
          perm_pair, y_pairs, path, ws, stream)
 
 
+def moe_expert_ffn_q3k_q4k(slot_pool, slot_stride, S, H, I, x, k, slot_offsets, active_slots, num_active, perm_pair,
+                           y_pairs, path=MOE_PATH_AUTO, ws=None, stream=None):
+    _ffn(lib().moe_expert_ffn_q3k_q4k, slot_pool, slot_stride, S, H, I, x, k, slot_offsets, active_slots, num_active,
+         perm_pair, y_pairs, path, ws, stream)
+
+
 def moe_expert_ffn(fmt: int):
     """The expert-FFN call of a block format."""
-    return {MOE_FMT_Q8_0: moe_expert_ffn_q8_0, MOE_FMT_Q4K: moe_expert_ffn_q4k, MOE_FMT_MXFP4: moe_expert_ffn_mxfp4}[fmt]
+    return {MOE_FMT_Q8_0: moe_expert_ffn_q8_0, MOE_FMT_Q4K: moe_expert_ffn_q4k, MOE_FMT_MXFP4: moe_expert_ffn_mxfp4,
+            MOE_FMT_Q3K_Q4K: moe_expert_ffn_q3k_q4k}[fmt]
 
 
 def moe_combine(y_pairs, topk_ids, topk_w, slot_of_expert, y_shared, y, stream=None):

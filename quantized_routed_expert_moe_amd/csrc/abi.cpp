@@ -46,10 +46,11 @@ moe_status check_route_shape(int T, int E, int k) {
 }
 
 moe_status check_shape(int format, int H, int I) {
-    if (format != MOE_FMT_Q8_0 && format != MOE_FMT_Q4K && format != MOE_FMT_MXFP4)
-        return fail(MOE_ERR_INVALID_ARGUMENT, "format = %d is not MOE_FMT_Q8_0, MOE_FMT_Q4K or MOE_FMT_MXFP4", format);
+    if (format < MOE_FMT_Q8_0 || format > MOE_FMT_Q3K_Q4K)
+        return fail(MOE_ERR_INVALID_ARGUMENT,
+                    "format = %d is not MOE_FMT_Q8_0, MOE_FMT_Q4K, MOE_FMT_MXFP4 or MOE_FMT_Q3K_Q4K", format);
     const int m = format == MOE_FMT_Q8_0 ? 128 : 256;
-    static const char* const kNames[] = {"Q8_0", "Q4_K", "MXFP4"};
+    static const char* const kNames[] = {"Q8_0", "Q4_K", "MXFP4", "Q3_K/Q4_K"};
     if (H <= 0 || I <= 0) return fail(MOE_ERR_INVALID_ARGUMENT, "H = %d, I = %d must be positive", H, I);
     if (H % m || I % m)
         return fail(MOE_ERR_UNSUPPORTED, "%s needs H and I multiples of %d (H = %d, I = %d)",
@@ -61,7 +62,19 @@ moe_status check_shape(int format, int H, int I) {
 
 size_t blob_bytes(int format, int H, int I) {
     const size_t w = (size_t)H * I;  // weights per matrix
-    return format == MOE_FMT_Q4K ? 3 * w / 256 * 144 : format == MOE_FMT_MXFP4 ? 3 * w / 32 * 17 : 3 * w / 32 * 34;
+    switch (format) {
+        case MOE_FMT_Q4K: return 3 * w / 256 * 144;
+        case MOE_FMT_MXFP4: return 3 * w / 32 * 17;
+        case MOE_FMT_Q3K_Q4K: return 2 * w / 256 * 110 + w / 256 * 144;
+        default: return 3 * w / 32 * 34;
+    }
+}
+
+// Bytes of a packed blob: the canonical count, except for the mixed expert,
+// whose Q3_K rows take a 16-byte header per 256 inputs (14 bytes stored).
+size_t packed_bytes(int format, int H, int I) {
+    if (format == MOE_FMT_Q3K_Q4K) return qmoe::q3k_gateup_bytes(H, I) + (size_t)H * I / 256 * 144;
+    return blob_bytes(format, H, I);
 }
 
 int resolve_path(int format, int T, int x_dtype, int path) {
@@ -111,13 +124,16 @@ void nibbles_unpack(const uint8_t* src, uint8_t* q) {
     }
 }
 
+template <bool PACK>
+void q4k_down_walk(const uint8_t* in, uint8_t* out, int H, int I, size_t canon_base, size_t base);
+
 // Move every field of a blob between the canonical and the packed layout
 // (PACK: canonical -> packed; otherwise packed -> canonical).
 template <bool PACK>
 void q4k_walk(const uint8_t* in, uint8_t* out, int H, int I) {
-    const size_t rbH = (size_t)H / 256 * 144, rbI = (size_t)I / 256 * 144;
+    const size_t rbH = (size_t)H / 256 * 144;
     const size_t gbytes = (size_t)I * rbH;
-    const int SBH = H / 256, SBI = I / 256;
+    const int SBH = H / 256;
     uint8_t q[32];
     // gate/up section
     for (int rg = 0; rg < I / 64; ++rg)
@@ -144,14 +160,21 @@ void q4k_walk(const uint8_t* in, uint8_t* out, int H, int I) {
                 }
             }
         }
-    // down section
-    const size_t base = qmoe::q4k_gateup_bytes(H, I);
+    q4k_down_walk<PACK>(in, out, H, I, 2 * gbytes, qmoe::q4k_gateup_bytes(H, I));
+}
+
+// The Q4_K down matrix: canonical rows at canon_base, packed tiles at base.
+template <bool PACK>
+void q4k_down_walk(const uint8_t* in, uint8_t* out, int H, int I, size_t canon_base, size_t base) {
+    const size_t rbI = (size_t)I / 256 * 144;
+    const int SBI = I / 256;
+    uint8_t q[32];
     for (int rg = 0; rg < H / 64; ++rg)
         for (int sb = 0; sb < SBI; ++sb) {
             const size_t tile = base + ((size_t)rg * SBI + sb) * qmoe::kQ4kDownTile;
             for (int r = 0; r < 64; ++r) {
                 const size_t row = (size_t)rg * 64 + r;
-                const size_t canon = 2 * gbytes + row * rbI + (size_t)sb * 144;
+                const size_t canon = canon_base + row * rbI + (size_t)sb * 144;
                 if (PACK) {
                     memcpy(out + tile + r * 16, in + canon, 16);
                     for (int j = 0; j < 8; ++j) {
@@ -281,6 +304,83 @@ void mx4_walk(const uint8_t* in, uint8_t* out, int H, int I) {
         }
 }
 
+// Q3_K: one canonical 110-byte super-block (high bits, low bits, scales, d)
+// <-> its packed fields: 16-byte header (scales, d, 2 zero bytes), the (LA,
+// LB) words of its 8 blocks and their HB words.
+void q3k_block(const uint8_t* canon, uint8_t* hdr, uint32_t* la, uint32_t* lb, uint32_t* hb, bool pack) {
+    if (pack) {
+        memcpy(hdr, canon + 96, 12);
+        memcpy(hdr + 12, canon + 108, 2);
+        hdr[14] = hdr[15] = 0;
+        for (int b = 0; b < 8; ++b) la[b] = lb[b] = hb[b] = 0;
+        for (int i = 0; i < 256; ++i) {
+            const int h = i / 128, g = (i % 128) / 32, l = i % 32;
+            const uint32_t low = (canon[32 + 32 * h + l] >> (2 * g)) & 3, high = (canon[l] >> (4 * h + g)) & 1;
+            const int b = i / 32, d = (i % 32) / 8, n = i % 8;
+            (d < 2 ? la : lb)[b] |= low << (4 * n + 2 * (d & 1));
+            hb[b] |= high << (4 * n + (2 + d) % 4);
+        }
+    } else {
+        uint8_t* dst = const_cast<uint8_t*>(canon);
+        memset(dst, 0, 110);
+        memcpy(dst + 96, hdr, 12);
+        memcpy(dst + 108, hdr + 12, 2);
+        for (int i = 0; i < 256; ++i) {
+            const int b = i / 32, d = (i % 32) / 8, n = i % 8;
+            const uint32_t low = ((d < 2 ? la : lb)[b] >> (4 * n + 2 * (d & 1))) & 3;
+            const uint32_t high = (hb[b] >> (4 * n + (2 + d) % 4)) & 1;
+            const int h = i / 128, g = (i % 128) / 32, l = i % 32;
+            dst[32 + 32 * h + l] |= (uint8_t)(low << (2 * g));
+            dst[l] |= (uint8_t)(high << (4 * h + g));
+        }
+    }
+}
+
+// The mixed blob: Q3_K gate/up tiles (layout in qmoe_internal.h), then the
+// Q4_K down section.
+template <bool PACK>
+void q3k_mix_walk(const uint8_t* in, uint8_t* out, int H, int I) {
+    const size_t rbH = (size_t)H / 256 * 110;
+    const size_t gbytes = (size_t)I * rbH;
+    const int UH = H / 256;
+    uint8_t* dev = PACK ? out : const_cast<uint8_t*>(in);
+    const uint8_t* canon_base = PACK ? in : out;
+    uint32_t la[8], lb[8], hb[8];
+    for (int rg = 0; rg < I / 64; ++rg)
+        for (int u = 0; u < UH; ++u) {
+            uint8_t* tile = dev + ((size_t)rg * UH + u) * qmoe::kQ3kGateUpTile;
+            for (int r = 0; r < 64; ++r) {
+                const size_t row = (size_t)rg * 64 + r;
+                for (int mat = 0; mat < 2; ++mat) {
+                    const uint8_t* canon = canon_base + mat * gbytes + row * rbH + (size_t)u * 110;
+                    uint8_t* hdr = tile + mat * 1024 + r * 16;
+                    if (!PACK) {
+                        for (int c = 0; c < 4; ++c) {
+                            const uint8_t* p = tile + 2048 + c * 2048 + mat * 1024 + r * 16;
+                            memcpy(&la[2 * c], p, 4);
+                            memcpy(&lb[2 * c], p + 4, 4);
+                            memcpy(&la[2 * c + 1], p + 8, 4);
+                            memcpy(&lb[2 * c + 1], p + 12, 4);
+                        }
+                        for (int c = 0; c < 2; ++c) memcpy(&hb[4 * c], tile + 10240 + c * 2048 + mat * 1024 + r * 16, 16);
+                    }
+                    q3k_block(canon, hdr, la, lb, hb, PACK);
+                    if (PACK) {
+                        for (int c = 0; c < 4; ++c) {
+                            uint8_t* p = tile + 2048 + c * 2048 + mat * 1024 + r * 16;
+                            memcpy(p, &la[2 * c], 4);
+                            memcpy(p + 4, &lb[2 * c], 4);
+                            memcpy(p + 8, &la[2 * c + 1], 4);
+                            memcpy(p + 12, &lb[2 * c + 1], 4);
+                        }
+                        for (int c = 0; c < 2; ++c) memcpy(tile + 10240 + c * 2048 + mat * 1024 + r * 16, &hb[4 * c], 16);
+                    }
+                }
+            }
+        }
+    q4k_down_walk<PACK>(in, out, H, I, 2 * gbytes, qmoe::q3k_gateup_bytes(H, I));
+}
+
 moe_status ffn_common(int format, const void* slot_pool, size_t slot_stride, int S, int H, int I, const void* x,
                       int x_dtype, int T, int k, const int32_t* slot_offsets, const int32_t* active_slots,
                       const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype, int path,
@@ -295,9 +395,9 @@ moe_status ffn_common(int format, const void* slot_pool, size_t slot_stride, int
         return fail(MOE_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
     if (!aligned16(slot_pool) || (slot_stride & 15u))
         return fail(MOE_ERR_INVALID_ARGUMENT, "slot_pool and slot_stride must be 16-byte aligned");
-    if (slot_stride < blob_bytes(format, H, I))
+    if (slot_stride < packed_bytes(format, H, I))
         return fail(MOE_ERR_INVALID_ARGUMENT, "slot_stride %zu is smaller than the blob (%zu bytes)", slot_stride,
-                    blob_bytes(format, H, I));
+                    packed_bytes(format, H, I));
     if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARGUMENT, "bad x_dtype %d", x_dtype);
     if (y_dtype != MOE_F32 && y_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARGUMENT, "bad y_dtype %d", y_dtype);
     if (path < MOE_PATH_AUTO || path > MOE_PATH_PREFILL) return fail(MOE_ERR_INVALID_ARGUMENT, "bad path %d", path);
@@ -310,7 +410,7 @@ moe_status ffn_common(int format, const void* slot_pool, size_t slot_stride, int
     } else {
         if (format != MOE_FMT_Q4K)
             return fail(MOE_ERR_UNSUPPORTED, "the prefill path is implemented for Q4_K only (MOE_PATH_DECODE serves "
-                                             "Q8_0 and MXFP4 at any T)");
+                                             "Q8_0, MXFP4 and Q3_K/Q4_K at any T)");
         if (x_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the prefill path takes MOE_BF16 x");
         // The GEMMs address x and h rows with 32-bit byte offsets, and the
         // tile list counts tiles in 16 bits.
@@ -457,17 +557,23 @@ size_t moe_expert_blob_bytes(int format, int H, int I) {
     return blob_bytes(format, H, I);
 }
 
+size_t moe_packed_blob_bytes(int format, int H, int I) {
+    if (check_shape(format, H, I) != MOE_OK) return 0;
+    return packed_bytes(format, H, I);
+}
+
 moe_status moe_pack_expert(int format, const void* canonical, void* packed, int H, int I) {
     moe_status st = check_shape(format, H, I);
     if (st != MOE_OK) return st;
     if (!canonical || !packed) return fail(MOE_ERR_INVALID_ARGUMENT, "NULL blob pointer");
     const uint8_t* in = static_cast<const uint8_t*>(canonical);
     uint8_t* out = static_cast<uint8_t*>(packed);
-    const size_t n = blob_bytes(format, H, I);
-    if (in < out + n && out < in + n) return fail(MOE_ERR_INVALID_ARGUMENT, "blobs overlap");
-    memset(out, 0, n);
+    const size_t nc = blob_bytes(format, H, I), np = packed_bytes(format, H, I);
+    if (in < out + np && out < in + nc) return fail(MOE_ERR_INVALID_ARGUMENT, "blobs overlap");
+    memset(out, 0, np);
     if (format == MOE_FMT_Q4K) q4k_walk<true>(in, out, H, I);
     else if (format == MOE_FMT_MXFP4) mx4_walk<true>(in, out, H, I);
+    else if (format == MOE_FMT_Q3K_Q4K) q3k_mix_walk<true>(in, out, H, I);
     else q8_walk<true>(in, out, H, I);
     return MOE_OK;
 }
@@ -478,11 +584,12 @@ moe_status moe_unpack_expert(int format, const void* packed, void* canonical, in
     if (!canonical || !packed) return fail(MOE_ERR_INVALID_ARGUMENT, "NULL blob pointer");
     const uint8_t* in = static_cast<const uint8_t*>(packed);
     uint8_t* out = static_cast<uint8_t*>(canonical);
-    const size_t n = blob_bytes(format, H, I);
-    if (in < out + n && out < in + n) return fail(MOE_ERR_INVALID_ARGUMENT, "blobs overlap");
-    memset(out, 0, n);
+    const size_t nc = blob_bytes(format, H, I), np = packed_bytes(format, H, I);
+    if (in < out + nc && out < in + np) return fail(MOE_ERR_INVALID_ARGUMENT, "blobs overlap");
+    memset(out, 0, nc);
     if (format == MOE_FMT_Q4K) q4k_walk<false>(in, out, H, I);
     else if (format == MOE_FMT_MXFP4) mx4_walk<false>(in, out, H, I);
+    else if (format == MOE_FMT_Q3K_Q4K) q3k_mix_walk<false>(in, out, H, I);
     else q8_walk<false>(in, out, H, I);
     return MOE_OK;
 }
@@ -533,6 +640,14 @@ moe_status moe_expert_ffn_mxfp4(const void* slot_pool, size_t slot_stride, int S
                                 const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype,
                                 int path, void* ws, size_t ws_bytes, void* stream) {
     return ffn_common(MOE_FMT_MXFP4, slot_pool, slot_stride, S, H, I, x, x_dtype, T, k, slot_offsets, active_slots,
+                      num_active, perm_pair, y_pairs, y_dtype, path, ws, ws_bytes, stream);
+}
+
+moe_status moe_expert_ffn_q3k_q4k(const void* slot_pool, size_t slot_stride, int S, int H, int I, const void* x,
+                                  int x_dtype, int T, int k, const int32_t* slot_offsets, const int32_t* active_slots,
+                                  const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype,
+                                  int path, void* ws, size_t ws_bytes, void* stream) {
+    return ffn_common(MOE_FMT_Q3K_Q4K, slot_pool, slot_stride, S, H, I, x, x_dtype, T, k, slot_offsets, active_slots,
                       num_active, perm_pair, y_pairs, y_dtype, path, ws, ws_bytes, stream);
 }
 

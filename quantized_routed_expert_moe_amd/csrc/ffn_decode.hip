@@ -22,6 +22,11 @@
 //     per instruction, exact), laid out in the Q4_K element order so the two
 //     formats share activation records; each 32-element block's dot product
 //     is scaled by its E8M0 power of two in fp32.
+//   * Q3_K gate/up rows (the mixed expert: Q3_K gate and up, Q4_K down) are
+//     packed as a 2-bit plane and a 1-bit plane arranged so that two
+//     and-or operations build an fp16 pair 1024 + v (v = q + 4, or 16v for
+//     the words whose records hold x/16), again in the Q4_K element order;
+//     their 16-element sub-blocks take per-half constants from the records.
 //   * Activations (token rows, and the intermediate h) are 64-byte records per
 //     32 elements, laid out in the order the nibble/byte extraction produces.
 //     Each wave puts the records of its K range for the tokens of the current
@@ -100,6 +105,45 @@ __device__ __forceinline__ float mx4_dot(const uint4 q, cu32* X) {
     return acc;
 }
 
+// Q3_K: one 32-element block of one row.  LA holds the low two bits of
+// elements 0-15 (group d = 0 at bits 4n, d = 1 at bits 4n + 2, n < 8; element
+// 8d + n), LB those of elements 16-31 (d = 2, 3 likewise); HB the high bits,
+// element 8d + n at bit 4n + (2 + d) % 4.  Aligning a group's high bits to
+// bit 4n + 2, above its low bits, then gives v = low + 4 high (0..7) in each
+// half of a pair by two and-or operations.  Returns the dot products over
+// the two 16-element sub-blocks (groups 0-1 and 2-3) of (1024 + v) with the
+// record's stored values.
+__device__ __forceinline__ float2 q3k_dot(uint32_t la, uint32_t lb, uint32_t hb, cu32* X) {
+    float acc[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t lw = (d < 2 ? la : lb) >> (2 * (d & 1));
+        const uint32_t hw = d == 0 ? hb : d == 1 ? hb >> 1 : d == 2 ? hb << 2 : hb << 1;
+        const uint32_t lw8 = lw >> 8, hw8 = hw >> 8;
+        float& a = acc[d >> 1];
+        a = fdot2u((hw & 0x00040004u) | ((lw & 0x00030003u) | kMagic), X[4 * d + 0], a);
+        a = fdot2u((hw & 0x00400040u) | ((lw & 0x00300030u) | kMagic), X[4 * d + 1], a);
+        a = fdot2u((hw8 & 0x00040004u) | ((lw8 & 0x00030003u) | kMagic), X[4 * d + 2], a);
+        a = fdot2u((hw8 & 0x00400040u) | ((lw8 & 0x00300030u) | kMagic), X[4 * d + 3], a);
+    }
+    return make_float2(acc[0], acc[1]);
+}
+
+// Q3_K header (packed): bytes 0-11 the 12 scale bytes as stored, bytes
+// 12-13 fp16 d.  Scales of sub-blocks 8h..8h+7 as d * (sc - 32): four 6-bit
+// scales at a time, one per byte (low nibbles from bytes 0-7, low or high
+// half; top bits from bytes 8-11, two per scale).
+__device__ __forceinline__ void q3k_scales(const uint4 hd, int h, float* ds) {
+    const float d = half_to_float(hd.w), d32 = -32.0f * d;
+    const uint32_t s0 = ((h == 0 ? hd.x : hd.x >> 4) & 0x0F0F0F0Fu) | (((hd.z >> (4 * h)) & 0x03030303u) << 4);
+    const uint32_t s1 = ((h == 0 ? hd.y : hd.y >> 4) & 0x0F0F0F0Fu) | (((hd.z >> (4 * h + 2)) & 0x03030303u) << 4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        ds[k] = fmaf(d, (float)((s0 >> (8 * k)) & 0xFFu), d32);
+        ds[k + 4] = fmaf(d, (float)((s1 >> (8 * k)) & 0xFFu), d32);
+    }
+}
+
 // E8M0 scale byte x -> 2^(x - 127) as fp32 bits: x << 23 for x = 1..254;
 // x = 0 (the subnormal 2^-127) and x = 255 (NaN) also need bit 22, which
 // bit 8 of x + 1 or of x - 1 supplies only for those two.  Integer
@@ -141,10 +185,16 @@ template <int NMAT> struct UnitRegs<0, NMAT> {
 template <int NMAT> struct UnitRegs<2, NMAT> {
     uint4 q[8][NMAT];
 };
+// Q3_K: per 64-element chunk c the (LA, LB) words of blocks 2c and 2c + 1;
+// per 128-element chunk the HB words of its four blocks.
+template <int NMAT> struct UnitRegs<3, NMAT> {
+    uint4 L[4][NMAT];
+    uint4 Hb[2][NMAT];
+};
 
 template <int FMT, int NMAT>
 __device__ __forceinline__ constexpr int tile_bytes() {
-    return FMT == 1 ? NMAT * 9216 : NMAT * 8704;
+    return FMT == 1 ? NMAT * 9216 : FMT == 3 ? NMAT * 7168 : NMAT * 8704;
 }
 
 // LDS region of one wave: words [kMaxTok][8][16] dwords, then (C, S) [kMaxTok][8][2].
@@ -224,6 +274,11 @@ __device__ __forceinline__ void act_arrived(ActRegs& a) {
     }
 }
 
+__device__ __forceinline__ float quad_sum(float v) {
+    v = dpp_add<0xB1>(v);      // quad_perm [1,0,3,2]
+    return dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]
+}
+
 __device__ __forceinline__ float sum8_lanes(float v) {
     v = dpp_add<0xB1>(v);   // quad_perm [1,0,3,2]
     v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]
@@ -274,9 +329,19 @@ __device__ __forceinline__ void act_store(const ActRegs& a, int x_dtype, int lan
                 const float s16 = FMT == 1 ? sum8_lanes(half_to_float(b0) + half_to_float(b1) + half_to_float(b2) +
                                                         half_to_float(b3))
                                            : 0.0f;
-                const float sx = sum8_lanes(v[0] + v[1] + v[2] + v[3]);
-                // all 8 lanes of the block hold the sums
-                *reinterpret_cast<float2*>(lc + (t * RB + jb) * 2) = make_float2(1024.0f * s16, sx);
+                const float sx = FMT == 3 ? 0.0f : sum8_lanes(v[0] + v[1] + v[2] + v[3]);
+                if (FMT == 3) {
+                    // Q3_K: per 16-element half (a quad of lanes), K = 1024 * sum of
+                    // the stored values + 4 * sum x (the magic number and the
+                    // offset of v = q + 4)
+                    const float h16 = quad_sum(half_to_float(b0) + half_to_float(b1) + half_to_float(b2) +
+                                               half_to_float(b3));
+                    const float hx = quad_sum(v[0] + v[1] + v[2] + v[3]);
+                    lc[(t * RB + jb) * 2 + (sl >> 2)] = fmaf(4.0f, hx, 1024.0f * h16);
+                } else {
+                    // all 8 lanes of the block hold the sums
+                    *reinterpret_cast<float2*>(lc + (t * RB + jb) * 2) = make_float2(1024.0f * s16, sx);
+                }
             }
         } else {
             // token lane / 32 (< kMaxTok: with one token, lanes 32-63 fill
@@ -421,6 +486,46 @@ __device__ __forceinline__ void half_dots(const UnitRegs<2, NMAT>& r, const uint
             const uint32_t* X = lw + (t * 8 + j) * 16;
 #pragma unroll
             for (int m = 0; m < NMAT; ++m) acc[t][m] += s[m] * mx4_dot(r.q[j][m], X);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <int NMAT>
+__device__ __forceinline__ void load_half(__amdgpu_buffer_rsrc_t src, int uoff, int lane, int h,
+                                          UnitRegs<3, NMAT>& r, uint4* hdr) {
+    if (h == 0) {
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) hdr[m] = ldb16(src, lane * 16, uoff + m * 1024);
+    }
+#pragma unroll
+    for (int c = 2 * h; c < 2 * h + 2; ++c)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) r.L[c][m] = ldb16(src, lane * 16, uoff + NMAT * 1024 + c * NMAT * 1024 + m * 1024);
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) r.Hb[h][m] = ldb16(src, lane * 16, uoff + NMAT * 5120 + h * NMAT * 1024 + m * 1024);
+}
+template <int NT, int NMAT>
+__device__ __forceinline__ void half_dots(const UnitRegs<3, NMAT>& r, const uint4* hdr, int h, const uint32_t* lw,
+                                          const float* lc, float (*acc)[NMAT]) {
+    float ds[NMAT][8];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) q3k_scales(hdr[m], h, ds[m]);
+#pragma unroll
+    for (int j = 4 * h; j < 4 * h + 4; ++j) {
+        const int c = j >> 1, i = j & 3;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const uint32_t* X = lw + (t * 8 + j) * 16;
+            const float ka = lc[(t * 8 + j) * 2], kb = lc[(t * 8 + j) * 2 + 1];
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) {
+                const uint4 L = r.L[c][m], Hv = r.Hb[h][m];
+                const uint32_t la = (j & 1) ? L.z : L.x, lb = (j & 1) ? L.w : L.y;
+                const uint32_t hb = i == 0 ? Hv.x : i == 1 ? Hv.y : i == 2 ? Hv.z : Hv.w;
+                const float2 dd = q3k_dot(la, lb, hb, X);
+                acc[t][m] += ds[m][2 * (j & 3)] * (dd.x - ka) + ds[m][2 * (j & 3) + 1] * (dd.y - kb);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -774,9 +879,11 @@ hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s) {
     const int max_active = (int)std::min<size_t>((size_t)a.S, P);
     if (max_active == 0 || a.T == 0) return hipSuccess;
 
+    // block types of the gate/up and down matrices (the mixed expert: Q3_K, then Q4_K)
+    const int fgu = a.format == 3 ? 3 : a.format, fdn = a.format == 3 ? 1 : a.format;
     // gate/up + SwiGLU
     {
-        const int units = a.format == 0 ? a.H / 128 : a.H / 256;
+        const int units = fgu == 0 ? a.H / 128 : a.H / 256;
         int nw, upw;
         split_k(units, (long)(a.I / 64) * max_active, &nw, &upw);
         const int kparts = split_k_parts(units, (long)(a.I / 64) * max_active, (int)P, &nw, &upw);
@@ -785,10 +892,12 @@ hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s) {
         const GemvLaunch g{a.pool, a.stride, a.S, a.H, a.I, 0, a.x, a.x_dtype, nullptr, nullptr, a.T, a.k,
                            a.slot_offsets, a.active_slots, a.num_active, a.perm_pair, hw, hcs, nullptr, upw,
                            kparts, part};
-        if (a.format == 1)
+        if (fgu == 1)
             launch_gemv<1, 2>(g, grid, block, s);
-        else if (a.format == 2)
+        else if (fgu == 2)
             launch_gemv<2, 2>(g, grid, block, s);
+        else if (fgu == 3)
+            launch_gemv<3, 2>(g, grid, block, s);
         else
             launch_gemv<0, 2>(g, grid, block, s);
         timer_after(kStageGateUp, s);
@@ -797,21 +906,22 @@ hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s) {
     }
     // down
     {
-        const int units = a.format == 0 ? a.I / 128 : a.I / 256;
+        const int units = fdn == 0 ? a.I / 128 : a.I / 256;
         int nw, upw;
         split_k(units, (long)(a.H / 64) * max_active, &nw, &upw);
         const int kparts = split_k_parts(units, (long)(a.H / 64) * max_active, (int)P, &nw, &upw);
         const dim3 grid(a.H / 64, max_active), block(64 * nw);
         const size_t section = a.format == 1   ? q4k_gateup_bytes(a.H, a.I)
                                : a.format == 2 ? mx4_gateup_bytes(a.H, a.I)
+                               : a.format == 3 ? q3k_gateup_bytes(a.H, a.I)
                                                : q8_gateup_bytes(a.H, a.I);
         timer_before(kStageDown, s);
         const GemvLaunch g{a.pool, a.stride, a.S, a.I, a.H, section, nullptr, 0, hw, hcs, a.T, a.k,
                            a.slot_offsets, a.active_slots, a.num_active, a.perm_pair, nullptr, nullptr,
                            static_cast<float*>(a.y_pairs), upw, kparts, part};
-        if (a.format == 1)
+        if (fdn == 1)
             launch_gemv<1, 1>(g, grid, block, s);
-        else if (a.format == 2)
+        else if (fdn == 2)
             launch_gemv<2, 1>(g, grid, block, s);
         else
             launch_gemv<0, 1>(g, grid, block, s);

@@ -58,6 +58,25 @@ namespace qmoe {
 // the order 0, 2, 1, 3 (the Q4_K element order, so both formats share the
 // decode path's activation records).
 
+//
+// Packed mixed blob (Q3_K gate and up, Q4_K down; H, I multiples of 256):
+// the gate/up section in Q3_K tiles of 64 rows x 256 inputs, then the Q4_K
+// down section exactly as in the Q4_K blob.  Q3_K gate/up tile (rg, u),
+// u < H/256, 14336 bytes:
+//     [0, 1024)         gate headers: row r at 16r: the 12 scale bytes as
+//                       stored, then fp16 d, then 2 zero bytes
+//     [1024, 2048)      up headers
+//     [2048 + 2048c, +1024)    gate low bits of elements 64c..64c+63 (c < 4):
+//                       row r at 16r: LA, LB of block 2c, then of block 2c+1
+//     [3072 + 2048c, +1024)    up, same
+//     [10240 + 2048c, +1024)   gate high bits of elements 128c..128c+127
+//                       (c < 2): row r at 16r: HB of blocks 4c..4c+3
+//     [11264 + 2048c, +1024)   up, same
+// A 32-element block's LA holds the low two bits of elements 8d + n for
+// d < 2 at bits 4n + 2d, LB those of d = 2, 3 at bits 4n + 2(d - 2), and HB
+// the high bit of element 8d + n at bit 4n + (2 + d) % 4, where the stored
+// quant is q + 4 = low + 4 * high.
+
 constexpr int kMaxExpertsInternal = 1024;  // equals MOE_MAX_EXPERTS of the C ABI
 
 constexpr int kQ4kGateUpTile = 18432;
@@ -70,6 +89,8 @@ __host__ __device__ inline size_t q8_gateup_bytes(int H, int I) { return (size_t
 constexpr int kMx4GateUpTile = 17408;
 constexpr int kMx4DownTile = 8704;
 __host__ __device__ inline size_t mx4_gateup_bytes(int H, int I) { return (size_t)(I / 64) * (H / 256) * kMx4GateUpTile; }
+constexpr int kQ3kGateUpTile = 14336;
+__host__ __device__ inline size_t q3k_gateup_bytes(int H, int I) { return (size_t)(I / 64) * (H / 256) * kQ3kGateUpTile; }
 
 // Per-token activation records of the decode path, one per 32-element
 // block of the input dimension: 16 dwords of fp16 pairs laid out to match

@@ -70,10 +70,13 @@ uint16_t load_u16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
 constexpr int kQ4kBlock = 256, kQ4kBytes = 144;
 constexpr int kQ8Block = 32, kQ8Bytes = 34;
 constexpr int kMx4Block = 32, kMx4Bytes = 17;
+constexpr int kQ3kBlock = 256, kQ3kBytes = 110;
+constexpr int kRowQ3k = 100;  // block type of a Q3_K matrix (the mixed expert's gate and up)
 
-size_t row_bytes(int format, int n) {
-    if (format == MOE_FMT_Q4K) return (size_t)(n / kQ4kBlock) * kQ4kBytes;
-    if (format == MOE_FMT_MXFP4) return (size_t)(n / kMx4Block) * kMx4Bytes;
+size_t row_bytes(int type, int n) {
+    if (type == MOE_FMT_Q4K) return (size_t)(n / kQ4kBlock) * kQ4kBytes;
+    if (type == MOE_FMT_MXFP4) return (size_t)(n / kMx4Block) * kMx4Bytes;
+    if (type == kRowQ3k) return (size_t)(n / kQ3kBlock) * kQ3kBytes;
     return (size_t)(n / kQ8Block) * kQ8Bytes;
 }
 
@@ -172,6 +175,48 @@ void dequant_row_mxfp4(const uint8_t* row, int n, float* out) {
     }
 }
 
+// One Q3_K row of n weights (n / 256 super-blocks of 110 bytes: 32 bytes of
+// high bits, 64 of 2-bit quants, 12 of 6-bit scales, fp16 d; element i =
+// 128h + 32g + l has its low bits at bits 2g of quant byte 32h + l and its
+// high bit at bit 4h + g of byte l; scale j of the 16-element sub-block i /
+// 16: low nibble of byte j (j < 8) or the high nibble of byte j - 8, top two
+// bits at bit 2 (j / 4) of byte 8 + j % 4) -> n floats d (sc_j - 32) (low + 4
+// high - 4).  Per 32 elements (one g of one h), one 32-byte load of the
+// quant bytes and of the high-bit bytes.
+__attribute__((target("avx2,fma")))
+void dequant_row_q3k(const uint8_t* row, int n, float* out) {
+    const __m256i three = _mm256_set1_epi8(3), one = _mm256_set1_epi8(1);
+    alignas(32) int8_t q[32];
+    for (int sb = 0; sb < n / kQ3kBlock; ++sb, row += kQ3kBytes, out += kQ3kBlock) {
+        const uint8_t* hm = row;
+        const uint8_t* qs = row + 32;
+        const uint8_t* s = row + 96;
+        const float d = half_bits_to_float(load_u16(row + 108));
+        float ds[16];
+        for (int j = 0; j < 16; ++j) {
+            const int lo = j < 8 ? (s[j] & 15) : (s[j - 8] >> 4);
+            const int hi = (s[8 + j % 4] >> (2 * (j / 4))) & 3;
+            ds[j] = d * (float)((lo | (hi << 4)) - 32);
+        }
+        const __m256i hbits = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(hm));
+        for (int h = 0; h < 2; ++h) {
+            const __m256i qv = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(qs + 32 * h));
+            for (int g = 0; g < 4; ++g) {
+                const __m256i low = _mm256_and_si256(_mm256_srli_epi16(qv, 2 * g), three);
+                const __m256i high = _mm256_and_si256(_mm256_srli_epi16(hbits, 4 * h + g), one);
+                // q = low + 4 high - 4, in -4..3
+                const __m256i v = _mm256_sub_epi8(_mm256_add_epi8(low, _mm256_slli_epi16(high, 2)), _mm256_set1_epi8(4));
+                _mm256_store_si256(reinterpret_cast<__m256i*>(q), v);
+                float* o = out + 128 * h + 32 * g;
+                for (int k = 0; k < 4; ++k) {
+                    const __m256 f = _mm256_cvtepi32_ps(_mm256_cvtepi8_epi32(_mm_loadl_epi64(reinterpret_cast<const __m128i*>(q + 8 * k))));
+                    _mm256_storeu_ps(o + 8 * k, _mm256_mul_ps(f, _mm256_set1_ps(ds[(128 * h + 32 * g + 8 * k) / 16])));
+                }
+            }
+        }
+    }
+}
+
 // sum_i a[i] b[i], n a multiple of 32: four 8-wide FMA accumulators, then a
 // fixed reduction tree.
 __attribute__((target("avx2,fma")))
@@ -205,8 +250,18 @@ void run(int format, const uint8_t* const* expert_blob, int H, int I, const floa
     std::stable_sort(order.begin(), order.end(),
                      [&](int a, int b) { return host_expert[a] < host_expert[b]; });
     const int nthreads = threads > 0 ? threads : omp_get_max_threads();
-    const size_t rbH = row_bytes(format, H), rbI = row_bytes(format, I);
-    auto dequant = format == MOE_FMT_Q4K ? dequant_row_q4k : format == MOE_FMT_MXFP4 ? dequant_row_mxfp4 : dequant_row_q8_0;
+    // block types of the gate/up and down matrices (the mixed expert: Q3_K, then Q4_K)
+    const int tgu = format == MOE_FMT_Q3K_Q4K ? kRowQ3k : format;
+    const int tdn = format == MOE_FMT_Q3K_Q4K ? MOE_FMT_Q4K : format;
+    const size_t rbH = row_bytes(tgu, H), rbI = row_bytes(tdn, I);
+    auto pick = [](int type) {
+        return type == MOE_FMT_Q4K ? dequant_row_q4k
+             : type == MOE_FMT_MXFP4 ? dequant_row_mxfp4
+             : type == kRowQ3k ? dequant_row_q3k
+                               : dequant_row_q8_0;
+    };
+    auto dequant = pick(tgu);
+    auto dequant_down = pick(tdn);
     std::vector<float> g, u;
     for (int g0 = 0; g0 < count;) {
         const int e = host_expert[order[g0]];
@@ -235,7 +290,7 @@ void run(int format, const uint8_t* const* expert_blob, int H, int I, const floa
             }
 #pragma omp for schedule(static)
             for (int c = 0; c < H; ++c) {
-                dequant(wd + (size_t)c * rbI, I, wrow.data());
+                dequant_down(wd + (size_t)c * rbI, I, wrow.data());
                 for (int t = 0; t < n; ++t) {
                     const int p = order[g0 + t];
                     y[(size_t)host_token[p] * H + c] += host_weight[p] * dot(wrow.data(), g.data() + (size_t)t * I, I);
@@ -263,9 +318,10 @@ const char* moe_host_last_error(void) { return g_error.c_str(); }
 int moe_host_leg(int format, const uint8_t* const* expert_blob, int E, int H, int I, const float* x, int T,
                  const int32_t* host_token, const int32_t* host_expert, const float* host_weight, int count,
                  float* y_host, int threads) {
-    if (format != MOE_FMT_Q4K && format != MOE_FMT_Q8_0 && format != MOE_FMT_MXFP4)
-        return fail(MOE_ERR_UNSUPPORTED, "bad format %d", format);
-    const int blk = format == MOE_FMT_Q4K ? kQ4kBlock : format == MOE_FMT_MXFP4 ? kMx4Block : kQ8Block;
+    if (format < MOE_FMT_Q8_0 || format > MOE_FMT_Q3K_Q4K) return fail(MOE_ERR_UNSUPPORTED, "bad format %d", format);
+    const int blk = (format == MOE_FMT_Q4K || format == MOE_FMT_Q3K_Q4K) ? kQ4kBlock
+                    : format == MOE_FMT_MXFP4                           ? kMx4Block
+                                                                        : kQ8Block;
     if (H <= 0 || I <= 0 || H % blk || I % blk)
         return fail(MOE_ERR_UNSUPPORTED, "H = %d and I = %d must be positive multiples of %d", H, I, blk);
     if (E < 1 || T < 0 || count < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "E = %d, T = %d, count = %d", E, T, count);

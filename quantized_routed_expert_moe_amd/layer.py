@@ -15,14 +15,14 @@ import numpy as np
 import torch
 
 from . import (MOE_FMT_Q8_0, MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL, moe_batches_workspace_size, moe_combine,
-               moe_expert_blob_bytes, moe_expert_ffn, moe_expert_ffn_q8_0, moe_ffn_workspace_size, moe_pack_expert,
+               moe_expert_ffn, moe_packed_blob_bytes, moe_expert_ffn_q8_0, moe_ffn_workspace_size, moe_pack_expert,
                moe_route_and_batch)
 
 
 def upload_packed_experts(fmt: int, canonical_blobs: np.ndarray, H: int, I: int, stride: int | None = None,
                           device="cuda") -> tuple[torch.Tensor, int]:
     """Pack canonical blobs [n, bytes] on the host and upload them as a slot pool [n, stride] (uint8)."""
-    n_bytes = moe_expert_blob_bytes(fmt, H, I)
+    n_bytes = moe_packed_blob_bytes(fmt, H, I)
     stride = stride or (n_bytes + 255) // 256 * 256
     n = canonical_blobs.shape[0]
     host = np.zeros((n, stride), dtype=np.uint8)

@@ -26,7 +26,7 @@ def say(msg: str) -> None:
 
 def pack_pool(fmt: int, blobs: np.ndarray, H: int, I: int, slots: list, n_slots: int) -> tuple[torch.Tensor, int]:
     """Device slot pool [n_slots, stride]: slot s holds the packed blob blobs[slots[s]] (None = empty)."""
-    nb = Q.moe_expert_blob_bytes(fmt, H, I)
+    nb = Q.moe_packed_blob_bytes(fmt, H, I)
     stride = (nb + 255) // 256 * 256
     host = np.zeros((n_slots, stride), dtype=np.uint8)
 

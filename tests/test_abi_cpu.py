@@ -159,12 +159,14 @@ def test_workspace_sizes_are_monotone():
 
 @pytest.mark.parametrize("fmt,H,I", [(Q.MOE_FMT_Q4K, 512, 256), (Q.MOE_FMT_Q4K, 768, 512), (Q.MOE_FMT_Q8_0, 256, 128),
                                      (Q.MOE_FMT_Q8_0, 384, 256), (Q.MOE_FMT_MXFP4, 512, 256),
-                                     (Q.MOE_FMT_MXFP4, 768, 512)])
+                                     (Q.MOE_FMT_MXFP4, 768, 512), (Q.MOE_FMT_Q3K_Q4K, 512, 256),
+                                     (Q.MOE_FMT_Q3K_Q4K, 768, 512)])
 def test_pack_round_trip(fmt, H, I):
     blob = F.expert_blob(fmt, 5, 0, 1, H, I)
     packed = Q.moe_pack_expert(fmt, blob, H, I)
-    assert packed.nbytes == blob.nbytes == Q.moe_expert_blob_bytes(fmt, H, I)
-    assert not np.array_equal(packed, blob)
+    assert blob.nbytes == Q.moe_expert_blob_bytes(fmt, H, I) and packed.nbytes == Q.moe_packed_blob_bytes(fmt, H, I)
+    assert packed.nbytes == blob.nbytes or fmt == Q.MOE_FMT_Q3K_Q4K
+    assert packed.nbytes != blob.nbytes or not np.array_equal(packed, blob)
     assert np.array_equal(Q.moe_unpack_expert(fmt, packed, H, I), blob)
 
 
@@ -209,6 +211,35 @@ def test_pack_places_mxfp4_fields():
             d, n = e // 8, e % 8
             p, half = n % 4, n // 4
             assert (int(words[[0, 2, 1, 3][d]]) >> (8 * p + 4 * half)) & 15 == codes[e]
+
+
+def test_pack_places_q3k_fields():
+    """Mixed blob, row r of W_gate, super-block u: header (12 scale bytes, d) at gate/up tile (r//64, u), offset
+    16*(r%64); element 32b + 8d + n's low bits in LA (d < 2) or LB at bit 4n + 2(d % 2), its high bit in HB at bit
+    4n + (2 + d) % 4; the Q4_K down section follows the Q3_K tiles."""
+    H, I = 512, 256
+    blob = F.expert_blob(Q.MOE_FMT_Q3K_Q4K, 4, 0, 0, H, I)
+    packed = Q.moe_pack_expert(Q.MOE_FMT_Q3K_Q4K, blob, H, I)
+    rb = H // 256 * 110
+    for r, u in [(0, 0), (70, 1), (255, 1)]:
+        canon = blob[r * rb + u * 110: r * rb + (u + 1) * 110]
+        tile = ((r // 64) * (H // 256) + u) * 14336
+        hdr = packed[tile + 16 * (r % 64): tile + 16 * (r % 64) + 16]
+        assert np.array_equal(hdr[:12], canon[96:108]) and np.array_equal(hdr[12:14], canon[108:110])
+        for i in (0, 37, 129, 255):
+            h, g, l = i // 128, (i % 128) // 32, i % 32
+            low, high = (canon[32 + 32 * h + l] >> (2 * g)) & 3, (canon[l] >> (4 * h + g)) & 1
+            b, d, n = i // 32, (i % 32) // 8, i % 8
+            lw = packed[tile + 2048 + (b // 2) * 2048 + 16 * (r % 64): tile + 2064 + (b // 2) * 2048 + 16 * (r % 64)]
+            word = int(lw.view(np.uint32)[2 * (b % 2) + (d // 2)])
+            assert (word >> (4 * n + 2 * (d % 2))) & 3 == low
+            hw = packed[tile + 10240 + (b // 4) * 2048 + 16 * (r % 64): tile + 10256 + (b // 4) * 2048 + 16 * (r % 64)]
+            assert (int(hw.view(np.uint32)[b % 4]) >> (4 * n + (2 + d) % 4)) & 1 == high
+    # the down section is the Q4_K blob's: same bytes as packing a Q4_K expert with this W_down
+    q4 = np.concatenate([np.zeros(2 * I * (H // 256 * 144), np.uint8), blob[2 * I * rb:]])
+    q4p = Q.moe_pack_expert(Q.MOE_FMT_Q4K, q4, H, I)
+    base3, base4 = (I // 64) * (H // 256) * 14336, (I // 64) * (H // 256) * 18432
+    assert np.array_equal(packed[base3:], q4p[base4:])
 
 
 def test_validate_slot_map():

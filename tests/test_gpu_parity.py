@@ -333,9 +333,13 @@ def _check_layer(wl, got, want, soe, S, tol=DECODE_TOL):
 
 
 MXFP4_SMALL = W.Workload("small MXFP4 layer (H256 E8 k2 I256 T4)", F.MXFP4, 256, 256, 8, 2, 4)
+Q3K_SMALL = W.Workload("small Q3_K/Q4_K layer (H512 E8 k2 I256 T4)", F.Q3K_Q4K, 512, 256, 8, 2, 4)
+Q3K_QWEN3_T2 = W.Workload("Qwen3-30B-A3B-shaped MoE layer, Q3_K/Q4_K experts, decode T=2", F.Q3K_Q4K, 2048, 768, 128,
+                          8, 2)
 
 
-@pytest.mark.parametrize("wl", [W.TINY, W.QWEN3_DECODE_T1, W.QWEN3_DECODE_T2, MXFP4_SMALL, W.QWEN3_MXFP4_DECODE_T2],
+@pytest.mark.parametrize("wl", [W.TINY, W.QWEN3_DECODE_T1, W.QWEN3_DECODE_T2, MXFP4_SMALL, W.QWEN3_MXFP4_DECODE_T2,
+                                Q3K_SMALL, Q3K_QWEN3_T2],
                          ids=lambda w: w.name.split(",")[0][:24] + f"-fmt{w.fmt}-T{w.T}")
 def test_decode_layer_matches_oracle(wl):
     say(f"decode layer {wl.name}")
@@ -393,13 +397,13 @@ def test_dsv3_experts_many_tokens_per_slot(dsv3_blobs):
     assert int(np.diff(got["slot_offsets"]).max()) > 2
 
 
-@pytest.mark.parametrize("fmt", [F.Q4K, F.Q8_0, F.MXFP4])
+@pytest.mark.parametrize("fmt", [F.Q4K, F.Q8_0, F.MXFP4, F.Q3K_Q4K])
 def test_decode_k_split_across_workgroups(fmt):
     """Two experts with a long K (H 7168): too few row tiles to fill the chip,
     so K is split across workgroups too (partial sums finished by the reduce
     kernel), with an uneven last part and a slot holding several chunks of
     tokens."""
-    name = {F.Q4K: "Q4_K", F.Q8_0: "Q8_0", F.MXFP4: "MXFP4"}[fmt]
+    name = {F.Q4K: "Q4_K", F.Q8_0: "Q8_0", F.MXFP4: "MXFP4", F.Q3K_Q4K: "Q3_K/Q4_K"}[fmt]
     wl = W.Workload(f"{name} layer H 7168, 2 experts, k 1, T 5", fmt, 7168, 256, 2, 1, 5)
     say(wl.name)
     got, want, soe, S = _layer_case(wl, path=Q.MOE_PATH_DECODE)
@@ -439,6 +443,36 @@ def test_dsv3_sized_mxfp4_experts_many_tokens():
     tokens: several K units per wave (the prefetching loop) and several
     chunks of tokens per slot."""
     wl = W.Workload("DeepSeek-V3-sized MXFP4 experts, 16 resident, 24 tokens", F.MXFP4, 7168, 2048, 16, 2, 24)
+    say(wl.name)
+    F.set_num_threads(THREADS)
+    got, want, soe, S = _layer_case(wl, path=Q.MOE_PATH_DECODE)
+    _check_layer(wl, got, want, soe, S)
+    assert int(np.diff(got["slot_offsets"]).max()) > 2
+
+
+def test_decode_q3k_many_tokens_partial_residency():
+    """Q3_K gate/up + Q4_K down experts, 37 tokens over 12 experts, 8 of them
+    resident: chunks of two tokens per slot plus remainders, and a host list
+    that the host leg completes."""
+    wl = W.Workload("small Q3_K/Q4_K layer, 37 tokens, partial residency", F.Q3K_Q4K, 512, 256, 12, 4, 37)
+    say(wl.name)
+    soe = np.array([3, -1, 0, 5, -1, 1, 2, -1, 4, 6, -1, 7], dtype=np.int32)
+    blobs = W.expert_blobs(wl)
+    got, want, soe, S = _layer_case(wl, blobs=blobs, soe=soe, S=9, path=Q.MOE_PATH_DECODE)
+    _check_layer(wl, got, want, soe, S)
+    assert got["host_count"] > 0
+    x, logits = W.x_of(wl), W.logits_of(wl)
+    y_host = Q.moe_host_leg(wl.fmt, list(blobs), wl.H, wl.I, x, got["host_token"], got["host_expert"],
+                            got["host_weight"], threads=THREADS)
+    full = run_oracle(wl, blobs, x, logits, np.arange(wl.E, dtype=np.int32), None)
+    assert rel_max_err(got["y"] + y_host, full["y"]) <= DECODE_TOL
+
+
+def test_dsv3_sized_q3k_experts_many_tokens():
+    """DeepSeek-V3-sized experts of the engine's V4.1 files (Q3_K gate/up,
+    Q4_K down; H 7168, I 2048), 16 of them, 24 tokens: several K units per
+    wave in both GEMVs and several chunks of tokens per slot."""
+    wl = W.Workload("DeepSeek-V3-sized Q3_K/Q4_K experts, 16 resident, 24 tokens", F.Q3K_Q4K, 7168, 2048, 16, 2, 24)
     say(wl.name)
     F.set_num_threads(THREADS)
     got, want, soe, S = _layer_case(wl, path=Q.MOE_PATH_DECODE)
