@@ -54,19 +54,51 @@ typedef const float cf32;  // (C, S) pairs, two floats each
 
 // ------------------------------------------------------- block dot products
 
+// (w & mask) | magic in one v_and_or_b32.  gfx9's three-operand encoding
+// takes no literal and one scalar operand, so with both constants as
+// literals the compiler emits an and and an or (two instructions per fp16
+// pair); here the mask is in a scalar register and the magic number in a
+// vector register.  Used by the gate/up GEMVs (in the down GEMV's prefetch
+// loop it made the register allocator spill).  Not volatile: a volatile
+// version pinned the instruction order and made the gate/up GEMV slower.
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t magic) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(mask), "v"(magic));
+    return r;
+}
+struct AndOr {
+    uint32_t magic, m0, m1, m2, m3;
+    __device__ __forceinline__ AndOr(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+        magic = kMagic;
+        asm volatile("" : "+v"(magic));
+        asm("s_mov_b32 %0, %1" : "=s"(m0) : "i"(a));
+        asm("s_mov_b32 %0, %1" : "=s"(m1) : "i"(b));
+        asm("s_mov_b32 %0, %1" : "=s"(m2) : "i"(c));
+        asm("s_mov_b32 %0, %1" : "=s"(m3) : "i"(d));
+    }
+};
+
 // Q4_K: 16 quant bytes of one row and sub-block (element 8d+n in nibble n of
 // group d; groups stored 0, 2, 1, 3) against one activation record.  Returns
 // sum_e (1024 + q_e) x'_e where x' is the record's stored value (x or x/16).
-__device__ __forceinline__ float q4k_dot(const uint4 q, cu32* X) {
+template <bool AO>
+__device__ __forceinline__ float q4k_dot(const uint4 q, cu32* X, const AndOr& k) {
     const uint32_t w[4] = {q.x, q.z, q.y, q.w};
     float acc = 0.0f;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
         const uint32_t w8 = w[d] >> 8;
-        acc = fdot2u((w[d] & 0x000F000Fu) | kMagic, X[4 * d + 0], acc);
-        acc = fdot2u((w[d] & 0x00F000F0u) | kMagic, X[4 * d + 1], acc);
-        acc = fdot2u((w8 & 0x000F000Fu) | kMagic, X[4 * d + 2], acc);
-        acc = fdot2u((w8 & 0x00F000F0u) | kMagic, X[4 * d + 3], acc);
+        if (AO) {
+            acc = fdot2u(and_or(w[d], k.m0, k.magic), X[4 * d + 0], acc);
+            acc = fdot2u(and_or(w[d], k.m1, k.magic), X[4 * d + 1], acc);
+            acc = fdot2u(and_or(w8, k.m0, k.magic), X[4 * d + 2], acc);
+            acc = fdot2u(and_or(w8, k.m1, k.magic), X[4 * d + 3], acc);
+        } else {
+            acc = fdot2u((w[d] & 0x000F000Fu) | kMagic, X[4 * d + 0], acc);
+            acc = fdot2u((w[d] & 0x00F000F0u) | kMagic, X[4 * d + 1], acc);
+            acc = fdot2u((w8 & 0x000F000Fu) | kMagic, X[4 * d + 2], acc);
+            acc = fdot2u((w8 & 0x00F000F0u) | kMagic, X[4 * d + 3], acc);
+        }
     }
     return acc;
 }
@@ -109,22 +141,24 @@ __device__ __forceinline__ float mx4_dot(const uint4 q, cu32* X) {
 // elements 0-15 (group d = 0 at bits 4n, d = 1 at bits 4n + 2, n < 8; element
 // 8d + n), LB those of elements 16-31 (d = 2, 3 likewise); HB the high bits,
 // element 8d + n at bit 4n + (2 + d) % 4.  Aligning a group's high bits to
-// bit 4n + 2, above its low bits, then gives v = low + 4 high (0..7) in each
-// half of a pair by two and-or operations.  Returns the dot products over
+// bit 4n + 2, above its low bits, gives the group's v = low + 4 high (0..7)
+// in nibble n with one and and one and-or; the pairs then come out as for
+// Q4_K.  Returns the dot products over
 // the two 16-element sub-blocks (groups 0-1 and 2-3) of (1024 + v) with the
 // record's stored values.
-__device__ __forceinline__ float2 q3k_dot(uint32_t la, uint32_t lb, uint32_t hb, cu32* X) {
+__device__ __forceinline__ float2 q3k_dot(uint32_t la, uint32_t lb, uint32_t hb, cu32* X, const AndOr& k) {
     float acc[2] = {0.0f, 0.0f};
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
         const uint32_t lw = (d < 2 ? la : lb) >> (2 * (d & 1));
         const uint32_t hw = d == 0 ? hb : d == 1 ? hb >> 1 : d == 2 ? hb << 2 : hb << 1;
-        const uint32_t lw8 = lw >> 8, hw8 = hw >> 8;
+        // the group's v = low + 4 high in nibble n (bits 4n..4n+2)
+        const uint32_t t = and_or(hw, k.m2, lw & 0x33333333u), t8 = t >> 8;
         float& a = acc[d >> 1];
-        a = fdot2u((hw & 0x00040004u) | ((lw & 0x00030003u) | kMagic), X[4 * d + 0], a);
-        a = fdot2u((hw & 0x00400040u) | ((lw & 0x00300030u) | kMagic), X[4 * d + 1], a);
-        a = fdot2u((hw8 & 0x00040004u) | ((lw8 & 0x00030003u) | kMagic), X[4 * d + 2], a);
-        a = fdot2u((hw8 & 0x00400040u) | ((lw8 & 0x00300030u) | kMagic), X[4 * d + 3], a);
+        a = fdot2u(and_or(t, k.m0, k.magic), X[4 * d + 0], a);
+        a = fdot2u(and_or(t, k.m1, k.magic), X[4 * d + 1], a);
+        a = fdot2u(and_or(t8, k.m0, k.magic), X[4 * d + 2], a);
+        a = fdot2u(and_or(t8, k.m1, k.magic), X[4 * d + 3], a);
     }
     return make_float2(acc[0], acc[1]);
 }
@@ -425,6 +459,7 @@ template <int NT, int NMAT>
 __device__ __forceinline__ void half_dots(const UnitRegs<1, NMAT>& r, const uint4* hdr, int h, const uint32_t* lw,
                                           const float* lc, float (*acc)[NMAT]) {
     float ds[NMAT][8], dm[NMAT][8];
+    const AndOr k(0x000F000Fu, 0x00F000F0u, 0, 0);
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) q4k_header(hdr[m], ds[m], dm[m]);
 #pragma unroll
@@ -434,7 +469,7 @@ __device__ __forceinline__ void half_dots(const UnitRegs<1, NMAT>& r, const uint
             const uint32_t* X = lw + (t * 8 + j) * 16;
             const float c = lc[(t * 8 + j) * 2], sx = lc[(t * 8 + j) * 2 + 1];
 #pragma unroll
-            for (int m = 0; m < NMAT; ++m) acc[t][m] += ds[m][j] * (q4k_dot(r.q[j][m], X) - c) - dm[m][j] * sx;
+            for (int m = 0; m < NMAT; ++m) acc[t][m] += ds[m][j] * (q4k_dot<NMAT == 2>(r.q[j][m], X, k) - c) - dm[m][j] * sx;
         }
         // keep the scheduler from hoisting every sub-block's nibble
         // extraction at once
@@ -509,6 +544,7 @@ template <int NT, int NMAT>
 __device__ __forceinline__ void half_dots(const UnitRegs<3, NMAT>& r, const uint4* hdr, int h, const uint32_t* lw,
                                           const float* lc, float (*acc)[NMAT]) {
     float ds[NMAT][8];
+    const AndOr k(0x00070007u, 0x00700070u, 0x44444444u, 0);
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) q3k_scales(hdr[m], h, ds[m]);
 #pragma unroll
@@ -523,7 +559,7 @@ __device__ __forceinline__ void half_dots(const UnitRegs<3, NMAT>& r, const uint
                 const uint4 L = r.L[c][m], Hv = r.Hb[h][m];
                 const uint32_t la = (j & 1) ? L.z : L.x, lb = (j & 1) ? L.w : L.y;
                 const uint32_t hb = i == 0 ? Hv.x : i == 1 ? Hv.y : i == 2 ? Hv.z : Hv.w;
-                const float2 dd = q3k_dot(la, lb, hb, X);
+                const float2 dd = q3k_dot(la, lb, hb, X, k);
                 acc[t][m] += ds[m][2 * (j & 3)] * (dd.x - ka) + ds[m][2 * (j & 3) + 1] * (dd.y - kb);
             }
         }
