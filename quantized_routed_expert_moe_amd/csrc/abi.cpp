@@ -79,7 +79,8 @@ size_t packed_bytes(int format, int H, int I) {
 
 int resolve_path(int format, int T, int x_dtype, int path) {
     if (path != MOE_PATH_AUTO) return path;
-    return (format == MOE_FMT_Q4K && x_dtype == MOE_BF16 && T > 32) ? MOE_PATH_PREFILL : MOE_PATH_DECODE;
+    return ((format == MOE_FMT_Q4K || format == MOE_FMT_MXFP4) && x_dtype == MOE_BF16 && T > 32) ? MOE_PATH_PREFILL
+                                                                                                  : MOE_PATH_DECODE;
 }
 
 // ------------------------------------------------------------------ timers
@@ -408,9 +409,9 @@ moe_status ffn_common(int format, const void* slot_pool, size_t slot_stride, int
         if (y_dtype != MOE_F32) return fail(MOE_ERR_UNSUPPORTED, "the decode path writes MOE_F32 y_pairs");
         need = qmoe::decode_workspace_bytes(T, k, H, I);
     } else {
-        if (format != MOE_FMT_Q4K)
-            return fail(MOE_ERR_UNSUPPORTED, "the prefill path is implemented for Q4_K only (MOE_PATH_DECODE serves "
-                                             "Q8_0, MXFP4 and Q3_K/Q4_K at any T)");
+        if (format != MOE_FMT_Q4K && format != MOE_FMT_MXFP4)
+            return fail(MOE_ERR_UNSUPPORTED, "the prefill path is implemented for Q4_K and MXFP4 (MOE_PATH_DECODE "
+                                             "serves Q8_0 and Q3_K/Q4_K at any T)");
         if (x_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the prefill path takes MOE_BF16 x");
         // The GEMMs address x and h rows with 32-bit byte offsets, and the
         // tile list counts tiles in 16 bits.
@@ -429,7 +430,7 @@ moe_status ffn_common(int format, const void* slot_pool, size_t slot_stride, int
     qmoe::FfnArgs a{format, static_cast<const uint8_t*>(slot_pool), slot_stride, S, H, I, x, x_dtype, T, k,
                     slot_offsets, active_slots, num_active, perm_pair, y_pairs, y_dtype, ws};
     hipError_t e = p == MOE_PATH_DECODE ? qmoe::launch_ffn_decode(a, (hipStream_t)stream)
-                                        : qmoe::launch_ffn_prefill_q4k(a, (hipStream_t)stream);
+                                        : qmoe::launch_ffn_prefill(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "expert FFN launch");
     return MOE_OK;
 }
@@ -613,7 +614,7 @@ size_t moe_ffn_workspace_size(int format, int T, int k, int H, int I, int path) 
     if (check_shape(format, H, I) != MOE_OK || T < 0 || k < 1 || k > MOE_MAX_TOPK) return 0;
     const size_t dec = qmoe::decode_workspace_bytes(T, k, H, I);
     static_assert(MOE_MAX_EXPERTS == qmoe::kMaxExpertsInternal, "expert limits differ");
-    if (format != MOE_FMT_Q4K || path == MOE_PATH_DECODE) return dec;
+    if ((format != MOE_FMT_Q4K && format != MOE_FMT_MXFP4) || path == MOE_PATH_DECODE) return dec;
     const size_t pre = qmoe::prefill_workspace_bytes(T, k, H, I);
     if (path == MOE_PATH_PREFILL) return pre;
     return std::max(dec, pre);

@@ -49,6 +49,11 @@
 // dequantization of k16 step s + 1 are issued between the MFMAs of step s.
 // Row blocks past the tile's rows are neither loaded nor multiplied (the
 // kernel body is instantiated per row-block count).
+// MXFP4 weights (FMT 2) take the same path with another dequantization:
+// the lane's dword of 8 codes (byte p: element p low, p + 4 high) goes
+// through four v_cvt_scalef32_pk_bf16_fp4 with the block's E8M0 scale (exact
+// bf16 values for every scale in bf16's range) and four v_perm_b32 that put
+// the pairs in element order.
 // Workgroup numbering: the N tiles of one M tile run on one XCD (hardware:
 // XCD = workgroup id mod 8), consecutive M tiles on consecutive XCDs, so the
 // L2 of an XCD serves the A rows shared by its N tiles.
@@ -224,6 +229,7 @@ __device__ __forceinline__ bf16x8 dequant_frag(uint32_t w, float ds512, float nd
 // elements 0-3 and 4-7.
 struct DqPart {
     float q[8];
+    uint32_t p[4];  // MXFP4: the four converted pairs
     uint32_t out[4];
 };
 
@@ -247,6 +253,39 @@ __device__ __forceinline__ void dq_bc(DqPart& d, int half, float ds512, float nd
     }
 }
 
+// MXFP4: the block's E8M0 byte -> 2^(x - 127) (integer operations only; the
+// decode path's conversion).
+__device__ __forceinline__ float e8m0_scale(uint32_t x) {
+    return __uint_as_float((x << 23) | ((((x + 1) | (x - 1)) & 0x100u) << 14));
+}
+
+// MXFP4 dequantization in the same three pieces: (a) four conversions of a
+// code byte each to a bf16 pair (element p, element p + 4), scaled; (b) and
+// (c) byte permutes to pairs (0, 1), (2, 3), then (4, 5), (6, 7).
+__device__ __forceinline__ void mx4_dq_a(DqPart& d, uint32_t w, float scale) {
+    const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+    const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+    const uint32_t p2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+    const uint32_t p3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+    d.p[0] = p0;
+    d.p[1] = p1;
+    d.p[2] = p2;
+    d.p[3] = p3;
+}
+__device__ __forceinline__ void mx4_dq_bc(DqPart& d, int half) {
+    const uint32_t p0 = d.p[0], p1 = d.p[1], p2 = d.p[2], p3 = d.p[3];
+    const uint32_t sel = half ? 0x07060302u : 0x05040100u;  // high or low halves of each pair
+    d.out[2 * half] = __builtin_amdgcn_perm(p1, p0, sel);
+    d.out[2 * half + 1] = __builtin_amdgcn_perm(p3, p2, sel);
+}
+__device__ __forceinline__ bf16x8 mx4_frag(uint32_t w, float scale) {
+    DqPart d;
+    mx4_dq_a(d, w, scale);
+    mx4_dq_bc(d, 0);
+    mx4_dq_bc(d, 1);
+    return __builtin_bit_cast(bf16x8, make_uint4(d.out[0], d.out[1], d.out[2], d.out[3]));
+}
+
 // ------------------------------------------------------------- GEMM body
 
 struct TileCtx {
@@ -258,7 +297,9 @@ struct TileCtx {
     int K;
 };
 
-template <bool GATEUP, int NB>
+// FMT 1: Q4_K tiles (16-byte headers); FMT 2: MXFP4 tiles (8 scale bytes
+// per row and 256 inputs, read into the header's first two words).
+template <int FMT, bool GATEUP, int NB>
 __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* sA1, int wave, int lane,
                                           f32x16 (&acc)[kRowBlocks][2]) {
     // Two distinct LDS arrays (not one [2][..] array): the compiler can then
@@ -294,8 +335,17 @@ __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* s
     auto load_hdr = [&](int sb, uint4* h) {
         const uint8_t* tile = c.b_rowgroup + (size_t)sb * c.tile_bytes;
 #pragma unroll
-        for (int m = 0; m < 2; ++m) h[m] = ldg<uint4>(tile + c.hdr_off[m]);
+        for (int m = 0; m < 2; ++m) {
+            if (FMT == 2) {
+                const uint2 v = ldg<uint2>(tile + c.hdr_off[m]);
+                h[m] = make_uint4(v.x, v.y, 0u, 0u);
+            } else {
+                h[m] = ldg<uint4>(tile + c.hdr_off[m]);
+            }
+        }
     };
+    // MXFP4 scale of block j (0..7) of a unit from its header words
+    auto mx_scale = [](const uint4& h, int j) { return e8m0_scale(((j < 4 ? h.x : h.y) >> (8 * (j & 3))) & 0xFFu); };
 
     BQuant rb[2];
     uint4 hdr[2];
@@ -310,9 +360,13 @@ __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* s
         HeaderWords hw0[2];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            hw0[m] = header_words(hdr[m]);
-            fb_next0[m] = dequant_frag(rb[0].v[m][0].x, hw0[m].d512 * (float)(hw0[m].sc[0] & 0xFFu),
-                                       -(hw0[m].dmin * (float)(hw0[m].mn[0] & 0xFFu)));
+            if (FMT == 2) {
+                fb_next0[m] = mx4_frag(rb[0].v[m][0].x, mx_scale(hdr[m], 0));
+            } else {
+                hw0[m] = header_words(hdr[m]);
+                fb_next0[m] = dequant_frag(rb[0].v[m][0].x, hw0[m].d512 * (float)(hw0[m].sc[0] & 0xFFu),
+                                           -(hw0[m].dmin * (float)(hw0[m].mn[0] & 0xFFu)));
+            }
         }
     }
     __syncthreads();
@@ -322,6 +376,7 @@ __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* s
         HeaderWords hw[2];
 #pragma unroll
         for (int m = 0; m < 2; ++m) hw[m] = header_words(hdr[m]);
+        const uint4 hraw[2] = {hdr[0], hdr[1]};  // MXFP4: this unit's scale bytes
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int st = 2 * sb + u;
@@ -334,14 +389,21 @@ __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* s
             // next one's headers.  Past the last stage the loads repeat it (in
             // bounds, cache hits, never used).
             const int nst = min(st + 1, nstages - 1);
+            // Q4_K: 512 d sc and -dmin m of each sub-block; MXFP4: the block
+            // scale in ds512, ndm unused
             float ds512[2][4], ndm[2][4];
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int j = 4 * u + jj;
-                    ds512[m][jj] = hw[m].d512 * (float)((hw[m].sc[j >> 2] >> (8 * (j & 3))) & 0xFFu);
-                    ndm[m][jj] = -(hw[m].dmin * (float)((hw[m].mn[j >> 2] >> (8 * (j & 3))) & 0xFFu));
+                    if (FMT == 2) {
+                        ds512[m][jj] = mx_scale(hraw[m], j);
+                        ndm[m][jj] = 0.0f;
+                    } else {
+                        ds512[m][jj] = hw[m].d512 * (float)((hw[m].sc[j >> 2] >> (8 * (j & 3))) & 0xFFu);
+                        ndm[m][jj] = -(hw[m].dmin * (float)((hw[m].mn[j >> 2] >> (8 * (j & 3))) & 0xFFu));
+                    }
                 }
             bf16x8 fa[2][NB], fb[2][2];
             // Fragment of row block i, k16 step s: row 32 i + lane % 32 sits in
@@ -388,7 +450,10 @@ __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* s
                         // first k16 step of the next stage: sub-block 4 of this
                         // super-block, or sub-block 0 of the next one
                         wsrc[m] = rb[cur ^ 1].v[m][0].x;
-                        if (u == 0) {
+                        if (FMT == 2) {
+                            dsv[m] = u == 0 ? mx_scale(hraw[m], 4) : mx_scale(hdr[m], 0);
+                            ndv[m] = 0.0f;
+                        } else if (u == 0) {
                             dsv[m] = hw[m].d512 * (float)(hw[m].sc[1] & 0xFFu);
                             ndv[m] = -(hw[m].dmin * (float)(hw[m].mn[1] & 0xFFu));
                         } else {
@@ -418,12 +483,30 @@ __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* s
                                 load_b_one(nst, rb[cur ^ 1], 1, s);
                             }
                             break;
-                        case 5: dq_a(dp[0], wsrc[0]); break;
-                        case 11: dq_bc(dp[0], 0, dsv[0], ndv[0]); break;
-                        case 12: dq_bc(dp[0], 1, dsv[0], ndv[0]); break;
-                        case 13: dq_a(dp[1], wsrc[1]); break;
-                        case 14: dq_bc(dp[1], 0, dsv[1], ndv[1]); break;
-                        case 15: dq_bc(dp[1], 1, dsv[1], ndv[1]); break;
+                        case 5:
+                            if (FMT == 2) mx4_dq_a(dp[0], wsrc[0], dsv[0]);
+                            else dq_a(dp[0], wsrc[0]);
+                            break;
+                        case 11:
+                            if (FMT == 2) mx4_dq_bc(dp[0], 0);
+                            else dq_bc(dp[0], 0, dsv[0], ndv[0]);
+                            break;
+                        case 12:
+                            if (FMT == 2) mx4_dq_bc(dp[0], 1);
+                            else dq_bc(dp[0], 1, dsv[0], ndv[0]);
+                            break;
+                        case 13:
+                            if (FMT == 2) mx4_dq_a(dp[1], wsrc[1], dsv[1]);
+                            else dq_a(dp[1], wsrc[1]);
+                            break;
+                        case 14:
+                            if (FMT == 2) mx4_dq_bc(dp[1], 0);
+                            else dq_bc(dp[1], 0, dsv[1], ndv[1]);
+                            break;
+                        case 15:
+                            if (FMT == 2) mx4_dq_bc(dp[1], 1);
+                            else dq_bc(dp[1], 1, dsv[1], ndv[1]);
+                            break;
                         default: {
                             // A fragment reads: items 0, 1, 3, 4, 6, 7, 9, 10
                             const int ri = j == 0 ? 0 : j == 1 ? 1 : j == 3 ? 2 : j == 4 ? 3 : j == 6 ? 4 : j == 7 ? 5
@@ -468,7 +551,7 @@ __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* s
     } while (++sb < nsb);
 }
 
-template <bool GATEUP>
+template <int FMT, bool GATEUP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_gemm_kernel(
     const uint8_t* __restrict__ pool, size_t stride, int S, int H, int I, const uint16_t* __restrict__ ain, int T,
     int k, const int32_t* __restrict__ perm, const int4* __restrict__ tiles, const int32_t* __restrict__ ntiles,
@@ -527,27 +610,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // block 0 its gate rows, block 1 its up rows.  Down: packed tile cb,
     // block m = rows 32m..32m+31.  Lane: row lane % 32, quant bytes
     // 8 * (lane / 32).. of each (row, sub-block) slot.
+    // Per tile: Q4_K headers are 16 bytes per row (1 KB per matrix), MXFP4
+    // scales 8 bytes per row (512 B per matrix); the quants of block j follow.
+    const int hb = FMT == 2 ? 8 : 16;
     if (GATEUP) {
         const int fb = nt * kWaves + wave;
-        c.b_rowgroup = wbase + (size_t)(fb >> 1) * (H / 256) * kQ4kGateUpTile;
+        const int gtile = FMT == 2 ? kMx4GateUpTile : kQ4kGateUpTile;
+        c.b_rowgroup = wbase + (size_t)(fb >> 1) * (H / 256) * gtile;
         const int r = (fb & 1) * 32 + r32;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            c.hdr_off[m] = m * 1024 + r * 16;
-            c.q_off[m] = 2048 + m * 1024 + r * 16 + 8 * hsel;
+            c.hdr_off[m] = m * 64 * hb + r * hb;
+            c.q_off[m] = 128 * hb + m * 1024 + r * 16 + 8 * hsel;
         }
         c.q_step = 2048;
-        c.tile_bytes = kQ4kGateUpTile;
+        c.tile_bytes = gtile;
     } else {
         const int cb = nt * kWaves + wave;
-        c.b_rowgroup = wbase + q4k_gateup_bytes(H, I) + (size_t)cb * (I / 256) * kQ4kDownTile;
+        const int dtile = FMT == 2 ? kMx4DownTile : kQ4kDownTile;
+        c.b_rowgroup = wbase + (FMT == 2 ? mx4_gateup_bytes(H, I) : q4k_gateup_bytes(H, I)) +
+                       (size_t)cb * (I / 256) * dtile;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            c.hdr_off[m] = (32 * m + r32) * 16;
-            c.q_off[m] = 1024 + (32 * m + r32) * 16 + 8 * hsel;
+            c.hdr_off[m] = (32 * m + r32) * hb;
+            c.q_off[m] = 64 * hb + (32 * m + r32) * 16 + 8 * hsel;
         }
         c.q_step = 1024;
-        c.tile_bytes = kQ4kDownTile;
+        c.tile_bytes = dtile;
     }
 
     f32x16 acc[kRowBlocks][2];
@@ -559,14 +648,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             for (int r = 0; r < 16; ++r) acc[i][m][r] = 0.f;
 
     switch (nblk) {
-        case 1: tile_gemm<GATEUP, 1>(c, sA0, sA1, wave, lane, acc); break;
-        case 2: tile_gemm<GATEUP, 2>(c, sA0, sA1, wave, lane, acc); break;
-        case 3: tile_gemm<GATEUP, 3>(c, sA0, sA1, wave, lane, acc); break;
-        case 4: tile_gemm<GATEUP, 4>(c, sA0, sA1, wave, lane, acc); break;
-        case 5: tile_gemm<GATEUP, 5>(c, sA0, sA1, wave, lane, acc); break;
-        case 6: tile_gemm<GATEUP, 6>(c, sA0, sA1, wave, lane, acc); break;
-        case 7: tile_gemm<GATEUP, 7>(c, sA0, sA1, wave, lane, acc); break;
-        default: tile_gemm<GATEUP, 8>(c, sA0, sA1, wave, lane, acc); break;
+        case 1: tile_gemm<FMT, GATEUP, 1>(c, sA0, sA1, wave, lane, acc); break;
+        case 2: tile_gemm<FMT, GATEUP, 2>(c, sA0, sA1, wave, lane, acc); break;
+        case 3: tile_gemm<FMT, GATEUP, 3>(c, sA0, sA1, wave, lane, acc); break;
+        case 4: tile_gemm<FMT, GATEUP, 4>(c, sA0, sA1, wave, lane, acc); break;
+        case 5: tile_gemm<FMT, GATEUP, 5>(c, sA0, sA1, wave, lane, acc); break;
+        case 6: tile_gemm<FMT, GATEUP, 6>(c, sA0, sA1, wave, lane, acc); break;
+        case 7: tile_gemm<FMT, GATEUP, 7>(c, sA0, sA1, wave, lane, acc); break;
+        default: tile_gemm<FMT, GATEUP, 8>(c, sA0, sA1, wave, lane, acc); break;
     }
 
     // Epilogue through LDS (both A buffers are free after the loop's last
@@ -675,7 +764,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
 // ----------------------------------------------------------------- launch
 
-hipError_t launch_ffn_prefill_q4k(const FfnArgs& a, hipStream_t s) {
+hipError_t launch_ffn_prefill(const FfnArgs& a, hipStream_t s) {
     const int P = a.T * a.k;
     const int mt = max_tiles(P, a.S);
     if (a.S > 1024) return hipErrorInvalidValue;  // one tiles-kernel thread per active slot
@@ -698,16 +787,18 @@ hipError_t launch_ffn_prefill_q4k(const FfnArgs& a, hipStream_t s) {
     const int mgroups = (mt + 7) / 8;
     const int nt_gu = a.I / kGateUpFeatures, nt_dn = a.H / kDownColumns;
     timer_before(kStagePrefillGateUp, s);
-    hipLaunchKernelGGL(prefill_gemm_kernel<true>, dim3(8 * nt_gu * mgroups), dim3(kThreads), 0, s, a.pool, a.stride,
-                       a.S, a.H, a.I, static_cast<const uint16_t*>(a.x), a.T, a.k, a.perm_pair, tiles, ntiles,
-                       static_cast<void*>(h), 0);
+    auto gateup = a.format == 2 ? prefill_gemm_kernel<2, true> : prefill_gemm_kernel<1, true>;
+    auto down = a.format == 2 ? prefill_gemm_kernel<2, false> : prefill_gemm_kernel<1, false>;
+    hipLaunchKernelGGL(gateup, dim3(8 * nt_gu * mgroups), dim3(kThreads), 0, s, a.pool, a.stride, a.S, a.H, a.I,
+                       static_cast<const uint16_t*>(a.x), a.T, a.k, a.perm_pair, tiles, ntiles, static_cast<void*>(h),
+                       0);
     timer_after(kStagePrefillGateUp, s);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 
     timer_before(kStagePrefillDown, s);
-    hipLaunchKernelGGL(prefill_gemm_kernel<false>, dim3(8 * nt_dn * mgroups), dim3(kThreads), 0, s, a.pool, a.stride,
-                       a.S, a.H, a.I, (const uint16_t*)h, a.T, a.k, a.perm_pair, tiles, ntiles, a.y_pairs, a.y_dtype);
+    hipLaunchKernelGGL(down, dim3(8 * nt_dn * mgroups), dim3(kThreads), 0, s, a.pool, a.stride, a.S, a.H, a.I,
+                       (const uint16_t*)h, a.T, a.k, a.perm_pair, tiles, ntiles, a.y_pairs, a.y_dtype);
     timer_after(kStagePrefillDown, s);
     return hipGetLastError();
 }
