@@ -264,9 +264,11 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def bench_prefill(args, blobs, pool, stride) -> dict:
+def bench_prefill(args, blobs, pool, stride, fmt=None, ceiling=True) -> dict:
     """The same Qwen3-30B-A3B-shaped layer at prefill: 4096 bf16 tokens with
-    Zipf(1.0)-skewed routing, through the grouped bf16 MFMA GEMM path."""
+    Zipf(1.0)-skewed routing, through the grouped bf16 MFMA GEMM path (Q4_K
+    experts, or fmt's)."""
+    import dataclasses
     import numpy as np
     import torch
 
@@ -274,7 +276,7 @@ def bench_prefill(args, blobs, pool, stride) -> dict:
     from fixtures import workloads as W
     from quantized_routed_expert_moe_amd.layer import LayerSpec, MoELayer
 
-    wl = W.QWEN3_PREFILL
+    wl = W.QWEN3_PREFILL if fmt is None else dataclasses.replace(W.QWEN3_PREFILL, fmt=fmt)
     x = torch.from_numpy(W.x_of(wl).view(np.int16)).cuda().view(torch.bfloat16)
     lg = torch.from_numpy(W.logits_of(wl)).cuda()
     soe = torch.arange(wl.E, dtype=torch.int32, device="cuda")
@@ -317,7 +319,8 @@ def bench_prefill(args, blobs, pool, stride) -> dict:
         "tokens_per_s": round(wl.T / (ms_step * 1e-3), 1),
         "expert_rows": {"total": M, "max": int(counts.max()), "median": float(np.median(counts)),
                         "min": int(counts.min())},
-        "roofline": {"bound": "mfma", "kernel": "prefill gate/up grouped GEMM (Q4_K->bf16 tiles, bf16 MFMA)",
+        "roofline": {"bound": "mfma", "kernel": "prefill gate/up grouped GEMM (%s->bf16 fragments, bf16 MFMA)" %
+                     ("Q4_K" if fmt is None else "MXFP4"),
                      "achieved": round(gu_tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gu_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                      "algorithmic_flop_per_launch": gu_flop, "avg_launch_us": round(kern["gemm_gateup"], 2)},
@@ -327,7 +330,7 @@ def bench_prefill(args, blobs, pool, stride) -> dict:
         "expert_gemms_frac": round((gu_flop + dn_flop) / ((kern["gemm_gateup"] + kern["gemm_down"]) * 1e-6) / 1e12 /
                                    MFMA_BF16_PEAK_TFLOPS, 4),
         "kernels_us": {k2: round(v, 2) for k2, v in kern.items()},
-        "library_gemm_ceiling": library_gemm_ceiling(M, wl.H, wl.I),
+        "library_gemm_ceiling": library_gemm_ceiling(M, wl.H, wl.I) if ceiling else None,
     }
 
 
@@ -529,6 +532,10 @@ def bench_formats(args, threads: int) -> dict:
              "layer_GBs": round(layer_bytes / (ms_step * 1e-3) / 1e9, 1),
              "layer_frac_of_hbm": round(layer_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
              "pool_copies": copies}
+        if key == "mxfp4_qwen3_T2" and args.prefill_steps > 0:
+            pre = bench_prefill(args, None, pools[0], stride, fmt=F.MXFP4, ceiling=False)
+            r["prefill_T4096"] = {kk: pre[kk] for kk in ("ms_per_step", "tokens_per_s", "roofline", "down_gemm_TFLOPs",
+                                                         "expert_gemms_frac", "kernels_us")}
         if not wl.I_shared:  # stage 3 then times only the routed gate/up GEMV
             gu_us = 1e3 * gu_ms / max(gu_n, 1)
             gbytes = mean_uniq * gateup_bytes(wl)
