@@ -403,10 +403,64 @@ void fx_encode_q3k(const float* x, int64_t n, uint8_t* out) {
     }
 }
 
+/* n floats (n % 256 == 0) -> n/256 Q5_K super-blocks of 176 bytes: the
+ * Q4_K scheme with 31 levels (scale_j = (hi - lo) / 31, q clamped to
+ * [0, 31]); fp16 d, dmin, the 12 scale bytes as in Q4_K, then 32 bytes of
+ * high bits (bit j of byte l: element l of sub-block j), then the low
+ * nibbles in the Q4_K order. */
+void fx_encode_q5k(const float* x, int64_t n, uint8_t* out) {
+    for (int64_t b = 0; b < n / 256; ++b) {
+        const float* v = x + b * 256;
+        uint8_t* o = out + b * 176;
+        memset(o, 0, 176);
+        float scale[8], mins[8], maxscale = 0.0f, maxmin = 0.0f;
+        for (int j = 0; j < 8; ++j) {
+            float lo = 0.0f, hi = v[j * 32];
+            for (int i = 0; i < 32; ++i) {
+                float t = v[j * 32 + i];
+                if (t < lo) lo = t;
+                if (t > hi) hi = t;
+            }
+            scale[j] = (hi - lo) / 31.0f;
+            mins[j] = -lo;
+            if (scale[j] > maxscale) maxscale = scale[j];
+            if (mins[j] > maxmin) maxmin = mins[j];
+        }
+        uint16_t dh = fx_f32_to_f16(maxscale / 63.0f), mh = fx_f32_to_f16(maxmin / 63.0f);
+        float df = fx_f16_to_f32(dh), mf = fx_f16_to_f32(mh);
+        int sc[8], mm[8];
+        for (int j = 0; j < 8; ++j) {
+            float s2 = df > 0.0f ? round_half_away(scale[j] / df) : 0.0f;
+            float m2 = mf > 0.0f ? round_half_away(mins[j] / mf) : 0.0f;
+            sc[j] = s2 < 0.0f ? 0 : (s2 > 63.0f ? 63 : (int)s2);
+            mm[j] = m2 < 0.0f ? 0 : (m2 > 63.0f ? 63 : (int)m2);
+        }
+        put_u16(o, dh);
+        put_u16(o + 2, mh);
+        uint8_t* s12 = o + 4;
+        for (int j = 0; j < 4; ++j) {
+            s12[j] = (uint8_t)((sc[j] & 63) | ((sc[j + 4] >> 4) << 6));
+            s12[j + 4] = (uint8_t)((mm[j] & 63) | ((mm[j + 4] >> 4) << 6));
+            s12[j + 8] = (uint8_t)((sc[j + 4] & 15) | ((mm[j + 4] & 15) << 4));
+        }
+        uint8_t* qh = o + 16;
+        uint8_t* qs = o + 48;
+        for (int j = 0; j < 8; ++j) {
+            float step = df * (float)sc[j], off = mf * (float)mm[j];
+            for (int i = 0; i < 32; ++i) {
+                float q = step > 0.0f ? round_half_away((v[j * 32 + i] + off) / step) : 0.0f;
+                int qi = q < 0.0f ? 0 : (q > 31.0f ? 31 : (int)q);
+                qs[(j / 2) * 32 + i] |= (uint8_t)((qi & 15) << (4 * (j % 2)));
+                qh[i] |= (uint8_t)((qi >> 4) << j);
+            }
+        }
+    }
+}
+
 /* ------------------------------------------------------------- experts */
 
 /* Block types; FX_Q3K_Q4K is the mixed expert (Q3_K gate and up, Q4_K down). */
-enum { FX_Q8_0 = 0, FX_Q4K = 1, FX_MXFP4 = 2, FX_Q3K_Q4K = 3, FX_Q3K = 4 };
+enum { FX_Q8_0 = 0, FX_Q4K = 1, FX_MXFP4 = 2, FX_Q3K_Q4K = 3, FX_Q5K = 4, FX_Q3K = 100 };
 
 static int gate_up_fmt(int fmt) { return fmt == FX_Q3K_Q4K ? FX_Q3K : fmt; }
 static int down_fmt(int fmt) { return fmt == FX_Q3K_Q4K ? FX_Q4K : fmt; }
@@ -416,6 +470,7 @@ static int64_t row_bytes(int fmt, int64_t cols) {
         case FX_Q8_0: return cols / 32 * 34;
         case FX_MXFP4: return cols / 32 * 17;
         case FX_Q3K: return cols / 256 * 110;
+        case FX_Q5K: return cols / 256 * 176;
         default: return cols / 256 * 144;
     }
 }
@@ -424,6 +479,7 @@ static void encode_row(int fmt, const float* x, int64_t n, uint8_t* out) {
     if (fmt == FX_Q8_0) fx_encode_q8_0(x, n, out);
     else if (fmt == FX_MXFP4) fx_encode_mxfp4(x, n, out);
     else if (fmt == FX_Q3K) fx_encode_q3k(x, n, out);
+    else if (fmt == FX_Q5K) fx_encode_q5k(x, n, out);
     else fx_encode_q4k(x, n, out);
 }
 

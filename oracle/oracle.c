@@ -33,7 +33,8 @@ enum {
     D_MXFP4_INTERLEAVED = 13,  /* MXFP4 elements read as consecutive nibble pairs */
     D_MXFP4_BIAS_128 = 14,     /* MXFP4 scale exponent bias 128 instead of 127 */
     D_Q3K_SCALE_UNBIASED = 15, /* Q3_K 6-bit scales used without the -32 */
-    D_Q3K_HMASK_INVERTED = 16  /* Q3_K high bit read with the opposite sense */
+    D_Q3K_HMASK_INVERTED = 16, /* Q3_K high bit read with the opposite sense */
+    D_Q5K_HIGH_BIT_ORDER = 17  /* Q5_K high bit of element l taken from byte j*4 + l/8 */
 };
 
 void oracle_set_threads(int n) {
@@ -187,10 +188,38 @@ void oracle_dequant_q3k(const uint8_t* blocks, int64_t n, double* out) {
     }
 }
 
+/* Q5_K super-block (176 bytes): fp16 d, fp16 dmin, 12 scale bytes (the Q4_K
+ * packing), 32 bytes of high bits (qh), 128 bytes of low nibbles (the Q4_K
+ * order).  Element l of sub-block j: low four bits as in Q4_K, high bit =
+ * bit j of qh[l]; q = low + 16 * high (0..31).  w = d * sc_j * q - dmin * m_j.
+ * Parity pinned by hand-built golden blocks and the encoder round trip. */
+void oracle_dequant_q5k(const uint8_t* blocks, int64_t n, double* out) {
+    for (int64_t b = 0; b < n / 256; ++b) {
+        const uint8_t* blk = blocks + b * 176;
+        double d = half_le(blk);
+        double dmin = half_le(blk + 2);
+        const uint8_t* s12 = blk + 4;
+        const uint8_t* qh = blk + 16;
+        const uint8_t* qs = blk + 48;
+        for (int j = 0; j < 8; ++j) {
+            int sc, m;
+            q4k_scale_min(s12, j, &sc, &m);
+            for (int l = 0; l < 32; ++l) {
+                uint8_t byte = qs[(j / 2) * 32 + l];
+                int low = (j % 2) ? (byte >> 4) : (byte & 15);
+                int high = g_defect == D_Q5K_HIGH_BIT_ORDER ? (qh[j * 4 + l / 8] >> (l % 8)) & 1 : (qh[l] >> j) & 1;
+                int q = low + 16 * high;
+                out[b * 256 + j * 32 + l] = d * (double)sc * (double)q - dmin * (double)m;
+            }
+        }
+    }
+}
+
 static void dequant_row(int fmt, const uint8_t* row, int64_t n, double* out) {
     if (fmt == ORACLE_Q8_0) oracle_dequant_q8_0(row, n, out);
     else if (fmt == ORACLE_MXFP4) oracle_dequant_mxfp4(row, n, out);
     else if (fmt == ORACLE_Q3K) oracle_dequant_q3k(row, n, out);
+    else if (fmt == ORACLE_Q5K) oracle_dequant_q5k(row, n, out);
     else oracle_dequant_q4k(row, n, out);
 }
 
@@ -199,6 +228,7 @@ static int64_t row_bytes(int fmt, int64_t cols) {
         case ORACLE_Q8_0: return cols / 32 * 34;
         case ORACLE_MXFP4: return cols / 32 * 17;
         case ORACLE_Q3K: return cols / 256 * 110;
+        case ORACLE_Q5K: return cols / 256 * 176;
         default: return cols / 256 * 144;
     }
 }

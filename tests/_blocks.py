@@ -126,9 +126,36 @@ def random_q3k_matrix(rng: np.random.Generator, rows: int, cols: int, d_bits: in
     return np.frombuffer(b"".join(parts), dtype=np.uint8).copy(), dense
 
 
+def q5k_superblock(d_bits: int, dmin_bits: int, sc, m, q) -> bytes:
+    """q: [8][32] ints in 0..31; sc, m: 8 ints in 0..63 (Q4_K header, 32 high-bit bytes, Q4_K nibbles)."""
+    base = bytearray(q4k_superblock(d_bits, dmin_bits, sc, m, [[int(v) & 15 for v in r] for r in q]))
+    qh = [0] * 32
+    for j in range(8):
+        for l in range(32):
+            qh[l] |= (int(q[j][l]) >> 4) << j
+    return bytes(base[:16]) + bytes(qh) + bytes(base[16:])
+
+
+def random_q5k_matrix(rng: np.random.Generator, rows: int, cols: int, d_bits: int = 0x2000, dmin_bits: int = 0x1C00):
+    """A Q5_K matrix with random 6-bit scales/mins and 5-bit quants; returns (bytes, exact dense values)."""
+    d, dmin = half_bits_value(d_bits), half_bits_value(dmin_bits)
+    dense = np.empty((rows, cols), dtype=np.float64)
+    parts = []
+    for r in range(rows):
+        for sb in range(cols // 256):
+            sc = rng.integers(0, 64, size=8)
+            m = rng.integers(0, 64, size=8)
+            q = rng.integers(0, 32, size=(8, 32))
+            parts.append(q5k_superblock(d_bits, dmin_bits, sc, m, q))
+            for j in range(8):
+                dense[r, sb * 256 + j * 32: sb * 256 + (j + 1) * 32] = d * sc[j] * q[j] - dmin * m[j]
+    return np.frombuffer(b"".join(parts), dtype=np.uint8).copy(), dense
+
+
 def random_expert(rng: np.random.Generator, fmt: int, H: int, I: int):
     """Canonical blob Wg|Wu|Wd with exactly known dense matrices (fmt 3: Q3_K gate/up, Q4_K down)."""
-    make_gu = {0: random_q8_0_matrix, 1: random_q4k_matrix, 2: random_mxfp4_matrix, 3: random_q3k_matrix}[fmt]
+    make_gu = {0: random_q8_0_matrix, 1: random_q4k_matrix, 2: random_mxfp4_matrix, 3: random_q3k_matrix,
+               4: random_q5k_matrix}[fmt]
     make_dn = random_q4k_matrix if fmt == 3 else make_gu
     bg, g = make_gu(rng, I, H)
     bu, u = make_gu(rng, I, H)

@@ -126,6 +126,31 @@ def q3k_case(name: str, d_bits: int, sc: list[int], q: list[int], note: str) -> 
                 expected=[frac_str(v) for v in expected])
 
 
+def q5k_case(name: str, d_bits: int, dmin_bits: int, sc: list[int], m: list[int], q: list[list[int]],
+             note: str) -> dict:
+    """One Q5_K super-block: the Q4_K header (d, dmin, 12 packed scale/min
+    bytes), 32 bytes of high bits (bit j of byte l: element l of sub-block
+    j), 128 bytes of low nibbles in the Q4_K order; q in 0..31."""
+    assert len(sc) == 8 and len(m) == 8 and len(q) == 8
+    assert all(0 <= v < 64 for v in sc + m) and all(len(r) == 32 and all(0 <= v < 32 for v in r) for r in q)
+    s12 = [0] * 12
+    for j in range(4):
+        s12[j] = (sc[j] & 63) | ((sc[j + 4] >> 4) << 6)
+        s12[j + 4] = (m[j] & 63) | ((m[j + 4] >> 4) << 6)
+        s12[j + 8] = (sc[j + 4] & 15) | ((m[j + 4] & 15) << 4)
+    qh, qs = [0] * 32, [0] * 128
+    for j in range(8):
+        for l in range(32):
+            qs[(j // 2) * 32 + l] |= (q[j][l] & 15) << (4 * (j % 2))
+            qh[l] |= (q[j][l] >> 4) << j
+    raw = [d_bits & 0xFF, d_bits >> 8, dmin_bits & 0xFF, dmin_bits >> 8] + s12 + qh + qs
+    assert len(raw) == 176
+    d, dmin = half_value(d_bits), half_value(dmin_bits)
+    expected = [d * sc[j] * q[j][l] - dmin * m[j] for j in range(8) for l in range(32)]
+    return dict(name=name, format="Q5_K", note=note, d_bits=d_bits, dmin_bits=dmin_bits, sc=sc, m=m, q=q,
+                bytes_hex=bytes(raw).hex(), expected=[frac_str(v) for v in expected])
+
+
 def main() -> None:
     cases = []
     cases.append(q8_0_case(
@@ -166,6 +191,10 @@ def main() -> None:
     cases.append(q3k_case(
         "q3k_high_bits", 0x2C00, [(5 * j) % 64 - 32 for j in range(16)], [3 if i % 3 else -4 for i in range(256)],
         "d = 1/16; q alternates between the extremes 3 and -4 (high bit set / clear)"))
+    cases.append(q5k_case(
+        "q5k_every_field", 0x3400, 0x3000, [1, 17, 33, 63, 20, 47, 5, 62], [63, 0, 16, 31, 48, 15, 32, 1],
+        [[(5 * l + 3 * j) % 32 for l in range(32)] for j in range(8)],
+        "d = 1/4, dmin = 1/8; every q in 0..31 in every sub-block (high bit set and clear); scales >= 16"))
     doc = dict(
         citation=("Stored block types: bloomery README of 2026-09-24 (shared experts in Q8_0) and bloomery README "
                   "0.3.1, 'Status (0.3.1)' table, 'Quant types' row (card experts in Q4_K to Q6_K and MXFP4); "
@@ -173,7 +202,8 @@ def main() -> None:
                   "MXFP4 element and scale encodings of the OCP Microscaling Formats (MX) v1.0 specification, "
                   "byte order as read for this build (scale byte, then elements 0-15 in low nibbles, 16-31 in "
                   "high nibbles); Q3_K (bloomery README 0.3.11, limits list: the V4.1 card experts' gate and up "
-                  "matrices) in the GGUF order as read for this build."),
+                  "matrices) in the GGUF order as read for this build; Q5_K (README 0.3.1 'Quant types' row: card "
+                  "experts in Q4_K to Q6_K) likewise."),
         derivation="expected[i] written by tests/golden/make_golden.py with exact rationals from the listed fields",
         cases=cases)
     with open(os.path.join(HERE, "quant_blocks.json"), "w") as f:

@@ -35,7 +35,7 @@ def pin_golden_blocks() -> bool:
     ok = True
     for case in doc["cases"]:
         raw = np.frombuffer(bytes.fromhex(case["bytes_hex"]), dtype=np.uint8)
-        fmt = {"Q8_0": O.Q8_0, "Q4_K": O.Q4K, "MXFP4": O.MXFP4, "Q3_K": O.Q3K}[case["format"]]
+        fmt = {"Q8_0": O.Q8_0, "Q4_K": O.Q4K, "MXFP4": O.MXFP4, "Q3_K": O.Q3K, "Q5_K": O.Q5K}[case["format"]]
         got = O.dequant(fmt, raw, len(case["expected"]))
         want = np.array([float(Fraction(v)) for v in case["expected"]])
         ok &= bool(np.array_equal(got, want))
@@ -74,6 +74,16 @@ def pin_encoder_round_trip() -> bool:
     ok &= bool(np.all(np.abs(got - w) <= np.repeat(s, 32, axis=1)))
     ok &= bool(np.all(np.abs(w).reshape(64, -1, 32).max(axis=2) <= 6 * s))
     ok &= bool(np.corrcoef(got.ravel(), w.ravel())[0, 1] > 0.95)
+    # Q5_K: as Q4_K with 31 steps: q rounding (<= d*sc/2 <= 31.5 d), scale
+    # rounding over 31 steps (<= 15.5 d), min rounding (<= dmin/2), fp16 slack.
+    raw = F.encode(O.Q5K, w.astype(np.float32))
+    got = O.dequant(O.Q5K, raw, w.size).reshape(w.shape)
+    blk = raw.reshape(-1, 176)
+    d = np.array([B.half_bits_value(int(b[0]) | (int(b[1]) << 8)) for b in blk])
+    dm = np.array([B.half_bits_value(int(b[2]) | (int(b[3]) << 8)) for b in blk])
+    bound = np.repeat((48 * d + 0.5 * dm) * (1 + 2.0 ** -9) + 1e-12, 256).reshape(w.shape)
+    ok &= bool(np.all(np.abs(got - w) <= bound))
+    ok &= bool(np.corrcoef(got.ravel(), w.ravel())[0, 1] > 0.99)
     # Q3_K: the step d*sc_j of sub-block j maps its largest element to -4 up
     # to scale rounding (half a d) and clamping at 3; every weight lies within
     # |d sc_j| + 2.5 d of its value (d: the super-block's fp16 scale).
@@ -144,7 +154,7 @@ def _dense_ffn(g, u, dn, x):
 
 def pin_ffn_dense(fmt: int) -> bool:
     rng = np.random.default_rng(17 + fmt)
-    H, I = {O.Q4K: (512, 256), O.Q8_0: (96, 64), O.MXFP4: (128, 96), O.Q3K_Q4K: (512, 256)}[fmt]
+    H, I = {O.Q4K: (512, 256), O.Q8_0: (96, 64), O.MXFP4: (128, 96), O.Q3K_Q4K: (512, 256), O.Q5K: (512, 256)}[fmt]
     blob, (g, u, dn) = B.random_expert(rng, fmt, H, I)
     x = rng.normal(size=H)
     got = O.expert_ffn(fmt, blob, H, I, x)
@@ -244,6 +254,7 @@ PINS = {
     "ffn_dense_q4k": lambda: pin_ffn_dense(O.Q4K),
     "ffn_dense_mxfp4": lambda: pin_ffn_dense(O.MXFP4),
     "ffn_dense_q3k_q4k": lambda: pin_ffn_dense(O.Q3K_Q4K),
+    "ffn_dense_q5k": lambda: pin_ffn_dense(O.Q5K),
     "layer_brute_softmax_partial": lambda: pin_layer_brute_force(O.SOFTMAX, True),
     "layer_brute_sigmoid_full": lambda: pin_layer_brute_force(O.SIGMOID, False),
     "disjoint_halves": pin_disjoint_halves,
@@ -291,6 +302,8 @@ DEFECTS = [
     (16, "golden_blocks"),                 # Q3_K high bit inverted
     (16, "ffn_dense_q3k_q4k"),
     (16, "encoder_round_trip"),
+    (17, "golden_blocks"),                 # Q5_K high bits from the wrong byte
+    (17, "ffn_dense_q5k"),
 ]
 
 
