@@ -470,10 +470,11 @@ def bench_formats(args, threads: int) -> dict:
     res = {}
     def gateup_bytes(wl) -> int:  # stored bytes of one expert's gate and up matrices
         w = 2 * wl.H * wl.I
-        return {F.MXFP4: w // 32 * 17, F.Q3K_Q4K: w // 256 * 110, F.Q4K: w // 256 * 144}[wl.fmt]
+        return {F.MXFP4: w // 32 * 17, F.Q3K_Q4K: w // 256 * 110, F.Q4K: w // 256 * 144, F.Q5K: w // 256 * 176}[wl.fmt]
 
     for key, wl, copies in (("mxfp4_qwen3_T2", W.QWEN3_MXFP4_DECODE_T2, 8), ("mxfp4_dsv3_T2", W.DSV3_MXFP4_DECODE_T2, 1),
-                            ("q3k_q4k_dsv3_T2", W.DSV3_Q3K_DECODE_T2, 1)):
+                            ("q3k_q4k_dsv3_T2", W.DSV3_Q3K_DECODE_T2, 1), ("q5k_qwen3_T2", W.QWEN3_Q5K_DECODE_T2, 8),
+                            ("q5k_dsv3_T2", W.DSV3_Q5K_DECODE_T2, 1)):
         blobs = W.expert_blobs(wl)
         nb = Q.moe_expert_blob_bytes(wl.fmt, wl.H, wl.I)
         npk = Q.moe_packed_blob_bytes(wl.fmt, wl.H, wl.I)
@@ -545,9 +546,9 @@ def bench_formats(args, threads: int) -> dict:
         res[key] = r
         del graphs, layer, pools, shared
         torch.cuda.empty_cache()
-    res["note"] = ("MXFP4 codes converted to fp16 by the hardware FP4 conversion, Q3_K quants by two and-or "
-                   "operations per fp16 pair; fp16 x fp16 dot products, fp32 accumulate; expert_bytes and layer bytes "
-                   "count the stored (canonical) bytes")
+    res["note"] = ("MXFP4 codes converted to fp16 by the hardware FP4 conversion, Q3_K and Q5_K quants by and-or "
+                   "operations into fp16 magic numbers; fp16 x fp16 dot products, fp32 accumulate; expert_bytes and "
+                   "layer bytes count the stored (canonical) bytes")
     return res
 
 

@@ -17,7 +17,8 @@
  *   moe_expert_ffn_q4k /      dequantize + SwiGLU expert FFN over each slot's
  *   moe_expert_ffn_q8_0 /     batch (decode GEMV or prefill MFMA GEMM)
  *   moe_expert_ffn_mxfp4 /
- *   moe_expert_ffn_q3k_q4k
+ *   moe_expert_ffn_q3k_q4k /
+ *   moe_expert_ffn_q5k
  *   moe_combine               weighted sum of the pairs (+ shared expert)
  *
  * Conventions for every call:
@@ -63,7 +64,8 @@ typedef enum moe_format {
     MOE_FMT_Q8_0 = 0,
     MOE_FMT_Q4K = 1,
     MOE_FMT_MXFP4 = 2,
-    MOE_FMT_Q3K_Q4K = 3 /* mixed expert: Q3_K gate and up, Q4_K down */
+    MOE_FMT_Q3K_Q4K = 3, /* mixed expert: Q3_K gate and up, Q4_K down */
+    MOE_FMT_Q5K = 4
 } moe_format;
 
 /* Limits checked by the calls below. */
@@ -205,13 +207,18 @@ moe_status moe_count_routes(const int32_t* topk_ids, int T, int k, int E, uint32
  *        q = low + 4*high - 4; scale j: low four bits from byte j (j < 8) or
  *        the high nibble of byte j - 8, top two bits at bit 2*(j/4) of byte
  *        8 + j%4;                                     w = d*(sc_j - 32)*q.
+ *   Q5_K (176 B / 256 weights; a card expert type, README 0.3.1 "Quant
+ *        types" row): fp16 d, fp16 dmin, the 12 scale bytes of Q4_K, 32 B of
+ *        high bits, 128 B of low nibbles in the Q4_K order; element l of
+ *        sub-block j has its high bit at bit j of high-bit byte l;
+ *        q = low + 16*high (0..31);                 w = d*sc_j*q - dmin*m_j.
  *   MOE_FMT_Q3K_Q4K is the mixed expert DeepSeek-V4.1-class files put on the
  *        card (bloomery README 0.3.11, limits list: V4.1's card experts are
  *        Q3_K gate and up with a Q4_K down): W_gate and W_up in Q3_K, W_down
  *        in Q4_K.
  * Canonical blob = W_gate | W_up | W_down, each row-major.
  *
- * Supported shapes: Q4_K, MXFP4 and Q3_K/Q4_K need H % 256 == 0 and
+ * Supported shapes: Q4_K, Q5_K, MXFP4 and Q3_K/Q4_K need H % 256 == 0 and
  * I % 256 == 0; Q8_0 needs H % 128 == 0 and I % 128 == 0.
  */
 size_t moe_expert_blob_bytes(int format, int H, int I);
@@ -263,7 +270,7 @@ moe_status moe_validate_slot_map(const int32_t* slot_of_expert, int E, int S);
  *               (MXFP4 weights beyond bf16's range, |w| > 3.39e38, become
  *               infinite there.)
  *               MOE_PATH_AUTO: PREFILL for Q4_K and MXFP4 with bf16 x when
- *               T > 32, else DECODE (always DECODE for Q8_0 and Q3_K/Q4_K).
+ *               T > 32, else DECODE (always DECODE for the other formats).
  * ws, ws_bytes  device workspace, at least moe_ffn_workspace_size(format, T,
  *               k, H, I, path).
  *
@@ -288,6 +295,10 @@ moe_status moe_expert_ffn_q3k_q4k(const void* slot_pool, size_t slot_stride, int
                                   int x_dtype, int T, int k, const int32_t* slot_offsets, const int32_t* active_slots,
                                   const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype,
                                   int path, void* ws, size_t ws_bytes, void* stream);
+moe_status moe_expert_ffn_q5k(const void* slot_pool, size_t slot_stride, int S, int H, int I, const void* x,
+                              int x_dtype, int T, int k, const int32_t* slot_offsets, const int32_t* active_slots,
+                              const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype,
+                              int path, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- combine
  * y[t] = sum over j < k, in j order, of [slot_of_expert[id] >= 0] *

@@ -46,11 +46,11 @@ moe_status check_route_shape(int T, int E, int k) {
 }
 
 moe_status check_shape(int format, int H, int I) {
-    if (format < MOE_FMT_Q8_0 || format > MOE_FMT_Q3K_Q4K)
+    if (format < MOE_FMT_Q8_0 || format > MOE_FMT_Q5K)
         return fail(MOE_ERR_INVALID_ARGUMENT,
-                    "format = %d is not MOE_FMT_Q8_0, MOE_FMT_Q4K, MOE_FMT_MXFP4 or MOE_FMT_Q3K_Q4K", format);
+                    "format = %d is not MOE_FMT_Q8_0, MOE_FMT_Q4K, MOE_FMT_MXFP4, MOE_FMT_Q3K_Q4K or MOE_FMT_Q5K", format);
     const int m = format == MOE_FMT_Q8_0 ? 128 : 256;
-    static const char* const kNames[] = {"Q8_0", "Q4_K", "MXFP4", "Q3_K/Q4_K"};
+    static const char* const kNames[] = {"Q8_0", "Q4_K", "MXFP4", "Q3_K/Q4_K", "Q5_K"};
     if (H <= 0 || I <= 0) return fail(MOE_ERR_INVALID_ARGUMENT, "H = %d, I = %d must be positive", H, I);
     if (H % m || I % m)
         return fail(MOE_ERR_UNSUPPORTED, "%s needs H and I multiples of %d (H = %d, I = %d)",
@@ -66,6 +66,7 @@ size_t blob_bytes(int format, int H, int I) {
         case MOE_FMT_Q4K: return 3 * w / 256 * 144;
         case MOE_FMT_MXFP4: return 3 * w / 32 * 17;
         case MOE_FMT_Q3K_Q4K: return 2 * w / 256 * 110 + w / 256 * 144;
+        case MOE_FMT_Q5K: return 3 * w / 256 * 176;
         default: return 3 * w / 32 * 34;
     }
 }
@@ -382,6 +383,72 @@ void q3k_mix_walk(const uint8_t* in, uint8_t* out, int H, int I) {
     q4k_down_walk<PACK>(in, out, H, I, 2 * gbytes, qmoe::q3k_gateup_bytes(H, I));
 }
 
+// Q5_K: one canonical 176-byte super-block (d, dmin, 12 scale bytes, 32
+// bytes of high bits, 128 bytes of nibbles) <-> header (the first 16 bytes),
+// eight 16-byte nibble slots in the Q4_K packed order, eight HB words
+// (element 8d + n's high bit at bit 4n + d).
+void q5k_block(const uint8_t* canon, uint8_t* hdr, uint8_t* const* nib, uint32_t* hb, bool pack) {
+    uint8_t q[32];
+    if (pack) {
+        memcpy(hdr, canon, 16);
+        for (int j = 0; j < 8; ++j) {
+            hb[j] = 0;
+            for (int l = 0; l < 32; ++l) {
+                const uint8_t byte = canon[48 + (j / 2) * 32 + l];
+                q[l] = (j % 2) ? (byte >> 4) : (byte & 15);
+                hb[j] |= (uint32_t)((canon[16 + l] >> j) & 1) << (4 * (l % 8) + l / 8);
+            }
+            nibbles_pack(q, nib[j]);
+        }
+    } else {
+        uint8_t* dst = const_cast<uint8_t*>(canon);
+        memset(dst, 0, 176);
+        memcpy(dst, hdr, 16);
+        for (int j = 0; j < 8; ++j) {
+            nibbles_unpack(nib[j], q);
+            for (int l = 0; l < 32; ++l) {
+                dst[48 + (j / 2) * 32 + l] |= (uint8_t)(q[l] << (4 * (j % 2)));
+                dst[16 + l] |= (uint8_t)(((hb[j] >> (4 * (l % 8) + l / 8)) & 1) << j);
+            }
+        }
+    }
+}
+
+template <bool PACK>
+void q5k_walk(const uint8_t* in, uint8_t* out, int H, int I) {
+    const size_t rbH = (size_t)H / 256 * 176, rbI = (size_t)I / 256 * 176;
+    const size_t gbytes = (size_t)I * rbH;
+    uint8_t* dev = PACK ? out : const_cast<uint8_t*>(in);
+    const uint8_t* canon_base = PACK ? in : out;
+    uint32_t hb[8];
+    uint8_t* nib[8];
+    // one matrix section: tiles of `rows` x 256 inputs, NMAT matrices interleaved
+    auto section = [&](size_t base, int nmat, int row_tiles, int units, size_t rb, size_t canon0, size_t cstride) {
+        const size_t tbytes = (size_t)nmat * qmoe::kQ5kDownTile;
+        for (int rg = 0; rg < row_tiles; ++rg)
+            for (int u = 0; u < units; ++u) {
+                uint8_t* tile = dev + base + ((size_t)rg * units + u) * tbytes;
+                for (int r = 0; r < 64; ++r)
+                    for (int m = 0; m < nmat; ++m) {
+                        const uint8_t* canon = canon_base + canon0 + m * cstride + ((size_t)rg * 64 + r) * rb + (size_t)u * 176;
+                        for (int j = 0; j < 8; ++j) nib[j] = tile + nmat * 1024 + j * nmat * 1024 + m * 1024 + r * 16;
+                        uint8_t* hw = tile + nmat * 9216 + m * 1024 + r * 16;  // chunk 0; chunk 1 at + nmat KB
+                        if (!PACK) {
+                            memcpy(hb, hw, 16);
+                            memcpy(hb + 4, hw + nmat * 1024, 16);
+                        }
+                        q5k_block(canon, tile + m * 1024 + r * 16, nib, hb, PACK);
+                        if (PACK) {
+                            memcpy(hw, hb, 16);
+                            memcpy(hw + nmat * 1024, hb + 4, 16);
+                        }
+                    }
+            }
+    };
+    section(0, 2, I / 64, H / 256, rbH, 0, gbytes);
+    section(qmoe::q5k_gateup_bytes(H, I), 1, H / 64, I / 256, rbI, 2 * gbytes, 0);
+}
+
 moe_status ffn_common(int format, const void* slot_pool, size_t slot_stride, int S, int H, int I, const void* x,
                       int x_dtype, int T, int k, const int32_t* slot_offsets, const int32_t* active_slots,
                       const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype, int path,
@@ -411,7 +478,7 @@ moe_status ffn_common(int format, const void* slot_pool, size_t slot_stride, int
     } else {
         if (format != MOE_FMT_Q4K && format != MOE_FMT_MXFP4)
             return fail(MOE_ERR_UNSUPPORTED, "the prefill path is implemented for Q4_K and MXFP4 (MOE_PATH_DECODE "
-                                             "serves Q8_0 and Q3_K/Q4_K at any T)");
+                                             "serves the other formats at any T)");
         if (x_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the prefill path takes MOE_BF16 x");
         // The GEMMs address x and h rows with 32-bit byte offsets, and the
         // tile list counts tiles in 16 bits.
@@ -575,6 +642,7 @@ moe_status moe_pack_expert(int format, const void* canonical, void* packed, int 
     if (format == MOE_FMT_Q4K) q4k_walk<true>(in, out, H, I);
     else if (format == MOE_FMT_MXFP4) mx4_walk<true>(in, out, H, I);
     else if (format == MOE_FMT_Q3K_Q4K) q3k_mix_walk<true>(in, out, H, I);
+    else if (format == MOE_FMT_Q5K) q5k_walk<true>(in, out, H, I);
     else q8_walk<true>(in, out, H, I);
     return MOE_OK;
 }
@@ -591,6 +659,7 @@ moe_status moe_unpack_expert(int format, const void* packed, void* canonical, in
     if (format == MOE_FMT_Q4K) q4k_walk<false>(in, out, H, I);
     else if (format == MOE_FMT_MXFP4) mx4_walk<false>(in, out, H, I);
     else if (format == MOE_FMT_Q3K_Q4K) q3k_mix_walk<false>(in, out, H, I);
+    else if (format == MOE_FMT_Q5K) q5k_walk<false>(in, out, H, I);
     else q8_walk<false>(in, out, H, I);
     return MOE_OK;
 }
@@ -649,6 +718,14 @@ moe_status moe_expert_ffn_q3k_q4k(const void* slot_pool, size_t slot_stride, int
                                   const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype,
                                   int path, void* ws, size_t ws_bytes, void* stream) {
     return ffn_common(MOE_FMT_Q3K_Q4K, slot_pool, slot_stride, S, H, I, x, x_dtype, T, k, slot_offsets, active_slots,
+                      num_active, perm_pair, y_pairs, y_dtype, path, ws, ws_bytes, stream);
+}
+
+moe_status moe_expert_ffn_q5k(const void* slot_pool, size_t slot_stride, int S, int H, int I, const void* x,
+                              int x_dtype, int T, int k, const int32_t* slot_offsets, const int32_t* active_slots,
+                              const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype,
+                              int path, void* ws, size_t ws_bytes, void* stream) {
+    return ffn_common(MOE_FMT_Q5K, slot_pool, slot_stride, S, H, I, x, x_dtype, T, k, slot_offsets, active_slots,
                       num_active, perm_pair, y_pairs, y_dtype, path, ws, ws_bytes, stream);
 }
 

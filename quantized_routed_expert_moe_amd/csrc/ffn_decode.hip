@@ -103,6 +103,33 @@ __device__ __forceinline__ float q4k_dot(const uint4 q, cu32* X, const AndOr& k)
     return acc;
 }
 
+// Q5_K: the Q4_K nibbles plus one high bit per element, HB holding element
+// 8d + n's at bit 4n + d.  A group's high bits shifted left by 4 - d land on
+// bit 4 (and 20) of pairs 0 and 1's halves, shifted right by 4 + d on those
+// of pairs 2 and 3; OR-ed in as bit 4 of q (pairs 0, 2) or bit 8 of 16 q
+// (pairs 1, 3).  Returns sum_e (1024 + q_e) x'_e as q4k_dot does.
+template <bool AO>
+__device__ __forceinline__ float q5k_dot(const uint4 q, uint32_t hb, cu32* X, const AndOr& k) {
+    const uint32_t w[4] = {q.x, q.z, q.y, q.w};
+    float acc = 0.0f;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t w8 = w[d] >> 8, hl = hb << (4 - d), hr = hb >> (4 + d);
+        if (AO) {
+            acc = fdot2u(and_or(hl, k.m2, and_or(w[d], k.m0, k.magic)), X[4 * d + 0], acc);
+            acc = fdot2u(and_or(hl, k.m3, and_or(w[d], k.m1, k.magic)), X[4 * d + 1], acc);
+            acc = fdot2u(and_or(hr, k.m2, and_or(w8, k.m0, k.magic)), X[4 * d + 2], acc);
+            acc = fdot2u(and_or(hr, k.m3, and_or(w8, k.m1, k.magic)), X[4 * d + 3], acc);
+        } else {
+            acc = fdot2u((hl & 0x00100010u) | (w[d] & 0x000F000Fu) | kMagic, X[4 * d + 0], acc);
+            acc = fdot2u((hl & 0x01000100u) | (w[d] & 0x00F000F0u) | kMagic, X[4 * d + 1], acc);
+            acc = fdot2u((hr & 0x00100010u) | (w8 & 0x000F000Fu) | kMagic, X[4 * d + 2], acc);
+            acc = fdot2u((hr & 0x01000100u) | (w8 & 0x00F000F0u) | kMagic, X[4 * d + 3], acc);
+        }
+    }
+    return acc;
+}
+
 // Q8_0: 32 offset bytes (u = q + 128; elements 0-15 in a, 16-31 in b)
 // against one record.  Returns sum_e (1024 + u_e) x_e = sum (1152 + q_e) x_e.
 __device__ __forceinline__ float q8_dot(const uint4 a, const uint4 b, cu32* X) {
@@ -221,6 +248,12 @@ template <int NMAT> struct UnitRegs<2, NMAT> {
 };
 // Q3_K: per 64-element chunk c the (LA, LB) words of blocks 2c and 2c + 1;
 // per 128-element chunk the HB words of its four blocks.
+// Q5_K: the Q4_K nibbles and, per half unit, the HB words of its four
+// sub-blocks.
+template <int NMAT> struct UnitRegs<4, NMAT> {
+    uint4 q[8][NMAT];
+    uint4 hb[2][NMAT];
+};
 template <int NMAT> struct UnitRegs<3, NMAT> {
     uint4 L[4][NMAT];
     uint4 Hb[2][NMAT];
@@ -228,7 +261,7 @@ template <int NMAT> struct UnitRegs<3, NMAT> {
 
 template <int FMT, int NMAT>
 __device__ __forceinline__ constexpr int tile_bytes() {
-    return FMT == 1 ? NMAT * 9216 : FMT == 3 ? NMAT * 7168 : NMAT * 8704;
+    return FMT == 1 ? NMAT * 9216 : FMT == 3 ? NMAT * 7168 : FMT == 4 ? NMAT * 11264 : NMAT * 8704;
 }
 
 // LDS region of one wave: words [kMaxTok][8][16] dwords, then (C, S) [kMaxTok][8][2].
@@ -360,9 +393,9 @@ __device__ __forceinline__ void act_store(const ActRegs& a, int x_dtype, int lan
                 *reinterpret_cast<uint2*>(lw + (t * RB + jb) * 16 + 2 * sl) =
                     make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
                 // (MXFP4 has no magic-number constant to remove: C stays 0)
-                const float s16 = FMT == 1 ? sum8_lanes(half_to_float(b0) + half_to_float(b1) + half_to_float(b2) +
-                                                        half_to_float(b3))
-                                           : 0.0f;
+                const float s16 = (FMT == 1 || FMT == 4) ? sum8_lanes(half_to_float(b0) + half_to_float(b1) +
+                                                                      half_to_float(b2) + half_to_float(b3))
+                                                           : 0.0f;
                 const float sx = FMT == 3 ? 0.0f : sum8_lanes(v[0] + v[1] + v[2] + v[3]);
                 if (FMT == 3) {
                     // Q3_K: per 16-element half (a quad of lanes), K = 1024 * sum of
@@ -561,6 +594,45 @@ __device__ __forceinline__ void half_dots(const UnitRegs<3, NMAT>& r, const uint
                 const uint32_t hb = i == 0 ? Hv.x : i == 1 ? Hv.y : i == 2 ? Hv.z : Hv.w;
                 const float2 dd = q3k_dot(la, lb, hb, X, k);
                 acc[t][m] += ds[m][2 * (j & 3)] * (dd.x - ka) + ds[m][2 * (j & 3) + 1] * (dd.y - kb);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <int NMAT>
+__device__ __forceinline__ void load_half(__amdgpu_buffer_rsrc_t src, int uoff, int lane, int h,
+                                          UnitRegs<4, NMAT>& r, uint4* hdr) {
+    if (h == 0) {
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) hdr[m] = ldb16(src, lane * 16, uoff + m * 1024);
+    }
+#pragma unroll
+    for (int j = 4 * h; j < 4 * h + 4; ++j)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) r.q[j][m] = ldb16(src, lane * 16, uoff + NMAT * 1024 + j * NMAT * 1024 + m * 1024);
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) r.hb[h][m] = ldb16(src, lane * 16, uoff + NMAT * 9216 + h * NMAT * 1024 + m * 1024);
+}
+template <int NT, int NMAT>
+__device__ __forceinline__ void half_dots(const UnitRegs<4, NMAT>& r, const uint4* hdr, int h, const uint32_t* lw,
+                                          const float* lc, float (*acc)[NMAT]) {
+    float ds[NMAT][8], dm[NMAT][8];
+    const AndOr k(0x000F000Fu, 0x00F000F0u, 0x00100010u, 0x01000100u);
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) q4k_header(hdr[m], ds[m], dm[m]);
+#pragma unroll
+    for (int j = 4 * h; j < 4 * h + 4; ++j) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const uint32_t* X = lw + (t * 8 + j) * 16;
+            const float c = lc[(t * 8 + j) * 2], sx = lc[(t * 8 + j) * 2 + 1];
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) {
+                const uint4 hv = r.hb[h][m];
+                const int i = j & 3;
+                const uint32_t hb = i == 0 ? hv.x : i == 1 ? hv.y : i == 2 ? hv.z : hv.w;
+                acc[t][m] += ds[m][j] * (q5k_dot<NMAT == 2>(r.q[j][m], hb, X, k) - c) - dm[m][j] * sx;
             }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -822,7 +894,7 @@ static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // A K split across workgroups keeps kparts x P x NMAT x rows fp32 partial
 // sums; kparts x P is held to this many, which bounds the buffer.
-constexpr int kMaxPartRows = 64;
+constexpr int kMaxPartRows = 128;
 
 // Workspace: h records [T*k][I/32] (64 B + 8 B), then the partial sums of a
 // K split across workgroups (gate/up and down use it in turn).
@@ -836,9 +908,11 @@ size_t decode_workspace_bytes(int T, int k, int H, int I) {
 // workgroup per tile leave most of the chip idle while each streams several
 // units.  Then split K across workgroups as well: one unit per wave, as many
 // waves as the unit count allows, kparts workgroups per tile, finished by
-// the reduce kernel (if the partial sums fit).
-static int split_k_parts(int units, long tiles_total, int P, int* nw, int* upw) {
-    if (*upw <= 1 || tiles_total * *nw >= 2048) return 1;
+// the reduce kernel (if the partial sums fit).  Also whenever the pipelined
+// kernel of the format would spill (pipe_spills: Q5_K gate/up, whose unit
+// is 160 bytes per row and matrix).
+static int split_k_parts(int units, long tiles_total, int P, int* nw, int* upw, bool pipe_spills = false) {
+    if (*upw <= 1 || (tiles_total * *nw >= 2048 && !pipe_spills)) return 1;
     const int nw1 = std::min(kMaxWaves, units);
     const int kp = (units + nw1 - 1) / nw1;
     if ((long)kp * P > kMaxPartRows) return 1;
@@ -922,7 +996,7 @@ hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s) {
         const int units = fgu == 0 ? a.H / 128 : a.H / 256;
         int nw, upw;
         split_k(units, (long)(a.I / 64) * max_active, &nw, &upw);
-        const int kparts = split_k_parts(units, (long)(a.I / 64) * max_active, (int)P, &nw, &upw);
+        const int kparts = split_k_parts(units, (long)(a.I / 64) * max_active, (int)P, &nw, &upw, fgu == 4);
         const dim3 grid(a.I / 64, max_active), block(64 * nw);
         timer_before(kStageGateUp, s);
         const GemvLaunch g{a.pool, a.stride, a.S, a.H, a.I, 0, a.x, a.x_dtype, nullptr, nullptr, a.T, a.k,
@@ -934,6 +1008,8 @@ hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s) {
             launch_gemv<2, 2>(g, grid, block, s);
         else if (fgu == 3)
             launch_gemv<3, 2>(g, grid, block, s);
+        else if (fgu == 4)
+            launch_gemv<4, 2>(g, grid, block, s);
         else
             launch_gemv<0, 2>(g, grid, block, s);
         timer_after(kStageGateUp, s);
@@ -950,6 +1026,7 @@ hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s) {
         const size_t section = a.format == 1   ? q4k_gateup_bytes(a.H, a.I)
                                : a.format == 2 ? mx4_gateup_bytes(a.H, a.I)
                                : a.format == 3 ? q3k_gateup_bytes(a.H, a.I)
+                               : a.format == 4 ? q5k_gateup_bytes(a.H, a.I)
                                                : q8_gateup_bytes(a.H, a.I);
         timer_before(kStageDown, s);
         const GemvLaunch g{a.pool, a.stride, a.S, a.I, a.H, section, nullptr, 0, hw, hcs, a.T, a.k,
@@ -959,6 +1036,8 @@ hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s) {
             launch_gemv<1, 1>(g, grid, block, s);
         else if (fdn == 2)
             launch_gemv<2, 1>(g, grid, block, s);
+        else if (fdn == 4)
+            launch_gemv<4, 1>(g, grid, block, s);
         else
             launch_gemv<0, 1>(g, grid, block, s);
         timer_after(kStageDown, s);

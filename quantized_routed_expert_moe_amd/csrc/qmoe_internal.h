@@ -77,6 +77,17 @@ namespace qmoe {
 // the high bit of element 8d + n at bit 4n + (2 + d) % 4, where the stored
 // quant is q + 4 = low + 4 * high.
 
+//
+// Packed Q5_K blob (H, I multiples of 256): tiles of 64 rows x 256 inputs,
+// per matrix (NMAT = 2 interleaved for gate/up as in Q4_K):
+//     [0, NMAT KB)                  headers (as stored: d, dmin, 12 scale bytes)
+//     [NMAT KB + j NMAT KB + m KB)  low nibbles of sub-block j, the Q4_K order
+//     [9 NMAT KB + c NMAT KB + m KB)   high bits of sub-blocks 4c..4c+3 (c < 2):
+//                       row r at 16r, one word HB per sub-block, element
+//                       8d + n's high bit at bit 4n + d
+// gate/up tile 22528 bytes, down tile 11264 bytes (the stored 176 bytes per
+// row and 256 inputs).
+
 constexpr int kMaxExpertsInternal = 1024;  // equals MOE_MAX_EXPERTS of the C ABI
 
 constexpr int kQ4kGateUpTile = 18432;
@@ -89,6 +100,9 @@ __host__ __device__ inline size_t q8_gateup_bytes(int H, int I) { return (size_t
 constexpr int kMx4GateUpTile = 17408;
 constexpr int kMx4DownTile = 8704;
 __host__ __device__ inline size_t mx4_gateup_bytes(int H, int I) { return (size_t)(I / 64) * (H / 256) * kMx4GateUpTile; }
+constexpr int kQ5kGateUpTile = 22528;
+constexpr int kQ5kDownTile = 11264;
+__host__ __device__ inline size_t q5k_gateup_bytes(int H, int I) { return (size_t)(I / 64) * (H / 256) * kQ5kGateUpTile; }
 constexpr int kQ3kGateUpTile = 14336;
 __host__ __device__ inline size_t q3k_gateup_bytes(int H, int I) { return (size_t)(I / 64) * (H / 256) * kQ3kGateUpTile; }
 

@@ -71,12 +71,14 @@ constexpr int kQ4kBlock = 256, kQ4kBytes = 144;
 constexpr int kQ8Block = 32, kQ8Bytes = 34;
 constexpr int kMx4Block = 32, kMx4Bytes = 17;
 constexpr int kQ3kBlock = 256, kQ3kBytes = 110;
+constexpr int kQ5kBytes = 176;
 constexpr int kRowQ3k = 100;  // block type of a Q3_K matrix (the mixed expert's gate and up)
 
 size_t row_bytes(int type, int n) {
     if (type == MOE_FMT_Q4K) return (size_t)(n / kQ4kBlock) * kQ4kBytes;
     if (type == MOE_FMT_MXFP4) return (size_t)(n / kMx4Block) * kMx4Bytes;
     if (type == kRowQ3k) return (size_t)(n / kQ3kBlock) * kQ3kBytes;
+    if (type == MOE_FMT_Q5K) return (size_t)(n / kQ4kBlock) * kQ5kBytes;
     return (size_t)(n / kQ8Block) * kQ8Bytes;
 }
 
@@ -175,6 +177,45 @@ void dequant_row_mxfp4(const uint8_t* row, int n, float* out) {
     }
 }
 
+// One Q5_K row of n weights (n / 256 super-blocks of 176 bytes: the Q4_K
+// header, 32 bytes of high bits (bit j of byte l: element l of sub-block j),
+// 128 bytes of nibbles in the Q4_K order) -> n floats d sc_j q - dmin m_j,
+// q = nibble + 16 high bit.
+__attribute__((target("avx2,fma")))
+void dequant_row_q5k(const uint8_t* row, int n, float* out) {
+    const __m256i low4 = _mm256_set1_epi8(0x0F), one = _mm256_set1_epi8(1);
+    for (int sb = 0; sb < n / kQ4kBlock; ++sb, row += kQ5kBytes, out += kQ4kBlock) {
+        const float d = half_bits_to_float(load_u16(row)), dmin = half_bits_to_float(load_u16(row + 2));
+        const uint8_t* s = row + 4;
+        float dsc[8], dm[8];
+        for (int j = 0; j < 8; ++j) {
+            int sc, m;
+            if (j < 4) {
+                sc = s[j] & 63;
+                m = s[j + 4] & 63;
+            } else {
+                sc = (s[j + 4] & 0x0F) | ((s[j - 4] >> 6) << 4);
+                m = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
+            }
+            dsc[j] = d * (float)sc;
+            dm[j] = dmin * (float)m;
+        }
+        const __m256i hbits = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(row + 16));
+        const uint8_t* q = row + 48;
+        for (int c = 0; c < 4; ++c) {
+            const __m256i v = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(q + 32 * c));
+            for (int half = 0; half < 2; ++half) {
+                const int j = 2 * c + half;
+                const __m256i nib = half ? _mm256_and_si256(_mm256_srli_epi16(v, 4), low4) : _mm256_and_si256(v, low4);
+                const __m256i hb = _mm256_and_si256(_mm256_srli_epi16(hbits, j), one);
+                const __m256i qv = _mm256_or_si256(nib, _mm256_slli_epi16(hb, 4));
+                widen_store(_mm256_castsi256_si128(qv), _mm256_extracti128_si256(qv, 1), _mm256_set1_ps(dsc[j]),
+                            _mm256_set1_ps(dm[j]), out + 32 * j);
+            }
+        }
+    }
+}
+
 // One Q3_K row of n weights (n / 256 super-blocks of 110 bytes: 32 bytes of
 // high bits, 64 of 2-bit quants, 12 of 6-bit scales, fp16 d; element i =
 // 128h + 32g + l has its low bits at bits 2g of quant byte 32h + l and its
@@ -258,6 +299,7 @@ void run(int format, const uint8_t* const* expert_blob, int H, int I, const floa
         return type == MOE_FMT_Q4K ? dequant_row_q4k
              : type == MOE_FMT_MXFP4 ? dequant_row_mxfp4
              : type == kRowQ3k ? dequant_row_q3k
+             : type == MOE_FMT_Q5K ? dequant_row_q5k
                                : dequant_row_q8_0;
     };
     auto dequant = pick(tgu);
@@ -318,8 +360,8 @@ const char* moe_host_last_error(void) { return g_error.c_str(); }
 int moe_host_leg(int format, const uint8_t* const* expert_blob, int E, int H, int I, const float* x, int T,
                  const int32_t* host_token, const int32_t* host_expert, const float* host_weight, int count,
                  float* y_host, int threads) {
-    if (format < MOE_FMT_Q8_0 || format > MOE_FMT_Q3K_Q4K) return fail(MOE_ERR_UNSUPPORTED, "bad format %d", format);
-    const int blk = (format == MOE_FMT_Q4K || format == MOE_FMT_Q3K_Q4K) ? kQ4kBlock
+    if (format < MOE_FMT_Q8_0 || format > MOE_FMT_Q5K) return fail(MOE_ERR_UNSUPPORTED, "bad format %d", format);
+    const int blk = (format == MOE_FMT_Q4K || format == MOE_FMT_Q3K_Q4K || format == MOE_FMT_Q5K) ? kQ4kBlock
                     : format == MOE_FMT_MXFP4                           ? kMx4Block
                                                                         : kQ8Block;
     if (H <= 0 || I <= 0 || H % blk || I % blk)

@@ -160,7 +160,8 @@ def test_workspace_sizes_are_monotone():
 @pytest.mark.parametrize("fmt,H,I", [(Q.MOE_FMT_Q4K, 512, 256), (Q.MOE_FMT_Q4K, 768, 512), (Q.MOE_FMT_Q8_0, 256, 128),
                                      (Q.MOE_FMT_Q8_0, 384, 256), (Q.MOE_FMT_MXFP4, 512, 256),
                                      (Q.MOE_FMT_MXFP4, 768, 512), (Q.MOE_FMT_Q3K_Q4K, 512, 256),
-                                     (Q.MOE_FMT_Q3K_Q4K, 768, 512)])
+                                     (Q.MOE_FMT_Q3K_Q4K, 768, 512), (Q.MOE_FMT_Q5K, 512, 256),
+                                     (Q.MOE_FMT_Q5K, 768, 512)])
 def test_pack_round_trip(fmt, H, I):
     blob = F.expert_blob(fmt, 5, 0, 1, H, I)
     packed = Q.moe_pack_expert(fmt, blob, H, I)
@@ -240,6 +241,31 @@ def test_pack_places_q3k_fields():
     q4p = Q.moe_pack_expert(Q.MOE_FMT_Q4K, q4, H, I)
     base3, base4 = (I // 64) * (H // 256) * 14336, (I // 64) * (H // 256) * 18432
     assert np.array_equal(packed[base3:], q4p[base4:])
+
+
+def test_pack_places_q5k_fields():
+    """Row r of W_up, super-block u: header at gate/up tile (r//64, u), offset 1024 + 16*(r%64); element 8d+n of
+    sub-block j's nibble in nibble n of group d's dword (groups stored 0, 2, 1, 3) and its high bit at bit 4n + d of
+    the sub-block's HB word."""
+    H, I = 512, 256
+    blob = F.expert_blob(Q.MOE_FMT_Q5K, 6, 0, 0, H, I)
+    packed = Q.moe_pack_expert(Q.MOE_FMT_Q5K, blob, H, I)
+    rb = H // 256 * 176
+    for r, u in [(0, 0), (70, 1), (255, 1)]:
+        canon = blob[I * rb + r * rb + u * 176: I * rb + r * rb + (u + 1) * 176]
+        tile = ((r // 64) * (H // 256) + u) * 22528
+        assert np.array_equal(packed[tile + 1024 + 16 * (r % 64): tile + 1040 + 16 * (r % 64)], canon[:16])
+        for j in (0, 3, 6):
+            words = packed[tile + 2048 + j * 2048 + 1024 + 16 * (r % 64): tile + 2064 + j * 2048 + 1024 +
+                           16 * (r % 64)].view(np.uint32)
+            hw = packed[tile + 18432 + (j // 4) * 2048 + 1024 + 16 * (r % 64):
+                        tile + 18448 + (j // 4) * 2048 + 1024 + 16 * (r % 64)].view(np.uint32)[j % 4]
+            for e in (0, 9, 21, 31):
+                byte = canon[48 + (j // 2) * 32 + e]
+                low = (byte >> 4) if j % 2 else (byte & 15)
+                high = (canon[16 + e] >> j) & 1
+                assert (int(words[[0, 2, 1, 3][e // 8]]) >> (4 * (e % 8))) & 15 == low
+                assert (int(hw) >> (4 * (e % 8) + e // 8)) & 1 == high
 
 
 def test_validate_slot_map():

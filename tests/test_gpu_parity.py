@@ -334,12 +334,14 @@ def _check_layer(wl, got, want, soe, S, tol=DECODE_TOL):
 
 MXFP4_SMALL = W.Workload("small MXFP4 layer (H256 E8 k2 I256 T4)", F.MXFP4, 256, 256, 8, 2, 4)
 Q3K_SMALL = W.Workload("small Q3_K/Q4_K layer (H512 E8 k2 I256 T4)", F.Q3K_Q4K, 512, 256, 8, 2, 4)
+Q5K_SMALL = W.Workload("small Q5_K layer (H512 E8 k2 I256 T4)", F.Q5K, 512, 256, 8, 2, 4)
+Q5K_QWEN3_T2 = W.Workload("Qwen3-30B-A3B-shaped MoE layer, Q5_K experts, decode T=2", F.Q5K, 2048, 768, 128, 8, 2)
 Q3K_QWEN3_T2 = W.Workload("Qwen3-30B-A3B-shaped MoE layer, Q3_K/Q4_K experts, decode T=2", F.Q3K_Q4K, 2048, 768, 128,
                           8, 2)
 
 
 @pytest.mark.parametrize("wl", [W.TINY, W.QWEN3_DECODE_T1, W.QWEN3_DECODE_T2, MXFP4_SMALL, W.QWEN3_MXFP4_DECODE_T2,
-                                Q3K_SMALL, Q3K_QWEN3_T2],
+                                Q3K_SMALL, Q3K_QWEN3_T2, Q5K_SMALL, Q5K_QWEN3_T2],
                          ids=lambda w: w.name.split(",")[0][:24] + f"-fmt{w.fmt}-T{w.T}")
 def test_decode_layer_matches_oracle(wl):
     say(f"decode layer {wl.name}")
@@ -397,13 +399,13 @@ def test_dsv3_experts_many_tokens_per_slot(dsv3_blobs):
     assert int(np.diff(got["slot_offsets"]).max()) > 2
 
 
-@pytest.mark.parametrize("fmt", [F.Q4K, F.Q8_0, F.MXFP4, F.Q3K_Q4K])
+@pytest.mark.parametrize("fmt", [F.Q4K, F.Q8_0, F.MXFP4, F.Q3K_Q4K, F.Q5K])
 def test_decode_k_split_across_workgroups(fmt):
     """Two experts with a long K (H 7168): too few row tiles to fill the chip,
     so K is split across workgroups too (partial sums finished by the reduce
     kernel), with an uneven last part and a slot holding several chunks of
     tokens."""
-    name = {F.Q4K: "Q4_K", F.Q8_0: "Q8_0", F.MXFP4: "MXFP4", F.Q3K_Q4K: "Q3_K/Q4_K"}[fmt]
+    name = {F.Q4K: "Q4_K", F.Q8_0: "Q8_0", F.MXFP4: "MXFP4", F.Q3K_Q4K: "Q3_K/Q4_K", F.Q5K: "Q5_K"}[fmt]
     wl = W.Workload(f"{name} layer H 7168, 2 experts, k 1, T 5", fmt, 7168, 256, 2, 1, 5)
     say(wl.name)
     got, want, soe, S = _layer_case(wl, path=Q.MOE_PATH_DECODE)
@@ -478,6 +480,28 @@ def test_dsv3_sized_q3k_experts_many_tokens():
     got, want, soe, S = _layer_case(wl, path=Q.MOE_PATH_DECODE)
     _check_layer(wl, got, want, soe, S)
     assert int(np.diff(got["slot_offsets"]).max()) > 2
+
+
+@pytest.mark.parametrize("T", [8, 24], ids=["K-split", "pipelined"])
+def test_dsv3_sized_q5k_experts(T):
+    """DeepSeek-V3-sized Q5_K experts (H 7168, I 2048), 16 of them: at 16
+    pairs the gate/up GEMV splits K across workgroups (its pipelined kernel
+    would spill); at 48 pairs the partial sums would not fit and the
+    pipelined kernel runs.  The down GEMV pipelines in both."""
+    wl = W.Workload(f"DeepSeek-V3-sized Q5_K experts, 16 resident, {T} tokens", F.Q5K, 7168, 2048, 16, 2, T)
+    say(wl.name)
+    F.set_num_threads(THREADS)
+    got, want, soe, S = _layer_case(wl, path=Q.MOE_PATH_DECODE)
+    _check_layer(wl, got, want, soe, S)
+
+
+def test_decode_q5k_many_tokens_partial_residency():
+    wl = W.Workload("small Q5_K layer, 37 tokens, partial residency", F.Q5K, 512, 256, 12, 4, 37)
+    say(wl.name)
+    soe = np.array([3, -1, 0, 5, -1, 1, 2, -1, 4, 6, -1, 7], dtype=np.int32)
+    got, want, soe, S = _layer_case(wl, soe=soe, S=9, path=Q.MOE_PATH_DECODE)
+    _check_layer(wl, got, want, soe, S)
+    assert got["host_count"] > 0
 
 
 def test_host_list_written_into_pinned_memory():

@@ -19,6 +19,7 @@ CASES = {
     "qwen3_T2": W.QWEN3_DECODE_T2,
     "mxfp4_small": W.Workload("MXFP4 layer H512 I256 E16 k4 T6", F.MXFP4, 512, 256, 16, 4, 6),
     "q3k_q4k_small": W.Workload("Q3_K/Q4_K layer H512 I256 E16 k4 T6", F.Q3K_Q4K, 512, 256, 16, 4, 6),
+    "q5k_small": W.Workload("Q5_K layer H512 I256 E16 k4 T6", F.Q5K, 512, 256, 16, 4, 6),
 }
 
 
