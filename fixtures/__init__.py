@@ -24,6 +24,7 @@ MXFP4 = 2
 Q3K_Q4K = 3  # mixed expert: Q3_K gate and up, Q4_K down
 Q3K = 100  # block type of a Q3_K matrix (the mixed expert's gate and up)
 Q5K = 4
+Q6K = 5
 
 # Counter-stream tags (the second Philox key word) of the non-weight inputs.
 TAG_X = 0x58000000
@@ -61,6 +62,7 @@ def lib() -> ctypes.CDLL:
         L.fx_encode_mxfp4.argtypes = [vp, i64, vp]
         L.fx_encode_q3k.argtypes = [vp, i64, vp]
         L.fx_encode_q5k.argtypes = [vp, i64, vp]
+        L.fx_encode_q6k.argtypes = [vp, i64, vp]
         L.fx_matrix_bytes.argtypes = [i32, i64, i64]
         L.fx_matrix_bytes.restype = i64
         L.fx_expert_bytes.argtypes = [i32, i64, i64]
@@ -112,11 +114,11 @@ def encode(fmt: int, x: np.ndarray) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float32)
     cols = x.shape[-1]
     rows = x.size // cols
-    if cols % (256 if fmt in (Q4K, Q3K, Q5K) else 32) != 0:
+    if cols % (256 if fmt in (Q4K, Q3K, Q5K, Q6K) else 32) != 0:
         raise ValueError(f"row length {cols} is not a whole number of blocks")
     out = np.empty(lib().fx_matrix_bytes(fmt, rows, cols), dtype=np.uint8)
     enc = {Q8_0: lib().fx_encode_q8_0, Q4K: lib().fx_encode_q4k, MXFP4: lib().fx_encode_mxfp4,
-           Q3K: lib().fx_encode_q3k, Q5K: lib().fx_encode_q5k}[fmt]
+           Q3K: lib().fx_encode_q3k, Q5K: lib().fx_encode_q5k, Q6K: lib().fx_encode_q6k}[fmt]
     enc(_p(x), x.size, _p(out))
     return out
 

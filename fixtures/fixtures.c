@@ -457,10 +457,50 @@ void fx_encode_q5k(const float* x, int64_t n, uint8_t* out) {
     }
 }
 
+/* n floats (n % 256 == 0) -> n/256 Q6_K super-blocks of 210 bytes.  Per
+ * 16-weight sub-block j: the element of largest magnitude m_j sets the
+ * signed scale s_j = -m_j / 32 (it encodes as q - 32 = -32); d = fp16(max
+ * |s_j| / 127); sc_j = round(s_j / d) clamped to [-128, 127]; q - 32 =
+ * round(x / (d sc_j)) clamped to [-32, 31].  Layout: low nibbles (element
+ * 128h + 32g + l: byte 64h + l + 32 (g % 2), low nibble for g < 2), high bit
+ * pairs (bits 2g of byte 128 + 32h + l), the 16 scales, fp16 d. */
+void fx_encode_q6k(const float* x, int64_t n, uint8_t* out) {
+    for (int64_t b = 0; b < n / 256; ++b) {
+        const float* v = x + b * 256;
+        uint8_t* o = out + b * 210;
+        memset(o, 0, 210);
+        float s[16], smax = 0.0f;
+        for (int j = 0; j < 16; ++j) {
+            float m = 0.0f;
+            for (int i = 0; i < 16; ++i)
+                if (fabsf(v[16 * j + i]) > fabsf(m)) m = v[16 * j + i];
+            s[j] = -m / 32.0f;
+            if (fabsf(s[j]) > smax) smax = fabsf(s[j]);
+        }
+        uint16_t dh = fx_f32_to_f16(smax / 127.0f);
+        float df = fx_f16_to_f32(dh);
+        for (int j = 0; j < 16; ++j) {
+            float r = df > 0.0f ? round_half_away(s[j] / df) : 0.0f;
+            int sc = r < -128.0f ? -128 : (r > 127.0f ? 127 : (int)r);
+            o[192 + j] = (uint8_t)(int8_t)sc;
+            float step = df * (float)sc;
+            for (int i = 0; i < 16; ++i) {
+                int e = 16 * j + i;
+                float q = step != 0.0f ? round_half_away(v[e] / step) : 0.0f;
+                int qi = (q < -32.0f ? -32 : (q > 31.0f ? 31 : (int)q)) + 32;
+                int h = e / 128, g = (e % 128) / 32, l = e % 32;
+                o[64 * h + l + 32 * (g % 2)] |= (uint8_t)((qi & 15) << (g < 2 ? 0 : 4));
+                o[128 + 32 * h + l] |= (uint8_t)((qi >> 4) << (2 * g));
+            }
+        }
+        put_u16(o + 208, dh);
+    }
+}
+
 /* ------------------------------------------------------------- experts */
 
 /* Block types; FX_Q3K_Q4K is the mixed expert (Q3_K gate and up, Q4_K down). */
-enum { FX_Q8_0 = 0, FX_Q4K = 1, FX_MXFP4 = 2, FX_Q3K_Q4K = 3, FX_Q5K = 4, FX_Q3K = 100 };
+enum { FX_Q8_0 = 0, FX_Q4K = 1, FX_MXFP4 = 2, FX_Q3K_Q4K = 3, FX_Q5K = 4, FX_Q6K = 5, FX_Q3K = 100 };
 
 static int gate_up_fmt(int fmt) { return fmt == FX_Q3K_Q4K ? FX_Q3K : fmt; }
 static int down_fmt(int fmt) { return fmt == FX_Q3K_Q4K ? FX_Q4K : fmt; }
@@ -471,6 +511,7 @@ static int64_t row_bytes(int fmt, int64_t cols) {
         case FX_MXFP4: return cols / 32 * 17;
         case FX_Q3K: return cols / 256 * 110;
         case FX_Q5K: return cols / 256 * 176;
+        case FX_Q6K: return cols / 256 * 210;
         default: return cols / 256 * 144;
     }
 }
@@ -480,6 +521,7 @@ static void encode_row(int fmt, const float* x, int64_t n, uint8_t* out) {
     else if (fmt == FX_MXFP4) fx_encode_mxfp4(x, n, out);
     else if (fmt == FX_Q3K) fx_encode_q3k(x, n, out);
     else if (fmt == FX_Q5K) fx_encode_q5k(x, n, out);
+    else if (fmt == FX_Q6K) fx_encode_q6k(x, n, out);
     else fx_encode_q4k(x, n, out);
 }
 

@@ -23,6 +23,7 @@ MXFP4 = 2
 Q3K_Q4K = 3  # mixed expert: Q3_K gate and up, Q4_K down
 Q3K = 100  # block type of a Q3_K matrix (the mixed expert's gate and up)
 Q5K = 4
+Q6K = 5
 SOFTMAX = 0
 SIGMOID = 1
 
@@ -49,6 +50,7 @@ def lib() -> ctypes.CDLL:
         L.oracle_dequant_mxfp4.argtypes = [vp, i64, vp]
         L.oracle_dequant_q3k.argtypes = [vp, i64, vp]
         L.oracle_dequant_q5k.argtypes = [vp, i64, vp]
+        L.oracle_dequant_q6k.argtypes = [vp, i64, vp]
         L.oracle_route.argtypes = [vp, i32, i32, i32, i32, i32, f64, vp, vp]
         L.oracle_route.restype = i32
         L.oracle_batches.argtypes = [vp, vp, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -85,12 +87,13 @@ def set_defect(d: int) -> None:
 
 def dequant(fmt: int, blocks: np.ndarray, n: int) -> np.ndarray:
     blocks = np.ascontiguousarray(blocks, dtype=np.uint8)
-    bs, bb = {Q8_0: (32, 34), Q4K: (256, 144), MXFP4: (32, 17), Q3K: (256, 110), Q5K: (256, 176)}[fmt]
+    bs, bb = {Q8_0: (32, 34), Q4K: (256, 144), MXFP4: (32, 17), Q3K: (256, 110), Q5K: (256, 176),
+              Q6K: (256, 210)}[fmt]
     if n % bs or blocks.nbytes < n // bs * bb:
         raise ValueError("block count does not match n")
     out = np.empty(n, dtype=np.float64)
     fn = {Q8_0: lib().oracle_dequant_q8_0, Q4K: lib().oracle_dequant_q4k, MXFP4: lib().oracle_dequant_mxfp4,
-          Q3K: lib().oracle_dequant_q3k, Q5K: lib().oracle_dequant_q5k}[fmt]
+          Q3K: lib().oracle_dequant_q3k, Q5K: lib().oracle_dequant_q5k, Q6K: lib().oracle_dequant_q6k}[fmt]
     fn(_p(blocks), n, _p(out))
     return out
 

@@ -34,7 +34,8 @@ enum {
     D_MXFP4_BIAS_128 = 14,     /* MXFP4 scale exponent bias 128 instead of 127 */
     D_Q3K_SCALE_UNBIASED = 15, /* Q3_K 6-bit scales used without the -32 */
     D_Q3K_HMASK_INVERTED = 16, /* Q3_K high bit read with the opposite sense */
-    D_Q5K_HIGH_BIT_ORDER = 17  /* Q5_K high bit of element l taken from byte j*4 + l/8 */
+    D_Q5K_HIGH_BIT_ORDER = 17, /* Q5_K high bit of element l taken from byte j*4 + l/8 */
+    D_Q6K_NO_OFFSET = 18       /* Q6_K q used without the -32 */
 };
 
 void oracle_set_threads(int n) {
@@ -215,11 +216,38 @@ void oracle_dequant_q5k(const uint8_t* blocks, int64_t n, double* out) {
     }
 }
 
+/* Q6_K super-block (210 bytes): 128 bytes of low nibbles (ql), 64 bytes of
+ * high bit pairs (qh), 16 signed 8-bit scales, fp16 d.  Element i: half
+ * h = i / 128, quarter g = (i % 128) / 32, l = i % 32; low four bits from
+ * ql[64h + l + 32 (g % 2)], its low nibble for g < 2 and high nibble
+ * otherwise; high two bits = bits 2g..2g+1 of qh[32h + l]; q = low + 16 *
+ * high (0..63).  Sub-block j = i / 16 has the signed scale sc_j.
+ * w = d * sc_j * (q - 32).
+ * Parity pinned by hand-built golden blocks and the encoder round trip. */
+void oracle_dequant_q6k(const uint8_t* blocks, int64_t n, double* out) {
+    for (int64_t b = 0; b < n / 256; ++b) {
+        const uint8_t* blk = blocks + b * 210;
+        const uint8_t* ql = blk;
+        const uint8_t* qh = blk + 128;
+        const int8_t* sc = (const int8_t*)(blk + 192);
+        double d = half_le(blk + 208);
+        for (int i = 0; i < 256; ++i) {
+            int h = i / 128, g = (i % 128) / 32, l = i % 32;
+            uint8_t byte = ql[64 * h + l + 32 * (g % 2)];
+            int low = g < 2 ? (byte & 15) : (byte >> 4);
+            int high = (qh[32 * h + l] >> (2 * g)) & 3;
+            int q = low + 16 * high - (g_defect == D_Q6K_NO_OFFSET ? 0 : 32);
+            out[b * 256 + i] = d * (double)sc[i / 16] * (double)q;
+        }
+    }
+}
+
 static void dequant_row(int fmt, const uint8_t* row, int64_t n, double* out) {
     if (fmt == ORACLE_Q8_0) oracle_dequant_q8_0(row, n, out);
     else if (fmt == ORACLE_MXFP4) oracle_dequant_mxfp4(row, n, out);
     else if (fmt == ORACLE_Q3K) oracle_dequant_q3k(row, n, out);
     else if (fmt == ORACLE_Q5K) oracle_dequant_q5k(row, n, out);
+    else if (fmt == ORACLE_Q6K) oracle_dequant_q6k(row, n, out);
     else oracle_dequant_q4k(row, n, out);
 }
 
@@ -229,6 +257,7 @@ static int64_t row_bytes(int fmt, int64_t cols) {
         case ORACLE_MXFP4: return cols / 32 * 17;
         case ORACLE_Q3K: return cols / 256 * 110;
         case ORACLE_Q5K: return cols / 256 * 176;
+        case ORACLE_Q6K: return cols / 256 * 210;
         default: return cols / 256 * 144;
     }
 }

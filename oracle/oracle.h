@@ -17,6 +17,9 @@
  *               Q5_K:  w = d*sc_j*q - dmin*m_j      (as Q4_K, q in 0..31; a card
  *                                                    expert type: README 0.3.1
  *                                                    "Quant types" row)
+ *               Q6_K:  w = d*sc_j*(q - 32)            (256 per super-block, 16
+ *                                                    sub-blocks of 16, q in 0..63,
+ *                                                    signed 8-bit sc_j)
  *               MXFP4: w = 2^(X-127) * fp4(q)        (32 per block; OCP MX v1.0
  *                                                    E8M0 scale, E2M1 elements;
  *                                                    card expert type: README
@@ -51,7 +54,8 @@ extern "C" {
 #endif
 
 /* Block types; ORACLE_Q3K_Q4K is the mixed expert: Q3_K gate and up, Q4_K down. */
-enum { ORACLE_Q8_0 = 0, ORACLE_Q4K = 1, ORACLE_MXFP4 = 2, ORACLE_Q3K_Q4K = 3, ORACLE_Q5K = 4, ORACLE_Q3K = 100 };
+enum { ORACLE_Q8_0 = 0, ORACLE_Q4K = 1, ORACLE_MXFP4 = 2, ORACLE_Q3K_Q4K = 3, ORACLE_Q5K = 4, ORACLE_Q6K = 5,
+       ORACLE_Q3K = 100 };
 enum { ORACLE_SOFTMAX = 0, ORACLE_SIGMOID = 1 };
 
 /* Dequantize n weights (n a multiple of the block size) from stored blocks. */
@@ -60,6 +64,7 @@ void oracle_dequant_q4k(const uint8_t* blocks, int64_t n, double* out);
 void oracle_dequant_mxfp4(const uint8_t* blocks, int64_t n, double* out);
 void oracle_dequant_q3k(const uint8_t* blocks, int64_t n, double* out);
 void oracle_dequant_q5k(const uint8_t* blocks, int64_t n, double* out);
+void oracle_dequant_q6k(const uint8_t* blocks, int64_t n, double* out);
 
 /* Top-k routing of T rows of E logits.  Returns 0, or -1 on bad sizes. */
 int oracle_route(const float* logits, int T, int E, int k, int score, int renormalize, double scale,

@@ -152,10 +152,35 @@ def random_q5k_matrix(rng: np.random.Generator, rows: int, cols: int, d_bits: in
     return np.frombuffer(b"".join(parts), dtype=np.uint8).copy(), dense
 
 
+def q6k_superblock(d_bits: int, sc, q) -> bytes:
+    """sc: 16 ints in -128..127; q: 256 ints in 0..63 (low nibbles, high bit pairs, scales, d)."""
+    ql, qh = [0] * 128, [0] * 64
+    for i in range(256):
+        v = int(q[i])
+        h, g, l = i // 128, (i % 128) // 32, i % 32
+        ql[64 * h + l + 32 * (g % 2)] |= (v & 15) << (0 if g < 2 else 4)
+        qh[32 * h + l] |= (v >> 4) << (2 * g)
+    return bytes(ql + qh + [int(v) & 0xFF for v in sc] + [d_bits & 0xFF, d_bits >> 8])
+
+
+def random_q6k_matrix(rng: np.random.Generator, rows: int, cols: int, d_bits: int = 0x1800):
+    """A Q6_K matrix with random signed 8-bit scales and 6-bit quants; returns (bytes, exact dense values)."""
+    d = half_bits_value(d_bits)
+    dense = np.empty((rows, cols), dtype=np.float64)
+    parts = []
+    for r in range(rows):
+        for sb in range(cols // 256):
+            sc = rng.integers(-128, 128, size=16)
+            q = rng.integers(0, 64, size=256)
+            parts.append(q6k_superblock(d_bits, sc, q))
+            dense[r, sb * 256:(sb + 1) * 256] = d * np.repeat(sc, 16) * (q - 32)
+    return np.frombuffer(b"".join(parts), dtype=np.uint8).copy(), dense
+
+
 def random_expert(rng: np.random.Generator, fmt: int, H: int, I: int):
     """Canonical blob Wg|Wu|Wd with exactly known dense matrices (fmt 3: Q3_K gate/up, Q4_K down)."""
     make_gu = {0: random_q8_0_matrix, 1: random_q4k_matrix, 2: random_mxfp4_matrix, 3: random_q3k_matrix,
-               4: random_q5k_matrix}[fmt]
+               4: random_q5k_matrix, 5: random_q6k_matrix}[fmt]
     make_dn = random_q4k_matrix if fmt == 3 else make_gu
     bg, g = make_gu(rng, I, H)
     bu, u = make_gu(rng, I, H)

@@ -151,6 +151,27 @@ def q5k_case(name: str, d_bits: int, dmin_bits: int, sc: list[int], m: list[int]
                 bytes_hex=bytes(raw).hex(), expected=[frac_str(v) for v in expected])
 
 
+def q6k_case(name: str, d_bits: int, sc: list[int], q: list[int], note: str) -> dict:
+    """One Q6_K super-block: 16 signed 8-bit scales, 256 quants q in 0..63
+    (w uses q - 32).  Bytes as read for this build: 128 bytes of low nibbles
+    (element 128h + 32g + l: byte 64h + l + 32 (g % 2), low nibble for g < 2,
+    high nibble otherwise), 64 bytes of high bit pairs (bits 2g of byte
+    32h + l), the 16 scales, fp16 d."""
+    assert len(sc) == 16 and len(q) == 256
+    assert all(-128 <= v <= 127 for v in sc) and all(0 <= v <= 63 for v in q)
+    ql, qh = [0] * 128, [0] * 64
+    for i, v in enumerate(q):
+        h, g, l = i // 128, (i % 128) // 32, i % 32
+        ql[64 * h + l + 32 * (g % 2)] |= (v & 15) << (0 if g < 2 else 4)
+        qh[32 * h + l] |= (v >> 4) << (2 * g)
+    raw = ql + qh + [v & 0xFF for v in sc] + [d_bits & 0xFF, d_bits >> 8]
+    assert len(raw) == 210
+    d = half_value(d_bits)
+    expected = [d * sc[i // 16] * (q[i] - 32) for i in range(256)]
+    return dict(name=name, format="Q6_K", note=note, d_bits=d_bits, sc=sc, q=q, bytes_hex=bytes(raw).hex(),
+                expected=[frac_str(v) for v in expected])
+
+
 def main() -> None:
     cases = []
     cases.append(q8_0_case(
@@ -195,6 +216,10 @@ def main() -> None:
         "q5k_every_field", 0x3400, 0x3000, [1, 17, 33, 63, 20, 47, 5, 62], [63, 0, 16, 31, 48, 15, 32, 1],
         [[(5 * l + 3 * j) % 32 for l in range(32)] for j in range(8)],
         "d = 1/4, dmin = 1/8; every q in 0..31 in every sub-block (high bit set and clear); scales >= 16"))
+    cases.append(q6k_case(
+        "q6k_every_field", 0x2C00, [-128, 127, -1, 0, 1, 64, -64, 33, -33, 100, -100, 7, -7, 90, -90, 2],
+        [(13 * i + i // 16) % 64 for i in range(256)],
+        "d = 1/16; scales span -128..127; every q in 0..63 with every high bit pair"))
     doc = dict(
         citation=("Stored block types: bloomery README of 2026-09-24 (shared experts in Q8_0) and bloomery README "
                   "0.3.1, 'Status (0.3.1)' table, 'Quant types' row (card experts in Q4_K to Q6_K and MXFP4); "

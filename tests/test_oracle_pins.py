@@ -35,7 +35,8 @@ def pin_golden_blocks() -> bool:
     ok = True
     for case in doc["cases"]:
         raw = np.frombuffer(bytes.fromhex(case["bytes_hex"]), dtype=np.uint8)
-        fmt = {"Q8_0": O.Q8_0, "Q4_K": O.Q4K, "MXFP4": O.MXFP4, "Q3_K": O.Q3K, "Q5_K": O.Q5K}[case["format"]]
+        fmt = {"Q8_0": O.Q8_0, "Q4_K": O.Q4K, "MXFP4": O.MXFP4, "Q3_K": O.Q3K, "Q5_K": O.Q5K,
+               "Q6_K": O.Q6K}[case["format"]]
         got = O.dequant(fmt, raw, len(case["expected"]))
         want = np.array([float(Fraction(v)) for v in case["expected"]])
         ok &= bool(np.array_equal(got, want))
@@ -83,6 +84,17 @@ def pin_encoder_round_trip() -> bool:
     dm = np.array([B.half_bits_value(int(b[2]) | (int(b[3]) << 8)) for b in blk])
     bound = np.repeat((48 * d + 0.5 * dm) * (1 + 2.0 ** -9) + 1e-12, 256).reshape(w.shape)
     ok &= bool(np.all(np.abs(got - w) <= bound))
+    ok &= bool(np.corrcoef(got.ravel(), w.ravel())[0, 1] > 0.99)
+    # Q6_K: each sub-block's largest element maps to -32 steps; scale rounding
+    # (half a d per step count) and clamping at 31 leave every weight within
+    # |d sc_j| + 16.5 d of its value.
+    raw = F.encode(O.Q6K, w.astype(np.float32))
+    got = O.dequant(O.Q6K, raw, w.size).reshape(w.shape)
+    blk = raw.reshape(-1, 210)
+    d = np.array([B.half_bits_value(int(b[208]) | (int(b[209]) << 8)) for b in blk])
+    sc = blk[:, 192:208].view(np.int8).astype(np.float64)
+    bound = np.repeat((np.abs(sc) * d[:, None] * 1.001 + 16.5 * d[:, None]).reshape(-1), 16).reshape(w.shape)
+    ok &= bool(np.all(np.abs(got - w) <= bound + 1e-12))
     ok &= bool(np.corrcoef(got.ravel(), w.ravel())[0, 1] > 0.99)
     # Q3_K: the step d*sc_j of sub-block j maps its largest element to -4 up
     # to scale rounding (half a d) and clamping at 3; every weight lies within
@@ -154,7 +166,8 @@ def _dense_ffn(g, u, dn, x):
 
 def pin_ffn_dense(fmt: int) -> bool:
     rng = np.random.default_rng(17 + fmt)
-    H, I = {O.Q4K: (512, 256), O.Q8_0: (96, 64), O.MXFP4: (128, 96), O.Q3K_Q4K: (512, 256), O.Q5K: (512, 256)}[fmt]
+    H, I = {O.Q4K: (512, 256), O.Q8_0: (96, 64), O.MXFP4: (128, 96), O.Q3K_Q4K: (512, 256), O.Q5K: (512, 256),
+              O.Q6K: (512, 256)}[fmt]
     blob, (g, u, dn) = B.random_expert(rng, fmt, H, I)
     x = rng.normal(size=H)
     got = O.expert_ffn(fmt, blob, H, I, x)
@@ -255,6 +268,7 @@ PINS = {
     "ffn_dense_mxfp4": lambda: pin_ffn_dense(O.MXFP4),
     "ffn_dense_q3k_q4k": lambda: pin_ffn_dense(O.Q3K_Q4K),
     "ffn_dense_q5k": lambda: pin_ffn_dense(O.Q5K),
+    "ffn_dense_q6k": lambda: pin_ffn_dense(O.Q6K),
     "layer_brute_softmax_partial": lambda: pin_layer_brute_force(O.SOFTMAX, True),
     "layer_brute_sigmoid_full": lambda: pin_layer_brute_force(O.SIGMOID, False),
     "disjoint_halves": pin_disjoint_halves,
@@ -304,6 +318,8 @@ DEFECTS = [
     (16, "encoder_round_trip"),
     (17, "golden_blocks"),                 # Q5_K high bits from the wrong byte
     (17, "ffn_dense_q5k"),
+    (18, "golden_blocks"),                 # Q6_K without the -32 offset
+    (18, "ffn_dense_q6k"),
 ]
 
 
