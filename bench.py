@@ -15,8 +15,9 @@ Cache cannot serve it and the GEMV reads HBM.
 Printed: one JSON line with the throughput of the timed region (K steps of
 hipGraph replays, one graph per step, bracketed by synchronisation), the
 roofline of the dominant kernel (the gate/up GEMV: algorithmic bytes =
-selected experts' gate and up weights, over its HIP-event-timed duration in
-an eager pass of the same K steps), and the CPU oracle timed on a bounded
+selected experts' gate and up weights, over its duration in an eager pass of
+the same K steps, from HIP events attached to its dispatches on the launch
+stream), and the CPU oracle timed on a bounded
 sample of the same workload on the host cores.
 """
 from __future__ import annotations
@@ -147,7 +148,8 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # ---- eager pass with HIP-event stage timers (kernel durations on the launch stream)
+    # ---- eager pass with the stage timers (HIP events attached to the stages' own
+    # dispatches on the launch stream: kernel begin to kernel end)
     stages = {"route_batches": 8, "ffn_gateup": 3, "ffn_down": 4, "combine": 5}
     for s in stages.values():
         Q.moe_timer_begin(s, args.steps)
@@ -470,11 +472,13 @@ def bench_formats(args, threads: int) -> dict:
     res = {}
     def gateup_bytes(wl) -> int:  # stored bytes of one expert's gate and up matrices
         w = 2 * wl.H * wl.I
-        return {F.MXFP4: w // 32 * 17, F.Q3K_Q4K: w // 256 * 110, F.Q4K: w // 256 * 144, F.Q5K: w // 256 * 176}[wl.fmt]
+        return {F.MXFP4: w // 32 * 17, F.Q3K_Q4K: w // 256 * 110, F.Q4K: w // 256 * 144, F.Q5K: w // 256 * 176,
+                F.Q6K: w // 256 * 210}[wl.fmt]
 
     for key, wl, copies in (("mxfp4_qwen3_T2", W.QWEN3_MXFP4_DECODE_T2, 8), ("mxfp4_dsv3_T2", W.DSV3_MXFP4_DECODE_T2, 1),
                             ("q3k_q4k_dsv3_T2", W.DSV3_Q3K_DECODE_T2, 1), ("q5k_qwen3_T2", W.QWEN3_Q5K_DECODE_T2, 8),
-                            ("q5k_dsv3_T2", W.DSV3_Q5K_DECODE_T2, 1)):
+                            ("q5k_dsv3_T2", W.DSV3_Q5K_DECODE_T2, 1), ("q6k_qwen3_T2", W.QWEN3_Q6K_DECODE_T2, 8),
+                            ("q6k_dsv3_T2", W.DSV3_Q6K_DECODE_T2, 1)):
         blobs = W.expert_blobs(wl)
         nb = Q.moe_expert_blob_bytes(wl.fmt, wl.H, wl.I)
         npk = Q.moe_packed_blob_bytes(wl.fmt, wl.H, wl.I)
@@ -546,7 +550,7 @@ def bench_formats(args, threads: int) -> dict:
         res[key] = r
         del graphs, layer, pools, shared
         torch.cuda.empty_cache()
-    res["note"] = ("MXFP4 codes converted to fp16 by the hardware FP4 conversion, Q3_K and Q5_K quants by and-or "
+    res["note"] = ("MXFP4 codes converted to fp16 by the hardware FP4 conversion, Q3_K, Q5_K and Q6_K quants by and-or "
                    "operations into fp16 magic numbers; fp16 x fp16 dot products, fp32 accumulate; expert_bytes and "
                    "layer bytes count the stored (canonical) bytes")
     return res
@@ -692,6 +696,7 @@ def bench_stack(args, threads: int) -> dict:
         "swap_during_replays_ms": round(swap_during_ms, 1),
         "swap_during_replays_GBs": round(swap_bytes / (swap_during_ms * 1e-3) / 1e9, 1),
         "replays_during_swap": n_during, "replay_ms_during_swap": round(replay_ms_during, 3),
+        "copy_stream": {"candidates_tried": st.side_probes, "overlaps_replays": st.side_overlaps},
         "pcie_gen5_x16_GBs": 64.0,
         "host_leg": host_leg,
         "adaptive_residency": residency,

@@ -11,7 +11,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from . import MXFP4, Q3K_Q4K, Q4K, Q5K, Q8_0, TAG_SHARED_EXPERT, activations, expert_blob, logits_normal, logits_zipf, to_bf16_bits
+from . import MXFP4, Q3K_Q4K, Q4K, Q5K, Q6K, Q8_0, TAG_SHARED_EXPERT, activations, expert_blob, logits_normal, logits_zipf, to_bf16_bits
 from . import expert_blobs as _expert_blobs
 
 SOFTMAX, SIGMOID = 0, 1
@@ -72,8 +72,14 @@ QWEN3_Q5K_DECODE_T2 = Workload("Qwen3-30B-A3B-shaped MoE layer, Q5_K experts, de
 DSV3_Q5K_DECODE_T2 = Workload("DeepSeek-V3-shaped MoE layer, Q5_K experts, decode T=2 (+shared Q8_0 expert)", Q5K,
                               7168, 2048, 256, 8, 2, score=SIGMOID, scale=2.5, I_shared=2048)
 
+# Q6_K experts (the top of the engine's card K-quant range).
+QWEN3_Q6K_DECODE_T2 = Workload("Qwen3-30B-A3B-shaped MoE layer, Q6_K experts, decode T=2", Q6K, 2048, 768, 128, 8, 2)
+DSV3_Q6K_DECODE_T2 = Workload("DeepSeek-V3-shaped MoE layer, Q6_K experts, decode T=2 (+shared Q8_0 expert)", Q6K,
+                              7168, 2048, 256, 8, 2, score=SIGMOID, scale=2.5, I_shared=2048)
+
 ALL = [TINY, QWEN3_DECODE_T1, QWEN3_DECODE_T2, QWEN3_PREFILL, DSV3_DECODE_T2, DSV3_DECODE_T4, DSV3_STACK,
-       QWEN3_MXFP4_DECODE_T2, DSV3_MXFP4_DECODE_T2, DSV3_Q3K_DECODE_T2, QWEN3_Q5K_DECODE_T2, DSV3_Q5K_DECODE_T2]
+       QWEN3_MXFP4_DECODE_T2, DSV3_MXFP4_DECODE_T2, DSV3_Q3K_DECODE_T2, QWEN3_Q5K_DECODE_T2, DSV3_Q5K_DECODE_T2,
+       QWEN3_Q6K_DECODE_T2, DSV3_Q6K_DECODE_T2]
 
 
 def x_of(w: Workload, layer: int = 0, seed: int | None = None) -> np.ndarray:

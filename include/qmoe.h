@@ -19,6 +19,7 @@
  *   moe_expert_ffn_mxfp4 /
  *   moe_expert_ffn_q3k_q4k /
  *   moe_expert_ffn_q5k
+ *   moe_expert_ffn_q6k
  *   moe_combine               weighted sum of the pairs (+ shared expert)
  *
  * Conventions for every call:
@@ -65,7 +66,8 @@ typedef enum moe_format {
     MOE_FMT_Q4K = 1,
     MOE_FMT_MXFP4 = 2,
     MOE_FMT_Q3K_Q4K = 3, /* mixed expert: Q3_K gate and up, Q4_K down */
-    MOE_FMT_Q5K = 4
+    MOE_FMT_Q5K = 4,
+    MOE_FMT_Q6K = 5
 } moe_format;
 
 /* Limits checked by the calls below. */
@@ -212,13 +214,20 @@ moe_status moe_count_routes(const int32_t* topk_ids, int T, int k, int E, uint32
  *        high bits, 128 B of low nibbles in the Q4_K order; element l of
  *        sub-block j has its high bit at bit j of high-bit byte l;
  *        q = low + 16*high (0..31);                 w = d*sc_j*q - dmin*m_j.
+ *   Q6_K (210 B / 256 weights; the top of the card's K-quant range in
+ *        README 0.3.1 "Quant types" row): 128 B of low nibbles, 64 B of
+ *        high bit pairs, 16 signed 8-bit scales for 16 sub-blocks of 16,
+ *        fp16 d; element i (half h = i/128, quarter g = (i%128)/32,
+ *        l = i%32): low four bits in byte 64h + l + 32(g%2) (low nibble for
+ *        g < 2, else high), high two bits at bits 2g of high-bit byte
+ *        32h + l; q = low + 16*high (0..63);        w = d*sc_j*(q - 32).
  *   MOE_FMT_Q3K_Q4K is the mixed expert DeepSeek-V4.1-class files put on the
  *        card (bloomery README 0.3.11, limits list: V4.1's card experts are
  *        Q3_K gate and up with a Q4_K down): W_gate and W_up in Q3_K, W_down
  *        in Q4_K.
  * Canonical blob = W_gate | W_up | W_down, each row-major.
  *
- * Supported shapes: Q4_K, Q5_K, MXFP4 and Q3_K/Q4_K need H % 256 == 0 and
+ * Supported shapes: Q4_K, Q5_K, Q6_K, MXFP4 and Q3_K/Q4_K need H % 256 == 0 and
  * I % 256 == 0; Q8_0 needs H % 128 == 0 and I % 128 == 0.
  */
 size_t moe_expert_blob_bytes(int format, int H, int I);
@@ -299,6 +308,10 @@ moe_status moe_expert_ffn_q5k(const void* slot_pool, size_t slot_stride, int S, 
                               int x_dtype, int T, int k, const int32_t* slot_offsets, const int32_t* active_slots,
                               const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype,
                               int path, void* ws, size_t ws_bytes, void* stream);
+moe_status moe_expert_ffn_q6k(const void* slot_pool, size_t slot_stride, int S, int H, int I, const void* x,
+                              int x_dtype, int T, int k, const int32_t* slot_offsets, const int32_t* active_slots,
+                              const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype,
+                              int path, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- combine
  * y[t] = sum over j < k, in j order, of [slot_of_expert[id] >= 0] *
@@ -317,8 +330,12 @@ moe_status moe_combine(const void* y_pairs, int y_pairs_dtype, const int32_t* to
                        int y_dtype, void* stream);
 
 /* ------------------------------------------------------------ stage timers
- * Diagnostics: hipEvent pairs recorded around every launch of one stage, on
- * the launch's stream.  Not for use while a stream is being captured.
+ * Diagnostics: one hipEvent pair per launch of a stage, attached to the
+ * stage's kernel dispatches themselves (hipExtLaunchKernelGGL: the first
+ * kernel of the stage takes the start event, the last the stop event), so a
+ * launch's time runs from its first kernel's start to its last kernel's end,
+ * as a kernel trace measures it.  Not for use while a stream is being
+ * captured.
  *   stage: 0 route, 1 batches, 2 prefill tile list, 3 ffn gate/up (decode),
  *          4 ffn down (decode), 5 combine, 6 prefill gate/up GEMM, 7 prefill down GEMM,
  *          8 fused route + batches.
@@ -327,7 +344,7 @@ moe_status moe_combine(const void* y_pairs, int y_pairs_dtype, const int32_t* to
  * recorded event, returns the summed kernel time in milliseconds and the
  * number of launches timed, and releases the events.
  */
-#define MOE_STAGE_COUNT 8
+#define MOE_STAGE_COUNT 9
 moe_status moe_timer_begin(int stage, int capacity);
 moe_status moe_timer_end(int stage, double* total_ms, int* launches);
 

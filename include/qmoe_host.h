@@ -37,12 +37,13 @@ extern "C" {
  * FFN_e(x) = W_down,e (silu(W_gate,e x) * W_up,e x), silu(z) = z / (1 + e^-z).
  *
  * format        0 = Q8_0, 1 = Q4_K, 2 = MXFP4, 3 = Q3_K gate/up with a Q4_K
- *               down, 4 = Q5_K (the blocks' stored types, as in qmoe.h).
+ *               down, 4 = Q5_K, 5 = Q6_K (the blocks' stored types, as in
+ *               qmoe.h).
  * expert_blob   host, [E] pointers: expert e's canonical blob (W_gate [I,H],
  *               then W_up [I,H], then W_down [H,I], rows of blocks along the
  *               input dimension, as moe_pack_expert takes them), or NULL for
  *               an expert that no listed pair uses.  Read only.
- * E, H, I       experts, hidden, intermediate.  Q4_K, Q5_K and Q3_K/Q4_K:
+ * E, H, I       experts, hidden, intermediate.  Q4_K, Q5_K, Q6_K, Q3_K/Q4_K:
  *               H, I multiples of 256; Q8_0 and MXFP4: multiples of 32.
  * x             host, fp32 [T, H].
  * host_token, host_expert, host_weight
@@ -56,7 +57,8 @@ extern "C" {
  * that order, so the result is the same for any thread count.  fp32
  * arithmetic: each weight row is dequantized to fp32 (Q4_K: d sc_j q -
  * dmin m_j by one fused multiply-add; Q8_0: d q; MXFP4: 2^(X-127) fp4(q),
- * exact; Q3_K: d (sc_j - 32) q, exact; Q5_K as Q4_K) and dotted with x, or h,
+ * exact; Q3_K: d (sc_j - 32) q, exact; Q5_K as Q4_K; Q6_K: q (d sc_j) -
+ * 32 d sc_j by one fused multiply-subtract) and dotted with x, or h,
  * in fp32 fused multiply-adds; h = silu(g) u in fp32.
  * Returns MOE_OK, MOE_ERR_INVALID_ARGUMENT (bad sizes, a pair outside [0, T)
  * x [0, E), a listed expert without a blob, NULL buffers) or

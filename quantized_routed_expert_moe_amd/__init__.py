@@ -22,7 +22,8 @@ MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMA
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_F32, MOE_BF16 = 0, 1
 MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL = 0, 1, 2
-MOE_FMT_Q8_0, MOE_FMT_Q4K, MOE_FMT_MXFP4, MOE_FMT_Q3K_Q4K, MOE_FMT_Q5K = 0, 1, 2, 3, 4  # Q3K_Q4K: Q3_K gate/up, Q4_K down
+MOE_FMT_Q8_0, MOE_FMT_Q4K, MOE_FMT_MXFP4, MOE_FMT_Q3K_Q4K, MOE_FMT_Q5K, MOE_FMT_Q6K = 0, 1, 2, 3, 4, 5
+# (MOE_FMT_Q3K_Q4K: Q3_K gate and up, Q4_K down)
 STAGES = ("route", "batches", "prefill_tiles", "ffn_gateup", "ffn_down", "combine", "prefill_gateup", "prefill_down",
           "route_batches")
 
@@ -70,13 +71,14 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_ffn_mxfp4.argtypes = ffn
         L.moe_expert_ffn_q3k_q4k.argtypes = ffn
         L.moe_expert_ffn_q5k.argtypes = ffn
+        L.moe_expert_ffn_q6k.argtypes = ffn
         L.moe_combine.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, i32, i32, vp, i32, vp]
         L.moe_timer_begin.argtypes = [i32, i32]
         L.moe_timer_end.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
         for name in ("moe_route_topk", "moe_build_expert_batches", "moe_route_and_batch", "moe_count_routes",
                      "moe_pack_expert", "moe_unpack_expert",
                      "moe_validate_slot_map", "moe_expert_ffn_q4k", "moe_expert_ffn_q8_0", "moe_expert_ffn_mxfp4",
-                     "moe_expert_ffn_q3k_q4k", "moe_expert_ffn_q5k",
+                     "moe_expert_ffn_q3k_q4k", "moe_expert_ffn_q5k", "moe_expert_ffn_q6k",
                      "moe_combine",
                      "moe_timer_begin", "moe_timer_end"):
             getattr(L, name).restype = i32
@@ -316,10 +318,17 @@ def moe_expert_ffn_q5k(slot_pool, slot_stride, S, H, I, x, k, slot_offsets, acti
          perm_pair, y_pairs, path, ws, stream)
 
 
+def moe_expert_ffn_q6k(slot_pool, slot_stride, S, H, I, x, k, slot_offsets, active_slots, num_active, perm_pair,
+                       y_pairs, path=MOE_PATH_AUTO, ws=None, stream=None):
+    _ffn(lib().moe_expert_ffn_q6k, slot_pool, slot_stride, S, H, I, x, k, slot_offsets, active_slots, num_active,
+         perm_pair, y_pairs, path, ws, stream)
+
+
 def moe_expert_ffn(fmt: int):
     """The expert-FFN call of a block format."""
     return {MOE_FMT_Q8_0: moe_expert_ffn_q8_0, MOE_FMT_Q4K: moe_expert_ffn_q4k, MOE_FMT_MXFP4: moe_expert_ffn_mxfp4,
-            MOE_FMT_Q3K_Q4K: moe_expert_ffn_q3k_q4k, MOE_FMT_Q5K: moe_expert_ffn_q5k}[fmt]
+            MOE_FMT_Q3K_Q4K: moe_expert_ffn_q3k_q4k, MOE_FMT_Q5K: moe_expert_ffn_q5k,
+            MOE_FMT_Q6K: moe_expert_ffn_q6k}[fmt]
 
 
 def moe_combine(y_pairs, topk_ids, topk_w, slot_of_expert, y_shared, y, stream=None):

@@ -46,11 +46,12 @@ moe_status check_route_shape(int T, int E, int k) {
 }
 
 moe_status check_shape(int format, int H, int I) {
-    if (format < MOE_FMT_Q8_0 || format > MOE_FMT_Q5K)
+    if (format < MOE_FMT_Q8_0 || format > MOE_FMT_Q6K)
         return fail(MOE_ERR_INVALID_ARGUMENT,
-                    "format = %d is not MOE_FMT_Q8_0, MOE_FMT_Q4K, MOE_FMT_MXFP4, MOE_FMT_Q3K_Q4K or MOE_FMT_Q5K", format);
+                    "format = %d is not MOE_FMT_Q8_0, MOE_FMT_Q4K, MOE_FMT_MXFP4, MOE_FMT_Q3K_Q4K, MOE_FMT_Q5K or "
+                    "MOE_FMT_Q6K", format);
     const int m = format == MOE_FMT_Q8_0 ? 128 : 256;
-    static const char* const kNames[] = {"Q8_0", "Q4_K", "MXFP4", "Q3_K/Q4_K", "Q5_K"};
+    static const char* const kNames[] = {"Q8_0", "Q4_K", "MXFP4", "Q3_K/Q4_K", "Q5_K", "Q6_K"};
     if (H <= 0 || I <= 0) return fail(MOE_ERR_INVALID_ARGUMENT, "H = %d, I = %d must be positive", H, I);
     if (H % m || I % m)
         return fail(MOE_ERR_UNSUPPORTED, "%s needs H and I multiples of %d (H = %d, I = %d)",
@@ -67,6 +68,7 @@ size_t blob_bytes(int format, int H, int I) {
         case MOE_FMT_MXFP4: return 3 * w / 32 * 17;
         case MOE_FMT_Q3K_Q4K: return 2 * w / 256 * 110 + w / 256 * 144;
         case MOE_FMT_Q5K: return 3 * w / 256 * 176;
+        case MOE_FMT_Q6K: return 3 * w / 256 * 210;
         default: return 3 * w / 32 * 34;
     }
 }
@@ -92,6 +94,7 @@ struct StageTimer {
     std::vector<hipEvent_t> start, stop;
 };
 StageTimer g_timer[qmoe::kStageCount];
+static_assert(MOE_STAGE_COUNT == qmoe::kStageCount, "stage counts differ");
 std::mutex g_timer_mu;
 
 // ------------------------------------------------------------------ packing
@@ -449,6 +452,76 @@ void q5k_walk(const uint8_t* in, uint8_t* out, int H, int I) {
     section(qmoe::q5k_gateup_bytes(H, I), 1, H / 64, I / 256, rbI, 2 * gbytes, 0);
 }
 
+// Q6_K: one canonical 210-byte super-block (low nibbles, high bit pairs, 16
+// signed scales, fp16 d) <-> its packed fields: the 16 scale bytes, eight
+// 16-byte nibble slots in the Q4_K packed order, per block the words (H0,
+// H1) of two high bits per element, and d.
+void q6k_block(const uint8_t* canon, uint8_t* sc, uint8_t* const* nib, uint32_t* hw, uint8_t* d, bool pack) {
+    uint8_t q[32];
+    if (pack) {
+        memcpy(sc, canon + 192, 16);
+        memcpy(d, canon + 208, 2);
+        for (int j = 0; j < 8; ++j) {
+            hw[2 * j] = hw[2 * j + 1] = 0;
+            for (int e = 0; e < 32; ++e) {
+                const int i = 32 * j + e, h = i / 128, g = (i % 128) / 32, l = i % 32;
+                const uint8_t byte = canon[64 * h + l + 32 * (g % 2)];
+                q[e] = g < 2 ? (byte & 15) : (byte >> 4);
+                const uint32_t high = (canon[128 + 32 * h + l] >> (2 * g)) & 3;
+                const int dd = e / 8, n = e % 8;
+                hw[2 * j + dd / 2] |= high << (4 * n + 2 * (dd % 2));
+            }
+            nibbles_pack(q, nib[j]);
+        }
+    } else {
+        uint8_t* dst = const_cast<uint8_t*>(canon);
+        memset(dst, 0, 210);
+        memcpy(dst + 192, sc, 16);
+        memcpy(dst + 208, d, 2);
+        for (int j = 0; j < 8; ++j) {
+            nibbles_unpack(nib[j], q);
+            for (int e = 0; e < 32; ++e) {
+                const int i = 32 * j + e, h = i / 128, g = (i % 128) / 32, l = i % 32;
+                const int dd = e / 8, n = e % 8;
+                const uint32_t high = (hw[2 * j + dd / 2] >> (4 * n + 2 * (dd % 2))) & 3;
+                dst[64 * h + l + 32 * (g % 2)] |= (uint8_t)(q[e] << (g < 2 ? 0 : 4));
+                dst[128 + 32 * h + l] |= (uint8_t)(high << (2 * g));
+            }
+        }
+    }
+}
+
+template <bool PACK>
+void q6k_walk(const uint8_t* in, uint8_t* out, int H, int I) {
+    const size_t rbH = (size_t)H / 256 * 210, rbI = (size_t)I / 256 * 210;
+    const size_t gbytes = (size_t)I * rbH;
+    uint8_t* dev = PACK ? out : const_cast<uint8_t*>(in);
+    const uint8_t* canon_base = PACK ? in : out;
+    uint32_t hw[16];
+    uint8_t* nib[8];
+    auto section = [&](size_t base, int nmat, int row_tiles, int units, size_t rb, size_t canon0, size_t cstride) {
+        const size_t tbytes = (size_t)nmat * qmoe::kQ6kDownTile;
+        for (int rg = 0; rg < row_tiles; ++rg)
+            for (int u = 0; u < units; ++u) {
+                uint8_t* tile = dev + base + ((size_t)rg * units + u) * tbytes;
+                for (int r = 0; r < 64; ++r)
+                    for (int m = 0; m < nmat; ++m) {
+                        const uint8_t* canon = canon_base + canon0 + m * cstride + ((size_t)rg * 64 + r) * rb + (size_t)u * 210;
+                        for (int j = 0; j < 8; ++j) nib[j] = tile + nmat * 1024 + j * nmat * 1024 + m * 1024 + r * 16;
+                        uint8_t* hp = tile + nmat * 9216 + m * 1024 + r * 16;  // chunk c at + c nmat KB
+                        uint8_t* dp = tile + nmat * 13312 + 2 * nmat * r + 2 * m;
+                        if (!PACK)
+                            for (int c = 0; c < 4; ++c) memcpy(hw + 4 * c, hp + c * nmat * 1024, 16);
+                        q6k_block(canon, tile + m * 1024 + r * 16, nib, hw, dp, PACK);
+                        if (PACK)
+                            for (int c = 0; c < 4; ++c) memcpy(hp + c * nmat * 1024, hw + 4 * c, 16);
+                    }
+            }
+    };
+    section(0, 2, I / 64, H / 256, rbH, 0, gbytes);
+    section(qmoe::q6k_gateup_bytes(H, I), 1, H / 64, I / 256, rbI, 2 * gbytes, 0);
+}
+
 moe_status ffn_common(int format, const void* slot_pool, size_t slot_stride, int S, int H, int I, const void* x,
                       int x_dtype, int T, int k, const int32_t* slot_offsets, const int32_t* active_slots,
                       const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype, int path,
@@ -506,21 +579,17 @@ moe_status ffn_common(int format, const void* slot_pool, size_t slot_stride, int
 
 namespace qmoe {
 
-void timer_before(int stage, hipStream_t s) {
+StageEvents timer_events(int stage) {
     StageTimer& t = g_timer[stage];
-    if (!t.armed.load(std::memory_order_relaxed)) return;
+    StageEvents ev;
+    if (!t.armed.load(std::memory_order_relaxed)) return ev;
     std::lock_guard<std::mutex> lk(g_timer_mu);
-    if (t.used < t.capacity) hipEventRecord(t.start[t.used], s);
-}
-
-void timer_after(int stage, hipStream_t s) {
-    StageTimer& t = g_timer[stage];
-    if (!t.armed.load(std::memory_order_relaxed)) return;
-    std::lock_guard<std::mutex> lk(g_timer_mu);
-    if (t.used < t.capacity) {
-        hipEventRecord(t.stop[t.used], s);
+    if (t.armed.load() && t.used < t.capacity) {
+        ev.start = t.start[t.used];
+        ev.stop = t.stop[t.used];
         ++t.used;
     }
+    return ev;
 }
 
 }  // namespace qmoe
@@ -643,6 +712,7 @@ moe_status moe_pack_expert(int format, const void* canonical, void* packed, int 
     else if (format == MOE_FMT_MXFP4) mx4_walk<true>(in, out, H, I);
     else if (format == MOE_FMT_Q3K_Q4K) q3k_mix_walk<true>(in, out, H, I);
     else if (format == MOE_FMT_Q5K) q5k_walk<true>(in, out, H, I);
+    else if (format == MOE_FMT_Q6K) q6k_walk<true>(in, out, H, I);
     else q8_walk<true>(in, out, H, I);
     return MOE_OK;
 }
@@ -660,6 +730,7 @@ moe_status moe_unpack_expert(int format, const void* packed, void* canonical, in
     else if (format == MOE_FMT_MXFP4) mx4_walk<false>(in, out, H, I);
     else if (format == MOE_FMT_Q3K_Q4K) q3k_mix_walk<false>(in, out, H, I);
     else if (format == MOE_FMT_Q5K) q5k_walk<false>(in, out, H, I);
+    else if (format == MOE_FMT_Q6K) q6k_walk<false>(in, out, H, I);
     else q8_walk<false>(in, out, H, I);
     return MOE_OK;
 }
@@ -726,6 +797,14 @@ moe_status moe_expert_ffn_q5k(const void* slot_pool, size_t slot_stride, int S, 
                               const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype,
                               int path, void* ws, size_t ws_bytes, void* stream) {
     return ffn_common(MOE_FMT_Q5K, slot_pool, slot_stride, S, H, I, x, x_dtype, T, k, slot_offsets, active_slots,
+                      num_active, perm_pair, y_pairs, y_dtype, path, ws, ws_bytes, stream);
+}
+
+moe_status moe_expert_ffn_q6k(const void* slot_pool, size_t slot_stride, int S, int H, int I, const void* x,
+                              int x_dtype, int T, int k, const int32_t* slot_offsets, const int32_t* active_slots,
+                              const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype,
+                              int path, void* ws, size_t ws_bytes, void* stream) {
+    return ffn_common(MOE_FMT_Q6K, slot_pool, slot_stride, S, H, I, x, x_dtype, T, k, slot_offsets, active_slots,
                       num_active, perm_pair, y_pairs, y_dtype, path, ws, ws_bytes, stream);
 }
 

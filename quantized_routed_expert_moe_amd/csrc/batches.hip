@@ -394,33 +394,33 @@ hipError_t launch_batches(const int32_t* ids, const float* w, int T, int k, int 
     int nbits = 1;
     while ((1 << nbits) <= S) ++nbits;  // buckets 0..S
     const long P = (long)T * k;
-    timer_before(kStageBatches, s);
+    const StageEvents ev = timer_events(kStageBatches);
     if (P <= 64) {
-        hipLaunchKernelGGL(batches_wave_kernel, dim3(1), dim3(64), (size_t)(S + 1) * sizeof(int), s, ids, w, T, k, E,
-                           soe, S, nbits, offsets, active, num_active, perm, host_token, host_expert, host_weight,
-                           host_count);
+        launch_timed(batches_wave_kernel, dim3(1), dim3(64), (size_t)(S + 1) * sizeof(int), s, ev.start, ev.stop, ids,
+                     w, T, k, E, soe, S, nbits, offsets, active, num_active, perm, host_token, host_expert,
+                     host_weight, host_count);
     } else if (P <= kSingleMaxPairs) {
         const size_t lds = (size_t)(kBatchWaves + 1) * (S + 1) * sizeof(int);
-        hipLaunchKernelGGL(batches_kernel, dim3(1), dim3(64 * kBatchWaves), lds, s, ids, w, T, k, E, soe, S, nbits,
-                           offsets, active, num_active, perm, host_token, host_expert, host_weight, host_count);
+        launch_timed(batches_kernel, dim3(1), dim3(64 * kBatchWaves), lds, s, ev.start, ev.stop, ids, w, T, k, E, soe,
+                     S, nbits, offsets, active, num_active, perm, host_token, host_expert, host_weight, host_count);
     } else {
         const int nblk = (int)((P + kBlockPairs - 1) / kBlockPairs);
         int32_t* gcnt = static_cast<int32_t*>(ws);
         const size_t lds = (size_t)kMbWaves * (S + 1) * sizeof(int);
-        hipLaunchKernelGGL(batches_count_kernel, dim3(nblk), dim3(256), lds, s, ids, soe, (int)P, E, S, nbits, gcnt);
+        launch_timed(batches_count_kernel, dim3(nblk), dim3(256), lds, s, ev.start, nullptr, ids, soe, (int)P, E, S,
+                     nbits, gcnt);
         if (nblk <= kScanInScatterBlocks) {
             const size_t lds2 = (size_t)(kMbWaves + 2) * (S + 1) * sizeof(int);
-            hipLaunchKernelGGL(batches_scan_scatter_kernel, dim3(nblk), dim3(256), lds2, s, ids, w, T, k, E, soe, S,
-                               nbits, nblk, (const int32_t*)gcnt, offsets, active, num_active, perm, host_token,
-                               host_expert, host_weight, host_count);
+            launch_timed(batches_scan_scatter_kernel, dim3(nblk), dim3(256), lds2, s, nullptr, ev.stop, ids, w, T, k,
+                         E, soe, S, nbits, nblk, (const int32_t*)gcnt, offsets, active, num_active, perm, host_token,
+                         host_expert, host_weight, host_count);
         } else {
             hipLaunchKernelGGL(batches_scan_kernel, dim3(1), dim3(1024), 0, s, nblk, S, gcnt, offsets, active,
                                num_active, host_count);
-            hipLaunchKernelGGL(batches_scatter_kernel, dim3(nblk), dim3(256), lds, s, ids, w, T, k, E, soe, S, nbits,
-                               (const int32_t*)gcnt, perm, host_token, host_expert, host_weight);
+            launch_timed(batches_scatter_kernel, dim3(nblk), dim3(256), lds, s, nullptr, ev.stop, ids, w, T, k, E, soe,
+                         S, nbits, (const int32_t*)gcnt, perm, host_token, host_expert, host_weight);
         }
     }
-    timer_after(kStageBatches, s);
     return hipGetLastError();
 }
 

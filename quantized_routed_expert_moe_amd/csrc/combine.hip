@@ -93,10 +93,9 @@ hipError_t launch_combine(const void* y_pairs, int yp_dtype, const int32_t* ids,
                           hipStream_t s) {
     if (T == 0) return hipSuccess;
     dim3 grid((H / 8 + 255) / 256, T);
-    timer_before(kStageCombine, s);
-    hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, y_pairs, yp_dtype, ids, w, soe, E, y_shared, T, k, H, y,
-                       y_dtype);
-    timer_after(kStageCombine, s);
+    const StageEvents ev = timer_events(kStageCombine);
+    launch_timed(combine_kernel, grid, dim3(256), 0, s, ev.start, ev.stop, y_pairs, yp_dtype, ids, w, soe, E, y_shared,
+                 T, k, H, y, y_dtype);
     return hipGetLastError();
 }
 

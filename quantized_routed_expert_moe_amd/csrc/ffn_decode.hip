@@ -27,6 +27,10 @@
 //     and-or operations build an fp16 pair 1024 + v (v = q + 4, or 16v for
 //     the words whose records hold x/16), again in the Q4_K element order;
 //     their 16-element sub-blocks take per-half constants from the records.
+//   * Q5_K and Q6_K add one or two high bits per element to the Q4_K
+//     nibbles with a second and-or per fp16 pair; Q6_K's 16-element
+//     sub-blocks take per-half constants as Q3_K's do (in the h records
+//     too, since its down matrix is Q6_K as well).
 //   * Activations (token rows, and the intermediate h) are 64-byte records per
 //     32 elements, laid out in the order the nibble/byte extraction produces.
 //     Each wave puts the records of its K range for the tokens of the current
@@ -128,6 +132,39 @@ __device__ __forceinline__ float q5k_dot(const uint4 q, uint32_t hb, cu32* X, co
         }
     }
     return acc;
+}
+
+// Q6_K: the Q4_K nibbles plus two high bits per element, H0 holding those of
+// elements 0-15 and H1 those of 16-31, element 8d + n's at bits 4n + 2 (d %
+// 2).  Shifted left by 4 - 2 (d % 2) a group's pairs land on bits 4-5 (and
+// 20-21) of pairs 0 and bits 8-9 (24-25) of pairs 1, shifted right by
+// 4 + 2 (d % 2) on those of pairs 2 and 3: bits 4-5 of q, or 8-9 of 16 q
+// (16 q <= 1008 still fits under the exponent of 1024).  Returns the dot
+// products over the two 16-element sub-blocks of (1024 + q) with the
+// record's stored values.
+template <bool AO>
+__device__ __forceinline__ float2 q6k_dot(const uint4 q, uint32_t h0, uint32_t h1, cu32* X, const AndOr& k) {
+    const uint32_t w[4] = {q.x, q.z, q.y, q.w};
+    float acc[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t hw = d < 2 ? h0 : h1;
+        const int s = 2 * (d & 1);
+        const uint32_t w8 = w[d] >> 8, hl = hw << (4 - s), hr = hw >> (4 + s);
+        float& a = acc[d >> 1];
+        if (AO) {
+            a = fdot2u(and_or(hl, k.m2, and_or(w[d], k.m0, k.magic)), X[4 * d + 0], a);
+            a = fdot2u(and_or(hl, k.m3, and_or(w[d], k.m1, k.magic)), X[4 * d + 1], a);
+            a = fdot2u(and_or(hr, k.m2, and_or(w8, k.m0, k.magic)), X[4 * d + 2], a);
+            a = fdot2u(and_or(hr, k.m3, and_or(w8, k.m1, k.magic)), X[4 * d + 3], a);
+        } else {
+            a = fdot2u((hl & 0x00300030u) | (w[d] & 0x000F000Fu) | kMagic, X[4 * d + 0], a);
+            a = fdot2u((hl & 0x03000300u) | (w[d] & 0x00F000F0u) | kMagic, X[4 * d + 1], a);
+            a = fdot2u((hr & 0x00300030u) | (w8 & 0x000F000Fu) | kMagic, X[4 * d + 2], a);
+            a = fdot2u((hr & 0x03000300u) | (w8 & 0x00F000F0u) | kMagic, X[4 * d + 3], a);
+        }
+    }
+    return make_float2(acc[0], acc[1]);
 }
 
 // Q8_0: 32 offset bytes (u = q + 128; elements 0-15 in a, 16-31 in b)
@@ -258,10 +295,19 @@ template <int NMAT> struct UnitRegs<3, NMAT> {
     uint4 L[4][NMAT];
     uint4 Hb[2][NMAT];
 };
+// Q6_K: the Q4_K nibbles and, per pair of blocks, their (H0, H1) words.
+template <int NMAT> struct UnitRegs<5, NMAT> {
+    uint4 q[8][NMAT];
+    uint4 hb[4][NMAT];
+};
 
 template <int FMT, int NMAT>
 __device__ __forceinline__ constexpr int tile_bytes() {
-    return FMT == 1 ? NMAT * 9216 : FMT == 3 ? NMAT * 7168 : FMT == 4 ? NMAT * 11264 : NMAT * 8704;
+    return FMT == 1   ? NMAT * 9216
+           : FMT == 3 ? NMAT * 7168
+           : FMT == 4 ? NMAT * 11264
+           : FMT == 5 ? NMAT * 13440
+                      : NMAT * 8704;
 }
 
 // LDS region of one wave: words [kMaxTok][8][16] dwords, then (C, S) [kMaxTok][8][2].
@@ -279,6 +325,12 @@ constexpr int kStageFloats = kMaxTok * 8 * 2;
 // another lane's (same value to the same LDS address), so that no branch on
 // the lane index splits the loop body: a divergent branch there makes the
 // compiler wait for all outstanding loads, the weight prefetch included.
+// Q6_K header: the 16 signed scale bytes and fp16 d (low half of d).
+struct Q6Hdr {
+    uint4 s;
+    uint32_t d;
+};
+
 struct ActRegs {
     uint4 xr[kMaxTok];
     uint2 rw[kMaxTok];
@@ -396,15 +448,15 @@ __device__ __forceinline__ void act_store(const ActRegs& a, int x_dtype, int lan
                 const float s16 = (FMT == 1 || FMT == 4) ? sum8_lanes(half_to_float(b0) + half_to_float(b1) +
                                                                       half_to_float(b2) + half_to_float(b3))
                                                            : 0.0f;
-                const float sx = FMT == 3 ? 0.0f : sum8_lanes(v[0] + v[1] + v[2] + v[3]);
-                if (FMT == 3) {
-                    // Q3_K: per 16-element half (a quad of lanes), K = 1024 * sum of
-                    // the stored values + 4 * sum x (the magic number and the
-                    // offset of v = q + 4)
+                const float sx = (FMT == 3 || FMT == 5) ? 0.0f : sum8_lanes(v[0] + v[1] + v[2] + v[3]);
+                if (FMT == 3 || FMT == 5) {
+                    // Q3_K, Q6_K: per 16-element half (a quad of lanes), K =
+                    // 1024 * sum of the stored values + o * sum x (the magic
+                    // number and the offset o: v = q + 4, or q - 32 = v - 32)
                     const float h16 = quad_sum(half_to_float(b0) + half_to_float(b1) + half_to_float(b2) +
                                                half_to_float(b3));
                     const float hx = quad_sum(v[0] + v[1] + v[2] + v[3]);
-                    lc[(t * RB + jb) * 2 + (sl >> 2)] = fmaf(4.0f, hx, 1024.0f * h16);
+                    lc[(t * RB + jb) * 2 + (sl >> 2)] = fmaf(FMT == 5 ? 32.0f : 4.0f, hx, 1024.0f * h16);
                 } else {
                     // all 8 lanes of the block hold the sums
                     *reinterpret_cast<float2*>(lc + (t * RB + jb) * 2) = make_float2(1024.0f * s16, sx);
@@ -639,9 +691,67 @@ __device__ __forceinline__ void half_dots(const UnitRegs<4, NMAT>& r, const uint
     }
 }
 
+template <int NMAT>
+__device__ __forceinline__ void load_half(__amdgpu_buffer_rsrc_t src, int uoff, int lane, int h,
+                                          UnitRegs<5, NMAT>& r, Q6Hdr* hdr) {
+    if (h == 0) {
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) hdr[m].s = ldb16(src, lane * 16, uoff + m * 1024);
+        if (NMAT == 2) {
+            const uint32_t dd = __builtin_amdgcn_raw_buffer_load_b32(src, lane * 4, uoff + 2 * 13312, 0);
+            hdr[0].d = dd;
+            hdr[NMAT - 1].d = dd >> 16;
+        } else {
+            hdr[0].d = __builtin_amdgcn_raw_buffer_load_b16(src, lane * 2, uoff + 13312, 0);
+        }
+    }
+#pragma unroll
+    for (int j = 4 * h; j < 4 * h + 4; ++j)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) r.q[j][m] = ldb16(src, lane * 16, uoff + NMAT * 1024 + j * NMAT * 1024 + m * 1024);
+#pragma unroll
+    for (int c = 2 * h; c < 2 * h + 2; ++c)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) r.hb[c][m] = ldb16(src, lane * 16, uoff + NMAT * 9216 + c * NMAT * 1024 + m * 1024);
+}
+template <int NT, int NMAT>
+__device__ __forceinline__ void half_dots(const UnitRegs<5, NMAT>& r, const Q6Hdr* hdr, int h, const uint32_t* lw,
+                                          const float* lc, float (*acc)[NMAT]) {
+    float ds[NMAT][8];
+    const AndOr k(0x000F000Fu, 0x00F000F0u, 0x00300030u, 0x03000300u);
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+        // d * sc of sub-blocks 8h..8h+7 (signed scale bytes)
+        const float d = half_to_float(hdr[m].d & 0xFFFFu);
+        const uint32_t s0 = h == 0 ? hdr[m].s.x : hdr[m].s.z, s1 = h == 0 ? hdr[m].s.y : hdr[m].s.w;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            ds[m][b] = d * (float)((int32_t)(s0 << (24 - 8 * b)) >> 24);
+            ds[m][b + 4] = d * (float)((int32_t)(s1 << (24 - 8 * b)) >> 24);
+        }
+    }
+#pragma unroll
+    for (int j = 4 * h; j < 4 * h + 4; ++j) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const uint32_t* X = lw + (t * 8 + j) * 16;
+            const float ka = lc[(t * 8 + j) * 2], kb = lc[(t * 8 + j) * 2 + 1];
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) {
+                const uint4 hv = r.hb[j >> 1][m];
+                const uint32_t h0 = (j & 1) ? hv.z : hv.x, h1 = (j & 1) ? hv.w : hv.y;
+                const float2 dd = q6k_dot<NMAT == 2>(r.q[j][m], h0, h1, X, k);
+                acc[t][m] += ds[m][2 * (j & 3)] * (dd.x - ka) + ds[m][2 * (j & 3) + 1] * (dd.y - kb);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 template <int FMT> struct HdrType { typedef uint4 T; };
 template <> struct HdrType<0> { typedef uint2 T; };
 template <> struct HdrType<2> { typedef uint2 T; };
+template <> struct HdrType<5> { typedef Q6Hdr T; };
 
 // K units [u0, u0 + nu) of this lane's row(s) for NT tokens.  On entry `w`
 // and `hdr0` hold (or are loading) unit u0.  Per unit u: its records go to
@@ -727,6 +837,13 @@ __device__ __forceinline__ void store_h_record(float h, int rg, int lane, uint32
     }
     const uint32_t bits = float_to_half_bits(v);
     reinterpret_cast<uint16_t*>(hw_q + (size_t)blk * 16)[word * 2 + half] = (uint16_t)bits;
+    if (FMT == 5) {
+        // per 16-element half (a row of 16 lanes): K = 1024 * sum of the
+        // stored values + 32 * sum h
+        const float kh = fmaf(32.0f, row16_sum(h), 1024.0f * row16_sum(half_to_float(bits)));
+        if ((e & 15) == 0) reinterpret_cast<float*>(hcs_q + blk)[e >> 4] = kh;
+        return;
+    }
     const float c = half_wave_sum(half_to_float(bits)) * (FMT == 0 ? 1152.0f : 1024.0f);
     const float sx = half_wave_sum(h);
     if (e == 0) hcs_q[blk] = make_float2(c, sx);
@@ -909,8 +1026,8 @@ size_t decode_workspace_bytes(int T, int k, int H, int I) {
 // units.  Then split K across workgroups as well: one unit per wave, as many
 // waves as the unit count allows, kparts workgroups per tile, finished by
 // the reduce kernel (if the partial sums fit).  Also whenever the pipelined
-// kernel of the format would spill (pipe_spills: Q5_K gate/up, whose unit
-// is 160 bytes per row and matrix).
+// kernel of the format would spill (pipe_spills: Q5_K and Q6_K gate/up,
+// whose units are 160 and 208 bytes per row and matrix).
 static int split_k_parts(int units, long tiles_total, int P, int* nw, int* upw, bool pipe_spills = false) {
     if (*upw <= 1 || (tiles_total * *nw >= 2048 && !pipe_spills)) return 1;
     const int nw1 = std::min(kMaxWaves, units);
@@ -961,21 +1078,17 @@ struct GemvLaunch {
 // The pipelined kernel when a wave has more than one K unit; with a K split
 // across workgroups (grid.z parts) the reduce kernel follows.
 template <int FMT, int NMAT>
-static void launch_gemv(const GemvLaunch& g, dim3 grid, dim3 block, hipStream_t s) {
+static void launch_gemv(const GemvLaunch& g, dim3 grid, dim3 block, hipStream_t s, StageEvents ev) {
     float* part = g.kparts > 1 ? g.part : nullptr;
     grid.z = g.kparts;
-    if (g.units_per_wave > 1)
-        hipLaunchKernelGGL((gemv_kernel<FMT, NMAT, true>), grid, block, 0, s, g.pool, g.stride, g.S, g.K, g.rows,
-                           g.section, g.x, g.x_dtype, g.rw, g.rcs, g.T, g.k, g.offsets, g.active, g.num_active, g.perm,
-                           g.hw, g.hcs, g.y_pairs, g.units_per_wave, part);
-    else
-        hipLaunchKernelGGL((gemv_kernel<FMT, NMAT, false>), grid, block, 0, s, g.pool, g.stride, g.S, g.K, g.rows,
-                           g.section, g.x, g.x_dtype, g.rw, g.rcs, g.T, g.k, g.offsets, g.active, g.num_active, g.perm,
-                           g.hw, g.hcs, g.y_pairs, g.units_per_wave, part);
+    hipEvent_t stop = part ? nullptr : ev.stop;
+    launch_timed(g.units_per_wave > 1 ? gemv_kernel<FMT, NMAT, true> : gemv_kernel<FMT, NMAT, false>, grid, block, 0,
+                 s, ev.start, stop, g.pool, g.stride, g.S, g.K, g.rows, g.section, g.x, g.x_dtype, g.rw, g.rcs, g.T,
+                 g.k, g.offsets, g.active, g.num_active, g.perm, g.hw, g.hcs, g.y_pairs, g.units_per_wave, part);
     if (part) {
         const int P = g.T * g.k;
-        hipLaunchKernelGGL((gemv_reduce_kernel<FMT, NMAT>), dim3(g.rows / 64, P), dim3(64), 0, s, part, g.kparts, P,
-                           g.rows, g.offsets + g.S, g.perm, g.hw, g.hcs, g.y_pairs);
+        launch_timed(gemv_reduce_kernel<FMT, NMAT>, dim3(g.rows / 64, P), dim3(64), 0, s, nullptr, ev.stop, part,
+                     g.kparts, P, g.rows, g.offsets + g.S, g.perm, g.hw, g.hcs, g.y_pairs);
     }
 }
 
@@ -996,23 +1109,24 @@ hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s) {
         const int units = fgu == 0 ? a.H / 128 : a.H / 256;
         int nw, upw;
         split_k(units, (long)(a.I / 64) * max_active, &nw, &upw);
-        const int kparts = split_k_parts(units, (long)(a.I / 64) * max_active, (int)P, &nw, &upw, fgu == 4);
+        const int kparts = split_k_parts(units, (long)(a.I / 64) * max_active, (int)P, &nw, &upw, fgu == 4 || fgu == 5);
         const dim3 grid(a.I / 64, max_active), block(64 * nw);
-        timer_before(kStageGateUp, s);
+        const StageEvents ev = timer_events(kStageGateUp);
         const GemvLaunch g{a.pool, a.stride, a.S, a.H, a.I, 0, a.x, a.x_dtype, nullptr, nullptr, a.T, a.k,
                            a.slot_offsets, a.active_slots, a.num_active, a.perm_pair, hw, hcs, nullptr, upw,
                            kparts, part};
         if (fgu == 1)
-            launch_gemv<1, 2>(g, grid, block, s);
+            launch_gemv<1, 2>(g, grid, block, s, ev);
         else if (fgu == 2)
-            launch_gemv<2, 2>(g, grid, block, s);
+            launch_gemv<2, 2>(g, grid, block, s, ev);
         else if (fgu == 3)
-            launch_gemv<3, 2>(g, grid, block, s);
+            launch_gemv<3, 2>(g, grid, block, s, ev);
         else if (fgu == 4)
-            launch_gemv<4, 2>(g, grid, block, s);
+            launch_gemv<4, 2>(g, grid, block, s, ev);
+        else if (fgu == 5)
+            launch_gemv<5, 2>(g, grid, block, s, ev);
         else
-            launch_gemv<0, 2>(g, grid, block, s);
-        timer_after(kStageGateUp, s);
+            launch_gemv<0, 2>(g, grid, block, s, ev);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1027,20 +1141,22 @@ hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s) {
                                : a.format == 2 ? mx4_gateup_bytes(a.H, a.I)
                                : a.format == 3 ? q3k_gateup_bytes(a.H, a.I)
                                : a.format == 4 ? q5k_gateup_bytes(a.H, a.I)
+                               : a.format == 5 ? q6k_gateup_bytes(a.H, a.I)
                                                : q8_gateup_bytes(a.H, a.I);
-        timer_before(kStageDown, s);
+        const StageEvents ev = timer_events(kStageDown);
         const GemvLaunch g{a.pool, a.stride, a.S, a.I, a.H, section, nullptr, 0, hw, hcs, a.T, a.k,
                            a.slot_offsets, a.active_slots, a.num_active, a.perm_pair, nullptr, nullptr,
                            static_cast<float*>(a.y_pairs), upw, kparts, part};
         if (fdn == 1)
-            launch_gemv<1, 1>(g, grid, block, s);
+            launch_gemv<1, 1>(g, grid, block, s, ev);
         else if (fdn == 2)
-            launch_gemv<2, 1>(g, grid, block, s);
+            launch_gemv<2, 1>(g, grid, block, s, ev);
         else if (fdn == 4)
-            launch_gemv<4, 1>(g, grid, block, s);
+            launch_gemv<4, 1>(g, grid, block, s, ev);
+        else if (fdn == 5)
+            launch_gemv<5, 1>(g, grid, block, s, ev);
         else
-            launch_gemv<0, 1>(g, grid, block, s);
-        timer_after(kStageDown, s);
+            launch_gemv<0, 1>(g, grid, block, s, ev);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -776,30 +776,27 @@ hipError_t launch_ffn_prefill(const FfnArgs& a, hipStream_t s) {
     off += align256((size_t)max_tiles(P, kMaxExpertsInternal) * 16);
     int32_t* ntiles = reinterpret_cast<int32_t*>(ws + off);
 
-    timer_before(kStagePrefillTiles, s);
-    hipLaunchKernelGGL(prefill_tiles_kernel, dim3(1), dim3(1024), 0, s, a.slot_offsets, a.active_slots, a.num_active,
-                       a.S, P, tiles, ntiles);
-    timer_after(kStagePrefillTiles, s);
+    const StageEvents ev_t = timer_events(kStagePrefillTiles);
+    launch_timed(prefill_tiles_kernel, dim3(1), dim3(1024), 0, s, ev_t.start, ev_t.stop, a.slot_offsets,
+                 a.active_slots, a.num_active, a.S, P, tiles, ntiles);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
     // Grid: 8 XCD lanes x (N tiles x ceil(M tiles / 8)).
     const int mgroups = (mt + 7) / 8;
     const int nt_gu = a.I / kGateUpFeatures, nt_dn = a.H / kDownColumns;
-    timer_before(kStagePrefillGateUp, s);
     auto gateup = a.format == 2 ? prefill_gemm_kernel<2, true> : prefill_gemm_kernel<1, true>;
     auto down = a.format == 2 ? prefill_gemm_kernel<2, false> : prefill_gemm_kernel<1, false>;
-    hipLaunchKernelGGL(gateup, dim3(8 * nt_gu * mgroups), dim3(kThreads), 0, s, a.pool, a.stride, a.S, a.H, a.I,
-                       static_cast<const uint16_t*>(a.x), a.T, a.k, a.perm_pair, tiles, ntiles, static_cast<void*>(h),
-                       0);
-    timer_after(kStagePrefillGateUp, s);
+    const StageEvents ev_g = timer_events(kStagePrefillGateUp);
+    launch_timed(gateup, dim3(8 * nt_gu * mgroups), dim3(kThreads), 0, s, ev_g.start, ev_g.stop, a.pool, a.stride, a.S,
+                 a.H, a.I, static_cast<const uint16_t*>(a.x), a.T, a.k, a.perm_pair, tiles, ntiles,
+                 static_cast<void*>(h), 0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 
-    timer_before(kStagePrefillDown, s);
-    hipLaunchKernelGGL(down, dim3(8 * nt_dn * mgroups), dim3(kThreads), 0, s, a.pool, a.stride, a.S, a.H, a.I,
-                       (const uint16_t*)h, a.T, a.k, a.perm_pair, tiles, ntiles, a.y_pairs, a.y_dtype);
-    timer_after(kStagePrefillDown, s);
+    const StageEvents ev_d = timer_events(kStagePrefillDown);
+    launch_timed(down, dim3(8 * nt_dn * mgroups), dim3(kThreads), 0, s, ev_d.start, ev_d.stop, a.pool, a.stride, a.S,
+                 a.H, a.I, (const uint16_t*)h, a.T, a.k, a.perm_pair, tiles, ntiles, a.y_pairs, a.y_dtype);
     return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 // Internal declarations of the qmoe HIP library: packed-blob layout,
 // kernel launchers and the stage timers.  Not part of the C ABI.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -88,6 +89,20 @@ namespace qmoe {
 // gate/up tile 22528 bytes, down tile 11264 bytes (the stored 176 bytes per
 // row and 256 inputs).
 
+//
+// Packed Q6_K blob (H, I multiples of 256): tiles of 64 rows x 256 inputs,
+// NMAT matrices interleaved (2 for gate/up, 1 for down):
+//     [0, NMAT KB)                  signed scales: row r at 16r, the 16 bytes as stored
+//     [NMAT KB + j NMAT KB + m KB)  low nibbles of block j, the Q4_K order
+//     [9 NMAT KB + c NMAT KB + m KB)   high bits of blocks 2c, 2c+1 (c < 4):
+//                       row r at 16r: (H0, H1) of block 2c, then of 2c+1;
+//                       H0 holds elements 0-15 (groups d = 0, 1), H1
+//                       elements 16-31 (d = 2, 3), element 8d + n's two
+//                       high bits at bits 4n + 2 (d % 2)
+//     [13 NMAT KB, + NMAT 128)      fp16 d: row r at 2 NMAT r + 2m
+// gate/up tile 26880 bytes, down tile 13440 bytes (the stored 210 bytes per
+// row and 256 inputs).
+
 constexpr int kMaxExpertsInternal = 1024;  // equals MOE_MAX_EXPERTS of the C ABI
 
 constexpr int kQ4kGateUpTile = 18432;
@@ -103,6 +118,9 @@ __host__ __device__ inline size_t mx4_gateup_bytes(int H, int I) { return (size_
 constexpr int kQ5kGateUpTile = 22528;
 constexpr int kQ5kDownTile = 11264;
 __host__ __device__ inline size_t q5k_gateup_bytes(int H, int I) { return (size_t)(I / 64) * (H / 256) * kQ5kGateUpTile; }
+constexpr int kQ6kGateUpTile = 26880;
+constexpr int kQ6kDownTile = 13440;
+__host__ __device__ inline size_t q6k_gateup_bytes(int H, int I) { return (size_t)(I / 64) * (H / 256) * kQ6kGateUpTile; }
 constexpr int kQ3kGateUpTile = 14336;
 __host__ __device__ inline size_t q3k_gateup_bytes(int H, int I) { return (size_t)(I / 64) * (H / 256) * kQ3kGateUpTile; }
 
@@ -126,9 +144,25 @@ enum Stage {
     kStageCount = 9
 };
 
-// Record the start / stop event of a launch of `stage` if its timer is armed.
-void timer_before(int stage, hipStream_t s);
-void timer_after(int stage, hipStream_t s);
+// The events of one timed launch of `stage`: the next slot of its timer when
+// armed, else two null events.  The stage's first kernel carries `start` and
+// its last `stop` (launch_timed), so the events take those dispatches' own
+// begin and end timestamps: the elapsed time runs from the first kernel's
+// start to the last one's end, as a kernel trace measures it, without the
+// gap an event recorded between launches adds.
+struct StageEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+StageEvents timer_events(int stage);
+
+template <typename... Params, typename... Args>
+inline void launch_timed(void (*kernel)(Params...), dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                         hipEvent_t start, hipEvent_t stop, Args... args) {
+    if (start || stop)
+        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, start, stop, 0u, static_cast<Params>(args)...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+}
 
 // --------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.  Arguments are checked by the

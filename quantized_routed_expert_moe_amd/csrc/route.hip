@@ -140,19 +140,19 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int score
                              int32_t* ids, float* w, hipStream_t s) {
     if (T == 0) return hipSuccess;
     dim3 grid((T + 3) / 4), block(256);
-    timer_before(kStageRoute, s);
+    const StageEvents ev = timer_events(kStageRoute);
     if (E <= 128)
-        hipLaunchKernelGGL(route_rank_kernel<128>, dim3(T), dim3(256), 0, s, logits, T, E, k, score, renormalize, scale,
-                           ids, w);
+        launch_timed(route_rank_kernel<128>, dim3(T), dim3(256), 0, s, ev.start, ev.stop, logits, T, E, k, score,
+                     renormalize, scale, ids, w);
     else if (E <= 256)
-        hipLaunchKernelGGL(route_rank_kernel<256>, dim3(T), dim3(256), 0, s, logits, T, E, k, score, renormalize, scale,
-                           ids, w);
+        launch_timed(route_rank_kernel<256>, dim3(T), dim3(256), 0, s, ev.start, ev.stop, logits, T, E, k, score,
+                     renormalize, scale, ids, w);
     else if (E <= 512)
-        hipLaunchKernelGGL(route_topk_kernel<8>, grid, block, 0, s, logits, T, E, k, score, renormalize, scale, ids, w);
+        launch_timed(route_topk_kernel<8>, grid, block, 0, s, ev.start, ev.stop, logits, T, E, k, score, renormalize,
+                     scale, ids, w);
     else
-        hipLaunchKernelGGL(route_topk_kernel<16>, grid, block, 0, s, logits, T, E, k, score, renormalize, scale, ids,
-                           w);
-    timer_after(kStageRoute, s);
+        launch_timed(route_topk_kernel<16>, grid, block, 0, s, ev.start, ev.stop, logits, T, E, k, score, renormalize,
+                     scale, ids, w);
     return hipGetLastError();
 }
 

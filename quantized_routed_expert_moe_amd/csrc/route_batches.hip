@@ -70,16 +70,15 @@ hipError_t launch_route_batches(const float* logits, int T, int E, int k, int sc
     }
     int nbits = 1;
     while ((1 << nbits) <= S) ++nbits;  // buckets 0..S
-    timer_before(kStageRouteBatches, s);
+    const StageEvents ev = timer_events(kStageRouteBatches);
     if (E <= 128)
-        hipLaunchKernelGGL(route_batches_kernel<128>, dim3(1), dim3(256 * T), 0, s, logits, T, E, k, score, renormalize,
-                           scale, ids, w, soe, S, nbits, offsets, active, num_active, perm, host_token, host_expert,
-                           host_weight, host_count, route_counts);
+        launch_timed(route_batches_kernel<128>, dim3(1), dim3(256 * T), 0, s, ev.start, ev.stop, logits, T, E, k,
+                     score, renormalize, scale, ids, w, soe, S, nbits, offsets, active, num_active, perm, host_token,
+                     host_expert, host_weight, host_count, route_counts);
     else
-        hipLaunchKernelGGL(route_batches_kernel<256>, dim3(1), dim3(256 * T), 0, s, logits, T, E, k, score, renormalize,
-                           scale, ids, w, soe, S, nbits, offsets, active, num_active, perm, host_token, host_expert,
-                           host_weight, host_count, route_counts);
-    timer_after(kStageRouteBatches, s);
+        launch_timed(route_batches_kernel<256>, dim3(1), dim3(256 * T), 0, s, ev.start, ev.stop, logits, T, E, k,
+                     score, renormalize, scale, ids, w, soe, S, nbits, offsets, active, num_active, perm, host_token,
+                     host_expert, host_weight, host_count, route_counts);
     return hipGetLastError();
 }
 

@@ -72,6 +72,7 @@ constexpr int kQ8Block = 32, kQ8Bytes = 34;
 constexpr int kMx4Block = 32, kMx4Bytes = 17;
 constexpr int kQ3kBlock = 256, kQ3kBytes = 110;
 constexpr int kQ5kBytes = 176;
+constexpr int kQ6kBytes = 210;
 constexpr int kRowQ3k = 100;  // block type of a Q3_K matrix (the mixed expert's gate and up)
 
 size_t row_bytes(int type, int n) {
@@ -79,6 +80,7 @@ size_t row_bytes(int type, int n) {
     if (type == MOE_FMT_MXFP4) return (size_t)(n / kMx4Block) * kMx4Bytes;
     if (type == kRowQ3k) return (size_t)(n / kQ3kBlock) * kQ3kBytes;
     if (type == MOE_FMT_Q5K) return (size_t)(n / kQ4kBlock) * kQ5kBytes;
+    if (type == MOE_FMT_Q6K) return (size_t)(n / kQ4kBlock) * kQ6kBytes;
     return (size_t)(n / kQ8Block) * kQ8Bytes;
 }
 
@@ -173,6 +175,40 @@ void dequant_row_mxfp4(const uint8_t* row, int n, float* out) {
             const __m256 m = _mm256_permutevar8x32_ps(mag, _mm256_and_si256(c, seven));
             const __m256 sign = _mm256_castsi256_ps(_mm256_slli_epi32(_mm256_and_si256(c, eight), 28));
             _mm256_storeu_ps(out + 8 * k, _mm256_mul_ps(_mm256_xor_ps(m, sign), scale));
+        }
+    }
+}
+
+// One Q6_K row of n weights (n / 256 super-blocks of 210 bytes: 128 bytes of
+// low nibbles, 64 bytes of high bit pairs, 16 signed scales, fp16 d; element
+// 128h + 32g + l has its low four bits in byte 64h + l + 32 (g % 2), low
+// nibble for g < 2, and its high two bits at bits 2g of byte 128 + 32h + l)
+// -> n floats d sc_j (q - 32) = q (d sc_j) - 32 d sc_j, one fused
+// multiply-subtract each (d sc_j is exact in fp32).
+__attribute__((target("avx2,fma")))
+void dequant_row_q6k(const uint8_t* row, int n, float* out) {
+    const __m256i low4 = _mm256_set1_epi8(0x0F), three = _mm256_set1_epi8(3);
+    for (int sb = 0; sb < n / kQ4kBlock; ++sb, row += kQ6kBytes, out += kQ4kBlock) {
+        const float d = half_bits_to_float(load_u16(row + 208));
+        const int8_t* sc = reinterpret_cast<const int8_t*>(row + 192);
+        for (int h = 0; h < 2; ++h) {
+            const __m256i hbytes = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(row + 128 + 32 * h));
+            for (int g = 0; g < 4; ++g) {
+                const __m256i v = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(row + 64 * h + 32 * (g % 2)));
+                const __m256i nib = g < 2 ? _mm256_and_si256(v, low4) : _mm256_and_si256(_mm256_srli_epi16(v, 4), low4);
+                const __m256i hb = _mm256_and_si256(_mm256_srli_epi16(hbytes, 2 * g), three);
+                const __m256i qv = _mm256_or_si256(nib, _mm256_slli_epi16(hb, 4));
+                const int j = 8 * h + 2 * g;  // sub-blocks j (elements 0-15) and j + 1 (16-31)
+                const float s0 = d * (float)sc[j], s1 = d * (float)sc[j + 1];
+                const __m128i lo8 = _mm256_castsi256_si128(qv), hi8 = _mm256_extracti128_si256(qv, 1);
+                const __m256 a0 = _mm256_set1_ps(s0), a1 = _mm256_set1_ps(s1);
+                const __m256 o0 = _mm256_set1_ps(32.0f * s0), o1 = _mm256_set1_ps(32.0f * s1);
+                float* o = out + 128 * h + 32 * g;
+                _mm256_storeu_ps(o, _mm256_fmsub_ps(_mm256_cvtepi32_ps(_mm256_cvtepu8_epi32(lo8)), a0, o0));
+                _mm256_storeu_ps(o + 8, _mm256_fmsub_ps(_mm256_cvtepi32_ps(_mm256_cvtepu8_epi32(_mm_srli_si128(lo8, 8))), a0, o0));
+                _mm256_storeu_ps(o + 16, _mm256_fmsub_ps(_mm256_cvtepi32_ps(_mm256_cvtepu8_epi32(hi8)), a1, o1));
+                _mm256_storeu_ps(o + 24, _mm256_fmsub_ps(_mm256_cvtepi32_ps(_mm256_cvtepu8_epi32(_mm_srli_si128(hi8, 8))), a1, o1));
+            }
         }
     }
 }
@@ -300,6 +336,7 @@ void run(int format, const uint8_t* const* expert_blob, int H, int I, const floa
              : type == MOE_FMT_MXFP4 ? dequant_row_mxfp4
              : type == kRowQ3k ? dequant_row_q3k
              : type == MOE_FMT_Q5K ? dequant_row_q5k
+             : type == MOE_FMT_Q6K ? dequant_row_q6k
                                : dequant_row_q8_0;
     };
     auto dequant = pick(tgu);
@@ -360,8 +397,9 @@ const char* moe_host_last_error(void) { return g_error.c_str(); }
 int moe_host_leg(int format, const uint8_t* const* expert_blob, int E, int H, int I, const float* x, int T,
                  const int32_t* host_token, const int32_t* host_expert, const float* host_weight, int count,
                  float* y_host, int threads) {
-    if (format < MOE_FMT_Q8_0 || format > MOE_FMT_Q5K) return fail(MOE_ERR_UNSUPPORTED, "bad format %d", format);
-    const int blk = (format == MOE_FMT_Q4K || format == MOE_FMT_Q3K_Q4K || format == MOE_FMT_Q5K) ? kQ4kBlock
+    if (format < MOE_FMT_Q8_0 || format > MOE_FMT_Q6K) return fail(MOE_ERR_UNSUPPORTED, "bad format %d", format);
+    const int blk = (format == MOE_FMT_Q4K || format == MOE_FMT_Q3K_Q4K || format == MOE_FMT_Q5K ||
+                     format == MOE_FMT_Q6K) ? kQ4kBlock
                     : format == MOE_FMT_MXFP4                           ? kMx4Block
                                                                         : kQ8Block;
     if (H <= 0 || I <= 0 || H % blk || I % blk)

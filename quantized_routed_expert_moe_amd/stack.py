@@ -104,7 +104,8 @@ class ResidentStack:
             self.x.append(torch.zeros((T, spec.H), dtype=torch.float32, device=dev))
         self.pin_maps = [torch.zeros(E, dtype=torch.int32).pin_memory() for _ in range(n_layers)]
         self.graph = None
-        self.side = torch.cuda.Stream()
+        self.side = torch.cuda.Stream()  # swap copies; capture() may replace it (_pick_copy_stream)
+        self.side_probes, self.side_overlaps = 0, None
         self.replay_done = torch.cuda.Event(enable_timing=True)
         self.replay_start = torch.cuda.Event(enable_timing=True)
         self.swap_start = torch.cuda.Event(enable_timing=True)
@@ -162,7 +163,41 @@ class ResidentStack:
             self._step_body()
         g.instantiate()
         self.graph = g
+        self._pick_copy_stream()
         return g
+
+    def _pick_copy_stream(self, tries: int = 8, n_copies: int = 40) -> None:
+        """Choose the swap-copy stream that the replays do not queue behind.
+        Streams share the process's few hardware queues, and a replay's
+        kernels, forked branches included, queued on the copy stream's queue
+        would wait for a whole round of copies.  Which queue a stream sits on
+        is not visible, so candidates from torch's stream pool are tried with
+        the captured graph itself: about 1 GB of expert blobs is copied into
+        one free slot on the candidate while the graph replays on the current
+        stream, and the candidate is kept if the replay ends while the copies
+        still run.  Free slots hold nothing a replay reads, and the replay only
+        repeats the step of the current inputs."""
+        if self.swap_in_flight or not self.free[0]:
+            return
+        cand = self.side
+        slot = self.pools[0][self.free[0][0]]
+        srcs = [self.host_blobs[b % self.host_blobs.shape[0]] for b in range(n_copies)]
+        copied = torch.cuda.Event()
+        for n in range(1, tries + 1):
+            torch.cuda.synchronize()
+            with torch.cuda.stream(cand):
+                for src in srcs:
+                    slot.copy_(src, non_blocking=True)
+                copied.record(cand)
+            self.replay()
+            self.replay_done.synchronize()
+            overlapped = not copied.query()
+            copied.synchronize()
+            self.side_probes, self.side_overlaps = n, overlapped
+            if overlapped:
+                self.side = cand
+                return
+            cand = torch.cuda.Stream()
 
     def graph_node_count(self) -> int:
         import ctypes

@@ -161,7 +161,8 @@ def test_workspace_sizes_are_monotone():
                                      (Q.MOE_FMT_Q8_0, 384, 256), (Q.MOE_FMT_MXFP4, 512, 256),
                                      (Q.MOE_FMT_MXFP4, 768, 512), (Q.MOE_FMT_Q3K_Q4K, 512, 256),
                                      (Q.MOE_FMT_Q3K_Q4K, 768, 512), (Q.MOE_FMT_Q5K, 512, 256),
-                                     (Q.MOE_FMT_Q5K, 768, 512)])
+                                     (Q.MOE_FMT_Q5K, 768, 512), (Q.MOE_FMT_Q6K, 512, 256),
+                                     (Q.MOE_FMT_Q6K, 768, 512)])
 def test_pack_round_trip(fmt, H, I):
     blob = F.expert_blob(fmt, 5, 0, 1, H, I)
     packed = Q.moe_pack_expert(fmt, blob, H, I)
@@ -266,6 +267,42 @@ def test_pack_places_q5k_fields():
                 high = (canon[16 + e] >> j) & 1
                 assert (int(words[[0, 2, 1, 3][e // 8]]) >> (4 * (e % 8))) & 15 == low
                 assert (int(hw) >> (4 * (e % 8) + e // 8)) & 1 == high
+
+
+def test_pack_places_q6k_fields():
+    """Row r of W_up (gate/up tiles, matrix 1) and row r of W_down (down tiles, one matrix), super-block u:
+    the 16 scale bytes at m KB + 16 (r % 64) of the tile (matrix m of NMAT); element 8d+n of block j's low nibble in nibble n of
+    group d's dword (groups stored 0, 2, 1, 3); its two high bits at bits 4n + 2 (d % 2) of word d // 2 of the
+    block's (H0, H1) pair; fp16 d at 13 NMAT KB + 2 NMAT (r % 64) + 2m."""
+    H, I = 512, 256
+    blob = F.expert_blob(Q.MOE_FMT_Q6K, 7, 0, 0, H, I)
+    packed = Q.moe_pack_expert(Q.MOE_FMT_Q6K, blob, H, I)
+    rbH, rbI = H // 256 * 210, I // 256 * 210
+    gate_up = (I // 64) * (H // 256) * 26880
+    cases = [(1, 2, I * rbH + r * rbH, H // 256, 0, r) for r in (0, 70, 255)]            # W_up rows
+    cases += [(0, 1, 2 * I * rbH + r * rbI, I // 256, gate_up, r) for r in (1, 200, 511)]  # W_down rows
+    for m, nmat, row0, units, base, r in cases:
+        for u in range(units):
+            canon = blob[row0 + u * 210: row0 + (u + 1) * 210]
+            tile = base + ((r // 64) * units + u) * nmat * 13440
+            lr = r % 64
+            assert np.array_equal(packed[tile + m * 1024 + 16 * lr: tile + m * 1024 + 16 * lr + 16], canon[192:208])
+            dpos = tile + nmat * 13312 + 2 * nmat * lr + 2 * m
+            assert np.array_equal(packed[dpos: dpos + 2], canon[208:210])
+            for j in (0, 3, 5, 7):
+                nib = tile + nmat * 1024 + j * nmat * 1024 + m * 1024 + 16 * lr
+                words = packed[nib: nib + 16].view(np.uint32)
+                hp = tile + nmat * 9216 + (j // 2) * nmat * 1024 + m * 1024 + 16 * lr
+                hw = packed[hp: hp + 16].view(np.uint32)[2 * (j % 2): 2 * (j % 2) + 2]
+                for e in (0, 6, 9, 15, 16, 21, 31):
+                    i = 32 * j + e
+                    h, g, l = i // 128, (i % 128) // 32, i % 32
+                    byte = canon[64 * h + l + 32 * (g % 2)]
+                    low = (byte & 15) if g < 2 else (byte >> 4)
+                    high = (canon[128 + 32 * h + l] >> (2 * g)) & 3
+                    dd, n = e // 8, e % 8
+                    assert (int(words[[0, 2, 1, 3][dd]]) >> (4 * n)) & 15 == low
+                    assert (int(hw[dd // 2]) >> (4 * n + 2 * (dd % 2))) & 3 == high
 
 
 def test_validate_slot_map():

@@ -336,12 +336,14 @@ MXFP4_SMALL = W.Workload("small MXFP4 layer (H256 E8 k2 I256 T4)", F.MXFP4, 256,
 Q3K_SMALL = W.Workload("small Q3_K/Q4_K layer (H512 E8 k2 I256 T4)", F.Q3K_Q4K, 512, 256, 8, 2, 4)
 Q5K_SMALL = W.Workload("small Q5_K layer (H512 E8 k2 I256 T4)", F.Q5K, 512, 256, 8, 2, 4)
 Q5K_QWEN3_T2 = W.Workload("Qwen3-30B-A3B-shaped MoE layer, Q5_K experts, decode T=2", F.Q5K, 2048, 768, 128, 8, 2)
+Q6K_SMALL = W.Workload("small Q6_K layer (H512 E8 k2 I256 T4)", F.Q6K, 512, 256, 8, 2, 4)
 Q3K_QWEN3_T2 = W.Workload("Qwen3-30B-A3B-shaped MoE layer, Q3_K/Q4_K experts, decode T=2", F.Q3K_Q4K, 2048, 768, 128,
                           8, 2)
 
 
 @pytest.mark.parametrize("wl", [W.TINY, W.QWEN3_DECODE_T1, W.QWEN3_DECODE_T2, MXFP4_SMALL, W.QWEN3_MXFP4_DECODE_T2,
-                                Q3K_SMALL, Q3K_QWEN3_T2, Q5K_SMALL, Q5K_QWEN3_T2],
+                                Q3K_SMALL, Q3K_QWEN3_T2, Q5K_SMALL, Q5K_QWEN3_T2, Q6K_SMALL,
+                                W.QWEN3_Q6K_DECODE_T2],
                          ids=lambda w: w.name.split(",")[0][:24] + f"-fmt{w.fmt}-T{w.T}")
 def test_decode_layer_matches_oracle(wl):
     say(f"decode layer {wl.name}")
@@ -399,13 +401,14 @@ def test_dsv3_experts_many_tokens_per_slot(dsv3_blobs):
     assert int(np.diff(got["slot_offsets"]).max()) > 2
 
 
-@pytest.mark.parametrize("fmt", [F.Q4K, F.Q8_0, F.MXFP4, F.Q3K_Q4K, F.Q5K])
+@pytest.mark.parametrize("fmt", [F.Q4K, F.Q8_0, F.MXFP4, F.Q3K_Q4K, F.Q5K, F.Q6K])
 def test_decode_k_split_across_workgroups(fmt):
     """Two experts with a long K (H 7168): too few row tiles to fill the chip,
     so K is split across workgroups too (partial sums finished by the reduce
     kernel), with an uneven last part and a slot holding several chunks of
     tokens."""
-    name = {F.Q4K: "Q4_K", F.Q8_0: "Q8_0", F.MXFP4: "MXFP4", F.Q3K_Q4K: "Q3_K/Q4_K", F.Q5K: "Q5_K"}[fmt]
+    name = {F.Q4K: "Q4_K", F.Q8_0: "Q8_0", F.MXFP4: "MXFP4", F.Q3K_Q4K: "Q3_K/Q4_K", F.Q5K: "Q5_K",
+            F.Q6K: "Q6_K"}[fmt]
     wl = W.Workload(f"{name} layer H 7168, 2 experts, k 1, T 5", fmt, 7168, 256, 2, 1, 5)
     say(wl.name)
     got, want, soe, S = _layer_case(wl, path=Q.MOE_PATH_DECODE)
@@ -502,6 +505,36 @@ def test_decode_q5k_many_tokens_partial_residency():
     got, want, soe, S = _layer_case(wl, soe=soe, S=9, path=Q.MOE_PATH_DECODE)
     _check_layer(wl, got, want, soe, S)
     assert got["host_count"] > 0
+
+
+@pytest.mark.parametrize("T", [8, 24], ids=["K-split", "pipelined"])
+def test_dsv3_sized_q6k_experts(T):
+    """DeepSeek-V3-sized Q6_K experts (H 7168, I 2048), 16 of them: the
+    gate/up GEMV splits K across workgroups at 16 pairs and runs its
+    pipelined kernel at 48; the down GEMV (per-half constants in the h
+    records) pipelines in both."""
+    wl = W.Workload(f"DeepSeek-V3-sized Q6_K experts, 16 resident, {T} tokens", F.Q6K, 7168, 2048, 16, 2, T)
+    say(wl.name)
+    F.set_num_threads(THREADS)
+    got, want, soe, S = _layer_case(wl, path=Q.MOE_PATH_DECODE)
+    _check_layer(wl, got, want, soe, S)
+
+
+def test_decode_q6k_many_tokens_partial_residency():
+    """Q6_K, 37 tokens over 12 experts, 8 resident: chunks of two tokens per
+    slot plus remainders; the host leg completes the layer."""
+    wl = W.Workload("small Q6_K layer, 37 tokens, partial residency", F.Q6K, 512, 256, 12, 4, 37)
+    say(wl.name)
+    soe = np.array([3, -1, 0, 5, -1, 1, 2, -1, 4, 6, -1, 7], dtype=np.int32)
+    blobs = W.expert_blobs(wl)
+    got, want, soe, S = _layer_case(wl, blobs=blobs, soe=soe, S=9, path=Q.MOE_PATH_DECODE)
+    _check_layer(wl, got, want, soe, S)
+    assert got["host_count"] > 0
+    x, logits = W.x_of(wl), W.logits_of(wl)
+    y_host = Q.moe_host_leg(wl.fmt, list(blobs), wl.H, wl.I, x, got["host_token"], got["host_expert"],
+                            got["host_weight"], threads=THREADS)
+    full = run_oracle(wl, blobs, x, logits, np.arange(wl.E, dtype=np.int32), None)
+    assert rel_max_err(got["y"] + y_host, full["y"]) <= DECODE_TOL
 
 
 def test_host_list_written_into_pinned_memory():

@@ -117,6 +117,26 @@ def test_stack_graph_replay(stack):
     say(f"  card-served share of routed pairs: {share:.3f}")
 
 
+def test_stack_replays_run_during_a_swap_round(stack):
+    """The swap copies go on a stream whose work the replays do not queue
+    behind: a replay issued after a round's copies ends while they still
+    stream (11.5 GB at PCIe rates against a few ms per replay)."""
+    st = stack["st"]
+    if st.graph is None:
+        st.capture()
+    say(f"copy stream: {st.side_probes} candidate(s) tried against a replay, overlaps = {st.side_overlaps}")
+    assert st.side_overlaps
+    st.swap_begin(8)
+    st.replay()
+    st.replay_done.synchronize()
+    still_copying = not st.swap_copies_done.query()
+    st.swap_commit(block=True)
+    st.replay()
+    torch.cuda.synchronize()
+    assert still_copying
+    _check_replay(stack, (7,))
+
+
 def test_stack_swap_rounds(stack):
     st = stack["st"]
     if st.graph is None:

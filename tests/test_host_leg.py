@@ -20,6 +20,7 @@ CASES = {
     "mxfp4_small": W.Workload("MXFP4 layer H512 I256 E16 k4 T6", F.MXFP4, 512, 256, 16, 4, 6),
     "q3k_q4k_small": W.Workload("Q3_K/Q4_K layer H512 I256 E16 k4 T6", F.Q3K_Q4K, 512, 256, 16, 4, 6),
     "q5k_small": W.Workload("Q5_K layer H512 I256 E16 k4 T6", F.Q5K, 512, 256, 16, 4, 6),
+    "q6k_small": W.Workload("Q6_K layer H512 I256 E16 k4 T6", F.Q6K, 512, 256, 16, 4, 6),
 }
 
 
