@@ -274,6 +274,7 @@ def bench_prefill(args, blobs, pool, stride, fmt=None, ceiling=True) -> dict:
     import numpy as np
     import torch
 
+    import fixtures as F
     import quantized_routed_expert_moe_amd as Q
     from fixtures import workloads as W
     from quantized_routed_expert_moe_amd.layer import LayerSpec, MoELayer
@@ -322,7 +323,7 @@ def bench_prefill(args, blobs, pool, stride, fmt=None, ceiling=True) -> dict:
         "expert_rows": {"total": M, "max": int(counts.max()), "median": float(np.median(counts)),
                         "min": int(counts.min())},
         "roofline": {"bound": "mfma", "kernel": "prefill gate/up grouped GEMM (%s->bf16 fragments, bf16 MFMA)" %
-                     ("Q4_K" if fmt is None else "MXFP4"),
+                     ("Q4_K" if fmt is None else {F.MXFP4: "MXFP4", F.Q5K: "Q5_K", F.Q6K: "Q6_K", F.Q4K: "Q4_K"}[fmt]),
                      "achieved": round(gu_tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gu_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                      "algorithmic_flop_per_launch": gu_flop, "avg_launch_us": round(kern["gemm_gateup"], 2)},
@@ -537,8 +538,8 @@ def bench_formats(args, threads: int) -> dict:
              "layer_GBs": round(layer_bytes / (ms_step * 1e-3) / 1e9, 1),
              "layer_frac_of_hbm": round(layer_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
              "pool_copies": copies}
-        if key == "mxfp4_qwen3_T2" and args.prefill_steps > 0:
-            pre = bench_prefill(args, None, pools[0], stride, fmt=F.MXFP4, ceiling=False)
+        if key in ("mxfp4_qwen3_T2", "q5k_qwen3_T2", "q6k_qwen3_T2") and args.prefill_steps > 0:
+            pre = bench_prefill(args, None, pools[0], stride, fmt=wl.fmt, ceiling=False)
             r["prefill_T4096"] = {kk: pre[kk] for kk in ("ms_per_step", "tokens_per_s", "roofline", "down_gemm_TFLOPs",
                                                          "expert_gemms_frac", "kernels_us")}
         if not wl.I_shared:  # stage 3 then times only the routed gate/up GEMV

@@ -80,10 +80,15 @@ size_t packed_bytes(int format, int H, int I) {
     return blob_bytes(format, H, I);
 }
 
+// Formats the prefill GEMM takes (the mixed Q3_K/Q4_K expert and Q8_0 run
+// the decode path at any T).
+bool has_prefill(int format) {
+    return format == MOE_FMT_Q4K || format == MOE_FMT_MXFP4 || format == MOE_FMT_Q5K || format == MOE_FMT_Q6K;
+}
+
 int resolve_path(int format, int T, int x_dtype, int path) {
     if (path != MOE_PATH_AUTO) return path;
-    return ((format == MOE_FMT_Q4K || format == MOE_FMT_MXFP4) && x_dtype == MOE_BF16 && T > 32) ? MOE_PATH_PREFILL
-                                                                                                  : MOE_PATH_DECODE;
+    return (has_prefill(format) && x_dtype == MOE_BF16 && T > 32) ? MOE_PATH_PREFILL : MOE_PATH_DECODE;
 }
 
 // ------------------------------------------------------------------ timers
@@ -549,9 +554,9 @@ moe_status ffn_common(int format, const void* slot_pool, size_t slot_stride, int
         if (y_dtype != MOE_F32) return fail(MOE_ERR_UNSUPPORTED, "the decode path writes MOE_F32 y_pairs");
         need = qmoe::decode_workspace_bytes(T, k, H, I);
     } else {
-        if (format != MOE_FMT_Q4K && format != MOE_FMT_MXFP4)
-            return fail(MOE_ERR_UNSUPPORTED, "the prefill path is implemented for Q4_K and MXFP4 (MOE_PATH_DECODE "
-                                             "serves the other formats at any T)");
+        if (!has_prefill(format))
+            return fail(MOE_ERR_UNSUPPORTED, "the prefill path is implemented for Q4_K, Q5_K, Q6_K and MXFP4 "
+                                             "(MOE_PATH_DECODE serves the other formats at any T)");
         if (x_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the prefill path takes MOE_BF16 x");
         // The GEMMs address x and h rows with 32-bit byte offsets, and the
         // tile list counts tiles in 16 bits.
@@ -754,7 +759,7 @@ size_t moe_ffn_workspace_size(int format, int T, int k, int H, int I, int path) 
     if (check_shape(format, H, I) != MOE_OK || T < 0 || k < 1 || k > MOE_MAX_TOPK) return 0;
     const size_t dec = qmoe::decode_workspace_bytes(T, k, H, I);
     static_assert(MOE_MAX_EXPERTS == qmoe::kMaxExpertsInternal, "expert limits differ");
-    if ((format != MOE_FMT_Q4K && format != MOE_FMT_MXFP4) || path == MOE_PATH_DECODE) return dec;
+    if (!has_prefill(format) || path == MOE_PATH_DECODE) return dec;
     const size_t pre = qmoe::prefill_workspace_bytes(T, k, H, I);
     if (path == MOE_PATH_PREFILL) return pre;
     return std::max(dec, pre);

@@ -278,6 +278,27 @@ __device__ __forceinline__ void mx4_dq_bc(DqPart& d, int half) {
     d.out[2 * half] = __builtin_amdgcn_perm(p1, p0, sel);
     d.out[2 * half + 1] = __builtin_amdgcn_perm(p3, p2, sel);
 }
+// Q5_K and Q6_K: the lane's eight weights as bytes q = nibble | high bits <<
+// 4 (elements 0, 2, 4, 6 in the bytes of lo, 1, 3, 5, 7 in hi), taken to
+// fp32 exactly (v_cvt_f32_ubyte); dq_bc then forms w = ds q + c with one fma
+// (Q5_K: ds = d sc, c = -dmin m; Q6_K: ds = d sc, c = -32 d sc).
+__device__ __forceinline__ void qb_dq_a(DqPart& d, uint32_t lo, uint32_t hi) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        d.q[2 * b] = (float)((lo >> (8 * b)) & 0xFFu);
+        d.q[2 * b + 1] = (float)((hi >> (8 * b)) & 0xFFu);
+    }
+}
+// The bytes of one group: w is its dword of nibbles (element n in nibble n),
+// hb the word holding its high bits; element n's high bits sit at bit
+// 4n + sh (Q5_K: one bit, sh = the group index; Q6_K: two bits, sh = 2 (d %
+// 2)), masked by hmask (0x01010101 or 0x03030303).
+__device__ __forceinline__ uint2 qb_bytes(uint32_t w, uint32_t hb, int sh, uint32_t hmask) {
+    const uint32_t lo = (w & 0x0F0F0F0Fu) | (((hb >> sh) & hmask) << 4);
+    const uint32_t hi = ((w >> 4) & 0x0F0F0F0Fu) | (((hb >> (sh + 4)) & hmask) << 4);
+    return make_uint2(lo, hi);
+}
+
 __device__ __forceinline__ bf16x8 mx4_frag(uint32_t w, float scale) {
     DqPart d;
     mx4_dq_a(d, w, scale);
@@ -291,6 +312,7 @@ __device__ __forceinline__ bf16x8 mx4_frag(uint32_t w, float scale) {
 struct TileCtx {
     const uint8_t* b_rowgroup;  // first super-block tile of this wave's packed row group
     int hdr_off[2], q_off[2];   // per block: header / quant byte offsets inside a tile (lane's row)
+    int hb_off[2], d_off[2];    // Q5_K, Q6_K: high-bit chunk 0 of the lane's row; Q6_K: its fp16 d
     int q_step, tile_bytes;
     const uint8_t* a_base;      // A matrix
     uint32_t a_off[kRowBlocks]; // byte offset of this lane's DMA row in row group wave + 4 t, plus its chunk
@@ -298,7 +320,10 @@ struct TileCtx {
 };
 
 // FMT 1: Q4_K tiles (16-byte headers); FMT 2: MXFP4 tiles (8 scale bytes
-// per row and 256 inputs, read into the header's first two words).
+// per row and 256 inputs, read into the header's first two words); FMT 4:
+// Q5_K (Q4_K headers and nibbles, one 16-byte chunk of high-bit words per
+// row and stage); FMT 5: Q6_K (16 signed scale bytes as the header, fp16 d
+// apart, two 16-byte chunks of (H0, H1) words per row and stage).
 template <int FMT, bool GATEUP, int NB>
 __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* sA1, int wave, int lane,
                                           f32x16 (&acc)[kRowBlocks][2]) {
@@ -307,7 +332,12 @@ __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* s
     // does not make those reads wait for the DMA.
     auto buffer = [&](int b) { return b ? sA1 : sA0; };
     const int nsb = c.K / 256, nstages = 2 * nsb;
-    struct BQuant { uint2 v[2][4]; };  // [block][sub-block of the stage]
+    struct BQuant {
+        uint2 v[2][4];  // [block][sub-block of the stage]
+        uint4 h[2][2];  // Q5_K: [block][0] the stage's four HB words; Q6_K: [block][i] blocks 2i, 2i+1's (H0, H1)
+    };
+    constexpr bool kHighBits = FMT == 4 || FMT == 5;
+    constexpr int kHChunks = FMT == 5 ? 2 : 1;
 
     // DMA unit (row group g = wave + 4 t, half h): 8 rows x 64 K values into
     // the 1 KB block 2 g + h.  Row groups past the tile's row blocks are
@@ -326,12 +356,21 @@ __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* s
         const uint8_t* tile = c.b_rowgroup + (size_t)(st >> 1) * c.tile_bytes;
         r.v[m][jj] = ldg<uint2>(tile + c.q_off[m] + (4 * (st & 1) + jj) * c.q_step);
     };
+    auto load_h_one = [&](int st, BQuant& r, int m, int i) {
+        const uint8_t* tile = c.b_rowgroup + (size_t)(st >> 1) * c.tile_bytes;
+        r.h[m][i] = ldg<uint4>(tile + c.hb_off[m] + (kHChunks * (st & 1) + i) * c.q_step);
+    };
     auto load_b = [&](int st, BQuant& r) {
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < 2; ++m) {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) load_b_one(st, r, m, jj);
+            if (kHighBits)
+#pragma unroll
+                for (int i = 0; i < kHChunks; ++i) load_h_one(st, r, m, i);
+        }
     };
+    uint32_t dq[2] = {0u, 0u};  // Q6_K: fp16 d of the header's super-block (low half)
     auto load_hdr = [&](int sb, uint4* h) {
         const uint8_t* tile = c.b_rowgroup + (size_t)sb * c.tile_bytes;
 #pragma unroll
@@ -342,7 +381,26 @@ __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* s
             } else {
                 h[m] = ldg<uint4>(tile + c.hdr_off[m]);
             }
+            if (FMT == 5) dq[m] = ldg<uint16_t>(tile + c.d_off[m]);
         }
+    };
+    // Q6_K: d sc of 16-weight sub-block i16 (0..15) from the signed scale bytes
+    auto q6_scale = [](const uint4& h, uint32_t dbits, int i16) {
+        const uint32_t w = i16 < 4 ? h.x : i16 < 8 ? h.y : i16 < 12 ? h.z : h.w;
+        return half_to_float(dbits) * (float)((int32_t)(w << (24 - 8 * (i16 & 3))) >> 24);
+    };
+    // Q5_K, Q6_K: the two byte words of the lane's group in step s of
+    // sub-block jj (group d = 2 (s % 2) + lane / 32)
+    auto hq = [&](const BQuant& r, int m, int jj, int s, uint32_t w) {
+        const int hsel = lane >> 5;
+        if (FMT == 4) {
+            const uint4 hv = r.h[m][0];
+            const uint32_t hb = jj == 0 ? hv.x : jj == 1 ? hv.y : jj == 2 ? hv.z : hv.w;
+            return qb_bytes(w, hb, 2 * (s & 1) + hsel, 0x01010101u);
+        }
+        const uint4 hv = r.h[m][jj >> 1];
+        const uint32_t h0 = (jj & 1) ? hv.z : hv.x, h1 = (jj & 1) ? hv.w : hv.y;
+        return qb_bytes(w, (s & 1) ? h1 : h0, 2 * hsel, 0x03030303u);
     };
     // MXFP4 scale of block j (0..7) of a unit from its header words
     auto mx_scale = [](const uint4& h, int j) { return e8m0_scale(((j < 4 ? h.x : h.y) >> (8 * (j & 3))) & 0xFFu); };
@@ -362,6 +420,22 @@ __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* s
         for (int m = 0; m < 2; ++m) {
             if (FMT == 2) {
                 fb_next0[m] = mx4_frag(rb[0].v[m][0].x, mx_scale(hdr[m], 0));
+            } else if (kHighBits) {
+                float ds, nc;
+                if (FMT == 4) {
+                    hw0[m] = header_words(hdr[m]);
+                    ds = hw0[m].d512 * (1.0f / 512.0f) * (float)(hw0[m].sc[0] & 0xFFu);
+                    nc = -(hw0[m].dmin * (float)(hw0[m].mn[0] & 0xFFu));
+                } else {
+                    ds = q6_scale(hdr[m], dq[m], 0);
+                    nc = -32.0f * ds;
+                }
+                const uint2 qb = hq(rb[0], m, 0, 0, rb[0].v[m][0].x);
+                DqPart d0;
+                qb_dq_a(d0, qb.x, qb.y);
+                dq_bc(d0, 0, ds, nc);
+                dq_bc(d0, 1, ds, nc);
+                fb_next0[m] = __builtin_bit_cast(bf16x8, make_uint4(d0.out[0], d0.out[1], d0.out[2], d0.out[3]));
             } else {
                 hw0[m] = header_words(hdr[m]);
                 fb_next0[m] = dequant_frag(rb[0].v[m][0].x, hw0[m].d512 * (float)(hw0[m].sc[0] & 0xFFu),
@@ -376,7 +450,8 @@ __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* s
         HeaderWords hw[2];
 #pragma unroll
         for (int m = 0; m < 2; ++m) hw[m] = header_words(hdr[m]);
-        const uint4 hraw[2] = {hdr[0], hdr[1]};  // MXFP4: this unit's scale bytes
+        const uint4 hraw[2] = {hdr[0], hdr[1]};  // MXFP4, Q6_K: this unit's scale bytes
+        const uint32_t draw[2] = {dq[0], dq[1]};  // Q6_K: this unit's d
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int st = 2 * sb + u;
@@ -389,20 +464,32 @@ __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* s
             // next one's headers.  Past the last stage the loads repeat it (in
             // bounds, cache hits, never used).
             const int nst = min(st + 1, nstages - 1);
-            // Q4_K: 512 d sc and -dmin m of each sub-block; MXFP4: the block
-            // scale in ds512, ndm unused
-            float ds512[2][4], ndm[2][4];
+            // Per sub-block jj and half (k16 step parity) hf, index 2 jj + hf:
+            // Q4_K: 512 d sc and -dmin m; MXFP4: the block scale in ds512, ndm
+            // unused; Q5_K: d sc and -dmin m; Q6_K: d sc and -32 d sc of the
+            // half's 16-weight sub-block.
+            float ds512[2][8], ndm[2][8];
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int j = 4 * u + jj;
-                    if (FMT == 2) {
-                        ds512[m][jj] = mx_scale(hraw[m], j);
-                        ndm[m][jj] = 0.0f;
-                    } else {
-                        ds512[m][jj] = hw[m].d512 * (float)((hw[m].sc[j >> 2] >> (8 * (j & 3))) & 0xFFu);
-                        ndm[m][jj] = -(hw[m].dmin * (float)((hw[m].mn[j >> 2] >> (8 * (j & 3))) & 0xFFu));
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        float a, b;
+                        if (FMT == 2) {
+                            a = mx_scale(hraw[m], j);
+                            b = 0.0f;
+                        } else if (FMT == 5) {
+                            a = q6_scale(hraw[m], draw[m], 2 * j + hf);
+                            b = -32.0f * a;
+                        } else {
+                            a = hw[m].d512 * (FMT == 4 ? 1.0f / 512.0f : 1.0f) *
+                                (float)((hw[m].sc[j >> 2] >> (8 * (j & 3))) & 0xFFu);
+                            b = -(hw[m].dmin * (float)((hw[m].mn[j >> 2] >> (8 * (j & 3))) & 0xFFu));
+                        }
+                        ds512[m][2 * jj + hf] = a;
+                        ndm[m][2 * jj + hf] = b;
                     }
                 }
             bf16x8 fa[2][NB], fb[2][2];
@@ -415,14 +502,6 @@ __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* s
                 const int off = frag_row + (chunk >> 3) * 64 + ((chunk & 7) ^ (lane & 7));
 #pragma unroll
                 for (int i = 0; i < NB; ++i) fa[slot][i] = __builtin_bit_cast(bf16x8, buffer(cur)[i * 512 + off]);
-            };
-            auto b_frags = [&](int s, int slot) {
-                const int jj = s >> 1;
-#pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    const uint32_t w = (s & 1) ? rb[cur].v[m][jj].y : rb[cur].v[m][jj].x;
-                    fb[slot][m] = dequant_frag(w, ds512[m][jj], ndm[m][jj]);
-                }
             };
             a_frags(0, 0);
 #pragma unroll
@@ -439,13 +518,16 @@ __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* s
                 DqPart dp[2];
                 uint32_t wsrc[2];
                 float dsv[2], ndv[2];
+                int nj = 0, ns = 0;  // sub-block and step of the fragment prepared here
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
                     if (!last) {
                         const int jj = (s + 1) >> 1;
+                        nj = jj;
+                        ns = s + 1;
                         wsrc[m] = ((s + 1) & 1) ? rb[cur].v[m][jj].y : rb[cur].v[m][jj].x;
-                        dsv[m] = ds512[m][jj];
-                        ndv[m] = ndm[m][jj];
+                        dsv[m] = ds512[m][2 * jj + ((s + 1) & 1)];
+                        ndv[m] = ndm[m][2 * jj + ((s + 1) & 1)];
                     } else {
                         // first k16 step of the next stage: sub-block 4 of this
                         // super-block, or sub-block 0 of the next one
@@ -453,6 +535,16 @@ __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* s
                         if (FMT == 2) {
                             dsv[m] = u == 0 ? mx_scale(hraw[m], 4) : mx_scale(hdr[m], 0);
                             ndv[m] = 0.0f;
+                        } else if (FMT == 5) {
+                            dsv[m] = u == 0 ? q6_scale(hraw[m], draw[m], 8) : q6_scale(hdr[m], dq[m], 0);
+                            ndv[m] = -32.0f * dsv[m];
+                        } else if (FMT == 4 && u == 0) {
+                            dsv[m] = hw[m].d512 * (1.0f / 512.0f) * (float)(hw[m].sc[1] & 0xFFu);
+                            ndv[m] = -(hw[m].dmin * (float)(hw[m].mn[1] & 0xFFu));
+                        } else if (FMT == 4) {
+                            const HeaderWords hn = header_words(hdr[m]);
+                            dsv[m] = hn.d512 * (1.0f / 512.0f) * (float)(hn.sc[0] & 0xFFu);
+                            ndv[m] = -(hn.dmin * (float)(hn.mn[0] & 0xFFu));
                         } else if (u == 0) {
                             dsv[m] = hw[m].d512 * (float)(hw[m].sc[1] & 0xFFu);
                             ndv[m] = -(hw[m].dmin * (float)(hw[m].mn[1] & 0xFFu));
@@ -475,17 +567,25 @@ __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* s
                                 if (2 * s < NB) dma_unit(nst, cur ^ 1, 2 * s);
                                 load_b_one(nst, rb[cur ^ 1], 0, s);
                                 if (u == 1 && s == 0) load_hdr(min(sb + 1, nsb - 1), hdr);
+                                if (kHighBits && s < kHChunks) load_h_one(nst, rb[cur ^ 1], 0, s);
                             }
                             break;
                         case 8:
                             if (s < 4) {
                                 if (2 * s + 1 < NB) dma_unit(nst, cur ^ 1, 2 * s + 1);
                                 load_b_one(nst, rb[cur ^ 1], 1, s);
+                                if (kHighBits && s < kHChunks) load_h_one(nst, rb[cur ^ 1], 1, s);
                             }
                             break;
                         case 5:
-                            if (FMT == 2) mx4_dq_a(dp[0], wsrc[0], dsv[0]);
-                            else dq_a(dp[0], wsrc[0]);
+                            if (FMT == 2) {
+                                mx4_dq_a(dp[0], wsrc[0], dsv[0]);
+                            } else if (kHighBits) {
+                                const uint2 qb = last ? hq(rb[cur ^ 1], 0, 0, 0, wsrc[0]) : hq(rb[cur], 0, nj, ns, wsrc[0]);
+                                qb_dq_a(dp[0], qb.x, qb.y);
+                            } else {
+                                dq_a(dp[0], wsrc[0]);
+                            }
                             break;
                         case 11:
                             if (FMT == 2) mx4_dq_bc(dp[0], 0);
@@ -496,8 +596,14 @@ __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* s
                             else dq_bc(dp[0], 1, dsv[0], ndv[0]);
                             break;
                         case 13:
-                            if (FMT == 2) mx4_dq_a(dp[1], wsrc[1], dsv[1]);
-                            else dq_a(dp[1], wsrc[1]);
+                            if (FMT == 2) {
+                                mx4_dq_a(dp[1], wsrc[1], dsv[1]);
+                            } else if (kHighBits) {
+                                const uint2 qb = last ? hq(rb[cur ^ 1], 1, 0, 0, wsrc[1]) : hq(rb[cur], 1, nj, ns, wsrc[1]);
+                                qb_dq_a(dp[1], qb.x, qb.y);
+                            } else {
+                                dq_a(dp[1], wsrc[1]);
+                            }
                             break;
                         case 14:
                             if (FMT == 2) mx4_dq_bc(dp[1], 0);
@@ -612,28 +718,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // 8 * (lane / 32).. of each (row, sub-block) slot.
     // Per tile: Q4_K headers are 16 bytes per row (1 KB per matrix), MXFP4
     // scales 8 bytes per row (512 B per matrix); the quants of block j follow.
+    // Q5_K / Q6_K tiles add high-bit chunks after the nibbles (9 KB per
+    // matrix in) and Q6_K the d row after those (13 KB per matrix in).
     const int hb = FMT == 2 ? 8 : 16;
+    const int gtile = FMT == 2 ? kMx4GateUpTile : FMT == 4 ? kQ5kGateUpTile : FMT == 5 ? kQ6kGateUpTile
+                                                                                        : kQ4kGateUpTile;
+    const int dtile = FMT == 2 ? kMx4DownTile : FMT == 4 ? kQ5kDownTile : FMT == 5 ? kQ6kDownTile : kQ4kDownTile;
+    const size_t gu_bytes = FMT == 2 ? mx4_gateup_bytes(H, I) : FMT == 4 ? q5k_gateup_bytes(H, I)
+                            : FMT == 5 ? q6k_gateup_bytes(H, I) : q4k_gateup_bytes(H, I);
     if (GATEUP) {
         const int fb = nt * kWaves + wave;
-        const int gtile = FMT == 2 ? kMx4GateUpTile : kQ4kGateUpTile;
         c.b_rowgroup = wbase + (size_t)(fb >> 1) * (H / 256) * gtile;
         const int r = (fb & 1) * 32 + r32;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             c.hdr_off[m] = m * 64 * hb + r * hb;
             c.q_off[m] = 128 * hb + m * 1024 + r * 16 + 8 * hsel;
+            c.hb_off[m] = 9 * 2048 + m * 1024 + r * 16;
+            c.d_off[m] = 13 * 2048 + 4 * r + 2 * m;
         }
         c.q_step = 2048;
         c.tile_bytes = gtile;
     } else {
         const int cb = nt * kWaves + wave;
-        const int dtile = FMT == 2 ? kMx4DownTile : kQ4kDownTile;
-        c.b_rowgroup = wbase + (FMT == 2 ? mx4_gateup_bytes(H, I) : q4k_gateup_bytes(H, I)) +
-                       (size_t)cb * (I / 256) * dtile;
+        c.b_rowgroup = wbase + gu_bytes + (size_t)cb * (I / 256) * dtile;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             c.hdr_off[m] = (32 * m + r32) * hb;
             c.q_off[m] = 64 * hb + (32 * m + r32) * 16 + 8 * hsel;
+            c.hb_off[m] = 9 * 1024 + (32 * m + r32) * 16;
+            c.d_off[m] = 13 * 1024 + 2 * (32 * m + r32);
         }
         c.q_step = 1024;
         c.tile_bytes = dtile;
@@ -785,8 +899,14 @@ hipError_t launch_ffn_prefill(const FfnArgs& a, hipStream_t s) {
     // Grid: 8 XCD lanes x (N tiles x ceil(M tiles / 8)).
     const int mgroups = (mt + 7) / 8;
     const int nt_gu = a.I / kGateUpFeatures, nt_dn = a.H / kDownColumns;
-    auto gateup = a.format == 2 ? prefill_gemm_kernel<2, true> : prefill_gemm_kernel<1, true>;
-    auto down = a.format == 2 ? prefill_gemm_kernel<2, false> : prefill_gemm_kernel<1, false>;
+    auto gateup = a.format == 2   ? prefill_gemm_kernel<2, true>
+                  : a.format == 4 ? prefill_gemm_kernel<4, true>
+                  : a.format == 5 ? prefill_gemm_kernel<5, true>
+                                  : prefill_gemm_kernel<1, true>;
+    auto down = a.format == 2   ? prefill_gemm_kernel<2, false>
+                : a.format == 4 ? prefill_gemm_kernel<4, false>
+                : a.format == 5 ? prefill_gemm_kernel<5, false>
+                                : prefill_gemm_kernel<1, false>;
     const StageEvents ev_g = timer_events(kStagePrefillGateUp);
     launch_timed(gateup, dim3(8 * nt_gu * mgroups), dim3(kThreads), 0, s, ev_g.start, ev_g.stop, a.pool, a.stride, a.S,
                  a.H, a.I, static_cast<const uint16_t*>(a.x), a.T, a.k, a.perm_pair, tiles, ntiles,

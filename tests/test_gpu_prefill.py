@@ -1,5 +1,5 @@
-"""Parity of the prefill path (bf16 MFMA grouped GEMM over Q4_K or MXFP4
-tiles) with the CPU oracle.
+"""Parity of the prefill path (bf16 MFMA grouped GEMM over Q4_K, MXFP4, Q5_K
+or Q6_K tiles) with the CPU oracle.
 
 Ids, slot offsets, active slots, permutation and host list: bit-exact on
 every row.  Outputs: per token row t, max_i |y_ti - y*_ti| <= 1e-2 *
@@ -54,11 +54,12 @@ def _prefill_case(wl, soe=None, S=None, pair_dtype=torch.bfloat16, y_dtype=torch
     return err
 
 
-@pytest.mark.parametrize("fmt", [F.Q4K, F.MXFP4], ids=["Q4_K", "MXFP4"])
+@pytest.mark.parametrize("fmt", [F.Q4K, F.MXFP4, F.Q5K, F.Q6K], ids=["Q4_K", "MXFP4", "Q5_K", "Q6_K"])
 def test_prefill_qwen3_full_size(fmt):
     """4096 tokens, Zipf(1.0)-skewed loads over 128 experts, all resident."""
-    wl = W.QWEN3_PREFILL if fmt == F.Q4K else dataclasses.replace(W.QWEN3_PREFILL, fmt=F.MXFP4,
-                                                                  name=W.QWEN3_PREFILL.name + ", MXFP4 experts")
+    names = {F.MXFP4: "MXFP4", F.Q5K: "Q5_K", F.Q6K: "Q6_K"}
+    wl = W.QWEN3_PREFILL if fmt == F.Q4K else dataclasses.replace(W.QWEN3_PREFILL, fmt=fmt,
+                                                                  name=W.QWEN3_PREFILL.name + f", {names[fmt]} experts")
     say(wl.name)
     F.set_num_threads(THREADS)
     rng = np.random.default_rng(0)
@@ -66,7 +67,7 @@ def test_prefill_qwen3_full_size(fmt):
     assert _prefill_case(wl, sample=sample) <= PREFILL_TOL
 
 
-@pytest.mark.parametrize("fmt", [F.Q4K, F.MXFP4], ids=["Q4_K", "MXFP4"])
+@pytest.mark.parametrize("fmt", [F.Q4K, F.MXFP4, F.Q5K, F.Q6K], ids=["Q4_K", "MXFP4", "Q5_K", "Q6_K"])
 @pytest.mark.parametrize("T,E,k,pd,yd", [
     (300, 16, 4, torch.bfloat16, torch.bfloat16),
     (129, 8, 2, torch.float32, torch.float32),
@@ -79,7 +80,7 @@ def test_prefill_small_layers(T, E, k, pd, yd, fmt):
     assert _prefill_case(wl, pair_dtype=pd, y_dtype=yd) <= PREFILL_TOL
 
 
-@pytest.mark.parametrize("fmt", [F.Q4K, F.MXFP4], ids=["Q4_K", "MXFP4"])
+@pytest.mark.parametrize("fmt", [F.Q4K, F.MXFP4, F.Q5K, F.Q6K], ids=["Q4_K", "MXFP4", "Q5_K", "Q6_K"])
 def test_prefill_partial_residency(fmt):
     wl = W.Workload("prefill T200 E24 k3, 15 resident of 24", fmt, 768, 512, 24, 3, 200, x_bf16=True,
                     zipf_s=1.2, seed=5)
@@ -90,7 +91,7 @@ def test_prefill_partial_residency(fmt):
     assert _prefill_case(wl, soe=soe, S=17) <= PREFILL_TOL
 
 
-@pytest.mark.parametrize("fmt", [F.Q4K, F.MXFP4], ids=["Q4_K", "MXFP4"])
+@pytest.mark.parametrize("fmt", [F.Q4K, F.MXFP4, F.Q5K, F.Q6K], ids=["Q4_K", "MXFP4", "Q5_K", "Q6_K"])
 def test_prefill_tile_boundaries(fmt):
     """One expert receives exactly 128, another 129, another 1 pair."""
     wl = W.Workload("prefill tile boundaries", fmt, 256, 256, 4, 1, 258, x_bf16=True, seed=7)
@@ -128,7 +129,7 @@ def _bf16_round(a: np.ndarray) -> np.ndarray:
     return F.bf16_bits_to_f32(F.to_bf16_bits(a.astype(np.float32))).astype(np.float64)
 
 
-@pytest.mark.parametrize("fmt", [F.Q4K, F.MXFP4], ids=["Q4_K", "MXFP4"])
+@pytest.mark.parametrize("fmt", [F.Q4K, F.MXFP4, F.Q5K, F.Q6K], ids=["Q4_K", "MXFP4", "Q5_K", "Q6_K"])
 def test_prefill_equals_its_bf16_rounding_model(fmt):
     """The prefill arithmetic is the exact layer with three roundings: each
     dequantized weight to fp32 then bf16 (MXFP4 weights are bf16 values
