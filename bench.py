@@ -323,7 +323,8 @@ def bench_prefill(args, blobs, pool, stride, fmt=None, ceiling=True) -> dict:
         "expert_rows": {"total": M, "max": int(counts.max()), "median": float(np.median(counts)),
                         "min": int(counts.min())},
         "roofline": {"bound": "mfma", "kernel": "prefill gate/up grouped GEMM (%s->bf16 fragments, bf16 MFMA)" %
-                     ("Q4_K" if fmt is None else {F.MXFP4: "MXFP4", F.Q5K: "Q5_K", F.Q6K: "Q6_K", F.Q4K: "Q4_K"}[fmt]),
+                     ("Q4_K" if fmt is None else {F.MXFP4: "MXFP4", F.Q5K: "Q5_K", F.Q6K: "Q6_K", F.Q4K: "Q4_K",
+                                              F.Q3K_Q4K: "Q3_K gate/up"}[fmt]),
                      "achieved": round(gu_tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gu_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                      "algorithmic_flop_per_launch": gu_flop, "avg_launch_us": round(kern["gemm_gateup"], 2)},
@@ -477,7 +478,8 @@ def bench_formats(args, threads: int) -> dict:
                 F.Q6K: w // 256 * 210}[wl.fmt]
 
     for key, wl, copies in (("mxfp4_qwen3_T2", W.QWEN3_MXFP4_DECODE_T2, 8), ("mxfp4_dsv3_T2", W.DSV3_MXFP4_DECODE_T2, 1),
-                            ("q3k_q4k_dsv3_T2", W.DSV3_Q3K_DECODE_T2, 1), ("q5k_qwen3_T2", W.QWEN3_Q5K_DECODE_T2, 8),
+                            ("q3k_q4k_dsv3_T2", W.DSV3_Q3K_DECODE_T2, 1), ("q3k_q4k_qwen3_T2", W.QWEN3_Q3K_DECODE_T2, 8),
+                            ("q5k_qwen3_T2", W.QWEN3_Q5K_DECODE_T2, 8),
                             ("q5k_dsv3_T2", W.DSV3_Q5K_DECODE_T2, 1), ("q6k_qwen3_T2", W.QWEN3_Q6K_DECODE_T2, 8),
                             ("q6k_dsv3_T2", W.DSV3_Q6K_DECODE_T2, 1)):
         blobs = W.expert_blobs(wl)
@@ -538,7 +540,7 @@ def bench_formats(args, threads: int) -> dict:
              "layer_GBs": round(layer_bytes / (ms_step * 1e-3) / 1e9, 1),
              "layer_frac_of_hbm": round(layer_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
              "pool_copies": copies}
-        if key in ("mxfp4_qwen3_T2", "q5k_qwen3_T2", "q6k_qwen3_T2") and args.prefill_steps > 0:
+        if key in ("mxfp4_qwen3_T2", "q3k_q4k_qwen3_T2", "q5k_qwen3_T2", "q6k_qwen3_T2") and args.prefill_steps > 0:
             pre = bench_prefill(args, None, pools[0], stride, fmt=wl.fmt, ceiling=False)
             r["prefill_T4096"] = {kk: pre[kk] for kk in ("ms_per_step", "tokens_per_s", "roofline", "down_gemm_TFLOPs",
                                                          "expert_gemms_frac", "kernels_us")}

@@ -67,6 +67,9 @@ DSV3_Q3K_DECODE_T2 = Workload("DeepSeek-V3-shaped MoE layer, Q3_K gate/up + Q4_K
                               "(+shared Q8_0 expert)", Q3K_Q4K, 7168, 2048, 256, 8, 2, score=SIGMOID, scale=2.5,
                               I_shared=2048)
 
+QWEN3_Q3K_DECODE_T2 = Workload("Qwen3-30B-A3B-shaped MoE layer, Q3_K gate/up + Q4_K down experts, decode T=2",
+                               Q3K_Q4K, 2048, 768, 128, 8, 2)
+
 # Q5_K experts (a card expert type of the engine).
 QWEN3_Q5K_DECODE_T2 = Workload("Qwen3-30B-A3B-shaped MoE layer, Q5_K experts, decode T=2", Q5K, 2048, 768, 128, 8, 2)
 DSV3_Q5K_DECODE_T2 = Workload("DeepSeek-V3-shaped MoE layer, Q5_K experts, decode T=2 (+shared Q8_0 expert)", Q5K,
@@ -79,7 +82,7 @@ DSV3_Q6K_DECODE_T2 = Workload("DeepSeek-V3-shaped MoE layer, Q6_K experts, decod
 
 ALL = [TINY, QWEN3_DECODE_T1, QWEN3_DECODE_T2, QWEN3_PREFILL, DSV3_DECODE_T2, DSV3_DECODE_T4, DSV3_STACK,
        QWEN3_MXFP4_DECODE_T2, DSV3_MXFP4_DECODE_T2, DSV3_Q3K_DECODE_T2, QWEN3_Q5K_DECODE_T2, DSV3_Q5K_DECODE_T2,
-       QWEN3_Q6K_DECODE_T2, DSV3_Q6K_DECODE_T2]
+       QWEN3_Q6K_DECODE_T2, DSV3_Q6K_DECODE_T2, QWEN3_Q3K_DECODE_T2]
 
 
 def x_of(w: Workload, layer: int = 0, seed: int | None = None) -> np.ndarray:

@@ -273,14 +273,13 @@ moe_status moe_validate_slot_map(const int32_t* slot_of_expert, int E, int S);
  *               exactly to fp16 by the hardware FP4 conversion, the block's
  *               dot product then scaled by 2^(X - 127) in fp32; Q3_K: each
  *               16-element sub-block's dot product scaled by d (sc_j - 32)).
- *               MOE_PATH_PREFILL (Q4_K, Q5_K, Q6_K and MXFP4): bf16 x, weights
+ *               MOE_PATH_PREFILL (every format but Q8_0): bf16 x, weights
  *               dequantized to bf16 fragments, bf16 MFMA with fp32
  *               accumulate, h rounded to bf16; y_pairs MOE_F32 or MOE_BF16.
  *               (MXFP4 weights beyond bf16's range, |w| > 3.39e38, become
  *               infinite there.)
- *               MOE_PATH_AUTO: PREFILL for Q4_K, Q5_K, Q6_K and MXFP4 with
- *               bf16 x when T > 32, else DECODE (always DECODE for Q8_0 and
- *               the Q3_K/Q4_K mixed expert).
+ *               MOE_PATH_AUTO: PREFILL for every format but Q8_0 with bf16
+ *               x when T > 32, else DECODE (always DECODE for Q8_0).
  * ws, ws_bytes  device workspace, at least moe_ffn_workspace_size(format, T,
  *               k, H, I, path).
  *

@@ -80,11 +80,8 @@ size_t packed_bytes(int format, int H, int I) {
     return blob_bytes(format, H, I);
 }
 
-// Formats the prefill GEMM takes (the mixed Q3_K/Q4_K expert and Q8_0 run
-// the decode path at any T).
-bool has_prefill(int format) {
-    return format == MOE_FMT_Q4K || format == MOE_FMT_MXFP4 || format == MOE_FMT_Q5K || format == MOE_FMT_Q6K;
-}
+// Formats the prefill GEMM takes (Q8_0 runs the decode path at any T).
+bool has_prefill(int format) { return format != MOE_FMT_Q8_0; }
 
 int resolve_path(int format, int T, int x_dtype, int path) {
     if (path != MOE_PATH_AUTO) return path;
@@ -555,8 +552,8 @@ moe_status ffn_common(int format, const void* slot_pool, size_t slot_stride, int
         need = qmoe::decode_workspace_bytes(T, k, H, I);
     } else {
         if (!has_prefill(format))
-            return fail(MOE_ERR_UNSUPPORTED, "the prefill path is implemented for Q4_K, Q5_K, Q6_K and MXFP4 "
-                                             "(MOE_PATH_DECODE serves the other formats at any T)");
+            return fail(MOE_ERR_UNSUPPORTED, "the prefill path is implemented for Q4_K, Q5_K, Q6_K, MXFP4 and "
+                                             "Q3_K/Q4_K (MOE_PATH_DECODE serves Q8_0 at any T)");
         if (x_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the prefill path takes MOE_BF16 x");
         // The GEMMs address x and h rows with 32-bit byte offsets, and the
         // tile list counts tiles in 16 bits.

@@ -278,10 +278,12 @@ __device__ __forceinline__ void mx4_dq_bc(DqPart& d, int half) {
     d.out[2 * half] = __builtin_amdgcn_perm(p1, p0, sel);
     d.out[2 * half + 1] = __builtin_amdgcn_perm(p3, p2, sel);
 }
-// Q5_K and Q6_K: the lane's eight weights as bytes q = nibble | high bits <<
-// 4 (elements 0, 2, 4, 6 in the bytes of lo, 1, 3, 5, 7 in hi), taken to
-// fp32 exactly (v_cvt_f32_ubyte); dq_bc then forms w = ds q + c with one fma
-// (Q5_K: ds = d sc, c = -dmin m; Q6_K: ds = d sc, c = -32 d sc).
+// Q5_K, Q6_K and Q3_K: the lane's eight weights as bytes (Q5_K, Q6_K: q =
+// nibble | high bits << 4; Q3_K: v = q + 4 = low | high << 2; elements 0,
+// 2, 4, 6 in the bytes of lo, 1, 3, 5, 7 in hi), taken to fp32 exactly
+// (v_cvt_f32_ubyte); dq_bc then forms w = ds q + c with one fma (Q5_K: ds =
+// d sc, c = -dmin m; Q6_K: ds = d sc, c = -32 d sc; Q3_K: ds = d (sc - 32),
+// c = -4 ds).
 __device__ __forceinline__ void qb_dq_a(DqPart& d, uint32_t lo, uint32_t hi) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
@@ -296,6 +298,14 @@ __device__ __forceinline__ void qb_dq_a(DqPart& d, uint32_t lo, uint32_t hi) {
 __device__ __forceinline__ uint2 qb_bytes(uint32_t w, uint32_t hb, int sh, uint32_t hmask) {
     const uint32_t lo = (w & 0x0F0F0F0Fu) | (((hb >> sh) & hmask) << 4);
     const uint32_t hi = ((w >> 4) & 0x0F0F0F0Fu) | (((hb >> (sh + 4)) & hmask) << 4);
+    return make_uint2(lo, hi);
+}
+
+// Q3_K: the bytes of one group from its low-bit word (element n's two bits
+// at bit 4n + sl) and high-bit word (element n's bit at 4n + sh).
+__device__ __forceinline__ uint2 q3_bytes(uint32_t lw, uint32_t hb, int sl, int sh) {
+    const uint32_t lo = ((lw >> sl) & 0x03030303u) | (((hb >> sh) & 0x01010101u) << 2);
+    const uint32_t hi = ((lw >> (sl + 4)) & 0x03030303u) | (((hb >> (sh + 4)) & 0x01010101u) << 2);
     return make_uint2(lo, hi);
 }
 
@@ -324,9 +334,12 @@ struct TileCtx {
 // Q5_K (Q4_K headers and nibbles, one 16-byte chunk of high-bit words per
 // row and stage); FMT 5: Q6_K (16 signed scale bytes as the header, fp16 d
 // apart, two 16-byte chunks of (H0, H1) words per row and stage).
-template <int FMT, bool GATEUP, int NB>
+template <int FMT_, bool GATEUP, int NB>
 __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* sA1, int wave, int lane,
                                           f32x16 (&acc)[kRowBlocks][2]) {
+    // block type of the matrix read: the mixed expert (3) reads Q3_K gate/up
+    // rows and a Q4_K down matrix
+    constexpr int FMT = (FMT_ == 3 && !GATEUP) ? 1 : FMT_;
     // Two distinct LDS arrays (not one [2][..] array): the compiler can then
     // tell the DMA into one buffer from the fragment reads of the other and
     // does not make those reads wait for the DMA.
@@ -336,7 +349,7 @@ __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* s
         uint2 v[2][4];  // [block][sub-block of the stage]
         uint4 h[2][2];  // Q5_K: [block][0] the stage's four HB words; Q6_K: [block][i] blocks 2i, 2i+1's (H0, H1)
     };
-    constexpr bool kHighBits = FMT == 4 || FMT == 5;
+    constexpr bool kHighBits = FMT == 3 || FMT == 4 || FMT == 5;
     constexpr int kHChunks = FMT == 5 ? 2 : 1;
 
     // DMA unit (row group g = wave + 4 t, half h): 8 rows x 64 K values into
@@ -354,7 +367,10 @@ __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* s
     };
     auto load_b_one = [&](int st, BQuant& r, int m, int jj) {
         const uint8_t* tile = c.b_rowgroup + (size_t)(st >> 1) * c.tile_bytes;
-        r.v[m][jj] = ldg<uint2>(tile + c.q_off[m] + (4 * (st & 1) + jj) * c.q_step);
+        if (FMT == 3)  // Q3_K: (LA, LB) of block 4 (st % 2) + jj, two blocks per 16-byte chunk
+            r.v[m][jj] = ldg<uint2>(tile + c.q_off[m] + (2 * (st & 1) + (jj >> 1)) * c.q_step + 8 * (jj & 1));
+        else
+            r.v[m][jj] = ldg<uint2>(tile + c.q_off[m] + (4 * (st & 1) + jj) * c.q_step);
     };
     auto load_h_one = [&](int st, BQuant& r, int m, int i) {
         const uint8_t* tile = c.b_rowgroup + (size_t)(st >> 1) * c.tile_bytes;
@@ -389,10 +405,26 @@ __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* s
         const uint32_t w = i16 < 4 ? h.x : i16 < 8 ? h.y : i16 < 12 ? h.z : h.w;
         return half_to_float(dbits) * (float)((int32_t)(w << (24 - 8 * (i16 & 3))) >> 24);
     };
-    // Q5_K, Q6_K: the two byte words of the lane's group in step s of
+    // Q3_K: d (sc - 32) of 16-weight sub-block i16 (0..15): header bytes 0-11
+    // the packed 6-bit scales (low four bits in byte i16, or the high nibble
+    // of byte i16 - 8; top two bits at bit 2 (i16 / 4) of byte 8 + i16 % 4),
+    // bytes 12-13 fp16 d
+    auto q3_scale = [](const uint4& h, int i16) {
+        const uint32_t lw = (i16 & 7) < 4 ? h.x : h.y;
+        const uint32_t low = (lw >> (8 * (i16 & 3) + (i16 < 8 ? 0 : 4))) & 0xFu;
+        const uint32_t top = (h.z >> (8 * (i16 & 3) + 2 * (i16 >> 2))) & 3u;
+        return half_to_float(h.w) * (float)((int)(low | (top << 4)) - 32);
+    };
+    // Q5_K, Q6_K, Q3_K: the two byte words of the lane's group in step s of
     // sub-block jj (group d = 2 (s % 2) + lane / 32)
     auto hq = [&](const BQuant& r, int m, int jj, int s, uint32_t w) {
         const int hsel = lane >> 5;
+        if (FMT == 3) {
+            const uint4 hv = r.h[m][0];
+            const uint32_t hb = jj == 0 ? hv.x : jj == 1 ? hv.y : jj == 2 ? hv.z : hv.w;
+            const int d = 2 * (s & 1) + hsel;
+            return q3_bytes(w, hb, 2 * hsel, (2 + d) & 3);
+        }
         if (FMT == 4) {
             const uint4 hv = r.h[m][0];
             const uint32_t hb = jj == 0 ? hv.x : jj == 1 ? hv.y : jj == 2 ? hv.z : hv.w;
@@ -422,7 +454,10 @@ __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* s
                 fb_next0[m] = mx4_frag(rb[0].v[m][0].x, mx_scale(hdr[m], 0));
             } else if (kHighBits) {
                 float ds, nc;
-                if (FMT == 4) {
+                if (FMT == 3) {
+                    ds = q3_scale(hdr[m], 0);
+                    nc = -4.0f * ds;
+                } else if (FMT == 4) {
                     hw0[m] = header_words(hdr[m]);
                     ds = hw0[m].d512 * (1.0f / 512.0f) * (float)(hw0[m].sc[0] & 0xFFu);
                     nc = -(hw0[m].dmin * (float)(hw0[m].mn[0] & 0xFFu));
@@ -483,6 +518,9 @@ __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* s
                         } else if (FMT == 5) {
                             a = q6_scale(hraw[m], draw[m], 2 * j + hf);
                             b = -32.0f * a;
+                        } else if (FMT == 3) {
+                            a = q3_scale(hraw[m], 2 * j + hf);
+                            b = -4.0f * a;
                         } else {
                             a = hw[m].d512 * (FMT == 4 ? 1.0f / 512.0f : 1.0f) *
                                 (float)((hw[m].sc[j >> 2] >> (8 * (j & 3))) & 0xFFu);
@@ -538,6 +576,9 @@ __device__ __forceinline__ void tile_gemm(const TileCtx& c, uint4* sA0, uint4* s
                         } else if (FMT == 5) {
                             dsv[m] = u == 0 ? q6_scale(hraw[m], draw[m], 8) : q6_scale(hdr[m], dq[m], 0);
                             ndv[m] = -32.0f * dsv[m];
+                        } else if (FMT == 3) {
+                            dsv[m] = u == 0 ? q3_scale(hraw[m], 8) : q3_scale(hdr[m], 0);
+                            ndv[m] = -4.0f * dsv[m];
                         } else if (FMT == 4 && u == 0) {
                             dsv[m] = hw[m].d512 * (1.0f / 512.0f) * (float)(hw[m].sc[1] & 0xFFu);
                             ndv[m] = -(hw[m].dmin * (float)(hw[m].mn[1] & 0xFFu));
@@ -719,13 +760,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // Per tile: Q4_K headers are 16 bytes per row (1 KB per matrix), MXFP4
     // scales 8 bytes per row (512 B per matrix); the quants of block j follow.
     // Q5_K / Q6_K tiles add high-bit chunks after the nibbles (9 KB per
-    // matrix in) and Q6_K the d row after those (13 KB per matrix in).
+    // matrix in) and Q6_K the d row after those (13 KB per matrix in).  Q3_K
+    // gate/up tiles (the mixed expert) hold two blocks' low-bit words per
+    // 16-byte chunk (from 2 KB) and the high-bit words from 10 KB; its down
+    // matrix is Q4_K, after the Q3_K gate/up section.
     const int hb = FMT == 2 ? 8 : 16;
-    const int gtile = FMT == 2 ? kMx4GateUpTile : FMT == 4 ? kQ5kGateUpTile : FMT == 5 ? kQ6kGateUpTile
-                                                                                        : kQ4kGateUpTile;
+    const int gtile = FMT == 2 ? kMx4GateUpTile : FMT == 3 ? kQ3kGateUpTile : FMT == 4 ? kQ5kGateUpTile
+                      : FMT == 5 ? kQ6kGateUpTile : kQ4kGateUpTile;
     const int dtile = FMT == 2 ? kMx4DownTile : FMT == 4 ? kQ5kDownTile : FMT == 5 ? kQ6kDownTile : kQ4kDownTile;
-    const size_t gu_bytes = FMT == 2 ? mx4_gateup_bytes(H, I) : FMT == 4 ? q5k_gateup_bytes(H, I)
-                            : FMT == 5 ? q6k_gateup_bytes(H, I) : q4k_gateup_bytes(H, I);
+    const size_t gu_bytes = FMT == 2 ? mx4_gateup_bytes(H, I) : FMT == 3 ? q3k_gateup_bytes(H, I)
+                            : FMT == 4 ? q5k_gateup_bytes(H, I) : FMT == 5 ? q6k_gateup_bytes(H, I)
+                                                                          : q4k_gateup_bytes(H, I);
     if (GATEUP) {
         const int fb = nt * kWaves + wave;
         c.b_rowgroup = wbase + (size_t)(fb >> 1) * (H / 256) * gtile;
@@ -733,8 +778,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             c.hdr_off[m] = m * 64 * hb + r * hb;
-            c.q_off[m] = 128 * hb + m * 1024 + r * 16 + 8 * hsel;
-            c.hb_off[m] = 9 * 2048 + m * 1024 + r * 16;
+            c.q_off[m] = FMT == 3 ? 2048 + m * 1024 + r * 16 : 128 * hb + m * 1024 + r * 16 + 8 * hsel;
+            c.hb_off[m] = (FMT == 3 ? 10240 : 9 * 2048) + m * 1024 + r * 16;
             c.d_off[m] = 13 * 2048 + 4 * r + 2 * m;
         }
         c.q_step = 2048;
@@ -900,10 +945,12 @@ hipError_t launch_ffn_prefill(const FfnArgs& a, hipStream_t s) {
     const int mgroups = (mt + 7) / 8;
     const int nt_gu = a.I / kGateUpFeatures, nt_dn = a.H / kDownColumns;
     auto gateup = a.format == 2   ? prefill_gemm_kernel<2, true>
+                  : a.format == 3 ? prefill_gemm_kernel<3, true>
                   : a.format == 4 ? prefill_gemm_kernel<4, true>
                   : a.format == 5 ? prefill_gemm_kernel<5, true>
                                   : prefill_gemm_kernel<1, true>;
     auto down = a.format == 2   ? prefill_gemm_kernel<2, false>
+                : a.format == 3 ? prefill_gemm_kernel<3, false>
                 : a.format == 4 ? prefill_gemm_kernel<4, false>
                 : a.format == 5 ? prefill_gemm_kernel<5, false>
                                 : prefill_gemm_kernel<1, false>;

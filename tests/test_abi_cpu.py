@@ -127,7 +127,7 @@ def test_ffn_q4k_rejects(kw, want, needle):
 def test_ffn_q8_0_rejects_prefill():
     st, msg = _ffn("moe_expert_ffn_q8_0", H=256, I=128, stride=Q.moe_expert_blob_bytes(Q.MOE_FMT_Q8_0, 256, 128) + 64,
                    path=Q.MOE_PATH_PREFILL, x_dtype=Q.MOE_BF16)
-    assert st == Q.MOE_ERR_UNSUPPORTED and "Q4_K, Q5_K, Q6_K and MXFP4" in msg
+    assert st == Q.MOE_ERR_UNSUPPORTED and "serves Q8_0" in msg
 
 
 def test_ffn_q4k_prefill_size_limits():

@@ -1,5 +1,5 @@
-"""Parity of the prefill path (bf16 MFMA grouped GEMM over Q4_K, MXFP4, Q5_K
-or Q6_K tiles) with the CPU oracle.
+"""Parity of the prefill path (bf16 MFMA grouped GEMM over Q4_K, MXFP4, Q5_K,
+Q6_K or Q3_K/Q4_K tiles) with the CPU oracle.
 
 Ids, slot offsets, active slots, permutation and host list: bit-exact on
 every row.  Outputs: per token row t, max_i |y_ti - y*_ti| <= 1e-2 *
@@ -54,10 +54,10 @@ def _prefill_case(wl, soe=None, S=None, pair_dtype=torch.bfloat16, y_dtype=torch
     return err
 
 
-@pytest.mark.parametrize("fmt", [F.Q4K, F.MXFP4, F.Q5K, F.Q6K], ids=["Q4_K", "MXFP4", "Q5_K", "Q6_K"])
+@pytest.mark.parametrize("fmt", [F.Q4K, F.MXFP4, F.Q5K, F.Q6K, F.Q3K_Q4K], ids=["Q4_K", "MXFP4", "Q5_K", "Q6_K", "Q3_K-Q4_K"])
 def test_prefill_qwen3_full_size(fmt):
     """4096 tokens, Zipf(1.0)-skewed loads over 128 experts, all resident."""
-    names = {F.MXFP4: "MXFP4", F.Q5K: "Q5_K", F.Q6K: "Q6_K"}
+    names = {F.MXFP4: "MXFP4", F.Q5K: "Q5_K", F.Q6K: "Q6_K", F.Q3K_Q4K: "Q3_K gate/up + Q4_K down"}
     wl = W.QWEN3_PREFILL if fmt == F.Q4K else dataclasses.replace(W.QWEN3_PREFILL, fmt=fmt,
                                                                   name=W.QWEN3_PREFILL.name + f", {names[fmt]} experts")
     say(wl.name)
@@ -67,7 +67,7 @@ def test_prefill_qwen3_full_size(fmt):
     assert _prefill_case(wl, sample=sample) <= PREFILL_TOL
 
 
-@pytest.mark.parametrize("fmt", [F.Q4K, F.MXFP4, F.Q5K, F.Q6K], ids=["Q4_K", "MXFP4", "Q5_K", "Q6_K"])
+@pytest.mark.parametrize("fmt", [F.Q4K, F.MXFP4, F.Q5K, F.Q6K, F.Q3K_Q4K], ids=["Q4_K", "MXFP4", "Q5_K", "Q6_K", "Q3_K-Q4_K"])
 @pytest.mark.parametrize("T,E,k,pd,yd", [
     (300, 16, 4, torch.bfloat16, torch.bfloat16),
     (129, 8, 2, torch.float32, torch.float32),
@@ -80,7 +80,7 @@ def test_prefill_small_layers(T, E, k, pd, yd, fmt):
     assert _prefill_case(wl, pair_dtype=pd, y_dtype=yd) <= PREFILL_TOL
 
 
-@pytest.mark.parametrize("fmt", [F.Q4K, F.MXFP4, F.Q5K, F.Q6K], ids=["Q4_K", "MXFP4", "Q5_K", "Q6_K"])
+@pytest.mark.parametrize("fmt", [F.Q4K, F.MXFP4, F.Q5K, F.Q6K, F.Q3K_Q4K], ids=["Q4_K", "MXFP4", "Q5_K", "Q6_K", "Q3_K-Q4_K"])
 def test_prefill_partial_residency(fmt):
     wl = W.Workload("prefill T200 E24 k3, 15 resident of 24", fmt, 768, 512, 24, 3, 200, x_bf16=True,
                     zipf_s=1.2, seed=5)
@@ -91,7 +91,7 @@ def test_prefill_partial_residency(fmt):
     assert _prefill_case(wl, soe=soe, S=17) <= PREFILL_TOL
 
 
-@pytest.mark.parametrize("fmt", [F.Q4K, F.MXFP4, F.Q5K, F.Q6K], ids=["Q4_K", "MXFP4", "Q5_K", "Q6_K"])
+@pytest.mark.parametrize("fmt", [F.Q4K, F.MXFP4, F.Q5K, F.Q6K, F.Q3K_Q4K], ids=["Q4_K", "MXFP4", "Q5_K", "Q6_K", "Q3_K-Q4_K"])
 def test_prefill_tile_boundaries(fmt):
     """One expert receives exactly 128, another 129, another 1 pair."""
     wl = W.Workload("prefill tile boundaries", fmt, 256, 256, 4, 1, 258, x_bf16=True, seed=7)
@@ -129,7 +129,7 @@ def _bf16_round(a: np.ndarray) -> np.ndarray:
     return F.bf16_bits_to_f32(F.to_bf16_bits(a.astype(np.float32))).astype(np.float64)
 
 
-@pytest.mark.parametrize("fmt", [F.Q4K, F.MXFP4, F.Q5K, F.Q6K], ids=["Q4_K", "MXFP4", "Q5_K", "Q6_K"])
+@pytest.mark.parametrize("fmt", [F.Q4K, F.MXFP4, F.Q5K, F.Q6K, F.Q3K_Q4K], ids=["Q4_K", "MXFP4", "Q5_K", "Q6_K", "Q3_K-Q4_K"])
 def test_prefill_equals_its_bf16_rounding_model(fmt):
     """The prefill arithmetic is the exact layer with three roundings: each
     dequantized weight to fp32 then bf16 (MXFP4 weights are bf16 values
@@ -145,16 +145,17 @@ def test_prefill_equals_its_bf16_rounding_model(fmt):
     got = run_device(device_layer(wl, blobs, soe, S, None, wl.T, Q.MOE_PATH_PREFILL, pair_dtype=torch.float32),
                      x, logits)
     H, I = wl.H, wl.I
-    gb = F.matrix_bytes(fmt, I, H)
+    fgu, fdn = (F.Q3K, F.Q4K) if fmt == F.Q3K_Q4K else (fmt, fmt)  # block types of gate/up and down
+    gb = F.matrix_bytes(fgu, I, H)
     xf = W.x_f64(wl, x)
     worst = 0.0
     for t in range(wl.T):
         for j in range(wl.k):
             e = int(got["ids"][t, j])
             b = blobs[e]
-            Wg = _bf16_round(O.dequant(fmt, b[:gb], I * H)).reshape(I, H)
-            Wu = _bf16_round(O.dequant(fmt, b[gb:2 * gb], I * H)).reshape(I, H)
-            Wd = _bf16_round(O.dequant(fmt, b[2 * gb:], H * I)).reshape(H, I)
+            Wg = _bf16_round(O.dequant(fgu, b[:gb], I * H)).reshape(I, H)
+            Wu = _bf16_round(O.dequant(fgu, b[gb:2 * gb], I * H)).reshape(I, H)
+            Wd = _bf16_round(O.dequant(fdn, b[2 * gb:], H * I)).reshape(H, I)
             g, u = Wg @ xf[t], Wu @ xf[t]
             hx = g / (1 + np.exp(-g)) * u
             h = _bf16_round(hx)
