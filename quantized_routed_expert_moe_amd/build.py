@@ -20,6 +20,9 @@ HOST_SO = os.path.join(HERE, "libqmoe_host.so")  # host leg + residency policy (
 
 SOURCES = ["abi.cpp", "route.hip", "batches.hip", "route_batches.hip", "ffn_decode.hip", "ffn_prefill.hip",
            "combine.hip"]
+# ffn_prefill.hip is compiled once more per block type with only that type's
+# GEMM kernels (QMOE_PREFILL_FMT), so the types compile in parallel.
+PREFILL_TYPES = [1, 2, 3, 4, 5]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -29,9 +32,11 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job) -> str:
+    src, defines = job if isinstance(job, tuple) else (job, ())
+    tag = "".join(f"_{d.split('=')[-1]}" for d in defines)
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + tag + ".o")
+    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
@@ -40,8 +45,9 @@ def _compile(src: str) -> str:
 
 def build(jobs: int = 8) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    jobs_list = [("ffn_prefill.hip", (f"QMOE_PREFILL_FMT={t}",)) for t in PREFILL_TYPES] + SOURCES
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(_compile, jobs_list))
     tmp = SO + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

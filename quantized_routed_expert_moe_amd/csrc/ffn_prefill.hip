@@ -82,6 +82,11 @@ static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // Upper bound of the tile count: sum over slots of ceil(n_s / 256).
 static int max_tiles(int P, int S) { return (P + kBM - 1) / kBM + std::min(S, P); }
 
+// This file is compiled once per block type with QMOE_PREFILL_FMT set (the
+// GEMM kernels of that type only, explicitly instantiated at the end of the
+// GEMM body) and once without it (everything else: workspace size, the tile
+// list, the launcher), so the types' GEMMs compile in parallel.
+#ifndef QMOE_PREFILL_FMT
 size_t prefill_workspace_bytes(int T, int k, int H, int I) {
     (void)H;
     const int P = T * k;
@@ -177,6 +182,8 @@ __global__ __launch_bounds__(1024) void prefill_tiles_kernel(const int32_t* __re
     }
     if (tid == 0) *ntiles = acc_base;
 }
+
+#endif  // !QMOE_PREFILL_FMT
 
 // ------------------------------------------------------------- helpers
 
@@ -921,6 +928,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
 }
 
+#ifdef QMOE_PREFILL_FMT
+template __global__ void prefill_gemm_kernel<QMOE_PREFILL_FMT, true>(const uint8_t* __restrict__, size_t, int, int, int, const uint16_t* __restrict__, int, int,
+                                         const int32_t* __restrict__, const int4* __restrict__,
+                                         const int32_t* __restrict__, void* __restrict__, int);
+template __global__ void prefill_gemm_kernel<QMOE_PREFILL_FMT, false>(const uint8_t* __restrict__, size_t, int, int, int, const uint16_t* __restrict__, int, int,
+                                         const int32_t* __restrict__, const int4* __restrict__,
+                                         const int32_t* __restrict__, void* __restrict__, int);
+#else
+// instantiated in the per-type objects
+#define QMOE_EXTERN_PREFILL(F)                                                                                     \
+    extern template __global__ void prefill_gemm_kernel<F, true>(const uint8_t* __restrict__, size_t, int, int, int, const uint16_t* __restrict__, int, int, \
+                                         const int32_t* __restrict__, const int4* __restrict__, \
+                                         const int32_t* __restrict__, void* __restrict__, int); \
+    extern template __global__ void prefill_gemm_kernel<F, false>(const uint8_t* __restrict__, size_t, int, int, int, const uint16_t* __restrict__, int, int, \
+                                         const int32_t* __restrict__, const int4* __restrict__, \
+                                         const int32_t* __restrict__, void* __restrict__, int);
+QMOE_EXTERN_PREFILL(1)
+QMOE_EXTERN_PREFILL(2)
+QMOE_EXTERN_PREFILL(3)
+QMOE_EXTERN_PREFILL(4)
+QMOE_EXTERN_PREFILL(5)
+#undef QMOE_EXTERN_PREFILL
+
 // ----------------------------------------------------------------- launch
 
 hipError_t launch_ffn_prefill(const FfnArgs& a, hipStream_t s) {
@@ -966,5 +996,7 @@ hipError_t launch_ffn_prefill(const FfnArgs& a, hipStream_t s) {
                  a.H, a.I, (const uint16_t*)h, a.T, a.k, a.perm_pair, tiles, ntiles, a.y_pairs, a.y_dtype);
     return hipGetLastError();
 }
+
+#endif  // QMOE_PREFILL_FMT
 
 }  // namespace qmoe
