@@ -263,7 +263,8 @@ moe_status moe_validate_slot_map(const int32_t* slot_of_expert, int E, int S);
  * S             slots, 1..MOE_MAX_EXPERTS (the S given to the batches call).
  * H, I          hidden and expert-intermediate sizes.
  * x             device, [T, H] row-major, x_dtype MOE_F32 or MOE_BF16.
- * T, k          as in the batches call.
+ * T, k          as in the batches call.  With T = 0 nothing is launched and
+ *               x, perm_pair and y_pairs may be NULL.
  * slot_offsets, active_slots, num_active, perm_pair
  *               device, outputs of moe_build_expert_batches for this T, k, S.
  * y_pairs       device, [T*k, H] of y_dtype, indexed by pair p.  Rows of

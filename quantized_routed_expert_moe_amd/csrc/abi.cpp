@@ -534,7 +534,8 @@ moe_status ffn_common(int format, const void* slot_pool, size_t slot_stride, int
     if (T < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "T = %d must be >= 0", T);
     if (k < 1 || k > MOE_MAX_TOPK) return fail(MOE_ERR_INVALID_ARGUMENT, "k = %d outside 1..%d", k, MOE_MAX_TOPK);
     if ((long long)T * k > kMaxPairs) return fail(MOE_ERR_INVALID_ARGUMENT, "T*k exceeds 2^24");
-    if (!slot_pool || !x || !slot_offsets || !active_slots || !num_active || !perm_pair || !y_pairs)
+    // (with T = 0 nothing is read or written: x, perm_pair and y_pairs may be NULL)
+    if (!slot_pool || !slot_offsets || !active_slots || !num_active || (T > 0 && (!x || !perm_pair || !y_pairs)))
         return fail(MOE_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
     if (!aligned16(slot_pool) || (slot_stride & 15u))
         return fail(MOE_ERR_INVALID_ARGUMENT, "slot_pool and slot_stride must be 16-byte aligned");

@@ -118,10 +118,20 @@ def _ffn(name, **kw):
     (dict(y_dtype=Q.MOE_BF16), Q.MOE_ERR_UNSUPPORTED, "decode path"),
     (dict(path=7), Q.MOE_ERR_INVALID_ARGUMENT, "bad path"),
     (dict(x_dtype=5), Q.MOE_ERR_INVALID_ARGUMENT, "bad x_dtype"),
+    (dict(x=None), Q.MOE_ERR_INVALID_ARGUMENT, "NULL"),
+    (dict(perm=None), Q.MOE_ERR_INVALID_ARGUMENT, "NULL"),
+    (dict(T=0, offs=None), Q.MOE_ERR_INVALID_ARGUMENT, "NULL"),
 ])
 def test_ffn_q4k_rejects(kw, want, needle):
     st, msg = _ffn("moe_expert_ffn_q4k", **kw)
     assert st == want and needle in msg, msg
+
+
+def test_ffn_with_no_tokens_takes_null_activations():
+    """T = 0: nothing is launched, so x, perm_pair and y_pairs may be NULL
+    (zero-size tensors have no storage); the call returns before any HIP call."""
+    st, msg = _ffn("moe_expert_ffn_q4k", T=0, x=None, perm=None, yp=None)
+    assert st == Q.MOE_OK, msg
 
 
 def test_ffn_q8_0_rejects_prefill():
