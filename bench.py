@@ -210,6 +210,16 @@ def main():
         cpu_s = time.time() - c0
         cpu = {"value": round(wl.T * n_done / cpu_s, 3), "unit": "tokens/s", "cores": O.threads(), "kind": "oracle",
                "sample": f"{n_done} steps of the same layer (T={wl.T}, fp64 oracle), {cpu_s:.1f} s wall"}
+        # the same oracle on one thread, for a third of the time
+        O.set_threads(1)
+        n1, c1 = 0, time.time()
+        while time.time() - c1 < args.cpu_seconds / 3:
+            i = n1 % nbatch
+            O.moe_layer(wl.fmt, blobs, wl.H, wl.I, xs[i].cpu().numpy().astype(np.float64), ls[i].cpu().numpy(), wl.k,
+                        wl.score, wl.renormalize, wl.scale)
+            n1 += 1
+        cpu["value_1_thread"] = round(wl.T * n1 / (time.time() - c1), 3)
+        O.set_threads(threads)
 
     if args.profile_copy:
         a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
