@@ -167,6 +167,24 @@ def test_workspace_sizes_are_monotone():
     assert Q.moe_ffn_workspace_size(Q.MOE_FMT_Q4K, 2, 8, 7000, 2048, Q.MOE_PATH_DECODE) == 0
 
 
+@pytest.mark.parametrize("fmt", [Q.MOE_FMT_Q4K, Q.MOE_FMT_MXFP4, Q.MOE_FMT_Q3K_Q4K, Q.MOE_FMT_Q5K, Q.MOE_FMT_Q6K])
+def test_prefill_workspace_for_every_prefill_format(fmt):
+    """Every format but Q8_0 has a prefill path: its prefill workspace is the
+    Q4_K one (bf16 h rows and the tile list do not depend on the block type),
+    and AUTO asks for the larger of the two paths'."""
+    T, k, H, I = 4096, 8, 2048, 768
+    pre = Q.moe_ffn_workspace_size(fmt, T, k, H, I, Q.MOE_PATH_PREFILL)
+    dec = Q.moe_ffn_workspace_size(fmt, T, k, H, I, Q.MOE_PATH_DECODE)
+    assert pre == Q.moe_ffn_workspace_size(Q.MOE_FMT_Q4K, T, k, H, I, Q.MOE_PATH_PREFILL) > 0
+    assert Q.moe_ffn_workspace_size(fmt, T, k, H, I, Q.MOE_PATH_AUTO) == max(pre, dec)
+
+
+def test_q8_0_has_no_prefill_workspace():
+    T, k, H, I = 4096, 8, 2048, 768
+    dec = Q.moe_ffn_workspace_size(Q.MOE_FMT_Q8_0, T, k, H, I, Q.MOE_PATH_DECODE)
+    assert Q.moe_ffn_workspace_size(Q.MOE_FMT_Q8_0, T, k, H, I, Q.MOE_PATH_AUTO) == dec
+
+
 @pytest.mark.parametrize("fmt,H,I", [(Q.MOE_FMT_Q4K, 512, 256), (Q.MOE_FMT_Q4K, 768, 512), (Q.MOE_FMT_Q8_0, 256, 128),
                                      (Q.MOE_FMT_Q8_0, 384, 256), (Q.MOE_FMT_MXFP4, 512, 256),
                                      (Q.MOE_FMT_MXFP4, 768, 512), (Q.MOE_FMT_Q3K_Q4K, 512, 256),
