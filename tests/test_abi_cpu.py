@@ -348,3 +348,14 @@ def test_timer_misuse():
     assert st == Q.MOE_ERR_INVALID_ARGUMENT and "not armed" in msg
     st, msg = _call("moe_timer_begin", 99, 4)
     assert st == Q.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_product_path_fails_loudly_without_the_library(monkeypatch):
+    """No libqmoe.so, no computation: the first call raises (there is no CPU
+    fallback anywhere in the package)."""
+    monkeypatch.setattr(Q, "_lib", None)
+    monkeypatch.setattr(Q, "LIB_PATH", "/nonexistent/libqmoe.so")
+    with pytest.raises(ImportError, match="not built"):
+        Q.lib()
+    with pytest.raises(ImportError, match="not built"):
+        Q.moe_expert_blob_bytes(Q.MOE_FMT_Q4K, 512, 256)
