@@ -57,6 +57,7 @@ def test_route_matches_oracle(wl):
     (1, 1, 1, 0, True, 1.0),
     (3, 256, 64, 0, True, 1.0),    # two-level rank: every key a candidate
     (4, 200, 33, 1, True, 2.5),    # two-level rank, ragged last group
+    (2, 1024, 64, 1, True, 2.5),   # both maxima: MOE_MAX_EXPERTS and MOE_MAX_TOPK
 ])
 def test_route_shapes(T, E, k, score, renorm, scale):
     say(f"route T={T} E={E} k={k} score={score} renorm={renorm}")
@@ -535,6 +536,20 @@ def test_decode_q6k_many_tokens_partial_residency():
                             got["host_weight"], threads=THREADS)
     full = run_oracle(wl, blobs, x, logits, np.arange(wl.E, dtype=np.int32), None)
     assert rel_max_err(got["y"] + y_host, full["y"]) <= DECODE_TOL
+
+
+@pytest.mark.parametrize("fmt", [F.Q4K, F.Q6K])
+def test_decode_layer_every_expert_per_token(fmt):
+    """k = E = 64 (MOE_MAX_TOPK): every token goes to every expert, 3 tokens,
+    so every slot holds three pairs (one chunk of two tokens and a remainder)
+    and the combine sums 64 terms per token; 40 of the 64 experts resident."""
+    wl = W.Workload("small layer, k = E = 64, T 3", fmt, 256 if fmt == F.Q4K else 512, 256, 64, 64, 3)
+    say(wl.name)
+    soe = np.full(64, -1, dtype=np.int32)
+    soe[np.random.default_rng(2).permutation(64)[:40]] = np.arange(40, dtype=np.int32)
+    got, want, soe, S = _layer_case(wl, soe=soe, S=40, path=Q.MOE_PATH_DECODE)
+    _check_layer(wl, got, want, soe, S)
+    assert got["host_count"] == 3 * 24
 
 
 def test_host_list_written_into_pinned_memory():
