@@ -80,6 +80,20 @@ def test_prefill_small_layers(T, E, k, pd, yd, fmt):
     assert _prefill_case(wl, pair_dtype=pd, y_dtype=yd) <= PREFILL_TOL
 
 
+def test_prefill_at_the_slot_limit():
+    """E = S = 1024 (MOE_MAX_EXPERTS, one tile-list thread per slot): 640
+    tokens x k 8 spread over every expert, so most slots hold a handful of
+    rows in one ragged tile and a few (Zipf head) several tiles."""
+    wl = W.Workload("prefill T640 E1024 k8, all resident", F.Q4K, 256, 256, 1024, 8, 640, x_bf16=True,
+                    zipf_s=1.0, seed=9)
+    say(wl.name)
+    F.set_num_threads(THREADS)
+    # fp32 y_pairs and y: the case is about the tile list at 1024 slots; the
+    # error left is the bf16 model's own (weights and h rounded once each),
+    # about 5e-3 of a row's largest output at this short K
+    assert _prefill_case(wl, pair_dtype=torch.float32, y_dtype=torch.float32) <= PREFILL_TOL
+
+
 @pytest.mark.parametrize("fmt", [F.Q4K, F.MXFP4, F.Q5K, F.Q6K, F.Q3K_Q4K], ids=["Q4_K", "MXFP4", "Q5_K", "Q6_K", "Q3_K-Q4_K"])
 def test_prefill_partial_residency(fmt):
     wl = W.Workload("prefill T200 E24 k3, 15 resident of 24", fmt, 768, 512, 24, 3, 200, x_bf16=True,
