@@ -249,7 +249,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "q4_k weights dequantized to fp16, fp16 x fp16 dot products, fp32 accumulate",
+        "dtype": "f16",
+        "arithmetic": "q4_k weights dequantized to fp16, fp16 x fp16 dot products, fp32 accumulate",
         "data": "synthetic (seeded N(0,0.02) weights quantized to Q4_K, N(0,1) activations and gate logits)",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "top_k": wl.k, "I": wl.I,
                    "routing": "softmax, renormalised over top-k", "weights": "Q4_K", "resident": "all 128",
