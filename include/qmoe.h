@@ -245,6 +245,31 @@ moe_status moe_pack_expert(int format, const void* canonical, void* packed, int 
 /* Host, synchronous: packed blob -> canonical blob (the exact inverse). */
 moe_status moe_unpack_expert(int format, const void* packed, void* canonical, int H, int I);
 
+/* Host, synchronous: one matrix of an expert, or its gate/up pair, from its
+ * canonical blocks to the device layout of the slot blobs above, so that a
+ * caller holding the matrices apart (e.g. as separate tensors of a model
+ * file) can build a slot: blob = pack(W_gate | W_up, interleave 1) followed
+ * by pack(W_down, interleave 0), the bytes moe_pack_expert writes for the
+ * whole expert (card experts in their stored quantization: bloomery README
+ * 0.3.1, "Status (0.3.1)" table, "Quant types" row; shared experts in Q8_0:
+ * README of 2026-09-24).
+ *
+ * canonical      host: gate_up_interleave = 1: W_gate [rows, cols] then W_up
+ *                [rows, cols] (rows = I, cols = H); 0: one matrix [rows,
+ *                cols] (W_down: rows = H, cols = I).  Rows row-major, blocks
+ *                along cols.
+ * device_layout  host, the same number of bytes (Q4_K 144 per 256 weights,
+ *                Q8_0 34 per 32): with interleave 1 the gate/up tiles (64
+ *                features x one block group, the gate rows then the up rows
+ *                of the same features, as the fused SwiGLU reads them), with
+ *                0 the single-matrix tiles.  Not overlapping `canonical`.
+ * rows, cols     rows a multiple of 64; cols a multiple of 256 (Q4_K) or 128
+ *                (Q8_0).  Otherwise MOE_ERR_UNSUPPORTED.
+ * Returns MOE_OK, MOE_ERR_INVALID_ARGUMENT (NULL, overlap, interleave not 0
+ * or 1) or MOE_ERR_UNSUPPORTED; nothing is written on failure. */
+moe_status moe_pack_q4k(const void* canonical, void* device_layout, int rows, int cols, int gate_up_interleave);
+moe_status moe_pack_q8_0(const void* canonical, void* device_layout, int rows, int cols, int gate_up_interleave);
+
 /* Host: checks that every value is -1 or in [0, S) and that no slot is used
  * twice.  E in 1..MOE_MAX_EXPERTS, S in 0..E. */
 moe_status moe_validate_slot_map(const int32_t* slot_of_expert, int E, int S);
@@ -315,20 +340,24 @@ moe_status moe_expert_ffn_q6k(const void* slot_pool, size_t slot_stride, int S, 
                               int path, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- combine
- * y[t] = sum over j < k, in j order, of [slot_of_expert[id] >= 0] *
- * topk_w[t,j] * y_pairs[t*k+j]  (+ y_shared[t] if y_shared is not NULL).
- * Non-resident pairs contribute exactly 0 on the card; the host leg adds
- * them (bloomery README of 2026-09-24: experts split between card and host).
+ * y[t] = sum over j < k, in j order, of [resident(t,j)] * topk_w[t,j] *
+ * y_pairs[t*k+j]  (+ y_shared[t] if y_shared is not NULL), where pair (t, j)
+ * is resident iff slot_of_expert[topk_ids[t,j]] is in [0, S): the rule of
+ * moe_build_expert_batches, so a pair is either in a slot's batch and added
+ * here, or on the host list and left out here, never both.  Non-resident
+ * pairs contribute exactly 0 on the card; the host leg adds them (bloomery
+ * README of 2026-09-24: experts split between card and host).
  *
  * y_pairs   device, [T*k, H], y_pairs_dtype.
  * topk_ids, topk_w, slot_of_expert (E entries): device, as above.
+ * S         slots, 0..E (the S of the batches call).
  * y_shared  device, fp32 [T, H], or NULL.
  * y         device, [T, H], y_dtype (MOE_F32 or MOE_BF16, round to nearest even).
  * H % 8 == 0.  Accumulation in fp32.
  */
 moe_status moe_combine(const void* y_pairs, int y_pairs_dtype, const int32_t* topk_ids, const float* topk_w,
-                       const int32_t* slot_of_expert, int E, const float* y_shared, int T, int k, int H, void* y,
-                       int y_dtype, void* stream);
+                       const int32_t* slot_of_expert, int E, int S, const float* y_shared, int T, int k, int H,
+                       void* y, int y_dtype, void* stream);
 
 /* ------------------------------------------------------------ stage timers
  * Diagnostics: one hipEvent pair per launch of a stage, attached to the

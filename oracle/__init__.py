@@ -56,8 +56,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_batches.argtypes = [vp, vp, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
         L.oracle_batches.restype = i32
         L.oracle_expert_ffn.argtypes = [i32, vp, i32, i32, vp, vp]
-        L.oracle_moe_layer.argtypes = [i32, vp, i32, i32, i32, i32, vp, vp, i32, i32, i32, f64, vp, i32, vp, i32,
-                                       vp, vp, vp, vp]
+        L.oracle_moe_layer.argtypes = [i32, vp, i32, i32, i32, i32, vp, vp, i32, i32, i32, f64, vp, i32, i32, vp,
+                                       i32, vp, vp, vp, vp]
         L.oracle_moe_layer.restype = i32
         L.oracle_set_threads.argtypes = [i32]
         L.oracle_threads.restype = i32
@@ -150,9 +150,10 @@ def expert_ffn(fmt: int, blob: np.ndarray, H: int, I: int, x: np.ndarray) -> np.
 def moe_layer(fmt: int, expert_blobs, H: int, I: int, x: np.ndarray, logits: np.ndarray, k: int,
               score: int = SOFTMAX, renormalize: bool = True, scale: float = 1.0,
               slot_of_expert: np.ndarray | None = None, shared_blob: np.ndarray | None = None,
-              shared_fmt: int = Q8_0, I_shared: int = 0, want_pairs: bool = False) -> dict:
+              shared_fmt: int = Q8_0, I_shared: int = 0, want_pairs: bool = False, S: int | None = None) -> dict:
     """The whole layer in fp64.  expert_blobs: sequence of E canonical blobs
-    (None for an expert that is never selected) or a 2-D uint8 array [E, bytes]."""
+    (None for an expert that is never selected) or a 2-D uint8 array [E, bytes].
+    A pair is on the card iff its expert's slot is in [0, S) (S defaults to E)."""
     x = np.ascontiguousarray(x, dtype=np.float64)
     logits = np.ascontiguousarray(logits, dtype=np.float32)
     T, E = logits.shape
@@ -173,8 +174,9 @@ def moe_layer(fmt: int, expert_blobs, H: int, I: int, x: np.ndarray, logits: np.
     ids = np.empty((T, k), dtype=np.int32)
     w = np.empty((T, k), dtype=np.float64)
     yp = np.empty((T * k, H), dtype=np.float64) if want_pairs else None
+    S = E if S is None else int(S)
     rc = lib().oracle_moe_layer(fmt, ctypes.cast(ptrs, ctypes.c_void_p), E, H, I, T, _p(x), _p(logits), k, score,
-                                int(bool(renormalize)), float(scale), _p(soe), shared_fmt, _p(sb), int(I_shared),
+                                int(bool(renormalize)), float(scale), _p(soe), S, shared_fmt, _p(sb), int(I_shared),
                                 _p(y), _p(ids), _p(w), _p(yp))
     if rc != 0:
         raise ValueError(f"oracle_moe_layer failed ({rc})")

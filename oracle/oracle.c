@@ -404,8 +404,9 @@ void oracle_expert_ffn(int fmt, const uint8_t* blob, int H, int I, const double*
 
 int oracle_moe_layer(int fmt, const uint8_t* const* expert_blob, int E, int H, int I, int T, const double* x,
                      const float* logits, int k, int score, int renormalize, double scale,
-                     const int32_t* slot_of_expert, int shared_fmt, const uint8_t* shared_blob, int I_shared,
+                     const int32_t* slot_of_expert, int S, int shared_fmt, const uint8_t* shared_blob, int I_shared,
                      double* y, int32_t* ids, double* w, double* y_pairs) {
+    if (S < 0 || S > E) return -1;
     if (oracle_route(logits, T, E, k, score, renormalize, scale, ids, w) != 0) return -1;
     double* yp = (double*)malloc((size_t)H * sizeof(double));
     for (int t = 0; t < T; ++t) {
@@ -415,7 +416,7 @@ int oracle_moe_layer(int fmt, const uint8_t* const* expert_blob, int E, int H, i
         for (int j = 0; j < k; ++j) {
             int64_t p = (int64_t)t * k + j;
             int id = ids[p];
-            int resident = slot_of_expert[id] >= 0;
+            int resident = slot_of_expert[id] >= 0 && slot_of_expert[id] < S;
             if (!resident && g_defect != D_IGNORE_RESIDENCY) {
                 if (y_pairs) memset(y_pairs + p * H, 0, (size_t)H * sizeof(double));
                 continue;

@@ -28,7 +28,8 @@
  *               ids.  softmax: p = softmax over all E, w_j = p_j / sum p_sel
  *               (renormalised) or p_j; sigmoid: s = 1/(1+e^-l),
  *               w_j = s_j / sum s_sel or s_j; then w *= scale.
- *   residency   pair (t, j) is on the card iff slot_of_expert[id] >= 0.
+ *   residency   pair (t, j) is on the card iff 0 <= slot_of_expert[id] < S
+ *               (S = the card's slot count); every other pair is the host's.
  *   batches     for each slot ascending, its resident pairs in ascending
  *               pair index p = t*k + j; non-resident pairs in ascending p
  *               form the host list.
@@ -83,7 +84,7 @@ void oracle_expert_ffn(int fmt, const uint8_t* blob, int H, int I, const double*
  * NULL, receives [T*k, H] with zero rows for non-resident pairs. */
 int oracle_moe_layer(int fmt, const uint8_t* const* expert_blob, int E, int H, int I, int T, const double* x,
                      const float* logits, int k, int score, int renormalize, double scale,
-                     const int32_t* slot_of_expert, int shared_fmt, const uint8_t* shared_blob, int I_shared,
+                     const int32_t* slot_of_expert, int S, int shared_fmt, const uint8_t* shared_blob, int I_shared,
                      double* y, int32_t* ids, double* w, double* y_pairs);
 
 void oracle_set_threads(int n);

@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
         L.moe_packed_blob_bytes.restype = sz
         L.moe_pack_expert.argtypes = [i32, vp, vp, i32, i32]
         L.moe_unpack_expert.argtypes = [i32, vp, vp, i32, i32]
+        L.moe_pack_q4k.argtypes = [vp, vp, i32, i32, i32]
+        L.moe_pack_q8_0.argtypes = [vp, vp, i32, i32, i32]
         L.moe_validate_slot_map.argtypes = [vp, i32, i32]
         L.moe_ffn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
         L.moe_ffn_workspace_size.restype = sz
@@ -72,11 +74,11 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_ffn_q3k_q4k.argtypes = ffn
         L.moe_expert_ffn_q5k.argtypes = ffn
         L.moe_expert_ffn_q6k.argtypes = ffn
-        L.moe_combine.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, i32, i32, vp, i32, vp]
+        L.moe_combine.argtypes = [vp, i32, vp, vp, vp, i32, i32, vp, i32, i32, i32, vp, i32, vp]
         L.moe_timer_begin.argtypes = [i32, i32]
         L.moe_timer_end.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
         for name in ("moe_route_topk", "moe_build_expert_batches", "moe_route_and_batch", "moe_count_routes",
-                     "moe_pack_expert", "moe_unpack_expert",
+                     "moe_pack_expert", "moe_unpack_expert", "moe_pack_q4k", "moe_pack_q8_0",
                      "moe_validate_slot_map", "moe_expert_ffn_q4k", "moe_expert_ffn_q8_0", "moe_expert_ffn_mxfp4",
                      "moe_expert_ffn_q3k_q4k", "moe_expert_ffn_q5k", "moe_expert_ffn_q6k",
                      "moe_combine",
@@ -267,6 +269,27 @@ def moe_unpack_expert(fmt: int, packed: np.ndarray, H: int, I: int) -> np.ndarra
     return out
 
 
+def _pack_matrix(fn, block_w: int, block_b: int, canonical: np.ndarray, rows: int, cols: int,
+                 gate_up_interleave: bool) -> np.ndarray:
+    n = rows * cols * (2 if gate_up_interleave else 1) // block_w * block_b
+    canonical = np.ascontiguousarray(canonical, dtype=np.uint8)
+    if canonical.nbytes != n:
+        raise ValueError(f"canonical matrix data has {canonical.nbytes} bytes, expected {n}")
+    out = np.empty(n, dtype=np.uint8)
+    _check(fn(canonical.ctypes.data, out.ctypes.data, rows, cols, int(bool(gate_up_interleave))))
+    return out
+
+
+def moe_pack_q4k(canonical: np.ndarray, rows: int, cols: int, gate_up_interleave: bool) -> np.ndarray:
+    """Device layout of one Q4_K matrix [rows, cols] (or of W_gate | W_up with gate_up_interleave)."""
+    return _pack_matrix(lib().moe_pack_q4k, 256, 144, canonical, rows, cols, gate_up_interleave)
+
+
+def moe_pack_q8_0(canonical: np.ndarray, rows: int, cols: int, gate_up_interleave: bool) -> np.ndarray:
+    """Device layout of one Q8_0 matrix [rows, cols] (or of W_gate | W_up with gate_up_interleave)."""
+    return _pack_matrix(lib().moe_pack_q8_0, 32, 34, canonical, rows, cols, gate_up_interleave)
+
+
 def moe_validate_slot_map(slot_of_expert: np.ndarray, S: int) -> None:
     soe = np.ascontiguousarray(slot_of_expert, dtype=np.int32)
     _check(lib().moe_validate_slot_map(soe.ctypes.data, soe.size, S))
@@ -331,12 +354,12 @@ def moe_expert_ffn(fmt: int):
             MOE_FMT_Q6K: moe_expert_ffn_q6k}[fmt]
 
 
-def moe_combine(y_pairs, topk_ids, topk_w, slot_of_expert, y_shared, y, stream=None):
+def moe_combine(y_pairs, topk_ids, topk_w, slot_of_expert, S: int, y_shared, y, stream=None):
     T, k = topk_ids.shape
     H = y.shape[1]
     E = slot_of_expert.numel()
     _check(lib().moe_combine(_dev(y_pairs, _fb(), "y_pairs"), _dtype_code(y_pairs), _dev(topk_ids, _i32(), "topk_ids"),
-                             _dev(topk_w, _f32(), "topk_w"), _dev(slot_of_expert, _i32(), "slot_of_expert"), E,
+                             _dev(topk_w, _f32(), "topk_w"), _dev(slot_of_expert, _i32(), "slot_of_expert"), E, S,
                              _dev(y_shared, _f32(), "y_shared"), T, k, H, _dev(y, _fb(), "y"), _dtype_code(y),
                              _stream(stream)))
 

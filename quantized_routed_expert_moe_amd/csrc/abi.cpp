@@ -131,18 +131,15 @@ void nibbles_unpack(const uint8_t* src, uint8_t* q) {
     }
 }
 
+// The Q4_K gate/up section: canonical W_gate [I, H] at offset 0 and W_up
+// right after it, packed tiles at offset 0 (PACK: canonical -> packed;
+// otherwise packed -> canonical).
 template <bool PACK>
-void q4k_down_walk(const uint8_t* in, uint8_t* out, int H, int I, size_t canon_base, size_t base);
-
-// Move every field of a blob between the canonical and the packed layout
-// (PACK: canonical -> packed; otherwise packed -> canonical).
-template <bool PACK>
-void q4k_walk(const uint8_t* in, uint8_t* out, int H, int I) {
+void q4k_gateup_walk(const uint8_t* in, uint8_t* out, int H, int I) {
     const size_t rbH = (size_t)H / 256 * 144;
     const size_t gbytes = (size_t)I * rbH;
     const int SBH = H / 256;
     uint8_t q[32];
-    // gate/up section
     for (int rg = 0; rg < I / 64; ++rg)
         for (int sb = 0; sb < SBH; ++sb) {
             const size_t tile = ((size_t)rg * SBH + sb) * qmoe::kQ4kGateUpTile;
@@ -167,7 +164,17 @@ void q4k_walk(const uint8_t* in, uint8_t* out, int H, int I) {
                 }
             }
         }
-    q4k_down_walk<PACK>(in, out, H, I, 2 * gbytes, qmoe::q4k_gateup_bytes(H, I));
+}
+
+template <bool PACK>
+void q4k_down_walk(const uint8_t* in, uint8_t* out, int H, int I, size_t canon_base, size_t base);
+
+// Move every field of a blob between the canonical and the packed layout
+// (PACK: canonical -> packed; otherwise packed -> canonical).
+template <bool PACK>
+void q4k_walk(const uint8_t* in, uint8_t* out, int H, int I) {
+    q4k_gateup_walk<PACK>(in, out, H, I);
+    q4k_down_walk<PACK>(in, out, H, I, 2 * (size_t)I * (H / 256 * 144), qmoe::q4k_gateup_bytes(H, I));
 }
 
 // The Q4_K down matrix: canonical rows at canon_base, packed tiles at base.
@@ -199,56 +206,70 @@ void q4k_down_walk(const uint8_t* in, uint8_t* out, int H, int I, size_t canon_b
         }
 }
 
+// One Q8_0 34-byte block <-> (2-byte scale, two 16-byte halves), quants
+// offset by 128.
+void q8_block(const uint8_t* canon, uint8_t* scale, uint8_t* lo, uint8_t* hi, bool pack) {
+    if (pack) {
+        memcpy(scale, canon, 2);
+        for (int e = 0; e < 16; ++e) lo[e] = canon[2 + e] ^ 0x80;
+        for (int e = 0; e < 16; ++e) hi[e] = canon[18 + e] ^ 0x80;
+    } else {
+        uint8_t* dst = const_cast<uint8_t*>(canon);
+        memcpy(dst, scale, 2);
+        for (int e = 0; e < 16; ++e) dst[2 + e] = lo[e] ^ 0x80;
+        for (int e = 0; e < 16; ++e) dst[18 + e] = hi[e] ^ 0x80;
+    }
+}
+
+// The Q8_0 gate/up section: canonical W_gate [I, H] at offset 0 and W_up
+// right after it, packed tiles at offset 0.
 template <bool PACK>
-void q8_walk(const uint8_t* in, uint8_t* out, int H, int I) {
-    const size_t rbH = (size_t)H / 32 * 34, rbI = (size_t)I / 32 * 34;
+void q8_gateup_walk(const uint8_t* in, uint8_t* out, int H, int I) {
+    const size_t rbH = (size_t)H / 32 * 34;
     const size_t gbytes = (size_t)I * rbH;
-    const int BH = H / 128, BI = I / 128;
-    // one 34-byte block <-> (2-byte scale, two 16-byte halves), quants offset by 128
-    auto move = [](const uint8_t* src_blk, uint8_t* scale, uint8_t* lo, uint8_t* hi, uint8_t* dst_blk, bool pack) {
-        if (pack) {
-            memcpy(scale, src_blk, 2);
-            for (int e = 0; e < 16; ++e) lo[e] = src_blk[2 + e] ^ 0x80;
-            for (int e = 0; e < 16; ++e) hi[e] = src_blk[18 + e] ^ 0x80;
-        } else {
-            memcpy(dst_blk, scale, 2);
-            for (int e = 0; e < 16; ++e) dst_blk[2 + e] = lo[e] ^ 0x80;
-            for (int e = 0; e < 16; ++e) dst_blk[18 + e] = hi[e] ^ 0x80;
-        }
-    };
+    const int BH = H / 128;
+    uint8_t* dev = PACK ? out : const_cast<uint8_t*>(in);
+    const uint8_t* canon_base = PACK ? in : out;
     for (int rg = 0; rg < I / 64; ++rg)
         for (int bg = 0; bg < BH; ++bg) {
-            const size_t tile = ((size_t)rg * BH + bg) * qmoe::kQ8GateUpTile;
+            uint8_t* tile = dev + ((size_t)rg * BH + bg) * qmoe::kQ8GateUpTile;
             for (int r = 0; r < 64; ++r) {
                 const size_t row = (size_t)rg * 64 + r;
                 for (int mat = 0; mat < 2; ++mat)
                     for (int jj = 0; jj < 4; ++jj) {
-                        const size_t canon = mat * gbytes + row * rbH + (size_t)(bg * 4 + jj) * 34;
-                        uint8_t* sc = (PACK ? out : const_cast<uint8_t*>(in)) + tile + mat * 512 + r * 8 + jj * 2;
-                        uint8_t* lo =
-                            (PACK ? out : const_cast<uint8_t*>(in)) + tile + 1024 + mat * 2048 + jj * 4096 + r * 16;
-                        uint8_t* hi = lo + 1024;
-                        if (PACK) move(in + canon, sc, lo, hi, nullptr, true);
-                        else move(nullptr, sc, lo, hi, out + canon, false);
+                        uint8_t* lo = tile + 1024 + mat * 2048 + jj * 4096 + r * 16;
+                        q8_block(canon_base + mat * gbytes + row * rbH + (size_t)(bg * 4 + jj) * 34,
+                                 tile + mat * 512 + r * 8 + jj * 2, lo, lo + 1024, PACK);
                     }
             }
         }
-    const size_t base = qmoe::q8_gateup_bytes(H, I);
+}
+
+// The Q8_0 down matrix [H, I]: canonical rows at canon_base, packed tiles at base.
+template <bool PACK>
+void q8_down_walk(const uint8_t* in, uint8_t* out, int H, int I, size_t canon_base, size_t base) {
+    const size_t rbI = (size_t)I / 32 * 34;
+    const int BI = I / 128;
+    uint8_t* dev = PACK ? out : const_cast<uint8_t*>(in);
+    const uint8_t* canon = (PACK ? in : out) + canon_base;
     for (int rg = 0; rg < H / 64; ++rg)
         for (int bg = 0; bg < BI; ++bg) {
-            const size_t tile = base + ((size_t)rg * BI + bg) * qmoe::kQ8DownTile;
+            uint8_t* tile = dev + base + ((size_t)rg * BI + bg) * qmoe::kQ8DownTile;
             for (int r = 0; r < 64; ++r) {
                 const size_t row = (size_t)rg * 64 + r;
                 for (int jj = 0; jj < 4; ++jj) {
-                    const size_t canon = 2 * gbytes + row * rbI + (size_t)(bg * 4 + jj) * 34;
-                    uint8_t* sc = (PACK ? out : const_cast<uint8_t*>(in)) + tile + r * 8 + jj * 2;
-                    uint8_t* lo = (PACK ? out : const_cast<uint8_t*>(in)) + tile + 512 + jj * 2048 + r * 16;
-                    uint8_t* hi = lo + 1024;
-                    if (PACK) move(in + canon, sc, lo, hi, nullptr, true);
-                    else move(nullptr, sc, lo, hi, out + canon, false);
+                    uint8_t* lo = tile + 512 + jj * 2048 + r * 16;
+                    q8_block(canon + row * rbI + (size_t)(bg * 4 + jj) * 34, tile + r * 8 + jj * 2, lo, lo + 1024,
+                             PACK);
                 }
             }
         }
+}
+
+template <bool PACK>
+void q8_walk(const uint8_t* in, uint8_t* out, int H, int I) {
+    q8_gateup_walk<PACK>(in, out, H, I);
+    q8_down_walk<PACK>(in, out, H, I, 2 * (size_t)I * (H / 32 * 34), qmoe::q8_gateup_bytes(H, I));
 }
 
 // MXFP4: one 17-byte block (E8M0 scale, element i < 16 in the low nibble of
@@ -524,6 +545,35 @@ void q6k_walk(const uint8_t* in, uint8_t* out, int H, int I) {
     section(qmoe::q6k_gateup_bytes(H, I), 1, H / 64, I / 256, rbI, 2 * gbytes, 0);
 }
 
+// One matrix, or the gate/up pair, of a blob (the pieces moe_pack_expert
+// puts together).
+moe_status pack_matrix(int format, const void* canonical, void* packed, int rows, int cols, int gate_up_interleave) {
+    const char* name = format == MOE_FMT_Q4K ? "moe_pack_q4k" : "moe_pack_q8_0";
+    const int cb = format == MOE_FMT_Q4K ? 256 : 128;
+    if (!canonical || !packed) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: NULL pointer", name);
+    if (gate_up_interleave != 0 && gate_up_interleave != 1)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "%s: gate_up_interleave = %d is not 0 or 1", name, gate_up_interleave);
+    if (rows <= 0 || cols <= 0 || rows % 64 || cols % cb)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: rows must be a positive multiple of 64 and cols of %d (rows = %d, "
+                                         "cols = %d)", name, cb, rows, cols);
+    if ((long long)rows * cols > (1ll << 31))
+        return fail(MOE_ERR_UNSUPPORTED, "%s: rows*cols = %lld too large", name, (long long)rows * cols);
+    const size_t w = (size_t)rows * cols * (gate_up_interleave ? 2 : 1);
+    const size_t n = format == MOE_FMT_Q4K ? w / 256 * 144 : w / 32 * 34;
+    const uint8_t* in = static_cast<const uint8_t*>(canonical);
+    uint8_t* out = static_cast<uint8_t*>(packed);
+    if (in < out + n && out < in + n) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: buffers overlap", name);
+    memset(out, 0, n);
+    if (format == MOE_FMT_Q4K) {
+        if (gate_up_interleave) q4k_gateup_walk<true>(in, out, cols, rows);
+        else q4k_down_walk<true>(in, out, rows, cols, 0, 0);
+    } else {
+        if (gate_up_interleave) q8_gateup_walk<true>(in, out, cols, rows);
+        else q8_down_walk<true>(in, out, rows, cols, 0, 0);
+    }
+    return MOE_OK;
+}
+
 moe_status ffn_common(int format, const void* slot_pool, size_t slot_stride, int S, int H, int I, const void* x,
                       int x_dtype, int T, int k, const int32_t* slot_offsets, const int32_t* active_slots,
                       const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype, int path,
@@ -738,6 +788,14 @@ moe_status moe_unpack_expert(int format, const void* packed, void* canonical, in
     return MOE_OK;
 }
 
+moe_status moe_pack_q4k(const void* canonical, void* device_layout, int rows, int cols, int gate_up_interleave) {
+    return pack_matrix(MOE_FMT_Q4K, canonical, device_layout, rows, cols, gate_up_interleave);
+}
+
+moe_status moe_pack_q8_0(const void* canonical, void* device_layout, int rows, int cols, int gate_up_interleave) {
+    return pack_matrix(MOE_FMT_Q8_0, canonical, device_layout, rows, cols, gate_up_interleave);
+}
+
 moe_status moe_validate_slot_map(const int32_t* slot_of_expert, int E, int S) {
     if (!slot_of_expert) return fail(MOE_ERR_INVALID_ARGUMENT, "slot_of_expert is NULL");
     if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_ERR_INVALID_ARGUMENT, "E = %d outside 1..%d", E, MOE_MAX_EXPERTS);
@@ -812,10 +870,11 @@ moe_status moe_expert_ffn_q6k(const void* slot_pool, size_t slot_stride, int S, 
 }
 
 moe_status moe_combine(const void* y_pairs, int y_pairs_dtype, const int32_t* topk_ids, const float* topk_w,
-                       const int32_t* slot_of_expert, int E, const float* y_shared, int T, int k, int H, void* y,
-                       int y_dtype, void* stream) {
+                       const int32_t* slot_of_expert, int E, int S, const float* y_shared, int T, int k, int H,
+                       void* y, int y_dtype, void* stream) {
     if (T < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "T = %d must be >= 0", T);
     if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_ERR_INVALID_ARGUMENT, "E = %d outside 1..%d", E, MOE_MAX_EXPERTS);
+    if (S < 0 || S > E) return fail(MOE_ERR_INVALID_ARGUMENT, "S = %d outside 0..E (%d)", S, E);
     if (k < 1 || k > MOE_MAX_TOPK) return fail(MOE_ERR_INVALID_ARGUMENT, "k = %d outside 1..%d", k, MOE_MAX_TOPK);
     if (H <= 0 || H % 8) return fail(MOE_ERR_UNSUPPORTED, "H = %d must be a positive multiple of 8", H);
     if ((long long)T * k > kMaxPairs) return fail(MOE_ERR_INVALID_ARGUMENT, "T*k exceeds 2^24");
@@ -825,8 +884,8 @@ moe_status moe_combine(const void* y_pairs, int y_pairs_dtype, const int32_t* to
         return fail(MOE_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
     if (T > 0 && (!aligned16(y_pairs) || !aligned16(y) || (y_shared && !aligned16(y_shared))))
         return fail(MOE_ERR_INVALID_ARGUMENT, "y_pairs, y and y_shared must be 16-byte aligned");
-    hipError_t e = qmoe::launch_combine(y_pairs, y_pairs_dtype, topk_ids, topk_w, slot_of_expert, E, y_shared, T, k,
-                                        H, y, y_dtype, (hipStream_t)stream);
+    hipError_t e = qmoe::launch_combine(y_pairs, y_pairs_dtype, topk_ids, topk_w, slot_of_expert, E, S, y_shared, T,
+                                        k, H, y, y_dtype, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     return MOE_OK;
 }

@@ -25,7 +25,7 @@ __device__ __forceinline__ void load8(const void* base, int dtype, size_t idx, f
 
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ yp, int yp_dtype,
                                                       const int32_t* __restrict__ ids, const float* __restrict__ w,
-                                                      const int32_t* __restrict__ soe, int E,
+                                                      const int32_t* __restrict__ soe, int E, int S,
                                                       const float* __restrict__ ysh, int T, int k, int H,
                                                       void* __restrict__ y, int y_dtype) {
     // The slot map goes to LDS, loaded together with the first batch of pair
@@ -56,7 +56,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
 #pragma unroll
         for (int jj = 0; jj < kBatch; ++jj) {
             const int id = idb[jj];
-            const bool res = (j0 + jj < k) && id >= 0 && id < E && sm[id] >= 0;
+            // resident iff the slot is in [0, S): the batching kernels' rule
+            const bool res = (j0 + jj < k) && id >= 0 && id < E && (unsigned)sm[id] < (unsigned)S;
 #pragma unroll
             for (int i = 0; i < 8; ++i) acc[i] = res ? fmaf(wj[jj], v[jj][i], acc[i]) : acc[i];
         }
@@ -89,13 +90,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
 }
 
 hipError_t launch_combine(const void* y_pairs, int yp_dtype, const int32_t* ids, const float* w,
-                          const int32_t* soe, int E, const float* y_shared, int T, int k, int H, void* y, int y_dtype,
-                          hipStream_t s) {
+                          const int32_t* soe, int E, int S, const float* y_shared, int T, int k, int H, void* y,
+                          int y_dtype, hipStream_t s) {
     if (T == 0) return hipSuccess;
     dim3 grid((H / 8 + 255) / 256, T);
     const StageEvents ev = timer_events(kStageCombine);
-    launch_timed(combine_kernel, grid, dim3(256), 0, s, ev.start, ev.stop, y_pairs, yp_dtype, ids, w, soe, E, y_shared,
-                 T, k, H, y, y_dtype);
+    launch_timed(combine_kernel, grid, dim3(256), 0, s, ev.start, ev.stop, y_pairs, yp_dtype, ids, w, soe, E, S,
+                 y_shared, T, k, H, y, y_dtype);
     return hipGetLastError();
 }
 

@@ -210,7 +210,7 @@ size_t prefill_workspace_bytes(int T, int k, int H, int I);
 hipError_t launch_ffn_prefill(const FfnArgs& a, hipStream_t s);  // Q4_K or MXFP4
 
 hipError_t launch_combine(const void* y_pairs, int yp_dtype, const int32_t* ids, const float* w,
-                          const int32_t* slot_of_expert, int E, const float* y_shared, int T, int k, int H, void* y,
-                          int y_dtype, hipStream_t s);
+                          const int32_t* slot_of_expert, int E, int S, const float* y_shared, int T, int k, int H,
+                          void* y, int y_dtype, hipStream_t s);
 
 }  // namespace qmoe

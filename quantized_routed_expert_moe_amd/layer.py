@@ -126,5 +126,5 @@ class MoELayer:
         if spec.I_shared:
             main.wait_event(self.sh_join)
             y_shared = self.y_shared
-        moe_combine(self.y_pairs, self.ids, self.w, self.slot_of_expert, y_shared, self.y, stream)
+        moe_combine(self.y_pairs, self.ids, self.w, self.slot_of_expert, self.S, y_shared, self.y, stream)
         return self.y

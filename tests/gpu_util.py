@@ -88,12 +88,13 @@ def run_device(layer: MoELayer, x: np.ndarray, logits: np.ndarray) -> dict:
 
 
 def run_oracle(w: W.Workload, blobs: np.ndarray, x: np.ndarray, logits: np.ndarray, soe: np.ndarray,
-               shared: np.ndarray | None, want_pairs: bool = False) -> dict:
+               shared: np.ndarray | None, want_pairs: bool = False, S: int | None = None) -> dict:
+    """The oracle's layer; a pair is on the card iff its slot is in [0, S) (S defaults to E)."""
     O.set_threads(THREADS)
     ids_needed = set(np.argsort(-logits, axis=1, kind="stable")[:, :w.k].ravel().tolist())
     expert_list = [blobs[e] if e in ids_needed else None for e in range(w.E)]
     return O.moe_layer(w.fmt, expert_list, w.H, w.I, W.x_f64(w, x), logits, w.k, w.score, w.renormalize, w.scale,
-                       soe, shared, F.Q8_0, w.I_shared, want_pairs)
+                       soe, shared, F.Q8_0, w.I_shared, want_pairs, S=S)
 
 
 def rel_max_err(got: np.ndarray, want: np.ndarray) -> float:

@@ -154,10 +154,13 @@ def test_ffn_q8_0_rejects_shape():
 
 
 def test_combine_rejects():
-    st, msg = _call("moe_combine", FAKE, 0, FAKE, FAKE, FAKE, 8, None, 4, 2, 252, FAKE, 0, None)
+    st, msg = _call("moe_combine", FAKE, 0, FAKE, FAKE, FAKE, 8, 8, None, 4, 2, 252, FAKE, 0, None)
     assert st == Q.MOE_ERR_UNSUPPORTED and "multiple of 8" in msg
-    st, msg = _call("moe_combine", FAKE, 3, FAKE, FAKE, FAKE, 8, None, 4, 2, 256, FAKE, 0, None)
+    st, msg = _call("moe_combine", FAKE, 3, FAKE, FAKE, FAKE, 8, 8, None, 4, 2, 256, FAKE, 0, None)
     assert st == Q.MOE_ERR_INVALID_ARGUMENT
+    # S must lie in 0..E: the residency rule (slot in [0, S)) needs it
+    st, msg = _call("moe_combine", FAKE, 0, FAKE, FAKE, FAKE, 8, 9, None, 4, 2, 256, FAKE, 0, None)
+    assert st == Q.MOE_ERR_INVALID_ARGUMENT and "S = 9" in msg
 
 
 def test_workspace_sizes_are_monotone():
@@ -359,3 +362,32 @@ def test_product_path_fails_loudly_without_the_library(monkeypatch):
         Q.lib()
     with pytest.raises(ImportError, match="not built"):
         Q.moe_expert_blob_bytes(Q.MOE_FMT_Q4K, 512, 256)
+
+
+@pytest.mark.parametrize("fmt,H,I", [(Q.MOE_FMT_Q4K, 512, 256), (Q.MOE_FMT_Q4K, 768, 512), (Q.MOE_FMT_Q8_0, 256, 128),
+                                     (Q.MOE_FMT_Q8_0, 384, 256)])
+def test_per_matrix_pack_builds_the_expert_blob(fmt, H, I):
+    """moe_pack_q4k / moe_pack_q8_0 of W_gate | W_up (interleaved) followed by W_down (not) give
+    exactly the bytes moe_pack_expert writes for the whole expert, through the C ABI."""
+    blob = F.expert_blob(fmt, 7, 0, 1, H, I)
+    wb, bb = (256, 144) if fmt == Q.MOE_FMT_Q4K else (32, 34)
+    gate_up = blob[:2 * I * H // wb * bb]
+    down = blob[2 * I * H // wb * bb:]
+    pack = Q.moe_pack_q4k if fmt == Q.MOE_FMT_Q4K else Q.moe_pack_q8_0
+    got = np.concatenate([pack(gate_up, I, H, True), pack(down, H, I, False)])
+    assert np.array_equal(got, Q.moe_pack_expert(fmt, blob, H, I))
+
+
+def test_per_matrix_pack_rejects():
+    buf = np.zeros(1 << 16, dtype=np.uint8)
+    out = np.zeros(1 << 16, dtype=np.uint8)
+    st, msg = _call("moe_pack_q4k", buf.ctypes.data, out.ctypes.data, 64, 200, 0)
+    assert st == Q.MOE_ERR_UNSUPPORTED and "cols of 256" in msg
+    st, msg = _call("moe_pack_q8_0", buf.ctypes.data, out.ctypes.data, 32, 128, 1)
+    assert st == Q.MOE_ERR_UNSUPPORTED and "multiple of 64" in msg
+    st, msg = _call("moe_pack_q4k", buf.ctypes.data, out.ctypes.data, 64, 256, 2)
+    assert st == Q.MOE_ERR_INVALID_ARGUMENT and "gate_up_interleave" in msg
+    st, msg = _call("moe_pack_q8_0", None, out.ctypes.data, 64, 128, 0)
+    assert st == Q.MOE_ERR_INVALID_ARGUMENT
+    st, msg = _call("moe_pack_q4k", buf.ctypes.data, buf.ctypes.data + 16, 64, 256, 0)
+    assert st == Q.MOE_ERR_INVALID_ARGUMENT and "overlap" in msg

@@ -5,6 +5,8 @@ the host list) must match bit for bit.  Routing weights: |w - w*| <= 1e-6 *
 max(1, scale).  Decode outputs: max |y - y*| <= 2e-3 * max |y*| over the
 whole [T, H] output (fp16 activations, fp32 accumulation).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -14,7 +16,7 @@ import oracle as O
 from oracle import residency as OR
 import quantized_routed_expert_moe_amd as Q
 from fixtures import workloads as W
-from tests.gpu_util import THREADS, device_layer, rel_max_err, run_device, run_oracle, say
+from tests.gpu_util import THREADS, device_layer, pack_pool, rel_max_err, run_device, run_oracle, say
 
 pytestmark = pytest.mark.gpu
 
@@ -317,7 +319,7 @@ def _layer_case(wl, blobs=None, soe=None, S=None, T=None, path=Q.MOE_PATH_AUTO, 
     shared = W.shared_blob(wl)
     layer = device_layer(wl, blobs, soe, S, shared, T, path, host_list_pinned=host_list_pinned)
     got = run_device(layer, x, logits)
-    want = run_oracle(wl, blobs, x, logits, soe, shared, want_pairs=True)
+    want = run_oracle(wl, blobs, x, logits, soe, shared, want_pairs=True, S=S)
     return got, want, soe, S
 
 
@@ -351,7 +353,7 @@ def test_decode_layer_matches_oracle(wl):
     got, want, soe, S = _layer_case(wl)
     _check_layer(wl, got, want, soe, S)
     # every resident pair's own output, too
-    res = [p for p in range(wl.T * wl.k) if soe[want["ids"].ravel()[p]] >= 0]
+    res = [p for p in range(wl.T * wl.k) if 0 <= soe[want["ids"].ravel()[p]] < S]
     assert rel_max_err(got["y_pairs"][res], want["y_pairs"][res]) <= DECODE_TOL
 
 
@@ -388,6 +390,64 @@ def test_dsv3_partial_residency(dsv3_blobs):
     err = rel_max_err(got["y"] + y_host, full["y"])
     say(f"  card + host leg vs all experts served: {err:.2e}")
     assert err <= DECODE_TOL
+
+
+def test_dsv3_disjoint_halves_add_up(dsv3_blobs):
+    """The single-GPU stand-in for an expert-parallel split: the DeepSeek-V3-
+    shaped layer at T = 2 with the even experts resident (map A, shared
+    expert included) and with the odd ones (map B, no shared expert) adds up
+    to the layer with every expert resident, y(A) + y(B) = y(A u B), and each
+    half matches the oracle at its own map.  One slot pool (slot = expert id)
+    serves the three maps."""
+    wl = W.DSV3_DECODE_T2
+    wl_b = dataclasses.replace(wl, I_shared=0)
+    x, logits = W.x_of(wl), W.logits_of(wl)
+    pool = pack_pool(wl.fmt, dsv3_blobs, wl.H, wl.I, list(range(wl.E)), wl.E)
+    ids = np.arange(wl.E, dtype=np.int32)
+    soe_a = np.where(ids % 2 == 0, ids, -1).astype(np.int32)
+    soe_b = np.where(ids % 2 == 1, ids, -1).astype(np.int32)
+    shared = W.shared_blob(wl)
+    out = {}
+    for name, w_, soe, sh in (("all", wl, ids, shared), ("A", wl, soe_a, shared), ("B", wl_b, soe_b, None)):
+        say(f"  map {name}")
+        layer = device_layer(w_, dsv3_blobs, soe, wl.E, sh, wl.T, Q.MOE_PATH_DECODE, pool=pool)
+        out[name] = run_device(layer, x, logits)
+        del layer
+    torch.cuda.empty_cache()
+    sel = out["all"]["ids"].ravel()
+    assert (sel % 2 == 0).any() and (sel % 2 == 1).any(), "both halves must hold selected experts"
+    err = rel_max_err(out["A"]["y"] + out["B"]["y"], out["all"]["y"])
+    say(f"  y(A) + y(B) vs y(A u B): {err:.2e}")
+    assert err <= DECODE_TOL
+    for name, w_, soe, sh in (("A", wl, soe_a, shared), ("B", wl_b, soe_b, None)):
+        want = run_oracle(w_, dsv3_blobs, x, logits, soe, sh, S=wl.E)
+        _check_layer(w_, out[name], want, soe, wl.E)
+
+
+def test_slot_values_beyond_s_go_to_the_host():
+    """A slot-map value of S or more is not a slot: the pair goes to the host
+    list and adds nothing on the card, in the batching and the combine alike
+    (the oracle's rule 0 <= slot < S).  Qwen3-shaped layer at T = 2 with 64
+    slots: experts 0..63 in slots 0..63, experts 64..127 mapped to their own
+    id (>= S), so about half the routed pairs carry such values."""
+    wl = W.QWEN3_DECODE_T2
+    S = 64
+    soe = np.arange(wl.E, dtype=np.int32)
+    say(wl.name + ", 64 slots, slot values up to 127")
+    blobs = W.expert_blobs(wl)
+    pool = pack_pool(wl.fmt, blobs, wl.H, wl.I, list(range(S)), S)
+    x, logits = W.x_of(wl), W.logits_of(wl)
+    layer = device_layer(wl, blobs, soe, S, None, wl.T, Q.MOE_PATH_DECODE, pool=pool)
+    got = run_device(layer, x, logits)
+    want = run_oracle(wl, blobs, x, logits, soe, None, S=S)
+    assert (got["ids"] >= S).any() and (got["ids"] < S).any()
+    _check_layer(wl, got, want, soe, S)
+    assert sorted(got["host_expert"].tolist()) == sorted(e for e in got["ids"].ravel().tolist() if e >= S)
+    # the same layer with those experts marked -1 gives the same outputs, bit for bit
+    soe_m = np.where(soe < S, soe, -1).astype(np.int32)
+    layer_m = device_layer(wl, blobs, soe_m, S, None, wl.T, Q.MOE_PATH_DECODE, pool=pool)
+    got_m = run_device(layer_m, x, logits)
+    assert np.array_equal(got_m["y"], got["y"])
 
 
 def test_dsv3_experts_many_tokens_per_slot(dsv3_blobs):

@@ -62,9 +62,27 @@ def test_prefill_qwen3_full_size(fmt):
                                                                   name=W.QWEN3_PREFILL.name + f", {names[fmt]} experts")
     say(wl.name)
     F.set_num_threads(THREADS)
-    rng = np.random.default_rng(0)
-    sample = np.sort(rng.choice(wl.T, size=96, replace=False))
+    sample = _covering_sample(wl, 320)
     assert _prefill_case(wl, sample=sample) <= PREFILL_TOL
+
+
+def _covering_sample(wl, n_rows: int) -> np.ndarray:
+    """Rows whose outputs the oracle checks at full size: for every expert the
+    first and the last row routed to it (a slot's pairs are in row order, so
+    these sit in its first and its last, ragged, M tile), then seeded random
+    rows up to n_rows.  Every expert's weights are thus compared."""
+    ids, _ = O.route(W.logits_of(wl), wl.k, wl.score, wl.renormalize, wl.scale)
+    rows = set()
+    for e in range(wl.E):
+        r = np.nonzero((ids == e).any(axis=1))[0]
+        if r.size:
+            rows.update((int(r[0]), int(r[-1])))
+    rng = np.random.default_rng(0)
+    rest = rng.permutation(np.setdiff1d(np.arange(wl.T), sorted(rows)))
+    sample = np.sort(np.concatenate([np.array(sorted(rows), dtype=np.int64), rest[:max(0, n_rows - len(rows))]]))
+    covered = set(np.unique(ids[sample]).tolist())
+    assert covered == set(np.unique(ids).tolist()) and len(covered) == wl.E, "sample misses an expert"
+    return sample
 
 
 @pytest.mark.parametrize("fmt", [F.Q4K, F.MXFP4, F.Q5K, F.Q6K, F.Q3K_Q4K], ids=["Q4_K", "MXFP4", "Q5_K", "Q6_K", "Q3_K-Q4_K"])

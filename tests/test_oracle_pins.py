@@ -223,6 +223,36 @@ def pin_disjoint_halves() -> bool:
     return ok
 
 
+def pin_slot_beyond_s_is_host() -> bool:
+    """Residency is 0 <= slot < S: a slot-map value of S or more puts the pair
+    on the host exactly as -1 does.  Brute force over all experts with the
+    mask [0 <= slot < S], dense matrices, and the same host list from the
+    batches as for -1."""
+    rng = np.random.default_rng(47)
+    E, H, I, T, k, S = 6, 256, 256, 4, 3, 3
+    experts, _, _, x, lg = _layer_case(O.Q4K, rng, E, H, I, T, k)
+    blobs = [b for b, _ in experts]
+    soe = np.array([0, 5, 1, -1, 2, 3], dtype=np.int32)  # experts 1 and 5 hold slots >= S
+    out = O.moe_layer(O.Q4K, blobs, H, I, x, lg, k, slot_of_expert=soe, S=S)
+    order = np.argsort(-lg, axis=1, kind="stable")
+    p = softmax(lg.astype(np.float64), axis=1)
+    want = np.zeros((T, H))
+    for t in range(T):
+        sel = order[t, :k]
+        z = p[t, sel].sum()
+        for e in sel:
+            if 0 <= soe[e] < S:
+                want[t] += p[t, e] / z * _dense_ffn(*experts[e][1], x[t])
+    ok = bool(np.allclose(out["y"], want, rtol=1e-11, atol=1e-11 * np.abs(want).max()))
+    as_host = soe.copy()
+    as_host[as_host >= S] = -1
+    ok &= bool(np.array_equal(O.moe_layer(O.Q4K, blobs, H, I, x, lg, k, slot_of_expert=as_host, S=S)["y"], out["y"]))
+    b1, b2 = O.batches(out["ids"], out["w"], E, soe, S), O.batches(out["ids"], out["w"], E, as_host, S)
+    ok &= all(np.array_equal(b1[key], b2[key]) for key in b1)
+    ok &= bool(np.isin([1, 5], order[:, :k]).any())  # the case exercises the rule
+    return ok
+
+
 def pin_host_leg_completion() -> bool:
     """The card's partial y plus the host list's pairs, served by the same FFN, is the all-resident y."""
     rng = np.random.default_rng(37)
@@ -272,6 +302,7 @@ PINS = {
     "layer_brute_softmax_partial": lambda: pin_layer_brute_force(O.SOFTMAX, True),
     "layer_brute_sigmoid_full": lambda: pin_layer_brute_force(O.SIGMOID, False),
     "disjoint_halves": pin_disjoint_halves,
+    "slot_beyond_s_is_host": pin_slot_beyond_s_is_host,
     "host_leg_completion": pin_host_leg_completion,
     "shared_is_forced_expert": pin_shared_is_forced_expert,
     "zero_input": pin_zero_input,
@@ -306,6 +337,7 @@ DEFECTS = [
     (11, "encoder_round_trip"),
     (12, "disjoint_halves"),               # residency ignored in the combine
     (12, "layer_brute_softmax_partial"),
+    (12, "slot_beyond_s_is_host"),
     (13, "golden_blocks"),                 # MXFP4 elements as consecutive nibble pairs
     (13, "ffn_dense_mxfp4"),
     (13, "encoder_round_trip"),
