@@ -377,6 +377,11 @@ moe_status moe_combine(const void* y_pairs, int y_pairs_dtype, const int32_t* to
 #define MOE_STAGE_COUNT 9
 moe_status moe_timer_begin(int stage, int capacity);
 moe_status moe_timer_end(int stage, double* total_ms, int* launches);
+/* While the stage is armed: waits for its last recorded event and writes the
+ * kernel time of each of the first min(launches, capacity) timed launches,
+ * in the order they were enqueued, into ms_each; *launches = the number
+ * timed so far.  The timer stays armed (moe_timer_end releases it). */
+moe_status moe_timer_read(int stage, float* ms_each, int capacity, int* launches);
 
 #ifdef __cplusplus
 }

@@ -77,12 +77,13 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.argtypes = [vp, i32, vp, vp, vp, i32, i32, vp, i32, i32, i32, vp, i32, vp]
         L.moe_timer_begin.argtypes = [i32, i32]
         L.moe_timer_end.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
+        L.moe_timer_read.argtypes = [i32, vp, i32, ctypes.POINTER(ctypes.c_int)]
         for name in ("moe_route_topk", "moe_build_expert_batches", "moe_route_and_batch", "moe_count_routes",
                      "moe_pack_expert", "moe_unpack_expert", "moe_pack_q4k", "moe_pack_q8_0",
                      "moe_validate_slot_map", "moe_expert_ffn_q4k", "moe_expert_ffn_q8_0", "moe_expert_ffn_mxfp4",
                      "moe_expert_ffn_q3k_q4k", "moe_expert_ffn_q5k", "moe_expert_ffn_q6k",
                      "moe_combine",
-                     "moe_timer_begin", "moe_timer_end"):
+                     "moe_timer_begin", "moe_timer_end", "moe_timer_read"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -457,6 +458,14 @@ def moe_residency_plan(score, slot_of_expert, max_swaps: int, margin: int = 0) -
 
 def moe_timer_begin(stage: int, capacity: int) -> None:
     _check(lib().moe_timer_begin(stage, capacity))
+
+
+def moe_timer_read(stage: int, capacity: int) -> np.ndarray:
+    """Kernel milliseconds of each launch timed so far (the timer stays armed)."""
+    out = np.zeros(max(int(capacity), 1), dtype=np.float32)
+    n = ctypes.c_int(0)
+    _check(lib().moe_timer_read(stage, out.ctypes.data, int(capacity), ctypes.byref(n)))
+    return out[:min(n.value, int(capacity))].copy()
 
 
 def moe_timer_end(stage: int) -> tuple[float, int]:

@@ -574,10 +574,12 @@ moe_status pack_matrix(int format, const void* canonical, void* packed, int rows
     return MOE_OK;
 }
 
-moe_status ffn_common(int format, const void* slot_pool, size_t slot_stride, int S, int H, int I, const void* x,
-                      int x_dtype, int T, int k, const int32_t* slot_offsets, const int32_t* active_slots,
-                      const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype, int path,
-                      void* ws, size_t ws_bytes, void* stream) {
+// Every check of an expert-FFN call but those of the workspace; on success
+// *need is the workspace the call needs and *resolved its path.
+moe_status ffn_check(int format, const void* slot_pool, size_t slot_stride, int S, int H, int I, const void* x,
+                     int x_dtype, int T, int k, const int32_t* slot_offsets, const int32_t* active_slots,
+                     const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype, int path,
+                     size_t* need, int* resolved) {
     moe_status st = check_shape(format, H, I);
     if (st != MOE_OK) return st;
     if (S < 1 || S > MOE_MAX_EXPERTS) return fail(MOE_ERR_INVALID_ARGUMENT, "S = %d outside 1..%d", S, MOE_MAX_EXPERTS);
@@ -597,10 +599,10 @@ moe_status ffn_common(int format, const void* slot_pool, size_t slot_stride, int
     if (path < MOE_PATH_AUTO || path > MOE_PATH_PREFILL) return fail(MOE_ERR_INVALID_ARGUMENT, "bad path %d", path);
     if (!aligned16(x) || !aligned16(y_pairs)) return fail(MOE_ERR_INVALID_ARGUMENT, "x and y_pairs must be 16-byte aligned");
     const int p = resolve_path(format, T, x_dtype, path);
-    size_t need;
+    *resolved = p;
     if (p == MOE_PATH_DECODE) {
         if (y_dtype != MOE_F32) return fail(MOE_ERR_UNSUPPORTED, "the decode path writes MOE_F32 y_pairs");
-        need = qmoe::decode_workspace_bytes(T, k, H, I);
+        *need = qmoe::decode_workspace_bytes(T, k, H, I);
     } else {
         if (!has_prefill(format))
             return fail(MOE_ERR_UNSUPPORTED, "the prefill path is implemented for Q4_K, Q5_K, Q6_K, MXFP4 and "
@@ -612,8 +614,20 @@ moe_status ffn_common(int format, const void* slot_pool, size_t slot_stride, int
         if ((long long)T * H * 2 > 0xFFFFFFFFLL || P * I * 2 > 0xFFFFFFFFLL || (P + 255) / 256 + 1024 > 0xFFFF)
             return fail(MOE_ERR_UNSUPPORTED, "prefill path limits: T*H*2 and T*k*I*2 below 4 GiB, T*k below %d",
                         (0xFFFF - 1024) * 256);
-        need = qmoe::prefill_workspace_bytes(T, k, H, I);
+        *need = qmoe::prefill_workspace_bytes(T, k, H, I);
     }
+    return MOE_OK;
+}
+
+moe_status ffn_common(int format, const void* slot_pool, size_t slot_stride, int S, int H, int I, const void* x,
+                      int x_dtype, int T, int k, const int32_t* slot_offsets, const int32_t* active_slots,
+                      const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype, int path,
+                      void* ws, size_t ws_bytes, void* stream) {
+    size_t need = 0;
+    int p = MOE_PATH_DECODE;
+    moe_status st = ffn_check(format, slot_pool, slot_stride, S, H, I, x, x_dtype, T, k, slot_offsets, active_slots,
+                              num_active, perm_pair, y_pairs, y_dtype, path, &need, &p);
+    if (st != MOE_OK) return st;
     if (ws_bytes < need)
         return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, %zu needed", ws_bytes, need);
     if (need > 0 && !ws) return fail(MOE_ERR_INVALID_ARGUMENT, "workspace pointer is NULL");
@@ -914,6 +928,22 @@ moe_status moe_timer_begin(int stage, int capacity) {
     t.capacity = capacity;
     t.used = 0;
     t.armed.store(1);
+    return MOE_OK;
+}
+
+moe_status moe_timer_read(int stage, float* ms_each, int capacity, int* launches) {
+    if (stage < 0 || stage >= qmoe::kStageCount) return fail(MOE_ERR_INVALID_ARGUMENT, "bad stage %d", stage);
+    if (!launches || (capacity > 0 && !ms_each) || capacity < 0)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "bad output buffer");
+    std::lock_guard<std::mutex> lk(g_timer_mu);
+    StageTimer& t = g_timer[stage];
+    if (!t.armed.load()) return fail(MOE_ERR_INVALID_ARGUMENT, "stage %d timer not armed", stage);
+    hipError_t err = hipSuccess;
+    if (t.used > 0) err = hipEventSynchronize(t.stop[t.used - 1]);
+    const int n = std::min(t.used, capacity);
+    for (int i = 0; i < n && err == hipSuccess; ++i) err = hipEventElapsedTime(&ms_each[i], t.start[i], t.stop[i]);
+    *launches = t.used;
+    if (err != hipSuccess) return hip_fail(err, "stage timer");
     return MOE_OK;
 }
 

@@ -104,15 +104,19 @@ class MoELayer:
             self.sh_fork = torch.cuda.Event()
             self.sh_join = torch.cuda.Event()
 
-    def forward(self, x: torch.Tensor, logits: torch.Tensor, stream=None, slot_pool: torch.Tensor | None = None):
+    def forward(self, x: torch.Tensor, logits: torch.Tensor, stream=None, slot_pool: torch.Tensor | None = None,
+                shared_pool: torch.Tensor | None = None):
+        """slot_pool / shared_pool: another pool of the same layout for this
+        call (e.g. one of several copies a benchmark rotates through)."""
         spec, T = self.spec, x.shape[0]
         assert T == self.T_max, "buffers are sized for T_max rows"
         pool = self.slot_pool if slot_pool is None else slot_pool
+        sh_pool = self.shared_pool if shared_pool is None else shared_pool
         main = torch.cuda.current_stream() if stream is None else stream
         if spec.I_shared:
             self.sh_fork.record(main)
             self.sh_stream.wait_event(self.sh_fork)
-            moe_expert_ffn_q8_0(self.shared_pool, self.sh_stride, 1, spec.H, spec.I_shared, x, 1, self.sh_offsets,
+            moe_expert_ffn_q8_0(sh_pool, self.sh_stride, 1, spec.H, spec.I_shared, x, 1, self.sh_offsets,
                                 self.sh_active, self.sh_num, self.sh_perm, self.y_shared, MOE_PATH_DECODE, self.sh_ws,
                                 self.sh_stream)
             self.sh_join.record(self.sh_stream)

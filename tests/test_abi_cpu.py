@@ -391,3 +391,4 @@ def test_per_matrix_pack_rejects():
     assert st == Q.MOE_ERR_INVALID_ARGUMENT
     st, msg = _call("moe_pack_q4k", buf.ctypes.data, buf.ctypes.data + 16, 64, 256, 0)
     assert st == Q.MOE_ERR_INVALID_ARGUMENT and "overlap" in msg
+

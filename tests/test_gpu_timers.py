@@ -92,3 +92,25 @@ def test_timer_counts_nothing_without_launches():
     lg = np.zeros((0, wl.E), dtype=np.float32)
     out, _ = _timed(layer, x, lg, (STAGE_GATEUP,))
     assert out[STAGE_GATEUP] == (0.0, 0)
+
+
+def test_timer_read_gives_each_launch():
+    """moe_timer_read: one positive time per launch, in launch order, whose
+    sum is the total moe_timer_end returns; reading leaves the timer armed."""
+    wl = W.Workload("small Q4_K layer (H512 E8 k2 I256 T4)", F.Q4K, 512, 256, 8, 2, 4)
+    soe, S = W.slot_map(wl)
+    layer = device_layer(wl, W.expert_blobs(wl), soe, S, None, wl.T, Q.MOE_PATH_DECODE)
+    xd, ld = to_dev_x(W.x_of(wl)), torch.from_numpy(W.logits_of(wl)).cuda()
+    layer.forward(xd, ld)
+    torch.cuda.synchronize()
+    Q.moe_timer_begin(STAGE_GATEUP, 2 * N)
+    for _ in range(N):
+        layer.forward(xd, ld)
+    each = Q.moe_timer_read(STAGE_GATEUP, 2 * N)
+    assert each.shape == (N,) and (each > 0).all()
+    layer.forward(xd, ld)  # still armed: one more launch is timed
+    again = Q.moe_timer_read(STAGE_GATEUP, 2 * N)
+    ms, n = Q.moe_timer_end(STAGE_GATEUP)
+    assert n == N + 1 and again.shape == (N + 1,)
+    assert np.array_equal(again[:N], each)
+    assert abs(float(again.astype(np.float64).sum()) - ms) <= 1e-5 * ms
