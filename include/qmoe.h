@@ -339,6 +339,28 @@ moe_status moe_expert_ffn_q6k(const void* slot_pool, size_t slot_stride, int S, 
                               const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype,
                               int path, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------ allocation-free FFN
+ * For callers that cannot allocate device memory (code under hipGraph
+ * capture that must not call hipMalloc, tight serving loops, harnesses that
+ * forbid allocation): moe_expert_ffn_q4k without the workspace arguments.
+ * Its workspace is a file-scope device array of MOE_NOALLOC_SCRATCH_BYTES
+ * inside the library, one per GPU, set up on the first call on that GPU and
+ * held until the process ends; the call itself allocates nothing.
+ *   - Arguments, results and errors as moe_expert_ffn_q4k (same kernels);
+ *     a call whose workspace (moe_ffn_workspace_size) exceeds the scratch
+ *     returns MOE_ERR_UNSUPPORTED before anything is enqueued.
+ *   - Every call on one GPU shares that GPU's scratch: calls whose work can
+ *     overlap on one GPU (other streams, other threads, graphs replayed
+ *     concurrently) race and give wrong results; order them on one stream.
+ *     Nothing in the scratch needs to start at zero: each call writes every
+ *     part it reads before reading it.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_expert_ffn_q4k_noalloc(const void* slot_pool, size_t slot_stride, int S, int H, int I, const void* x,
+                                      int x_dtype, int T, int k, const int32_t* slot_offsets,
+                                      const int32_t* active_slots, const int32_t* num_active,
+                                      const int32_t* perm_pair, void* y_pairs, int y_dtype, int path, void* stream);
+
 /* ---------------------------------------------------------------- combine
  * y[t] = sum over j < k, in j order, of [resident(t,j)] * topk_w[t,j] *
  * y_pairs[t*k+j]  (+ y_shared[t] if y_shared is not NULL), where pair (t, j)

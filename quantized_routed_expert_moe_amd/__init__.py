@@ -74,6 +74,7 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_ffn_q3k_q4k.argtypes = ffn
         L.moe_expert_ffn_q5k.argtypes = ffn
         L.moe_expert_ffn_q6k.argtypes = ffn
+        L.moe_expert_ffn_q4k_noalloc.argtypes = ffn[:16] + [vp]
         L.moe_combine.argtypes = [vp, i32, vp, vp, vp, i32, i32, vp, i32, i32, i32, vp, i32, vp]
         L.moe_timer_begin.argtypes = [i32, i32]
         L.moe_timer_end.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
@@ -81,7 +82,7 @@ def lib() -> ctypes.CDLL:
         for name in ("moe_route_topk", "moe_build_expert_batches", "moe_route_and_batch", "moe_count_routes",
                      "moe_pack_expert", "moe_unpack_expert", "moe_pack_q4k", "moe_pack_q8_0",
                      "moe_validate_slot_map", "moe_expert_ffn_q4k", "moe_expert_ffn_q8_0", "moe_expert_ffn_mxfp4",
-                     "moe_expert_ffn_q3k_q4k", "moe_expert_ffn_q5k", "moe_expert_ffn_q6k",
+                     "moe_expert_ffn_q3k_q4k", "moe_expert_ffn_q5k", "moe_expert_ffn_q6k", "moe_expert_ffn_q4k_noalloc",
                      "moe_combine",
                      "moe_timer_begin", "moe_timer_end", "moe_timer_read"):
             getattr(L, name).restype = i32
@@ -316,6 +317,21 @@ def moe_expert_ffn_q4k(slot_pool, slot_stride, S, H, I, x, k, slot_offsets, acti
                        y_pairs, path=MOE_PATH_AUTO, ws=None, stream=None):
     _ffn(lib().moe_expert_ffn_q4k, slot_pool, slot_stride, S, H, I, x, k, slot_offsets, active_slots, num_active,
          perm_pair, y_pairs, path, ws, stream)
+
+
+def moe_expert_ffn_q4k_noalloc(slot_pool, slot_stride, S, H, I, x, k, slot_offsets, active_slots, num_active,
+                               perm_pair, y_pairs, path=MOE_PATH_AUTO, stream=None):
+    """moe_expert_ffn_q4k with the library's own scratch as its workspace (no allocation)."""
+    T = x.shape[0]
+    pool_ptr = slot_pool if isinstance(slot_pool, int) else _dev(slot_pool, None, "slot_pool")
+    _check(lib().moe_expert_ffn_q4k_noalloc(
+        pool_ptr, slot_stride, S, H, I, _dev(x, _fb(), "x"), _dtype_code(x), T, k,
+        _dev(slot_offsets, _i32(), "slot_offsets"), _dev(active_slots, _i32(), "active_slots"),
+        _dev(num_active, _i32(), "num_active"), _dev(perm_pair, _i32(), "perm_pair"), _dev(y_pairs, _fb(), "y_pairs"),
+        _dtype_code(y_pairs), path, _stream(stream)))
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def moe_expert_ffn_q8_0(slot_pool, slot_stride, S, H, I, x, k, slot_offsets, active_slots, num_active, perm_pair,

@@ -642,6 +642,36 @@ moe_status ffn_common(int format, const void* slot_pool, size_t slot_stride, int
     return MOE_OK;
 }
 
+// ------------------------------------------------- allocation-free FFN
+// The workspace of moe_expert_ffn_q4k_noalloc: one file-scope device array
+// per GPU (each device holds its own copy, at its own address, from the
+// first such call on it until the process ends).  Host code must not pass
+// `scratch` itself to a kernel (its host-side name is not a device address):
+// its device address is looked up once per device with
+// hipGetSymbolAddress and kept in g_scratch_ptr.
+static_assert(MOE_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+moe_status scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
 }  // namespace
 
 namespace qmoe {
@@ -841,6 +871,27 @@ moe_status moe_expert_ffn_q4k(const void* slot_pool, size_t slot_stride, int S, 
                               int path, void* ws, size_t ws_bytes, void* stream) {
     return ffn_common(MOE_FMT_Q4K, slot_pool, slot_stride, S, H, I, x, x_dtype, T, k, slot_offsets, active_slots,
                       num_active, perm_pair, y_pairs, y_dtype, path, ws, ws_bytes, stream);
+}
+
+moe_status moe_expert_ffn_q4k_noalloc(const void* slot_pool, size_t slot_stride, int S, int H, int I, const void* x,
+                                      int x_dtype, int T, int k, const int32_t* slot_offsets,
+                                      const int32_t* active_slots, const int32_t* num_active,
+                                      const int32_t* perm_pair, void* y_pairs, int y_dtype, int path, void* stream) {
+    size_t need = 0;
+    int p = MOE_PATH_DECODE;
+    moe_status st = ffn_check(MOE_FMT_Q4K, slot_pool, slot_stride, S, H, I, x, x_dtype, T, k, slot_offsets,
+                              active_slots, num_active, perm_pair, y_pairs, y_dtype, path, &need, &p);
+    if (st != MOE_OK) return st;
+    if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+        return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn_q4k_noalloc: this call needs %zu bytes of workspace, the "
+                                         "library's scratch holds %zu (call moe_expert_ffn_q4k with a workspace)",
+                    need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+    if (T == 0) return MOE_OK;
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != MOE_OK) return st;
+    return ffn_common(MOE_FMT_Q4K, slot_pool, slot_stride, S, H, I, x, x_dtype, T, k, slot_offsets, active_slots,
+                      num_active, perm_pair, y_pairs, y_dtype, path, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 moe_status moe_expert_ffn_q8_0(const void* slot_pool, size_t slot_stride, int S, int H, int I, const void* x,

@@ -392,3 +392,21 @@ def test_per_matrix_pack_rejects():
     st, msg = _call("moe_pack_q4k", buf.ctypes.data, buf.ctypes.data + 16, 64, 256, 0)
     assert st == Q.MOE_ERR_INVALID_ARGUMENT and "overlap" in msg
 
+
+def test_noalloc_ffn_rejects_beyond_its_scratch_without_touching_the_device():
+    """moe_expert_ffn_q4k_noalloc: the checks of moe_expert_ffn_q4k, then the
+    workspace against the library's fixed scratch; a call that needs more is
+    refused by name before any HIP call (so this runs without a GPU)."""
+    stride = Q.moe_expert_blob_bytes(Q.MOE_FMT_Q4K, 2048, 768) // 16 * 16 + 256
+    args = [FAKE, stride, 128, 2048, 768, FAKE, Q.MOE_BF16, 8192, 8, FAKE, FAKE, FAKE, FAKE, FAKE, Q.MOE_BF16,
+            Q.MOE_PATH_PREFILL, None]
+    need = Q.moe_ffn_workspace_size(Q.MOE_FMT_Q4K, 8192, 8, 2048, 768, Q.MOE_PATH_PREFILL)
+    assert need > Q.MOE_NOALLOC_SCRATCH_BYTES
+    st, msg = _call("moe_expert_ffn_q4k_noalloc", *args)
+    assert st == Q.MOE_ERR_UNSUPPORTED and f"needs {need} bytes" in msg and str(Q.MOE_NOALLOC_SCRATCH_BYTES) in msg
+    # the other checks come first, as in moe_expert_ffn_q4k
+    args[3] = 2000
+    st, msg = _call("moe_expert_ffn_q4k_noalloc", *args)
+    assert st == Q.MOE_ERR_UNSUPPORTED and "multiples of 256" in msg
+    # the 4096-token prefill layer's workspace fits
+    assert Q.moe_ffn_workspace_size(Q.MOE_FMT_Q4K, 4096, 8, 2048, 768, Q.MOE_PATH_PREFILL) <= Q.MOE_NOALLOC_SCRATCH_BYTES
