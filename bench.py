@@ -47,6 +47,8 @@ METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA util (prefill),
 DSV3_GATEUP_BYTES = 2 * 7168 * 2048 // 256 * 144    # one routed Q4_K expert's gate and up matrices
 DSV3_DOWN_BYTES = 7168 * 2048 // 256 * 144
 DSV3_SHARED_BYTES = 3 * 7168 * 2048 // 32 * 34       # the Q8_0 shared expert
+DSV3_SHARED_GATEUP_BYTES = 2 * 7168 * 2048 // 32 * 34
+DSV3_SHARED_DOWN_BYTES = 7168 * 2048 // 32 * 34
 # rocprofv3 --pmc summaries of the decode gate/up kernel (HBM bytes per launch),
 # valid only while the kernel's sources hash to the value recorded in them
 TRAFFIC = {
@@ -54,7 +56,7 @@ TRAFFIC = {
     "qwen3": os.path.join(ROOT, "profiles", "traffic_ffn_gateup_q4k_qwen3_decode.txt"),
 }
 KERNEL_SOURCES = [os.path.join(ROOT, "quantized_routed_expert_moe_amd", "csrc", f)
-                  for f in ("ffn_decode.hip", "device_common.h", "qmoe_internal.h")]
+                  for f in ("ffn_decode.hip", "gemv_core.h", "device_common.h", "qmoe_internal.h")]
 LEGS = ("stack", "dsv3", "prefill", "qwen3")
 STAGE_GATEUP, STAGE_DOWN, STAGE_COMBINE, STAGE_ROUTE_BATCHES = 3, 4, 5, 8
 STAGE_ROUTE, STAGE_BATCHES, STAGE_TILES, STAGE_PF_GATEUP, STAGE_PF_DOWN = 0, 1, 2, 6, 7
@@ -201,27 +203,29 @@ def leg_stack(args, thr: dict, extra: dict | None) -> dict:
         st.replay()
     replay_ms = timed_replays(lambda i: st.replay(), args.steps)
 
-    # ---- eager pass with the stage timers: per-launch kernel times (each
-    # layer enqueues its shared expert's launches first, then its routed ones)
+    # ---- eager pass with the stage timers: per-launch kernel times.  Each
+    # layer is four launches: L0 routing + batching beside the shared gate/up
+    # (stage 8), L1 routed gate/up + SwiGLU beside the shared down (stage 3),
+    # L2 routed down (stage 4), L3 combine (stage 5).
     ne = max(1, min(args.steps, 20))
     st.run_eager()
     torch.cuda.synchronize()
-    for s, c in ((STAGE_GATEUP, 2 * L * ne), (STAGE_DOWN, 2 * L * ne), (STAGE_ROUTE_BATCHES, L * ne),
-                 (STAGE_COMBINE, L * ne)):
-        Q.moe_timer_begin(s, c)
+    stages = (STAGE_GATEUP, STAGE_DOWN, STAGE_ROUTE_BATCHES, STAGE_COMBINE)
+    for s in stages:
+        Q.moe_timer_begin(s, L * ne)
     for _ in range(ne):
         st.run_eager()
     torch.cuda.synchronize()
-    each = {s: Q.moe_timer_read(s, 2 * L * ne) for s in (STAGE_GATEUP, STAGE_DOWN, STAGE_ROUTE_BATCHES, STAGE_COMBINE)}
-    for s in each:
+    each = {s: Q.moe_timer_read(s, L * ne) for s in stages}
+    for s in stages:
         Q.moe_timer_end(s)
-    gu_routed, gu_shared = each[STAGE_GATEUP][1::2], each[STAGE_GATEUP][0::2]
-    dn_routed, dn_shared = each[STAGE_DOWN][1::2], each[STAGE_DOWN][0::2]
-    assert len(gu_routed) == L * ne and len(dn_routed) == L * ne
-    gu_bytes = sum(uniq) * DSV3_GATEUP_BYTES / L           # algorithmic bytes per routed gate/up launch
-    gu_us = 1e3 * float(np.mean(gu_routed))
+    assert all(len(each[s]) == L * ne for s in stages), {s: len(each[s]) for s in stages}
+    # algorithmic bytes per launch, averaged over the layers
+    gu_bytes = sum(uniq) * DSV3_GATEUP_BYTES / L + DSV3_SHARED_DOWN_BYTES
+    gu_us = 1e3 * float(np.mean(each[STAGE_GATEUP]))
     dn_bytes = sum(uniq) * DSV3_DOWN_BYTES / L
-    dn_us = 1e3 * float(np.mean(dn_routed))
+    dn_us = 1e3 * float(np.mean(each[STAGE_DOWN]))
+    l0_us = 1e3 * float(np.mean(each[STAGE_ROUTE_BATCHES]))
     traffic = read_traffic("stack")
 
     # ---- the oracle on the same layers (card part: resident pairs + shared expert)
@@ -248,11 +252,12 @@ def leg_stack(args, thr: dict, extra: dict | None) -> dict:
     out = {
         "value": wl.T * L / (replay_ms * 1e-3),
         "ms_per_step": replay_ms,
-        "roofline": {"bound": "hbm", "kernel": "routed Q4_K gate/up GEMV + SwiGLU (gemv_kernel<1,2,true>) in the stack",
+        "roofline": {"bound": "hbm", "kernel": "layer_l1_kernel<1,true>: routed Q4_K gate/up GEMV + SwiGLU with the "
+                               "shared expert's Q8_0 down GEMV in the same launch, in the stack",
                      "achieved": round(gu_bytes / (gu_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_bytes / (gu_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": round(gu_bytes), "avg_launch_us": round(gu_us, 3),
-                     "launches_timed": int(len(gu_routed))},
+                     "launches_timed": int(len(each[STAGE_GATEUP]))},
         "cpu_baseline": cpu,
         "stack": {"layers": L, "resident": wl.resident, "staging": wl.staging, "graph_nodes": nodes,
                   "replay_ms": round(replay_ms, 4), "layer_us": round(1e3 * replay_ms / L, 2),
@@ -262,12 +267,12 @@ def leg_stack(args, thr: dict, extra: dict | None) -> dict:
                   "replay_frac_of_hbm": round(bytes_per_replay / (replay_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                   "unique_resident_experts_per_layer": round(float(np.mean(uniq)), 3),
                   "card_served_share": round(float(np.mean(served)), 4),
-                  "gateup_us": round(gu_us, 2), "gateup_GBs": round(gu_bytes / (gu_us * 1e-6) / 1e9, 1),
-                  "down_us": round(dn_us, 2), "down_GBs": round(dn_bytes / (dn_us * 1e-6) / 1e9, 1),
-                  "shared_gateup_us": round(1e3 * float(np.mean(gu_shared)), 2),
-                  "shared_down_us": round(1e3 * float(np.mean(dn_shared)), 2),
-                  "route_batch_us": round(1e3 * float(np.mean(each[STAGE_ROUTE_BATCHES])), 2),
-                  "combine_us": round(1e3 * float(np.mean(each[STAGE_COMBINE])), 2),
+                  "l0_route_and_shared_gateup_us": round(l0_us, 2),
+                  "l0_GBs": round(DSV3_SHARED_GATEUP_BYTES / (l0_us * 1e-6) / 1e9, 1),
+                  "l1_gateup_and_shared_down_us": round(gu_us, 2),
+                  "l1_GBs": round(gu_bytes / (gu_us * 1e-6) / 1e9, 1),
+                  "l2_down_us": round(dn_us, 2), "l2_GBs": round(dn_bytes / (dn_us * 1e-6) / 1e9, 1),
+                  "l3_combine_us": round(1e3 * float(np.mean(each[STAGE_COMBINE])), 2),
                   "eager_steps_timed": ne, "setup_s": round(setup_s, 1)},
     }
     if extra is not None:
@@ -365,14 +370,14 @@ def leg_dsv3(args, thr: dict) -> dict:
         torch.cuda.synchronize()
         steps = args.dsv3_steps
         step = lambda i: layer.forward(xs[i % nb], ls[i % nb], shared_pool=shared[i % nb])  # noqa: E731
-        for s in (STAGE_GATEUP, STAGE_DOWN):
-            Q.moe_timer_begin(s, 2 * steps)
+        stages = (STAGE_ROUTE_BATCHES, STAGE_GATEUP, STAGE_DOWN, STAGE_COMBINE)
+        for s in stages:
+            Q.moe_timer_begin(s, steps)
         for i in range(steps):
             step(i)
         torch.cuda.synchronize()
-        gu = Q.moe_timer_read(STAGE_GATEUP, 2 * steps)
-        dn = Q.moe_timer_read(STAGE_DOWN, 2 * steps)
-        for s in (STAGE_GATEUP, STAGE_DOWN):
+        t_us = {s: 1e3 * float(np.mean(Q.moe_timer_read(s, steps))) for s in stages}
+        for s in stages:
             Q.moe_timer_end(s)
         graphs = []
         for i in range(nb):
@@ -385,22 +390,23 @@ def leg_dsv3(args, thr: dict) -> dict:
         ms = timed_replays(lambda i: graphs[i % nb].replay(), steps)
         mean_uniq = float(np.mean([uniq[i % nb] for i in range(steps)]))
         layer_bytes = mean_uniq * (DSV3_GATEUP_BYTES + DSV3_DOWN_BYTES) + DSV3_SHARED_BYTES
-        gu_us = 1e3 * float(np.mean(gu[1::2]))
-        gu_bytes = mean_uniq * DSV3_GATEUP_BYTES
-        dn_us = 1e3 * float(np.mean(dn[1::2]))
+        gu_us = t_us[STAGE_GATEUP]
+        gu_bytes = mean_uniq * DSV3_GATEUP_BYTES + DSV3_SHARED_DOWN_BYTES
+        dn_us = t_us[STAGE_DOWN]
         res[f"T{wl.T}"] = {
             "workload": wl.name, "tokens_per_s": round(wl.T / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
             "unique_experts_per_step": round(mean_uniq, 2), "layer_bytes_per_step": round(layer_bytes),
             "layer_GBs": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
             "layer_frac_of_hbm": round(layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "roofline_kernel": "routed Q4_K gate/up GEMV + SwiGLU", "roofline_bound": "hbm",
+            "roofline_kernel": "layer_l1_kernel: routed Q4_K gate/up GEMV + SwiGLU with the shared Q8_0 down GEMV",
+            "roofline_bound": "hbm",
             "roofline_achieved_GBs": round(gu_bytes / (gu_us * 1e-6) / 1e9, 1), "roofline_peak_GBs": HBM_PEAK_GBS,
             "roofline_frac": round(gu_bytes / (gu_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "roofline_algorithmic_bytes_per_launch": round(gu_bytes), "roofline_avg_launch_us": round(gu_us, 3),
-            "down_us": round(dn_us, 3),
-            "down_GBs": round(mean_uniq * DSV3_DOWN_BYTES / (dn_us * 1e-6) / 1e9, 1),
-            "shared_gateup_us": round(1e3 * float(np.mean(gu[0::2])), 3),
-            "shared_down_us": round(1e3 * float(np.mean(dn[0::2])), 3),
+            "l0_route_and_shared_gateup_us": round(t_us[STAGE_ROUTE_BATCHES], 3),
+            "l2_down_us": round(dn_us, 3),
+            "l2_down_GBs": round(mean_uniq * DSV3_DOWN_BYTES / (dn_us * 1e-6) / 1e9, 1),
+            "l3_combine_us": round(t_us[STAGE_COMBINE], 3),
             "steps": steps, "shared_copies": nb,
         }
         del graphs, layer

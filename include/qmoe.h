@@ -339,6 +339,49 @@ moe_status moe_expert_ffn_q6k(const void* slot_pool, size_t slot_stride, int S, 
                               const int32_t* num_active, const int32_t* perm_pair, void* y_pairs, int y_dtype,
                               int path, void* ws, size_t ws_bytes, void* stream);
 
+/* ----------------------------------------------------- fused decode layer
+ * The whole layer of a decode step in one call: moe_route_and_batch, the
+ * routed expert FFN on the decode path, the shared expert (Q8_0, weight 1,
+ * every row) and moe_combine, enqueued as four dependent launches on one
+ * stream with the shared expert folded into them (its gate/up GEMV beside
+ * the routing, its down GEMV beside the routed gate/up, its partial sums
+ * added by the combine) instead of a second stream of launches.  The layer
+ * the pages' engine runs per decode step, one CUDA graph per step (bloomery
+ * README 0.3.1, "Why it is fast"), with the shared experts in Q8_0 (README
+ * of 2026-09-24) and the routed ones in their stored type (README 0.3.1,
+ * "Status (0.3.1)" table, "Quant types" row).
+ *
+ * format        the routed experts' block type (any MOE_FMT_*).
+ * logits        device, fp32 [T, E] gate logits.
+ * x, x_dtype    device, [T, H] activations, MOE_F32 or MOE_BF16 (both enter
+ *               the dot products as fp16, as on the expert FFN's decode path).
+ * T, E, k, score, renormalize, scale, slot_of_expert, S (1..E), slot_pool,
+ * slot_stride, H, I
+ *               as for moe_route_and_batch and moe_expert_ffn_*.
+ * shared_pool   device: one packed Q8_0 blob (moe_pack_expert) of
+ *               intermediate I_shared (a multiple of 128), 16-byte aligned;
+ *               NULL with I_shared = 0 for a layer without a shared expert.
+ * topk_ids .. host_count, route_counts
+ *               outputs exactly as moe_route_and_batch writes them.
+ * y_pairs       device, fp32 [T*k, H]: the resident pairs' outputs (as the
+ *               routed FFN's decode path writes them).
+ * y             device, fp32 [T, H]: sum over resident pairs of w * y_pair,
+ *               in j order, plus the shared expert.
+ * ws, ws_bytes  device workspace of moe_layer_decode_workspace_size().
+ * Integer outputs and y_pairs are bit for bit those of the separate calls;
+ * y agrees with their combine to rounding (the shared expert's sums are
+ * split differently).  Errors as for the separate calls, all checked before
+ * anything is enqueued.
+ */
+size_t moe_layer_decode_workspace_size(int format, int T, int k, int E, int S, int H, int I, int I_shared);
+moe_status moe_layer_decode(int format, const float* logits, const void* x, int x_dtype, int T, int E, int k,
+                            int score, int renormalize, float scale, const int32_t* slot_of_expert, int S, const void* slot_pool,
+                            size_t slot_stride, int H, int I, const void* shared_pool, int I_shared,
+                            int32_t* topk_ids, float* topk_w, int32_t* slot_offsets, int32_t* active_slots,
+                            int32_t* num_active, int32_t* perm_pair, int32_t* host_token, int32_t* host_expert,
+                            float* host_weight, int32_t* host_count, uint32_t* route_counts, float* y_pairs,
+                            float* y, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------ allocation-free FFN
  * For callers that cannot allocate device memory (code under hipGraph
  * capture that must not call hipMalloc, tight serving loops, harnesses that

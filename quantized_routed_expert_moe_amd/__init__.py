@@ -76,6 +76,11 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_ffn_q6k.argtypes = ffn
         L.moe_expert_ffn_q4k_noalloc.argtypes = ffn[:16] + [vp]
         L.moe_combine.argtypes = [vp, i32, vp, vp, vp, i32, i32, vp, i32, i32, i32, vp, i32, vp]
+        L.moe_layer_decode_workspace_size.argtypes = [i32] * 8
+        L.moe_layer_decode_workspace_size.restype = sz
+        L.moe_layer_decode.argtypes = [i32, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, i32, vp, sz, i32, i32, vp,
+                                       i32] + \
+            [vp] * 13 + [vp, sz, vp]
         L.moe_timer_begin.argtypes = [i32, i32]
         L.moe_timer_end.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
         L.moe_timer_read.argtypes = [i32, vp, i32, ctypes.POINTER(ctypes.c_int)]
@@ -83,7 +88,7 @@ def lib() -> ctypes.CDLL:
                      "moe_pack_expert", "moe_unpack_expert", "moe_pack_q4k", "moe_pack_q8_0",
                      "moe_validate_slot_map", "moe_expert_ffn_q4k", "moe_expert_ffn_q8_0", "moe_expert_ffn_mxfp4",
                      "moe_expert_ffn_q3k_q4k", "moe_expert_ffn_q5k", "moe_expert_ffn_q6k", "moe_expert_ffn_q4k_noalloc",
-                     "moe_combine",
+                     "moe_combine", "moe_layer_decode",
                      "moe_timer_begin", "moe_timer_end", "moe_timer_read"):
             getattr(L, name).restype = i32
         _lib = L
@@ -379,6 +384,31 @@ def moe_combine(y_pairs, topk_ids, topk_w, slot_of_expert, S: int, y_shared, y, 
                              _dev(topk_w, _f32(), "topk_w"), _dev(slot_of_expert, _i32(), "slot_of_expert"), E, S,
                              _dev(y_shared, _f32(), "y_shared"), T, k, H, _dev(y, _fb(), "y"), _dtype_code(y),
                              _stream(stream)))
+
+
+def moe_layer_decode_workspace_size(fmt: int, T: int, k: int, E: int, S: int, H: int, I: int, I_shared: int) -> int:
+    return int(lib().moe_layer_decode_workspace_size(fmt, T, k, E, S, H, I, I_shared))
+
+
+def moe_layer_decode(fmt: int, logits, x, k: int, score: int, renormalize: bool, scale: float, slot_of_expert, S: int,
+                     slot_pool, slot_stride: int, I: int, shared_pool, I_shared: int, topk_ids, topk_w, slot_offsets,
+                     active_slots, num_active, perm_pair, host_token, host_expert, host_weight, host_count, y_pairs, y,
+                     ws, stream=None, route_counts=None):
+    """The whole decode layer (routing, batching, routed and shared expert FFN, combine) in one call."""
+    T, E = logits.shape
+    H = x.shape[1]
+    pool_ptr = slot_pool if isinstance(slot_pool, int) else _dev(slot_pool, None, "slot_pool")
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().moe_layer_decode(
+        fmt, _dev(logits, _f32(), "logits"), _dev(x, _fb(), "x"), _dtype_code(x), T, E, k, score, int(bool(renormalize)),
+        float(scale), _dev(slot_of_expert, _i32(), "slot_of_expert"), S, pool_ptr, slot_stride, H, I,
+        _dev(shared_pool, None, "shared_pool"), I_shared if shared_pool is not None else 0,
+        _dev(topk_ids, _i32(), "topk_ids"), _dev(topk_w, _f32(), "topk_w"), _dev(slot_offsets, _i32(), "slot_offsets"),
+        _dev(active_slots, _i32(), "active_slots"), _dev(num_active, _i32(), "num_active"),
+        _dev(perm_pair, _i32(), "perm_pair"), _dev_or_mapped(host_token, _i32(), "host_token"),
+        _dev_or_mapped(host_expert, _i32(), "host_expert"), _dev_or_mapped(host_weight, _f32(), "host_weight"),
+        _dev_or_mapped(host_count, _i32(), "host_count"), _dev(route_counts, _u32(), "route_counts"),
+        _dev(y_pairs, _f32(), "y_pairs"), _dev(y, _f32(), "y"), _dev(ws, None, "ws"), ws_bytes, _stream(stream)))
 
 
 # ------------------------------------------------------------ host leg

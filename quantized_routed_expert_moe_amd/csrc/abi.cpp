@@ -934,6 +934,57 @@ moe_status moe_expert_ffn_q6k(const void* slot_pool, size_t slot_stride, int S, 
                       num_active, perm_pair, y_pairs, y_dtype, path, ws, ws_bytes, stream);
 }
 
+size_t moe_layer_decode_workspace_size(int format, int T, int k, int E, int S, int H, int I, int I_shared) {
+    if (check_shape(format, H, I) != MOE_OK || T < 0 || k < 1 || k > MOE_MAX_TOPK || E < 1 ||
+        E > MOE_MAX_EXPERTS || S < 1 || S > E || I_shared < 0 || (I_shared > 0 && I_shared % 128))
+        return 0;
+    return qmoe::layer_decode_workspace_bytes(format, T, k, E, S, H, I, I_shared);
+}
+
+moe_status moe_layer_decode(int format, const float* logits, const void* x, int x_dtype, int T, int E, int k,
+                            int score, int renormalize, float scale, const int32_t* slot_of_expert, int S, const void* slot_pool,
+                            size_t slot_stride, int H, int I, const void* shared_pool, int I_shared,
+                            int32_t* topk_ids, float* topk_w, int32_t* slot_offsets, int32_t* active_slots,
+                            int32_t* num_active, int32_t* perm_pair, int32_t* host_token, int32_t* host_expert,
+                            float* host_weight, int32_t* host_count, uint32_t* route_counts, float* y_pairs,
+                            float* y, void* ws, size_t ws_bytes, void* stream) {
+    moe_status st = check_route_shape(T, E, k);
+    if (st != MOE_OK) return st;
+    if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "score = %d is not softmax or sigmoid", score);
+    if (!(scale == scale)) return fail(MOE_ERR_INVALID_ARGUMENT, "scale is NaN");
+    if (S < 1 || S > E) return fail(MOE_ERR_INVALID_ARGUMENT, "S = %d outside 1..E (%d)", S, E);
+    if (!slot_of_expert || !slot_offsets || !num_active || !host_count || !active_slots)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+    if (T > 0 && (!logits || !topk_ids || !topk_w || !host_token || !host_expert || !host_weight || !y))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+    size_t need_ffn = 0;
+    int p = MOE_PATH_DECODE;
+    st = ffn_check(format, slot_pool, slot_stride, S, H, I, x, x_dtype, T, k, slot_offsets, active_slots, num_active,
+                   perm_pair, y_pairs, MOE_F32, MOE_PATH_DECODE, &need_ffn, &p);
+    if (st != MOE_OK) return st;
+    if (I_shared < 0 || (I_shared > 0) != (shared_pool != nullptr))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "shared_pool and I_shared > 0 go together (I_shared = %d)", I_shared);
+    if (I_shared > 0) {
+        st = check_shape(MOE_FMT_Q8_0, H, I_shared);
+        if (st != MOE_OK) return st;
+        if (!aligned16(shared_pool)) return fail(MOE_ERR_INVALID_ARGUMENT, "shared_pool must be 16-byte aligned");
+    }
+    if (T > 0 && !aligned16(y)) return fail(MOE_ERR_INVALID_ARGUMENT, "y must be 16-byte aligned");
+    const size_t need = qmoe::layer_decode_workspace_bytes(format, T, k, E, S, H, I, I_shared);
+    if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, %zu needed", ws_bytes, need);
+    if (need > 0 && (!ws || !aligned16(ws)))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 16-byte aligned");
+    if (T == 0) return MOE_OK;
+    const qmoe::LayerDecodeArgs a{format, logits, x, x_dtype, T, E, k, score, renormalize, scale, slot_of_expert, S,
+                                  slot_pool, slot_stride, H, I, shared_pool, I_shared, topk_ids, topk_w, slot_offsets,
+                                  active_slots, num_active, perm_pair, host_token, host_expert, host_weight,
+                                  host_count, route_counts, y_pairs, y, ws};
+    hipError_t e = qmoe::launch_layer_decode(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "decode layer launch");
+    return MOE_OK;
+}
+
 moe_status moe_combine(const void* y_pairs, int y_pairs_dtype, const int32_t* topk_ids, const float* topk_w,
                        const int32_t* slot_of_expert, int E, int S, const float* y_shared, int T, int k, int H,
                        void* y, int y_dtype, void* stream) {

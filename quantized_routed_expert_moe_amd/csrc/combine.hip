@@ -26,8 +26,8 @@ __device__ __forceinline__ void load8(const void* base, int dtype, size_t idx, f
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ yp, int yp_dtype,
                                                       const int32_t* __restrict__ ids, const float* __restrict__ w,
                                                       const int32_t* __restrict__ soe, int E, int S,
-                                                      const float* __restrict__ ysh, int T, int k, int H,
-                                                      void* __restrict__ y, int y_dtype) {
+                                                      const float* __restrict__ ysh, int sh_parts, int T, int k,
+                                                      int H, void* __restrict__ y, int y_dtype) {
     // The slot map goes to LDS, loaded together with the first batch of pair
     // ids, weights and rows, so the residency test is an LDS read rather than
     // a second dependent global load.  Rows of non-resident pairs are read too
@@ -70,9 +70,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
         load_batch(j0);
         add_batch(j0);
     }
-    if (ysh) {
-        float u[8];
-        load8(ysh, 0, (size_t)t * H + h0, u);
+    if (sh_parts > 0) {
+        // the shared expert's output: one [T, H] array, or the partial sums
+        // [part][T, H] of its K-split down GEMV, added in part order
+        float u[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int pt = 0; pt < sh_parts; ++pt) {
+            float v8[8];
+            load8(ysh, 0, ((size_t)pt * T + t) * H + h0, v8);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) u[i] += v8[i];
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] += u[i];
     }
@@ -89,15 +96,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
     }
 }
 
-hipError_t launch_combine(const void* y_pairs, int yp_dtype, const int32_t* ids, const float* w,
-                          const int32_t* soe, int E, int S, const float* y_shared, int T, int k, int H, void* y,
-                          int y_dtype, hipStream_t s) {
+hipError_t launch_combine_parts(const void* y_pairs, int yp_dtype, const int32_t* ids, const float* w,
+                                const int32_t* soe, int E, int S, const float* sh_part, int sh_parts, int T, int k,
+                                int H, void* y, int y_dtype, hipStream_t s) {
     if (T == 0) return hipSuccess;
     dim3 grid((H / 8 + 255) / 256, T);
     const StageEvents ev = timer_events(kStageCombine);
     launch_timed(combine_kernel, grid, dim3(256), 0, s, ev.start, ev.stop, y_pairs, yp_dtype, ids, w, soe, E, S,
-                 y_shared, T, k, H, y, y_dtype);
+                 sh_part, sh_part ? sh_parts : 0, T, k, H, y, y_dtype);
     return hipGetLastError();
+}
+
+hipError_t launch_combine(const void* y_pairs, int yp_dtype, const int32_t* ids, const float* w,
+                          const int32_t* soe, int E, int S, const float* y_shared, int T, int k, int H, void* y,
+                          int y_dtype, hipStream_t s) {
+    return launch_combine_parts(y_pairs, yp_dtype, ids, w, soe, E, S, y_shared, y_shared ? 1 : 0, T, k, H, y, y_dtype,
+                                s);
 }
 
 }  // namespace qmoe

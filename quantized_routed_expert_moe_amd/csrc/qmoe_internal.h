@@ -206,11 +206,62 @@ struct FfnArgs {
 size_t decode_workspace_bytes(int T, int k, int H, int I);
 hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s);
 
+// The shared expert's down GEMV run inside the routed gate/up launch of the
+// fused decode layer: its Q8_0 blob, its gate/up partial sums (gu_parts
+// parts, [part][T][2][I_shared]) and where its own partial sums go
+// (dn_parts, set by the launcher, parts [part][T][H]).
+struct SharedDown {
+    const uint8_t* pool;
+    int I_shared;
+    const float* gu_part;
+    int gu_parts;
+    float* dn_part;
+    int dn_parts;
+};
+hipError_t launch_ffn_decode_with_shared(const FfnArgs& a, SharedDown* sd, hipStream_t s);
+// Waves per workgroup of the routed gate/up launch (what the shared down
+// GEMV beside it splits its K over).
+int ffn_gateup_waves(const FfnArgs& a);
+
 size_t prefill_workspace_bytes(int T, int k, int H, int I);
 hipError_t launch_ffn_prefill(const FfnArgs& a, hipStream_t s);  // Q4_K or MXFP4
 
 hipError_t launch_combine(const void* y_pairs, int yp_dtype, const int32_t* ids, const float* w,
                           const int32_t* slot_of_expert, int E, int S, const float* y_shared, int T, int k, int H,
                           void* y, int y_dtype, hipStream_t s);
+// The combine with the shared expert's output given as sh_parts partial sums
+// [part][T][H], added in part order (sh_parts = 0: no shared expert).
+hipError_t launch_combine_parts(const void* y_pairs, int yp_dtype, const int32_t* ids, const float* w,
+                                const int32_t* slot_of_expert, int E, int S, const float* sh_part, int sh_parts, int T,
+                                int k, int H, void* y, int y_dtype, hipStream_t s);
+
+// The fused decode layer (route + batches + expert FFN + shared expert +
+// combine in four launches).
+struct LayerDecodeArgs {
+    int format;
+    const float* logits;
+    const void* x;
+    int x_dtype;
+    int T, E, k, score, renormalize;
+    float scale;
+    const int32_t* soe;
+    int S;
+    const void* pool;
+    size_t stride;
+    int H, I;
+    const void* shared_pool;
+    int I_shared;
+    int32_t *ids;
+    float* w;
+    int32_t *offsets, *active, *num_active, *perm, *host_token, *host_expert;
+    float* host_weight;
+    int32_t* host_count;
+    uint32_t* route_counts;
+    float* y_pairs;
+    float* y;
+    void* ws;
+};
+size_t layer_decode_workspace_bytes(int format, int T, int k, int E, int S, int H, int I, int I_shared);
+hipError_t launch_layer_decode(const LayerDecodeArgs& a, hipStream_t s);
 
 }  // namespace qmoe

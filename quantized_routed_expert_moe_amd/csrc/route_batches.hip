@@ -14,42 +14,15 @@
 #include "batches_common.h"
 #include "device_common.h"
 #include "qmoe_internal.h"
-#include "route_common.h"
+#include "route_batches_wg.h"
 
 namespace qmoe {
 
 constexpr int kFusedMaxRows = 4;
 
 template <int EMAX>
-__global__ __launch_bounds__(256 * kFusedMaxRows) void route_batches_kernel(
-    const float* __restrict__ logits, int T, int E, int k, int score, int renormalize, float scale,
-    int32_t* __restrict__ ids, float* __restrict__ w, const int32_t* __restrict__ soe, int S, int nbits,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ active, int32_t* __restrict__ num_active,
-    int32_t* __restrict__ perm, int32_t* __restrict__ host_token, int32_t* __restrict__ host_expert,
-    float* __restrict__ host_weight, int32_t* __restrict__ host_count, uint32_t* __restrict__ route_counts) {
-    __shared__ __align__(16) RouteShared<EMAX> sh[kFusedMaxRows];
-    __shared__ int32_t s_ids[64];
-    __shared__ float s_w[64];
-    __shared__ int s_soe[EMAX];
-    __shared__ int cnt[EMAX + 1];
-    const int t = threadIdx.x >> 8, tid = threadIdx.x & 255;  // row, thread within its row's group (blockDim = 256 T)
-    const float* l = logits + (size_t)t * E;
-    const float v = tid < E ? l[tid] : 0.0f;
-    if (threadIdx.x < E) s_soe[threadIdx.x] = soe[threadIdx.x];
-    route_row<EMAX>(sh[t], tid, v, l, E, k, score, renormalize, scale, ids + t * k, w + t * k, s_ids + t * k,
-                    s_w + t * k);
-    __syncthreads();
-    if (threadIdx.x < 64) {
-        const int lane = threadIdx.x, P = T * k;
-        const bool valid = lane < P;
-        const int id = valid ? s_ids[lane] : 0;
-        const float wt = valid ? s_w[lane] : 0.0f;
-        const int sl = (valid && id >= 0 && id < E) ? s_soe[id] : -1;
-        if (route_counts && valid && id >= 0 && id < E)
-            __hip_atomic_fetch_add(route_counts + id, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        batch_wave(lane, P, k, S, nbits, id, wt, sl, cnt, offsets, active, num_active, perm, host_token, host_expert,
-                   host_weight, host_count);
-    }
+__global__ __launch_bounds__(256 * kFusedMaxRows) void route_batches_kernel(RouteBatchArgs r) {
+    route_batches_wg<EMAX, kFusedMaxRows>(r);
 }
 
 hipError_t launch_route_batches(const float* logits, int T, int E, int k, int score, int renormalize, float scale,
@@ -70,15 +43,13 @@ hipError_t launch_route_batches(const float* logits, int T, int E, int k, int sc
     }
     int nbits = 1;
     while ((1 << nbits) <= S) ++nbits;  // buckets 0..S
+    const RouteBatchArgs r{logits, T, E, k, score, renormalize, scale, ids, w, soe, S, nbits, offsets, active,
+                           num_active, perm, host_token, host_expert, host_weight, host_count, route_counts};
     const StageEvents ev = timer_events(kStageRouteBatches);
     if (E <= 128)
-        launch_timed(route_batches_kernel<128>, dim3(1), dim3(256 * T), 0, s, ev.start, ev.stop, logits, T, E, k,
-                     score, renormalize, scale, ids, w, soe, S, nbits, offsets, active, num_active, perm, host_token,
-                     host_expert, host_weight, host_count, route_counts);
+        launch_timed(route_batches_kernel<128>, dim3(1), dim3(256 * T), 0, s, ev.start, ev.stop, r);
     else
-        launch_timed(route_batches_kernel<256>, dim3(1), dim3(256 * T), 0, s, ev.start, ev.stop, logits, T, E, k,
-                     score, renormalize, scale, ids, w, soe, S, nbits, offsets, active, num_active, perm, host_token,
-                     host_expert, host_weight, host_count, route_counts);
+        launch_timed(route_batches_kernel<256>, dim3(1), dim3(256 * T), 0, s, ev.start, ev.stop, r);
     return hipGetLastError();
 }
 

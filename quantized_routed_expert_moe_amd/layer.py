@@ -1,11 +1,15 @@
-"""One MoE layer as a sequence of library calls, with its buffers.
+"""One MoE layer as library calls, with its buffers.
 
 Orchestration only: device buffers come from torch, every step is a call
-into libqmoe: routing and batching (moe_route_and_batch, one launch at decode
-sizes), the expert FFN, the combine.  The optional shared expert runs through moe_expert_ffn_q8_0
-with a one-slot identity batch, on a side stream forked from the layer's
-stream by an event and joined before the combine.  Nothing synchronises with
-the host, so `forward` can be captured into a HIP graph.
+into libqmoe.  On the decode path (path = MOE_PATH_DECODE) the layer is one
+call, moe_layer_decode: routing, batching, the routed and the shared expert
+FFN and the combine as four launches on one stream.  Otherwise (prefill, or
+fused=False) it is the sequence of separate calls: routing and batching
+(moe_route_and_batch, one launch at decode sizes), the expert FFN, the
+combine, with the optional shared expert served by moe_expert_ffn_q8_0 with
+a one-slot identity batch on a side stream forked from the layer's stream by
+an event and joined before the combine.  Nothing synchronises with the host,
+so `forward` can be captured into a HIP graph.
 """
 from __future__ import annotations
 
@@ -15,8 +19,8 @@ import numpy as np
 import torch
 
 from . import (MOE_FMT_Q8_0, MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL, moe_batches_workspace_size, moe_combine,
-               moe_expert_ffn, moe_packed_blob_bytes, moe_expert_ffn_q8_0, moe_ffn_workspace_size, moe_pack_expert,
-               moe_route_and_batch)
+               moe_expert_ffn, moe_expert_ffn_q8_0, moe_ffn_workspace_size, moe_layer_decode,
+               moe_layer_decode_workspace_size, moe_pack_expert, moe_packed_blob_bytes, moe_route_and_batch)
 
 
 def upload_packed_experts(fmt: int, canonical_blobs: np.ndarray, H: int, I: int, stride: int | None = None,
@@ -48,11 +52,15 @@ class MoELayer:
     def __init__(self, spec: LayerSpec, T_max: int, S: int, slot_pool: torch.Tensor, stride: int,
                  slot_of_expert: torch.Tensor, shared_pool: torch.Tensor | None = None,
                  path: int = MOE_PATH_AUTO, y_dtype=torch.float32, pair_dtype=torch.float32, device="cuda",
-                 host_list_pinned: bool = False, route_counts: torch.Tensor | None = None):
+                 host_list_pinned: bool = False, route_counts: torch.Tensor | None = None, fused: bool | None = None):
         """route_counts: optional device int32 [E] routing counters; every
         forward adds each routed pair to its expert's counter (the adaptive
-        residency policy reads them)."""
+        residency policy reads them).  fused: one moe_layer_decode call per
+        forward (default on the decode path) or the separate calls."""
         self.spec, self.T_max, self.S, self.path = spec, T_max, S, path
+        self.fused = (path == MOE_PATH_DECODE) if fused is None else bool(fused)
+        if self.fused and (path != MOE_PATH_DECODE or y_dtype != torch.float32 or pair_dtype != torch.float32):
+            raise ValueError("the fused layer is the decode path: fp32 y and y_pairs")
         self.slot_pool, self.stride, self.slot_of_expert = slot_pool, stride, slot_of_expert
         self.route_counts = route_counts
         self.shared_pool = shared_pool
@@ -79,12 +87,19 @@ class MoELayer:
         self.host_expert = self.host_list[Pl:2 * Pl]
         self.host_weight = self.host_list[2 * Pl:3 * Pl].view(torch.float32)
         self.host_count = self.host_list[3 * Pl:]
+        self.y_pairs = torch.zeros((max(1, P), H), dtype=pair_dtype, device=device)
+        self.y = torch.zeros((T_max, H), dtype=y_dtype, device=device)
+        if spec.I_shared:
+            assert shared_pool is not None
+        if self.fused:
+            self.ws = torch.zeros(max(1, moe_layer_decode_workspace_size(spec.fmt, T_max, k, E, S, H, spec.I,
+                                                                         spec.I_shared)), dtype=torch.uint8,
+                                  device=device)
+            return
         bws = moe_batches_workspace_size(T_max, k, E, S)
         self.batch_ws = torch.zeros(max(1, bws), dtype=torch.uint8, device=device) if bws else None
         self.ws = torch.zeros(max(1, moe_ffn_workspace_size(spec.fmt, T_max, k, H, spec.I, path)), dtype=torch.uint8,
                               device=device)
-        self.y_pairs = torch.zeros((max(1, P), H), dtype=pair_dtype, device=device)
-        self.y = torch.zeros((T_max, H), dtype=y_dtype, device=device)
         if spec.I_shared:
             assert shared_pool is not None
             self.sh_offsets = torch.tensor([0, T_max], **i32)
@@ -112,6 +127,14 @@ class MoELayer:
         assert T == self.T_max, "buffers are sized for T_max rows"
         pool = self.slot_pool if slot_pool is None else slot_pool
         sh_pool = self.shared_pool if shared_pool is None else shared_pool
+        if self.fused:
+            moe_layer_decode(spec.fmt, logits, x, spec.k, spec.score, spec.renormalize, spec.scale,
+                             self.slot_of_expert, self.S, pool, self.stride, spec.I,
+                             sh_pool if spec.I_shared else None, spec.I_shared, self.ids, self.w, self.slot_offsets,
+                             self.active_slots, self.num_active, self.perm_pair, self.host_token, self.host_expert,
+                             self.host_weight, self.host_count, self.y_pairs, self.y, self.ws, stream,
+                             route_counts=self.route_counts)
+            return self.y
         main = torch.cuda.current_stream() if stream is None else stream
         if spec.I_shared:
             self.sh_fork.record(main)

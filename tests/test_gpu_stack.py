@@ -26,7 +26,7 @@ pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 WL = W.DSV3_STACK
 N_BLOBS, N_SHARED = 256, 8
 SAMPLE_LAYERS = (0, 29, 57)
-NODES_PER_LAYER = 8  # route + batches, 2 expert-FFN kernels, 2 shared-FFN kernels + their K-split reductions, combine
+NODES_PER_LAYER = 4  # the fused decode layer: route + batches + shared gate/up, routed gate/up + shared down, down, combine
 
 
 def blob_of(l, e):
@@ -92,7 +92,7 @@ def _check_replay(ctx, check_layers, lgs=None):
         O.set_threads(THREADS)
         want = O.moe_layer(WL.fmt, experts, WL.H, WL.I, ctx["xs"][l].astype(np.float64), lgs[l], WL.k,
                            WL.score, WL.renormalize, WL.scale, maps[l], ctx["shared"][shared_of(l)], F.Q8_0,
-                           WL.I_shared)
+                           WL.I_shared, S=st.S)
         err = rel_max_err(st.layers[l].y.cpu().numpy(), want["y"])
         say(f"  layer {l}: max|y-y*|/max|y*| = {err:.2e}")
         assert err <= 2e-3
