@@ -67,22 +67,26 @@ __device__ __forceinline__ float fast_silu(float z) {
     return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
 }
 
-// d*sc_j and dmin*m_j of the eight sub-blocks of a Q4_K super-block header
-// (16 bytes: d, dmin, then the 12 packed scale bytes).
-__device__ __forceinline__ void q4k_header(const uint4 h, float* ds, float* dm) {
-    const float d = half_to_float(h.x);
-    const float dmin = half_to_float(h.x >> 16);
-    const uint32_t a = h.y, b = h.z, c = h.w;
-    const uint32_t sc_lo = a & 0x3F3F3F3Fu;
-    const uint32_t m_lo = b & 0x3F3F3F3Fu;
-    const uint32_t sc_hi = (c & 0x0F0F0F0Fu) | ((a >> 2) & 0x30303030u);
-    const uint32_t m_hi = ((c >> 4) & 0x0F0F0F0Fu) | ((b >> 2) & 0x30303030u);
+// sc_j and m_j (integers 0..63, as floats) of sub-blocks 4h..4h+3 of a Q4_K
+// super-block header (16 bytes: fp16 d and dmin, then the 12 packed scale
+// bytes).  Four 6-bit fields are gathered one per byte, then each byte
+// converts with v_cvt_f32_ubyteN; the empty asm keeps the compiler from
+// folding the masks into one bit-field extract per field.
+__device__ __forceinline__ void q4k_half_scales(const uint4 hd, int h, float* sc, float* mn) {
+    uint32_t s, m;
+    if (h == 0) {
+        s = hd.y & 0x3F3F3F3Fu;
+        m = hd.z & 0x3F3F3F3Fu;
+    } else {
+        s = (hd.w & 0x0F0F0F0Fu) | ((hd.y >> 2) & 0x30303030u);
+        m = ((hd.w >> 4) & 0x0F0F0F0Fu) | ((hd.z >> 2) & 0x30303030u);
+    }
+    asm("" : "+v"(s), "+v"(m));
+    const float d = half_to_float(hd.x), dmin = half_to_float(hd.x >> 16);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        ds[j] = d * (float)((sc_lo >> (8 * j)) & 0xFFu);
-        dm[j] = dmin * (float)((m_lo >> (8 * j)) & 0xFFu);
-        ds[j + 4] = d * (float)((sc_hi >> (8 * j)) & 0xFFu);
-        dm[j + 4] = dmin * (float)((m_hi >> (8 * j)) & 0xFFu);
+    for (int b = 0; b < 4; ++b) {
+        sc[b] = d * (float)((s >> (8 * b)) & 0xFFu);
+        mn[b] = dmin * (float)((m >> (8 * b)) & 0xFFu);
     }
 }
 

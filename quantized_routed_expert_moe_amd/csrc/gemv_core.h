@@ -580,26 +580,54 @@ __device__ __forceinline__ void load_half(__amdgpu_buffer_rsrc_t src, int uoff, 
 
 // acc[t][m] += dot of half h of the unit's weights (matrix m) with token t's
 // records; `hdr` is the unit's header (Q4_K) or block scales (Q8_0).
-template <int NT, int NMAT>
-__device__ __forceinline__ void half_dots(const UnitRegs<1, NMAT>& r, const uint4* hdr, int h, const uint32_t* lw,
-                                          const float* lc, float (*acc)[NMAT]) {
-    float ds[NMAT][8], dm[NMAT][8];
+// Q4_K half unit h; refill(j) runs after sub-block j's dot products.
+template <int NT, int NMAT, typename Refill>
+__device__ __forceinline__ void q4k_half(const UnitRegs<1, NMAT>& r, const uint4* hdr, int h, const uint32_t* lw,
+                                         const float* lc, float (*acc)[NMAT], Refill refill) {
     const AndOr k(0x000F000Fu, 0x00F000F0u, 0, 0);
+    float ds[NMAT][4], dm[NMAT][4];
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) q4k_header(hdr[m], ds[m], dm[m]);
+    for (int m = 0; m < NMAT; ++m) q4k_half_scales(hdr[m], h, ds[m], dm[m]);
 #pragma unroll
-    for (int j = 4 * h; j < 4 * h + 4; ++j) {
+    for (int i = 0; i < 4; ++i) {
+        const int j = 4 * h + i;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const uint32_t* X = lw + (t * 8 + j) * 16;
             const float c = lc[(t * 8 + j) * 2], sx = lc[(t * 8 + j) * 2 + 1];
 #pragma unroll
-            for (int m = 0; m < NMAT; ++m) acc[t][m] += ds[m][j] * (q4k_dot<NMAT == 2>(r.q[j][m], X, k) - c) - dm[m][j] * sx;
+            for (int m = 0; m < NMAT; ++m)
+                acc[t][m] = fmaf(ds[m][i], q4k_dot<NMAT == 2>(r.q[j][m], X, k) - c, fmaf(-dm[m][i], sx, acc[t][m]));
         }
+        refill(j);
         // keep the scheduler from hoisting every sub-block's nibble
-        // extraction at once
+        // extraction at once (and a refill above its sub-block's last use)
         __builtin_amdgcn_sched_barrier(0);
     }
+}
+
+template <int NT, int NMAT>
+__device__ __forceinline__ void half_dots(const UnitRegs<1, NMAT>& r, const uint4* hdr, int h, const uint32_t* lw,
+                                          const float* lc, float (*acc)[NMAT]) {
+    q4k_half<NT, NMAT>(r, hdr, h, lw, lc, acc, [](int) {});
+}
+
+// The same, refilling each sub-block's weight registers with that sub-block
+// of the unit at byte offset `unext` as soon as its dot products are done
+// (the header with sub-block 0): a load then has seven eighths of a unit's
+// compute to arrive in, instead of half with a refill per half unit.
+template <int NT, int NMAT>
+__device__ __forceinline__ void half_dots_refill(UnitRegs<1, NMAT>& r, const uint4* hdr, int h, const uint32_t* lw,
+                                                 const float* lc, float (*acc)[NMAT], __amdgpu_buffer_rsrc_t src,
+                                                 int unext, int lane, uint4* hn) {
+    q4k_half<NT, NMAT>(r, hdr, h, lw, lc, acc, [&](int j) {
+        if (j == 0) {
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) hn[m] = ldb16(src, lane * 16, unext + m * 1024);
+        }
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) r.q[j][m] = ldb16(src, lane * 16, unext + NMAT * 1024 + j * NMAT * 1024 + m * 1024);
+    });
 }
 template <int NT, int NMAT>
 __device__ __forceinline__ void half_dots(const UnitRegs<0, NMAT>& r, const uint2* sc, int h, const uint32_t* lw,
@@ -709,12 +737,13 @@ __device__ __forceinline__ void load_half(__amdgpu_buffer_rsrc_t src, int uoff, 
 template <int NT, int NMAT>
 __device__ __forceinline__ void half_dots(const UnitRegs<4, NMAT>& r, const uint4* hdr, int h, const uint32_t* lw,
                                           const float* lc, float (*acc)[NMAT]) {
-    float ds[NMAT][8], dm[NMAT][8];
     const AndOr k(0x000F000Fu, 0x00F000F0u, 0x00100010u, 0x01000100u);
+    float ds[NMAT][4], dm[NMAT][4];
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) q4k_header(hdr[m], ds[m], dm[m]);
+    for (int m = 0; m < NMAT; ++m) q4k_half_scales(hdr[m], h, ds[m], dm[m]);
 #pragma unroll
-    for (int j = 4 * h; j < 4 * h + 4; ++j) {
+    for (int i = 0; i < 4; ++i) {
+        const int j = 4 * h + i;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const uint32_t* X = lw + (t * 8 + j) * 16;
@@ -722,9 +751,9 @@ __device__ __forceinline__ void half_dots(const UnitRegs<4, NMAT>& r, const uint
 #pragma unroll
             for (int m = 0; m < NMAT; ++m) {
                 const uint4 hv = r.hb[h][m];
-                const int i = j & 3;
                 const uint32_t hb = i == 0 ? hv.x : i == 1 ? hv.y : i == 2 ? hv.z : hv.w;
-                acc[t][m] += ds[m][j] * (q5k_dot<NMAT == 2>(r.q[j][m], hb, X, k) - c) - dm[m][j] * sx;
+                acc[t][m] = fmaf(ds[m][i], q5k_dot<NMAT == 2>(r.q[j][m], hb, X, k) - c,
+                                 fmaf(-dm[m][i], sx, acc[t][m]));
             }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -844,16 +873,23 @@ __device__ __forceinline__ void gemv_units(__amdgpu_buffer_rsrc_t src, int u0, i
         act_load<FMT, NMAT, RB, NT, SRC>(xrow, x_dtype, rec_g, rcs_g, min(u0 + ul + 1, ulast) * RB, lane, a,
                                            sw);
         __builtin_amdgcn_sched_barrier(0);
-        half_dots<NT, NMAT>(w, hc, 0, lw, lc, acc);
-        load_half(src, unext, lane, 0, w, hn);
-        __builtin_amdgcn_sched_barrier(0);
-        half_dots<NT, NMAT>(w, hc, 1, lw, lc, acc);
-        load_half(src, unext, lane, 1, w, hn);
+        if constexpr (FMT == 1) {
+            half_dots_refill<NT, NMAT>(w, hc, 0, lw, lc, acc, src, unext, lane, hn);
+            half_dots_refill<NT, NMAT>(w, hc, 1, lw, lc, acc, src, unext, lane, hn);
+        } else {
+            half_dots<NT, NMAT>(w, hc, 0, lw, lc, acc);
+            load_half(src, unext, lane, 0, w, hn);
+            __builtin_amdgcn_sched_barrier(0);
+            half_dots<NT, NMAT>(w, hc, 1, lw, lc, acc);
+            load_half(src, unext, lane, 1, w, hn);
+        }
         __builtin_amdgcn_sched_barrier(0);
     };
-    for (int ul = 0; ul < nu; ul += 2) {
+#pragma unroll 1
+    for (int ul = 0; ul < nu; ++ul) {
         unit(ul, hdr0, hdr1);
-        if (ul + 1 < nu) unit(ul + 1, hdr1, hdr0);
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) hdr0[m] = hdr1[m];
     }
 }
 
@@ -1026,10 +1062,7 @@ __device__ __forceinline__ void gemv_body_r(const uint8_t* __restrict__ pool, co
         }
         // the last unit re-requested unit u0 for the next chunk; with an odd
         // unit count its header went to the second slot
-        if (PIPE && again && (nu & 1)) {
-#pragma unroll
-            for (int m = 0; m < NMAT; ++m) hdr0[m] = hdr1[m];
-        }
+
 #pragma unroll
         for (int i = 0; i < kMaxTok; ++i)
 #pragma unroll
