@@ -375,8 +375,9 @@ moe_status moe_expert_ffn_q6k(const void* slot_pool, size_t slot_stride, int S, 
  */
 size_t moe_layer_decode_workspace_size(int format, int T, int k, int E, int S, int H, int I, int I_shared);
 moe_status moe_layer_decode(int format, const float* logits, const void* x, int x_dtype, int T, int E, int k,
-                            int score, int renormalize, float scale, const int32_t* slot_of_expert, int S, const void* slot_pool,
-                            size_t slot_stride, int H, int I, const void* shared_pool, int I_shared,
+                            int score, int renormalize, float scale, const int32_t* slot_of_expert, int S,
+                            const void* slot_pool, size_t slot_stride, int H, int I, const void* shared_pool,
+                            int I_shared,
                             int32_t* topk_ids, float* topk_w, int32_t* slot_offsets, int32_t* active_slots,
                             int32_t* num_active, int32_t* perm_pair, int32_t* host_token, int32_t* host_expert,
                             float* host_weight, int32_t* host_count, uint32_t* route_counts, float* y_pairs,

@@ -7,7 +7,8 @@ bit for bit; routing weights |w - w*| <= 1e-6 * max(1, scale); y and the
 resident pairs' y_pairs within max |y - y*| <= 2e-3 * max |y*|.  The routed
 pairs' y_pairs are bit for bit those of the separate expert-FFN call (same
 kernels); y agrees with the separate calls' combine to rounding (the shared
-expert's partial sums are split differently)."""
+expert's partial sums are split differently), and bit for bit without a
+shared expert (the same combine kernel)."""
 import dataclasses
 
 import numpy as np
@@ -69,6 +70,8 @@ def _check(wl, got, two, want, soe, S):
     say(f"  max|y-y*|/max|y*| = {err:.3e}; vs separate calls {rel_max_err(got['y'], two['y']):.1e}")
     assert err <= DECODE_TOL
     assert rel_max_err(got["y"], two["y"]) <= 1e-5
+    if wl.I_shared == 0:
+        assert np.array_equal(got["y"], two["y"]), "combine differs from the separate combine"
 
 
 SMALL_SHARED = [
@@ -84,6 +87,9 @@ SMALL_SHARED = [
     W.Workload("T=8: routing in its own launches (beyond the one-workgroup step)", F.Q4K, 512, 256, 16, 4, 8,
                I_shared=256, seed=10),
     W.Workload("E=300: routing in its own launches", F.Q4K, 256, 256, 300, 4, 2, I_shared=128, seed=11),
+    W.Workload("k=16, T=4: 64 pairs, the one-workgroup routing's limit", F.Q4K, 512, 256, 64, 16, 4, I_shared=256,
+               seed=13),
+    W.Workload("k=32, T=2: 64 pairs over two rows", F.Q4K, 512, 256, 64, 32, 2, I_shared=256, seed=14),
 ]
 
 
@@ -93,8 +99,11 @@ def test_fused_decode_layer_small(wl):
     _check(wl, *_case(wl))
 
 
-def test_fused_decode_layer_without_shared_expert():
-    wl = W.QWEN3_DECODE_T2
+@pytest.mark.parametrize("wl", [W.QWEN3_DECODE_T2,
+                                W.Workload("small Q4_K, no shared, k=16 T=4", F.Q4K, 512, 256, 32, 16, 4, seed=15),
+                                W.Workload("small Q4_K, no shared, k=32 T=2", F.Q4K, 512, 256, 64, 32, 2, seed=16)],
+                         ids=["qwen3_T2", "k16_T4", "k32_T2"])
+def test_fused_decode_layer_without_shared_expert(wl):
     say(wl.name)
     _check(wl, *_case(wl))
 
