@@ -62,8 +62,30 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
             for (int i = 0; i < 8; ++i) acc[i] = res ? fmaf(wj[jj], v[jj][i], acc[i]) : acc[i];
         }
     };
+    // The shared expert's output: one [T, H] array, or the partial sums
+    // [part][T, H] of its K-split down GEMV, added in part order.  The first
+    // kShBatch parts are requested with the first batch of pair rows, so
+    // their latency overlaps it.
+    constexpr int kShBatch = 4;
+    float u[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float us[kShBatch][8];
+#pragma unroll
+    for (int pt = 0; pt < kShBatch; ++pt)
+        if (pt < sh_parts) load8(ysh, 0, ((size_t)pt * T + t) * H + h0, us[pt]);
     load_batch(0);
     for (int e = threadIdx.x; e < E; e += blockDim.x) sm[e] = soe[e];
+#pragma unroll
+    for (int pt = 0; pt < kShBatch; ++pt)
+        if (pt < sh_parts) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) u[i] += us[pt][i];
+        }
+    for (int pt = kShBatch; pt < sh_parts; ++pt) {
+        float v8[8];
+        load8(ysh, 0, ((size_t)pt * T + t) * H + h0, v8);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) u[i] += v8[i];
+    }
     __syncthreads();
     add_batch(0);
     for (int j0 = kBatch; j0 < k; j0 += kBatch) {
@@ -71,15 +93,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
         add_batch(j0);
     }
     if (sh_parts > 0) {
-        // the shared expert's output: one [T, H] array, or the partial sums
-        // [part][T, H] of its K-split down GEMV, added in part order
-        float u[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int pt = 0; pt < sh_parts; ++pt) {
-            float v8[8];
-            load8(ysh, 0, ((size_t)pt * T + t) * H + h0, v8);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) u[i] += v8[i];
-        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] += u[i];
     }
