@@ -69,9 +69,20 @@ def _row_errors(layer, fx, fh, fw=lambda a: a) -> np.ndarray:
 @pytest.mark.parametrize("block", [2048, 256, 32])
 def test_int8_activations_exceed_the_prefill_tolerance(layer, block):
     err = _row_errors(layer, lambda v: _q8(v, block), lambda v: _q8(v, min(block, v.size)))
+    print(f"x and h int8, one scale per {block}: max per-row error {err.max():.3e}, median {np.median(err):.3e}")
+    assert err.max() > PREFILL_TOL, err.max()
+
+
+def test_int8_x_alone_exceeds_it(layer):
+    """Only the gate/up GEMM's input quantized, one scale per 32 elements (the
+    Q4_K sub-block, as an int8 MFMA per sub-block would take it), weights and
+    h exact: still over the bound on some row."""
+    err = _row_errors(layer, lambda v: _q8(v, 32), lambda v: v)
+    print(f"x int8 per 32, weights and h exact: max per-row error {err.max():.3e}, median {np.median(err):.3e}")
     assert err.max() > PREFILL_TOL, err.max()
 
 
 def test_bf16_rounding_model_stays_inside_it(layer):
     err = _row_errors(layer, lambda v: v, _bf16, _bf16)
+    print(f"bf16 model: max per-row error {err.max():.3e}, median {np.median(err):.3e}")
     assert err.max() < PREFILL_TOL, err.max()
