@@ -117,6 +117,27 @@ __global__ __launch_bounds__(512) void layer_l1_kernel(GemvArgs gu, int r_tiles,
     gemv_body<FMT, 2, PIPE>(gu, b % r_tiles, (b / r_tiles) % r_slots, b / (r_tiles * r_slots));
 }
 
+// The fused layer's L1 for Q4_K experts: the routed gate/up over half
+// tiles (gateup_ht_body: workgroup b is half tile b % r_halves of active
+// slot b / r_halves, so the active slots' workgroups form a prefix of the
+// grid), then the shared down GEMV's workgroups as in layer_l1_kernel.
+// Three waves per SIMD.
+constexpr int kHtWaves = 4;
+__global__ __launch_bounds__(64 * kHtWaves) __attribute__((amdgpu_waves_per_eu(3))) void layer_l1_ht_kernel(
+    GemvArgs gu, int r_halves, GemvArgs sh_dn, int sh_tiles, int n_sh) {
+    const int nr = gridDim.x - n_sh;
+    const int b = blockIdx.x;
+    if (b >= nr) {
+        const int j = b - nr;
+        gemv_body<0, 1, false, true, 1>(sh_dn, j % sh_tiles, 0, j / sh_tiles);
+        return;
+    }
+    gateup_ht_body(gu, b % r_halves, b / r_halves);
+}
+
+// Whether the fused layer's L1 runs the half-tile kernel (Q4_K gate/up).
+static bool l1_half_tiles(const FfnArgs& a) { return a.format == 1; }
+
 // gate/up + SwiGLU (and, with sd, the shared expert's down GEMV in the same
 // launch), or down, of one expert-FFN call.
 static hipError_t launch_ffn_stage(const FfnArgs& a, bool gateup, SharedDown* sd, hipStream_t s) {
@@ -141,6 +162,30 @@ static hipError_t launch_ffn_stage(const FfnArgs& a, bool gateup, SharedDown* sd
         const GemvLaunch g{a.pool, a.stride, a.S, a.H, a.I, 0, a.x, a.x_dtype, nullptr, nullptr, a.T, a.k,
                            a.slot_offsets, a.active_slots, a.num_active, a.perm_pair, hw, hcs, nullptr, upw,
                            kparts, part};
+        if (sd && l1_half_tiles(a)) {
+            const int upw_ht = (units + kHtWaves - 1) / kHtWaves;
+            const int sh_units = sd->I_shared / 128, sh_tiles = a.H / 64;
+            sd->dn_parts = (sh_units + kHtWaves - 1) / kHtWaves;
+            const int n_sh = sh_tiles * sd->dn_parts;
+            GemvArgs dn{};
+            dn.pool = sd->pool;
+            dn.S = 1;
+            dn.K = sd->I_shared;
+            dn.rows = a.H;
+            dn.section = q8_gateup_bytes(a.H, sd->I_shared);
+            dn.T = a.T;
+            dn.k = 1;
+            dn.units_per_wave = 1;
+            dn.part = sd->dn_part;
+            dn.sw = SwiSrc{sd->gu_part, sd->gu_parts, a.T, sd->I_shared};
+            const GemvArgs gu{a.pool, a.stride, a.S, a.H, a.I, 0, a.x, a.x_dtype, nullptr, nullptr, a.T, a.k,
+                              a.slot_offsets, a.active_slots, a.num_active, a.perm_pair, hw, hcs, nullptr, upw_ht,
+                              nullptr, SwiSrc{}};
+            const int r_halves = 2 * (a.I / 64);
+            launch_timed(layer_l1_ht_kernel, dim3(n_sh + r_halves * max_active), dim3(64 * kHtWaves), 0, s, ev.start,
+                         ev.stop, gu, r_halves, dn, sh_tiles, n_sh);
+            return hipGetLastError();
+        }
         if (sd) {
             // the shared down GEMV: one unit per wave, the K split over this
             // launch's workgroup size
@@ -246,6 +291,7 @@ hipError_t launch_ffn_decode_with_shared(const FfnArgs& a, SharedDown* sd, hipSt
 }
 
 int ffn_gateup_waves(const FfnArgs& a) {
+    if (l1_half_tiles(a)) return kHtWaves;
     const size_t P = (size_t)a.T * a.k;
     const int max_active = (int)std::min<size_t>((size_t)a.S, P);
     const int fgu = a.format == 3 ? 3 : a.format;

@@ -581,7 +581,7 @@ __device__ __forceinline__ void load_half(__amdgpu_buffer_rsrc_t src, int uoff, 
 // acc[t][m] += dot of half h of the unit's weights (matrix m) with token t's
 // records; `hdr` is the unit's header (Q4_K) or block scales (Q8_0).
 // Q4_K half unit h; refill(j) runs after sub-block j's dot products.
-template <int NT, int NMAT, typename Refill>
+template <int NT, int NMAT, typename Refill, bool AO = NMAT == 2>
 __device__ __forceinline__ void q4k_half(const UnitRegs<1, NMAT>& r, const uint4* hdr, int h, const uint32_t* lw,
                                          const float* lc, float (*acc)[NMAT], Refill refill) {
     const AndOr k(0x000F000Fu, 0x00F000F0u, 0, 0);
@@ -597,7 +597,7 @@ __device__ __forceinline__ void q4k_half(const UnitRegs<1, NMAT>& r, const uint4
             const float c = lc[(t * 8 + j) * 2], sx = lc[(t * 8 + j) * 2 + 1];
 #pragma unroll
             for (int m = 0; m < NMAT; ++m)
-                acc[t][m] = fmaf(ds[m][i], q4k_dot<NMAT == 2>(r.q[j][m], X, k) - c, fmaf(-dm[m][i], sx, acc[t][m]));
+                acc[t][m] = fmaf(ds[m][i], q4k_dot<AO>(r.q[j][m], X, k) - c, fmaf(-dm[m][i], sx, acc[t][m]));
         }
         refill(j);
         // keep the scheduler from hoisting every sub-block's nibble
@@ -897,7 +897,7 @@ __device__ __forceinline__ void gemv_units(__amdgpu_buffer_rsrc_t src, int u0, i
 // of the down matrix's input block i/32 (same format as the weights).
 template <int FMT>
 __device__ __forceinline__ void store_h_record(float h, int rg, int lane, uint32_t* __restrict__ hw_q,
-                                               float2* __restrict__ hcs_q) {
+                                               float2* __restrict__ hcs_q, bool active = true) {
     const int blk = 2 * rg + (lane >> 5);
     const int e = lane & 31;
     int word, half;
@@ -913,17 +913,17 @@ __device__ __forceinline__ void store_h_record(float h, int rg, int lane, uint32
         half = bb >> 1;
     }
     const uint32_t bits = float_to_half_bits(v);
-    reinterpret_cast<uint16_t*>(hw_q + (size_t)blk * 16)[word * 2 + half] = (uint16_t)bits;
+    if (active) reinterpret_cast<uint16_t*>(hw_q + (size_t)blk * 16)[word * 2 + half] = (uint16_t)bits;
     if (FMT == 5) {
         // per 16-element half (a row of 16 lanes): K = 1024 * sum of the
         // stored values + 32 * sum h
         const float kh = fmaf(32.0f, row16_sum(h), 1024.0f * row16_sum(half_to_float(bits)));
-        if ((e & 15) == 0) reinterpret_cast<float*>(hcs_q + blk)[e >> 4] = kh;
+        if (active && (e & 15) == 0) reinterpret_cast<float*>(hcs_q + blk)[e >> 4] = kh;
         return;
     }
     const float c = half_wave_sum(half_to_float(bits)) * (FMT == 0 ? 1152.0f : 1024.0f);
     const float sx = half_wave_sum(h);
-    if (e == 0) hcs_q[blk] = make_float2(c, sx);
+    if (active && e == 0) hcs_q[blk] = make_float2(c, sx);
 }
 
 // One launch's arguments of the GEMV body.
@@ -1089,6 +1089,124 @@ __device__ __forceinline__ void gemv_body_r(const uint8_t* __restrict__ pool, co
                     const int p = IDENT ? q : perm[q];
                     if (p >= 0 && p < P) y_pairs[(size_t)p * rows + rg * 64 + lane] = v[0];
                 }
+            }
+        }
+        if (c + kMaxTok < q1) __syncthreads();  // red[] is reused by the next chunk
+    }
+}
+
+// ------------------------------------------------ Q4_K gate/up, half tiles
+// The same GEMV over half a 64-row tile: lanes 0-31 take gate rows
+// 32 hh .. 32 hh + 31 of the tile, lanes 32-63 the up rows of the same
+// features (one matrix per lane instead of both), reading the packed tile
+// as it is (512 contiguous bytes per matrix and chunk).  A unit's weights
+// then take half the registers, so three waves fit per SIMD, and a
+// workgroup's work is half a tile's: finer pieces for the dispatcher to
+// spread over the CUs when active slots x tiles is not a multiple of the
+// CU count.  SwiGLU pairs lane r's gate sum with lane r + 32's up sum.
+
+// lane's byte offset in a unit of the packed gate/up tile: its matrix's
+// 1 KB blocks, its row's 16 bytes
+__device__ __forceinline__ int ht_lane_offset(int lane, int hh) { return (lane >> 5) * 1024 + (hh * 32 + (lane & 31)) * 16; }
+
+template <int NT>
+__device__ __forceinline__ void ht_units(__amdgpu_buffer_rsrc_t src, int u0, int nu, int loff, int lane, bool again,
+                                         UnitRegs<1, 1>& w, uint4* hdr0, uint4* hdr1, const void* const* xrow,
+                                         int x_dtype, uint32_t* lw, float* lc, float (*acc)[1]) {
+    constexpr int RB = Unit<1>::kRecords;
+    constexpr int TB = tile_bytes<1, 2>();
+    const uint32_t* rec_g[kMaxTok] = {};
+    const float2* rcs_g[kMaxTok] = {};
+    ActRegs a;
+    const int ulast = u0 + nu - 1;
+    act_load<1, 2, RB, NT>(xrow, x_dtype, rec_g, rcs_g, u0 * RB, lane, a);
+    act_arrived<1, 2, NT>(a);
+#pragma unroll 1
+    for (int ul = 0; ul < nu; ++ul) {
+        const int unext = ul + 1 < nu ? (u0 + ul + 1) * TB : again ? u0 * TB : kPastEnd;
+        __builtin_amdgcn_sched_barrier(0);
+        act_store<1, 2, RB, NT>(a, x_dtype, lane, lw, lc);
+        act_load<1, 2, RB, NT>(xrow, x_dtype, rec_g, rcs_g, min(u0 + ul + 1, ulast) * RB, lane, a);
+        __builtin_amdgcn_sched_barrier(0);
+        const auto refill = [&](int j) {
+            if (j == 0) hdr1[0] = ldb16(src, loff, unext);
+            w.q[j][0] = ldb16(src, loff, unext + 2048 + j * 2048);
+        };
+        q4k_half<NT, 1, decltype(refill), true>(w, hdr0, 0, lw, lc, acc, refill);
+        q4k_half<NT, 1, decltype(refill), true>(w, hdr0, 1, lw, lc, acc, refill);
+        __builtin_amdgcn_sched_barrier(0);
+        hdr0[0] = hdr1[0];
+    }
+}
+
+// Workgroup (bx, by) = (half tile: 64-row tile bx / 2, half bx % 2; active
+// slot index by), its waves splitting K (units_per_wave each).  Writes the
+// h records of the half tile's 32 features at each of the slot's pair
+// positions.
+__device__ __forceinline__ void gateup_ht_body(const GemvArgs& g, int bx, int by) {
+    __shared__ __align__(16) uint32_t stage_w[kMaxWaves][kStageWords];
+    __shared__ __align__(16) float stage_c[kMaxWaves][kStageFloats];
+    __shared__ float red[kMaxWaves][kMaxTok][64];
+    const int na = *g.num_active;
+    const int slot = g.active[by];
+    if (by >= na || slot < 0 || slot >= g.S) return;
+    const int rg = bx >> 1, hh = bx & 1;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+    const int K = g.K, rows = g.rows, k = g.k;
+    const int units = K / 256;
+    constexpr int TB = tile_bytes<1, 2>();
+    const int u0 = min(units, wave * g.units_per_wave), nu = min(units, u0 + g.units_per_wave) - u0;
+    const uint8_t* tiles = g.pool + (size_t)slot * g.stride + g.section + (size_t)rg * units * TB;
+    const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc((void*)tiles, 0, units * TB, kBufferDword3);
+    const int loff = ht_lane_offset(lane, hh);
+    UnitRegs<1, 1> w;
+    uint4 hdr0[1], hdr1[1];
+    if (nu > 0) {
+        hdr0[0] = ldb16(src, loff, u0 * TB);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w.q[j][0] = ldb16(src, loff, u0 * TB + 2048 + j * 2048);
+    }
+    const int P = g.T * k;
+    const int q0 = g.offsets[slot], q1 = g.offsets[slot + 1];
+    if (q0 < 0 || q1 > P || q1 < q0) return;
+    uint32_t* lw = stage_w[wave];
+    float* lc = stage_c[wave];
+    for (int c = q0; c < q1; c += kMaxTok) {
+        const int nt = min(kMaxTok, q1 - c);
+        const void* xrow[kMaxTok];
+#pragma unroll
+        for (int i = 0; i < kMaxTok; ++i) {
+            const int p = g.perm[c + min(i, nt - 1)];
+            const size_t row = (p >= 0 && p < P) ? (size_t)(p / k) : 0;
+            xrow[i] = g.x_dtype == 0 ? (const void*)(static_cast<const float*>(g.x) + row * K)
+                                     : (const void*)(static_cast<const uint16_t*>(g.x) + row * K);
+        }
+        const bool again = c + kMaxTok < q1;
+        float acc[kMaxTok][1];
+#pragma unroll
+        for (int i = 0; i < kMaxTok; ++i) acc[i][0] = 0.f;
+        if (nu > 0) {
+            if (nt == 1)
+                ht_units<1>(src, u0, nu, loff, lane, again, w, hdr0, hdr1, xrow, g.x_dtype, lw, lc, acc);
+            else
+                ht_units<2>(src, u0, nu, loff, lane, again, w, hdr0, hdr1, xrow, g.x_dtype, lw, lc, acc);
+        }
+#pragma unroll
+        for (int i = 0; i < kMaxTok; ++i) red[wave][i][lane] = acc[i][0];
+        __syncthreads();
+        if (wave == 0) {
+            const int r = lane & 31;
+            const int nblk_out = rows / 32;
+            for (int i = 0; i < nt; ++i) {
+                float gs = 0.f, us = 0.f;
+                for (int wv = 0; wv < nw; ++wv) {
+                    gs += red[wv][i][r];
+                    us += red[wv][i][r + 32];
+                }
+                const int q = c + i;
+                store_h_record<1>(fast_silu(gs) * us, rg, hh * 32 + r, g.hw + (size_t)q * nblk_out * 16,
+                                  g.hcs + (size_t)q * nblk_out, lane < 32);
             }
         }
         if (c + kMaxTok < q1) __syncthreads();  // red[] is reused by the next chunk

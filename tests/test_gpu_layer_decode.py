@@ -4,11 +4,13 @@ CPU oracle, and against the separate calls it replaces.
 
 Integer outputs (ids, slot offsets, active slots, permutation, host list)
 bit for bit; routing weights |w - w*| <= 1e-6 * max(1, scale); y and the
-resident pairs' y_pairs within max |y - y*| <= 2e-3 * max |y*|.  The routed
-pairs' y_pairs are bit for bit those of the separate expert-FFN call (same
-kernels); y agrees with the separate calls' combine to rounding (the shared
-expert's partial sums are split differently), and bit for bit without a
-shared expert (the same combine kernel)."""
+resident pairs' y_pairs within max |y - y*| <= 2e-3 * max |y*|.  Without a
+shared expert the layer runs the separate calls' kernels, so the routed
+pairs' y_pairs and y are bit for bit theirs.  With one, the layer's gate/up
+launch (Q4_K: over half tiles, four waves splitting K) may split K at other
+points than the separate call, so the fp32 sums round differently and an h
+value can land on the neighbouring fp16: y_pairs and y agree with the
+separate calls within SPLIT_TOL of their largest value."""
 import dataclasses
 
 import numpy as np
@@ -24,6 +26,9 @@ from tests.gpu_util import THREADS, device_layer, pack_pool, rel_max_err, run_de
 pytestmark = pytest.mark.gpu
 
 DECODE_TOL = 2e-3
+# fused vs separate calls with a shared expert: a few h values one fp16 step
+# apart (relative 2^-11) through one down row each, far below DECODE_TOL
+SPLIT_TOL = 1e-4
 
 
 def _w_tol(wl):
@@ -63,13 +68,18 @@ def _check(wl, got, two, want, soe, S):
         assert np.array_equal(got[key], ob[key]), key
     assert np.abs(got["host_weight"] - ob["host_weight"]).max(initial=0.0) <= _w_tol(wl)
     res = [p for p in range(wl.T * wl.k) if 0 <= soe[want["ids"].ravel()[p]] < S]
-    assert np.array_equal(got["y_pairs"][res], two["y_pairs"][res]), "routed y_pairs differ from the separate call"
+    if wl.I_shared == 0:
+        assert np.array_equal(got["y_pairs"][res], two["y_pairs"][res]), "routed y_pairs differ from the separate call"
+    elif res:
+        split = rel_max_err(got["y_pairs"][res], two["y_pairs"][res])
+        say(f"  routed y_pairs vs the separate call: {split:.1e}")
+        assert split <= SPLIT_TOL
     if res:
         assert rel_max_err(got["y_pairs"][res], want["y_pairs"][res]) <= DECODE_TOL
     err = rel_max_err(got["y"], want["y"])
     say(f"  max|y-y*|/max|y*| = {err:.3e}; vs separate calls {rel_max_err(got['y'], two['y']):.1e}")
     assert err <= DECODE_TOL
-    assert rel_max_err(got["y"], two["y"]) <= 1e-5
+    assert rel_max_err(got["y"], two["y"]) <= SPLIT_TOL
     if wl.I_shared == 0:
         assert np.array_equal(got["y"], two["y"]), "combine differs from the separate combine"
 
