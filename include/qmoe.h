@@ -449,6 +449,20 @@ moe_status moe_timer_end(int stage, double* total_ms, int* launches);
  * timed so far.  The timer stays armed (moe_timer_end releases it). */
 moe_status moe_timer_read(int stage, float* ms_each, int capacity, int* launches);
 
+/* ------------------------------------------------------------ read probe
+ * Measurement, not part of the MoE path: one pass of a plain streaming-read
+ * kernel over the device buffer buf (16-byte aligned), for the practical
+ * HBM read rate the decode GEMV's fraction of the spec peak can be set
+ * against.  `waves` waves (a multiple of 8, 8..65536) each read a
+ * contiguous span with 16-byte loads, `depth` (1, 2, 4, 8 or 16) of them per
+ * lane in flight; *read = the bytes read, bytes rounded down to whole
+ * spans (at least 1024 * waves * depth bytes are required).  sink: device
+ * memory for waves * 64 uint32 words, overwritten.  Enqueued on `stream`
+ * (NULL: the default stream); the caller times it.
+ */
+moe_status moe_hbm_read_probe(const void* buf, size_t bytes, int waves, int depth, uint32_t* sink, size_t* read,
+                              void* stream);
+
 #ifdef __cplusplus
 }
 #endif

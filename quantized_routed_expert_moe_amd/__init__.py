@@ -84,12 +84,13 @@ def lib() -> ctypes.CDLL:
         L.moe_timer_begin.argtypes = [i32, i32]
         L.moe_timer_end.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
         L.moe_timer_read.argtypes = [i32, vp, i32, ctypes.POINTER(ctypes.c_int)]
+        L.moe_hbm_read_probe.argtypes = [vp, sz, i32, i32, vp, ctypes.POINTER(ctypes.c_size_t), vp]
         for name in ("moe_route_topk", "moe_build_expert_batches", "moe_route_and_batch", "moe_count_routes",
                      "moe_pack_expert", "moe_unpack_expert", "moe_pack_q4k", "moe_pack_q8_0",
                      "moe_validate_slot_map", "moe_expert_ffn_q4k", "moe_expert_ffn_q8_0", "moe_expert_ffn_mxfp4",
                      "moe_expert_ffn_q3k_q4k", "moe_expert_ffn_q5k", "moe_expert_ffn_q6k", "moe_expert_ffn_q4k_noalloc",
                      "moe_combine", "moe_layer_decode",
-                     "moe_timer_begin", "moe_timer_end", "moe_timer_read"):
+                     "moe_timer_begin", "moe_timer_end", "moe_timer_read", "moe_hbm_read_probe"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -512,6 +513,17 @@ def moe_timer_read(stage: int, capacity: int) -> np.ndarray:
     n = ctypes.c_int(0)
     _check(lib().moe_timer_read(stage, out.ctypes.data, int(capacity), ctypes.byref(n)))
     return out[:min(n.value, int(capacity))].copy()
+
+
+def moe_hbm_read_probe(buf, waves: int, depth: int, sink, stream=None) -> int:
+    """One pass of the streaming-read probe over the device tensor buf; returns the bytes read."""
+    if sink.numel() * sink.element_size() < 256 * int(waves):
+        raise ValueError(f"sink holds fewer than waves x 64 words ({waves} waves)")
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_hbm_read_probe(_dev(buf, name="buf"), buf.numel() * buf.element_size(), int(waves), int(depth),
+                                    _dev(sink, name="sink"), ctypes.byref(n),
+                                    _stream(stream)))
+    return n.value
 
 
 def moe_timer_end(stage: int) -> tuple[float, int]:

@@ -1049,6 +1049,21 @@ moe_status moe_timer_read(int stage, float* ms_each, int capacity, int* launches
     return MOE_OK;
 }
 
+moe_status moe_hbm_read_probe(const void* buf, size_t bytes, int waves, int depth, uint32_t* sink, size_t* read,
+                              void* stream) {
+    if (!buf || !sink || !read) return fail(MOE_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+    if (((uintptr_t)buf & 15) != 0) return fail(MOE_ERR_INVALID_ARGUMENT, "buf must be 16-byte aligned");
+    if (waves < 8 || waves > 65536 || waves % 8 != 0)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "waves = %d is not a multiple of 8 in 8..65536", waves);
+    if (depth != 1 && depth != 2 && depth != 4 && depth != 8 && depth != 16)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "depth = %d is not 1, 2, 4, 8 or 16", depth);
+    if (bytes / 1024 / (size_t)waves < (size_t)depth)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "%zu bytes is less than 1024 x waves x depth", bytes);
+    const hipError_t e = qmoe::launch_hbm_read(buf, bytes, waves, depth, sink, read, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "read probe launch");
+    return MOE_OK;
+}
+
 moe_status moe_timer_end(int stage, double* total_ms, int* launches) {
     if (stage < 0 || stage >= qmoe::kStageCount) return fail(MOE_ERR_INVALID_ARGUMENT, "bad stage %d", stage);
     if (!total_ms || !launches) return fail(MOE_ERR_INVALID_ARGUMENT, "NULL output pointer");

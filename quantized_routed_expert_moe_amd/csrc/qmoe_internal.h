@@ -223,6 +223,11 @@ hipError_t launch_ffn_decode_with_shared(const FfnArgs& a, SharedDown* sd, hipSt
 // GEMV beside it splits its K over).
 int ffn_gateup_waves(const FfnArgs& a);
 
+// The streaming-read probe (hbm_probe.hip): reads the first `read` bytes of
+// buf (bytes rounded down to whole spans of `waves` waves).
+hipError_t launch_hbm_read(const void* buf, size_t bytes, int waves, int depth, uint32_t* sink, size_t* read,
+                           hipStream_t s);
+
 size_t prefill_workspace_bytes(int T, int k, int H, int I);
 hipError_t launch_ffn_prefill(const FfnArgs& a, hipStream_t s);  // Q4_K or MXFP4
 
