@@ -830,9 +830,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // chunks of whole rows.  Passes alternate between the two buffers, so one
     // barrier per pass suffices.  Rows are unpadded; the 16-byte chunk index
     // is xor-ed with 4 on rows whose bit 2 is set, so the two half-waves'
-    // writes (rows r and r + 4) fall in different banks.
+    // writes (rows r and r + 4) fall in different banks.  The two epilogues
+    // are compiled apart (if constexpr): each kernel's registers are then
+    // allocated for its own epilogue only.
     auto swz = [](int row, int chunk) { return chunk ^ (((row >> 2) & 1) << 2); };
-    if (GATEUP) {
+    if constexpr (GATEUP) {
         // h = silu(g) * u, rounded to bf16: all rows x 128 features (256
         // bytes per row) in one pass, stored at position qb + row.
         constexpr int kRowBytes = kGateUpFeatures * 2;
@@ -842,13 +844,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         uint16_t* hout = static_cast<uint16_t*>(out) + (size_t)nt * kGateUpFeatures;
 #pragma unroll
         for (int i = 0; i < kRowBlocks; ++i) {
-            if (i >= nblk) break;
+            if (i < nblk) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = 32 * i + 8 * (r >> 2) + 4 * hsel + (r & 3);
-                const float hv = fast_silu(acc[i][0][r]) * acc[i][1][r];
-                *reinterpret_cast<uint16_t*>(stage + row * kRowBytes + 16 * swz(row, f >> 3) + 2 * (f & 7)) =
-                    __builtin_bit_cast(uint16_t, (__bf16)hv);
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 32 * i + 8 * (r >> 2) + 4 * hsel + (r & 3);
+                    const float hv = fast_silu(acc[i][0][r]) * acc[i][1][r];
+                    *reinterpret_cast<uint16_t*>(stage + row * kRowBytes + 16 * swz(row, f >> 3) + 2 * (f & 7)) =
+                        __builtin_bit_cast(uint16_t, (__bf16)hv);
+                }
             }
         }
         __syncthreads();
@@ -858,71 +861,73 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             *reinterpret_cast<uint4*>(hout + (size_t)(qb + row) * I + 8 * cc) = v;
         }
     } else {
-        // y: 256 columns per row, 128 rows per pass in bf16, 64 in fp32; each
-        // row stored to its pair's row of y_pairs.
+        // y: 256 columns per row.  The accumulators are staged as fp32 (the
+        // LDS writes take them straight from the accumulator registers), 64
+        // rows per pass, passes alternating between the two buffers; then
+        // every thread moves 16-byte chunks (4 values) of staged rows to
+        // their pair's row of y_pairs, rounded to bf16 on the way when
+        // y_pairs is bf16 (the same single rounding of the fp32 sum).
+        constexpr int kRowBytes = kDownColumns * 4;
+        constexpr int kCpr = kRowBytes / 16;       // staged 16-byte chunks per row
+        constexpr int kPassBlocks = 2;             // row blocks per pass (one 64 KB buffer)
+        constexpr int kPassRows = 32 * kPassBlocks;
         uint8_t* y = static_cast<uint8_t*>(out);
-        auto store_rows = [&](const uint8_t* stage, int row0, int nrows, int row_bytes) {
-            const int cpr = row_bytes / 16;
-            for (int ch = tid; ch < nrows * cpr; ch += kThreads) {
-                const int rl = ch / cpr, cc = ch - rl * cpr;
-                const int p = sidx[row0 + rl];
-                if (p >= 0) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(stage + rl * row_bytes + 16 * swz(rl, cc));
-                    *reinterpret_cast<uint4*>(y + ((size_t)p * H + (size_t)nt * kDownColumns) * (row_bytes / kDownColumns) +
-                                              16 * cc) = v;
-                }
-            }
-        };
-        if (y_dtype != 0) {
-            constexpr int kRowBytes = kDownColumns * 2;
 #pragma unroll
-            for (int pass = 0; pass < 2; ++pass) {
-                if (4 * pass >= nblk) break;
-                uint8_t* stage = reinterpret_cast<uint8_t*>(pass ? sA1 : sA0);
+        for (int pass = 0; pass < 4; ++pass) {
+            if (kPassBlocks * pass >= nblk) break;
+            uint8_t* stage = reinterpret_cast<uint8_t*>((pass & 1) ? sA1 : sA0);
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    const int i = 4 * pass + ii;
-                    if (i < nblk) {
+            for (int ii = 0; ii < kPassBlocks; ++ii) {
+                const int i = kPassBlocks * pass + ii;
+                if (i < nblk) {
 #pragma unroll
-                        for (int m = 0; m < 2; ++m) {
-                            const int col = 64 * wave + 32 * m + r32;
+                    for (int m = 0; m < 2; ++m) {
+                        const int col = 64 * wave + 32 * m + r32;
 #pragma unroll
-                            for (int r = 0; r < 16; ++r) {
-                                const int rl = 32 * ii + 8 * (r >> 2) + 4 * hsel + (r & 3);
-                                *reinterpret_cast<uint16_t*>(stage + rl * kRowBytes + 16 * swz(rl, col >> 3) +
-                                                             2 * (col & 7)) =
-                                    __builtin_bit_cast(uint16_t, (__bf16)acc[i][m][r]);
-                            }
+                        for (int r = 0; r < 16; ++r) {
+                            const int rl = 32 * ii + 8 * (r >> 2) + 4 * hsel + (r & 3);
+                            *reinterpret_cast<float*>(stage + rl * kRowBytes + 16 * swz(rl, col >> 2) +
+                                                      4 * (col & 3)) = acc[i][m][r];
                         }
                     }
                 }
-                __syncthreads();
-                store_rows(stage, 128 * pass, min(128, rows - 128 * pass), kRowBytes);
             }
-        } else {
-            constexpr int kRowBytes = kDownColumns * 4;
+            __syncthreads();
+            // Thread t takes chunk t % 64 of rows t / 64 + 4 j of the pass,
+            // in batches of eight whose LDS reads (pair indices, then
+            // chunks) are all issued before the batch's global stores.
+            const int row0 = kPassRows * pass, nrows = min(kPassRows, rows - row0);
+            constexpr int kStep = kThreads / kCpr, kBatch = 8;
+            const int cc = tid % kCpr, r0 = tid / kCpr;
+            for (int rb = 0; rb < nrows; rb += kStep * kBatch) {
+                int pj[kBatch];
+                float4 v[kBatch];
 #pragma unroll
-            for (int pass = 0; pass < 4; ++pass) {
-                if (2 * pass >= nblk) break;
-                uint8_t* stage = reinterpret_cast<uint8_t*>((pass & 1) ? sA1 : sA0);
+                for (int j = 0; j < kBatch; ++j) {
+                    const int rl = rb + r0 + kStep * j;
+                    pj[j] = rl < nrows ? sidx[row0 + rl] : -1;
+                }
 #pragma unroll
-                for (int ii = 0; ii < 2; ++ii) {
-                    const int i = 2 * pass + ii;
-                    if (i < nblk) {
+                for (int j = 0; j < kBatch; ++j) {
+                    const int rl = rb + r0 + kStep * j;
+                    v[j] = *reinterpret_cast<const float4*>(stage + rl * kRowBytes + 16 * swz(rl, cc));
+                }
 #pragma unroll
-                        for (int m = 0; m < 2; ++m) {
-                            const int col = 64 * wave + 32 * m + r32;
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) {
-                                const int rl = 32 * ii + 8 * (r >> 2) + 4 * hsel + (r & 3);
-                                *reinterpret_cast<float*>(stage + rl * kRowBytes + 16 * swz(rl, col >> 2) +
-                                                          4 * (col & 3)) = acc[i][m][r];
-                            }
-                        }
+                for (int j = 0; j < kBatch; ++j) {
+                    if (pj[j] < 0) continue;
+                    const size_t e = (size_t)pj[j] * H + (size_t)nt * kDownColumns + 4 * cc;  // first element
+                    if (y_dtype != 0) {
+                        bf16x2 lo, hi;
+                        lo[0] = (__bf16)v[j].x;
+                        lo[1] = (__bf16)v[j].y;
+                        hi[0] = (__bf16)v[j].z;
+                        hi[1] = (__bf16)v[j].w;
+                        *reinterpret_cast<uint2*>(y + 2 * e) =
+                            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+                    } else {
+                        *reinterpret_cast<float4*>(y + 4 * e) = v[j];
                     }
                 }
-                __syncthreads();
-                store_rows(stage, 64 * pass, min(64, rows - 64 * pass), kRowBytes);
             }
         }
     }
