@@ -43,6 +43,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_INT8_PEAK_TOPS = 5000.0
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA util (prefill), 1 GPU"
 DSV3_GATEUP_BYTES = 2 * 7168 * 2048 // 256 * 144    # one routed Q4_K expert's gate and up matrices
 DSV3_DOWN_BYTES = 7168 * 2048 // 256 * 144
@@ -57,7 +58,7 @@ TRAFFIC = {
 }
 KERNEL_SOURCES = [os.path.join(ROOT, "quantized_routed_expert_moe_amd", "csrc", f)
                   for f in ("ffn_decode.hip", "gemv_core.h", "device_common.h", "qmoe_internal.h")]
-LEGS = ("stack", "dsv3", "prefill", "qwen3", "hbm")
+LEGS = ("stack", "dsv3", "prefill", "qwen3", "hbm", "mfma")
 STAGE_GATEUP, STAGE_DOWN, STAGE_COMBINE, STAGE_ROUTE_BATCHES = 3, 4, 5, 8
 STAGE_ROUTE, STAGE_BATCHES, STAGE_TILES, STAGE_PF_GATEUP, STAGE_PF_DOWN = 0, 1, 2, 6, 7
 
@@ -762,6 +763,36 @@ def leg_hbm(args) -> dict:
             "best_frac_of_peak": round(grid[best] / HBM_PEAK_GBS, 4), "GBs": grid}
 
 
+def leg_mfma(args) -> dict:
+    """The prefill contraction's two designs side by side, operands in
+    registers: the library's inner-loop probe (variant 0: Q4_K nibbles
+    dequantized to bf16 + v_mfma_f32_32x32x16_bf16, the prefill GEMM's
+    design; variant 1: int8 activations + v_mfma_i32_32x32x32_i8 with the
+    per-sub-block fp32 rescaling and min term Q4_K needs), 5 timed launches
+    of 4096 sub-blocks per wave after 2 untimed ones.  The rate is the flops
+    of the contraction the loop stands for per second: the ceiling a GEMM
+    built on that design reaches with its memory traffic fully hidden."""
+    import torch
+
+    import quantized_routed_expert_moe_amd as Q
+    out = torch.zeros(Q.PREFILL_PROBE_OUT_FLOATS, dtype=torch.float32, device="cuda")
+    res = {}
+    for variant, name in ((0, "bf16_dequant_mfma"), (1, "int8_mfma_rescale")):
+        for _ in range(2):
+            Q.moe_prefill_inner_probe(variant, 4096, out)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        flops = sum(Q.moe_prefill_inner_probe(variant, 4096, out) for _ in range(5))
+        e1.record()
+        torch.cuda.synchronize()
+        tf = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+        res[name] = {"TFLOPs": round(tf, 1), "frac_of_bf16_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "frac_of_int8_peak": round(tf / MFMA_INT8_PEAK_TOPS, 4)}
+    res["int8_over_bf16"] = round(res["int8_mfma_rescale"]["TFLOPs"] / res["bf16_dequant_mfma"]["TFLOPs"], 3)
+    del out
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -805,6 +836,9 @@ def main():
     if "hbm" in legs:
         progress("streaming-read probe")
         res["hbm"] = leg_hbm(args)
+    if "mfma" in legs:
+        progress("prefill inner-loop probe (bf16 vs int8 designs)")
+        res["mfma"] = leg_mfma(args)
     if extra is not None:
         progress("other card expert types")
         extra["formats"] = bench_formats(args, thr)
@@ -845,6 +879,7 @@ def main():
         "c3_prefill": res.get("prefill"),
         "c2_decode_T2": res.get("qwen3"),
         "hbm_read_probe": res.get("hbm"),
+        "prefill_inner_loop_probe": res.get("mfma"),
         "host_threads": thr,
         "wall_s": round(time.time() - t_start, 1),
     }

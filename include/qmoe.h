@@ -463,6 +463,26 @@ moe_status moe_timer_read(int stage, float* ms_each, int capacity, int* launches
 moe_status moe_hbm_read_probe(const void* buf, size_t bytes, int waves, int depth, uint32_t* sink, size_t* read,
                               void* stream);
 
+/* ------------------------------------------------------- prefill inner-loop probe
+ * Measurement, not part of the MoE path: the issue rate of the per-Q4_K-
+ * sub-block instruction mix of two ways to run the prompt contraction on the
+ * matrix cores (bloomery README 0.3.1, "Why it is fast": prompts as int8
+ * tensor-core GEMMs), with operands in registers and no memory traffic.
+ * variant 0: weights dequantized to bf16 and bf16 MFMA (the prefill GEMM's
+ * design, a 256 x 64 tile per wave); variant 1: int8 activations and the
+ * nibbles as int8 on the i8 MFMA, each sub-block's integer sums converted
+ * and scaled into fp32 accumulators with the min term from the activations'
+ * sums (a 128 x 64 tile per wave, two waves per SIMD).  Every wave runs
+ * `sub_blocks` (1..1048576) sub-blocks of its tile: 1024 x sub_blocks x
+ * 1,048,576 flops per launch for either variant (each sub-block counted as
+ * the 2 x rows x 64 x 32 flops of the contraction it stands for).  out:
+ * device memory for at least 131072 floats (overwritten with one sum per
+ * thread).  Enqueued on `stream` (NULL: the default stream); the caller
+ * times it.
+ */
+#define MOE_PREFILL_PROBE_OUT_FLOATS 131072
+moe_status moe_prefill_inner_probe(int variant, int sub_blocks, float* out, size_t out_floats, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -85,12 +85,14 @@ def lib() -> ctypes.CDLL:
         L.moe_timer_end.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
         L.moe_timer_read.argtypes = [i32, vp, i32, ctypes.POINTER(ctypes.c_int)]
         L.moe_hbm_read_probe.argtypes = [vp, sz, i32, i32, vp, ctypes.POINTER(ctypes.c_size_t), vp]
+        L.moe_prefill_inner_probe.argtypes = [i32, i32, vp, sz, vp]
         for name in ("moe_route_topk", "moe_build_expert_batches", "moe_route_and_batch", "moe_count_routes",
                      "moe_pack_expert", "moe_unpack_expert", "moe_pack_q4k", "moe_pack_q8_0",
                      "moe_validate_slot_map", "moe_expert_ffn_q4k", "moe_expert_ffn_q8_0", "moe_expert_ffn_mxfp4",
                      "moe_expert_ffn_q3k_q4k", "moe_expert_ffn_q5k", "moe_expert_ffn_q6k", "moe_expert_ffn_q4k_noalloc",
                      "moe_combine", "moe_layer_decode",
-                     "moe_timer_begin", "moe_timer_end", "moe_timer_read", "moe_hbm_read_probe"):
+                     "moe_timer_begin", "moe_timer_end", "moe_timer_read", "moe_hbm_read_probe",
+                     "moe_prefill_inner_probe"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -524,6 +526,19 @@ def moe_hbm_read_probe(buf, waves: int, depth: int, sink, stream=None) -> int:
                                     _dev(sink, name="sink"), ctypes.byref(n),
                                     _stream(stream)))
     return n.value
+
+
+PREFILL_PROBE_OUT_FLOATS = 131072  # MOE_PREFILL_PROBE_OUT_FLOATS
+
+
+def moe_prefill_inner_probe(variant: int, sub_blocks: int, out, stream=None) -> float:
+    """One launch of the prefill inner-loop probe (variant 0: bf16
+    dequantization + bf16 MFMA; 1: int8 MFMA + fp32 rescaling per
+    sub-block); returns the flops the launch stands for."""
+    import torch
+    ptr = _dev(out, (torch.float32,), name="out")
+    _check(lib().moe_prefill_inner_probe(int(variant), int(sub_blocks), ptr, out.numel(), _stream(stream)))
+    return 1024.0 * int(sub_blocks) * 2 * 256 * 64 * 32
 
 
 def moe_timer_end(stage: int) -> tuple[float, int]:

@@ -1064,6 +1064,20 @@ moe_status moe_hbm_read_probe(const void* buf, size_t bytes, int waves, int dept
     return MOE_OK;
 }
 
+moe_status moe_prefill_inner_probe(int variant, int sub_blocks, float* out, size_t out_floats, void* stream) {
+    if (!out) return fail(MOE_ERR_INVALID_ARGUMENT, "out is NULL");
+    if (variant != 0 && variant != 1) return fail(MOE_ERR_INVALID_ARGUMENT, "variant = %d is not 0 or 1", variant);
+    if (sub_blocks < 1 || sub_blocks > (1 << 20))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "sub_blocks = %d is not in 1..1048576", sub_blocks);
+    if (out_floats < (size_t)MOE_PREFILL_PROBE_OUT_FLOATS)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "out holds %zu floats, fewer than %d", out_floats,
+                    MOE_PREFILL_PROBE_OUT_FLOATS);
+    static_assert(qmoe::kPrefillProbeWorkgroups * 256 == MOE_PREFILL_PROBE_OUT_FLOATS, "probe output size");
+    const hipError_t e = qmoe::launch_prefill_probe(variant, sub_blocks, out, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "prefill probe launch");
+    return MOE_OK;
+}
+
 moe_status moe_timer_end(int stage, double* total_ms, int* launches) {
     if (stage < 0 || stage >= qmoe::kStageCount) return fail(MOE_ERR_INVALID_ARGUMENT, "bad stage %d", stage);
     if (!total_ms || !launches) return fail(MOE_ERR_INVALID_ARGUMENT, "NULL output pointer");

@@ -223,6 +223,13 @@ hipError_t launch_ffn_decode_with_shared(const FfnArgs& a, SharedDown* sd, hipSt
 // GEMV beside it splits its K over).
 int ffn_gateup_waves(const FfnArgs& a);
 
+// The prefill inner-loop probe (prefill_probe.hip): variant 0 (bf16
+// dequantization + bf16 MFMA) or 1 (int8 MFMA + per-sub-block fp32
+// rescaling), sub_blocks iterations per wave, one float per thread into out
+// (kPrefillProbeWorkgroups x 256 floats).
+constexpr int kPrefillProbeWorkgroups = 512;
+hipError_t launch_prefill_probe(int variant, int sub_blocks, float* out, hipStream_t s);
+
 // The streaming-read probe (hbm_probe.hip): reads the first `read` bytes of
 // buf (bytes rounded down to whole spans of `waves` waves).
 hipError_t launch_hbm_read(const void* buf, size_t bytes, int waves, int depth, uint32_t* sink, size_t* read,
