@@ -30,12 +30,35 @@ SIGMOID = 1
 _lib = None
 
 
-def build() -> str:
-    """Compile the oracle with gcc: -O2, OpenMP, strict IEEE (no fast-math)."""
-    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", _SRC, "-o", _SO + ".tmp", "-lm"]
+def build(src: str = _SRC, out: str = _SO) -> str:
+    """Compile the oracle (or, for the pin tests' mutants, another version of
+    its source) with gcc: -O2, OpenMP, strict IEEE (no fast-math)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-I" + _HERE, src, "-o", out + ".tmp", "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(_SO + ".tmp", _SO)
-    return _SO
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def _bind(path: str) -> ctypes.CDLL:
+    L = ctypes.CDLL(path)
+    i32, i64, f64, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+    L.oracle_dequant_q8_0.argtypes = [vp, i64, vp]
+    L.oracle_dequant_q4k.argtypes = [vp, i64, vp]
+    L.oracle_dequant_mxfp4.argtypes = [vp, i64, vp]
+    L.oracle_dequant_q3k.argtypes = [vp, i64, vp]
+    L.oracle_dequant_q5k.argtypes = [vp, i64, vp]
+    L.oracle_dequant_q6k.argtypes = [vp, i64, vp]
+    L.oracle_route.argtypes = [vp, i32, i32, i32, i32, i32, f64, vp, vp]
+    L.oracle_route.restype = i32
+    L.oracle_batches.argtypes = [vp, vp, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.oracle_batches.restype = i32
+    L.oracle_expert_ffn.argtypes = [i32, vp, i32, i32, vp, vp]
+    L.oracle_moe_layer.argtypes = [i32, vp, i32, i32, i32, i32, vp, vp, i32, i32, i32, f64, vp, i32, i32, vp,
+                                   i32, vp, vp, vp, vp]
+    L.oracle_moe_layer.restype = i32
+    L.oracle_set_threads.argtypes = [i32]
+    L.oracle_threads.restype = i32
+    return L
 
 
 def lib() -> ctypes.CDLL:
@@ -43,27 +66,28 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(_SO):
             build()
-        L = ctypes.CDLL(_SO)
-        i32, i64, f64, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
-        L.oracle_dequant_q8_0.argtypes = [vp, i64, vp]
-        L.oracle_dequant_q4k.argtypes = [vp, i64, vp]
-        L.oracle_dequant_mxfp4.argtypes = [vp, i64, vp]
-        L.oracle_dequant_q3k.argtypes = [vp, i64, vp]
-        L.oracle_dequant_q5k.argtypes = [vp, i64, vp]
-        L.oracle_dequant_q6k.argtypes = [vp, i64, vp]
-        L.oracle_route.argtypes = [vp, i32, i32, i32, i32, i32, f64, vp, vp]
-        L.oracle_route.restype = i32
-        L.oracle_batches.argtypes = [vp, vp, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
-        L.oracle_batches.restype = i32
-        L.oracle_expert_ffn.argtypes = [i32, vp, i32, i32, vp, vp]
-        L.oracle_moe_layer.argtypes = [i32, vp, i32, i32, i32, i32, vp, vp, i32, i32, i32, f64, vp, i32, i32, vp,
-                                       i32, vp, vp, vp, vp]
-        L.oracle_moe_layer.restype = i32
-        L.oracle_set_threads.argtypes = [i32]
-        L.oracle_threads.restype = i32
-        L.oracle_set_defect.argtypes = [i32]
-        _lib = L
+        _lib = _bind(_SO)
     return _lib
+
+
+class use_library:
+    """Context manager for the pin tests: the module's functions call the
+    compiled oracle at `path` (a mutant of the source) instead of the
+    oracle, until the block ends."""
+
+    def __init__(self, path: str):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self.saved = lib()
+        _lib = _bind(self.path)
+        return _lib
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
 
 
 def _p(a) -> int:
@@ -79,10 +103,6 @@ def set_threads(n: int) -> None:
 
 def threads() -> int:
     return int(lib().oracle_threads())
-
-
-def set_defect(d: int) -> None:
-    lib().oracle_set_defect(int(d))
 
 
 def dequant(fmt: int, blocks: np.ndarray, n: int) -> np.ndarray:

@@ -13,31 +13,6 @@
 #include <omp.h>
 #endif
 
-static int g_defect = 0;
-void oracle_set_defect(int d) { g_defect = d; }
-
-/* Planted mistakes (used only by the pin tests, to show each pin catches one). */
-enum {
-    D_Q4K_NO_MIN = 1,          /* drop the -dmin*m term */
-    D_Q4K_HIGH_BITS = 2,       /* j>=4: high scale bits taken from the min byte */
-    D_Q8_UNSIGNED = 3,         /* Q8_0 quants read as unsigned */
-    D_SWIGLU_SWAP = 4,         /* silu(u)*g instead of silu(g)*u */
-    D_TIE_HIGH_ID = 5,         /* equal logits: higher id first */
-    D_SCALE_BEFORE_RENORM = 6, /* sigmoid: scale applied inside the renormalisation */
-    D_UNSTABLE = 7,            /* pairs of a slot in descending p */
-    D_NO_SHARED = 8,           /* combine drops the shared expert */
-    D_GATE_UP_SWAPPED = 9,     /* reads W_up as the gate matrix and W_gate as up */
-    D_NO_RENORM = 10,          /* softmax weights not renormalised over the k */
-    D_Q4K_NIBBLE_SWAP = 11,    /* even sub-blocks read the high nibbles */
-    D_IGNORE_RESIDENCY = 12,   /* combine adds non-resident pairs too */
-    D_MXFP4_INTERLEAVED = 13,  /* MXFP4 elements read as consecutive nibble pairs */
-    D_MXFP4_BIAS_128 = 14,     /* MXFP4 scale exponent bias 128 instead of 127 */
-    D_Q3K_SCALE_UNBIASED = 15, /* Q3_K 6-bit scales used without the -32 */
-    D_Q3K_HMASK_INVERTED = 16, /* Q3_K high bit read with the opposite sense */
-    D_Q5K_HIGH_BIT_ORDER = 17, /* Q5_K high bit of element l taken from byte j*4 + l/8 */
-    D_Q6K_NO_OFFSET = 18       /* Q6_K q used without the -32 */
-};
-
 void oracle_set_threads(int n) {
 #ifdef _OPENMP
     if (n > 0) omp_set_num_threads(n);
@@ -76,7 +51,7 @@ void oracle_dequant_q8_0(const uint8_t* blocks, int64_t n, double* out) {
         const uint8_t* blk = blocks + b * 34;
         double d = half_le(blk);
         for (int i = 0; i < 32; ++i) {
-            int q = g_defect == D_Q8_UNSIGNED ? (int)blk[2 + i] : (int)(int8_t)blk[2 + i];
+            int q = (int)(int8_t)blk[2 + i];
             out[b * 32 + i] = d * (double)q;
         }
     }
@@ -91,7 +66,7 @@ static void q4k_scale_min(const uint8_t* s12, int j, int* sc, int* m) {
         *sc = s12[j] & 63;
         *m = s12[j + 4] & 63;
     } else {
-        int hi_sc = (g_defect == D_Q4K_HIGH_BITS) ? (s12[j] >> 6) : (s12[j - 4] >> 6);
+        int hi_sc = s12[j - 4] >> 6;
         *sc = (s12[j + 4] & 15) | (hi_sc << 4);
         *m = (s12[j + 4] >> 4) | ((s12[j] >> 6) << 4);
     }
@@ -114,12 +89,11 @@ void oracle_dequant_q4k(const uint8_t* blocks, int64_t n, double* out) {
             int sc, m;
             q4k_scale_min(s12, j, &sc, &m);
             int high = (j % 2 == 1);
-            if (g_defect == D_Q4K_NIBBLE_SWAP && j % 2 == 0) high = 1;
             for (int l = 0; l < 32; ++l) {
                 uint8_t byte = qs[(j / 2) * 32 + l];
                 int q = high ? (byte >> 4) : (byte & 15);
                 double w = d * (double)sc * (double)q;
-                if (g_defect != D_Q4K_NO_MIN) w -= dmin * (double)m;
+                w -= dmin * (double)m;
                 out[b * 256 + j * 32 + l] = w;
             }
         }
@@ -144,11 +118,9 @@ void oracle_dequant_mxfp4(const uint8_t* blocks, int64_t n, double* out) {
     for (int64_t b = 0; b < n / 32; ++b) {
         const uint8_t* blk = blocks + b * 17;
         int x = blk[0];
-        double scale = x == 255 ? NAN : ldexp(1.0, x - (g_defect == D_MXFP4_BIAS_128 ? 128 : 127));
+        double scale = x == 255 ? NAN : ldexp(1.0, x - 127);
         for (int i = 0; i < 32; ++i) {
-            int code;
-            if (g_defect == D_MXFP4_INTERLEAVED) code = (blk[1 + i / 2] >> (4 * (i % 2))) & 15;
-            else code = i < 16 ? (blk[1 + i] & 15) : (blk[1 + i - 16] >> 4);
+            int code = i < 16 ? (blk[1 + i] & 15) : (blk[1 + i - 16] >> 4);
             out[b * 32 + i] = scale * e2m1_value(code);
         }
     }
@@ -181,9 +153,8 @@ void oracle_dequant_q3k(const uint8_t* blocks, int64_t n, double* out) {
             int h = i / 128, g = (i % 128) / 32, l = i % 32;
             int low = (qs[32 * h + l] >> (2 * g)) & 3;
             int high = (hm[l] >> (4 * h + g)) & 1;
-            if (g_defect == D_Q3K_HMASK_INVERTED) high = 1 - high;
             int q = low + 4 * high - 4;
-            int sc = q3k_scale(s12, i / 16) - (g_defect == D_Q3K_SCALE_UNBIASED ? 0 : 32);
+            int sc = q3k_scale(s12, i / 16) - 32;
             out[b * 256 + i] = d * (double)sc * (double)q;
         }
     }
@@ -208,7 +179,7 @@ void oracle_dequant_q5k(const uint8_t* blocks, int64_t n, double* out) {
             for (int l = 0; l < 32; ++l) {
                 uint8_t byte = qs[(j / 2) * 32 + l];
                 int low = (j % 2) ? (byte >> 4) : (byte & 15);
-                int high = g_defect == D_Q5K_HIGH_BIT_ORDER ? (qh[j * 4 + l / 8] >> (l % 8)) & 1 : (qh[l] >> j) & 1;
+                int high = (qh[l] >> j) & 1;
                 int q = low + 16 * high;
                 out[b * 256 + j * 32 + l] = d * (double)sc * (double)q - dmin * (double)m;
             }
@@ -236,7 +207,7 @@ void oracle_dequant_q6k(const uint8_t* blocks, int64_t n, double* out) {
             uint8_t byte = ql[64 * h + l + 32 * (g % 2)];
             int low = g < 2 ? (byte & 15) : (byte >> 4);
             int high = (qh[32 * h + l] >> (2 * g)) & 3;
-            int q = low + 16 * high - (g_defect == D_Q6K_NO_OFFSET ? 0 : 32);
+            int q = low + 16 * high - 32;
             out[b * 256 + i] = d * (double)sc[i / 16] * (double)q;
         }
     }
@@ -273,7 +244,7 @@ static int down_fmt(int fmt) { return fmt == ORACLE_Q3K_Q4K ? ORACLE_Q4K : fmt; 
  * lower id first.  Parity pinned against a library stable argsort. */
 static int ranks_before(float la, int a, float lb, int b) {
     if (la != lb) return la > lb;
-    return g_defect == D_TIE_HIGH_ID ? a > b : a < b;
+    return a < b;
 }
 
 int oracle_route(const float* logits, int T, int E, int k, int score, int renormalize, double scale,
@@ -308,10 +279,7 @@ int oracle_route(const float* logits, int T, int E, int k, int score, int renorm
         for (int j = 0; j < k; ++j) sel += p[ids[(int64_t)t * k + j]];
         for (int j = 0; j < k; ++j) {
             double v = p[ids[(int64_t)t * k + j]];
-            int renorm = renormalize && !(g_defect == D_NO_RENORM && score == ORACLE_SOFTMAX);
-            if (g_defect == D_SCALE_BEFORE_RENORM && renorm) v = (scale * v) / (scale * sel);
-            else v = renorm ? scale * (v / sel) : scale * v;
-            w[(int64_t)t * k + j] = v;
+            w[(int64_t)t * k + j] = renormalize ? scale * (v / sel) : scale * v;
         }
     }
     free(taken);
@@ -333,8 +301,7 @@ int oracle_batches(const int32_t* ids, const double* w, int T, int k, int E, con
     for (int s = 0; s < S; ++s) {
         slot_offsets[s] = pos;
         int32_t first = pos;
-        for (int64_t i = 0; i < P; ++i) {
-            int64_t p = (g_defect == D_UNSTABLE) ? P - 1 - i : i;
+        for (int64_t p = 0; p < P; ++p) {
             int id = ids[p];
             int slot = (id >= 0 && id < E) ? slot_of_expert[id] : -1;
             if (slot == s) perm_pair[pos++] = (int32_t)p;
@@ -370,11 +337,6 @@ void oracle_expert_ffn(int fmt, const uint8_t* blob, int H, int I, const double*
     const uint8_t* wg = blob;
     const uint8_t* wu = blob + (int64_t)I * rb_h;
     const uint8_t* wd = blob + 2 * (int64_t)I * rb_h;
-    if (g_defect == D_GATE_UP_SWAPPED) {
-        const uint8_t* t = wg;
-        wg = wu;
-        wu = t;
-    }
     double* h = (double*)malloc((size_t)I * sizeof(double));
 #pragma omp parallel
     {
@@ -386,7 +348,7 @@ void oracle_expert_ffn(int fmt, const uint8_t* blob, int H, int I, const double*
             for (int c = 0; c < H; ++c) g += row[c] * x[c];
             dequant_row(fgu, wu + (int64_t)i * rb_h, H, row);
             for (int c = 0; c < H; ++c) u += row[c] * x[c];
-            h[i] = (g_defect == D_SWIGLU_SWAP) ? silu(u) * g : silu(g) * u;
+            h[i] = silu(g) * u;
         }
 #pragma omp for schedule(static)
         for (int r = 0; r < H; ++r) {
@@ -417,7 +379,7 @@ int oracle_moe_layer(int fmt, const uint8_t* const* expert_blob, int E, int H, i
             int64_t p = (int64_t)t * k + j;
             int id = ids[p];
             int resident = slot_of_expert[id] >= 0 && slot_of_expert[id] < S;
-            if (!resident && g_defect != D_IGNORE_RESIDENCY) {
+            if (!resident) {
                 if (y_pairs) memset(y_pairs + p * H, 0, (size_t)H * sizeof(double));
                 continue;
             }
@@ -429,7 +391,7 @@ int oracle_moe_layer(int fmt, const uint8_t* const* expert_blob, int E, int H, i
             if (y_pairs) memcpy(y_pairs + p * H, yp, (size_t)H * sizeof(double));
             for (int c = 0; c < H; ++c) yt[c] += w[p] * yp[c];
         }
-        if (shared_blob && g_defect != D_NO_SHARED) {
+        if (shared_blob) {
             oracle_expert_ffn(shared_fmt, shared_blob, H, I_shared, xt, yp);
             for (int c = 0; c < H; ++c) yt[c] += yp[c];
         }

@@ -90,9 +90,6 @@ int oracle_moe_layer(int fmt, const uint8_t* const* expert_blob, int E, int H, i
 void oracle_set_threads(int n);
 int oracle_threads(void);
 
-/* Planted-mistake switch for the pin tests (0 = the oracle as written). */
-void oracle_set_defect(int d);
-
 #ifdef __cplusplus
 }
 #endif

@@ -1,8 +1,11 @@
 """Pins of the CPU oracle to things other than itself.
 
-Each pin is checked twice: the oracle as written passes it, and a planted
-mistake in the oracle (``oracle.set_defect``) makes it fail, so a pin that
-could not notice its defect is itself caught.
+Each pin is checked twice: the oracle as written passes it, and a mutant of
+the oracle with one planted mistake fails it, so a pin that could not notice
+its mistake is itself caught.  The mutants are made here, not in the
+oracle: each is a copy of oracle/oracle.c with one statement replaced (the
+statement must occur exactly once), compiled to a library of its own and
+called through the same wrapper.
 """
 import json
 import os
@@ -21,11 +24,8 @@ GOLD = os.path.join(ROOT, "tests", "golden")
 
 
 @pytest.fixture(autouse=True)
-def _clean_defect():
+def _threads():
     O.set_threads(4)
-    O.set_defect(0)
-    yield
-    O.set_defect(0)
 
 
 # ----------------------------------------------------------------- pins
@@ -314,51 +314,105 @@ def test_pin_holds(name):
     assert PINS[name]()
 
 
-# Each planted oracle mistake and a pin that must catch it.
+# Planted mistakes: name -> (the statement of oracle/oracle.c, its mutant).
+MUTANTS = {
+    "q4k_no_min": ("w -= dmin * (double)m;", "(void)m;"),  # drop the -dmin*m term
+    "q4k_high_bits": ("int hi_sc = s12[j - 4] >> 6;", "int hi_sc = s12[j] >> 6;"),  # wrong byte for the high scale bits
+    "q8_unsigned": ("int q = (int)(int8_t)blk[2 + i];", "int q = (int)blk[2 + i];"),  # Q8_0 quants read unsigned
+    "swiglu_swap": ("h[i] = silu(g) * u;", "h[i] = silu(u) * g;"),  # silu on the wrong operand
+    "tie_high_id": ("return a < b;", "return a > b;"),  # equal logits: higher id first
+    "scale_inside_renorm": ("renormalize ? scale * (v / sel) : scale * v;",
+                            "renormalize ? (scale * v) / (scale * sel) : scale * v;"),
+    "unstable_grouping": ("""        for (int64_t p = 0; p < P; ++p) {
+            int id = ids[p];
+            int slot = (id >= 0 && id < E) ? slot_of_expert[id] : -1;
+            if (slot == s) perm_pair[pos++] = (int32_t)p;""", """        for (int64_t p = P - 1; p >= 0; --p) {
+            int id = ids[p];
+            int slot = (id >= 0 && id < E) ? slot_of_expert[id] : -1;
+            if (slot == s) perm_pair[pos++] = (int32_t)p;"""),  # the pairs of a slot in descending p
+    "no_shared": ("if (shared_blob) {", "if (0) {"),  # the combine drops the shared expert
+    "gate_up_swapped": ("""    const uint8_t* wg = blob;
+    const uint8_t* wu = blob + (int64_t)I * rb_h;""", """    const uint8_t* wu = blob;
+    const uint8_t* wg = blob + (int64_t)I * rb_h;"""),  # W_up read as the gate matrix and W_gate as up
+    "softmax_no_renorm": ("w[(int64_t)t * k + j] = renormalize ?",
+                          "w[(int64_t)t * k + j] = renormalize && score != ORACLE_SOFTMAX ?"),
+    "q4k_nibble_swap": ("int high = (j % 2 == 1);", "int high = 1;"),  # even sub-blocks read the high nibbles
+    "ignore_residency": ("if (!resident) {", "if (0) {"),  # the combine adds non-resident pairs too
+    "mxfp4_interleaved": ("int code = i < 16 ? (blk[1 + i] & 15) : (blk[1 + i - 16] >> 4);",
+                          "int code = (blk[1 + i / 2] >> (4 * (i % 2))) & 15;"),  # consecutive nibble pairs
+    "mxfp4_bias_128": ("ldexp(1.0, x - 127)", "ldexp(1.0, x - 128)"),  # E8M0 bias 128 instead of 127
+    "q3k_scale_unbiased": ("int sc = q3k_scale(s12, i / 16) - 32;", "int sc = q3k_scale(s12, i / 16);"),
+    "q3k_hmask_inverted": ("int high = (hm[l] >> (4 * h + g)) & 1;", "int high = 1 - ((hm[l] >> (4 * h + g)) & 1);"),
+    "q5k_high_bit_order": ("int high = (qh[l] >> j) & 1;", "int high = (qh[j * 4 + l / 8] >> (l % 8)) & 1;"),
+    "q6k_no_offset": ("int q = low + 16 * high - 32;", "int q = low + 16 * high;"),  # Q6_K q without the -32
+}
+
+# Each planted mistake and a pin that must catch it.
 DEFECTS = [
-    (1, "golden_blocks"),                  # drop -dmin*m
-    (1, "ffn_dense_q4k"),
-    (2, "golden_blocks"),                  # wrong byte for the high scale bits
-    (3, "golden_blocks"),                  # Q8_0 read unsigned
-    (3, "ffn_dense_q8_0"),
-    (4, "ffn_dense_q4k"),                  # silu on the wrong operand
-    (4, "layer_brute_softmax_partial"),
-    (5, "routing_golden"),                 # tie order
-    (5, "routing_softmax_vs_library"),
-    (6, "routing_golden"),                 # scale inside the renormalisation
-    (6, "routing_sigmoid_vs_library"),
-    (7, "batches_vs_sort"),                # unstable grouping
-    (8, "shared_is_forced_expert"),        # shared expert dropped
-    (8, "layer_brute_sigmoid_full"),
-    (9, "ffn_dense_q8_0"),                 # gate and up matrices swapped
-    (10, "routing_golden"),                # no renormalisation
-    (10, "layer_brute_softmax_partial"),
-    (11, "golden_blocks"),                 # nibble halves swapped
-    (11, "encoder_round_trip"),
-    (12, "disjoint_halves"),               # residency ignored in the combine
-    (12, "layer_brute_softmax_partial"),
-    (12, "slot_beyond_s_is_host"),
-    (13, "golden_blocks"),                 # MXFP4 elements as consecutive nibble pairs
-    (13, "ffn_dense_mxfp4"),
-    (13, "encoder_round_trip"),
-    (14, "golden_blocks"),                 # MXFP4 scale bias 128
-    (14, "ffn_dense_mxfp4"),
-    (15, "golden_blocks"),                 # Q3_K scales without the -32
-    (15, "ffn_dense_q3k_q4k"),
-    (16, "golden_blocks"),                 # Q3_K high bit inverted
-    (16, "ffn_dense_q3k_q4k"),
-    (16, "encoder_round_trip"),
-    (17, "golden_blocks"),                 # Q5_K high bits from the wrong byte
-    (17, "ffn_dense_q5k"),
-    (18, "golden_blocks"),                 # Q6_K without the -32 offset
-    (18, "ffn_dense_q6k"),
+    ("q4k_no_min", "golden_blocks"),
+    ("q4k_no_min", "ffn_dense_q4k"),
+    ("q4k_high_bits", "golden_blocks"),
+    ("q8_unsigned", "golden_blocks"),
+    ("q8_unsigned", "ffn_dense_q8_0"),
+    ("swiglu_swap", "ffn_dense_q4k"),
+    ("swiglu_swap", "layer_brute_softmax_partial"),
+    ("tie_high_id", "routing_golden"),
+    ("tie_high_id", "routing_softmax_vs_library"),
+    ("scale_inside_renorm", "routing_golden"),
+    ("scale_inside_renorm", "routing_sigmoid_vs_library"),
+    ("unstable_grouping", "batches_vs_sort"),
+    ("no_shared", "shared_is_forced_expert"),
+    ("no_shared", "layer_brute_sigmoid_full"),
+    ("gate_up_swapped", "ffn_dense_q8_0"),
+    ("softmax_no_renorm", "routing_golden"),
+    ("softmax_no_renorm", "layer_brute_softmax_partial"),
+    ("q4k_nibble_swap", "golden_blocks"),
+    ("q4k_nibble_swap", "encoder_round_trip"),
+    ("ignore_residency", "disjoint_halves"),
+    ("ignore_residency", "layer_brute_softmax_partial"),
+    ("ignore_residency", "slot_beyond_s_is_host"),
+    ("mxfp4_interleaved", "golden_blocks"),
+    ("mxfp4_interleaved", "ffn_dense_mxfp4"),
+    ("mxfp4_interleaved", "encoder_round_trip"),
+    ("mxfp4_bias_128", "golden_blocks"),
+    ("mxfp4_bias_128", "ffn_dense_mxfp4"),
+    ("q3k_scale_unbiased", "golden_blocks"),
+    ("q3k_scale_unbiased", "ffn_dense_q3k_q4k"),
+    ("q3k_hmask_inverted", "golden_blocks"),
+    ("q3k_hmask_inverted", "ffn_dense_q3k_q4k"),
+    ("q3k_hmask_inverted", "encoder_round_trip"),
+    ("q5k_high_bit_order", "golden_blocks"),
+    ("q5k_high_bit_order", "ffn_dense_q5k"),
+    ("q6k_no_offset", "golden_blocks"),
+    ("q6k_no_offset", "ffn_dense_q6k"),
 ]
 
 
-@pytest.mark.parametrize("defect,pin", DEFECTS)
-def test_pin_catches_planted_defect(defect, pin):
-    O.set_defect(defect)
-    try:
+@pytest.fixture(scope="session")
+def mutant_dir(tmp_path_factory):
+    return tmp_path_factory.mktemp("oracle_mutants")
+
+
+def mutant_library(name: str, directory) -> str:
+    """The oracle compiled with MUTANTS[name] applied (built once per session)."""
+    out = os.path.join(str(directory), f"liboracle_{name}.so")
+    if not os.path.exists(out):
+        src = open(os.path.join(ROOT, "oracle", "oracle.c")).read()
+        old, new = MUTANTS[name]
+        assert src.count(old) == 1, f"mutant {name}: its statement must occur exactly once in oracle.c"
+        path = os.path.join(str(directory), f"oracle_{name}.c")
+        with open(path, "w") as f:
+            f.write(src.replace(old, new))
+        O.build(path, out)
+    return out
+
+
+def test_every_mutant_is_caught_by_a_pin():
+    assert {m for m, _ in DEFECTS} == set(MUTANTS)
+
+
+@pytest.mark.parametrize("mutant,pin", DEFECTS)
+def test_pin_catches_planted_defect(mutant, pin, mutant_dir):
+    with O.use_library(mutant_library(mutant, mutant_dir)):
+        O.set_threads(4)
         assert not PINS[pin]()
-    finally:
-        O.set_defect(0)
