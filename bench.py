@@ -482,7 +482,48 @@ def bench_prefill(args, pool, stride, fmt=None, ceiling=True) -> dict:
     }
     if ceiling:
         out.update(library_gemm_ceiling(M, wl.H, wl.I))
+    if fmt is None:
+        out["int8_path"] = bench_prefill_i8(args, pool, stride, wl, x, lg, soe, spec, gu_flop, dn_flop)
     return out
+
+
+def bench_prefill_i8(args, pool, stride, wl, x, lg, soe, spec, gu_flop: float, dn_flop: float) -> dict:
+    """The same layer through MOE_PATH_PREFILL_I8 (int8 activations in two
+    planes on the i8 MFMA, per-sub-block fp32 rescaling): its GEMMs' times
+    (stage timers) against the int8 peak, and a step's time."""
+    import torch
+
+    import quantized_routed_expert_moe_amd as Q
+    from quantized_routed_expert_moe_amd.layer import MoELayer
+
+    layer = MoELayer(spec, wl.T, wl.E, pool, stride, soe, path=Q.MOE_PATH_PREFILL_I8, y_dtype=torch.bfloat16,
+                     pair_dtype=torch.bfloat16)
+    for _ in range(3):
+        layer.forward(x, lg)
+    torch.cuda.synchronize()
+    steps = args.prefill_steps
+    for st in (STAGE_PF_GATEUP, STAGE_PF_DOWN):
+        Q.moe_timer_begin(st, steps)
+    for _ in range(steps):
+        layer.forward(x, lg)
+    torch.cuda.synchronize()
+    ms_gu, n_gu = Q.moe_timer_end(STAGE_PF_GATEUP)
+    ms_dn, n_dn = Q.moe_timer_end(STAGE_PF_DOWN)
+    gu_us, dn_us = 1e3 * ms_gu / max(n_gu, 1), 1e3 * ms_dn / max(n_dn, 1)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(x, lg)
+    g.replay()
+    ms_step = timed_replays(lambda i: g.replay(), steps)
+    # two int8 planes: the contraction's MACs run twice on the i8 MFMA
+    gu_tops = 2 * gu_flop / (gu_us * 1e-6) / 1e12
+    dn_tops = 2 * dn_flop / (dn_us * 1e-6) / 1e12
+    return {"ms_per_step": round(ms_step, 4), "tokens_per_s": round(wl.T / (ms_step * 1e-3), 1),
+            "gemm_gateup_us": round(gu_us, 2), "gemm_down_us": round(dn_us, 2),
+            "gateup_TFLOPs_of_the_contraction": round(gu_flop / (gu_us * 1e-6) / 1e12, 1),
+            "gateup_int8_TOPs": round(gu_tops, 1), "gateup_frac_of_int8_peak": round(gu_tops / MFMA_INT8_PEAK_TOPS, 4),
+            "down_int8_TOPs": round(dn_tops, 1), "down_frac_of_int8_peak": round(dn_tops / MFMA_INT8_PEAK_TOPS, 4),
+            "note": "int8 ops = 2 planes x the contraction's 2 M N K; the bf16 path (the object above) is AUTO's choice"}
 
 
 def library_gemm_ceiling(M: int, H: int, I: int, reps: int = 20) -> dict:

@@ -60,7 +60,7 @@ typedef enum moe_status {
 
 typedef enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
 typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
-typedef enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 } moe_path;
+typedef enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2, MOE_PATH_PREFILL_I8 = 3 } moe_path;
 typedef enum moe_format {
     MOE_FMT_Q8_0 = 0,
     MOE_FMT_Q4K = 1,
@@ -304,6 +304,19 @@ moe_status moe_validate_slot_map(const int32_t* slot_of_expert, int E, int S);
  *               accumulate, h rounded to bf16; y_pairs MOE_F32 or MOE_BF16.
  *               (MXFP4 weights beyond bf16's range, |w| > 3.39e38, become
  *               infinite there.)
+ *               MOE_PATH_PREFILL_I8 (Q4_K only): the pages' prompt design,
+ *               int8 activations on the i8 MFMA (bloomery README 0.3.1, "Why
+ *               it is fast"): bf16 x; each activation row split into two
+ *               int8 planes, x = s (q1 + q2 / 254) with s = max|x| / 127
+ *               (one plane alone exceeds the 1e-2 per-row bound on a
+ *               Qwen3-shaped layer); one v_mfma_i32_32x32x32_i8 per plane
+ *               and 32-weight sub-block against the 4-bit quants, each
+ *               sub-block's integer sums scaled into fp32 by d sc, the min
+ *               term from the planes' sub-block sums; h rounded to bf16 and
+ *               quantized the same way for the down GEMM; y_pairs MOE_F32
+ *               or MOE_BF16.  Slower than MOE_PATH_PREFILL on gfx950 (the
+ *               per-sub-block rescaling is VALU work the bf16 path does
+ *               not have); AUTO never takes it.
  *               MOE_PATH_AUTO: PREFILL for every format but Q8_0 with bf16
  *               x when T > 32, else DECODE (always DECODE for Q8_0).
  * ws, ws_bytes  device workspace, at least moe_ffn_workspace_size(format, T,

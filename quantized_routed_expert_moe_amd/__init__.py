@@ -21,7 +21,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "qmoe.h")
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_F32, MOE_BF16 = 0, 1
-MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL = 0, 1, 2
+MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL, MOE_PATH_PREFILL_I8 = 0, 1, 2, 3
 MOE_FMT_Q8_0, MOE_FMT_Q4K, MOE_FMT_MXFP4, MOE_FMT_Q3K_Q4K, MOE_FMT_Q5K, MOE_FMT_Q6K = 0, 1, 2, 3, 4, 5
 # (MOE_FMT_Q3K_Q4K: Q3_K gate and up, Q4_K down)
 STAGES = ("route", "batches", "prefill_tiles", "ffn_gateup", "ffn_down", "combine", "prefill_gateup", "prefill_down",

@@ -19,7 +19,7 @@ SO = os.path.join(HERE, "libqmoe.so")
 HOST_SO = os.path.join(HERE, "libqmoe_host.so")  # host leg + residency policy (CPU only, g++)
 
 SOURCES = ["abi.cpp", "route.hip", "batches.hip", "route_batches.hip", "ffn_decode.hip", "ffn_prefill.hip",
-           "combine.hip", "layer_decode.hip", "hbm_probe.hip", "prefill_probe.hip"]
+           "combine.hip", "layer_decode.hip", "hbm_probe.hip", "prefill_probe.hip", "ffn_prefill_i8.hip"]
 # ffn_prefill.hip is compiled once more per block type with only that type's
 # GEMM kernels (QMOE_PREFILL_FMT), so the types compile in parallel.
 PREFILL_TYPES = [1, 2, 3, 4, 5]

@@ -596,7 +596,9 @@ moe_status ffn_check(int format, const void* slot_pool, size_t slot_stride, int 
                     packed_bytes(format, H, I));
     if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARGUMENT, "bad x_dtype %d", x_dtype);
     if (y_dtype != MOE_F32 && y_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARGUMENT, "bad y_dtype %d", y_dtype);
-    if (path < MOE_PATH_AUTO || path > MOE_PATH_PREFILL) return fail(MOE_ERR_INVALID_ARGUMENT, "bad path %d", path);
+    if (path < MOE_PATH_AUTO || path > MOE_PATH_PREFILL_I8) return fail(MOE_ERR_INVALID_ARGUMENT, "bad path %d", path);
+    if (path == MOE_PATH_PREFILL_I8 && format != MOE_FMT_Q4K)
+        return fail(MOE_ERR_UNSUPPORTED, "MOE_PATH_PREFILL_I8 is implemented for Q4_K experts");
     if (!aligned16(x) || !aligned16(y_pairs)) return fail(MOE_ERR_INVALID_ARGUMENT, "x and y_pairs must be 16-byte aligned");
     const int p = resolve_path(format, T, x_dtype, path);
     *resolved = p;
@@ -614,7 +616,8 @@ moe_status ffn_check(int format, const void* slot_pool, size_t slot_stride, int 
         if ((long long)T * H * 2 > 0xFFFFFFFFLL || P * I * 2 > 0xFFFFFFFFLL || (P + 255) / 256 + 1024 > 0xFFFF)
             return fail(MOE_ERR_UNSUPPORTED, "prefill path limits: T*H*2 and T*k*I*2 below 4 GiB, T*k below %d",
                         (0xFFFF - 1024) * 256);
-        *need = qmoe::prefill_workspace_bytes(T, k, H, I);
+        *need = p == MOE_PATH_PREFILL_I8 ? qmoe::prefill_i8_workspace_bytes(T, k, H, I)
+                                         : qmoe::prefill_workspace_bytes(T, k, H, I);
     }
     return MOE_OK;
 }
@@ -636,8 +639,9 @@ moe_status ffn_common(int format, const void* slot_pool, size_t slot_stride, int
 
     qmoe::FfnArgs a{format, static_cast<const uint8_t*>(slot_pool), slot_stride, S, H, I, x, x_dtype, T, k,
                     slot_offsets, active_slots, num_active, perm_pair, y_pairs, y_dtype, ws};
-    hipError_t e = p == MOE_PATH_DECODE ? qmoe::launch_ffn_decode(a, (hipStream_t)stream)
-                                        : qmoe::launch_ffn_prefill(a, (hipStream_t)stream);
+    hipError_t e = p == MOE_PATH_DECODE       ? qmoe::launch_ffn_decode(a, (hipStream_t)stream)
+                   : p == MOE_PATH_PREFILL_I8 ? qmoe::launch_ffn_prefill_i8(a, (hipStream_t)stream)
+                                              : qmoe::launch_ffn_prefill(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "expert FFN launch");
     return MOE_OK;
 }
@@ -862,6 +866,7 @@ size_t moe_ffn_workspace_size(int format, int T, int k, int H, int I, int path) 
     if (!has_prefill(format) || path == MOE_PATH_DECODE) return dec;
     const size_t pre = qmoe::prefill_workspace_bytes(T, k, H, I);
     if (path == MOE_PATH_PREFILL) return pre;
+    if (path == MOE_PATH_PREFILL_I8) return format == MOE_FMT_Q4K ? qmoe::prefill_i8_workspace_bytes(T, k, H, I) : 0;
     return std::max(dec, pre);
 }
 

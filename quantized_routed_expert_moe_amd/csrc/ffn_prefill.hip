@@ -93,6 +93,12 @@ size_t prefill_workspace_bytes(int T, int k, int H, int I) {
     return align256((size_t)P * I * 2) + align256((size_t)max_tiles(P, kMaxExpertsInternal) * 16) + 256;
 }
 
+size_t prefill_i8_workspace_bytes(int T, int k, int H, int I) {
+    const size_t P = (size_t)T * k, K = (size_t)std::max(H, I);
+    return prefill_workspace_bytes(T, k, H, I) + 2 * align256(P * K) + align256(K / 32 * (P + 256) * 4) +
+           align256(P * 4);
+}
+
 // ---------------------------------------------------------------- tiles
 
 // One workgroup of 1024 threads, one active slot per thread.  Tiles are
@@ -1000,6 +1006,47 @@ hipError_t launch_ffn_prefill(const FfnArgs& a, hipStream_t s) {
     launch_timed(down, dim3(8 * nt_dn * mgroups), dim3(kThreads), 0, s, ev_d.start, ev_d.stop, a.pool, a.stride, a.S,
                  a.H, a.I, (const uint16_t*)h, a.T, a.k, a.perm_pair, tiles, ntiles, a.y_pairs, a.y_dtype);
     return hipGetLastError();
+}
+
+// The int8-activation path (Q4_K): the tile list, then per GEMM the
+// activations' quantization and the i8 GEMM (ffn_prefill_i8.hip).
+hipError_t launch_ffn_prefill_i8(const FfnArgs& a, hipStream_t s) {
+    const int P = a.T * a.k;
+    const int mt = max_tiles(P, a.S);
+    if (a.S > 1024 || mt > 0xFFFF) return hipErrorInvalidValue;
+    uint8_t* ws = static_cast<uint8_t*>(a.ws);
+    uint16_t* h = reinterpret_cast<uint16_t*>(ws);
+    size_t off = align256((size_t)P * a.I * 2);
+    int4* tiles = reinterpret_cast<int4*>(ws + off);
+    off += align256((size_t)max_tiles(P, kMaxExpertsInternal) * 16);
+    int32_t* ntiles = reinterpret_cast<int32_t*>(ws + off);
+    off += 256;
+    const size_t K = (size_t)std::max(a.H, a.I);
+    int8_t* a1 = reinterpret_cast<int8_t*>(ws + off);
+    off += align256((size_t)P * K);
+    int8_t* a2 = reinterpret_cast<int8_t*>(ws + off);
+    off += align256((size_t)P * K);
+    float* xs = reinterpret_cast<float*>(ws + off);
+    const int ld_xs = P + 256;
+    off += align256(K / 32 * (size_t)ld_xs * 4);
+    float* sc = reinterpret_cast<float*>(ws + off);
+
+    const StageEvents ev_t = timer_events(kStagePrefillTiles);
+    launch_timed(prefill_tiles_kernel, dim3(1), dim3(1024), 0, s, ev_t.start, ev_t.stop, a.slot_offsets,
+                 a.active_slots, a.num_active, a.S, P, tiles, ntiles);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int32_t* n_rows = a.slot_offsets + a.S;  // resident pair positions
+    e = launch_i8_quant(static_cast<const uint16_t*>(a.x), a.H, P, n_rows, a.perm_pair, a.k, a1, a2, xs, ld_xs, sc, s);
+    if (e != hipSuccess) return e;
+    const StageEvents ev_g = timer_events(kStagePrefillGateUp);
+    e = launch_i8_gemm(true, a, a1, a2, xs, ld_xs, sc, tiles, ntiles, mt, h, 0, s, ev_g.start, ev_g.stop);
+    if (e != hipSuccess) return e;
+    e = launch_i8_quant(h, a.I, P, n_rows, nullptr, 1, a1, a2, xs, ld_xs, sc, s);
+    if (e != hipSuccess) return e;
+    const StageEvents ev_d = timer_events(kStagePrefillDown);
+    return launch_i8_gemm(false, a, a1, a2, xs, ld_xs, sc, tiles, ntiles, mt, a.y_pairs, a.y_dtype, s, ev_d.start,
+                          ev_d.stop);
 }
 
 #endif  // QMOE_PREFILL_FMT

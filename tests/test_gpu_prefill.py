@@ -35,13 +35,14 @@ def _check_ints(wl, got, ids, w, soe, S):
         assert np.array_equal(got[key], ob[key]), key
 
 
-def _prefill_case(wl, soe=None, S=None, pair_dtype=torch.bfloat16, y_dtype=torch.bfloat16, sample=None, blobs=None):
+def _prefill_case(wl, soe=None, S=None, pair_dtype=torch.bfloat16, y_dtype=torch.bfloat16, sample=None, blobs=None,
+                  path=Q.MOE_PATH_PREFILL):
     soe_, S_ = W.slot_map(wl)
     soe = soe_ if soe is None else soe
     S = S_ if S is None else S
     x, logits = W.x_of(wl), W.logits_of(wl)
     blobs = W.expert_blobs(wl) if blobs is None else blobs
-    layer = device_layer(wl, blobs, soe, S, None, wl.T, Q.MOE_PATH_PREFILL, pair_dtype=pair_dtype, y_dtype=y_dtype)
+    layer = device_layer(wl, blobs, soe, S, None, wl.T, path, pair_dtype=pair_dtype, y_dtype=y_dtype)
     got = run_device(layer, x, logits)
     ids, w = O.route(logits, wl.k, wl.score, wl.renormalize, wl.scale)
     assert np.array_equal(got["ids"], ids)
