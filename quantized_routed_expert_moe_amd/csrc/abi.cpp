@@ -13,6 +13,7 @@
 
 #include "qmoe.h"
 #include "qmoe_internal.h"
+#include "prefill_i8.h"
 
 namespace {
 

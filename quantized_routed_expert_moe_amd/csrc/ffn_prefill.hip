@@ -59,6 +59,7 @@
 // L2 of an XCD serves the A rows shared by its N tiles.
 #include "device_common.h"
 #include "qmoe_internal.h"
+#include "prefill_i8.h"
 
 namespace qmoe {
 

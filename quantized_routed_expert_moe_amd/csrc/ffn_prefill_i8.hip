@@ -29,6 +29,7 @@
 // The down GEMM's activations are h, quantized the same way.
 #include "device_common.h"
 #include "qmoe_internal.h"
+#include "prefill_i8.h"
 
 namespace qmoe {
 
