@@ -110,7 +110,8 @@ def read_traffic(key: str) -> float | None:
 
 def host_threads() -> dict:
     """Threads the CPU legs use: the run's CPU share (OMP_NUM_THREADS when
-    set, as on the GPU machines), else the affinity mask's size."""
+    set, as on a machine that caps a job's threads), else the affinity
+    mask's size."""
     aff = len(os.sched_getaffinity(0))
     env = os.environ.get("OMP_NUM_THREADS", "")
     n = min(aff, int(env)) if env.isdigit() and int(env) > 0 else aff

@@ -53,7 +53,7 @@ extern "C" {
 typedef enum moe_status {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARGUMENT = 1,   /* null pointer, size out of range, bad enum */
-    MOE_ERR_UNSUPPORTED = 2,        /* valid request this build does not implement */
+    MOE_ERR_UNSUPPORTED = 2,        /* valid request the library does not implement */
     MOE_ERR_WORKSPACE_TOO_SMALL = 3,
     MOE_ERR_HIP = 4                 /* a HIP runtime call failed */
 } moe_status;
