@@ -810,7 +810,8 @@ def leg_mfma(args) -> dict:
     registers: the library's inner-loop probe (variant 0: Q4_K nibbles
     dequantized to bf16 + v_mfma_f32_32x32x16_bf16, the prefill GEMM's
     design; variant 1: int8 activations + v_mfma_i32_32x32x32_i8 with the
-    per-sub-block fp32 rescaling and min term Q4_K needs), 5 timed launches
+    per-sub-block fp32 rescaling and min term Q4_K needs; variant 2: variant
+    1 with the two activation planes the int8 prefill path runs), 5 timed launches
     of 4096 sub-blocks per wave after 2 untimed ones.  The rate is the flops
     of the contraction the loop stands for per second: the ceiling a GEMM
     built on that design reaches with its memory traffic fully hidden."""
@@ -819,7 +820,7 @@ def leg_mfma(args) -> dict:
     import quantized_routed_expert_moe_amd as Q
     out = torch.zeros(Q.PREFILL_PROBE_OUT_FLOATS, dtype=torch.float32, device="cuda")
     res = {}
-    for variant, name in ((0, "bf16_dequant_mfma"), (1, "int8_mfma_rescale")):
+    for variant, name in ((0, "bf16_dequant_mfma"), (1, "int8_mfma_rescale"), (2, "int8_two_plane_rescale")):
         for _ in range(2):
             Q.moe_prefill_inner_probe(variant, 4096, out)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -831,6 +832,8 @@ def leg_mfma(args) -> dict:
         res[name] = {"TFLOPs": round(tf, 1), "frac_of_bf16_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                      "frac_of_int8_peak": round(tf / MFMA_INT8_PEAK_TOPS, 4)}
     res["int8_over_bf16"] = round(res["int8_mfma_rescale"]["TFLOPs"] / res["bf16_dequant_mfma"]["TFLOPs"], 3)
+    res["int8_two_plane_over_bf16"] = round(res["int8_two_plane_rescale"]["TFLOPs"]
+                                            / res["bf16_dequant_mfma"]["TFLOPs"], 3)
     del out
     return res
 

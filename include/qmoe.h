@@ -485,7 +485,10 @@ moe_status moe_hbm_read_probe(const void* buf, size_t bytes, int waves, int dept
  * design, a 256 x 64 tile per wave); variant 1: int8 activations and the
  * nibbles as int8 on the i8 MFMA, each sub-block's integer sums converted
  * and scaled into fp32 accumulators with the min term from the activations'
- * sums (a 128 x 64 tile per wave, two waves per SIMD).  Every wave runs
+ * sums (a 128 x 64 tile per wave, two waves per SIMD); variant 2: the int8
+ * path as built (MOE_PATH_PREFILL_I8): variant 1's tile with two int8
+ * activation planes, two MFMAs per sub-block and weight block, the planes'
+ * sums in registers.  Every wave runs
  * `sub_blocks` (1..1048576) sub-blocks of its tile: 1024 x sub_blocks x
  * 1,048,576 flops per launch for either variant (each sub-block counted as
  * the 2 x rows x 64 x 32 flops of the contraction it stands for).  out:

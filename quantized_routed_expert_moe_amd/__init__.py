@@ -534,7 +534,8 @@ PREFILL_PROBE_OUT_FLOATS = 131072  # MOE_PREFILL_PROBE_OUT_FLOATS
 def moe_prefill_inner_probe(variant: int, sub_blocks: int, out, stream=None) -> float:
     """One launch of the prefill inner-loop probe (variant 0: bf16
     dequantization + bf16 MFMA; 1: int8 MFMA + fp32 rescaling per
-    sub-block); returns the flops the launch stands for."""
+    sub-block; 2: variant 1 with two int8 activation planes); returns the
+    flops the launch stands for."""
     import torch
     ptr = _dev(out, (torch.float32,), name="out")
     _check(lib().moe_prefill_inner_probe(int(variant), int(sub_blocks), ptr, out.numel(), _stream(stream)))

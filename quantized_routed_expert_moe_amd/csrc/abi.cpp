@@ -1072,7 +1072,7 @@ moe_status moe_hbm_read_probe(const void* buf, size_t bytes, int waves, int dept
 
 moe_status moe_prefill_inner_probe(int variant, int sub_blocks, float* out, size_t out_floats, void* stream) {
     if (!out) return fail(MOE_ERR_INVALID_ARGUMENT, "out is NULL");
-    if (variant != 0 && variant != 1) return fail(MOE_ERR_INVALID_ARGUMENT, "variant = %d is not 0 or 1", variant);
+    if (variant < 0 || variant > 2) return fail(MOE_ERR_INVALID_ARGUMENT, "variant = %d is not 0, 1 or 2", variant);
     if (sub_blocks < 1 || sub_blocks > (1 << 20))
         return fail(MOE_ERR_INVALID_ARGUMENT, "sub_blocks = %d is not in 1..1048576", sub_blocks);
     if (out_floats < (size_t)MOE_PREFILL_PROBE_OUT_FLOATS)

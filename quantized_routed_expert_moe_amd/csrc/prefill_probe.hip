@@ -20,8 +20,13 @@
 //     sums taken by one more MFMA against a ones operand) is added per
 //     output.  The fp32 accumulators live in arithmetic registers, so the
 //     wave tile is 128 rows x 64 columns (two waves per SIMD).
+//   variant 2 (the int8 path as built, MOE_PATH_PREFILL_I8): variant 1's tile
+//     with the activations in two int8 planes, two MFMAs per row block and
+//     weight block per sub-block, each output taking d sc (T1 + T2 / 254)
+//     plus the min term from the planes' sums over the sub-block (held in
+//     registers here; the GEMM loads them).
 // The per-row activation scale multiplies each output once after the whole
-// K loop and is left out of both.
+// K loop and is left out of all three.
 #include "device_common.h"
 #include "qmoe_internal.h"
 
@@ -193,13 +198,75 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     out[gid] = sum;
 }
 
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_probe_int8x2(
+    int sub_blocks, float* __restrict__ out) {
+    const uint32_t gid = blockIdx.x * 256 + threadIdx.x;
+    pb_i32x4 fa[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) fa[i][pl][d] = (int)(mix(gid * 32 + i * 8 + pl * 4 + d) & 0x7F7F7F7Fu);
+    const uint32_t hdr = mix(gid ^ 0x51ED27u);
+    const float dd = 0.25f + (float)(hdr & 7), dmin = 0.125f * (float)((hdr >> 3) & 7);
+    float xv[16];  // the planes' sums of the lane's 16 output rows
+#pragma unroll
+    for (int r = 0; r < 16; ++r) xv[r] = (float)(mix(gid * 16 + r + 3) & 255) - 128.0f;
+    uint32_t wq[2][2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) wq[m][s] = mix(gid * 4 + m * 2 + s + 7);
+    float acc[4][2][16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][m][r] = 0.f;
+    pb_i32x16 zero;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) zero[r] = 0;
+    for (int j = 0; j < sub_blocks; ++j) {
+        const uint32_t salt = (uint32_t)j * 0x9E3779B9u;
+        const float dsc[2] = {dd * (float)((hdr >> (j & 15)) & 63u), dd * (float)((hdr >> ((j + 6) & 15)) & 63u)};
+        const float ndm[2] = {-(dmin * (float)((salt >> 26) & 63u)), -(dmin * (float)((salt >> 20) & 63u))};
+        pb_i32x4 fb[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) fb[m] = probe_unpack(wq[m][0] ^ salt, wq[m][1] ^ salt);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const pb_i32x16 t1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i][0], fb[m], zero, 0, 0, 0);
+                const pb_i32x16 t2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i][1], fb[m], zero, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float t = (float)t1[r] + (float)t2[r] * (1.0f / 254.0f);
+                    acc[i][m][r] = fmaf(dsc[m], t, fmaf(ndm[m], xv[r], acc[i][m][r]));
+                }
+            }
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sum += acc[i][m][r];
+    out[gid] = sum;
+}
+
 }  // namespace
 
 hipError_t launch_prefill_probe(int variant, int sub_blocks, float* out, hipStream_t s) {
     if (variant == 0)
         hipLaunchKernelGGL(prefill_probe_bf16, dim3(kPrefillProbeWorkgroups / 2), dim3(256), 0, s, sub_blocks, out);
-    else
+    else if (variant == 1)
         hipLaunchKernelGGL(prefill_probe_int8, dim3(kPrefillProbeWorkgroups), dim3(256), 0, s, sub_blocks, out);
+    else
+        hipLaunchKernelGGL(prefill_probe_int8x2, dim3(kPrefillProbeWorkgroups), dim3(256), 0, s, sub_blocks, out);
     return hipGetLastError();
 }
 

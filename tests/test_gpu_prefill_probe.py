@@ -1,6 +1,6 @@
-"""The prefill inner-loop probe (moe_prefill_inner_probe): both variants run
-to completion and write one finite sum per thread (the bf16 variant's 256
-workgroups the first half of out, the int8 variant's 512 all of it), the
+"""The prefill inner-loop probe (moe_prefill_inner_probe): every variant runs
+to completion and writes one finite sum per thread (the bf16 variant's 256
+workgroups the first half of out, each int8 variant's 512 all of it), the
 same sums on a second launch, and bad arguments are refused before any
 launch."""
 import pytest
@@ -11,7 +11,7 @@ import quantized_routed_expert_moe_amd as Q
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("variant,threads", [(0, 65536), (1, 131072)])
+@pytest.mark.parametrize("variant,threads", [(0, 65536), (1, 131072), (2, 131072)])
 def test_prefill_probe_writes_its_sums(variant, threads):
     out = torch.full((Q.PREFILL_PROBE_OUT_FLOATS + 64,), float("nan"), dtype=torch.float32, device="cuda")
     flops = Q.moe_prefill_inner_probe(variant, 64, out)
@@ -28,7 +28,9 @@ def test_prefill_probe_writes_its_sums(variant, threads):
 def test_prefill_probe_refusals():
     out = torch.zeros(Q.PREFILL_PROBE_OUT_FLOATS, dtype=torch.float32, device="cuda")
     with pytest.raises(Q.QmoeError, match="variant"):
-        Q.moe_prefill_inner_probe(2, 8, out)
+        Q.moe_prefill_inner_probe(3, 8, out)
+    with pytest.raises(Q.QmoeError, match="variant"):
+        Q.moe_prefill_inner_probe(-1, 8, out)
     with pytest.raises(Q.QmoeError, match="sub_blocks"):
         Q.moe_prefill_inner_probe(0, 0, out)
     with pytest.raises(Q.QmoeError, match="fewer than"):
