@@ -39,3 +39,15 @@ def test_noalloc_matches_workspace_entry_point_twice():
         got, want, n_res = _both(wl, path, pd)
         assert n_res == wl.T * wl.k
         assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), wl.name
+
+
+def test_noalloc_int8_path_matches_workspace_entry_point_twice():
+    """The same on the int8-activation prefill path, whose workspace adds the
+    activation planes and their sums to the bf16 path's."""
+    big = W.Workload("prefill int8 T300 E16 k4 Q4_K", F.Q4K, 512, 256, 16, 4, 300, x_bf16=True, zipf_s=1.0, seed=3)
+    small = W.Workload("prefill int8 T129 E8 k2 Q4_K", F.Q4K, 512, 256, 8, 2, 129, x_bf16=True, zipf_s=1.0, seed=3)
+    for wl, pd in ((big, torch.bfloat16), (small, torch.float32)):
+        say(f"noalloc vs workspace: {wl.name}")
+        got, want, n_res = _both(wl, Q.MOE_PATH_PREFILL_I8, pd)
+        assert n_res == wl.T * wl.k
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), wl.name
