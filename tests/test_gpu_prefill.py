@@ -205,3 +205,34 @@ def test_prefill_equals_its_bf16_rounding_model(fmt):
             worst = max(worst, float(np.max((dev - slack) / np.abs(y).max())))
     say(f"  max (|y_pair - model| - rounding-flip allowance) / max |model| = {worst:.3e}")
     assert worst <= 2e-5
+
+
+@pytest.mark.parametrize("path", [Q.MOE_PATH_PREFILL, Q.MOE_PATH_PREFILL_I8], ids=["bf16", "int8"])
+def test_prefill_nothing_resident(path):
+    """Every expert on the host (slot map all -1, four empty slots): no
+    active slot and no tile, every pair on the host list, y zero."""
+    wl = W.Workload("prefill T96 E8 k2, nothing resident", F.Q4K, 256, 256, 8, 2, 96, x_bf16=True, seed=11)
+    say(f"{wl.name}, path {path}")
+    assert _prefill_case(wl, soe=np.full(8, -1, dtype=np.int32), S=4, path=path) == 0.0
+
+
+@pytest.mark.parametrize("path", [Q.MOE_PATH_DECODE, Q.MOE_PATH_PREFILL, Q.MOE_PATH_PREFILL_I8],
+                         ids=["decode", "bf16", "int8"])
+def test_expert_ffn_empty_step(path):
+    """T = 0 through moe_expert_ffn_q4k: the call succeeds and leaves y_pairs
+    as it was."""
+    say(f"expert FFN T=0, path {path}")
+    H, I, S, k = 256, 256, 2, 2
+    dev = dict(device="cuda")
+    stride = (Q.moe_packed_blob_bytes(F.Q4K, H, I) + 255) // 256 * 256
+    pool = torch.zeros(S * stride, dtype=torch.uint8, **dev)
+    x = torch.zeros((0, H), dtype=torch.float32 if path == Q.MOE_PATH_DECODE else torch.bfloat16, **dev)
+    offsets = torch.zeros(S + 1, dtype=torch.int32, **dev)
+    active = torch.zeros(S, dtype=torch.int32, **dev)
+    num = torch.zeros(1, dtype=torch.int32, **dev)
+    perm = torch.zeros(1, dtype=torch.int32, **dev)
+    y_pairs = torch.full((1, H), float("nan"), dtype=torch.float32, **dev)
+    ws = torch.zeros(max(1, Q.moe_ffn_workspace_size(F.Q4K, 0, k, H, I, path)), dtype=torch.uint8, **dev)
+    Q.moe_expert_ffn_q4k(pool, stride, S, H, I, x, k, offsets, active, num, perm, y_pairs, path, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(y_pairs).all()
