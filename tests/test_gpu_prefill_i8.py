@@ -4,7 +4,8 @@ fp32 rescaling) with the CPU oracle, to the prefill bound: per token row t,
 max_i |y_ti - y*_ti| <= 1e-2 * max_i |y*_ti|; ids, batches and host list
 bit-exact.  The cases are the bf16 path's: the 4096-token Qwen3-shaped layer
 on a sample of rows covering every expert, small layers with several and
-ragged M tiles and both y_pairs types, partial residency, tile boundaries."""
+ragged M tiles and both y_pairs types, partial residency, tile boundaries,
+1024 slots."""
 import numpy as np
 import pytest
 import torch
@@ -67,6 +68,16 @@ def test_prefill_i8_tile_boundaries():
     err = float(np.max(np.abs(got["y"] - want["y"]).max(axis=1) / np.abs(want["y"]).max(axis=1)))
     say(f"  max per-row error {err:.3e}")
     assert err <= PREFILL_TOL
+
+
+def test_prefill_i8_at_the_slot_limit():
+    """E = S = 1024 (MOE_MAX_EXPERTS): 640 tokens x k 8 over every expert,
+    most slots a handful of rows in one ragged tile, a few several tiles."""
+    wl = W.Workload("prefill int8 T640 E1024 k8, all resident", F.Q4K, 256, 256, 1024, 8, 640, x_bf16=True,
+                    zipf_s=1.0, seed=9)
+    say(wl.name)
+    F.set_num_threads(THREADS)
+    assert _prefill_case(wl, pair_dtype=torch.float32, y_dtype=torch.float32, path=I8) <= PREFILL_TOL
 
 
 def test_prefill_i8_refuses_other_formats():
