@@ -410,3 +410,45 @@ def test_noalloc_ffn_rejects_beyond_its_scratch_without_touching_the_device():
     assert st == Q.MOE_ERR_UNSUPPORTED and "multiples of 256" in msg
     # the 4096-token prefill layer's workspace fits
     assert Q.moe_ffn_workspace_size(Q.MOE_FMT_Q4K, 4096, 8, 2048, 768, Q.MOE_PATH_PREFILL) <= Q.MOE_NOALLOC_SCRATCH_BYTES
+
+
+def test_ffn_int8_path_refusals():
+    """MOE_PATH_PREFILL_I8 serves Q4_K experts with bf16 activations, with the
+    larger workspace the activation planes need."""
+    mx_stride = Q.moe_expert_blob_bytes(Q.MOE_FMT_MXFP4, 2048, 768) // 16 * 16 + 256
+    st, msg = _ffn("moe_expert_ffn_mxfp4", stride=mx_stride, path=Q.MOE_PATH_PREFILL_I8, x_dtype=Q.MOE_BF16,
+                   y_dtype=Q.MOE_BF16)
+    assert st == Q.MOE_ERR_UNSUPPORTED and "MOE_PATH_PREFILL_I8" in msg, msg
+    st, msg = _ffn("moe_expert_ffn_q4k", path=Q.MOE_PATH_PREFILL_I8, x_dtype=Q.MOE_F32, y_dtype=Q.MOE_BF16)
+    assert st == Q.MOE_ERR_UNSUPPORTED and "MOE_BF16 x" in msg, msg
+    need = Q.moe_ffn_workspace_size(Q.MOE_FMT_Q4K, 2, 8, 2048, 768, Q.MOE_PATH_PREFILL_I8)
+    assert need > Q.moe_ffn_workspace_size(Q.MOE_FMT_Q4K, 2, 8, 2048, 768, Q.MOE_PATH_PREFILL)
+    st, msg = _ffn("moe_expert_ffn_q4k", path=Q.MOE_PATH_PREFILL_I8, x_dtype=Q.MOE_BF16, y_dtype=Q.MOE_BF16,
+                   ws_bytes=need - 1)
+    assert st == Q.MOE_ERR_WORKSPACE_TOO_SMALL, msg
+
+
+@pytest.mark.parametrize("args,needle", [
+    ((0, 8, None, 131072, None), "NULL"),
+    ((3, 8, FAKE, 131072, None), "variant"),
+    ((-1, 8, FAKE, 131072, None), "variant"),
+    ((0, 0, FAKE, 131072, None), "sub_blocks"),
+    ((1, (1 << 20) + 1, FAKE, 131072, None), "sub_blocks"),
+    ((2, 8, FAKE, 131071, None), "fewer than"),
+])
+def test_prefill_probe_refusals(args, needle):
+    st, msg = _call("moe_prefill_inner_probe", *args)
+    assert st == Q.MOE_ERR_INVALID_ARGUMENT and needle in msg, msg
+
+
+@pytest.mark.parametrize("args,needle", [
+    ((None, 1 << 20, 64, 8, FAKE, FAKE, None), "NULL"),
+    ((FAKE + 8, 1 << 20, 64, 8, FAKE, FAKE, None), "aligned"),
+    ((FAKE, 1 << 20, 12, 8, FAKE, FAKE, None), "multiple of 8"),
+    ((FAKE, 1 << 20, 64, 3, FAKE, FAKE, None), "depth"),
+    ((FAKE, 64 * 1024 * 8 - 1, 64, 8, FAKE, FAKE, None), "less than"),
+])
+def test_read_probe_refusals(args, needle):
+    n = ctypes.c_size_t(0)  # a host location for the byte count, never written on these paths
+    st, msg = _call("moe_hbm_read_probe", *args[:5], ctypes.byref(n), args[6])
+    assert st == Q.MOE_ERR_INVALID_ARGUMENT and needle in msg, msg
