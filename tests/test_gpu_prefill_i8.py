@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import fixtures as F
+import oracle as O
 import quantized_routed_expert_moe_amd as Q
 from fixtures import workloads as W
 from tests.gpu_util import THREADS, say
@@ -78,6 +79,68 @@ def test_prefill_i8_at_the_slot_limit():
     say(wl.name)
     F.set_num_threads(THREADS)
     assert _prefill_case(wl, pair_dtype=torch.float32, y_dtype=torch.float32, path=I8) <= PREFILL_TOL
+
+
+def _two_planes(v: np.ndarray) -> np.ndarray:
+    """A row as the int8 path represents it, in fp64: s (q1 + q2 / 254) with
+    s = max|v| / 127, each code decided in fp32 (v * (1 / s) rounded to
+    nearest even, the remainder times 254 likewise), clamped to [-127, 127]."""
+    v32 = v.astype(np.float32)
+    mx = np.float32(np.max(np.abs(v32)))
+    s = mx / np.float32(127.0) if mx > 0 else np.float32(1.0)
+    y = v32 * (np.float32(1.0) / s)
+    f1 = np.clip(np.rint(y), -127, 127).astype(np.float32)
+    f2 = np.clip(np.rint((y - f1) * np.float32(254.0)), -127, 127)
+    return float(s) * (f1.astype(np.float64) + f2.astype(np.float64) / 254.0)
+
+
+def test_prefill_i8_equals_its_two_plane_model():
+    """The int8 path is the exact layer with three roundings: x split into
+    two int8 planes per row, h rounded to bf16, and h split into two planes;
+    the Q4_K weights enter exactly (d sc and dmin m are exact in fp32).
+    Emulating those on the oracle's fp64 dequantized weights reproduces the
+    GPU's y_pairs up to fp32 accumulation noise.  Each sub-block's scale
+    term d sc (T1 + T2 / 254) and min term dmin m X are formed apart in fp32
+    and largely cancel, so g and u carry up to about 2^-14 of their own value
+    in rounding error: an h that close to a bf16 rounding midpoint may round
+    either way, which moves that element by one bf16 ulp plus the two planes'
+    representation error (allowed for); a pair whose largest |h| is such an
+    element (its scale may differ) is left out, and such pairs must be rare
+    (measured: 3 of 128, the rest within 1.2e-7 of the model)."""
+    from tests.gpu_util import device_layer, run_device
+    wl = W.Workload("prefill int8 rounding model", F.Q4K, 512, 256, 4, 2, 64, x_bf16=True, seed=11)
+    say(wl.name)
+    x, logits = W.x_of(wl), W.logits_of(wl)
+    blobs = W.expert_blobs(wl)
+    soe, S = W.slot_map(wl)
+    got = run_device(device_layer(wl, blobs, soe, S, None, wl.T, I8, pair_dtype=torch.float32), x, logits)
+    H, I = wl.H, wl.I
+    gb = F.matrix_bytes(F.Q4K, I, H)
+    xf = W.x_f64(wl, x)
+    worst, left_out = 0.0, 0
+    for t in range(wl.T):
+        xt = _two_planes(xf[t])
+        for j in range(wl.k):
+            b = blobs[int(got["ids"][t, j])]
+            Wg = O.dequant(F.Q4K, b[:gb], I * H).reshape(I, H)
+            Wu = O.dequant(F.Q4K, b[gb:2 * gb], I * H).reshape(I, H)
+            Wd = O.dequant(F.Q4K, b[2 * gb:], H * I).reshape(H, I)
+            g, u = Wg @ xt, Wu @ xt
+            hx = g / (1 + np.exp(-g)) * u
+            h = F.bf16_bits_to_f32(F.to_bf16_bits(hx.astype(np.float32))).astype(np.float64)
+            ulp = np.ldexp(1.0, np.frexp(np.abs(h) + 1e-300)[1] - 8)
+            mid = np.minimum(np.abs(np.abs(hx) - (np.abs(h) - ulp / 2)), np.abs(np.abs(hx) - (np.abs(h) + ulp / 2)))
+            amb = mid <= np.abs(hx) * 2.0 ** -14
+            if amb.any() and np.abs(h[amb]).max() >= np.abs(h).max() - ulp.max():
+                left_out += 1
+                continue
+            y = Wd @ _two_planes(h)
+            slack = np.abs(Wd[:, amb]) @ (ulp[amb] + np.abs(h).max() / 127 / 254)
+            dev = np.abs(got["y_pairs"][t * wl.k + j] - y)
+            worst = max(worst, float(np.max((dev - slack) / np.abs(y).max())))
+    say(f"  max (|y_pair - model| - midpoint allowance) / max |model| = {worst:.3e}, pairs left out {left_out}")
+    assert left_out <= 6
+    assert worst <= 2e-5
 
 
 def test_prefill_i8_refuses_other_formats():
