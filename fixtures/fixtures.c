@@ -27,7 +27,7 @@
  *     The bloomery README (0.3.1) names these "k-quant" stored types in its
  *     Status table ("Quant types" row) and its "References and credits"
  *     section; the per-block formulas are the problem statement's.  The byte
- *     order inside a Q4_K block is the GGUF order as read for this build.
+ *     order inside a Q4_K block is the GGUF order as read here.
  */
 #include <math.h>
 #include <stdint.h>

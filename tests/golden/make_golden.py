@@ -14,7 +14,7 @@ computed here with exact rational arithmetic from the block formula:
 Stored types: bloomery README of 2026-09-24 (shared experts kept in Q8_0)
 and bloomery README 0.3.1 ("Status (0.3.1)" table, "Quant types" row: card
 experts in k-quant types).  The Q4_K byte order is the GGUF order as read
-for this build (12 scale bytes: low 6 bits of bytes 0-3 / 4-7 are sc/m of
+here (12 scale bytes: low 6 bits of bytes 0-3 / 4-7 are sc/m of
 sub-blocks 0-3; sub-blocks 4-7 take their low nibbles from bytes 8-11 and
 their top two bits from the top of bytes 0-3 / 4-7; quant byte 32c+l holds
 element l of sub-block 2c low and of 2c+1 high).
@@ -98,7 +98,7 @@ def mxfp4_case(name: str, x_bits: int, codes: list[int], note: str) -> dict:
 def q3k_case(name: str, d_bits: int, sc: list[int], q: list[int], note: str) -> dict:
     """One Q3_K super-block from its fields: 16 signed scales sc_j in -32..31
     (stored + 32 in six bits) and 256 quants q in -4..3 (stored q + 4: two low
-    bits and one high bit).  Byte order as read for this build: 32 bytes of
+    bits and one high bit).  Byte order as read here: 32 bytes of
     high bits (element i = 128h + 32g + l: bit 4h + g of byte l), 64 bytes of
     low bits (bits 2g of byte 32h + l), 12 scale bytes (scale j: low nibble of
     byte j for j < 8, high nibble of byte j - 8 otherwise; top two bits at bit
@@ -153,7 +153,7 @@ def q5k_case(name: str, d_bits: int, dmin_bits: int, sc: list[int], m: list[int]
 
 def q6k_case(name: str, d_bits: int, sc: list[int], q: list[int], note: str) -> dict:
     """One Q6_K super-block: 16 signed 8-bit scales, 256 quants q in 0..63
-    (w uses q - 32).  Bytes as read for this build: 128 bytes of low nibbles
+    (w uses q - 32).  Bytes as read here: 128 bytes of low nibbles
     (element 128h + 32g + l: byte 64h + l + 32 (g % 2), low nibble for g < 2,
     high nibble otherwise), 64 bytes of high bit pairs (bits 2g of byte
     32h + l), the 16 scales, fp16 d."""
@@ -223,11 +223,11 @@ def main() -> None:
     doc = dict(
         citation=("Stored block types: bloomery README of 2026-09-24 (shared experts in Q8_0) and bloomery README "
                   "0.3.1, 'Status (0.3.1)' table, 'Quant types' row (card experts in Q4_K to Q6_K and MXFP4); "
-                  "block formulas of the problem statement; Q4_K byte order as read for this build (GGUF order); "
+                  "block formulas of the problem statement; Q4_K byte order as read here (GGUF order); "
                   "MXFP4 element and scale encodings of the OCP Microscaling Formats (MX) v1.0 specification, "
-                  "byte order as read for this build (scale byte, then elements 0-15 in low nibbles, 16-31 in "
+                  "byte order as read here (scale byte, then elements 0-15 in low nibbles, 16-31 in "
                   "high nibbles); Q3_K (bloomery README 0.3.11, limits list: the V4.1 card experts' gate and up "
-                  "matrices) in the GGUF order as read for this build; Q5_K (README 0.3.1 'Quant types' row: card "
+                  "matrices) in the GGUF order as read here; Q5_K (README 0.3.1 'Quant types' row: card "
                   "experts in Q4_K to Q6_K) likewise."),
         derivation="expected[i] written by tests/golden/make_golden.py with exact rationals from the listed fields",
         cases=cases)
@@ -240,7 +240,7 @@ def main() -> None:
     routing = dict(
         citation=("Top-k by score with ids exact: bloomery README of 2026-09-24, oracle sets (integer router "
                   "outputs match exactly outside tie bands); tie rule (equal logits: lower id first) and the "
-                  "softmax / sigmoid weight rules as read for this build."),
+                  "softmax / sigmoid weight rules as read here."),
         cases=[
             dict(name="softmax_top2", logits=[[2.0, 1.0, 0.0, -1.0]], k=2, score="softmax", renormalize=True,
                  scale=1.0, ids=[[0, 1]], w=[[e / (e + 1), 1 / (e + 1)]],
