@@ -410,6 +410,12 @@ def test_noalloc_ffn_rejects_beyond_its_scratch_without_touching_the_device():
     assert st == Q.MOE_ERR_UNSUPPORTED and "multiples of 256" in msg
     # the 4096-token prefill layer's workspace fits
     assert Q.moe_ffn_workspace_size(Q.MOE_FMT_Q4K, 4096, 8, 2048, 768, Q.MOE_PATH_PREFILL) <= Q.MOE_NOALLOC_SCRATCH_BYTES
+    # through the int8-activation path (two activation planes) it does not
+    args[3], args[7], args[15] = 2048, 4096, Q.MOE_PATH_PREFILL_I8
+    need = Q.moe_ffn_workspace_size(Q.MOE_FMT_Q4K, 4096, 8, 2048, 768, Q.MOE_PATH_PREFILL_I8)
+    assert need > Q.MOE_NOALLOC_SCRATCH_BYTES
+    st, msg = _call("moe_expert_ffn_q4k_noalloc", *args)
+    assert st == Q.MOE_ERR_UNSUPPORTED and f"needs {need} bytes" in msg
 
 
 def test_ffn_int8_path_refusals():
