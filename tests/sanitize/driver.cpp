@@ -110,6 +110,27 @@ static void refusals() {
                               MOE_PATH_PREFILL, v, 1 << 30, nullptr) == MOE_ERR_UNSUPPORTED);
     CHECK(moe_expert_ffn_q4k_noalloc(kFake, stride, 128, 2048, 768, f, MOE_BF16, 8192, 8, i, i, i, i, v, MOE_BF16,
                                      MOE_PATH_PREFILL, nullptr) == MOE_ERR_UNSUPPORTED);
+    // the int8-activation path: Q4_K only, bf16 activations, its larger workspace
+    const size_t stride_mx = moe_packed_blob_bytes(MOE_FMT_MXFP4, 2048, 768);
+    CHECK(moe_expert_ffn_mxfp4(kFake, stride_mx, 128, 2048, 768, f, MOE_BF16, 64, 8, i, i, i, i, v, MOE_BF16,
+                               MOE_PATH_PREFILL_I8, v, 1 << 30, nullptr) == MOE_ERR_UNSUPPORTED);
+    CHECK(moe_expert_ffn_q4k(kFake, stride, 128, 2048, 768, f, MOE_F32, 64, 8, i, i, i, i, v, MOE_BF16,
+                             MOE_PATH_PREFILL_I8, v, 1 << 30, nullptr) == MOE_ERR_UNSUPPORTED);
+    const size_t need_i8 = moe_ffn_workspace_size(MOE_FMT_Q4K, 64, 8, 2048, 768, MOE_PATH_PREFILL_I8);
+    CHECK(need_i8 > moe_ffn_workspace_size(MOE_FMT_Q4K, 64, 8, 2048, 768, MOE_PATH_PREFILL));
+    CHECK(moe_expert_ffn_q4k(kFake, stride, 128, 2048, 768, f, MOE_BF16, 64, 8, i, i, i, i, v, MOE_BF16,
+                             MOE_PATH_PREFILL_I8, v, need_i8 - 1, nullptr) == MOE_ERR_WORKSPACE_TOO_SMALL);
+    CHECK(moe_expert_ffn_q4k_noalloc(kFake, stride, 128, 2048, 768, f, MOE_BF16, 4096, 8, i, i, i, i, v, MOE_BF16,
+                                     MOE_PATH_PREFILL_I8, nullptr) == MOE_ERR_UNSUPPORTED);
+    // the measurement probes' argument checks
+    CHECK(moe_prefill_inner_probe(3, 8, fo, MOE_PREFILL_PROBE_OUT_FLOATS, nullptr) == MOE_ERR_INVALID_ARGUMENT);
+    CHECK(moe_prefill_inner_probe(0, 0, fo, MOE_PREFILL_PROBE_OUT_FLOATS, nullptr) == MOE_ERR_INVALID_ARGUMENT);
+    CHECK(moe_prefill_inner_probe(2, 8, fo, MOE_PREFILL_PROBE_OUT_FLOATS - 1, nullptr) == MOE_ERR_INVALID_ARGUMENT);
+    size_t nread = 0;
+    uint32_t* sink = reinterpret_cast<uint32_t*>(v);
+    CHECK(moe_hbm_read_probe(kFake, 1 << 20, 12, 8, sink, &nread, nullptr) == MOE_ERR_INVALID_ARGUMENT);
+    CHECK(moe_hbm_read_probe(kFake, 1 << 20, 64, 3, sink, &nread, nullptr) == MOE_ERR_INVALID_ARGUMENT);
+    CHECK(moe_hbm_read_probe(kFake, 1024, 64, 8, sink, &nread, nullptr) == MOE_ERR_INVALID_ARGUMENT);
     CHECK(moe_combine(v, MOE_F32, i, f, i, 8, 9, nullptr, 4, 2, 256, v, MOE_F32, nullptr) ==
           MOE_ERR_INVALID_ARGUMENT);
     CHECK(moe_combine(v, MOE_F32, i, f, i, 8, 8, nullptr, 4, 2, 252, v, MOE_F32, nullptr) == MOE_ERR_UNSUPPORTED);
