@@ -266,3 +266,25 @@ def test_prefill_graph_replay_equals_eager(path):
             g.replay()
             torch.cuda.synchronize()
             assert torch.equal(y_graph, eager[i]), (rep, i)
+
+
+@pytest.mark.parametrize("path", [Q.MOE_PATH_PREFILL, Q.MOE_PATH_PREFILL_I8], ids=["bf16", "int8"])
+def test_prefill_zero_and_outlier_rows(path):
+    """Token rows of zeros give y exactly zero (on the int8 path the row
+    scale of a zero row falls back to 1 with every code 0); a row with one
+    element 1000 times the others' scale stays within the bound."""
+    from tests.gpu_util import run_oracle
+    wl = W.Workload("prefill zero and outlier rows", F.Q4K, 512, 256, 8, 2, 96, x_bf16=True, seed=13)
+    say(f"{wl.name}, path {path}")
+    x = W.x_of(wl).copy()
+    zero = np.arange(wl.T) % 3 == 0
+    x[zero] = 0
+    x[1, 5] = F.to_bf16_bits(np.array([1000.0], dtype=np.float32))[0]
+    logits = W.logits_of(wl)
+    soe, S = W.slot_map(wl)
+    blobs = W.expert_blobs(wl)
+    got = run_device(device_layer(wl, blobs, soe, S, None, wl.T, path), x, logits)
+    want = run_oracle(wl, blobs, x, logits, soe, None)
+    assert np.all(got["y"][zero] == 0)
+    assert np.all(want["y"][zero] == 0)
+    assert _row_err(got["y"][~zero], want["y"][~zero]) <= PREFILL_TOL
